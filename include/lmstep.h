@@ -1,0 +1,175 @@
+/*
+ * lmstep.h - C ABI of the MI355X (gfx950) training-step library.
+ *
+ * One training step of a pre-LayerNorm decoder-only transformer, as the pages
+ * on building GPT-style models without a framework describe it:
+ *   - token embedding plus a learned positional embedding added directly
+ *     (Feste page, "Model Architecture");
+ *   - blocks of LayerNorm -> causal multi-head self-attention (future
+ *     positions masked with -inf before the softmax) -> residual, then
+ *     LayerNorm -> GELU MLP -> residual; a final LayerNorm (Feste page,
+ *     "Model Architecture"; RustGPT page, file list: layer_norm, self_attention,
+ *     feed_forward);
+ *   - the vocabulary projection with softmax cross-entropy (RustGPT page,
+ *     technical-implementation list; Smallem page, "Ce qu'est un modele de
+ *     langage": V probabilities that sum to 1);
+ *   - a hand-derived backward pass and AdamW with decoupled weight decay and
+ *     global L2 gradient clipping (Feste page, "Manual Backpropagation";
+ *     RustGPT page: clip to an L2 norm of 5.0);
+ *   - optional packing of several documents per row (LucilleAI page, "what
+ *     makes it special": sequence packing), with a block-diagonal causal mask.
+ *
+ * Readings fixed by this library where the pages are silent: GELU is the tanh
+ * form 0.5u(1 + tanh(sqrt(2/pi)(u + 0.044715u^3))); LayerNorm uses the biased
+ * variance; the attention scale is 1/sqrt(D); positions restart at 0 in every
+ * packed document; the vocabulary projection is tied to wte and has no bias;
+ * the loss is the mean over positions whose target is >= 0; the clip factor is
+ * clip/n only when the global norm n exceeds clip; weight decay applies to
+ * every parameter as lr*wd*p on the pre-update p.
+ *
+ * Conventions
+ *   - Every call returns lm_status (0 = LM_OK). On error lm_last_error()
+ *     returns a thread-local message. No C++ exception crosses this ABI.
+ *   - "d_" pointers are device pointers (hipMalloc'd or torch CUDA memory);
+ *     "stream" is a hipStream_t passed as void*. NULL means the null stream.
+ *   - The library never allocates device memory: the caller passes one arena
+ *     of lm_workspace_bytes() bytes (256-byte aligned) to model_create and
+ *     keeps it alive until model_destroy. The library owns only the opaque
+ *     host-side lm_model.
+ *   - train_step and forward_logits only enqueue work on the stream; they
+ *     return before the GPU finishes. Host-checkable argument errors are
+ *     returned before anything is enqueued. Inputs must stay valid until the
+ *     stream's work completes.
+ *   - A model is not thread-safe; separate models are independent.
+ */
+#ifndef LMSTEP_H
+#define LMSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LM_OK = 0,
+  LM_ERR_ARG = -1,         /* null pointer or out-of-range argument        */
+  LM_ERR_WORKSPACE = -2,   /* arena too small or misaligned                */
+  LM_ERR_SHAPE = -3,       /* B > max_batch, T > max_seq, bad model dims    */
+  LM_ERR_HIP = -4,         /* a HIP runtime call failed                    */
+  LM_ERR_UNSUPPORTED = -5  /* valid but not implemented (e.g. head dim 48) */
+} lm_status;
+
+/* Model dimensions. d_model must be a multiple of 64 and of n_heads; the head
+ * dimension d_model / n_heads must be 32 or 64; d_mlp a multiple of 64.
+ * precision: 0 = fp32 everywhere; 1 = bf16 GEMM/attention operands with fp32
+ * accumulation, fp32 residual stream, statistics, loss, gradients, Adam
+ * moments and master weights. */
+typedef struct {
+  int32_t vocab, d_model, n_heads, d_mlp, n_layers, max_seq, max_batch;
+  int32_t precision;
+  float ln_eps; /* LayerNorm epsilon, e.g. 1e-5 */
+} lm_config;
+
+/* Optimiser settings for one step. step is 1-based and drives the Adam bias
+ * corrections 1 - beta^step. clip_norm <= 0 disables clipping. */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay, clip_norm;
+  int32_t step;
+} lm_optim;
+
+typedef enum { LM_PARAMS = 0, LM_GRADS = 1, LM_ADAM_M = 2, LM_ADAM_V = 3 } lm_buf;
+
+/* One entry of the parameter table. offset is in floats from the start of the
+ * flat fp32 buffer; rows x cols is the tensor's shape (cols = 1 for vectors).
+ * Order: wte[V,C], wpe[max_seq,C]; per block l: ln1.g, ln1.b [C],
+ * attn.w_qkv [3C,C], attn.b_qkv [3C], attn.w_o [C,C], attn.b_o [C], ln2.g,
+ * ln2.b [C], mlp.w_fc [F,C], mlp.b_fc [F], mlp.w_proj [C,F], mlp.b_proj [C];
+ * then lnf.g, lnf.b [C]. Names are "wte", "blocks.<l>.attn.w_qkv", "lnf.g"...
+ * Offsets are 64-float (256-byte) aligned; gaps hold zeros. Weight matrices
+ * are [out, in] row-major (Y = X W^T + b). */
+typedef struct {
+  char name[48];
+  int64_t offset, rows, cols;
+} lm_tensor_info;
+
+typedef struct lm_model lm_model;
+
+/* Bytes of device arena the model needs (0 if the config is invalid). */
+size_t lm_workspace_bytes(const lm_config* cfg);
+
+/* Validates cfg, carves d_arena (arena_bytes >= lm_workspace_bytes(cfg),
+ * 256-byte aligned) and zeroes parameters, gradients and Adam moments on
+ * stream. Parameters are then set by the caller with model_set(LM_PARAMS). */
+lm_status model_create(const lm_config* cfg, void* d_arena, size_t arena_bytes, void* stream,
+                       lm_model** out);
+
+/* Frees the host-side handle; the arena stays the caller's. NULL is a no-op. */
+void model_destroy(lm_model* model);
+
+/* Copies up to *count entries of the parameter table into out (if out is
+ * non-NULL), sets *count to the number of tensors and *total to the length
+ * of the flat buffer in floats. */
+lm_status model_param_table(const lm_model* model, lm_tensor_info* out, int32_t* count,
+                            int64_t* total);
+
+/* Copy a whole flat fp32 buffer (total floats, layout of the table) in or out.
+ * With *_on_device = 0 the host pointer is copied synchronously; with 1 the
+ * copy is enqueued on stream. Setting LM_PARAMS also refreshes the bf16
+ * operand copies of the weights. */
+lm_status model_set(lm_model* model, lm_buf which, const float* src, int src_on_device, void* stream);
+lm_status model_get(const lm_model* model, lm_buf which, float* dst, int dst_on_device, void* stream);
+
+/* One training step on a batch of B rows of T tokens (B <= max_batch,
+ * T <= max_seq):
+ *   d_tokens  [B,T] int32 in [0, vocab)
+ *   d_targets [B,T] int32 in [-1, vocab); -1 = no loss at this position
+ *   d_doc_ids [B,T] int32 non-decreasing per row, or NULL for one document per
+ *             row; a maximal run of equal ids is one document, attention stays
+ *             inside it and positions restart at its first token
+ * Computes the mean loss over valid targets, every gradient (kept raw,
+ * before clipping, in the LM_GRADS buffer), the global norm n, the clip factor
+ * and the AdamW update of parameters and moments.
+ *   d_stats (may be NULL): 4 floats written on the device:
+ *     [0] loss, [1] pre-clip gradient norm, [2] flags, [3] number of valid
+ *     targets. flags bit 0: the norm was not finite, so the update was skipped
+ *     and parameters and moments are unchanged; bit 1 (only with LMSTEP_CHECK=1
+ *     in the environment): a token, target or doc id was out of range or doc ids
+ *     decreased. */
+lm_status train_step(lm_model* model, const int32_t* d_tokens, const int32_t* d_targets,
+                     const int32_t* d_doc_ids, int32_t B, int32_t T, const lm_optim* opt,
+                     float* d_stats, void* stream);
+
+/* Forward pass only: d_logits [B,T,vocab] fp32 (row-major) receives
+ * z = LN_f(x_L) wte^T. No loss, no backward, no update. */
+lm_status forward_logits(lm_model* model, const int32_t* d_tokens, const int32_t* d_doc_ids,
+                         int32_t B, int32_t T, float* d_logits, void* stream);
+
+/* Thread-local message for the last non-OK status of this thread. */
+const char* lm_last_error(void);
+
+/* ---- measurement hooks (used by the benchmark) ----
+ * With profiling on, every kernel launch of train_step is bracketed by a pair
+ * of HIP events recorded on the step's stream, and model_profile_read sums
+ * their elapsed times per kernel class. Off by default; enabling it adds a
+ * few microseconds per launch. */
+typedef struct {
+  char name[40];     /* kernel class, e.g. "gemm_head_fwd"             */
+  int64_t launches;  /* launches recorded since the last reset          */
+  double ms;         /* summed event time over those launches           */
+  double flops;      /* algorithmic flops per step of this class        */
+  double bytes;      /* algorithmic HBM bytes per step of this class    */
+} lm_profile_entry;
+
+lm_status model_profile_enable(lm_model* model, int enable);
+/* Synchronises the events, fills up to cap entries, returns the number of
+ * classes in *n, and resets the accumulators when reset != 0. */
+lm_status model_profile_read(lm_model* model, lm_profile_entry* out, int32_t cap, int32_t* n,
+                             int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMSTEP_H */

@@ -1,0 +1,320 @@
+"""Python binding of the gfx950 training-step library (liblmstep.so).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. PyTorch provides device memory (the arena and the input/output
+tensors) and the current stream. Importing fails loudly when the library has
+not been built; there is no CPU fallback.
+
+The C ABI is declared in include/lmstep.h (model level) and
+include/lmstep_kernels.h (one kernel at a time).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblmstep.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()' or python scratch_decoder_only_amd/build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+c_int, c_int64, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+c_char_p, c_double = ctypes.c_char_p, ctypes.c_double
+
+LM_OK, LM_ERR_ARG, LM_ERR_WORKSPACE, LM_ERR_SHAPE, LM_ERR_HIP, LM_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+LM_PARAMS, LM_GRADS, LM_ADAM_M, LM_ADAM_V = 0, 1, 2, 3
+EPI_STORE, EPI_RESID, EPI_GELU, EPI_DGELU = 0, 1, 2, 3
+
+
+class LmConfig(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("d_mlp", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("max_seq", ctypes.c_int32),
+                ("max_batch", ctypes.c_int32), ("precision", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+class LmOptim(ctypes.Structure):
+    _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
+                ("weight_decay", c_float), ("clip_norm", c_float), ("step", ctypes.c_int32)]
+
+
+class LmTensorInfo(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("offset", c_int64), ("rows", c_int64), ("cols", c_int64)]
+
+
+class LmProfileEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 40), ("launches", c_int64), ("ms", c_double), ("flops", c_double),
+                ("bytes", c_double)]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_sig("lm_workspace_bytes", c_size_t, [ctypes.POINTER(LmConfig)])
+_sig("model_create", c_int, [ctypes.POINTER(LmConfig), c_void_p, c_size_t, c_void_p, ctypes.POINTER(c_void_p)])
+_sig("model_destroy", None, [c_void_p])
+_sig("model_param_table", c_int, [c_void_p, ctypes.POINTER(LmTensorInfo), ctypes.POINTER(ctypes.c_int32),
+                                  ctypes.POINTER(c_int64)])
+_sig("model_set", c_int, [c_void_p, c_int, c_void_p, c_int, c_void_p])
+_sig("model_get", c_int, [c_void_p, c_int, c_void_p, c_int, c_void_p])
+_sig("train_step", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32,
+                           ctypes.POINTER(LmOptim), c_void_p, c_void_p])
+_sig("forward_logits", c_int, [c_void_p, c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_void_p])
+_sig("lm_last_error", c_char_p, [])
+_sig("model_profile_enable", c_int, [c_void_p, c_int])
+_sig("model_profile_read", c_int, [c_void_p, ctypes.POINTER(LmProfileEntry), ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_int32), c_int])
+
+_P = c_void_p
+_sig("lmk_gemm", c_int, [c_int, c_int, c_int, c_int, _P, c_int64, c_int, _P, c_int64, c_int, _P, c_int64, c_int, c_int,
+                         _P, _P, c_int64, _P, c_int64, c_int, c_int, _P, c_int64, _P])
+_sig("lmk_layernorm_fwd", c_int, [c_int, _P, _P, _P, c_int, c_int, c_float, _P, _P, _P, _P])
+_sig("lmk_layernorm_bwd", c_int, [c_int, _P, _P, _P, _P, _P, c_int, c_int, _P, _P, _P, _P, _P, _P, _P])
+_sig("lmk_layernorm_bwd_ws_floats", c_int64, [c_int, c_int])
+_sig("lmk_colsum", c_int, [c_int, _P, c_int64, c_int, c_int, _P, _P, _P])
+_sig("lmk_colsum_ws_floats", c_int64, [c_int, c_int])
+_sig("lmk_index_layout", c_int, [_P, c_int, c_int, _P, _P, _P, _P, _P])
+_sig("lmk_embed_fwd", c_int, [_P, _P, _P, _P, c_int, c_int, c_int, _P, _P, _P])
+_sig("lmk_attn_fwd", c_int, [c_int, _P, _P, _P, c_int, c_int, c_int, c_int, _P, _P, _P])
+_sig("lmk_attn_bwd", c_int, [c_int, _P, _P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, _P, _P, _P])
+_sig("lmk_xent", c_int, [c_int, _P, c_int64, c_int, c_int, _P, _P, _P, _P, _P, _P])
+_sig("lmk_csr", c_int, [_P, c_int, c_int, _P, _P, _P, _P, _P])
+_sig("lmk_segment_sum", c_int, [_P, c_int, c_int, c_int, _P, _P, _P, _P, _P, _P, c_int, _P])
+_sig("lmk_segment_sum_ws_floats", c_int64, [c_int, c_int, c_int])
+_sig("lmk_grad_norm", c_int, [_P, c_int64, c_float, _P, _P, _P, _P])
+_sig("lmk_adamw", c_int, [_P, _P, _P, _P, c_int64, c_float, c_float, c_float, c_float, c_float, c_int, _P, _P, _P, _P])
+
+lib = _lib
+
+
+class LmError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str):
+    if rc != LM_OK:
+        msg = _lib.lm_last_error()
+        raise LmError(f"{what} failed with status {rc}: {msg.decode() if msg else ''}")
+
+
+def _kcheck(rc: int, what: str):
+    if rc != 0:
+        raise LmError(f"{what}: the kernel rejected its arguments (rc {rc})")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+class Model:
+    """One model instance on the current CUDA (HIP) device.
+
+    dims: object with vocab, d_model, n_heads, d_mlp, n_layers, max_seq,
+    ln_eps (e.g. a synth.ModelShape); precision "fp32" or "bf16".
+    """
+
+    def __init__(self, dims, max_batch: int, precision: Optional[str] = None, device="cuda"):
+        torch = _torch()
+        prec = precision or getattr(dims, "precision", "bf16")
+        self.cfg = LmConfig(dims.vocab, dims.d_model, dims.n_heads, dims.d_mlp, dims.n_layers, dims.max_seq,
+                            max_batch, 1 if prec == "bf16" else 0, float(getattr(dims, "ln_eps", 1e-5)))
+        self.precision = prec
+        nbytes = _lib.lm_workspace_bytes(ctypes.byref(self.cfg))
+        if nbytes == 0:
+            _check(LM_ERR_SHAPE, "lm_workspace_bytes")
+        self.arena = torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+        self._h = c_void_p()
+        _check(_lib.model_create(ctypes.byref(self.cfg), _ptr(self.arena), nbytes, _stream(), ctypes.byref(self._h)),
+               "model_create")
+        n = ctypes.c_int32(0)
+        total = c_int64(0)
+        _check(_lib.model_param_table(self._h, None, ctypes.byref(n), ctypes.byref(total)), "model_param_table")
+        arr = (LmTensorInfo * n.value)()
+        _check(_lib.model_param_table(self._h, arr, ctypes.byref(n), ctypes.byref(total)), "model_param_table")
+        self.table: List[Tuple[str, int, int, int]] = [(e.name.decode(), e.offset, e.rows, e.cols) for e in arr]
+        self.total = total.value
+        self.stats = torch.zeros(4, dtype=torch.float32, device=device)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.model_destroy(h)
+            self._h = c_void_p()
+
+    # ---- flat buffers <-> named tensors
+    def flatten(self, named: Dict[str, np.ndarray]) -> np.ndarray:
+        flat = np.zeros(self.total, np.float32)
+        for name, off, rows, cols in self.table:
+            a = np.asarray(named[name], dtype=np.float32).reshape(-1)
+            assert a.size == rows * cols, (name, a.shape, rows, cols)
+            flat[off:off + a.size] = a
+        return flat
+
+    def unflatten(self, flat: np.ndarray) -> Dict[str, np.ndarray]:
+        out = {}
+        for name, off, rows, cols in self.table:
+            a = flat[off:off + rows * cols]
+            out[name] = a.reshape(rows, cols) if cols > 1 else a.copy()
+        return out
+
+    def set(self, which: int, named: Dict[str, np.ndarray]):
+        flat = np.ascontiguousarray(self.flatten(named))
+        _check(_lib.model_set(self._h, which, flat.ctypes.data, 0, _stream()), "model_set")
+
+    def set_flat_device(self, which: int, t):
+        _check(_lib.model_set(self._h, which, _ptr(t), 1, _stream()), "model_set")
+
+    def get(self, which: int) -> Dict[str, np.ndarray]:
+        flat = np.zeros(self.total, np.float32)
+        _check(_lib.model_get(self._h, which, flat.ctypes.data, 0, _stream()), "model_get")
+        return self.unflatten(flat)
+
+    def get_flat(self, which: int) -> np.ndarray:
+        flat = np.zeros(self.total, np.float32)
+        _check(_lib.model_get(self._h, which, flat.ctypes.data, 0, _stream()), "model_get")
+        return flat
+
+    def get_flat_device(self, which: int, out):
+        _check(_lib.model_get(self._h, which, _ptr(out), 1, _stream()), "model_get")
+
+    # ---- the step
+    def train_step(self, tokens, targets, doc_ids=None, *, lr, step, beta1=0.9, beta2=0.999, eps=1e-8,
+                   weight_decay=0.0, clip=1.0, stats=None):
+        B, T = tokens.shape
+        opt = LmOptim(lr, beta1, beta2, eps, weight_decay, clip, step)
+        st = self.stats if stats is None else stats
+        _check(_lib.train_step(self._h, _ptr(tokens), _ptr(targets), _ptr(doc_ids), B, T, ctypes.byref(opt),
+                               _ptr(st), _stream()), "train_step")
+        return st
+
+    def forward_logits(self, tokens, doc_ids=None, out=None):
+        torch = _torch()
+        B, T = tokens.shape
+        if out is None:
+            out = torch.empty((B, T, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _check(_lib.forward_logits(self._h, _ptr(tokens), _ptr(doc_ids), B, T, _ptr(out), _stream()),
+               "forward_logits")
+        return out
+
+    # ---- measurement hooks
+    def profile(self, enable: bool):
+        _check(_lib.model_profile_enable(self._h, 1 if enable else 0), "model_profile_enable")
+
+    def profile_read(self, reset=True) -> Dict[str, dict]:
+        n = ctypes.c_int32(0)
+        _check(_lib.model_profile_read(self._h, None, 0, ctypes.byref(n), 0), "model_profile_read")
+        arr = (LmProfileEntry * max(1, n.value))()
+        _check(_lib.model_profile_read(self._h, arr, n.value, ctypes.byref(n), 1 if reset else 0),
+               "model_profile_read")
+        return {e.name.decode(): {"launches": e.launches, "ms": e.ms, "flops": e.flops, "bytes": e.bytes}
+                for e in arr[:n.value]}
+
+
+# --------------------------------------------------------------- kernel level
+# Thin wrappers of include/lmstep_kernels.h for per-kernel parity tests; all
+# tensors are torch CUDA tensors.
+
+def gemm(precision, M, N, K, A, lda, a_kc, B, ldb, b_kc, C, ldc, epi=EPI_STORE, c_f32=False, bias=None, R=None,
+         ldr=0, aux=None, ld_aux=0, force_split=0, M_out=0, ws=None):
+    rc = _lib.lmk_gemm(precision, M, N, K, _ptr(A), lda, int(a_kc), _ptr(B), ldb, int(b_kc), _ptr(C), ldc, epi,
+                       int(c_f32), _ptr(bias), _ptr(R), ldr, _ptr(aux), ld_aux, force_split, M_out, _ptr(ws),
+                       0 if ws is None else ws.numel(), _stream())
+    _kcheck(rc, "lmk_gemm")
+
+
+def layernorm_fwd(precision, x, g, b, eps, y, mu, rstd):
+    M, C = x.shape
+    _kcheck(_lib.lmk_layernorm_fwd(precision, _ptr(x), _ptr(g), _ptr(b), M, C, eps, _ptr(y), _ptr(mu), _ptr(rstd),
+                                   _stream()), "lmk_layernorm_fwd")
+
+
+def layernorm_bwd_ws_floats(M, C):
+    return _lib.lmk_layernorm_bwd_ws_floats(M, C)
+
+
+def layernorm_bwd(precision, dy, x, mu, rstd, g, g_in, g_out, g_act, dgamma, dbeta, ws):
+    M, C = x.shape
+    _kcheck(_lib.lmk_layernorm_bwd(precision, _ptr(dy), _ptr(x), _ptr(mu), _ptr(rstd), _ptr(g), M, C, _ptr(g_in),
+                                   _ptr(g_out), _ptr(g_act), _ptr(dgamma), _ptr(dbeta), _ptr(ws), _stream()),
+            "lmk_layernorm_bwd")
+
+
+def colsum_ws_floats(M, N):
+    return _lib.lmk_colsum_ws_floats(M, N)
+
+
+def colsum(precision_of_a, a, lda, M, N, out, ws):
+    _kcheck(_lib.lmk_colsum(precision_of_a, _ptr(a), lda, M, N, _ptr(out), _ptr(ws), _stream()), "lmk_colsum")
+
+
+def index_layout(doc, B, T, start, end, pos, flags):
+    _kcheck(_lib.lmk_index_layout(_ptr(doc), B, T, _ptr(start), _ptr(end), _ptr(pos), _ptr(flags), _stream()),
+            "lmk_index_layout")
+
+
+def embed_fwd(tok, pos, wte, wpe, x, flags):
+    M = tok.numel()
+    V, C = wte.shape
+    _kcheck(_lib.lmk_embed_fwd(_ptr(tok), _ptr(pos), _ptr(wte), _ptr(wpe), M, C, V, _ptr(x), _ptr(flags), _stream()),
+            "lmk_embed_fwd")
+
+
+def attn_fwd(precision, qkv, start, end, B, T, H, D, o, lse):
+    _kcheck(_lib.lmk_attn_fwd(precision, _ptr(qkv), _ptr(start), _ptr(end), B, T, H, D, _ptr(o), _ptr(lse),
+                              _stream()), "lmk_attn_fwd")
+
+
+def attn_bwd(precision, qkv, o, lse, dout, start, end, B, T, H, D, delta, dqkv):
+    _kcheck(_lib.lmk_attn_bwd(precision, _ptr(qkv), _ptr(o), _ptr(lse), _ptr(dout), _ptr(start), _ptr(end), B, T, H,
+                              D, _ptr(delta), _ptr(dqkv), _stream()), "lmk_attn_bwd")
+
+
+def xent(precision, z, ldz, M, V, tgt, loss, ws_n, ws_rows, flags):
+    _kcheck(_lib.lmk_xent(precision, _ptr(z), ldz, M, V, _ptr(tgt), _ptr(loss), _ptr(ws_n), _ptr(ws_rows),
+                          _ptr(flags), _stream()), "lmk_xent")
+
+
+def csr(keys, M, nkeys, counts, offsets, chunk_base, perm):
+    _kcheck(_lib.lmk_csr(_ptr(keys), M, nkeys, _ptr(counts), _ptr(offsets), _ptr(chunk_base), _ptr(perm), _stream()),
+            "lmk_csr")
+
+
+def segment_sum_ws_floats(M, nkeys, C):
+    return _lib.lmk_segment_sum_ws_floats(M, nkeys, C)
+
+
+def segment_sum(dx, M, C, nkeys, counts, offsets, chunk_base, perm, partial, dst, accumulate):
+    _kcheck(_lib.lmk_segment_sum(_ptr(dx), M, C, nkeys, _ptr(counts), _ptr(offsets), _ptr(chunk_base), _ptr(perm),
+                                 _ptr(partial), _ptr(dst), int(accumulate), _stream()), "lmk_segment_sum")
+
+
+def grad_norm(g, clip, part, norm_scale, flags):
+    _kcheck(_lib.lmk_grad_norm(_ptr(g), g.numel(), clip, _ptr(part), _ptr(norm_scale), _ptr(flags), _stream()),
+            "lmk_grad_norm")
+
+
+def adamw(p, g, m, v, lr, beta1, beta2, eps, wd, step, norm_scale, flags, shadow=None):
+    _kcheck(_lib.lmk_adamw(_ptr(p), _ptr(g), _ptr(m), _ptr(v), p.numel(), lr, beta1, beta2, eps, wd, step,
+                           _ptr(norm_scale), _ptr(flags), _ptr(shadow), _stream()), "lmk_adamw")

@@ -1,0 +1,696 @@
+// Host side of the C ABI: configuration checks, the parameter table, carving
+// of the caller's arena, and the fixed kernel sequence of one training step.
+// Everything is enqueued on the caller's stream; the library never allocates
+// device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/lmstep.h"
+#include "kernels.h"
+
+using namespace lm;
+
+namespace {
+
+thread_local std::string g_err;
+
+lm_status fail(lm_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+long round_up(long v, long a) { return (v + a - 1) / a * a; }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t n) {
+    off = align_up(off, kAlign);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+struct TensorInfo {
+  std::string name;
+  long off, rows, cols;
+};
+
+// Per-class event timing of kernel launches (measurement hook).
+struct Profiler {
+  bool on = false;
+  struct Cls {
+    std::string name;
+    long launches = 0;
+    double ms = 0, flops = 0, bytes = 0;
+  };
+  std::vector<Cls> cls;
+  struct Pending {
+    int cls;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  size_t pool_used = 0;
+
+  int find(const char* name) {
+    for (size_t i = 0; i < cls.size(); ++i)
+      if (cls[i].name == name) return (int)i;
+    cls.push_back(Cls{name});
+    return (int)cls.size() - 1;
+  }
+  hipEvent_t take() {
+    if (pool_used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[pool_used++];
+  }
+  void drain() {
+    if (pending.empty()) return;
+    (void)hipEventSynchronize(pending.back().b);
+    for (auto& p : pending) {
+      float ms = 0;
+      if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) cls[p.cls].ms += ms;
+    }
+    pending.clear();
+    pool_used = 0;
+  }
+  ~Profiler() {
+    for (auto e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+}  // namespace
+
+struct lm_model {
+  lm_config cfg;
+  int V, C, H, D, F, L, S, Bmax;
+  bool bf;   // bf16 compute
+  long Vp;   // padded vocabulary (columns of the logits, rows of the bf16 wte copy)
+  long ldz;  // leading dimension of the logits
+  std::vector<TensorInfo> table;
+  long P = 0;  // floats in the flat parameter buffer
+  // tensor offsets
+  long o_wte, o_wpe, o_lnf_g, o_lnf_b;
+  struct Blk {
+    long ln1_g, ln1_b, w_qkv, b_qkv, w_o, b_o, ln2_g, ln2_b, w_fc, b_fc, w_proj, b_proj;
+  };
+  std::vector<Blk> blk;
+  size_t act_size;  // bytes of one activation element
+  // arena slices
+  float *params, *grads, *adam_m, *adam_v;
+  bf16* shadow;  // bf16 copy of the parameters (bf16 path), wte padded to Vp rows
+  float* x;      // [L+1][M][C]
+  float* xm;     // [L][M][C]
+  char *y1, *qkv, *o, *y2, *u, *a, *hf, *logits;
+  float *mu1, *r1, *mu2, *r2, *muf, *rf, *lse;
+  float *g, *dy, *delta;
+  char *g_act, *dbig, *dO;
+  float *ln_part, *col_part, *gemm_ws;
+  long gemm_ws_floats;
+  EmbedBwdWs emb_tok, emb_pos;
+  int32_t *start, *end, *pos, *n_valid;
+  uint32_t* flags;
+  float *row_loss, *norm_scale, *stats_own;
+  double* norm_part;
+  size_t bytes = 0;
+  Profiler prof;
+  int check = 0;
+
+  long M() const { return (long)Bmax * S; }
+  const float* P_(long off) const { return params + off; }
+  template <typename T>
+  T* act(char* base, long elem_off) const {
+    return reinterpret_cast<T*>(base + elem_off * act_size);
+  }
+  // operand copy of a weight: bf16 shadow (bf16 path) or the fp32 master
+  const void* W(long off) const {
+    if (!bf) return params + off;
+    long o = off >= o_wte + (long)V * C ? off + (Vp - V) * C : off;
+    return shadow + o;
+  }
+};
+
+namespace {
+
+lm_status validate(const lm_config* c) {
+  if (!c) return fail(LM_ERR_ARG, "config is NULL");
+  if (c->vocab < 1 || c->d_model < 1 || c->n_heads < 1 || c->d_mlp < 1 || c->n_layers < 0 || c->max_seq < 1 ||
+      c->max_batch < 1)
+    return fail(LM_ERR_SHAPE, "model dimensions must be positive (n_layers >= 0)");
+  if (c->d_model % c->n_heads) return fail(LM_ERR_SHAPE, "d_model must be a multiple of n_heads");
+  if (c->d_model % 128 || c->d_model > 1024)
+    return fail(LM_ERR_UNSUPPORTED, "d_model must be a multiple of 128 and at most 1024");
+  int D = c->d_model / c->n_heads;
+  if (D != 32 && D != 64) return fail(LM_ERR_UNSUPPORTED, "head dimension must be 32 or 64");
+  if (c->d_mlp % 64) return fail(LM_ERR_UNSUPPORTED, "d_mlp must be a multiple of 64");
+  if (c->precision != 0 && c->precision != 1) return fail(LM_ERR_ARG, "precision must be 0 (fp32) or 1 (bf16)");
+  if (!(c->ln_eps >= 0.f)) return fail(LM_ERR_ARG, "ln_eps must be >= 0");
+  if ((long)c->max_batch * c->max_seq > (1L << 24)) return fail(LM_ERR_SHAPE, "max_batch * max_seq too large");
+  return LM_OK;
+}
+
+void build_table(lm_model* m) {
+  auto add = [&](const std::string& n, long rows, long cols) {
+    long off = m->P;
+    m->table.push_back({n, off, rows, cols});
+    m->P = round_up(off + rows * cols, 64);
+    return off;
+  };
+  const int V = m->V, C = m->C, F = m->F, S = m->S;
+  m->o_wte = add("wte", V, C);
+  m->o_wpe = add("wpe", S, C);
+  m->blk.resize(m->L);
+  for (int l = 0; l < m->L; ++l) {
+    std::string p = "blocks." + std::to_string(l) + ".";
+    auto& b = m->blk[l];
+    b.ln1_g = add(p + "ln1.g", C, 1);
+    b.ln1_b = add(p + "ln1.b", C, 1);
+    b.w_qkv = add(p + "attn.w_qkv", 3L * C, C);
+    b.b_qkv = add(p + "attn.b_qkv", 3L * C, 1);
+    b.w_o = add(p + "attn.w_o", C, C);
+    b.b_o = add(p + "attn.b_o", C, 1);
+    b.ln2_g = add(p + "ln2.g", C, 1);
+    b.ln2_b = add(p + "ln2.b", C, 1);
+    b.w_fc = add(p + "mlp.w_fc", F, C);
+    b.b_fc = add(p + "mlp.b_fc", F, 1);
+    b.w_proj = add(p + "mlp.w_proj", C, F);
+    b.b_proj = add(p + "mlp.b_proj", C, 1);
+  }
+  m->o_lnf_g = add("lnf.g", C, 1);
+  m->o_lnf_b = add("lnf.b", C, 1);
+}
+
+// Lays out every slice of the arena (base == nullptr: size only).
+void carve(lm_model* m, char* base) {
+  Carver c{base};
+  const long M = m->M(), C = m->C, F = m->F, L = m->L;
+  const size_t A = m->act_size;
+  m->params = c.take<float>(m->P);
+  m->grads = c.take<float>(m->P);
+  m->adam_m = c.take<float>(m->P);
+  m->adam_v = c.take<float>(m->P);
+  m->shadow = m->bf ? c.take<bf16>(m->P + (m->Vp - m->V) * C) : nullptr;
+  m->x = c.take<float>((L + 1) * M * C);
+  m->xm = c.take<float>(L * M * C);
+  m->y1 = c.take<char>(L * M * C * A);
+  m->qkv = c.take<char>(L * M * 3 * C * A);
+  m->o = c.take<char>(L * M * C * A);
+  m->y2 = c.take<char>(L * M * C * A);
+  m->u = c.take<char>(L * M * F * A);
+  m->a = c.take<char>(L * M * F * A);
+  m->hf = c.take<char>(M * C * A);
+  m->logits = c.take<char>(M * m->ldz * A);
+  m->mu1 = c.take<float>(L * M);
+  m->r1 = c.take<float>(L * M);
+  m->mu2 = c.take<float>(L * M);
+  m->r2 = c.take<float>(L * M);
+  m->muf = c.take<float>(M);
+  m->rf = c.take<float>(M);
+  m->lse = c.take<float>(L * M * m->H);
+  m->g = c.take<float>(M * C);
+  m->dy = c.take<float>(M * C);
+  m->delta = c.take<float>(M * m->H);
+  m->g_act = c.take<char>(M * C * A);
+  m->dbig = c.take<char>(M * std::max(F, 3 * C) * A);
+  m->dO = c.take<char>(M * C * A);
+  long ln_blocks = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
+  m->ln_part = c.take<float>(2 * ln_blocks * C);
+  long col_blocks = (M + kColRows - 1) / kColRows;
+  m->col_part = c.take<float>(col_blocks * std::max(F, 3 * C));
+  m->gemm_ws_floats = 8L * std::max(F, 3 * C) * std::max(F, C);
+  m->gemm_ws = c.take<float>(m->gemm_ws_floats);
+  for (int k = 0; k < 2; ++k) {
+    EmbedBwdWs& e = k == 0 ? m->emb_tok : m->emb_pos;
+    long nkeys = k == 0 ? m->V : m->S;
+    e.counts = c.take<int32_t>(nkeys + 1);
+    e.offsets = c.take<int32_t>(nkeys + 1);
+    e.chunk_base = c.take<int32_t>(nkeys + 1);
+    e.perm = c.take<int32_t>(M);
+    e.partial = c.take<float>(embed_bwd_max_chunks((int)M, (int)nkeys) * C);
+  }
+  m->start = c.take<int32_t>(M);
+  m->end = c.take<int32_t>(M);
+  m->pos = c.take<int32_t>(M);
+  m->n_valid = c.take<int32_t>(4);
+  m->flags = c.take<uint32_t>(4);
+  m->row_loss = c.take<float>(M);
+  m->norm_scale = c.take<float>(4);
+  m->stats_own = c.take<float>(4);
+  m->norm_part = c.take<double>(kNormBlocks);
+  m->bytes = align_up(c.off, kAlign);
+}
+
+lm_model* new_model(const lm_config* cfg) {
+  lm_model* m = new lm_model();
+  m->cfg = *cfg;
+  m->V = cfg->vocab;
+  m->C = cfg->d_model;
+  m->H = cfg->n_heads;
+  m->D = cfg->d_model / cfg->n_heads;
+  m->F = cfg->d_mlp;
+  m->L = cfg->n_layers;
+  m->S = cfg->max_seq;
+  m->Bmax = cfg->max_batch;
+  m->bf = cfg->precision == 1;
+  m->act_size = m->bf ? 2 : 4;
+  m->Vp = m->bf ? round_up(m->V, 128) : m->V;
+  m->ldz = m->bf ? m->Vp : round_up(m->V, 4);
+  build_table(m);
+  carve(m, nullptr);
+  const char* chk = getenv("LMSTEP_CHECK");
+  m->check = chk && atoi(chk) != 0;
+  return m;
+}
+
+// --------------------------------------------------------------- launches
+struct Launcher {
+  lm_model* m;
+  hipStream_t s;
+  int cls = -1;
+  Launcher(lm_model* m_, hipStream_t s_) : m(m_), s(s_) {}
+  // bracket a group of launches of one kernel class with events
+  template <typename F>
+  void run(const char* name, double flops, double bytes, F&& f) {
+    if (!m->prof.on) {
+      f();
+      return;
+    }
+    int c = m->prof.find(name);
+    auto& cl = m->prof.cls[c];
+    cl.launches += 1;
+    cl.flops += flops;
+    cl.bytes += bytes;
+    hipEvent_t a = m->prof.take(), b = m->prof.take();
+    (void)hipEventRecord(a, s);
+    f();
+    (void)hipEventRecord(b, s);
+    m->prof.pending.push_back({c, a, b});
+    if (m->prof.pending.size() > 4096) m->prof.drain();
+  }
+};
+
+int gemm(lm_model* m, const GemmOp& op, hipStream_t s) {
+  return m->bf ? gemm_bf16(op, m->gemm_ws, m->gemm_ws_floats, s) : gemm_f32(op, m->gemm_ws, m->gemm_ws_floats, s);
+}
+
+// Y = X W^T (+ epilogue), X [M, K] activation, W [N, K] weight.
+GemmOp fwd_op(lm_model* m, const void* X, long M, long K, long w_off, long N, void* Y, int epi) {
+  GemmOp op;
+  op.M = (int)M; op.N = (int)N; op.K = (int)K;
+  op.A = X; op.lda = K; op.a_kc = true;
+  op.B = m->W(w_off); op.ldb = K; op.b_kc = true;
+  op.C = Y; op.ldc = N; op.epi = epi;
+  return op;
+}
+// dX = dY W: dY [M, N] activation, W [N, K] -> dX [M, K]
+GemmOp dx_op(lm_model* m, const void* dY, long M, long N, long w_off, long K, void* dX, int epi) {
+  GemmOp op;
+  op.M = (int)M; op.N = (int)K; op.K = (int)N;
+  op.A = dY; op.lda = N; op.a_kc = true;
+  op.B = m->W(w_off); op.ldb = K; op.b_kc = false;
+  op.C = dX; op.ldc = K; op.epi = epi;
+  return op;
+}
+// dW = dY^T X: dY [M, N], X [M, K] -> dW [N, K] fp32 (overwritten)
+GemmOp dw_op(const void* dY, long M, long N, const void* X, long K, float* dW) {
+  GemmOp op;
+  op.M = (int)N; op.N = (int)K; op.K = (int)M;
+  op.A = dY; op.lda = N; op.a_kc = false;
+  op.B = X; op.ldb = K; op.b_kc = false;
+  op.C = dW; op.ldc = K; op.epi = EPI_STORE; op.c_f32 = true;
+  return op;
+}
+
+template <typename E>
+int forward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* doc, int B, int T) {
+  hipStream_t s = Lr.s;
+  const long M = (long)B * T, C = m->C, F = m->F, H = m->H;
+  const double Mf = (double)M, A = (double)sizeof(E);
+  int rc = 0;
+  Lr.run("index_layout", 0, 12.0 * M, [&] { launch_index_layout(doc, B, T, m->start, m->end, m->pos, m->flags, s); });
+  Lr.run("embed_fwd", 0, Mf * C * 12.0, [&] {
+    launch_embed_fwd(tok, m->pos, m->params + m->o_wte, m->params + m->o_wpe, (int)M, (int)C, m->V, m->x, m->flags, s);
+  });
+  AttnArgs at{};
+  at.start = m->start; at.end = m->end; at.B = B; at.T = T; at.H = (int)H; at.D = m->D;
+  for (int l = 0; l < m->L; ++l) {
+    const auto& b = m->blk[l];
+    float* xl = m->x + l * M * C;
+    float* xml = m->xm + l * M * C;
+    E* y1 = m->act<E>(m->y1, l * M * C);
+    E* qkv = m->act<E>(m->qkv, l * M * 3 * C);
+    E* o = m->act<E>(m->o, l * M * C);
+    E* y2 = m->act<E>(m->y2, l * M * C);
+    E* u = m->act<E>(m->u, l * M * F);
+    E* a = m->act<E>(m->a, l * M * F);
+    Lr.run("layernorm_fwd", 0, Mf * C * (4 + A), [&] {
+      launch_ln_fwd<E>(xl, m->P_(b.ln1_g), m->P_(b.ln1_b), (int)M, (int)C, m->cfg.ln_eps, y1, m->mu1 + l * M,
+                       m->r1 + l * M, s);
+    });
+    {
+      GemmOp op = fwd_op(m, y1, M, C, b.w_qkv, 3 * C, qkv, EPI_STORE);
+      op.bias = m->P_(b.b_qkv);
+      Lr.run("gemm_qkv_fwd", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, op, s); });
+    }
+    at.qkv = qkv; at.o = o; at.lse = m->lse + l * M * H;
+    Lr.run("attn_fwd", 0, 0, [&] { rc |= m->bf ? attn_fwd_bf16(at, s) : attn_fwd_f32(at, s); });
+    {
+      GemmOp op = fwd_op(m, o, M, C, b.w_o, C, xml, EPI_RESID);
+      op.bias = m->P_(b.b_o); op.R = xl; op.ldr = C;
+      Lr.run("gemm_attnout_fwd", 2.0 * M * C * C, 0, [&] { rc |= gemm(m, op, s); });
+    }
+    Lr.run("layernorm_fwd", 0, Mf * C * (4 + A), [&] {
+      launch_ln_fwd<E>(xml, m->P_(b.ln2_g), m->P_(b.ln2_b), (int)M, (int)C, m->cfg.ln_eps, y2, m->mu2 + l * M,
+                       m->r2 + l * M, s);
+    });
+    {
+      GemmOp op = fwd_op(m, y2, M, C, b.w_fc, F, u, EPI_GELU);
+      op.bias = m->P_(b.b_fc); op.aux = a; op.ld_aux = F;
+      Lr.run("gemm_fc1_fwd", 2.0 * M * F * C, 0, [&] { rc |= gemm(m, op, s); });
+    }
+    {
+      GemmOp op = fwd_op(m, a, M, F, b.w_proj, C, m->x + (l + 1) * M * C, EPI_RESID);
+      op.bias = m->P_(b.b_proj); op.R = xml; op.ldr = C;
+      Lr.run("gemm_fc2_fwd", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, op, s); });
+    }
+  }
+  E* hf = m->act<E>(m->hf, 0);
+  Lr.run("layernorm_fwd", 0, Mf * C * (4 + A), [&] {
+    launch_ln_fwd<E>(m->x + m->L * M * C, m->P_(m->o_lnf_g), m->P_(m->o_lnf_b), (int)M, (int)C, m->cfg.ln_eps, hf,
+                     m->muf, m->rf, s);
+  });
+  {
+    // tied vocabulary projection z = h_f wte^T (bf16: N = Vp, padded rows of the copy are 0)
+    GemmOp op = fwd_op(m, hf, M, C, m->o_wte, m->bf ? m->Vp : m->V, m->act<E>(m->logits, 0), EPI_STORE);
+    op.ldc = m->ldz;
+    Lr.run("gemm_head_fwd", 2.0 * M * m->V * C, 0, [&] { rc |= gemm(m, op, s); });
+  }
+  return rc;
+}
+
+template <typename E>
+int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* tgt, int B, int T, float* stats) {
+  hipStream_t s = Lr.s;
+  const long M = (long)B * T, C = m->C, F = m->F, H = m->H, V = m->V;
+  const double Mf = (double)M, A = (double)sizeof(E);
+  int rc = 0;
+  E* z = m->act<E>(m->logits, 0);
+  Lr.run("count_valid", 0, 4.0 * M, [&] { launch_count_valid(tgt, (int)M, m->V, m->n_valid, stats, m->flags, s); });
+  Lr.run("xent", 0, Mf * V * 2 * A, [&] { launch_xent<E>(z, m->ldz, (int)M, m->V, tgt, m->n_valid, m->row_loss, s); });
+  Lr.run("loss_reduce", 0, 4.0 * M, [&] { launch_loss_reduce(m->row_loss, (int)M, m->n_valid, stats, s); });
+  E* hf = m->act<E>(m->hf, 0);
+  E* g_act = m->act<E>(m->g_act, 0);
+  // head: dwte = dz^T h_f (first writer of the wte gradient); dh_f = dz wte
+  {
+    GemmOp op = dw_op(z, M, m->bf ? m->Vp : V, hf, C, m->grads + m->o_wte);
+    op.lda = m->ldz;
+    op.M_out = (int)V;
+    Lr.run("gemm_head_bwd_dw", 2.0 * M * V * C, 0, [&] { rc |= gemm(m, op, s); });
+  }
+  {
+    GemmOp op = dx_op(m, z, M, m->bf ? m->Vp : V, m->o_wte, C, m->dy, EPI_STORE);
+    op.lda = m->ldz;
+    op.c_f32 = true;
+    Lr.run("gemm_head_bwd_dx", 2.0 * M * V * C, 0, [&] { rc |= gemm(m, op, s); });
+  }
+  long ln_blocks = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
+  float* pdg = m->ln_part;
+  float* pdb = m->ln_part + ln_blocks * C;
+  auto ln_bwd = [&](const float* x, const float* mu, const float* r, long g_off, long b_off, const float* g_in) {
+    Lr.run("layernorm_bwd", 0, Mf * C * (4 * 4 + A), [&] {
+      launch_ln_bwd<E>(m->dy, x, mu, r, m->P_(g_off), (int)M, (int)C, g_in, m->g, g_act, pdg, pdb, s);
+      launch_colsum_partials(pdg, pdb, (int)ln_blocks, (int)C, m->grads + g_off, m->grads + b_off, s);
+    });
+  };
+  ln_bwd(m->x + m->L * M * C, m->muf, m->rf, m->o_lnf_g, m->o_lnf_b, nullptr);
+  E* dbig = m->act<E>(m->dbig, 0);
+  E* dO = m->act<E>(m->dO, 0);
+  for (int l = m->L - 1; l >= 0; --l) {
+    const auto& b = m->blk[l];
+    float* xl = m->x + l * M * C;
+    float* xml = m->xm + l * M * C;
+    E* y1 = m->act<E>(m->y1, l * M * C);
+    E* qkv = m->act<E>(m->qkv, l * M * 3 * C);
+    E* o = m->act<E>(m->o, l * M * C);
+    E* y2 = m->act<E>(m->y2, l * M * C);
+    E* u = m->act<E>(m->u, l * M * F);
+    E* a = m->act<E>(m->a, l * M * F);
+    // MLP out: x_{l+1} = xm + a W_proj^T + b_proj
+    Lr.run("gemm_fc2_bwd_dw", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, dw_op(g_act, M, C, a, F, m->grads + b.w_proj), s); });
+    Lr.run("bias_grad", 0, Mf * C * 4, [&] { launch_colsum<float>(m->g, C, (int)M, (int)C, m->col_part, m->grads + b.b_proj, s); });
+    {
+      GemmOp op = dx_op(m, g_act, M, C, b.w_proj, F, dbig, EPI_DGELU);
+      op.aux = u; op.ld_aux = F;
+      Lr.run("gemm_fc2_bwd_dx", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, op, s); });
+    }
+    // MLP in: u = y2 W_fc^T + b_fc
+    Lr.run("gemm_fc1_bwd_dw", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, dw_op(dbig, M, F, y2, C, m->grads + b.w_fc), s); });
+    Lr.run("bias_grad", 0, Mf * F * A, [&] { launch_colsum<E>(dbig, F, (int)M, (int)F, m->col_part, m->grads + b.b_fc, s); });
+    {
+      GemmOp op = dx_op(m, dbig, M, F, b.w_fc, C, m->dy, EPI_STORE);
+      op.c_f32 = true;
+      Lr.run("gemm_fc1_bwd_dx", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, op, s); });
+    }
+    ln_bwd(xml, m->mu2 + l * M, m->r2 + l * M, b.ln2_g, b.ln2_b, m->g);
+    // attention out: xm = x + o W_o^T + b_o
+    Lr.run("gemm_attnout_bwd_dw", 2.0 * M * C * C, 0, [&] { rc |= gemm(m, dw_op(g_act, M, C, o, C, m->grads + b.w_o), s); });
+    Lr.run("bias_grad", 0, Mf * C * 4, [&] { launch_colsum<float>(m->g, C, (int)M, (int)C, m->col_part, m->grads + b.b_o, s); });
+    Lr.run("gemm_attnout_bwd_dx", 2.0 * M * C * C, 0, [&] { rc |= gemm(m, dx_op(m, g_act, M, C, b.w_o, C, dO, EPI_STORE), s); });
+    {
+      AttnArgs at{};
+      at.qkv = qkv; at.start = m->start; at.end = m->end; at.B = B; at.T = T; at.H = (int)H; at.D = m->D;
+      at.o = o; at.lse = m->lse + l * M * H; at.dout = dO; at.delta = m->delta; at.dqkv = dbig;
+      Lr.run("attn_bwd", 0, 0, [&] { rc |= m->bf ? attn_bwd_bf16(at, s) : attn_bwd_f32(at, s); });
+    }
+    Lr.run("gemm_qkv_bwd_dw", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, dw_op(dbig, M, 3 * C, y1, C, m->grads + b.w_qkv), s); });
+    Lr.run("bias_grad", 0, Mf * 3 * C * A, [&] { launch_colsum<E>(dbig, 3 * C, (int)M, (int)(3 * C), m->col_part, m->grads + b.b_qkv, s); });
+    {
+      GemmOp op = dx_op(m, dbig, M, 3 * C, b.w_qkv, C, m->dy, EPI_STORE);
+      op.c_f32 = true;
+      Lr.run("gemm_qkv_bwd_dx", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, op, s); });
+    }
+    ln_bwd(xl, m->mu1 + l * M, m->r1 + l * M, b.ln1_g, b.ln1_b, m->g);
+  }
+  // embedding: dwte[tok] += dx0 (on top of the head part), dwpe[pos] = sum dx0
+  Lr.run("embed_bwd", 0, Mf * C * 8, [&] {
+    launch_csr(tok, (int)M, m->V, m->emb_tok, s);
+    launch_segment_sum(m->g, tok, (int)M, (int)C, m->V, m->emb_tok, m->grads + m->o_wte, true, s);
+    launch_csr(m->pos, (int)M, m->S, m->emb_pos, s);
+    launch_segment_sum(m->g, m->pos, (int)M, (int)C, m->S, m->emb_pos, m->grads + m->o_wpe, false, s);
+  });
+  return rc;
+}
+
+lm_status check_batch(lm_model* m, int B, int T) {
+  if (B < 1 || T < 1) return fail(LM_ERR_SHAPE, "B and T must be >= 1");
+  if (B > m->Bmax) return fail(LM_ERR_SHAPE, "B exceeds max_batch");
+  if (T > m->S) return fail(LM_ERR_SHAPE, "T exceeds max_seq");
+  return LM_OK;
+}
+
+lm_status hip_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(LM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return LM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lm_workspace_bytes(const lm_config* cfg) {
+  if (validate(cfg) != LM_OK) return 0;
+  lm_model* m = new_model(cfg);
+  size_t b = m->bytes;
+  delete m;
+  return b;
+}
+
+lm_status model_create(const lm_config* cfg, void* d_arena, size_t arena_bytes, void* stream, lm_model** out) {
+  if (!out) return fail(LM_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  lm_status st = validate(cfg);
+  if (st != LM_OK) return st;
+  if (!d_arena) return fail(LM_ERR_ARG, "arena is NULL");
+  if (reinterpret_cast<uintptr_t>(d_arena) % kAlign) return fail(LM_ERR_WORKSPACE, "arena must be 256-byte aligned");
+  lm_model* m = new_model(cfg);
+  if (arena_bytes < m->bytes) {
+    size_t need = m->bytes;
+    delete m;
+    return fail(LM_ERR_WORKSPACE, "arena too small: need " + std::to_string(need) + " bytes");
+  }
+  carve(m, reinterpret_cast<char*>(d_arena));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // zero parameters, gradients, moments and the bf16 copy (one contiguous run)
+  char* z0 = reinterpret_cast<char*>(m->params);
+  char* z1 = m->shadow ? reinterpret_cast<char*>(m->shadow + m->P + (m->Vp - m->V) * m->C)
+                       : reinterpret_cast<char*>(m->adam_v + m->P);
+  launch_fill_u32(reinterpret_cast<uint32_t*>(z0), 0u, (long)((z1 - z0) / 4), s);
+  launch_fill_u32(m->flags, 0u, 4, s);
+  st = hip_status("model_create");
+  if (st != LM_OK) {
+    delete m;
+    return st;
+  }
+  *out = m;
+  return LM_OK;
+}
+
+void model_destroy(lm_model* m) { delete m; }
+
+lm_status model_param_table(const lm_model* m, lm_tensor_info* out, int32_t* count, int64_t* total) {
+  if (!m || !count) return fail(LM_ERR_ARG, "model or count is NULL");
+  int32_t cap = *count;
+  if (out) {
+    for (int32_t i = 0; i < cap && i < (int32_t)m->table.size(); ++i) {
+      std::memset(out[i].name, 0, sizeof(out[i].name));
+      std::strncpy(out[i].name, m->table[i].name.c_str(), sizeof(out[i].name) - 1);
+      out[i].offset = m->table[i].off;
+      out[i].rows = m->table[i].rows;
+      out[i].cols = m->table[i].cols;
+    }
+  }
+  *count = (int32_t)m->table.size();
+  if (total) *total = m->P;
+  return LM_OK;
+}
+
+static float* buf_of(const lm_model* m, lm_buf which) {
+  switch (which) {
+    case LM_PARAMS: return m->params;
+    case LM_GRADS: return m->grads;
+    case LM_ADAM_M: return m->adam_m;
+    case LM_ADAM_V: return m->adam_v;
+  }
+  return nullptr;
+}
+
+lm_status model_set(lm_model* m, lm_buf which, const float* src, int src_on_device, void* stream) {
+  if (!m || !src) return fail(LM_ERR_ARG, "model or src is NULL");
+  float* dst = buf_of(m, which);
+  if (!dst) return fail(LM_ERR_ARG, "unknown buffer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  size_t bytes = (size_t)m->P * 4;
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return fail(LM_ERR_HIP, std::string("model_set: ") + hipGetErrorString(e));
+  if (which == LM_PARAMS && m->bf) launch_make_shadow(m->params, m->P, m->shadow, (long)m->V * m->C, (m->Vp - m->V) * m->C, s);
+  if (!src_on_device) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(LM_ERR_HIP, std::string("model_set: ") + hipGetErrorString(e));
+  }
+  return hip_status("model_set");
+}
+
+lm_status model_get(const lm_model* m, lm_buf which, float* dst, int dst_on_device, void* stream) {
+  if (!m || !dst) return fail(LM_ERR_ARG, "model or dst is NULL");
+  const float* src = buf_of(m, which);
+  if (!src) return fail(LM_ERR_ARG, "unknown buffer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dst, src, (size_t)m->P * 4, dst_on_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && !dst_on_device) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(LM_ERR_HIP, std::string("model_get: ") + hipGetErrorString(e));
+  return LM_OK;
+}
+
+lm_status train_step(lm_model* m, const int32_t* tok, const int32_t* tgt, const int32_t* doc, int32_t B, int32_t T,
+                     const lm_optim* opt, float* d_stats, void* stream) {
+  if (!m || !tok || !tgt || !opt) return fail(LM_ERR_ARG, "model, tokens, targets or optim is NULL");
+  lm_status st = check_batch(m, B, T);
+  if (st != LM_OK) return st;
+  if (opt->step < 1) return fail(LM_ERR_ARG, "optim.step must be >= 1");
+  if (!(opt->beta1 >= 0.f && opt->beta1 < 1.f && opt->beta2 >= 0.f && opt->beta2 < 1.f))
+    return fail(LM_ERR_ARG, "betas must be in [0, 1)");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* stats = d_stats ? d_stats : m->stats_own;
+  Launcher Lr(m, s);
+  int rc = 0;
+  Lr.run("misc", 0, 0, [&] { launch_fill_u32(m->flags, 0u, 4, s); });
+  if (m->bf) {
+    rc |= forward_pass<bf16>(m, Lr, tok, doc, B, T);
+    rc |= backward_pass<bf16>(m, Lr, tok, tgt, B, T, stats);
+  } else {
+    rc |= forward_pass<float>(m, Lr, tok, doc, B, T);
+    rc |= backward_pass<float>(m, Lr, tok, tgt, B, T, stats);
+  }
+  if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
+  Lr.run("grad_norm", 0, 4.0 * m->P, [&] {
+    launch_sumsq_partials(m->grads, m->P, m->norm_part, s);
+    launch_norm_finalize(m->norm_part, opt->clip_norm, m->norm_scale, m->flags, stats, s);
+  });
+  AdamArgs a{};
+  a.p = m->params; a.g = m->grads; a.m = m->adam_m; a.v = m->adam_v; a.n = m->P;
+  a.lr = opt->lr; a.beta1 = opt->beta1; a.beta2 = opt->beta2; a.eps = opt->eps; a.wd = opt->weight_decay;
+  a.bc1 = (float)(1.0 - std::pow((double)opt->beta1, (double)opt->step));
+  a.bc2 = (float)(1.0 - std::pow((double)opt->beta2, (double)opt->step));
+  a.norm_scale = m->norm_scale; a.flags = m->flags;
+  a.shadow = m->shadow; a.shadow_split = (long)m->V * m->C; a.shadow_shift = (m->Vp - m->V) * m->C;
+  Lr.run("adamw", 0, (m->bf ? 34.0 : 32.0) * m->P, [&] { launch_adamw(a, s); });
+  Lr.run("misc", 0, 0, [&] { launch_write_flags(m->flags, stats, s); });
+  return hip_status("train_step");
+}
+
+lm_status forward_logits(lm_model* m, const int32_t* tok, const int32_t* doc, int32_t B, int32_t T, float* d_logits,
+                         void* stream) {
+  if (!m || !tok || !d_logits) return fail(LM_ERR_ARG, "model, tokens or logits is NULL");
+  lm_status st = check_batch(m, B, T);
+  if (st != LM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Launcher Lr(m, s);
+  int rc;
+  launch_fill_u32(m->flags, 0u, 4, s);
+  if (m->bf) {
+    rc = forward_pass<bf16>(m, Lr, tok, doc, B, T);
+    launch_logits_out<bf16>(m->act<bf16>(m->logits, 0), m->ldz, B * T, m->V, d_logits, s);
+  } else {
+    rc = forward_pass<float>(m, Lr, tok, doc, B, T);
+    launch_logits_out<float>(m->act<float>(m->logits, 0), m->ldz, B * T, m->V, d_logits, s);
+  }
+  if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
+  return hip_status("forward_logits");
+}
+
+const char* lm_last_error(void) { return g_err.c_str(); }
+
+lm_status model_profile_enable(lm_model* m, int enable) {
+  if (!m) return fail(LM_ERR_ARG, "model is NULL");
+  m->prof.drain();
+  m->prof.on = enable != 0;
+  return LM_OK;
+}
+
+lm_status model_profile_read(lm_model* m, lm_profile_entry* out, int32_t cap, int32_t* n, int reset) {
+  if (!m || !n) return fail(LM_ERR_ARG, "model or n is NULL");
+  m->prof.drain();
+  int32_t k = 0;
+  for (auto& c : m->prof.cls) {
+    if (out && k < cap) {
+      std::memset(out[k].name, 0, sizeof(out[k].name));
+      std::strncpy(out[k].name, c.name.c_str(), sizeof(out[k].name) - 1);
+      out[k].launches = c.launches;
+      out[k].ms = c.ms;
+      out[k].flops = c.flops;
+      out[k].bytes = c.bytes;
+    }
+    ++k;
+  }
+  *n = k;
+  if (reset)
+    for (auto& c : m->prof.cls) c.launches = 0, c.ms = 0, c.flops = 0, c.bytes = 0;
+  return LM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Device helpers shared by the gfx950 kernels of the training step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lm {
+
+typedef uint16_t bf16;  // storage of a bfloat16 value (upper half of an fp32)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// fp32 -> bf16 with round-to-nearest-even (hardware v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16 f2bf(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(bf16, b);
+}
+
+// Activation storage type helpers: float (fp32 path) or bf16 (bf16 path).
+template <typename T> struct Act;
+template <> struct Act<float> {
+  static __device__ __forceinline__ float ld(const float* p, long i) { return p[i]; }
+  static __device__ __forceinline__ void st(float* p, long i, float v) { p[i] = v; }
+};
+template <> struct Act<bf16> {
+  static __device__ __forceinline__ float ld(const bf16* p, long i) { return bf2f(p[i]); }
+  static __device__ __forceinline__ void st(bf16* p, long i, float v) { p[i] = f2bf(v); }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// tanh(y) = 1 - 2 / (exp(2y) + 1): saturates to +-1 without overflow trouble.
+__device__ __forceinline__ float tanh_exp(float y) { return 1.0f - 2.0f / (__expf(2.0f * y) + 1.0f); }
+
+// GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
+__device__ __forceinline__ float gelu_f(float u) {
+  const float c = 0.7978845608028654f, a = 0.044715f;
+  return 0.5f * u * (1.0f + tanh_exp(c * (u + a * u * u * u)));
+}
+// Its derivative: 0.5 (1 + t) + 0.5 u (1 - t^2) c (1 + 3 a u^2).
+__device__ __forceinline__ float gelu_grad_f(float u) {
+  const float c = 0.7978845608028654f, a = 0.044715f;
+  float t = tanh_exp(c * (u + a * u * u * u));
+  return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * c * (1.0f + 3.0f * a * u * u);
+}
+
+}  // namespace lm

@@ -1,0 +1,214 @@
+// LayerNorm forward and backward, one wavefront per row.
+//
+// Forward: mu = mean(x), var = mean((x - mu)^2) (biased), rstd =
+// (var + eps)^-1/2, y = g (x - mu) rstd + b. Backward (chain rule): with
+// xhat = (x - mu) rstd and dxhat = dy g,
+//   dx = rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)),
+// accumulated onto the incoming residual gradient, and per-block partial
+// column sums of dy xhat (dg) and dy (db), reduced afterwards in a fixed order
+// so the result is bit-reproducible.
+// (LayerNorm layer: RustGPT page, file list; final LayerNorm before the
+// vocabulary projection: Feste page, "Model Architecture".)
+#include "kernels.h"
+
+namespace lm {
+
+// NV float2 per lane: C = 128 * NV.
+template <int NV, typename T>
+__global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                     const float* __restrict__ b, int M, float eps,
+                                                     T* __restrict__ y, float* __restrict__ mu_out,
+                                                     float* __restrict__ rstd_out) {
+  constexpr int C = 128 * NV;
+  const int lane = threadIdx.x & 63;
+  const long m = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const float2* xr = reinterpret_cast<const float2*>(x + m * C);
+  float2 v[NV];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    v[j] = xr[lane + 64 * j];
+    s += v[j].x + v[j].y;
+  }
+  const float mu = wave_sum(s) * (1.0f / C);
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    float a = v[j].x - mu, c = v[j].y - mu;
+    q += a * a + c * c;
+  }
+  const float var = wave_sum(q) * (1.0f / C);
+  const float r = 1.0f / sqrtf(var + eps);
+  const float2* g2 = reinterpret_cast<const float2*>(g);
+  const float2* b2 = reinterpret_cast<const float2*>(b);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    int c = 2 * (lane + 64 * j);
+    float2 gg = g2[lane + 64 * j], bb = b2[lane + 64 * j];
+    Act<T>::st(y, m * C + c, (v[j].x - mu) * r * gg.x + bb.x);
+    Act<T>::st(y, m * C + c + 1, (v[j].y - mu) * r * gg.y + bb.y);
+  }
+  if (lane == 0) {
+    mu_out[m] = mu;
+    rstd_out[m] = r;
+  }
+}
+
+template <typename T>
+void launch_ln_fwd(const float* x, const float* g, const float* b, int M, int C, float eps, T* y, float* mu,
+                   float* rstd, hipStream_t s) {
+  dim3 grid((M + 3) / 4), block(256);
+  switch (C / 128) {
+#define LN_CASE(NV) \
+  case NV: hipLaunchKernelGGL((ln_fwd_kernel<NV, T>), grid, block, 0, s, x, g, b, M, eps, y, mu, rstd); break;
+    LN_CASE(1) LN_CASE(2) LN_CASE(3) LN_CASE(4) LN_CASE(5) LN_CASE(6) LN_CASE(7) LN_CASE(8)
+#undef LN_CASE
+    default: break;
+  }
+}
+template void launch_ln_fwd<float>(const float*, const float*, const float*, int, int, float, float*, float*,
+                                   float*, hipStream_t);
+template void launch_ln_fwd<bf16>(const float*, const float*, const float*, int, int, float, bf16*, float*,
+                                  float*, hipStream_t);
+
+// Backward. Each block owns kLnRowsPerBlock consecutive rows; wave w takes
+// rows w, w+4, ... of them. g_out = g_in + dx (g_in may alias g_out or be
+// null); g_act (nullable) receives g_out in the activation type.
+template <int NV, typename T>
+__global__ void __launch_bounds__(256) ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+                                                     const float* __restrict__ mu_in,
+                                                     const float* __restrict__ rstd_in,
+                                                     const float* __restrict__ g, int M,
+                                                     const float* g_in, float* g_out, T* __restrict__ g_act,
+                                                     float* __restrict__ part_dg, float* __restrict__ part_db) {
+  constexpr int C = 128 * NV;
+  __shared__ float s_dg[4][C];
+  __shared__ float s_db[4][C];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float2 gg[NV], adg[NV], adb[NV];
+  const float2* g2 = reinterpret_cast<const float2*>(g);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    gg[j] = g2[lane + 64 * j];
+    adg[j] = make_float2(0.f, 0.f);
+    adb[j] = make_float2(0.f, 0.f);
+  }
+  const long r0 = (long)blockIdx.x * kLnRowsPerBlock;
+  const long r1 = min((long)M, r0 + kLnRowsPerBlock);
+  for (long m = r0 + w; m < r1; m += 4) {
+    const float2* dyr = reinterpret_cast<const float2*>(dy + m * C);
+    const float2* xr = reinterpret_cast<const float2*>(x + m * C);
+    const float mu = mu_in[m], r = rstd_in[m];
+    float2 xh[NV], dxh[NV];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float2 d = dyr[lane + 64 * j], xv = xr[lane + 64 * j];
+      xh[j] = make_float2((xv.x - mu) * r, (xv.y - mu) * r);
+      dxh[j] = make_float2(d.x * gg[j].x, d.y * gg[j].y);
+      s1 += dxh[j].x + dxh[j].y;
+      s2 += dxh[j].x * xh[j].x + dxh[j].y * xh[j].y;
+      adg[j].x += d.x * xh[j].x;
+      adg[j].y += d.y * xh[j].y;
+      adb[j].x += d.x;
+      adb[j].y += d.y;
+    }
+    const float m1 = wave_sum(s1) * (1.0f / C), m2 = wave_sum(s2) * (1.0f / C);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      int c = 2 * (lane + 64 * j);
+      float dx0 = r * (dxh[j].x - m1 - xh[j].x * m2);
+      float dx1 = r * (dxh[j].y - m1 - xh[j].y * m2);
+      if (g_in) {
+        float2 gi = reinterpret_cast<const float2*>(g_in + m * C)[lane + 64 * j];
+        dx0 += gi.x;
+        dx1 += gi.y;
+      }
+      reinterpret_cast<float2*>(g_out + m * C)[lane + 64 * j] = make_float2(dx0, dx1);
+      if (g_act) {
+        Act<T>::st(g_act, m * C + c, dx0);
+        Act<T>::st(g_act, m * C + c + 1, dx1);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    int c = 2 * (lane + 64 * j);
+    s_dg[w][c] = adg[j].x;
+    s_dg[w][c + 1] = adg[j].y;
+    s_db[w][c] = adb[j].x;
+    s_db[w][c + 1] = adb[j].y;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += 256) {
+    part_dg[(long)blockIdx.x * C + c] = ((s_dg[0][c] + s_dg[1][c]) + s_dg[2][c]) + s_dg[3][c];
+    part_db[(long)blockIdx.x * C + c] = ((s_db[0][c] + s_db[1][c]) + s_db[2][c]) + s_db[3][c];
+  }
+}
+
+template <typename T>
+void launch_ln_bwd(const float* dy, const float* x, const float* mu, const float* rstd, const float* g, int M,
+                   int C, const float* g_in, float* g_out, T* g_act, float* part_dg, float* part_db,
+                   hipStream_t s) {
+  dim3 grid((M + kLnRowsPerBlock - 1) / kLnRowsPerBlock), block(256);
+  switch (C / 128) {
+#define LN_CASE(NV)                                                                                    \
+  case NV:                                                                                             \
+    hipLaunchKernelGGL((ln_bwd_kernel<NV, T>), grid, block, 0, s, dy, x, mu, rstd, g, M, g_in, g_out, g_act, \
+                       part_dg, part_db);                                                              \
+    break;
+    LN_CASE(1) LN_CASE(2) LN_CASE(3) LN_CASE(4) LN_CASE(5) LN_CASE(6) LN_CASE(7) LN_CASE(8)
+#undef LN_CASE
+    default: break;
+  }
+}
+template void launch_ln_bwd<float>(const float*, const float*, const float*, const float*, const float*, int, int,
+                                   const float*, float*, float*, float*, float*, hipStream_t);
+template void launch_ln_bwd<bf16>(const float*, const float*, const float*, const float*, const float*, int, int,
+                                  const float*, float*, bf16*, float*, float*, hipStream_t);
+
+// out[c] = sum over p < P of part[p][c], in increasing p (fixed order).
+// Two vectors at once (the dg and db partials of one LayerNorm).
+__global__ void colsum_partials_kernel(const float* __restrict__ pa, const float* __restrict__ pb, int P, int C,
+                                       float* __restrict__ oa, float* __restrict__ ob) {
+  int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float a = 0.f, b = 0.f;
+  for (int p = 0; p < P; ++p) {
+    a += pa[(long)p * C + c];
+    if (pb) b += pb[(long)p * C + c];
+  }
+  oa[c] = a;
+  if (ob) ob[c] = b;
+}
+
+void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + 255) / 256), dim3(256), 0, s, pa, pb, P, C, oa, ob);
+}
+
+// Column sums of an [M, N] matrix (bias gradients): stage 1 writes per-block
+// partials over kColRows rows, stage 2 (colsum_partials) sums them in order.
+template <typename T>
+__global__ void __launch_bounds__(256) colsum_stage1_kernel(const T* __restrict__ a, long lda, int M, int N,
+                                                            float* __restrict__ part) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= N) return;
+  const long r0 = (long)blockIdx.y * kColRows;
+  const long r1 = min((long)M, r0 + kColRows);
+  float acc = 0.f;
+  for (long r = r0; r < r1; ++r) acc += Act<T>::ld(a, r * lda + c);
+  part[(long)blockIdx.y * N + c] = acc;
+}
+
+template <typename T>
+void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s) {
+  int P = (M + kColRows - 1) / kColRows;
+  hipLaunchKernelGGL(colsum_stage1_kernel<T>, dim3((N + 255) / 256, P), dim3(256), 0, s, a, lda, M, N, part);
+  launch_colsum_partials(part, nullptr, P, N, out, nullptr, s);
+}
+template void launch_colsum<float>(const float*, long, int, int, float*, float*, hipStream_t);
+template void launch_colsum<bf16>(const bf16*, long, int, int, float*, float*, hipStream_t);
+
+}  // namespace lm

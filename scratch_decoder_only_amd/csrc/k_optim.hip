@@ -1,0 +1,125 @@
+// Global gradient-norm clip and AdamW (Feste page, "Manual Backpropagation":
+// AdamW with weight decay kept out of the gradient, and clipping against
+// exploding gradients; RustGPT page: clip to an L2 norm of 5.0).
+//
+// n = ||g||_2 over the whole flat gradient buffer (fixed-order two-stage
+// reduction in double), s = clip / n if n > clip else 1. Then per element,
+// with gh = s g and a 1-based step t:
+//   m = b1 m + (1 - b1) gh;  v = b2 v + (1 - b2) gh^2
+//   p = p - lr (m / (1 - b1^t) / (sqrt(v / (1 - b2^t)) + eps) + wd p)
+// and the bf16 operand copy of p is refreshed in the same pass. A non-finite
+// norm skips the update entirely (flags bit 0).
+#include "kernels.h"
+
+namespace lm {
+
+__global__ void __launch_bounds__(256) sumsq_kernel(const float* __restrict__ g, long n, double* __restrict__ part) {
+  __shared__ double s[256];
+  double acc = 0.0;
+  const long n4 = n / 4;
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    float4 v = g4[i];
+    acc += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+  }
+  for (long i = n4 * 4 + (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
+    acc += (double)g[i] * g[i];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = s[0];
+}
+
+void launch_sumsq_partials(const float* g, long n, double* part, hipStream_t s) {
+  hipLaunchKernelGGL(sumsq_kernel, dim3(kNormBlocks), dim3(256), 0, s, g, n, part);
+}
+
+__global__ void __launch_bounds__(256) norm_finalize_kernel(const double* __restrict__ part, float clip,
+                                                            float* __restrict__ norm_scale,
+                                                            uint32_t* __restrict__ flags, float* __restrict__ stats) {
+  __shared__ double s[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < kNormBlocks; i += 256) acc += part[i];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double n = sqrt(s[0]);
+    bool finite = isfinite(n);
+    double sc = (finite && clip > 0.f && n > (double)clip) ? (double)clip / n : 1.0;
+    norm_scale[0] = (float)n;
+    norm_scale[1] = (float)sc;
+    if (!finite) atomicOr(flags, 1u);
+    if (stats) stats[1] = (float)n;
+  }
+}
+
+void launch_norm_finalize(const double* part, float clip, float* norm_scale, uint32_t* flags, float* stats,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(256), 0, s, part, clip, norm_scale, flags, stats);
+}
+
+__device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, const AdamArgs& a, float sc) {
+  const float gh = sc * g;
+  m = a.beta1 * m + (1.0f - a.beta1) * gh;
+  v = a.beta2 * v + (1.0f - a.beta2) * gh * gh;
+  const float mh = m / a.bc1, vh = v / a.bc2;
+  p = p - a.lr * (mh / (sqrtf(vh) + a.eps) + a.wd * p);
+}
+
+__global__ void __launch_bounds__(256) adamw_kernel(AdamArgs a) {
+  if (*a.flags & 1u) return;  // non-finite gradient norm: leave everything as it was
+  const float sc = a.norm_scale[1];
+  const long n4 = a.n / 4;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    float4 p = reinterpret_cast<float4*>(a.p)[i];
+    float4 g = reinterpret_cast<const float4*>(a.g)[i];
+    float4 m = reinterpret_cast<float4*>(a.m)[i];
+    float4 v = reinterpret_cast<float4*>(a.v)[i];
+    adam_one(p.x, g.x, m.x, v.x, a, sc);
+    adam_one(p.y, g.y, m.y, v.y, a, sc);
+    adam_one(p.z, g.z, m.z, v.z, a, sc);
+    adam_one(p.w, g.w, m.w, v.w, a, sc);
+    reinterpret_cast<float4*>(a.p)[i] = p;
+    reinterpret_cast<float4*>(a.m)[i] = m;
+    reinterpret_cast<float4*>(a.v)[i] = v;
+    if (a.shadow) {
+      long e = i * 4;
+      long o = e < a.shadow_split ? e : e + a.shadow_shift;
+      uint2 w;
+      w.x = (uint32_t)f2bf(p.x) | ((uint32_t)f2bf(p.y) << 16);
+      w.y = (uint32_t)f2bf(p.z) | ((uint32_t)f2bf(p.w) << 16);
+      *reinterpret_cast<uint2*>(a.shadow + o) = w;
+    }
+  }
+}
+
+void launch_adamw(const AdamArgs& a, hipStream_t s) {
+  long n4 = a.n / 4;
+  long blocks = (n4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+}
+
+__global__ void make_shadow_kernel(const float* __restrict__ p, long n, bf16* __restrict__ shadow, long split,
+                                   long shift) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    long o = i < split ? i : i + shift;
+    shadow[o] = f2bf(p[i]);
+  }
+}
+
+void launch_make_shadow(const float* p, long n, bf16* shadow, long split, long shift, hipStream_t s) {
+  long blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(make_shadow_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, shadow, split, shift);
+}
+
+}  // namespace lm

@@ -1,0 +1,150 @@
+// Per-kernel C entry points (the kernels of the step, one at a time).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "../../include/lmstep_kernels.h"
+#include "kernels.h"
+
+using namespace lm;
+
+static hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+extern "C" {
+
+int lmk_gemm(int precision, int M, int N, int K, const void* A, int64_t lda, int a_kc, const void* B, int64_t ldb,
+             int b_kc, void* C, int64_t ldc, int epi, int c_f32, const float* bias, const float* R, int64_t ldr,
+             void* aux, int64_t ld_aux, int force_split, int M_out, float* ws, int64_t ws_floats, void* stream) {
+  if (!A || !B || !C || M < 0 || N < 0 || K < 0 || epi < 0 || epi > 3) return -1;
+  GemmOp op;
+  op.M = M; op.N = N; op.K = K;
+  op.A = A; op.lda = lda; op.a_kc = a_kc != 0;
+  op.B = B; op.ldb = ldb; op.b_kc = b_kc != 0;
+  op.C = C; op.ldc = ldc; op.epi = epi; op.c_f32 = c_f32 != 0;
+  op.bias = bias; op.R = R; op.ldr = ldr; op.aux = aux; op.ld_aux = ld_aux;
+  op.force_split = force_split; op.M_out = M_out;
+  if (epi == EPI_RESID && !R) return -1;
+  if ((epi == EPI_GELU || epi == EPI_DGELU) && !aux) return -1;
+  return precision ? gemm_bf16(op, ws, ws_floats, S(stream)) : gemm_f32(op, ws, ws_floats, S(stream));
+}
+
+static bool ln_shape_ok(int M, int C) { return M >= 0 && C >= 128 && C <= 1024 && C % 128 == 0; }
+
+int lmk_layernorm_fwd(int precision, const float* x, const float* g, const float* b, int M, int C, float eps, void* y,
+                      float* mu, float* rstd, void* stream) {
+  if (!ln_shape_ok(M, C)) return -1;
+  if (precision) launch_ln_fwd<bf16>(x, g, b, M, C, eps, reinterpret_cast<bf16*>(y), mu, rstd, S(stream));
+  else launch_ln_fwd<float>(x, g, b, M, C, eps, reinterpret_cast<float*>(y), mu, rstd, S(stream));
+  return 0;
+}
+
+int64_t lmk_layernorm_bwd_ws_floats(int M, int C) {
+  return 2L * ((M + kLnRowsPerBlock - 1) / kLnRowsPerBlock) * C;
+}
+
+int lmk_layernorm_bwd(int precision, const float* dy, const float* x, const float* mu, const float* rstd,
+                      const float* g, int M, int C, const float* g_in, float* g_out, void* g_act, float* dgamma,
+                      float* dbeta, float* ws, void* stream) {
+  if (!ln_shape_ok(M, C) || M == 0) return -1;
+  long nb = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
+  if (precision)
+    launch_ln_bwd<bf16>(dy, x, mu, rstd, g, M, C, g_in, g_out, reinterpret_cast<bf16*>(g_act), ws, ws + nb * C, S(stream));
+  else
+    launch_ln_bwd<float>(dy, x, mu, rstd, g, M, C, g_in, g_out, reinterpret_cast<float*>(g_act), ws, ws + nb * C,
+                         S(stream));
+  launch_colsum_partials(ws, ws + nb * C, (int)nb, C, dgamma, dbeta, S(stream));
+  return 0;
+}
+
+int64_t lmk_colsum_ws_floats(int M, int N) { return (int64_t)((M + kColRows - 1) / kColRows) * N; }
+
+int lmk_colsum(int precision_of_a, const void* a, int64_t lda, int M, int N, float* out, float* ws, void* stream) {
+  if (M <= 0 || N <= 0) return -1;
+  if (precision_of_a) launch_colsum<bf16>(reinterpret_cast<const bf16*>(a), lda, M, N, ws, out, S(stream));
+  else launch_colsum<float>(reinterpret_cast<const float*>(a), lda, M, N, ws, out, S(stream));
+  return 0;
+}
+
+int lmk_index_layout(const int32_t* doc, int B, int T, int32_t* start, int32_t* end, int32_t* pos, uint32_t* flags,
+                     void* stream) {
+  if (B <= 0 || T <= 0) return -1;
+  launch_index_layout(doc, B, T, start, end, pos, flags, S(stream));
+  return 0;
+}
+
+int lmk_embed_fwd(const int32_t* tok, const int32_t* pos, const float* wte, const float* wpe, int M, int C, int V,
+                  float* x, uint32_t* flags, void* stream) {
+  if (M <= 0 || C % 2) return -1;
+  launch_embed_fwd(tok, pos, wte, wpe, M, C, V, x, flags, S(stream));
+  return 0;
+}
+
+int lmk_attn_fwd(int precision, const void* qkv, const int32_t* start, const int32_t* end, int B, int T, int H, int D,
+                 void* o, float* lse, void* stream) {
+  if (B <= 0 || T <= 0 || H <= 0 || (D != 32 && D != 64)) return -1;
+  AttnArgs a{};
+  a.qkv = qkv; a.start = start; a.end = end; a.B = B; a.T = T; a.H = H; a.D = D; a.o = o; a.lse = lse;
+  return precision ? attn_fwd_bf16(a, S(stream)) : attn_fwd_f32(a, S(stream));
+}
+
+int lmk_attn_bwd(int precision, const void* qkv, const void* o, const float* lse, const void* dout,
+                 const int32_t* start, const int32_t* end, int B, int T, int H, int D, float* delta, void* dqkv,
+                 void* stream) {
+  if (B <= 0 || T <= 0 || H <= 0 || (D != 32 && D != 64)) return -1;
+  AttnArgs a{};
+  a.qkv = qkv; a.start = start; a.end = end; a.B = B; a.T = T; a.H = H; a.D = D;
+  a.o = const_cast<void*>(o); a.lse = const_cast<float*>(lse); a.dout = dout; a.delta = delta; a.dqkv = dqkv;
+  return precision ? attn_bwd_bf16(a, S(stream)) : attn_bwd_f32(a, S(stream));
+}
+
+int lmk_xent(int precision, void* z, int64_t ldz, int M, int V, const int32_t* tgt, float* loss, int32_t* ws_n,
+             float* ws_rows, uint32_t* flags, void* stream) {
+  if (M <= 0 || V <= 0 || ldz < V || ldz % 8) return -1;
+  launch_count_valid(tgt, M, V, ws_n, loss, flags, S(stream));
+  if (precision) launch_xent<bf16>(reinterpret_cast<bf16*>(z), ldz, M, V, tgt, ws_n, ws_rows, S(stream));
+  else launch_xent<float>(reinterpret_cast<float*>(z), ldz, M, V, tgt, ws_n, ws_rows, S(stream));
+  launch_loss_reduce(ws_rows, M, ws_n, loss, S(stream));
+  return 0;
+}
+
+int lmk_csr(const int32_t* keys, int M, int nkeys, int32_t* counts, int32_t* offsets, int32_t* chunk_base,
+            int32_t* perm, void* stream) {
+  if (M < 0 || nkeys <= 0) return -1;
+  EmbedBwdWs w{counts, offsets, chunk_base, perm, nullptr};
+  launch_csr(keys, M, nkeys, w, S(stream));
+  return 0;
+}
+
+int64_t lmk_segment_sum_ws_floats(int M, int nkeys, int C) { return embed_bwd_max_chunks(M, nkeys) * C; }
+
+int lmk_segment_sum(const float* dx, int M, int C, int nkeys, int32_t* counts, int32_t* offsets, int32_t* chunk_base,
+                    int32_t* perm, float* partial, float* dst, int accumulate, void* stream) {
+  if (M < 0 || nkeys <= 0 || C <= 0) return -1;
+  EmbedBwdWs w{counts, offsets, chunk_base, perm, partial};
+  launch_segment_sum(dx, nullptr, M, C, nkeys, w, dst, accumulate != 0, S(stream));
+  return 0;
+}
+
+int lmk_grad_norm(const float* g, int64_t n, float clip, double* part, float* norm_scale, uint32_t* flags,
+                  void* stream) {
+  if (n < 0) return -1;
+  launch_sumsq_partials(g, n, part, S(stream));
+  launch_norm_finalize(part, clip, norm_scale, flags, nullptr, S(stream));
+  return 0;
+}
+
+int lmk_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float beta1, float beta2, float eps,
+              float weight_decay, int step, const float* norm_scale, const uint32_t* flags, uint16_t* shadow,
+              void* stream) {
+  if (n < 0 || n % 4 || step < 1) return -1;
+  AdamArgs a{};
+  a.p = p; a.g = g; a.m = m; a.v = v; a.n = n;
+  a.lr = lr; a.beta1 = beta1; a.beta2 = beta2; a.eps = eps; a.wd = weight_decay;
+  a.bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
+  a.bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
+  a.norm_scale = norm_scale; a.flags = flags; a.shadow = shadow; a.shadow_split = n; a.shadow_shift = 0;
+  launch_adamw(a, S(stream));
+  return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Internal launch interface of the gfx950 kernels (host side).
+#pragma once
+
+#include "common.h"
+
+namespace lm {
+
+constexpr int kLnRowsPerBlock = 64;  // rows per block in the LayerNorm backward
+constexpr int kColRows = 256;        // rows per partial in the bias-gradient column sums
+
+// ------------------------------------------------------------------- GEMM
+// C[i, j] = sum_k A(i, k) B(j, k) for i < M, j < N, k < K, then an epilogue.
+// A(i, k) = A[i * lda + k] when a_kc (K-contiguous) else A[k * lda + i];
+// B(j, k) = B[j * ldb + k] when b_kc else B[k * ldb + j].
+//   forward  Y = X W^T : a_kc, b_kc
+//   dX = dY W          : a_kc, !b_kc
+//   dW = dY^T X        : !a_kc, !b_kc
+enum GemmEpi : int {
+  EPI_STORE = 0,    // C = acc (+ bias[j]); C fp32 or activation type
+  EPI_RESID = 1,    // C fp32 = R[i, j] + acc (+ bias[j])
+  EPI_GELU = 2,     // u = acc + bias[j]: C (act) = u, aux (act) = GELU(u)
+  EPI_DGELU = 3,    // C (act) = acc * GELU'(aux[i, j])
+  EPI_PARTIAL = 4,  // C fp32 [split][M][ldc] = acc (split-K partial sums)
+};
+
+struct GemmOp {
+  int M = 0, N = 0, K = 0;
+  const void* A = nullptr;
+  long lda = 0;
+  bool a_kc = true;
+  const void* B = nullptr;
+  long ldb = 0;
+  bool b_kc = true;
+  void* C = nullptr;
+  long ldc = 0;
+  int epi = EPI_STORE;
+  bool c_f32 = false;  // EPI_STORE output type
+  const float* bias = nullptr;
+  const float* R = nullptr;
+  long ldr = 0;
+  void* aux = nullptr;
+  long ld_aux = 0;
+  int force_split = 0;  // > 0: use exactly this many K splits (tests)
+  int M_out = 0;        // > 0: store only rows < M_out (rows M_out..M-1 are padding)
+};
+
+// Returns 0 or a negative code if the shape breaks the kernel's alignment
+// rules (leading dims and K-contiguous K multiples of 8, M/N multiples of 8
+// for the non-K-contiguous operands).
+int gemm_bf16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
+int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
+// Split count the bf16 dispatcher would pick (for workspace sizing).
+int gemm_bf16_splits(const GemmOp& op);
+
+// -------------------------------------------------------------- rows etc.
+void launch_fill_u32(uint32_t* p, uint32_t v, long n, hipStream_t s);
+void launch_index_layout(const int32_t* doc, int B, int T, int32_t* start, int32_t* end, int32_t* pos,
+                         uint32_t* flags, hipStream_t s);
+void launch_embed_fwd(const int32_t* tok, const int32_t* pos, const float* wte, const float* wpe, int M, int C,
+                      int V, float* x, uint32_t* flags, hipStream_t s);
+void launch_count_valid(const int32_t* tgt, int M, int V, int32_t* n_out, float* stats, uint32_t* flags,
+                        hipStream_t s);
+void launch_loss_reduce(const float* row_loss, int M, const int32_t* n_valid, float* out, hipStream_t s);
+void launch_write_flags(const uint32_t* flags, float* stats, hipStream_t s);
+void launch_f32_to_bf16(const float* src, bf16* dst, long n, hipStream_t s);
+template <typename T>
+void launch_logits_out(const T* z, long ldz, int M, int V, float* out, hipStream_t s);
+
+template <typename T>
+void launch_ln_fwd(const float* x, const float* g, const float* b, int M, int C, float eps, T* y, float* mu,
+                   float* rstd, hipStream_t s);
+template <typename T>
+void launch_ln_bwd(const float* dy, const float* x, const float* mu, const float* rstd, const float* g, int M,
+                   int C, const float* g_in, float* g_out, T* g_act, float* part_dg, float* part_db,
+                   hipStream_t s);
+void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob, hipStream_t s);
+template <typename T>
+void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s);
+
+template <typename T>
+void launch_xent(T* z, long ldz, int M, int V, const int32_t* tgt, const int32_t* n_valid, float* row_loss,
+                 hipStream_t s);
+
+// -------------------------------------------------------------- attention
+// qkv [B*T, 3C] (q | k | v, head h in columns h*D..h*D+D-1 of each third),
+// o [B*T, C], lse [B, H, T] (natural log), start/end [B, T].
+struct AttnArgs {
+  const void* qkv;
+  const int32_t* start;
+  const int32_t* end;
+  int B, T, H, D;
+  void* o;
+  float* lse;
+  // backward
+  const void* dout;  // [B*T, C]
+  float* delta;      // [B, H, T] rowsum(dO * O)
+  void* dqkv;        // [B*T, 3C]
+};
+int attn_fwd_bf16(const AttnArgs& a, hipStream_t s);
+int attn_bwd_bf16(const AttnArgs& a, hipStream_t s);
+int attn_fwd_f32(const AttnArgs& a, hipStream_t s);
+int attn_bwd_f32(const AttnArgs& a, hipStream_t s);
+
+// ------------------------------------------------------ embedding backward
+// Deterministic scatter-add: a stable counting sort of the keys (token ids,
+// then positions) gives each key's rows in ascending index order; rows are
+// summed in that order, in chunks of kSegRows, and the chunks of one key are
+// added in order.
+constexpr int kSegRows = 64;
+struct EmbedBwdWs {
+  int32_t* counts;     // [nkeys + 1]
+  int32_t* offsets;    // [nkeys + 1]
+  int32_t* chunk_base; // [nkeys + 1]
+  int32_t* perm;       // [M]
+  float* partial;      // [max_chunks, C]
+};
+void launch_csr(const int32_t* keys, int M, int nkeys, EmbedBwdWs ws, hipStream_t s);
+// dst[key] (+)= sum of dx rows of that key. accumulate: add onto dst (rows of
+// keys with no occurrence are left untouched) else overwrite (zero rows for
+// absent keys).
+void launch_segment_sum(const float* dx, const int32_t* keys, int M, int C, int nkeys, EmbedBwdWs ws, float* dst,
+                        bool accumulate, hipStream_t s);
+long embed_bwd_max_chunks(int M, int nkeys);
+
+// --------------------------------------------------------------- optimiser
+constexpr int kNormBlocks = 1024;
+void launch_sumsq_partials(const float* g, long n, double* part, hipStream_t s);
+// Final norm: stats[1] = n; scale = clip/n if n > clip > 0 else 1; sets flags
+// bit 0 if n is not finite.
+void launch_norm_finalize(const double* part, float clip, float* norm_scale, uint32_t* flags, float* stats,
+                          hipStream_t s);
+struct AdamArgs {
+  float* p;
+  const float* g;
+  float* m;
+  float* v;
+  long n;
+  float lr, beta1, beta2, eps, wd;
+  float bc1, bc2;  // 1 - beta1^t, 1 - beta2^t
+  const float* norm_scale;  // [norm, scale]
+  const uint32_t* flags;
+  bf16* shadow;      // bf16 copy (nullable)
+  long shadow_split; // elements < split map to shadow[i]; others to shadow[i + shadow_shift]
+  long shadow_shift;
+};
+void launch_adamw(const AdamArgs& a, hipStream_t s);
+void launch_make_shadow(const float* p, long n, bf16* shadow, long split, long shift, hipStream_t s);
+
+}  // namespace lm

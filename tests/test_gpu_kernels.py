@@ -1,0 +1,387 @@
+"""Per-kernel parity of the HIP kernels against the CPU oracle, through the
+per-kernel C ABI (include/lmstep_kernels.h).
+
+Inputs are seeded; bf16 operands are rounded to bf16 first so the oracle
+works on exactly the values the kernels read. Tolerances: integer and index
+outputs bit-exact; fp32 outputs of fp32-accumulated contractions rel 2e-5;
+outputs stored in bf16 rel 6e-3 (one bf16 rounding, 2^-9 relative, per
+element).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import act, bf16_exact, cos, dev, host, rel, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sd():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    import scratch_decoder_only_amd as m
+    return m
+
+
+def tol(prec, out_f32):
+    return 2e-5 if (prec == 0 or out_f32) else 6e-3
+
+
+def _operands(rng, prec, *shapes, scale=1.0):
+    out = []
+    for s in shapes:
+        a = (rng.standard_normal(s) * scale).astype(np.float32)
+        out.append(bf16_exact(a) if prec else a)
+    return out
+
+
+# ------------------------------------------------------------------- GEMM
+
+@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("layout", ["fwd", "dx", "dw"])
+@pytest.mark.parametrize("MNK", [(200, 136, 72), (1000, 648, 576), (8, 8, 8), (136, 264, 1536)])
+@pytest.mark.parametrize("split", [0, 3])
+def test_gemm_layouts(sd, prec, layout, MNK, split):
+    t = torch()
+    M, N, K = MNK
+    rng = np.random.default_rng(hash((prec, layout, MNK, split)) % 2**32)
+    print(f"gemm prec={prec} layout={layout} M,N,K={MNK} split={split}", flush=True)
+    if layout == "fwd":      # Y = X W^T
+        X, W = _operands(rng, prec, (M, K), (N, K))
+        A, lda, akc, B, ldb, bkc = X, K, True, W, K, True
+        expect = oracle.linear_fwd(X, W)
+    elif layout == "dx":     # dX = dY W, W stored [K, N]
+        dY, W = _operands(rng, prec, (M, K), (K, N))
+        A, lda, akc, B, ldb, bkc = dY, K, True, W, N, False
+        expect = dY.astype(np.float64) @ W
+    else:                    # dW = dY^T X, dY stored [K, M], X stored [K, N]
+        dY, X = _operands(rng, prec, (K, M), (K, N))
+        A, lda, akc, B, ldb, bkc = dY, M, False, X, N, False
+        expect = oracle.linear_bwd(dY, X, np.zeros((M, N)))[1]
+    C = t.zeros((M, N), dtype=t.float32, device="cuda")
+    ws = t.zeros(4 * M * N + 16, dtype=t.float32, device="cuda")
+    sd.gemm(prec, M, N, K, act(A, prec), lda, akc, act(B, prec), ldb, bkc, C, N, c_f32=True, force_split=split, ws=ws)
+    t.cuda.synchronize()
+    assert rel(host(C), expect) <= tol(prec, True)
+
+
+@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("epi", ["store", "resid", "gelu", "dgelu"])
+@pytest.mark.parametrize("split", [0, 2])
+def test_gemm_epilogues(sd, prec, epi, split):
+    t = torch()
+    M, N, K = 264, 200, 320
+    rng = np.random.default_rng(17 + prec)
+    print(f"gemm epilogue prec={prec} epi={epi} split={split}", flush=True)
+    X, W = _operands(rng, prec, (M, K), (N, K), scale=0.3)
+    bias = rng.standard_normal(N).astype(np.float32)
+    ws = t.zeros(4 * M * N, dtype=t.float32, device="cuda")
+    adt = t.bfloat16 if prec else t.float32
+    lin = oracle.linear_fwd(X, W, bias)
+    args = dict(bias=dev(bias), force_split=split, ws=ws)
+    if epi == "store":
+        C = t.zeros((M, N), dtype=adt, device="cuda")
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, C, N, sd.EPI_STORE, **args)
+        t.cuda.synchronize()
+        assert rel(host(C), lin) <= tol(prec, False)
+    elif epi == "resid":
+        R = rng.standard_normal((M, N)).astype(np.float32)
+        C = t.zeros((M, N), dtype=t.float32, device="cuda")
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, C, N, sd.EPI_RESID, R=dev(R), ldr=N, **args)
+        t.cuda.synchronize()
+        assert rel(host(C), R + lin) <= tol(prec, True)
+    elif epi == "gelu":
+        U = t.zeros((M, N), dtype=adt, device="cuda")
+        Aout = t.zeros((M, N), dtype=adt, device="cuda")
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, U, N, sd.EPI_GELU, aux=Aout, ld_aux=N, **args)
+        t.cuda.synchronize()
+        assert rel(host(U), lin) <= tol(prec, False)
+        assert rel(host(Aout), oracle.gelu(lin)) <= tol(prec, False)
+    else:
+        u = rng.standard_normal((M, N)).astype(np.float32) * 2
+        u = bf16_exact(u) if prec else u
+        C = t.zeros((M, N), dtype=adt, device="cuda")
+        args.pop("bias")
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, C, N, sd.EPI_DGELU, aux=act(u, prec),
+                ld_aux=N, **args)
+        t.cuda.synchronize()
+        assert rel(host(C), oracle.linear_fwd(X, W) * oracle.gelu_grad(u)) <= tol(prec, False)
+
+
+def test_gemm_output_row_limit(sd):
+    """Rows >= M_out are computed but never stored (the padded vocabulary)."""
+    t = torch()
+    rng = np.random.default_rng(3)
+    M, N, K = 136, 64, 96
+    A, B = _operands(rng, 1, (K, M), (K, N))
+    C = t.full((M, N), 7.0, dtype=t.float32, device="cuda")
+    sd.gemm(1, M, N, K, act(A, 1), M, False, act(B, 1), N, False, C, N, c_f32=True, M_out=131)
+    t.cuda.synchronize()
+    c = host(C)
+    assert rel(c[:131], (A.astype(np.float64).T @ B)[:131]) <= 2e-5
+    assert np.all(c[131:] == 7.0)
+
+
+# -------------------------------------------------------------- LayerNorm
+
+@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("C", [128, 768])
+def test_layernorm_fwd_bwd(sd, prec, C):
+    t = torch()
+    M, eps = 300, 1e-5
+    rng = np.random.default_rng(C + prec)
+    x = (rng.standard_normal((M, C)) * 2 + 0.3).astype(np.float32)
+    g = (1 + 0.2 * rng.standard_normal(C)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    adt = t.bfloat16 if prec else t.float32
+    y = t.zeros((M, C), dtype=adt, device="cuda")
+    mu = t.zeros(M, device="cuda")
+    rs = t.zeros(M, device="cuda")
+    sd.layernorm_fwd(prec, dev(x), dev(g), dev(b), eps, y, mu, rs)
+    ey, emu, ers = oracle.layernorm_fwd(x, g, b, eps)
+    t.cuda.synchronize()
+    assert rel(host(y), ey) <= tol(prec, False)
+    assert rel(host(mu), emu) <= 1e-5 and rel(host(rs), ers) <= 1e-5
+    dy = rng.standard_normal((M, C)).astype(np.float32)
+    gin = rng.standard_normal((M, C)).astype(np.float32)
+    gout = dev(gin)
+    gact = t.zeros((M, C), dtype=adt, device="cuda")
+    dg = t.zeros(C, device="cuda")
+    db = t.zeros(C, device="cuda")
+    ws = t.zeros(sd.layernorm_bwd_ws_floats(M, C), device="cuda")
+    sd.layernorm_bwd(prec, dev(dy), dev(x), mu, rs, dev(g), gout, gout, gact, dg, db, ws)
+    edx, edg, edb = oracle.layernorm_bwd(dy, x, host(mu), host(rs), g)
+    t.cuda.synchronize()
+    assert rel(host(gout), gin + edx) <= 2e-5
+    assert rel(host(gact), gin + edx) <= tol(prec, False)
+    assert rel(host(dg), edg) <= 2e-5 and rel(host(db), edb) <= 2e-5
+
+
+# ------------------------------------------------- index layout, embedding
+
+def _doc_ids(rng, B, T, lens=(1, 40)):
+    doc = np.zeros((B, T), np.int32)
+    for b in range(B):
+        t0, d = 0, 0
+        while t0 < T:
+            L = int(rng.integers(lens[0], lens[1] + 1))
+            doc[b, t0:t0 + L] = d
+            t0 += L
+            d += 1
+    return doc
+
+
+def test_index_layout_bit_exact(sd):
+    t = torch()
+    rng = np.random.default_rng(5)
+    B, T = 3, 300
+    doc = _doc_ids(rng, B, T)
+    doc[2] = 7  # one document
+    start, pos, end = (t.zeros((B, T), dtype=t.int32, device="cuda") for _ in range(3))
+    flags = t.zeros(4, dtype=t.int32, device="cuda")
+    sd.index_layout(dev(doc), B, T, start, end, pos, flags)
+    es, ep = oracle.index_layout(doc, B, T)
+    ee = np.zeros((B, T), np.int64)
+    for b in range(B):
+        for i in range(T):
+            j = i
+            while j < T and doc[b, j] == doc[b, i]:
+                j += 1
+            ee[b, i] = j
+    t.cuda.synchronize()
+    assert np.array_equal(start.cpu().numpy(), es) and np.array_equal(pos.cpu().numpy(), ep)
+    assert np.array_equal(end.cpu().numpy(), ee)
+    assert int(flags[0]) == 0
+    # no doc ids: start 0, pos t, end T
+    sd.index_layout(None, B, T, start, end, pos, flags)
+    t.cuda.synchronize()
+    assert np.all(start.cpu().numpy() == 0) and np.all(end.cpu().numpy() == T)
+    assert np.array_equal(pos.cpu().numpy(), np.tile(np.arange(T), (B, 1)))
+    # decreasing doc ids set flags bit 1
+    bad = doc.copy()
+    bad[0, 100] = -5
+    sd.index_layout(dev(bad), B, T, start, end, pos, flags)
+    t.cuda.synchronize()
+    assert int(flags[0]) & 2
+
+
+def test_embedding_forward(sd):
+    t = torch()
+    rng = np.random.default_rng(6)
+    V, S, C, M = 1000, 64, 256, 777
+    wte = rng.standard_normal((V, C)).astype(np.float32)
+    wpe = rng.standard_normal((S, C)).astype(np.float32)
+    tok = rng.integers(0, V, M).astype(np.int32)
+    pos = rng.integers(0, S, M).astype(np.int32)
+    x = t.zeros((M, C), device="cuda")
+    flags = t.zeros(4, dtype=t.int32, device="cuda")
+    sd.embed_fwd(dev(tok), dev(pos), dev(wte), dev(wpe), x, flags)
+    t.cuda.synchronize()
+    assert np.array_equal(host(x).astype(np.float32), wte[tok] + wpe[pos])
+    assert rel(host(x), oracle.embedding_fwd(wte, wpe, tok, pos)) <= 1e-7
+
+
+# -------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("packed", [False, True])
+def test_attention_fwd_bwd(sd, prec, D, packed):
+    t = torch()
+    B, T, H = 2, 200, 3
+    C = H * D
+    rng = np.random.default_rng(D + 2 * prec + 4 * packed)
+    print(f"attention prec={prec} D={D} packed={packed}", flush=True)
+    qkv = (rng.standard_normal((B, T, 3 * C)) * 1.5).astype(np.float32)
+    qkv = bf16_exact(qkv) if prec else qkv
+    doc = _doc_ids(rng, B, T, (1, 90)) if packed else None
+    start_np, _ = oracle.index_layout(doc, B, T)
+    start, end, pos = (t.zeros((B, T), dtype=t.int32, device="cuda") for _ in range(3))
+    flags = t.zeros(4, dtype=t.int32, device="cuda")
+    sd.index_layout(None if doc is None else dev(doc), B, T, start, end, pos, flags)
+    adt = t.bfloat16 if prec else t.float32
+    o = t.zeros((B, T, C), dtype=adt, device="cuda")
+    lse = t.zeros((B, H, T), device="cuda")
+    qkv_d = act(qkv, prec)
+    sd.attn_fwd(prec, qkv_d, start, end, B, T, H, D, o, lse)
+
+    def heads(a):
+        return a.reshape(B, T, H, D).transpose(0, 2, 1, 3)
+
+    q, k, v = heads(qkv[..., :C]), heads(qkv[..., C:2 * C]), heads(qkv[..., 2 * C:])
+    eo, else_ = oracle.attention_fwd(q, k, v, start_np)
+    eo = eo.transpose(0, 2, 1, 3).reshape(B, T, C)
+    t.cuda.synchronize()
+    assert rel(host(o), eo) <= (2e-5 if prec == 0 else 8e-3)
+    assert np.abs(host(lse) - else_).max() <= (2e-5 if prec == 0 else 2e-3)
+    do = rng.standard_normal((B, T, C)).astype(np.float32)
+    do = bf16_exact(do) if prec else do
+    dqkv = t.zeros((B, T, 3 * C), dtype=adt, device="cuda")
+    delta = t.zeros((B, H, T), device="cuda")
+    sd.attn_bwd(prec, qkv_d, o, lse, act(do, prec), start, end, B, T, H, D, delta, dqkv)
+    dq, dk, dv = oracle.attention_bwd(heads(do), q, k, v, start_np)
+    got = host(dqkv)
+    t.cuda.synchronize()
+    for i, e in enumerate((dq, dk, dv)):
+        e = e.transpose(0, 2, 1, 3).reshape(B, T, C)
+        g = got[..., i * C:(i + 1) * C]
+        if prec == 0:
+            assert rel(g, e) <= 5e-5, i
+        else:
+            assert rel(g, e) <= 2e-2 and cos(g, e) >= 0.9995, i
+
+
+# ----------------------------------------------------------- cross-entropy
+
+@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("V", [257, 8000])
+def test_cross_entropy(sd, prec, V):
+    t = torch()
+    M = 300
+    ldz = (V + 127) // 128 * 128
+    rng = np.random.default_rng(V + prec)
+    z = (rng.standard_normal((M, V)) * 3).astype(np.float32)
+    z = bf16_exact(z) if prec else z
+    tgt = rng.integers(0, V, M).astype(np.int32)
+    tgt[::7] = -1
+    zp = np.zeros((M, ldz), np.float32)
+    zp[:, :V] = z
+    zp[:, V:] = 5.0  # padding columns must be ignored and zeroed
+    zd = act(zp, prec)
+    loss = t.zeros(4, device="cuda")
+    ws_n = t.zeros(4, dtype=t.int32, device="cuda")
+    ws_rows = t.zeros(M, device="cuda")
+    flags = t.zeros(4, dtype=t.int32, device="cuda")
+    sd.xent(prec, zd, ldz, M, V, dev(tgt), loss, ws_n, ws_rows, flags)
+    el, edz, n = oracle.xent_fwd_bwd(z, tgt)
+    t.cuda.synchronize()
+    got = host(zd)
+    assert abs(float(loss[0]) - el) <= 2e-5 * abs(el)
+    assert int(loss[3]) == n
+    assert rel(got[:, :V], edz) <= (2e-5 if prec == 0 else 6e-3)
+    assert np.all(got[:, V:] == 0)
+    assert np.all(got[tgt < 0] == 0)
+
+
+# ------------------------------------------------ embedding backward (CSR)
+
+@pytest.mark.parametrize("nkeys,M", [(1000, 5000), (64, 3000), (50257, 8192)])
+def test_csr_bit_exact_and_segment_sums(sd, nkeys, M):
+    t = torch()
+    import synth
+    rng = np.random.Generator(np.random.PCG64(nkeys))
+    keys = synth.sample_ids(rng, ("zipf", 1.1), nkeys, M)
+    C = 128
+    counts, offsets, chunk = (t.zeros(nkeys + 1, dtype=t.int32, device="cuda") for _ in range(3))
+    perm = t.zeros(M, dtype=t.int32, device="cuda")
+    sd.csr(dev(keys), M, nkeys, counts, offsets, chunk, perm)
+    eoff, eperm = oracle.csr_by_key(keys, nkeys)
+    t.cuda.synchronize()
+    assert np.array_equal(offsets.cpu().numpy(), eoff)
+    assert np.array_equal(perm.cpu().numpy(), eperm)
+    dx = rng.standard_normal((M, C)).astype(np.float32)
+    base = rng.standard_normal((nkeys, C)).astype(np.float32)
+    dst = dev(base)
+    part = t.zeros(sd.segment_sum_ws_floats(M, nkeys, C), device="cuda")
+    sd.segment_sum(dev(dx), M, C, nkeys, counts, offsets, chunk, perm, part, dst, True)
+    ew, _ = oracle.embedding_bwd(dx, keys, np.zeros(M, np.int64), nkeys, 1)
+    t.cuda.synchronize()
+    assert rel(host(dst), base + ew) <= 1e-6
+    # bit-reproducible
+    dst2 = dev(base)
+    sd.segment_sum(dev(dx), M, C, nkeys, counts, offsets, chunk, perm, part, dst2, True)
+    t.cuda.synchronize()
+    assert t.equal(dst, dst2)
+
+
+# ---------------------------------------------------------- norm and AdamW
+
+@pytest.mark.parametrize("clip", [1.0, 1e9])
+def test_grad_norm_and_adamw(sd, clip):
+    t = torch()
+    rng = np.random.default_rng(9)
+    n = 1_000_004
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    p = rng.standard_normal(n).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (rng.random(n) * 1e-7).astype(np.float32)
+    part = t.zeros(1024, dtype=t.float64, device="cuda")
+    ns = t.zeros(2, device="cuda")
+    flags = t.zeros(4, dtype=t.int32, device="cuda")
+    gd = dev(g)
+    sd.grad_norm(gd, clip, part, ns, flags)
+    en, es = oracle.grad_norm_and_scale({"g": g}, clip)
+    t.cuda.synchronize()
+    assert abs(float(ns[0]) - en) <= 1e-6 * en and abs(float(ns[1]) - es) <= 1e-6 * es
+    pd, md, vd = dev(p), dev(m), dev(v)
+    shadow = t.zeros(n, dtype=t.bfloat16, device="cuda")
+    sd.adamw(pd, gd, md, vd, 3e-4, 0.9, 0.999, 1e-8, 0.1, 3, ns, flags, shadow)
+    ep, em, ev = oracle.adamw(p, g, m, v, 3, 3e-4, 0.9, 0.999, 1e-8, 0.1, es)
+    t.cuda.synchronize()
+    # p' is fp32, so p' - p is known to the ulp of p: compare p' within 4 ulp
+    # plus 1e-5 of the update
+    ulp = np.abs(p.astype(np.float64)) * 2.0 ** -23
+    assert np.all(np.abs(host(pd) - ep) <= 4 * ulp + 1e-5 * np.abs(ep - p))
+    assert rel(host(md), em) <= 1e-6 and rel(host(vd), ev) <= 1e-6
+    assert t.equal(shadow, pd.to(t.bfloat16))
+
+
+def test_adamw_skips_on_nonfinite_norm(sd):
+    t = torch()
+    n = 4096
+    g = np.ones(n, np.float32)
+    g[5] = np.inf
+    p = np.arange(n, dtype=np.float32)
+    part = t.zeros(1024, dtype=t.float64, device="cuda")
+    ns = t.zeros(2, device="cuda")
+    flags = t.zeros(4, dtype=t.int32, device="cuda")
+    gd, pd, md, vd = dev(g), dev(p), t.zeros(n, device="cuda"), t.zeros(n, device="cuda")
+    sd.grad_norm(gd, 1.0, part, ns, flags)
+    sd.adamw(pd, gd, md, vd, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, ns, flags)
+    t.cuda.synchronize()
+    assert int(flags[0]) & 1
+    assert np.array_equal(pd.cpu().numpy(), p) and float(md.abs().sum()) == 0
