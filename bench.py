@@ -158,8 +158,7 @@ def main():
         for k, v in prof.items():
             if k.startswith("attn"):
                 # attention flops: forward 4 D, backward 8 D per allowed pair
-                v["flops"] = attn_f / 3.0 * (1.0 if k == "attn_fwd" else 2.0) * v["launches"] / (
-                    shape.n_layers * args.steps)
+                v["flops"] = attn_f / 3.0 * (1.0 if k == "attn_fwd" else 2.0) * v["launches"] / shape.n_layers
         total_ms = sum(v["ms"] for v in prof.values())
         mm = {k: v for k, v in prof.items() if k.startswith("gemm") or k.startswith("attn")}
         mm_flops = sum(v["flops"] for v in mm.values())

@@ -17,6 +17,8 @@
 // fp32 path: fp32 matrix and vector peaks are equal on this chip (157 TF), so
 // the fp32 GEMM is a plain LDS-tiled FMA kernel (64 x 64 tile, 4 x 4 per
 // thread).
+#include <cstdlib>
+
 #include "kernels.h"
 
 namespace lm {
@@ -61,103 +63,230 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, long row, long col, 
   }
 }
 
-// ------------------------------------------------------------ bf16 MFMA GEMM
-constexpr int kBK = 64;
-constexpr int kPitch = 72;  // bf16 per LDS row (64 + 8 padding)
-
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
-  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+// Epilogue of 8 consecutive output columns (bf16 path; columns col..col+7
+// exist, leading dimensions are multiples of 8).
+__device__ __forceinline__ void ld8_bf16(const bf16* p, float* v) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void st8_bf16(bf16* p, const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void ld8_f32(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void st8_f32(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// Loads the ROWS x 64 tile of one operand for the K step at k0 into registers.
-// K-contiguous: ROWS * 8 chunks of 8 bf16. Otherwise: ROWS 8 x 8 blocks.
-template <int ROWS, bool KC>
-struct TileLoader {
-  static constexpr int NCH = KC ? (ROWS * 8 + 255) / 256 : 1;  // K-contiguous chunks per thread
-  static constexpr int NBLK = KC ? 0 : (ROWS + 255) / 256;     // 8x8 blocks per thread (<= 1 here)
-  uint4 r[KC ? NCH : 8];
-  static_assert(KC || ROWS <= 256, "one 8x8 block per thread at most");
+template <int EPI, typename TC>
+__device__ __forceinline__ void epilogue8(const GemmArgs& p, long row, long col, float* v, int z) {
+  if (EPI == EPI_PARTIAL) {
+    st8_f32(reinterpret_cast<float*>(p.C) + z * p.split_stride + row * p.ldc + col, v);
+    return;
+  }
+  if (EPI != EPI_DGELU && p.bias) {
+    float b[8];
+    ld8_f32(p.bias + col, b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += b[i];
+  }
+  if (EPI == EPI_STORE) {
+    if (sizeof(TC) == 4) st8_f32(reinterpret_cast<float*>(p.C) + row * p.ldc + col, v);
+    else st8_bf16(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+  } else if (EPI == EPI_RESID) {
+    float r[8];
+    ld8_f32(p.R + row * p.ldr + col, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += r[i];
+    st8_f32(reinterpret_cast<float*>(p.C) + row * p.ldc + col, v);
+  } else if (EPI == EPI_GELU) {
+    st8_bf16(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = gelu_f(v[i]);
+    st8_bf16(reinterpret_cast<bf16*>(p.aux) + row * p.ld_aux + col, a);
+  } else if (EPI == EPI_DGELU) {
+    float u[8];
+    ld8_bf16(reinterpret_cast<const bf16*>(p.aux) + row * p.ld_aux + col, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= gelu_grad_f(u[i]);
+    st8_bf16(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+  }
+}
 
-  __device__ __forceinline__ void load(const bf16* __restrict__ base, long ld, int row0, int rows_total, int k0,
-                                       int k_end, int tid) {
+// ------------------------------------------------------------ bf16 MFMA GEMM
+// Block tile BM x BN, K step 64, WGM x WGN wavefronts (wave tile WTM x WTN,
+// multiples of 32), two LDS stages; global loads of step k+1 are issued before
+// the MFMAs of step k.
+//
+// LDS layouts (no padding, XOR swizzles at 16-byte-chunk granularity):
+//  K-contiguous operand: [row][64 k], 128 B per row; chunk c of row r sits at
+//    c ^ ((r >> 1) & 7), so the 16-byte fragment reads of 16 consecutive rows
+//    hit 64 distinct banks.
+//  M/N-contiguous operand: [64 k][ROWS] copied as it is in memory (no register
+//    transpose); chunk q of k-row k sits at q ^ ((k & 3) << 2). Its MFMA
+//    fragments come from two ds_read_b64_tr_b16 per k-step: within each group
+//    of 16 lanes, source lane i reads 4 elements at k-row k0 + i/4, columns
+//    m0 + 4 (i % 4) .. + 3, and lane i receives column m0 + i at k-rows
+//    k0 .. k0 + 3 (the layout of the instruction, checked on the device).
+constexpr int kBK = 64;
+
+template <int ROWS>
+struct MNPitch {  // elements per k-row of an M/N-contiguous tile (>= 128 for the swizzle)
+  static constexpr int value = ROWS < 128 ? 128 : ROWS;
+};
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+
+__device__ __forceinline__ bf16x4_t ds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) bf16*)((uintptr_t)p)));
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr unsigned kOutOfRange = 0x80000000u;  // a byte offset past every buffer's range
+
+template <int ROWS, bool KC, int NT>
+struct Tile {
+  static constexpr int PITCH = KC ? 64 : MNPitch<ROWS>::value;  // bf16 elements per LDS row
+  static constexpr int ELEMS = KC ? ROWS * 64 : 64 * PITCH;
+  static constexpr int CHUNKS = ROWS * 8;                        // 16-byte chunks per K step
+  static constexpr int NL = (CHUNKS + NT - 1) / NT;
+  static constexpr bool FULL = CHUNKS % NT == 0;                 // every thread owns NL chunks
+  uint4 r[NL];
+  __amdgpu_buffer_rsrc_t rsrc;
+  unsigned voff[NL];  // byte offset of the chunk from the tile origin, without the K-step term
+  int kin[NL];        // K offset of the chunk inside the K step
+  int soff[NL];       // LDS element offset of the chunk
+  unsigned kstride;   // bytes per unit of K
+
+  // Per-thread addressing, computed once per block. The buffer starts at the
+  // tile origin and ends after the operand's last element, so chunks outside
+  // the operand read zeros (hardware range check) without a branch.
+  __device__ __forceinline__ void init(const bf16* g, long ld, int row0, int rows_total, int K, int tid) {
+    long origin, extent;
     if (KC) {
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        int c = tid + i * 256;
-        int row = c >> 3, kc = c & 7;
-        int gr = row0 + row, gk = k0 + kc * 8;
-        if (c < ROWS * 8 && gr < rows_total && gk < k_end)
-          r[i] = *reinterpret_cast<const uint4*>(base + (long)gr * ld + gk);
-        else
-          r[i] = make_uint4(0, 0, 0, 0);
-      }
+      origin = (long)row0 * ld;
+      extent = (long)(rows_total - 1 - row0) * ld + K;
     } else {
-      int b = tid;
-      if (b < ROWS) {
-        int ib = b % (ROWS / 8), kb = b / (ROWS / 8);
-        int gi = row0 + ib * 8;
+      origin = row0;
+      extent = (long)(K - 1) * ld + (rows_total - row0);
+    }
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(g + origin), (short)0,
+                                             (int)min(extent * 2, (long)0x7fffffff), 0x00020000);
+    kstride = KC ? 2u : (unsigned)(ld * 2);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          int gk = k0 + kb * 8 + j;
-          if (gi < rows_total && gk < k_end)
-            r[j] = *reinterpret_cast<const uint4*>(base + (long)gk * ld + gi);
-          else
-            r[j] = make_uint4(0, 0, 0, 0);
-        }
+    for (int i = 0; i < NL; ++i) {
+      const int c = min(tid + i * NT, CHUNKS - 1);
+      if (KC) {
+        const int row = c >> 3, kc = c & 7;
+        voff[i] = (unsigned)(((long)row * ld + kc * 8) * 2);
+        kin[i] = kc * 8;
+        soff[i] = row * 64 + ((kc ^ ((row >> 1) & 7)) << 3);
+      } else {
+        const int k = c / (ROWS / 8), q = c % (ROWS / 8);
+        voff[i] = (unsigned)(((long)k * ld + q * 8) * 2);
+        kin[i] = k;
+        soff[i] = k * PITCH + ((q ^ ((k & 3) << 2)) << 3);
       }
+    }
+  }
+
+  // Loads of one K step (k0 .. k0 + 63, nothing at or past k_end).
+  __device__ __forceinline__ void load(int k0, int k_end) {
+    const int so = (int)((unsigned)k0 * kstride);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const unsigned vo = (k0 + kin[i] < k_end) ? voff[i] : kOutOfRange;
+      u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vo, so, 0);
+      r[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
 
   __device__ __forceinline__ void store(bf16* __restrict__ s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      if (FULL || tid + i * NT < CHUNKS) *reinterpret_cast<uint4*>(s + soff[i]) = r[i];
+  }
+
+  // MFMA 32x32x16 operand fragment: rows row0 + lane % 32, k-slots
+  // ks*16 + 8 (lane / 32) .. + 7.
+  __device__ __forceinline__ bf16x8_t frag(const bf16* __restrict__ s, int row0, int ks, int lane) const {
     if (KC) {
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        int c = tid + i * 256;
-        if (c < ROWS * 8) {
-          int row = c >> 3, kc = c & 7;
-          *reinterpret_cast<uint4*>(s + row * kPitch + kc * 8) = r[i];
-        }
-      }
+      const int row = row0 + (lane & 31);
+      const int kc = ks * 2 + (lane >> 5);
+      return *reinterpret_cast<const bf16x8_t*>(s + row * 64 + ((kc ^ ((row >> 1) & 7)) << 3));
     } else {
-      int b = tid;
-      if (b < ROWS) {
-        int ib = b % (ROWS / 8), kb = b / (ROWS / 8);
-        // r[j] holds 8 consecutive rows-of-the-tile (i) at k = kb*8 + j.
-        // Output row i = ib*8 + c gets the 8 k-values of element c.
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          uint32_t o[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            uint32_t lo = word_of(r[2 * j], c >> 1), hi = word_of(r[2 * j + 1], c >> 1);
-            o[j] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-          }
-          *reinterpret_cast<uint4*>(s + (ib * 8 + c) * kPitch + kb * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-      }
+      const int g = lane >> 4, i = lane & 15;
+      const int m = row0 + (g & 1) * 16 + 4 * (i & 3);  // first of the 4 columns this lane reads
+      const int k = ks * 16 + (g >> 1) * 8 + (i >> 2);
+      const int q = m >> 3, h = m & 7;
+      const bf16* p0 = s + k * PITCH + (((q ^ ((k & 3) << 2))) << 3) + h;
+      const bf16* p1 = s + (k + 4) * PITCH + (((q ^ (((k + 4) & 3) << 2))) << 3) + h;
+      bf16x4_t lo = ds_read_tr(p0), hi = ds_read_tr(p1);
+      return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
 };
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, typename TC>
-__global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * kPitch];
-  __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * kPitch];
+// Maps the linear block id to a tile so that consecutive tiles of the grouped
+// order share an XCD (blocks are dealt to the 8 XCDs round-robin): each XCD
+// gets a contiguous range of tiles, walked GROUP_M m-tiles at a time, so an
+// XCD's L2 keeps the A row-panels and B column-panels its tiles share.
+__device__ __forceinline__ void tile_of(int b, int nb, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int xcd = b & 7, local = b >> 3, q = nb >> 3, r = nb & 7;
+  const int t = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = t / per_group, first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in = t % per_group;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+    __attribute__((amdgpu_waves_per_eu(BM * BN > 128 * 128 ? 1 : 2, BM * BN > 128 * 128 ? 1 : 2)))
+    gemm_bf16_kernel(GemmArgs p) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tiles are multiples of 32");
+  using TA = Tile<BM, AK, NT>;
+  using TB = Tile<BN, BKC, NT>;
+  __shared__ __attribute__((aligned(16))) bf16 sA[2][TA::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][TB::ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int z = blockIdx.z;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tmi, tni;
+  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tmi, tni);
+  const int m0 = tmi * BM, n0 = tni * BN;
+  const int z = blockIdx.y;
   const int k_begin = z * p.k_split;
   const int k_end = min(p.K, k_begin + p.k_split);
   const int nk = (k_end - k_begin + kBK - 1) / kBK;
   const bf16* A = reinterpret_cast<const bf16*>(p.A);
   const bf16* B = reinterpret_cast<const bf16*>(p.B);
 
-  TileLoader<BM, AK> la;
-  TileLoader<BN, BKC> lb;
+  TA la;
+  TB lb;
+  la.init(A, p.lda, m0, p.M, p.K, tid);
+  lb.init(B, p.ldb, n0, p.N, p.K, tid);
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -167,57 +296,94 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmArgs p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   if (nk > 0) {
-    la.load(A, p.lda, m0, p.M, k_begin, k_end, tid);
-    lb.load(B, p.ldb, n0, p.N, k_begin, k_end, tid);
+    la.load(k_begin, k_end);
+    lb.load(k_begin, k_end);
     la.store(sA[0], tid);
     lb.store(sB[0], tid);
   }
   __syncthreads();
 
+  // Software pipeline: the fragments of k-step ks+1 are read from LDS while
+  // the MFMAs of k-step ks run, and the global loads of the next K tile are in
+  // flight during the whole tile. The last iteration re-loads a clamped tile
+  // (its data are never stored), which keeps the loop body branch-free.
+  bf16x8_t af[2][TM], bfr[2][TN];
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = la.frag(sA[0], wm * WTM + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[0][j] = lb.frag(sB[0], wn * WTN + j * 32, 0, lane);
+  }
   for (int it = 0; it < nk; ++it) {
     const int cur = it & 1;
-    if (it + 1 < nk) {
-      la.load(A, p.lda, m0, p.M, k_begin + (it + 1) * kBK, k_end, tid);
-      lb.load(B, p.ldb, n0, p.N, k_begin + (it + 1) * kBK, k_end, tid);
-    }
-    const bf16* a_s = sA[cur];
-    const bf16* b_s = sB[cur];
+    const int kn = k_begin + min(it + 1, nk - 1) * kBK;
+    la.load(kn, k_end);
+    lb.load(kn, k_end);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t af[TM], bfr[TN];
-      const int kof = ks * 16 + (lane >> 5) * 8;
+      const int f = ks & 1;
+      if (ks + 1 < kBK / 16) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + (wm * WM + i * 32 + (lane & 31)) * kPitch + kof);
+        for (int i = 0; i < TM; ++i) af[f ^ 1][i] = la.frag(sA[cur], wm * WTM + i * 32, ks + 1, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(b_s + (wn * WN + j * 32 + (lane & 31)) * kPitch + kof);
+        for (int j = 0; j < TN; ++j) bfr[f ^ 1][j] = lb.frag(sB[cur], wn * WTN + j * 32, ks + 1, lane);
+      }
+      // keep the reads of k-step ks+1 ahead of the MFMAs of k-step ks
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (it + 1 < nk) {
-      la.store(sA[cur ^ 1], tid);
-      lb.store(sB[cur ^ 1], tid);
+    la.store(sA[cur ^ 1], tid);
+    lb.store(sB[cur ^ 1], tid);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = la.frag(sA[cur ^ 1], wm * WTM + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[0][j] = lb.frag(sB[cur ^ 1], wn * WTN + j * 32, 0, lane);
+  }
+
+  // Epilogue through LDS: the wave row w (WGN wavefronts, WTM rows) writes its
+  // fp32 accumulators to LDS (row pitch BN + 4 floats), then all threads walk
+  // that WTM x BN region in 8-column chunks, so bias, residual and GELU
+  // operands are read and results written with 16- and 32-byte accesses.
+  // Accumulator element e of tile (i, j): row (e/4)*8 + (lane/32)*4 + e%4,
+  // column lane%32.
+  constexpr int CP = BN + 4;
+  static_assert(WTM * CP * 4 <= 2 * (TA::ELEMS + TB::ELEMS) * 2, "epilogue tile fits in the stage buffers");
+  float* sC = reinterpret_cast<float*>(&sA[0][0]);
+  static_assert(sizeof(sA) + sizeof(sB) >= WTM * CP * 4, "");
+#pragma unroll 1
+  for (int w = 0; w < WGM; ++w) {
+    if (wm == w) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+            const int c = wn * WTN + j * 32 + (lane & 31);
+            sC[r * CP + c] = acc[i][j][e];
+          }
+    }
+    __syncthreads();
+    for (int c = tid; c < WTM * BN / 8; c += NT) {
+      const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+      const long row = m0 + w * WTM + r, col = n0 + c8;
+      if (row < p.M_out && col < p.N) {
+        float v[8];
+        const float4 x0 = *reinterpret_cast<const float4*>(sC + r * CP + c8);
+        const float4 x1 = *reinterpret_cast<const float4*>(sC + r * CP + c8 + 4);
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+        epilogue8<EPI, TC>(p, row, col, v, z);
+      }
     }
     __syncthreads();
   }
-
-  // accumulator element e of tile (i, j): row (e/4)*8 + (lane/32)*4 + e%4, column lane%32
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const long col = n0 + wn * WN + j * 32 + (lane & 31);
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const long row = m0 + wm * WM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        if (row < p.M_out) epilogue<EPI, TC, bf16>(p, row, col, acc[i][j][e], z);
-      }
-    }
 }
 
 // --------------------------------------------------------------- fp32 GEMM
@@ -299,51 +465,77 @@ static GemmArgs make_args(const GemmOp& op) {
 
 static bool check_bf16(const GemmOp& op) {
   if (op.lda % 8 || op.ldb % 8) return false;
+  // 8-column epilogue chunks: N and every leading dimension of the outputs
+  if (op.N % 8 || op.ldc % 8 || (op.R && op.ldr % 8) || (op.aux && op.ld_aux % 8)) return false;
   if ((op.a_kc || op.b_kc) && op.K % 8) return false;
   if (!op.a_kc && op.M % 8) return false;
   if (!op.b_kc && op.N % 8) return false;
-  if (!op.a_kc && !op.b_kc) return true;
   return true;
 }
 
-static void tile_for(const GemmOp& op, int& BM, int& BN) {
-  BM = 128;
-  BN = 128;
-  (void)op;
+// Tile configurations: 0 = 256 x 128 (4 waves of 128 x 64), 1 = 128 x 128
+// (4 waves of 64 x 64, two blocks per CU), 2 = 256 x 96 (4 waves of 64 x 96).
+static int tiles_of(const GemmOp& op, int cfg) {
+  const int BM = cfg == 1 ? 128 : 256, BN = cfg == 2 ? 96 : 128;
+  return ((op.M + BM - 1) / BM) * ((op.N + BN - 1) / BN);
+}
+
+static int forced_cfg() {
+  static int v = [] {
+    const char* e = getenv("LMSTEP_GEMM_CFG");
+    return e ? atoi(e) : -1;
+  }();
+  return v;
+}
+
+static int pick_cfg(const GemmOp& op) {
+  const int f = forced_cfg();
+  if (f >= 0 && f <= 2 && (f != 2 || op.N % 96 == 0)) return f;
+  // 128 x 128 at two blocks per CU measured fastest for every GEMM of the
+  // GPT-2-small-shaped step (the 256-row tiles run one block per CU)
+  return 1;
 }
 
 int gemm_bf16_splits(const GemmOp& op) {
   if (op.force_split > 0) return op.force_split;
-  int BM, BN;
-  tile_for(op, BM, BN);
-  long tiles = (long)((op.M + BM - 1) / BM) * ((op.N + BN - 1) / BN);
+  const int tiles = tiles_of(op, pick_cfg(op));
   // split K when the tile grid cannot fill the 256 compute units and K is long
   int s = 1;
   while (tiles * s < 256 && op.K / (s * 2) >= 512) s *= 2;
   return s;
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, typename TC>
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC>
 static void launch_bf16(const GemmArgs& a, int splits, hipStream_t s) {
-  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, splits);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BKC, EPI, TC>), grid, dim3(256), 0, s, a);
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BKC, EPI, TC>), dim3(tiles, splits),
+                     dim3(WGM * WGN * 64), 0, s, a);
 }
 
-template <bool AK, bool BKC>
-static int dispatch_bf16_epi(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC>
+static int dispatch_bf16_cfg(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
   if (splits > 1) {
-    launch_bf16<128, 128, AK, BKC, EPI_PARTIAL, float>(a, splits, s);
+    launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_PARTIAL, float>(a, splits, s);
     return 0;
   }
   switch (op.epi) {
     case EPI_STORE:
-      if (op.c_f32) launch_bf16<128, 128, AK, BKC, EPI_STORE, float>(a, 1, s);
-      else launch_bf16<128, 128, AK, BKC, EPI_STORE, bf16>(a, 1, s);
+      if (op.c_f32) launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_STORE, float>(a, 1, s);
+      else launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_STORE, bf16>(a, 1, s);
       return 0;
-    case EPI_RESID: launch_bf16<128, 128, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
-    case EPI_GELU: launch_bf16<128, 128, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
-    case EPI_DGELU: launch_bf16<128, 128, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
+    case EPI_RESID: launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
+    case EPI_GELU: launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
+    case EPI_DGELU: launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
     default: return -1;
+  }
+}
+
+template <bool AK, bool BKC>
+static int dispatch_bf16_epi(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
+  switch (pick_cfg(op)) {
+    case 0: return dispatch_bf16_cfg<256, 128, 2, 2, AK, BKC>(op, a, splits, s);
+    case 2: return dispatch_bf16_cfg<256, 96, 4, 1, AK, BKC>(op, a, splits, s);
+    default: return dispatch_bf16_cfg<128, 128, 2, 2, AK, BKC>(op, a, splits, s);
   }
 }
 

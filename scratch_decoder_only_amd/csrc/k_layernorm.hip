@@ -168,44 +168,80 @@ template void launch_ln_bwd<float>(const float*, const float*, const float*, con
 template void launch_ln_bwd<bf16>(const float*, const float*, const float*, const float*, const float*, int, int,
                                   const float*, float*, bf16*, float*, float*, hipStream_t);
 
-// out[c] = sum over p < P of part[p][c], in increasing p (fixed order).
-// Two vectors at once (the dg and db partials of one LayerNorm).
-__global__ void colsum_partials_kernel(const float* __restrict__ pa, const float* __restrict__ pb, int P, int C,
-                                       float* __restrict__ oa, float* __restrict__ ob) {
-  int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= C) return;
+// out[c] = sum over p < P of part[p][c] in a fixed order: thread (c, r) of a
+// block sums p = r, r + 4, ... for column c, then the four partial sums are
+// added in r order. Two vectors at once (the dg and db partials of one
+// LayerNorm).
+__global__ void __launch_bounds__(256) colsum_partials_kernel(const float* __restrict__ pa, const float* __restrict__ pb,
+                                                              int P, int C, float* __restrict__ oa,
+                                                              float* __restrict__ ob) {
+  __shared__ float sa[4][64], sb[4][64];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63), r = threadIdx.x >> 6;
   float a = 0.f, b = 0.f;
-  for (int p = 0; p < P; ++p) {
-    a += pa[(long)p * C + c];
-    if (pb) b += pb[(long)p * C + c];
+  if (c < C)
+    for (int p = r; p < P; p += 4) {
+      a += pa[(long)p * C + c];
+      if (pb) b += pb[(long)p * C + c];
+    }
+  sa[r][threadIdx.x & 63] = a;
+  sb[r][threadIdx.x & 63] = b;
+  __syncthreads();
+  if (r == 0 && c < C) {
+    const int t = threadIdx.x;
+    oa[c] = ((sa[0][t] + sa[1][t]) + sa[2][t]) + sa[3][t];
+    if (ob) ob[c] = ((sb[0][t] + sb[1][t]) + sb[2][t]) + sb[3][t];
   }
-  oa[c] = a;
-  if (ob) ob[c] = b;
 }
 
 void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob,
                             hipStream_t s) {
-  hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + 255) / 256), dim3(256), 0, s, pa, pb, P, C, oa, ob);
+  hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + 63) / 64), dim3(256), 0, s, pa, pb, P, C, oa, ob);
 }
 
-// Column sums of an [M, N] matrix (bias gradients): stage 1 writes per-block
-// partials over kColRows rows, stage 2 (colsum_partials) sums them in order.
+// Column sums of an [M, N] matrix (bias gradients), N a multiple of 4. Stage
+// 1: a block covers 256 columns (4 per thread) and kColRows rows, its four
+// wavefronts taking every fourth row, combined in a fixed order into one
+// partial row per block; stage 2 (colsum_partials) sums the partials.
+template <typename T> struct Quad;
+template <> struct Quad<float> {
+  static __device__ __forceinline__ float4 ld(const float* p) { return *reinterpret_cast<const float4*>(p); }
+};
+template <> struct Quad<bf16> {
+  static __device__ __forceinline__ float4 ld(const bf16* p) {
+    uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xffff0000u));
+  }
+};
+
 template <typename T>
 __global__ void __launch_bounds__(256) colsum_stage1_kernel(const T* __restrict__ a, long lda, int M, int N,
                                                             float* __restrict__ part) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= N) return;
+  __shared__ float4 s[4][64];
+  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int c = (blockIdx.x * 64 + lane) * 4;
   const long r0 = (long)blockIdx.y * kColRows;
   const long r1 = min((long)M, r0 + kColRows);
-  float acc = 0.f;
-  for (long r = r0; r < r1; ++r) acc += Act<T>::ld(a, r * lda + c);
-  part[(long)blockIdx.y * N + c] = acc;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < N)
+    for (long r = r0 + g; r < r1; r += 4) {
+      float4 v = Quad<T>::ld(a + r * lda + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+  s[g][lane] = acc;
+  __syncthreads();
+  if (g == 0 && c < N) {
+    float4 t0 = s[0][lane], t1 = s[1][lane], t2 = s[2][lane], t3 = s[3][lane];
+    float4 o = make_float4(((t0.x + t1.x) + t2.x) + t3.x, ((t0.y + t1.y) + t2.y) + t3.y,
+                           ((t0.z + t1.z) + t2.z) + t3.z, ((t0.w + t1.w) + t2.w) + t3.w);
+    *reinterpret_cast<float4*>(part + (long)blockIdx.y * N + c) = o;
+  }
 }
 
 template <typename T>
 void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s) {
   int P = (M + kColRows - 1) / kColRows;
-  hipLaunchKernelGGL(colsum_stage1_kernel<T>, dim3((N + 255) / 256, P), dim3(256), 0, s, a, lda, M, N, part);
+  hipLaunchKernelGGL(colsum_stage1_kernel<T>, dim3((N / 4 + 63) / 64, P), dim3(256), 0, s, a, lda, M, N, part);
   launch_colsum_partials(part, nullptr, P, N, out, nullptr, s);
 }
 template void launch_colsum<float>(const float*, long, int, int, float*, float*, hipStream_t);

@@ -59,7 +59,7 @@ int lmk_layernorm_bwd(int precision, const float* dy, const float* x, const floa
 int64_t lmk_colsum_ws_floats(int M, int N) { return (int64_t)((M + kColRows - 1) / kColRows) * N; }
 
 int lmk_colsum(int precision_of_a, const void* a, int64_t lda, int M, int N, float* out, float* ws, void* stream) {
-  if (M <= 0 || N <= 0) return -1;
+  if (M <= 0 || N <= 0 || N % 4 || lda % 4) return -1;
   if (precision_of_a) launch_colsum<bf16>(reinterpret_cast<const bf16*>(a), lda, M, N, ws, out, S(stream));
   else launch_colsum<float>(reinterpret_cast<const float*>(a), lda, M, N, ws, out, S(stream));
   return 0;

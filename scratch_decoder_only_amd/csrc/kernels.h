@@ -5,8 +5,8 @@
 
 namespace lm {
 
-constexpr int kLnRowsPerBlock = 64;  // rows per block in the LayerNorm backward
-constexpr int kColRows = 256;        // rows per partial in the bias-gradient column sums
+constexpr int kLnRowsPerBlock = 16;  // rows per block in the LayerNorm backward
+constexpr int kColRows = 128;        // rows per partial in the bias-gradient column sums
 
 // ------------------------------------------------------------------- GEMM
 // C[i, j] = sum_k A(i, k) B(j, k) for i < M, j < N, k < K, then an epilogue.
