@@ -11,21 +11,24 @@
 //
 // gfx950 design. Every block has 4 wavefronts of 64 lanes; a wavefront owns
 // 32 rows (queries in the forward and dQ passes, keys in the dK/dV pass) and
-// walks 64-row tiles of the other side staged in LDS. The MFMA is
-// v_mfma_f32_32x32x16_bf16 (lane l holds row l%32 of a 32x16 operand, k-slots
-// 8(l/32)..8(l/32)+7; the 32x32 result gives lane l column l%32 and rows
-// 8(e/4) + 4(l/32) + e%4, e = 0..15).
+// walks 64-row tiles of the other side, staged in LDS with a two-stage
+// pipeline (the next tile's buffer loads are in flight during the MFMAs of the
+// current one). The MFMA is v_mfma_f32_32x32x16_bf16 (lane l holds row l%32 of
+// a 32x16 operand, k-slots 8(l/32)..8(l/32)+7; the 32x32 result gives lane l
+// column l%32 and rows 8(e/4) + 4(l/32) + e%4, e = 0..15).
 // Forward and dQ compute S^T = K Q^T, so lane l keeps one query (l%32): the
-// running max and sum of the online softmax are per lane (two lanes, l and
-// l^32, share a query and combine once per tile), and O^T += V^T P^T takes P
-// straight from registers as the B operand. The key order inside an MFMA
-// k-step is the order in which the lane holds its scores; V^T (and K^T) are
-// read from LDS in that same order, so nothing is shuffled. dK/dV computes
-// S = Q K^T so lane l keeps one key. There are no atomics: dQ and dK/dV are
-// separate passes (P is recomputed in each), so results are bit-reproducible.
-// Tiles of a block are skipped outside [start of its first query, its last
-// query], so the block-diagonal mask of packed rows costs only the pairs it
-// keeps (plus the partial tiles on its edges).
+// running max and sum of the online softmax are per lane (lanes l and l^32
+// share a query and combine once per tile), and O^T += V^T P^T takes P
+// straight from registers as the B operand. dK/dV computes S = Q K^T so lane l
+// keeps one key. The k-slots of one MFMA step are taken in the order a lane
+// holds its scores (slot j <-> row 8(j/4) + 4(l/32) + j%4 of the 16-row step);
+// the transposed A operands (V^T, K^T, Q^T, dO^T) are read in that same order
+// from the row-major LDS tiles with ds_read_b64_tr_b16, so no tile is ever
+// transposed. There are no atomics: dQ and dK/dV are separate passes (P is
+// recomputed in each), so results are bit-reproducible. Tiles outside
+// [start of a block's first query, its last query] are skipped, so the
+// block-diagonal mask of packed rows costs only the pairs it keeps (plus the
+// partial tiles on its edges).
 #include "kernels.h"
 
 namespace lm {
@@ -34,94 +37,108 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+
+__device__ __forceinline__ bf16x4_t ds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) bf16*)((uintptr_t)p)));
+}
+
+// Row-major [64 rows][D] LDS tile, 16-byte chunks XOR-swizzled per row so that
+// both the 16-byte fragment reads of 16 consecutive rows and the transpose
+// reads of 4 rows x 32 columns hit distinct banks.
 template <int D>
-struct Cfg {
-  static constexpr int KS = D / 16;   // MFMA k-steps over the head dimension
-  static constexpr int DT = D / 32;   // 32-wide tiles of the head dimension
-  static constexpr int RP = D + 8;    // LDS pitch (bf16) of a row-major [rows][D] tile
-  static constexpr int TP = 64 + 4;   // LDS pitch (bf16) of a transposed [D][64] tile
+struct RowTile {
+  static constexpr int CH = D / 8;  // chunks per row
+  static constexpr int ELEMS = 64 * D;
+  static __device__ __forceinline__ int sw(int r) {
+    if (D == 64) {
+      const int x = (r >> 1) & 7;
+      return ((x & 1) << 2) | (x >> 1);
+    }
+    return (r >> 2) & 3;
+  }
+  static __device__ __forceinline__ int off(int r, int c) { return r * D + ((c ^ sw(r)) << 3); }
 };
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
 }
-
 __device__ __forceinline__ bf16x8_t as_frag(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-
 __device__ __forceinline__ uint4 pack_frag(const float* v) {
   return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
-  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
-}
-
-// Row-major tile: rows r0..r0+63 (zero beyond T) of a [*, ld] matrix,
-// columns col0..col0+D-1 -> s[r][0..D) with pitch RP.
+// Loader of one 64-row tile (rows r0..r0+63 of a [T, ld] bf16 matrix, columns
+// col0..col0+D-1) into a RowTile, through registers: buffer loads (rows past
+// T read zeros), then LDS stores after the current tile's MFMAs.
 template <int D>
-__device__ __forceinline__ void load_rows(bf16* __restrict__ s, const bf16* __restrict__ g, long ld, int r0, int T,
-                                          int col0, int tid) {
-  constexpr int CH = D / 8;  // 16-byte chunks per row
-  for (int c = tid; c < 64 * CH; c += 256) {
-    int r = c / CH, k = c % CH;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + r < T) v = *reinterpret_cast<const uint4*>(g + (long)(r0 + r) * ld + col0 + k * 8);
-    *reinterpret_cast<uint4*>(s + r * Cfg<D>::RP + k * 8) = v;
-  }
-}
-
-// Transposed tile: s[d][r] = g[r0 + r][col0 + d] for r < 64 (zero beyond T),
-// pitch TP. 8 x 8 blocks are transposed in registers.
-template <int D>
-__device__ __forceinline__ void load_cols(bf16* __restrict__ s, const bf16* __restrict__ g, long ld, int r0, int T,
-                                          int col0, int tid) {
-  constexpr int NB = 8 * (D / 8);
-  for (int b = tid; b < NB; b += 256) {
-    int rb = b % 8, db = b / 8;
-    uint4 in[8];
+struct TileLoad {
+  static constexpr int N = 64 * D / 8 / 256;  // 16-byte chunks per thread (1 or 2)
+  uint4 r[N];
+  __amdgpu_buffer_rsrc_t rsrc;
+  unsigned voff[N];
+  int soff[N];
+  long ld;
+  __device__ __forceinline__ void init(const bf16* base, long ld_, int T, int col0, int tid) {
+    ld = ld_;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + col0), (short)0,
+                                             (int)min(((long)(T - 1) * ld_ + D) * 2, (long)0x7fffffff), 0x00020000);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int r = r0 + rb * 8 + j;
-      in[j] = r < T ? *reinterpret_cast<const uint4*>(g + (long)r * ld + col0 + db * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t o[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t lo = word_of(in[2 * j], c >> 1), hi = word_of(in[2 * j + 1], c >> 1);
-        o[j] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      bf16* dst = s + (db * 8 + c) * Cfg<D>::TP + rb * 8;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
-      *reinterpret_cast<uint2*>(dst + 4) = make_uint2(o[2], o[3]);
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + i * 256;
+      const int row = c / RowTile<D>::CH, ch = c % RowTile<D>::CH;
+      voff[i] = (unsigned)(((long)row * ld_ + ch * 8) * 2);
+      soff[i] = RowTile<D>::off(row, ch);
     }
   }
-}
+  // The whole byte offset is in the per-lane offset, which the range check
+  // covers: rows at or past T read zeros.
+  __device__ __forceinline__ void load(int r0) {
+    const unsigned ro = (unsigned)r0 * (unsigned)(ld * 2);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(voff[i] + ro), 0, 0);
+      r[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* s) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) *reinterpret_cast<uint4*>(s + soff[i]) = r[i];
+  }
+};
 
-// A-operand fragment of a transposed tile: rows d (lane%32 of tile dt), the 8
-// k-slots of k-step group `base` in the lanes' hold order: base + 4h + 0..3
-// and base + 8 + 4h + 0..3 (h = lane / 32).
+// B/A operand fragment of rows r0 + lane%32 of a RowTile, k-step ks over D.
 template <int D>
-__device__ __forceinline__ bf16x8_t frag_t(const bf16* __restrict__ s, int dt, int base, int lane) {
-  const bf16* p = s + (dt * 32 + (lane & 31)) * Cfg<D>::TP + base + (lane >> 5) * 4;
-  uint2 a = *reinterpret_cast<const uint2*>(p);
-  uint2 b = *reinterpret_cast<const uint2*>(p + 8);
-  return as_frag(make_uint4(a.x, a.y, b.x, b.y));
+__device__ __forceinline__ bf16x8_t frag_r(const bf16* s, int r0, int ks, int lane) {
+  const int r = r0 + (lane & 31), c = ks * 2 + (lane >> 5);
+  return *reinterpret_cast<const bf16x8_t*>(s + RowTile<D>::off(r, c));
 }
 
-// Operand fragment of a row-major tile: row r0 + lane%32, k-step ks.
+// A operand "rows = d (tile dt), k-slots = 16 tile rows from base" of a
+// RowTile, in the lanes' score order: slots 0..3 <-> rows base + 4h + 0..3,
+// slots 4..7 <-> rows base + 8 + 4h + 0..3 (h = lane / 32). Two transpose
+// reads: within each 16-lane group, source lane i reads row k0 + i/4, columns
+// d0 + 4 (i % 4) .. + 3 and receives column d0 + i of rows k0 .. k0 + 3.
 template <int D>
-__device__ __forceinline__ bf16x8_t frag_r(const bf16* __restrict__ s, int r0, int ks, int lane) {
-  return *reinterpret_cast<const bf16x8_t*>(s + (r0 + (lane & 31)) * Cfg<D>::RP + ks * 16 + (lane >> 5) * 8);
+__device__ __forceinline__ bf16x8_t frag_t(const bf16* s, int dt, int base, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int d = dt * 32 + (g & 1) * 16 + 4 * (i & 3);
+  const int k = base + (g >> 1) * 4 + (i >> 2);
+  const int c = d >> 3, h = d & 7;
+  bf16x4_t lo = ds_read_tr(s + RowTile<D>::off(k, c) + h);
+  bf16x4_t hi = ds_read_tr(s + RowTile<D>::off(k + 8, c) + h);
+  return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Register fragments of rows row0 + lane%32 straight from global memory.
+// Register fragments of row `row` (zero past T) straight from global memory.
 template <int D>
 __device__ __forceinline__ void frags_global(bf16x8_t* f, const bf16* __restrict__ g, long ld, int row, int T,
                                              int col0, int lane) {
 #pragma unroll
-  for (int ks = 0; ks < Cfg<D>::KS; ++ks) {
+  for (int ks = 0; ks < D / 16; ++ks) {
     uint4 v = make_uint4(0, 0, 0, 0);
     if (row < T) v = *reinterpret_cast<const uint4*>(g + (long)row * ld + col0 + ks * 16 + (lane >> 5) * 8);
     f[ks] = as_frag(v);
@@ -130,8 +147,7 @@ __device__ __forceinline__ void frags_global(bf16x8_t* f, const bf16* __restrict
 
 __device__ __forceinline__ int acc_row(int e, int lane) { return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3); }
 
-// Store 16 accumulators of one 32-wide d tile for row `row`: d = dt*32 +
-// acc_row(e) -> four 8-byte stores of 4 consecutive bf16.
+// Store the 16 accumulators of one 32-wide d tile of row `dst`: d = acc_row(e).
 __device__ __forceinline__ void store_acc_row(bf16* __restrict__ dst, const f32x16_t& acc, float scale, int lane) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -142,16 +158,21 @@ __device__ __forceinline__ void store_acc_row(bf16* __restrict__ dst, const f32x
   }
 }
 
+__device__ __forceinline__ void zero(f32x16_t& a) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) a[e] = 0.f;
+}
+
 // ----------------------------------------------------------------- forward
 template <int D>
 __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
-  using C_ = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sK[64 * C_::RP];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[D * C_::TP];
+  constexpr int KS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][RowTile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][RowTile<D>::ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = a.T, H = a.H, C = H * D;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int q0 = blockIdx.x * 128;
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * 128;  // longest rows first
   const long ld = 3L * C;
   const bf16* base = reinterpret_cast<const bf16*>(a.qkv) + (long)b * T * ld;
   const int32_t* start = a.start + (long)b * T;
@@ -159,42 +180,48 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   const int q = q0 + w * 32 + (lane & 31);
   const bool qv = q < T;
   const int qs = qv ? start[q] : 0;
-  bf16x8_t qf[C_::KS];
+  bf16x8_t qf[KS];
   frags_global<D>(qf, base, ld, q, T, h * D, lane);
+
+  TileLoad<D> lk, lv;
+  lk.init(base, ld, T, C + h * D, tid);
+  lv.init(base, ld, T, 2 * C + h * D, tid);
 
   const float sc = kLog2e / sqrtf((float)D);
   float m = -INFINITY, l = 0.f;
-  f32x16_t acc_o[C_::DT];
+  f32x16_t acc_o[DT];
 #pragma unroll
-  for (int dt = 0; dt < C_::DT; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc_o[dt][e] = 0.f;
+  for (int dt = 0; dt < DT; ++dt) zero(acc_o[dt]);
 
-  const int k_lo = start[q0];
-  const int k_hi = min(T, q0 + 128) - 1;
-  for (int kt = k_lo / 64; kt <= k_hi / 64; ++kt) {
+  const int kt0 = start[q0] / 64, kt1 = (min(T, q0 + 128) - 1) / 64;
+  lk.load(kt0 * 64);
+  lv.load(kt0 * 64);
+  lk.store(sK[0]);
+  lv.store(sV[0]);
+  __syncthreads();
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
     const int k0 = kt * 64;
-    __syncthreads();
-    load_rows<D>(sK, base, ld, k0, T, C + h * D, tid);
-    load_cols<D>(sVt, base, ld, k0, T, 2 * C + h * D, tid);
-    __syncthreads();
-    // S^T for 2 sub-tiles of 32 keys
+    if (kt < kt1) {
+      lk.load(k0 + 64);
+      lv.load(k0 + 64);
+    }
     f32x16_t s[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      zero(s[sub]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[sub][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C_::KS; ++ks)
-        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sK, sub * 32, ks, lane), qf[ks], s[sub], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks)
+        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sK[cur], sub * 32, ks, lane), qf[ks], s[sub], 0,
+                                                         0, 0);
     }
     float mt = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        int j = k0 + sub * 32 + acc_row(e, lane);
-        float v = (qv && j >= qs && j <= q) ? s[sub][e] * sc : -INFINITY;
+        const int j = k0 + sub * 32 + acc_row(e, lane);
+        const float v = (qv && j >= qs && j <= q) ? s[sub][e] * sc : -INFINITY;
         s[sub][e] = v;
         mt = fmaxf(mt, v);
       }
@@ -207,81 +234,79 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float v = (mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[sub][e] - mn);
+        const float v = (mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[sub][e] - mn);
         p[sub][e] = v;
         ls += v;
       }
     l = l * corr + ls;
     m = mn;
 #pragma unroll
-    for (int dt = 0; dt < C_::DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc_o[dt][e] *= corr;
-    // O^T += V^T P^T over 4 k-steps of 16 keys
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      bf16x8_t pf = as_frag(pack_frag(&p[st >> 1][(st & 1) * 8]));
+      const bf16x8_t pf = as_frag(pack_frag(&p[st >> 1][(st & 1) * 8]));
 #pragma unroll
-      for (int dt = 0; dt < C_::DT; ++dt)
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sVt, dt, st * 16, lane), pf, acc_o[dt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt)
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sV[cur], dt, st * 16, lane), pf, acc_o[dt], 0,
+                                                            0, 0);
     }
+    if (kt < kt1) {
+      lk.store(sK[cur ^ 1]);
+      lv.store(sV[cur ^ 1]);
+    }
+    __syncthreads();
   }
   l += __shfl_xor(l, 32, 64);
   if (qv) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     bf16* orow = reinterpret_cast<bf16*>(a.o) + ((long)b * T + q) * C + h * D;
 #pragma unroll
-    for (int dt = 0; dt < C_::DT; ++dt) store_acc_row(orow + dt * 32, acc_o[dt], inv, lane);
+    for (int dt = 0; dt < DT; ++dt) store_acc_row(orow + dt * 32, acc_o[dt], inv, lane);
     if (lane < 32) a.lse[((long)b * H + h) * T + q] = (m + __log2f(l)) * 0.6931471805599453f;
   }
 }
 
 // ---------------------------------------------------------------- delta
-// delta_i = dO_i . O_i, one wavefront per (row, head), D/8 lanes x 8 values.
+// delta_i = dO_i . O_i, D/8 lanes per (row, head), 8 values each.
 template <int D>
 __global__ void __launch_bounds__(256) attn_delta_kernel_v(AttnArgs a) {
-  const int lane = threadIdx.x & 63;
-  constexpr int LPR = D / 8;  // lanes per (row, head)
+  constexpr int LPR = D / 8;
   const long idx = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;  // (b, t, h) flat
   const int sub = threadIdx.x % LPR;
   const int H = a.H, T = a.T, C = H * D;
   const long total = (long)a.B * T * H;
   float v = 0.f;
   if (idx < total) {
-    const int hh = idx % H;
-    const long row = idx / H;
-    const long off = row * C + hh * D + sub * 8;
-    uint4 x = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16*>(a.dout) + off);
-    uint4 y = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16*>(a.o) + off);
+    const long off = (idx / H) * C + (idx % H) * D + sub * 8;
+    const uint4 x = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16*>(a.dout) + off);
+    const uint4 y = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16*>(a.o) + off);
+    const uint32_t xa[4] = {x.x, x.y, x.z, x.w}, ya[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      uint32_t xa = word_of(x, k), ya = word_of(y, k);
-      v += __uint_as_float(xa << 16) * __uint_as_float(ya << 16);
-      v += __uint_as_float(xa & 0xffff0000u) * __uint_as_float(ya & 0xffff0000u);
+      v += __uint_as_float(xa[k] << 16) * __uint_as_float(ya[k] << 16);
+      v += __uint_as_float(xa[k] & 0xffff0000u) * __uint_as_float(ya[k] & 0xffff0000u);
     }
   }
 #pragma unroll
   for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   if (idx < total && sub == 0) {
-    const int hh = idx % H;
-    const long row = idx / H;
-    const long bb = row / T, t = row % T;
-    a.delta[(bb * H + hh) * T + t] = v;
+    const long row = idx / H, bb = row / T, t = row % T;
+    a.delta[(bb * H + idx % H) * T + t] = v;
   }
-  (void)lane;
 }
 
 // ------------------------------------------------------------ dQ pass
 template <int D>
 __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
-  using C_ = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sK[64 * C_::RP];
-  __shared__ __attribute__((aligned(16))) bf16 sV[64 * C_::RP];
-  __shared__ __attribute__((aligned(16))) bf16 sKt[D * C_::TP];
+  constexpr int KS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][RowTile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][RowTile<D>::ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = a.T, H = a.H, C = H * D;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int q0 = blockIdx.x * 128;
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * 128;  // longest rows first
   const long ld = 3L * C;
   const bf16* base = reinterpret_cast<const bf16*>(a.qkv) + (long)b * T * ld;
   const bf16* dob = reinterpret_cast<const bf16*>(a.dout) + (long)b * T * C;
@@ -292,74 +317,82 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
   const int qs = qv ? start[q] : 0;
   const float lse2 = qv ? a.lse[((long)b * H + h) * T + q] * kLog2e : 0.f;
   const float dlt = qv ? a.delta[((long)b * H + h) * T + q] : 0.f;
-  bf16x8_t qf[C_::KS], df[C_::KS];
+  bf16x8_t qf[KS], df[KS];
   frags_global<D>(qf, base, ld, q, T, h * D, lane);
   frags_global<D>(df, dob, C, q, T, h * D, lane);
+  TileLoad<D> lk, lv;
+  lk.init(base, ld, T, C + h * D, tid);
+  lv.init(base, ld, T, 2 * C + h * D, tid);
   const float sc = kLog2e / sqrtf((float)D);
-  f32x16_t acc[C_::DT];
+  f32x16_t acc[DT];
 #pragma unroll
-  for (int dt = 0; dt < C_::DT; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+  for (int dt = 0; dt < DT; ++dt) zero(acc[dt]);
 
-  const int k_lo = start[q0];
-  const int k_hi = min(T, q0 + 128) - 1;
-  for (int kt = k_lo / 64; kt <= k_hi / 64; ++kt) {
+  const int kt0 = start[q0] / 64, kt1 = (min(T, q0 + 128) - 1) / 64;
+  lk.load(kt0 * 64);
+  lv.load(kt0 * 64);
+  lk.store(sK[0]);
+  lv.store(sV[0]);
+  __syncthreads();
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
     const int k0 = kt * 64;
-    __syncthreads();
-    load_rows<D>(sK, base, ld, k0, T, C + h * D, tid);
-    load_rows<D>(sV, base, ld, k0, T, 2 * C + h * D, tid);
-    load_cols<D>(sKt, base, ld, k0, T, C + h * D, tid);
-    __syncthreads();
+    if (kt < kt1) {
+      lk.load(k0 + 64);
+      lv.load(k0 + 64);
+    }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       f32x16_t s, dp;
+      zero(s);
+      zero(dp);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C_::KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sK, sub * 32, ks, lane), qf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sV, sub * 32, ks, lane), df[ks], dp, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sK[cur], sub * 32, ks, lane), qf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sV[cur], sub * 32, ks, lane), df[ks], dp, 0, 0, 0);
       }
       float ds[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        int j = k0 + sub * 32 + acc_row(e, lane);
-        float p = (qv && j >= qs && j <= q) ? __builtin_amdgcn_exp2f(s[e] * sc - lse2) : 0.f;
+        const int j = k0 + sub * 32 + acc_row(e, lane);
+        const float p = (qv && j >= qs && j <= q) ? __builtin_amdgcn_exp2f(s[e] * sc - lse2) : 0.f;
         ds[e] = p * (dp[e] - dlt);
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        bf16x8_t f = as_frag(pack_frag(&ds[st * 8]));
+        const bf16x8_t f = as_frag(pack_frag(&ds[st * 8]));
 #pragma unroll
-        for (int dt = 0; dt < C_::DT; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sKt, dt, sub * 32 + st * 16, lane), f, acc[dt],
-                                                            0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sK[cur], dt, sub * 32 + st * 16, lane), f,
+                                                            acc[dt], 0, 0, 0);
       }
     }
+    if (kt < kt1) {
+      lk.store(sK[cur ^ 1]);
+      lv.store(sV[cur ^ 1]);
+    }
+    __syncthreads();
   }
   if (qv) {
     const float scale = 1.0f / sqrtf((float)D);
     bf16* row = reinterpret_cast<bf16*>(a.dqkv) + ((long)b * T + q) * ld + h * D;
 #pragma unroll
-    for (int dt = 0; dt < C_::DT; ++dt) store_acc_row(row + dt * 32, acc[dt], scale, lane);
+    for (int dt = 0; dt < DT; ++dt) store_acc_row(row + dt * 32, acc[dt], scale, lane);
   }
 }
 
 // ---------------------------------------------------------- dK / dV pass
 template <int D>
 __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
-  using C_ = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[64 * C_::RP];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[64 * C_::RP];
-  __shared__ __attribute__((aligned(16))) bf16 sQt[D * C_::TP];
-  __shared__ __attribute__((aligned(16))) bf16 sdOt[D * C_::TP];
-  __shared__ float sL[64], sD[64];
-  __shared__ int sS[64];
+  constexpr int KS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2][RowTile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[2][RowTile<D>::ELEMS];
+  __shared__ float sL[2][64], sD[2][64];
+  __shared__ int sS[2][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = a.T, H = a.H, C = H * D;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int kb0 = blockIdx.x * 128;
+  const int kb0 = blockIdx.x * 128;  // keys near the row start see the most queries: dispatched first
   const long ld = 3L * C;
   const bf16* base = reinterpret_cast<const bf16*>(a.qkv) + (long)b * T * ld;
   const bf16* dob = reinterpret_cast<const bf16*>(a.dout) + (long)b * T * C;
@@ -369,72 +402,88 @@ __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
 
   const int key = kb0 + w * 32 + (lane & 31);
   const bool kv = key < T;
-  bf16x8_t kf[C_::KS], vf[C_::KS];
+  bf16x8_t kf[KS], vf[KS];
   frags_global<D>(kf, base, ld, key, T, C + h * D, lane);
   frags_global<D>(vf, base, ld, key, T, 2 * C + h * D, lane);
+  TileLoad<D> lq, ldo;
+  lq.init(base, ld, T, h * D, tid);
+  ldo.init(dob, C, T, h * D, tid);
   const float sc = kLog2e / sqrtf((float)D);
-  f32x16_t dk[C_::DT], dv[C_::DT];
+  f32x16_t dk[DT], dv[DT];
 #pragma unroll
-  for (int dt = 0; dt < C_::DT; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) dk[dt][e] = dv[dt][e] = 0.f;
-
-  const int q_lo = kb0;
-  const int q_hi = a.end[(long)b * T + min(T, kb0 + 128) - 1] - 1;
-  for (int qt = q_lo / 64; qt <= q_hi / 64; ++qt) {
-    const int qb = qt * 64;
-    __syncthreads();
-    load_rows<D>(sQ, base, ld, qb, T, h * D, tid);
-    load_rows<D>(sdO, dob, C, qb, T, h * D, tid);
-    load_cols<D>(sQt, base, ld, qb, T, h * D, tid);
-    load_cols<D>(sdOt, dob, C, qb, T, h * D, tid);
+  for (int dt = 0; dt < DT; ++dt) {
+    zero(dk[dt]);
+    zero(dv[dt]);
+  }
+  auto load_vec = [&](int qb, int stage) {
     if (tid < 64) {
-      int qq = qb + tid;
-      bool ok = qq < T;
-      sL[tid] = ok ? lse[qq] * kLog2e : 0.f;
-      sD[tid] = ok ? dl[qq] : 0.f;
-      sS[tid] = ok ? start[qq] : T;  // rows beyond T admit no key
+      const int qq = qb + tid;
+      const bool ok = qq < T;
+      sL[stage][tid] = ok ? lse[qq] * kLog2e : 0.f;
+      sD[stage][tid] = ok ? dl[qq] : 0.f;
+      sS[stage][tid] = ok ? start[qq] : T;  // rows past T admit no key
     }
-    __syncthreads();
+  };
+
+  const int qt0 = kb0 / 64;
+  const int qt1 = (a.end[(long)b * T + min(T, kb0 + 128) - 1] - 1) / 64;
+  lq.load(qt0 * 64);
+  ldo.load(qt0 * 64);
+  lq.store(sQ[0]);
+  ldo.store(sdO[0]);
+  load_vec(qt0 * 64, 0);
+  __syncthreads();
+  for (int qt = qt0; qt <= qt1; ++qt) {
+    const int cur = (qt - qt0) & 1;
+    const int qb = qt * 64;
+    if (qt < qt1) {
+      lq.load(qb + 64);
+      ldo.load(qb + 64);
+    }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       f32x16_t s, dp;
+      zero(s);
+      zero(dp);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C_::KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sQ, sub * 32, ks, lane), kf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sdO, sub * 32, ks, lane), vf[ks], dp, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sQ[cur], sub * 32, ks, lane), kf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sdO[cur], sub * 32, ks, lane), vf[ks], dp, 0, 0, 0);
       }
       float p[16], ds[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        int r = sub * 32 + acc_row(e, lane);
-        int qq = qb + r;
-        bool ok = kv && key >= sS[r] && key <= qq;
-        float pv = ok ? __builtin_amdgcn_exp2f(s[e] * sc - sL[r]) : 0.f;
+        const int r = sub * 32 + acc_row(e, lane);
+        const bool ok = kv && key >= sS[cur][r] && key <= qb + r;
+        const float pv = ok ? __builtin_amdgcn_exp2f(s[e] * sc - sL[cur][r]) : 0.f;
         p[e] = pv;
-        ds[e] = pv * (dp[e] - sD[r]);
+        ds[e] = pv * (dp[e] - sD[cur][r]);
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        bf16x8_t pf = as_frag(pack_frag(&p[st * 8]));
-        bf16x8_t sf = as_frag(pack_frag(&ds[st * 8]));
+        const bf16x8_t pf = as_frag(pack_frag(&p[st * 8]));
+        const bf16x8_t sf = as_frag(pack_frag(&ds[st * 8]));
 #pragma unroll
-        for (int dt = 0; dt < C_::DT; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sdOt, dt, sub * 32 + st * 16, lane), pf, dv[dt],
-                                                           0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sQt, dt, sub * 32 + st * 16, lane), sf, dk[dt],
-                                                           0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt) {
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sdO[cur], dt, sub * 32 + st * 16, lane), pf,
+                                                           dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sQ[cur], dt, sub * 32 + st * 16, lane), sf,
+                                                           dk[dt], 0, 0, 0);
         }
       }
     }
+    if (qt < qt1) {
+      lq.store(sQ[cur ^ 1]);
+      ldo.store(sdO[cur ^ 1]);
+      load_vec(qb + 64, cur ^ 1);
+    }
+    __syncthreads();
   }
   if (kv) {
     const float scale = 1.0f / sqrtf((float)D);
     bf16* row = reinterpret_cast<bf16*>(a.dqkv) + ((long)b * T + key) * ld;
 #pragma unroll
-    for (int dt = 0; dt < C_::DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt) {
       store_acc_row(row + C + h * D + dt * 32, dk[dt], scale, lane);
       store_acc_row(row + 2 * C + h * D + dt * 32, dv[dt], 1.0f, lane);
     }
@@ -450,8 +499,7 @@ int fwd(const AttnArgs& a, hipStream_t s) {
 
 template <int D>
 int bwd(const AttnArgs& a, hipStream_t s) {
-  long rows = (long)a.B * a.T * a.H;
-  long threads = rows * (D / 8);
+  const long threads = (long)a.B * a.T * a.H * (D / 8);
   hipLaunchKernelGGL(attn_delta_kernel_v<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
   dim3 grid((a.T + 127) / 128, a.B * a.H);
   hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, a);

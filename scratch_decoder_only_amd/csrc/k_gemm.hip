@@ -170,6 +170,7 @@ struct Tile {
   unsigned voff[NL];  // byte offset of the chunk from the tile origin, without the K-step term
   int kin[NL];        // K offset of the chunk inside the K step
   int soff[NL];       // LDS element offset of the chunk
+  bool cok[NL];       // the chunk's 8 columns exist (M/N-contiguous operand)
   unsigned kstride;   // bytes per unit of K
 
   // Per-thread addressing, computed once per block. The buffer starts at the
@@ -201,16 +202,18 @@ struct Tile {
         kin[i] = k;
         soff[i] = k * PITCH + ((q ^ ((k & 3) << 2)) << 3);
       }
+      cok[i] = KC || row0 + (c % (ROWS / 8)) * 8 < rows_total;
     }
   }
 
-  // Loads of one K step (k0 .. k0 + 63, nothing at or past k_end).
+  // Loads of one K step (k0 .. k0 + 63, nothing at or past k_end). The whole
+  // byte offset is in the per-lane offset, which the range check covers.
   __device__ __forceinline__ void load(int k0, int k_end) {
-    const int so = (int)((unsigned)k0 * kstride);
+    const unsigned ko = (unsigned)k0 * kstride;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const unsigned vo = (k0 + kin[i] < k_end) ? voff[i] : kOutOfRange;
-      u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vo, so, 0);
+      const unsigned vo = (cok[i] && k0 + kin[i] < k_end) ? voff[i] + ko : kOutOfRange;
+      u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vo, 0, 0);
       r[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
