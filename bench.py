@@ -155,10 +155,13 @@ def main():
         torch.cuda.synchronize()
         prof = model.profile_read(reset=True)
         model.profile(False)
+        # algorithmic attention flops per allowed pair: forward 4 D (S, PV);
+        # backward 8 D, attributed 6 D to the dK/dV pass (dP, dV, dK) and 2 D to
+        # the dQ pass (dQ); score recomputation is not algorithmic work
+        share = {"attn_fwd": 1.0 / 3.0, "attn_bwd_dq": 1.0 / 6.0, "attn_bwd_dkv": 1.0 / 2.0}
         for k, v in prof.items():
-            if k.startswith("attn"):
-                # attention flops: forward 4 D, backward 8 D per allowed pair
-                v["flops"] = attn_f / 3.0 * (1.0 if k == "attn_fwd" else 2.0) * v["launches"] / shape.n_layers
+            if k in share:
+                v["flops"] = attn_f * share[k] * v["launches"] / shape.n_layers
         total_ms = sum(v["ms"] for v in prof.values())
         mm = {k: v for k, v in prof.items() if k.startswith("gemm") or k.startswith("attn")}
         mm_flops = sum(v["flops"] for v in mm.values())

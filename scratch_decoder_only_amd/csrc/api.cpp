@@ -431,8 +431,10 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   float* pdg = m->ln_part;
   float* pdb = m->ln_part + ln_blocks * C;
   auto ln_bwd = [&](const float* x, const float* mu, const float* r, long g_off, long b_off, const float* g_in) {
-    Lr.run("layernorm_bwd", 0, Mf * C * (4 * 4 + A), [&] {
+    Lr.run("layernorm_bwd", 0, Mf * C * ((g_in ? 4 * 4 : 3 * 4) + A), [&] {
       launch_ln_bwd<E>(m->dy, x, mu, r, m->P_(g_off), (int)M, (int)C, g_in, m->g, g_act, pdg, pdb, s);
+    });
+    Lr.run("layernorm_bwd_reduce", 0, 2.0 * ln_blocks * C * 4, [&] {
       launch_colsum_partials(pdg, pdb, (int)ln_blocks, (int)C, m->grads + g_off, m->grads + b_off, s);
     });
   };
@@ -474,7 +476,11 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
       AttnArgs at{};
       at.qkv = qkv; at.start = m->start; at.end = m->end; at.B = B; at.T = T; at.H = (int)H; at.D = m->D;
       at.o = o; at.lse = m->lse + l * M * H; at.dout = dO; at.delta = m->delta; at.dqkv = dbig;
-      Lr.run("attn_bwd", 0, 0, [&] { rc |= m->bf ? attn_bwd_bf16(at, s) : attn_bwd_f32(at, s); });
+      static const char* names[3] = {"attn_bwd_delta", "attn_bwd_dq", "attn_bwd_dkv"};
+      for (int part = 0; part < 3; ++part)
+        Lr.run(names[part], 0, part == 0 ? Mf * C * 2 * A : 0, [&] {
+          rc |= m->bf ? attn_bwd_part_bf16(at, part, s) : attn_bwd_part_f32(at, part, s);
+        });
     }
     Lr.run("gemm_qkv_bwd_dw", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, dw_op(dbig, M, 3 * C, y1, C, m->grads + b.w_qkv), s); });
     Lr.run("bias_grad", 0, Mf * 3 * C * A, [&] { launch_colsum<E>(dbig, 3 * C, (int)M, (int)(3 * C), m->col_part, m->grads + b.b_qkv, s); });

@@ -498,12 +498,16 @@ int fwd(const AttnArgs& a, hipStream_t s) {
 }
 
 template <int D>
-int bwd(const AttnArgs& a, hipStream_t s) {
-  const long threads = (long)a.B * a.T * a.H * (D / 8);
-  hipLaunchKernelGGL(attn_delta_kernel_v<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+int bwd_part(const AttnArgs& a, int part, hipStream_t s) {
   dim3 grid((a.T + 127) / 128, a.B * a.H);
-  hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL(attn_dkv_kernel<D>, grid, dim3(256), 0, s, a);
+  if (part == 0) {
+    const long threads = (long)a.B * a.T * a.H * (D / 8);
+    hipLaunchKernelGGL(attn_delta_kernel_v<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+  } else if (part == 1) {
+    hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(attn_dkv_kernel<D>, grid, dim3(256), 0, s, a);
+  }
   return 0;
 }
 
@@ -515,10 +519,16 @@ int attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
   return -1;
 }
 
-int attn_bwd_bf16(const AttnArgs& a, hipStream_t s) {
-  if (a.D == 64) return bwd<64>(a, s);
-  if (a.D == 32) return bwd<32>(a, s);
+int attn_bwd_part_bf16(const AttnArgs& a, int part, hipStream_t s) {
+  if (a.D == 64) return bwd_part<64>(a, part, s);
+  if (a.D == 32) return bwd_part<32>(a, part, s);
   return -1;
+}
+
+int attn_bwd_bf16(const AttnArgs& a, hipStream_t s) {
+  int rc = 0;
+  for (int part = 0; part < 3; ++part) rc |= attn_bwd_part_bf16(a, part, s);
+  return rc;
 }
 
 }  // namespace lm

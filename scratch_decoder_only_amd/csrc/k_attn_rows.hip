@@ -131,17 +131,22 @@ static int attn_fwd_rows(const AttnArgs& a, hipStream_t s) {
 }
 
 template <typename E>
-static int attn_bwd_rows(const AttnArgs& a, hipStream_t s) {
+static int attn_bwd_rows_part(const AttnArgs& a, int part, hipStream_t s) {
   if (a.D > 64) return -1;
   long rows = (long)a.B * a.H * a.T;
   dim3 g((unsigned)((rows + 3) / 4)), b(256);
-  hipLaunchKernelGGL(attn_delta_kernel<E>, g, b, 0, s, a);
-  hipLaunchKernelGGL(attn_dq_rows_kernel<E>, g, b, 0, s, a);
-  hipLaunchKernelGGL(attn_dkv_rows_kernel<E>, g, b, 0, s, a);
+  if (part == 0) hipLaunchKernelGGL(attn_delta_kernel<E>, g, b, 0, s, a);
+  else if (part == 1) hipLaunchKernelGGL(attn_dq_rows_kernel<E>, g, b, 0, s, a);
+  else hipLaunchKernelGGL(attn_dkv_rows_kernel<E>, g, b, 0, s, a);
   return 0;
 }
 
 int attn_fwd_f32(const AttnArgs& a, hipStream_t s) { return attn_fwd_rows<float>(a, s); }
-int attn_bwd_f32(const AttnArgs& a, hipStream_t s) { return attn_bwd_rows<float>(a, s); }
+int attn_bwd_part_f32(const AttnArgs& a, int part, hipStream_t s) { return attn_bwd_rows_part<float>(a, part, s); }
+int attn_bwd_f32(const AttnArgs& a, hipStream_t s) {
+  int rc = 0;
+  for (int part = 0; part < 3; ++part) rc |= attn_bwd_part_f32(a, part, s);
+  return rc;
+}
 
 }  // namespace lm

@@ -168,34 +168,39 @@ template void launch_ln_bwd<float>(const float*, const float*, const float*, con
 template void launch_ln_bwd<bf16>(const float*, const float*, const float*, const float*, const float*, int, int,
                                   const float*, float*, bf16*, float*, float*, hipStream_t);
 
-// out[c] = sum over p < P of part[p][c] in a fixed order: thread (c, r) of a
-// block sums p = r, r + 4, ... for column c, then the four partial sums are
-// added in r order. Two vectors at once (the dg and db partials of one
-// LayerNorm).
+// out[c] = sum over p < P of part[p][c] in a fixed order: a block covers 16
+// columns with 16 row groups; thread (c, r) sums p = r, r + 16, ... for its
+// column, then the 16 group sums are added in r order. Two vectors at once
+// (the dg and db partials of one LayerNorm).
 __global__ void __launch_bounds__(256) colsum_partials_kernel(const float* __restrict__ pa, const float* __restrict__ pb,
                                                               int P, int C, float* __restrict__ oa,
                                                               float* __restrict__ ob) {
-  __shared__ float sa[4][64], sb[4][64];
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63), r = threadIdx.x >> 6;
+  __shared__ float sa[16][17], sb[16][17];
+  const int cc = threadIdx.x & 15, r = threadIdx.x >> 4;
+  const int c = blockIdx.x * 16 + cc;
   float a = 0.f, b = 0.f;
   if (c < C)
-    for (int p = r; p < P; p += 4) {
+    for (int p = r; p < P; p += 16) {
       a += pa[(long)p * C + c];
       if (pb) b += pb[(long)p * C + c];
     }
-  sa[r][threadIdx.x & 63] = a;
-  sb[r][threadIdx.x & 63] = b;
+  sa[r][cc] = a;
+  sb[r][cc] = b;
   __syncthreads();
   if (r == 0 && c < C) {
-    const int t = threadIdx.x;
-    oa[c] = ((sa[0][t] + sa[1][t]) + sa[2][t]) + sa[3][t];
-    if (ob) ob[c] = ((sb[0][t] + sb[1][t]) + sb[2][t]) + sb[3][t];
+    float ta = 0.f, tb = 0.f;
+    for (int k = 0; k < 16; ++k) {
+      ta += sa[k][cc];
+      tb += sb[k][cc];
+    }
+    oa[c] = ta;
+    if (ob) ob[c] = tb;
   }
 }
 
 void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob,
                             hipStream_t s) {
-  hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + 63) / 64), dim3(256), 0, s, pa, pb, P, C, oa, ob);
+  hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + 15) / 16), dim3(256), 0, s, pa, pb, P, C, oa, ob);
 }
 
 // Column sums of an [M, N] matrix (bias gradients), N a multiple of 4. Stage

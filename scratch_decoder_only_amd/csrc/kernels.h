@@ -97,8 +97,12 @@ struct AttnArgs {
   void* dqkv;        // [B*T, 3C]
 };
 int attn_fwd_bf16(const AttnArgs& a, hipStream_t s);
-int attn_bwd_bf16(const AttnArgs& a, hipStream_t s);
 int attn_fwd_f32(const AttnArgs& a, hipStream_t s);
+// Backward in three launches: delta = rowsum(dO * O), the dQ pass, the dK/dV
+// pass (part 0, 1, 2); attn_bwd_* runs all three.
+int attn_bwd_part_bf16(const AttnArgs& a, int part, hipStream_t s);
+int attn_bwd_part_f32(const AttnArgs& a, int part, hipStream_t s);
+int attn_bwd_bf16(const AttnArgs& a, hipStream_t s);
 int attn_bwd_f32(const AttnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------ embedding backward
