@@ -18,6 +18,7 @@
 // the fp32 GEMM is a plain LDS-tiled FMA kernel (64 x 64 tile, 4 x 4 per
 // thread).
 #include <cstdlib>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -206,23 +207,26 @@ struct Tile {
     }
   }
 
-  // Loads of one K step (k0 .. k0 + 63, nothing at or past k_end). The whole
-  // byte offset is in the per-lane offset, which the range check covers.
-  __device__ __forceinline__ void load(int k0, int k_end) {
+  // Loads of one K step (k0 .. k0 + 63, nothing at or past k_end) into rr.
+  // The whole byte offset is in the per-lane offset, which the range check
+  // covers.
+  __device__ __forceinline__ void load(uint4* rr, int k0, int k_end) const {
     const unsigned ko = (unsigned)k0 * kstride;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const unsigned vo = (cok[i] && k0 + kin[i] < k_end) ? voff[i] + ko : kOutOfRange;
       u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vo, 0, 0);
-      r[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      rr[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
+  __device__ __forceinline__ void load(int k0, int k_end) { load(r, k0, k_end); }
 
-  __device__ __forceinline__ void store(bf16* __restrict__ s, int tid) const {
+  __device__ __forceinline__ void store(const uint4* rr, bf16* __restrict__ s, int tid) const {
 #pragma unroll
     for (int i = 0; i < NL; ++i)
-      if (FULL || tid + i * NT < CHUNKS) *reinterpret_cast<uint4*>(s + soff[i]) = r[i];
+      if (FULL || tid + i * NT < CHUNKS) *reinterpret_cast<uint4*>(s + soff[i]) = rr[i];
   }
+  __device__ __forceinline__ void store(bf16* __restrict__ s, int tid) const { store(r, s, tid); }
 
   // MFMA 32x32x16 operand fragment: rows row0 + lane % 32, k-slots
   // ks*16 + 8 (lane / 32) .. + 7.
@@ -244,6 +248,77 @@ struct Tile {
   }
 };
 
+// Direct global -> LDS tile loads (buffer_load_dwordx4 ... lds): lane j of a
+// wavefront writes its 16 bytes at the wave's LDS base + 16 j (checked on the
+// device), so each lane fetches the global chunk that belongs at its LDS slot
+// under the swizzles above. No VGPR staging and no ds_write; the MFMA
+// fragment reads are the same as for Tile. ROWS must be 128 or 256.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int ROWS, bool KC, int NT>
+struct DTile {
+  static_assert(ROWS == 128 || ROWS == 256, "direct tiles hold 128 or 256 rows");
+  using Base = Tile<ROWS, KC, NT>;
+  static constexpr int ELEMS = Base::ELEMS;
+  static constexpr int CHUNKS = ROWS * 8;     // 16-byte chunks per K step
+  static constexpr int NW = NT / 64;          // wavefronts
+  static constexpr int NI = CHUNKS / 64 / NW; // load instructions per wavefront per K step
+  static_assert(NI * 64 * NW == CHUNKS, "whole wavefront loads");
+  __amdgpu_buffer_rsrc_t rsrc;
+  unsigned voff[NI];
+  int kin[NI];
+  bool cok[NI];
+  unsigned kstride;
+  int wbase;  // this wavefront's first 16-byte slot
+
+  __device__ __forceinline__ void init(const bf16* g, long ld, int row0, int rows_total, int K, int tid) {
+    long origin, extent;
+    if (KC) {
+      origin = (long)row0 * ld;
+      extent = (long)(rows_total - 1 - row0) * ld + K;
+    } else {
+      origin = row0;
+      extent = (long)(K - 1) * ld + (rows_total - row0);
+    }
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(g + origin), (short)0,
+                                             (int)min(extent * 2, (long)0x7fffffff), 0x00020000);
+    kstride = KC ? 2u : (unsigned)(ld * 2);
+    const int w = tid >> 6, lane = tid & 63;
+    wbase = w * NI * 64;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int pos = wbase + i * 64 + lane;  // LDS slot this lane fills
+      if (KC) {
+        const int row = pos >> 3, kc = (pos & 7) ^ ((row >> 1) & 7);
+        voff[i] = (unsigned)(((long)row * ld + kc * 8) * 2);
+        kin[i] = kc * 8;
+        cok[i] = true;
+      } else {
+        const int k = pos / (ROWS / 8), q = (pos % (ROWS / 8)) ^ ((k & 3) << 2);
+        voff[i] = (unsigned)(((long)k * ld + q * 8) * 2);
+        kin[i] = k;
+        cok[i] = row0 + q * 8 < rows_total;
+      }
+    }
+  }
+
+  // Issue the loads of the K step at k0 into LDS stage s (asynchronous).
+  __device__ __forceinline__ void load(bf16* s, int k0, int k_end) const {
+    const unsigned ko = (unsigned)k0 * kstride;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const unsigned vo = (cok[i] && k0 + kin[i] < k_end) ? voff[i] + ko : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(s + (wbase + i * 64) * 8), 16, (int)vo, 0, 0, 0);
+    }
+  }
+};
+
+// s_waitcnt with only the vector-memory counter limited to n (n < 64).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Maps the linear block id to a tile so that consecutive tiles of the grouped
 // order share an XCD (blocks are dealt to the 8 XCDs round-robin): each XCD
 // gets a contiguous range of tiles, walked GROUP_M m-tiles at a time, so an
@@ -260,9 +335,18 @@ __device__ __forceinline__ void tile_of(int b, int nb, int tiles_m, int tiles_n,
   tn = in / gsize;
 }
 
+// Waves per SIMD of a configuration: blocks that fit the 160 KB LDS times the
+// block's wavefronts, over the 4 SIMDs of a CU.
+template <int BM, int BN, int WGM, int WGN>
+struct GemmOcc {
+  static constexpr int lds = 2 * 2 * (BM * 64 + BN * 64 + (BM < 128 ? 0 : 0));
+  static constexpr int blocks = (160 * 1024) / lds > 0 ? (160 * 1024) / lds : 1;
+  static constexpr int value = blocks * WGM * WGN / 4 > 0 ? blocks * WGM * WGN / 4 : 1;
+};
+
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC>
 __global__ void __launch_bounds__(WGM * WGN * 64)
-    __attribute__((amdgpu_waves_per_eu(BM * BN > 128 * 128 ? 1 : 2, BM * BN > 128 * 128 ? 1 : 2)))
+    __attribute__((amdgpu_waves_per_eu(GemmOcc<BM, BN, WGM, WGN>::value, GemmOcc<BM, BN, WGM, WGN>::value)))
     gemm_bf16_kernel(GemmArgs p) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -298,38 +382,39 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  if (nk > 0) {
-    la.load(k_begin, k_end);
-    lb.load(k_begin, k_end);
-    la.store(sA[0], tid);
-    lb.store(sB[0], tid);
-  }
+  // Software pipeline, two K steps of global loads in flight: at step it the
+  // LDS stage it%2 holds K step it, register set (it+1)%2 holds (or is
+  // receiving) step it+1, and step it+2 is loaded into set it%2. Loads past
+  // the last step re-load it (clamped) and are never read. Within a step the
+  // fragments of k-step ks+1 are read while the MFMAs of ks run. The loop is
+  // unrolled by two so the register sets stay static.
+  uint4 ra[2][TA::NL], rb[2][TB::NL];
+  bf16x8_t af[2][TM], bfr[2][TN];
+  auto kstep = [&](int it) { return k_begin + min(it, max(nk - 1, 0)) * kBK; };
+  la.load(ra[0], kstep(0), k_end);
+  lb.load(rb[0], kstep(0), k_end);
+  la.load(ra[1], kstep(1), k_end);
+  lb.load(rb[1], kstep(1), k_end);
+  la.store(ra[0], sA[0], tid);
+  lb.store(rb[0], sB[0], tid);
   __syncthreads();
 
-  // Software pipeline: the fragments of k-step ks+1 are read from LDS while
-  // the MFMAs of k-step ks run, and the global loads of the next K tile are in
-  // flight during the whole tile. The last iteration re-loads a clamped tile
-  // (its data are never stored), which keeps the loop body branch-free.
-  bf16x8_t af[2][TM], bfr[2][TN];
-  if (nk > 0) {
+  auto step = [&](auto P_, int it) {
+    constexpr int P = decltype(P_)::value;
+    la.load(ra[P], kstep(it + 2), k_end);
+    lb.load(rb[P], kstep(it + 2), k_end);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[0][i] = la.frag(sA[0], wm * WTM + i * 32, 0, lane);
+    for (int i = 0; i < TM; ++i) af[0][i] = la.frag(sA[P], wm * WTM + i * 32, 0, lane);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[0][j] = lb.frag(sB[0], wn * WTN + j * 32, 0, lane);
-  }
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    const int kn = k_begin + min(it + 1, nk - 1) * kBK;
-    la.load(kn, k_end);
-    lb.load(kn, k_end);
+    for (int j = 0; j < TN; ++j) bfr[0][j] = lb.frag(sB[P], wn * WTN + j * 32, 0, lane);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int f = ks & 1;
       if (ks + 1 < kBK / 16) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[f ^ 1][i] = la.frag(sA[cur], wm * WTM + i * 32, ks + 1, lane);
+        for (int i = 0; i < TM; ++i) af[f ^ 1][i] = la.frag(sA[P], wm * WTM + i * 32, ks + 1, lane);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[f ^ 1][j] = lb.frag(sB[cur], wn * WTN + j * 32, ks + 1, lane);
+        for (int j = 0; j < TN; ++j) bfr[f ^ 1][j] = lb.frag(sB[P], wn * WTN + j * 32, ks + 1, lane);
       }
       // keep the reads of k-step ks+1 ahead of the MFMAs of k-step ks
       __builtin_amdgcn_sched_barrier(0);
@@ -340,13 +425,13 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    la.store(sA[cur ^ 1], tid);
-    lb.store(sB[cur ^ 1], tid);
+    la.store(ra[P ^ 1], sA[P ^ 1], tid);
+    lb.store(rb[P ^ 1], sB[P ^ 1], tid);
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TM; ++i) af[0][i] = la.frag(sA[cur ^ 1], wm * WTM + i * 32, 0, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[0][j] = lb.frag(sB[cur ^ 1], wn * WTN + j * 32, 0, lane);
+  };
+  for (int it = 0; it < nk; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < nk) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   // Epilogue through LDS: the wave row w (WGN wavefronts, WTM rows) writes its
@@ -456,6 +541,139 @@ __global__ void splitk_reduce_kernel(GemmArgs p, const float* __restrict__ part,
   }
 }
 
+// GEMM with direct-to-LDS tile loads and S LDS stages: the loads of K step
+// it + S - 1 are issued at the top of step it, and before the barrier that
+// ends step it only those of step it + 1 are waited for.
+template <int BM, int BN, int WGM, int WGN, int S, bool AK, bool BKC, int EPI, typename TC>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+    __attribute__((amdgpu_waves_per_eu((160 * 1024) / (S * 2 * 64 * (BM + BN)) * WGM * WGN / 4 > 0
+                                           ? (160 * 1024) / (S * 2 * 64 * (BM + BN)) * WGM * WGN / 4 : 1,
+                                       (160 * 1024) / (S * 2 * 64 * (BM + BN)) * WGM * WGN / 4 > 0
+                                           ? (160 * 1024) / (S * 2 * 64 * (BM + BN)) * WGM * WGN / 4 : 1)))
+    gemm_bf16_direct_kernel(GemmArgs p) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  using TA = DTile<BM, AK, NT>;
+  using TB = DTile<BN, BKC, NT>;
+  using FA = Tile<BM, AK, NT>;
+  using FB = Tile<BN, BKC, NT>;
+  __shared__ __attribute__((aligned(16))) bf16 sA[S][TA::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sB[S][TB::ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tmi, tni;
+  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tmi, tni);
+  const int m0 = tmi * BM, n0 = tni * BN;
+  const int z = blockIdx.y;
+  const int k_begin = z * p.k_split;
+  const int k_end = min(p.K, k_begin + p.k_split);
+  const int nk = (k_end - k_begin + kBK - 1) / kBK;
+  const bf16* A = reinterpret_cast<const bf16*>(p.A);
+  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+
+  TA la;
+  TB lb;
+  FA fa;
+  FB fb;
+  la.init(A, p.lda, m0, p.M, p.K, tid);
+  lb.init(B, p.ldb, n0, p.N, p.K, tid);
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // prologue: steps 0 .. S-2 in flight (clamped steps re-load the last one)
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) {
+    const int kk = k_begin + min(st, max(nk - 1, 0)) * kBK;
+    la.load(sA[st], kk, k_end);
+    lb.load(sB[st], kk, k_end);
+  }
+  wait_vmcnt<(S - 2) * (TA::NI + TB::NI)>();
+  __syncthreads();
+
+  // Every fragment of the current stage is read before the next loads are
+  // issued: the compiler waits for all outstanding LDS-DMA loads before any
+  // later LDS read, so no LDS read may follow the loads inside an iteration.
+  bf16x8_t af[kBK / 16][TM], bfr[kBK / 16][TN];
+  for (int it = 0; it < nk; ++it) {
+    const int cur = it % S;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[ks][i] = fa.frag(sA[cur], wm * WTM + i * 32, ks, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[ks][j] = fb.frag(sB[cur], wn * WTN + j * 32, ks, lane);
+    }
+    // phases pinned in order: fragment reads | next loads | MFMAs | wait + barrier
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const int nxt = (it + S - 1) % S;
+      const int kk = k_begin + min(it + S - 1, nk - 1) * kBK;
+      la.load(sA[nxt], kk, k_end);
+      lb.load(sB[nxt], kk, k_end);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // the loads of step it + 1 are the oldest outstanding ones
+    wait_vmcnt<(S - 2) * (TA::NI + TB::NI)>();
+    __syncthreads();
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Epilogue through LDS in passes of ER = min(WTM, 64) rows per wave row.
+  constexpr int CP = BN + 4;
+  constexpr int ER = WTM < 64 ? WTM : 64;
+  constexpr int TE = ER / 32;  // MFMA row tiles per pass
+  static_assert(sizeof(sA) + sizeof(sB) >= ER * CP * 4, "epilogue tile fits in the stage buffers");
+  float* sC = reinterpret_cast<float*>(&sA[0][0]);
+#pragma unroll 1
+  for (int w = 0; w < WGM; ++w) {
+#pragma unroll
+    for (int h = 0; h < TM / TE; ++h) {
+      if (wm == w) {
+#pragma unroll
+        for (int i = 0; i < TE; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int r = i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+              const int c = wn * WTN + j * 32 + (lane & 31);
+              sC[r * CP + c] = acc[h * TE + i][j][e];
+            }
+      }
+      __syncthreads();
+      for (int c = tid; c < ER * BN / 8; c += NT) {
+        const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+        const long row = m0 + w * WTM + h * ER + r, col = n0 + c8;
+        if (row < p.M_out && col < p.N) {
+          float v[8];
+          const float4 x0 = *reinterpret_cast<const float4*>(sC + r * CP + c8);
+          const float4 x1 = *reinterpret_cast<const float4*>(sC + r * CP + c8 + 4);
+          v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+          epilogue8<EPI, TC>(p, row, col, v, z);
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // ------------------------------------------------------------- dispatch
 static GemmArgs make_args(const GemmOp& op) {
   GemmArgs a;
@@ -477,9 +695,11 @@ static bool check_bf16(const GemmOp& op) {
 }
 
 // Tile configurations: 0 = 256 x 128 (4 waves of 128 x 64), 1 = 128 x 128
-// (4 waves of 64 x 64, two blocks per CU), 2 = 256 x 96 (4 waves of 64 x 96).
+// (4 waves of 64 x 64, two blocks per CU), 2 = 256 x 96 (4 waves of 64 x 96),
+// 3 = 256 x 256 (8 waves of 64 x 128, two waves per SIMD).
 static int tiles_of(const GemmOp& op, int cfg) {
-  const int BM = cfg == 1 ? 128 : 256, BN = cfg == 2 ? 96 : 128;
+  const int BM = (cfg == 1 || cfg == 4 || cfg == 5) ? 128 : 256;
+  const int BN = cfg == 2 ? 96 : (cfg == 3 || cfg == 7 || cfg == 8) ? 256 : 128;
   return ((op.M + BM - 1) / BM) * ((op.N + BN - 1) / BN);
 }
 
@@ -493,7 +713,7 @@ static int forced_cfg() {
 
 static int pick_cfg(const GemmOp& op) {
   const int f = forced_cfg();
-  if (f >= 0 && f <= 2 && (f != 2 || op.N % 96 == 0)) return f;
+  if (f >= 0 && f <= 8 && (f != 2 || op.N % 96 == 0)) return f;
   // 128 x 128 at two blocks per CU measured fastest for every GEMM of the
   // GPT-2-small-shaped step (the 256-row tiles run one block per CU)
   return 1;
@@ -506,6 +726,31 @@ int gemm_bf16_splits(const GemmOp& op) {
   int s = 1;
   while (tiles * s < 256 && op.K / (s * 2) >= 512) s *= 2;
   return s;
+}
+
+template <int BM, int BN, int WGM, int WGN, int S, bool AK, bool BKC, int EPI, typename TC>
+static void launch_bf16_direct(const GemmArgs& a, int splits, hipStream_t s) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_bf16_direct_kernel<BM, BN, WGM, WGN, S, AK, BKC, EPI, TC>), dim3(tiles, splits),
+                     dim3(WGM * WGN * 64), 0, s, a);
+}
+
+template <int BM, int BN, int WGM, int WGN, int S, bool AK, bool BKC>
+static int dispatch_bf16_direct(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
+  if (splits > 1) {
+    launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_PARTIAL, float>(a, splits, s);
+    return 0;
+  }
+  switch (op.epi) {
+    case EPI_STORE:
+      if (op.c_f32) launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_STORE, float>(a, 1, s);
+      else launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_STORE, bf16>(a, 1, s);
+      return 0;
+    case EPI_RESID: launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
+    case EPI_GELU: launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
+    case EPI_DGELU: launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
+    default: return -1;
+  }
 }
 
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC>
@@ -538,6 +783,12 @@ static int dispatch_bf16_epi(const GemmOp& op, const GemmArgs& a, int splits, hi
   switch (pick_cfg(op)) {
     case 0: return dispatch_bf16_cfg<256, 128, 2, 2, AK, BKC>(op, a, splits, s);
     case 2: return dispatch_bf16_cfg<256, 96, 4, 1, AK, BKC>(op, a, splits, s);
+    case 3: return dispatch_bf16_cfg<256, 256, 4, 2, AK, BKC>(op, a, splits, s);
+    case 4: return dispatch_bf16_direct<128, 128, 2, 2, 2, AK, BKC>(op, a, splits, s);
+    case 5: return dispatch_bf16_direct<128, 128, 2, 2, 3, AK, BKC>(op, a, splits, s);
+    case 6: return dispatch_bf16_direct<256, 128, 2, 2, 2, AK, BKC>(op, a, splits, s);
+    case 7: return dispatch_bf16_direct<256, 256, 4, 2, 2, AK, BKC>(op, a, splits, s);
+    case 8: return dispatch_bf16_direct<256, 256, 2, 2, 2, AK, BKC>(op, a, splits, s);
     default: return dispatch_bf16_cfg<128, 128, 2, 2, AK, BKC>(op, a, splits, s);
   }
 }
