@@ -48,10 +48,12 @@ int lmk_layernorm_fwd(int precision, const float* x, const float* g, const float
 
 /* LayerNorm backward: g_out = g_in + dx (g_in may be NULL or equal g_out),
  * g_act (nullable) = g_out in the activation type, dgamma/dbeta [C] fp32
- * (overwritten). ws: fp32 scratch of lmk_layernorm_bwd_ws_floats(M, C). */
+ * (overwritten), dsum (nullable) [C] fp32 = column sums of g_out (the
+ * gradient of a bias added to the LayerNorm's input). ws: fp32 scratch of
+ * lmk_layernorm_bwd_ws_floats(M, C). */
 int lmk_layernorm_bwd(int precision, const float* dy, const float* x, const float* mu, const float* rstd,
                       const float* g, int M, int C, const float* g_in, float* g_out, void* g_act, float* dgamma,
-                      float* dbeta, float* ws, void* stream);
+                      float* dbeta, float* dsum, float* ws, void* stream);
 int64_t lmk_layernorm_bwd_ws_floats(int M, int C);
 
 /* Column sums of an [M,N] matrix (bias gradients) into out [N] fp32, summed
@@ -88,9 +90,10 @@ int lmk_xent(int precision, void* z, int64_t ldz, int M, int V, const int32_t* t
 
 /* Stable counting sort of keys [M] in [0, nkeys): counts/offsets/chunk_base
  * [nkeys+1], perm [M] (rows of key v at perm[offsets[v] .. offsets[v+1]),
- * ascending). */
+ * ascending); rank [M] int32 scratch (each row's count of equal keys before
+ * it). */
 int lmk_csr(const int32_t* keys, int M, int nkeys, int32_t* counts, int32_t* offsets, int32_t* chunk_base,
-            int32_t* perm, void* stream);
+            int32_t* perm, int32_t* rank, void* stream);
 /* dst[v,:] (+)= sum of dx rows with key v, in perm order (after lmk_csr).
  * partial: fp32 scratch of lmk_segment_sum_ws_floats(M, nkeys, C). */
 int lmk_segment_sum(const float* dx, int M, int C, int nkeys, int32_t* counts, int32_t* offsets,

@@ -80,7 +80,7 @@ _P = c_void_p
 _sig("lmk_gemm", c_int, [c_int, c_int, c_int, c_int, _P, c_int64, c_int, _P, c_int64, c_int, _P, c_int64, c_int, c_int,
                          _P, _P, c_int64, _P, c_int64, c_int, c_int, _P, c_int64, _P])
 _sig("lmk_layernorm_fwd", c_int, [c_int, _P, _P, _P, c_int, c_int, c_float, _P, _P, _P, _P])
-_sig("lmk_layernorm_bwd", c_int, [c_int, _P, _P, _P, _P, _P, c_int, c_int, _P, _P, _P, _P, _P, _P, _P])
+_sig("lmk_layernorm_bwd", c_int, [c_int, _P, _P, _P, _P, _P, c_int, c_int, _P, _P, _P, _P, _P, _P, _P, _P])
 _sig("lmk_layernorm_bwd_ws_floats", c_int64, [c_int, c_int])
 _sig("lmk_colsum", c_int, [c_int, _P, c_int64, c_int, c_int, _P, _P, _P])
 _sig("lmk_colsum_ws_floats", c_int64, [c_int, c_int])
@@ -89,7 +89,7 @@ _sig("lmk_embed_fwd", c_int, [_P, _P, _P, _P, c_int, c_int, c_int, _P, _P, _P])
 _sig("lmk_attn_fwd", c_int, [c_int, _P, _P, _P, c_int, c_int, c_int, c_int, _P, _P, _P])
 _sig("lmk_attn_bwd", c_int, [c_int, _P, _P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, _P, _P, _P])
 _sig("lmk_xent", c_int, [c_int, _P, c_int64, c_int, c_int, _P, _P, _P, _P, _P, _P])
-_sig("lmk_csr", c_int, [_P, c_int, c_int, _P, _P, _P, _P, _P])
+_sig("lmk_csr", c_int, [_P, c_int, c_int, _P, _P, _P, _P, _P, _P])
 _sig("lmk_segment_sum", c_int, [_P, c_int, c_int, c_int, _P, _P, _P, _P, _P, _P, c_int, _P])
 _sig("lmk_segment_sum_ws_floats", c_int64, [c_int, c_int, c_int])
 _sig("lmk_grad_norm", c_int, [_P, c_int64, c_float, _P, _P, _P, _P])
@@ -254,10 +254,11 @@ def layernorm_bwd_ws_floats(M, C):
     return _lib.lmk_layernorm_bwd_ws_floats(M, C)
 
 
-def layernorm_bwd(precision, dy, x, mu, rstd, g, g_in, g_out, g_act, dgamma, dbeta, ws):
+def layernorm_bwd(precision, dy, x, mu, rstd, g, g_in, g_out, g_act, dgamma, dbeta, ws, dsum=None):
     M, C = x.shape
     _kcheck(_lib.lmk_layernorm_bwd(precision, _ptr(dy), _ptr(x), _ptr(mu), _ptr(rstd), _ptr(g), M, C, _ptr(g_in),
-                                   _ptr(g_out), _ptr(g_act), _ptr(dgamma), _ptr(dbeta), _ptr(ws), _stream()),
+                                   _ptr(g_out), _ptr(g_act), _ptr(dgamma), _ptr(dbeta), _ptr(dsum), _ptr(ws),
+                                   _stream()),
             "lmk_layernorm_bwd")
 
 
@@ -296,9 +297,9 @@ def xent(precision, z, ldz, M, V, tgt, loss, ws_n, ws_rows, flags):
                           _ptr(flags), _stream()), "lmk_xent")
 
 
-def csr(keys, M, nkeys, counts, offsets, chunk_base, perm):
-    _kcheck(_lib.lmk_csr(_ptr(keys), M, nkeys, _ptr(counts), _ptr(offsets), _ptr(chunk_base), _ptr(perm), _stream()),
-            "lmk_csr")
+def csr(keys, M, nkeys, counts, offsets, chunk_base, perm, rank):
+    _kcheck(_lib.lmk_csr(_ptr(keys), M, nkeys, _ptr(counts), _ptr(offsets), _ptr(chunk_base), _ptr(perm),
+                         _ptr(rank), _stream()), "lmk_csr")
 
 
 def segment_sum_ws_floats(M, nkeys, C):

@@ -228,7 +228,7 @@ void carve(lm_model* m, char* base) {
   m->dbig = c.take<char>(M * std::max(F, 3 * C) * A);
   m->dO = c.take<char>(M * C * A);
   long ln_blocks = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
-  m->ln_part = c.take<float>(2 * ln_blocks * C);
+  m->ln_part = c.take<float>(3 * ln_blocks * C);
   long col_blocks = (M + kColRows - 1) / kColRows;
   m->col_part = c.take<float>(col_blocks * std::max(F, 3 * C));
   m->gemm_ws_floats = 8L * std::max(F, 3 * C) * std::max(F, C);
@@ -240,6 +240,7 @@ void carve(lm_model* m, char* base) {
     e.offsets = c.take<int32_t>(nkeys + 1);
     e.chunk_base = c.take<int32_t>(nkeys + 1);
     e.perm = c.take<int32_t>(M);
+    e.rank = c.take<int32_t>(M);
     e.partial = c.take<float>(embed_bwd_max_chunks((int)M, (int)nkeys) * C);
   }
   m->start = c.take<int32_t>(M);
@@ -430,15 +431,23 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   long ln_blocks = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
   float* pdg = m->ln_part;
   float* pdb = m->ln_part + ln_blocks * C;
-  auto ln_bwd = [&](const float* x, const float* mu, const float* r, long g_off, long b_off, const float* g_in) {
+  float* pdc = m->ln_part + 2 * ln_blocks * C;
+  // LayerNorm backward; the column sums of its output gradient g are the
+  // gradient of the bias added to the residual stream right before the
+  // LayerNorm's input (b_proj of the block below for ln_1 and ln_f, b_o of
+  // the same block for ln_2), so they come out of the same pass (dcol).
+  auto ln_bwd = [&](const float* x, const float* mu, const float* r, long g_off, long b_off, const float* g_in,
+                    float* dcol) {
     Lr.run("layernorm_bwd", 0, Mf * C * ((g_in ? 4 * 4 : 3 * 4) + A), [&] {
-      launch_ln_bwd<E>(m->dy, x, mu, r, m->P_(g_off), (int)M, (int)C, g_in, m->g, g_act, pdg, pdb, s);
+      launch_ln_bwd<E>(m->dy, x, mu, r, m->P_(g_off), (int)M, (int)C, g_in, m->g, g_act, pdg, pdb,
+                       dcol ? pdc : nullptr, s);
     });
-    Lr.run("layernorm_bwd_reduce", 0, 2.0 * ln_blocks * C * 4, [&] {
-      launch_colsum_partials(pdg, pdb, (int)ln_blocks, (int)C, m->grads + g_off, m->grads + b_off, s);
+    Lr.run("layernorm_bwd_reduce", 0, (dcol ? 3.0 : 2.0) * ln_blocks * C * 4, [&] {
+      launch_colsum_partials(pdg, pdb, (int)ln_blocks, (int)C, m->grads + g_off, m->grads + b_off, s,
+                             dcol ? pdc : nullptr, dcol);
     });
   };
-  ln_bwd(m->x + m->L * M * C, m->muf, m->rf, m->o_lnf_g, m->o_lnf_b, nullptr);
+  ln_bwd(m->x + m->L * M * C, m->muf, m->rf, m->o_lnf_g, m->o_lnf_b, nullptr, m->grads + m->blk[m->L - 1].b_proj);
   E* dbig = m->act<E>(m->dbig, 0);
   E* dO = m->act<E>(m->dO, 0);
   for (int l = m->L - 1; l >= 0; --l) {
@@ -453,7 +462,6 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
     E* a = m->act<E>(m->a, l * M * F);
     // MLP out: x_{l+1} = xm + a W_proj^T + b_proj
     Lr.run("gemm_fc2_bwd_dw", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, dw_op(g_act, M, C, a, F, m->grads + b.w_proj), s); });
-    Lr.run("bias_grad", 0, Mf * C * 4, [&] { launch_colsum<float>(m->g, C, (int)M, (int)C, m->col_part, m->grads + b.b_proj, s); });
     {
       GemmOp op = dx_op(m, g_act, M, C, b.w_proj, F, dbig, EPI_DGELU);
       op.aux = u; op.ld_aux = F;
@@ -467,10 +475,9 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
       op.c_f32 = true;
       Lr.run("gemm_fc1_bwd_dx", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, op, s); });
     }
-    ln_bwd(xml, m->mu2 + l * M, m->r2 + l * M, b.ln2_g, b.ln2_b, m->g);
+    ln_bwd(xml, m->mu2 + l * M, m->r2 + l * M, b.ln2_g, b.ln2_b, m->g, m->grads + b.b_o);
     // attention out: xm = x + o W_o^T + b_o
     Lr.run("gemm_attnout_bwd_dw", 2.0 * M * C * C, 0, [&] { rc |= gemm(m, dw_op(g_act, M, C, o, C, m->grads + b.w_o), s); });
-    Lr.run("bias_grad", 0, Mf * C * 4, [&] { launch_colsum<float>(m->g, C, (int)M, (int)C, m->col_part, m->grads + b.b_o, s); });
     Lr.run("gemm_attnout_bwd_dx", 2.0 * M * C * C, 0, [&] { rc |= gemm(m, dx_op(m, g_act, M, C, b.w_o, C, dO, EPI_STORE), s); });
     {
       AttnArgs at{};
@@ -489,7 +496,7 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
       op.c_f32 = true;
       Lr.run("gemm_qkv_bwd_dx", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, op, s); });
     }
-    ln_bwd(xl, m->mu1 + l * M, m->r1 + l * M, b.ln1_g, b.ln1_b, m->g);
+    ln_bwd(xl, m->mu1 + l * M, m->r1 + l * M, b.ln1_g, b.ln1_b, m->g, l > 0 ? m->grads + m->blk[l - 1].b_proj : nullptr);
   }
   // embedding: dwte[tok] += dx0 (on top of the head part), dwpe[pos] = sum dx0
   Lr.run("embed_bwd", 0, Mf * C * 8, [&] {

@@ -63,8 +63,13 @@ struct RowTile {
   static __device__ __forceinline__ int off(int r, int c) { return r * D + ((c ^ sw(r)) << 3); }
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to a packed bf16 pair (round to nearest even), one
+// conversion instruction.
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 __device__ __forceinline__ bf16x8_t as_frag(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 __device__ __forceinline__ uint4 pack_frag(const float* v) {
@@ -177,9 +182,12 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   const bf16* base = reinterpret_cast<const bf16*>(a.qkv) + (long)b * T * ld;
   const int32_t* start = a.start + (long)b * T;
 
-  const int q = q0 + w * 32 + (lane & 31);
+  const int qw0 = q0 + w * 32;
+  const int q = qw0 + (lane & 31);
   const bool qv = q < T;
   const int qs = qv ? start[q] : 0;
+  const bool wave_last_ok = qw0 + 31 < T;           // every query of the wave exists
+  const int qs_last = __shfl(qs, 31, 64);           // start of the wave's last query
   bf16x8_t qf[KS];
   frags_global<D>(qf, base, ld, q, T, h * D, lane);
 
@@ -215,29 +223,53 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
         s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sK[cur], sub * 32, ks, lane), qf[ks], s[sub], 0,
                                                          0, 0);
     }
+    // A tile every score of which is kept (all 64 keys at or before the
+    // wave's first query and at or after its last query's start) needs no
+    // mask: the max is taken on the raw scores and the scale folded into the
+    // exponent.
+    const bool full = wave_last_ok && k0 + 63 <= qw0 && qs_last <= k0;
     float mt = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = k0 + sub * 32 + acc_row(e, lane);
-        const float v = (qv && j >= qs && j <= q) ? s[sub][e] * sc : -INFINITY;
-        s[sub][e] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);
-    const float corr = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
     float p[2][16];
-    float ls = 0.f;
+    float ls = 0.f, mn;
+    if (full) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float v = (mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[sub][e] - mn);
-        p[sub][e] = v;
-        ls += v;
-      }
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[sub][e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sc;
+      mn = fmaxf(m, mt);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][e], sc, -mn));
+          p[sub][e] = v;
+          ls += v;
+        }
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = k0 + sub * 32 + acc_row(e, lane);
+          const float v = (qv && j >= qs && j <= q) ? s[sub][e] * sc : -INFINITY;
+          s[sub][e] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mn = fmaxf(m, mt);
+      // exp2(-inf) = 0 covers masked scores; a fully masked row so far keeps 0
+      const float sub_mn = (mn == -INFINITY) ? 0.f : mn;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float v = __builtin_amdgcn_exp2f(s[sub][e] - sub_mn);
+          p[sub][e] = v;
+          ls += v;
+        }
+    }
+    const float corr = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
     l = l * corr + ls;
     m = mn;
 #pragma unroll
@@ -312,9 +344,12 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
   const bf16* dob = reinterpret_cast<const bf16*>(a.dout) + (long)b * T * C;
   const int32_t* start = a.start + (long)b * T;
 
-  const int q = q0 + w * 32 + (lane & 31);
+  const int qw0 = q0 + w * 32;
+  const int q = qw0 + (lane & 31);
   const bool qv = q < T;
   const int qs = qv ? start[q] : 0;
+  const bool wave_last_ok = qw0 + 31 < T;
+  const int qs_last = __shfl(qs, 31, 64);
   const float lse2 = qv ? a.lse[((long)b * H + h) * T + q] * kLog2e : 0.f;
   const float dlt = qv ? a.delta[((long)b * H + h) * T + q] : 0.f;
   bf16x8_t qf[KS], df[KS];
@@ -352,11 +387,18 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sV[cur], sub * 32, ks, lane), df[ks], dp, 0, 0, 0);
       }
       float ds[16];
+      const int kb = k0 + sub * 32;
+      if (wave_last_ok && kb + 31 <= qw0 && qs_last <= kb) {
+        // every score of this 32 x 32 block is kept
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = k0 + sub * 32 + acc_row(e, lane);
-        const float p = (qv && j >= qs && j <= q) ? __builtin_amdgcn_exp2f(s[e] * sc - lse2) : 0.f;
-        ds[e] = p * (dp[e] - dlt);
+        for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sc, -lse2)) * (dp[e] - dlt);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = kb + acc_row(e, lane);
+          const bool ok = qv && j >= qs && j <= q;
+          ds[e] = __builtin_amdgcn_exp2f(ok ? __builtin_fmaf(s[e], sc, -lse2) : -INFINITY) * (dp[e] - dlt);
+        }
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -387,8 +429,9 @@ __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sQ[2][RowTile<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 sdO[2][RowTile<D>::ELEMS];
-  __shared__ float sL[2][64], sD[2][64];
-  __shared__ int sS[2][64];
+  __shared__ __attribute__((aligned(16))) float sL[2][64];
+  __shared__ __attribute__((aligned(16))) float sD[2][64];
+  __shared__ __attribute__((aligned(16))) int sS[2][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = a.T, H = a.H, C = H * D;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -400,8 +443,10 @@ __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
   const float* lse = a.lse + ((long)b * H + h) * T;
   const float* dl = a.delta + ((long)b * H + h) * T;
 
-  const int key = kb0 + w * 32 + (lane & 31);
+  const int kw0 = kb0 + w * 32;
+  const int key = kw0 + (lane & 31);
   const bool kv = key < T;
+  const bool wave_keys_ok = kw0 + 31 < T;  // every key of the wave exists
   bf16x8_t kf[KS], vf[KS];
   frags_global<D>(kf, base, ld, key, T, C + h * D, lane);
   frags_global<D>(vf, base, ld, key, T, 2 * C + h * D, lane);
@@ -451,13 +496,33 @@ __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sdO[cur], sub * 32, ks, lane), vf[ks], dp, 0, 0, 0);
       }
       float p[16], ds[16];
+      // rows of element e: sub*32 + acc_row(e), four consecutive rows per
+      // group of four elements, read as one vector
+      const int rq = qb + sub * 32;  // first query of this 32-query block
+      const bool full = wave_keys_ok && kw0 + 31 <= rq && rq + 31 < T && sS[cur][sub * 32 + 31] <= kw0;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = sub * 32 + acc_row(e, lane);
-        const bool ok = kv && key >= sS[cur][r] && key <= qb + r;
-        const float pv = ok ? __builtin_amdgcn_exp2f(s[e] * sc - sL[cur][r]) : 0.f;
-        p[e] = pv;
-        ds[e] = pv * (dp[e] - sD[cur][r]);
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = sub * 32 + g * 8 + (lane >> 5) * 4;
+        const f32x4_t L4 = *reinterpret_cast<const f32x4_t*>(&sL[cur][r0]);
+        const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(&sD[cur][r0]);
+        if (full) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + i], sc, -L4[i]));
+            p[4 * g + i] = pv;
+            ds[4 * g + i] = pv * (dp[4 * g + i] - D4[i]);
+          }
+        } else {
+          const int4 S4 = *reinterpret_cast<const int4*>(&sS[cur][r0]);
+          const int st4[4] = {S4.x, S4.y, S4.z, S4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = kv && key >= st4[i] && key <= qb + r0 + i;
+            const float pv = __builtin_amdgcn_exp2f(ok ? __builtin_fmaf(s[4 * g + i], sc, -L4[i]) : -INFINITY);
+            p[4 * g + i] = pv;
+            ds[4 * g + i] = pv * (dp[4 * g + i] - D4[i]);
+          }
+        }
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {

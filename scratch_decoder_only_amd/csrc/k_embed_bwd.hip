@@ -28,8 +28,8 @@ __global__ void csr_count_kernel(const int32_t* __restrict__ keys, int M, int nk
 
 // Exclusive scans of counts (-> offsets) and of ceil(count / kSegRows)
 // (-> chunk_base), each with nkeys + 1 entries. One block of 1024 threads;
-// every thread scans a contiguous slice serially, then the slice totals are
-// scanned in LDS.
+// every thread scans a contiguous slice serially (its loads issued in
+// batches of 8), then the slice totals are scanned in LDS.
 __global__ void __launch_bounds__(1024) csr_scan_kernel(const int32_t* __restrict__ counts, int nkeys,
                                                         int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ chunk_base) {
@@ -37,11 +37,17 @@ __global__ void __launch_bounds__(1024) csr_scan_kernel(const int32_t* __restric
   const int n = nkeys + 1;
   const int per = (n + 1023) / 1024;
   const int t = threadIdx.x, lo = t * per, hi = min(n, lo + per);
+  auto cnt = [&](int v) { return v < hi && v < nkeys ? counts[v] : 0; };
   int sa = 0, sb = 0;
-  for (int v = lo; v < hi; ++v) {
-    int c = v < nkeys ? counts[v] : 0;
-    sa += c;
-    sb += (c + kSegRows - 1) / kSegRows;
+  for (int v = lo; v < hi; v += 8) {
+    int c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = cnt(v + u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sa += c[u];
+      sb += (c[u] + kSegRows - 1) / kSegRows;
+    }
   }
   s_a[t] = sa;
   s_b[t] = sb;
@@ -55,32 +61,49 @@ __global__ void __launch_bounds__(1024) csr_scan_kernel(const int32_t* __restric
     __syncthreads();
   }
   int ra = s_a[t] - sa, rb = s_b[t] - sb;
-  for (int v = lo; v < hi; ++v) {
-    int c = v < nkeys ? counts[v] : 0;
-    offsets[v] = ra;
-    chunk_base[v] = rb;
-    ra += c;
-    rb += (c + kSegRows - 1) / kSegRows;
+  for (int v = lo; v < hi; v += 8) {
+    int c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = cnt(v + u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (v + u < hi) {
+        offsets[v + u] = ra;
+        chunk_base[v + u] = rb;
+        ra += c[u];
+        rb += (c[u] + kSegRows - 1) / kSegRows;
+      }
   }
 }
 
-// perm[offsets[key_i] + rank_i] = i, rank_i = #{j < i : key_j == key_i}.
-__global__ void __launch_bounds__(256) csr_scatter_kernel(const int32_t* __restrict__ keys, int M, int nkeys,
-                                                          const int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ perm) {
+// rank[i] += #{j < i in row block jb : key_j == key_i} for the rows i of row
+// block b (blocks of 256 rows; grid (b, jb), jb <= b). Integer sums, so the
+// result does not depend on the order of the atomic additions.
+__global__ void __launch_bounds__(256) csr_rank_kernel(const int32_t* __restrict__ keys, int M, int nkeys,
+                                                       int32_t* __restrict__ rank) {
+  const int b = blockIdx.x, jb = blockIdx.y;
+  if (jb > b) return;
   __shared__ int s_k[256];
+  const int j = jb * 256 + threadIdx.x;
+  s_k[threadIdx.x] = j < M ? clamp_key(keys[j], nkeys) : -2;
+  __syncthreads();
+  const int i = b * 256 + threadIdx.x;
+  if (i >= M) return;
+  const int my = clamp_key(keys[i], nkeys);
+  const int lim = jb == b ? (int)threadIdx.x : 256;
+  int cnt = 0;
+#pragma unroll 8
+  for (int q = 0; q < lim; ++q) cnt += (s_k[q] == my);
+  if (cnt) atomicAdd(&rank[i], cnt);
+}
+
+// perm[offsets[key_i] + rank_i] = i.
+__global__ void __launch_bounds__(256) csr_place_kernel(const int32_t* __restrict__ keys, int M, int nkeys,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ rank,
+                                                        int32_t* __restrict__ perm) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  const int my = i < M ? clamp_key(keys[i], nkeys) : -1;
-  int rank = 0;
-  for (int j0 = 0; j0 <= blockIdx.x * 256; j0 += 256) {
-    __syncthreads();
-    int j = j0 + threadIdx.x;
-    s_k[threadIdx.x] = j < M ? clamp_key(keys[j], nkeys) : -2;
-    __syncthreads();
-    const int lim = (j0 == blockIdx.x * 256) ? (int)threadIdx.x : 256;
-    for (int q = 0; q < lim; ++q) rank += (s_k[q] == my);
-  }
-  if (i < M) perm[offsets[my] + rank] = i;
+  if (i < M) perm[offsets[clamp_key(keys[i], nkeys)] + rank[i]] = i;
 }
 
 __device__ __forceinline__ int find_key(const int32_t* __restrict__ chunk_base, int nkeys, int w) {
@@ -136,9 +159,12 @@ void launch_csr(const int32_t* keys, int M, int nkeys, EmbedBwdWs ws, hipStream_
   launch_fill_u32(reinterpret_cast<uint32_t*>(ws.counts), 0u, nkeys + 1, s);
   if (M > 0) hipLaunchKernelGGL(csr_count_kernel, dim3((M + 255) / 256), dim3(256), 0, s, keys, M, nkeys, ws.counts);
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, ws.counts, nkeys, ws.offsets, ws.chunk_base);
-  if (M > 0)
-    hipLaunchKernelGGL(csr_scatter_kernel, dim3((M + 255) / 256), dim3(256), 0, s, keys, M, nkeys, ws.offsets,
-                       ws.perm);
+  if (M > 0) {
+    const int nb = (M + 255) / 256;
+    launch_fill_u32(reinterpret_cast<uint32_t*>(ws.rank), 0u, M, s);
+    hipLaunchKernelGGL(csr_rank_kernel, dim3(nb, nb), dim3(256), 0, s, keys, M, nkeys, ws.rank);
+    hipLaunchKernelGGL(csr_place_kernel, dim3(nb), dim3(256), 0, s, keys, M, nkeys, ws.offsets, ws.rank, ws.perm);
+  }
 }
 
 void launch_segment_sum(const float* dx, const int32_t* keys, int M, int C, int nkeys, EmbedBwdWs ws, float* dst,

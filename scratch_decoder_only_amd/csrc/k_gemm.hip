@@ -674,6 +674,349 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
   }
 }
 
+// --------------------------------------------- persistent pipelined GEMM
+// Large tiles (256 x 256 with 8 wavefronts) cut the global-load bytes per
+// flop to what one CU's load path sustains (about 50 B/clock measured, while
+// a 128 x 128 tile needs 64 B/clock at the MFMA rate). Tiles arrive by
+// direct-to-LDS loads in S stages of BK K-values; each stage is its own LDS
+// array, so the compiler can tell that fragment reads of stage i do not
+// depend on the loads still landing in the other stages, and the kernel
+// itself waits (vmcnt) for exactly the loads of the step it is about to read.
+//
+// The MFMA takes the B fragment as its first operand, so a lane's
+// accumulator holds one output row (lane % 32) and groups of 4 consecutive
+// columns, which the epilogue writes straight from registers with 8- or
+// 16-byte stores (no LDS staging, no barrier). Blocks are persistent: each
+// walks work units (tile, K slice) with a stride of the grid, and the first
+// loads of its next unit are issued before the epilogue of the current one.
+
+template <int ROWS, bool KC, int NT, int BK>
+struct PTile {
+  static_assert(ROWS == 128 || ROWS == 256, "pipelined tiles hold 128 or 256 rows");
+  static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
+  static constexpr int CPR = BK / 8;                  // 16-byte chunks per K-contiguous row
+  static constexpr int RPW = 128 / BK;                // K-contiguous rows per 256-byte bank window
+  static constexpr int PITCH = KC ? BK : ROWS;        // bf16 elements per LDS row
+  static constexpr int ELEMS = ROWS * BK;
+  static constexpr int CHUNKS = ROWS * BK / 8;        // 16-byte chunks per K step
+  static constexpr int NW = NT / 64;
+  static constexpr int NI = CHUNKS / 64 / NW;         // load instructions per wavefront per K step
+  static_assert(NI * 64 * NW == CHUNKS, "whole wavefront loads");
+  __amdgpu_buffer_rsrc_t rsrc;
+  unsigned voff[NI];
+  int kin[NI];
+  bool cok[NI];
+  unsigned kstride;
+  int wbase;
+
+  // KC: chunk c of row r at position c ^ ((r / RPW) % CPR), so 16 lanes
+  // reading 16 consecutive rows at one chunk cover distinct banks. MN: chunk q
+  // of k-row k at q ^ ((k & 3) << 2) (the transposing reads take 4 k-rows).
+  static __device__ __forceinline__ int kc_pos(int row, int c) { return c ^ ((row / RPW) % CPR); }
+
+  __device__ __forceinline__ void setup(const bf16* g, long ld, int row0, int rows_total, int K, int tid) {
+    long origin, extent;
+    if (KC) {
+      origin = (long)row0 * ld;
+      extent = (long)(rows_total - 1 - row0) * ld + K;
+    } else {
+      origin = row0;
+      extent = (long)(K - 1) * ld + (rows_total - row0);
+    }
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(g + origin), (short)0,
+                                             (int)min(extent * 2, (long)0x7fffffff), 0x00020000);
+    kstride = KC ? 2u : (unsigned)(ld * 2);
+    const int w = tid >> 6, lane = tid & 63;
+    wbase = w * NI * 64;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int pos = wbase + i * 64 + lane;  // LDS slot this lane fills
+      if (KC) {
+        const int row = pos / CPR, kc = kc_pos(row, pos % CPR);
+        voff[i] = (unsigned)(((long)row * ld + kc * 8) * 2);
+        kin[i] = kc * 8;
+        cok[i] = true;
+      } else {
+        const int k = pos / (ROWS / 8), q = (pos % (ROWS / 8)) ^ ((k & 3) << 2);
+        voff[i] = (unsigned)(((long)k * ld + q * 8) * 2);
+        kin[i] = k;
+        cok[i] = row0 + q * 8 < rows_total;
+      }
+    }
+  }
+
+  // Issue the loads of the K step at k0 into the stage tile s (asynchronous).
+  __device__ __forceinline__ void load(bf16* s, int k0, int k_end) const {
+    const unsigned ko = (unsigned)k0 * kstride;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const unsigned vo = (cok[i] && k0 + kin[i] < k_end) ? voff[i] + ko : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(s + (wbase + i * 64) * 8), 16, (int)vo, 0, 0, 0);
+    }
+  }
+
+  // MFMA 32x32x16 operand fragment: rows row0 + lane % 32, k-slots
+  // ks*16 + 8 (lane / 32) .. + 7.
+  static __device__ __forceinline__ bf16x8_t frag(const bf16* __restrict__ s, int row0, int ks, int lane) {
+    if (KC) {
+      const int row = row0 + (lane & 31);
+      const int kc = ks * 2 + (lane >> 5);
+      return *reinterpret_cast<const bf16x8_t*>(s + row * BK + (kc_pos(row, kc) << 3));
+    } else {
+      const int g = lane >> 4, i = lane & 15;
+      const int m = row0 + (g & 1) * 16 + 4 * (i & 3);
+      const int k = ks * 16 + (g >> 1) * 8 + (i >> 2);
+      const int q = m >> 3, h = m & 7;
+      const bf16* p0 = s + k * PITCH + ((q ^ ((k & 3) << 2)) << 3) + h;
+      const bf16* p1 = s + (k + 4) * PITCH + ((q ^ (((k + 4) & 3) << 2)) << 3) + h;
+      bf16x4_t lo = ds_read_tr(p0), hi = ds_read_tr(p1);
+      return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+};
+
+// One LDS array per pipeline stage (a distinct object per I).
+template <int I, int ELEMS>
+__device__ __forceinline__ bf16* lds_stage() {
+  __shared__ __attribute__((aligned(1024))) bf16 buf[ELEMS];
+  return buf;
+}
+
+// Workgroup barrier without a memory fence: LDS data from direct loads is
+// made visible by each wavefront's own vmcnt wait before it; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+// Epilogue of 4 consecutive output columns col..col+3 of one row.
+template <int EPI, typename TC>
+__device__ __forceinline__ void epilogue4(const GemmArgs& p, long row, long col, f32x4_t v, int z) {
+  if (EPI == EPI_PARTIAL) {
+    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + z * p.split_stride + row * p.ldc + col) = v;
+    return;
+  }
+  if (EPI != EPI_DGELU && p.bias) v += *reinterpret_cast<const f32x4_t*>(p.bias + col);
+  auto st4 = [](bf16* d, f32x4_t x) {
+    const uint32_t w0 = (uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16);
+    const uint32_t w1 = (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16);
+    *reinterpret_cast<uint2*>(d) = make_uint2(w0, w1);
+  };
+  if (EPI == EPI_STORE) {
+    if (sizeof(TC) == 4) *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + row * p.ldc + col) = v;
+    else st4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+  } else if (EPI == EPI_RESID) {
+    v += *reinterpret_cast<const f32x4_t*>(p.R + row * p.ldr + col);
+    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + row * p.ldc + col) = v;
+  } else if (EPI == EPI_GELU) {
+    st4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+    f32x4_t a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = gelu_f(v[i]);
+    st4(reinterpret_cast<bf16*>(p.aux) + row * p.ld_aux + col, a);
+  } else if (EPI == EPI_DGELU) {
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16*>(p.aux) + row * p.ld_aux + col);
+    v[0] *= gelu_grad_f(__uint_as_float(u.x << 16));
+    v[1] *= gelu_grad_f(__uint_as_float(u.x & 0xffff0000u));
+    v[2] *= gelu_grad_f(__uint_as_float(u.y << 16));
+    v[3] *= gelu_grad_f(__uint_as_float(u.y & 0xffff0000u));
+    st4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+  }
+}
+
+// Split-K reduction, 4 columns per thread (N a multiple of 4, leading
+// dimensions multiples of 8): sums the S partial slices in slice order, then
+// applies the real epilogue.
+template <int EPI, typename TC>
+__global__ void __launch_bounds__(256) splitk_reduce4_kernel(GemmArgs p, const float* __restrict__ part, int S,
+                                                            long part_ld) {
+  const int nq = p.N >> 2;
+  const long total = (long)p.M_out * nq;
+  const long slice = (long)p.M * part_ld;
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (long)gridDim.x * blockDim.x) {
+    const long row = q / nq, col = (q - row * nq) * 4;
+    const float* src = part + row * part_ld + col;
+    f32x4_t acc = *reinterpret_cast<const f32x4_t*>(src);
+    int z = 1;
+    for (; z + 3 < S; z += 4) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + z * slice);
+      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + (z + 1) * slice);
+      const f32x4_t c = *reinterpret_cast<const f32x4_t*>(src + (z + 2) * slice);
+      const f32x4_t d = *reinterpret_cast<const f32x4_t*>(src + (z + 3) * slice);
+      acc += a;
+      acc += b;
+      acc += c;
+      acc += d;
+    }
+    for (; z < S; ++z) acc += *reinterpret_cast<const f32x4_t*>(src + z * slice);
+    epilogue4<EPI, TC>(p, row, col, acc, 0);
+  }
+}
+
+// Work unit u -> (tile m, tile n, K slice z). Units are numbered slice-major
+// and, inside a slice, in groups of GM m-tiles walked n-tile by n-tile. Block
+// b runs on XCD b % 8; the 32 blocks of one XCD take 32 consecutive units per
+// round, so the panels they share stay in that XCD's L2.
+__device__ __forceinline__ int pipe_unit(int round, int b, int nblocks) {
+  const int xcd = b & 7, local = b >> 3;
+  const int per_xcd = nblocks >> 3;  // nblocks is a multiple of 8
+  return round * nblocks + xcd * per_xcd + local;
+}
+__device__ __forceinline__ void pipe_tile(int u, int tiles_m, int tiles_n, int& tm, int& tn, int& z) {
+  const int tiles = tiles_m * tiles_n;
+  z = u / tiles;
+  const int t = u - z * tiles;
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = t / per_group, first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in = t - group * per_group;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int S, bool AK, bool BKC, int EPI, typename TC>
+__global__ void __launch_bounds__(WGM * WGN * 64) gemm_bf16_pipe_kernel(GemmArgs p, int units, int tiles_m,
+                                                                         int tiles_n) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tiles are multiples of 32");
+  static_assert(S >= 2, "at least two stages");
+  using LA = PTile<BM, AK, NT, BK>;
+  using LB = PTile<BN, BKC, NT, BK>;
+  constexpr int SE = LA::ELEMS + LB::ELEMS;  // bf16 elements per stage: A tile, then B tile
+  constexpr int NLD = LA::NI + LB::NI;       // load instructions per wavefront per K step
+  constexpr int KS = BK / 16;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const bf16* A = reinterpret_cast<const bf16*>(p.A);
+  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+  const int nb = gridDim.x;
+
+  LA la;
+  LB lb;
+  auto stage = [](auto I_) -> bf16* { return lds_stage<decltype(I_)::value, SE>(); };
+  auto k_range = [&](int z, int& kb, int& ke) {
+    kb = z * p.k_split;
+    ke = min(p.K, kb + p.k_split);
+  };
+  // set up the loaders of unit u and issue its first S - 1 K steps
+  auto prologue = [&](int u) {
+    int tm, tn, z, kb, ke;
+    pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
+    k_range(z, kb, ke);
+    la.setup(A, p.lda, tm * BM, p.M, p.K, tid);
+    lb.setup(B, p.ldb, tn * BN, p.N, p.K, tid);
+    const int nk = (ke - kb + BK - 1) / BK;
+    static_for<S - 1>([&](auto I_) {
+      constexpr int I = decltype(I_)::value;
+      if (I < nk) {
+        la.load(stage(I_), kb + I * BK, ke);
+        lb.load(stage(I_) + LA::ELEMS, kb + I * BK, ke);
+      }
+    });
+  };
+
+  f32x16_t acc[TM][TN];
+  int round = 0;
+  int u = pipe_unit(0, blockIdx.x, nb);
+  if (u < units) prologue(u);
+  for (; u < units; u = pipe_unit(++round, blockIdx.x, nb)) {
+    int tm, tn, z, kb, ke;
+    pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
+    k_range(z, kb, ke);
+    const int nk = (ke - kb + BK - 1) / BK;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    for (int it0 = 0; it0 < nk; it0 += S) {
+      static_for<S>([&](auto I_) {
+        constexpr int I = decltype(I_)::value;
+        const int it = it0 + I;
+        if (it < nk) {
+          // own loads of step it complete (later steps may still be landing),
+          // then every wavefront's: the stage is readable, and the stage read
+          // at step it - 1 is free
+          if (it + S - 2 < nk) wait_vmcnt<(S - 2) * NLD>();
+          else wait_vmcnt<0>();
+          lds_barrier();
+          if (it + S - 1 < nk) {
+            constexpr int NX = (I + S - 1) % S;
+            bf16* sx = stage(std::integral_constant<int, NX>{});
+            la.load(sx, kb + (it + S - 1) * BK, ke);
+            lb.load(sx + LA::ELEMS, kb + (it + S - 1) * BK, ke);
+          }
+          const bf16* sa = stage(I_);
+          const bf16* sb = sa + LA::ELEMS;
+          bf16x8_t af[2][TM], bfr[2][TN];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) af[0][i] = LA::frag(sa, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bfr[0][j] = LB::frag(sb, wn * WTN + j * 32, 0, lane);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const int f = ks & 1;
+            if (ks + 1 < KS) {
+#pragma unroll
+              for (int i = 0; i < TM; ++i) af[f ^ 1][i] = LA::frag(sa, wm * WTM + i * 32, ks + 1, lane);
+#pragma unroll
+              for (int j = 0; j < TN; ++j) bfr[f ^ 1][j] = LB::frag(sb, wn * WTN + j * 32, ks + 1, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[f][j], af[f][i], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      });
+    }
+    // every wavefront is done reading the stages: start the next unit's loads,
+    // then write this unit's outputs while they land
+    lds_barrier();
+    const int un = pipe_unit(round + 1, blockIdx.x, nb);
+    if (un < units) prologue(un);
+
+    // accumulator element e of tile (i, j): row lane % 32, column
+    // (e / 4) * 8 + (lane / 32) * 4 + e % 4
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const long row = (long)tm * BM + wm * WTM + i * 32 + (lane & 31);
+      if (row >= p.M_out) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const long col = (long)tn * BN + wn * WTN + j * 32 + g * 8 + (lane >> 5) * 4;
+          if (col < p.N) {
+            f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            epilogue4<EPI, TC>(p, row, col, v, z);
+          }
+        }
+    }
+  }
+  // no direct load may still be writing LDS when the workgroup ends
+  wait_vmcnt<0>();
+}
+
 // ------------------------------------------------------------- dispatch
 static GemmArgs make_args(const GemmOp& op) {
   GemmArgs a;
@@ -699,8 +1042,22 @@ static bool check_bf16(const GemmOp& op) {
 // 3 = 256 x 256 (8 waves of 64 x 128, two waves per SIMD).
 static int tiles_of(const GemmOp& op, int cfg) {
   const int BM = (cfg == 1 || cfg == 4 || cfg == 5) ? 128 : 256;
-  const int BN = cfg == 2 ? 96 : (cfg == 3 || cfg == 7 || cfg == 8) ? 256 : 128;
+  const int BN = cfg == 2 ? 96 : (cfg == 3 || cfg >= 7) ? 256 : 128;
   return ((op.M + BM - 1) / BM) * ((op.N + BN - 1) / BN);
+}
+
+static bool is_pipe(int cfg) { return cfg >= 9 && cfg <= 11; }
+
+// Compute units of the current device (the persistent grid's size).
+static int device_cus() {
+  static int n[64] = {0};
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return 256;
+  if (!n[d]) {
+    int v = 0;
+    n[d] = (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, d) == hipSuccess && v > 0) ? v : 256;
+  }
+  return n[d];
 }
 
 static int forced_cfg() {
@@ -713,15 +1070,37 @@ static int forced_cfg() {
 
 static int pick_cfg(const GemmOp& op) {
   const int f = forced_cfg();
-  if (f >= 0 && f <= 8 && (f != 2 || op.N % 96 == 0)) return f;
-  // 128 x 128 at two blocks per CU measured fastest for every GEMM of the
-  // GPT-2-small-shaped step (the 256-row tiles run one block per CU)
+  if (f >= 0 && f <= 11 && (f != 2 || op.N % 96 == 0)) return f;
+  // Measured on the GPT-2-small-shaped step: the persistent 256 x 256 kernel
+  // (8 waves of 128 x 64) wins on the vocabulary projection's forward (very
+  // wide N) and its input gradient (very long K), and on the MLP weight
+  // gradients (3072 x 768 outputs over K = 8192); 128 x 128 at two blocks per
+  // CU wins everywhere else.
+  const int mn_max = op.M > op.N ? op.M : op.N, mn_min = op.M < op.N ? op.M : op.N;
+  if (op.N >= 16384 || op.K >= 16384) return 11;
+  if (op.K >= 8192 && mn_max >= 3072 && mn_max <= 4096 && mn_min <= 1024) return 11;
   return 1;
 }
 
 int gemm_bf16_splits(const GemmOp& op) {
   if (op.force_split > 0) return op.force_split;
-  const int tiles = tiles_of(op, pick_cfg(op));
+  const int cfg = pick_cfg(op);
+  const int tiles = tiles_of(op, cfg);
+  if (is_pipe(cfg)) {
+    // persistent grid of one block per CU: pick the K split whose work units
+    // fill the last round best (smallest split within 10% of the best fill),
+    // with at least 512 K-values per slice
+    const int cus = device_cus();
+    auto fill = [&](int s) {
+      const long u = (long)tiles * s;
+      return (double)u / (double)(((u + cus - 1) / cus) * cus);
+    };
+    double best = fill(1);
+    for (int s = 2; s <= 16 && op.K / s >= 512; ++s) best = fill(s) > best ? fill(s) : best;
+    for (int s = 1; s <= 16; ++s)
+      if ((s == 1 || op.K / s >= 512) && fill(s) >= 0.9 * best) return s;
+    return 1;
+  }
   // split K when the tile grid cannot fill the 256 compute units and K is long
   int s = 1;
   while (tiles * s < 256 && op.K / (s * 2) >= 512) s *= 2;
@@ -749,6 +1128,35 @@ static int dispatch_bf16_direct(const GemmOp& op, const GemmArgs& a, int splits,
     case EPI_RESID: launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
     case EPI_GELU: launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
     case EPI_DGELU: launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
+    default: return -1;
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int S, bool AK, bool BKC, int EPI, typename TC>
+static void launch_bf16_pipe(const GemmArgs& a, int splits, hipStream_t s) {
+  const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  const int units = tiles_m * tiles_n * splits;
+  int nb = device_cus();
+  if (units < nb) nb = units;
+  nb = (nb + 7) / 8 * 8;  // whole XCD rounds
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI, TC>), dim3(nb),
+                     dim3(WGM * WGN * 64), 0, s, a, units, tiles_m, tiles_n);
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int S, bool AK, bool BKC>
+static int dispatch_bf16_pipe(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
+  if (splits > 1) {
+    launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_PARTIAL, float>(a, splits, s);
+    return 0;
+  }
+  switch (op.epi) {
+    case EPI_STORE:
+      if (op.c_f32) launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_STORE, float>(a, 1, s);
+      else launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_STORE, bf16>(a, 1, s);
+      return 0;
+    case EPI_RESID: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
+    case EPI_GELU: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
+    case EPI_DGELU: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
     default: return -1;
   }
 }
@@ -789,17 +1197,38 @@ static int dispatch_bf16_epi(const GemmOp& op, const GemmArgs& a, int splits, hi
     case 6: return dispatch_bf16_direct<256, 128, 2, 2, 2, AK, BKC>(op, a, splits, s);
     case 7: return dispatch_bf16_direct<256, 256, 4, 2, 2, AK, BKC>(op, a, splits, s);
     case 8: return dispatch_bf16_direct<256, 256, 2, 2, 2, AK, BKC>(op, a, splits, s);
+    case 9: return dispatch_bf16_pipe<256, 256, 4, 2, 64, 2, AK, BKC>(op, a, splits, s);
+    case 10: return dispatch_bf16_pipe<256, 256, 4, 2, 32, 4, AK, BKC>(op, a, splits, s);
+    case 11: return dispatch_bf16_pipe<256, 256, 2, 4, 64, 2, AK, BKC>(op, a, splits, s);
     default: return dispatch_bf16_cfg<128, 128, 2, 2, AK, BKC>(op, a, splits, s);
   }
 }
 
 template <typename TA>
 static void launch_reduce(const GemmOp& op, const GemmArgs& a, const float* part, int S, hipStream_t s) {
+  long ld = op.N;
+  if (sizeof(TA) == 2) {
+    // bf16 path: N and all leading dimensions are multiples of 8
+    long total = (long)a.M_out * (op.N / 4);
+    long blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    dim3 g((unsigned)blocks), b(256);
+    switch (op.epi) {
+      case EPI_STORE:
+        if (op.c_f32) hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_STORE, float>), g, b, 0, s, a, part, S, ld);
+        else hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_STORE, bf16>), g, b, 0, s, a, part, S, ld);
+        break;
+      case EPI_RESID: hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_RESID, float>), g, b, 0, s, a, part, S, ld); break;
+      case EPI_GELU: hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_GELU, bf16>), g, b, 0, s, a, part, S, ld); break;
+      case EPI_DGELU: hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_DGELU, bf16>), g, b, 0, s, a, part, S, ld); break;
+      default: break;
+    }
+    return;
+  }
   long total = (long)op.M * op.N;
   long blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   dim3 g((unsigned)blocks), b(256);
-  long ld = op.N;
   switch (op.epi) {
     case EPI_STORE:
       if (op.c_f32) hipLaunchKernelGGL((splitk_reduce_kernel<EPI_STORE, float, TA>), g, b, 0, s, a, part, S, ld);

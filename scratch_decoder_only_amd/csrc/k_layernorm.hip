@@ -74,25 +74,31 @@ template void launch_ln_fwd<bf16>(const float*, const float*, const float*, int,
 
 // Backward. Each block owns kLnRowsPerBlock consecutive rows; wave w takes
 // rows w, w+4, ... of them. g_out = g_in + dx (g_in may alias g_out or be
-// null); g_act (nullable) receives g_out in the activation type.
+// null); g_act (nullable) receives g_out in the activation type. Per-block
+// column partials: dgamma, dbeta and (part_dc non-null) the column sums of
+// g_out itself, which are the gradient of the bias added to the residual
+// stream just before this LayerNorm's input.
 template <int NV, typename T>
 __global__ void __launch_bounds__(256) ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mu_in,
                                                      const float* __restrict__ rstd_in,
                                                      const float* __restrict__ g, int M,
                                                      const float* g_in, float* g_out, T* __restrict__ g_act,
-                                                     float* __restrict__ part_dg, float* __restrict__ part_db) {
+                                                     float* __restrict__ part_dg, float* __restrict__ part_db,
+                                                     float* __restrict__ part_dc) {
   constexpr int C = 128 * NV;
   __shared__ float s_dg[4][C];
   __shared__ float s_db[4][C];
+  __shared__ float s_dc[4][C];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float2 gg[NV], adg[NV], adb[NV];
+  float2 gg[NV], adg[NV], adb[NV], adc[NV];
   const float2* g2 = reinterpret_cast<const float2*>(g);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     gg[j] = g2[lane + 64 * j];
     adg[j] = make_float2(0.f, 0.f);
     adb[j] = make_float2(0.f, 0.f);
+    adc[j] = make_float2(0.f, 0.f);
   }
   const long r0 = (long)blockIdx.x * kLnRowsPerBlock;
   const long r1 = min((long)M, r0 + kLnRowsPerBlock);
@@ -126,6 +132,8 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const float* __restrict__ d
         dx1 += gi.y;
       }
       reinterpret_cast<float2*>(g_out + m * C)[lane + 64 * j] = make_float2(dx0, dx1);
+      adc[j].x += dx0;
+      adc[j].y += dx1;
       if (g_act) {
         Act<T>::st(g_act, m * C + c, dx0);
         Act<T>::st(g_act, m * C + c + 1, dx1);
@@ -139,24 +147,27 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const float* __restrict__ d
     s_dg[w][c + 1] = adg[j].y;
     s_db[w][c] = adb[j].x;
     s_db[w][c + 1] = adb[j].y;
+    s_dc[w][c] = adc[j].x;
+    s_dc[w][c + 1] = adc[j].y;
   }
   __syncthreads();
   for (int c = threadIdx.x; c < C; c += 256) {
     part_dg[(long)blockIdx.x * C + c] = ((s_dg[0][c] + s_dg[1][c]) + s_dg[2][c]) + s_dg[3][c];
     part_db[(long)blockIdx.x * C + c] = ((s_db[0][c] + s_db[1][c]) + s_db[2][c]) + s_db[3][c];
+    if (part_dc) part_dc[(long)blockIdx.x * C + c] = ((s_dc[0][c] + s_dc[1][c]) + s_dc[2][c]) + s_dc[3][c];
   }
 }
 
 template <typename T>
 void launch_ln_bwd(const float* dy, const float* x, const float* mu, const float* rstd, const float* g, int M,
                    int C, const float* g_in, float* g_out, T* g_act, float* part_dg, float* part_db,
-                   hipStream_t s) {
+                   float* part_dc, hipStream_t s) {
   dim3 grid((M + kLnRowsPerBlock - 1) / kLnRowsPerBlock), block(256);
   switch (C / 128) {
 #define LN_CASE(NV)                                                                                    \
   case NV:                                                                                             \
     hipLaunchKernelGGL((ln_bwd_kernel<NV, T>), grid, block, 0, s, dy, x, mu, rstd, g, M, g_in, g_out, g_act, \
-                       part_dg, part_db);                                                              \
+                       part_dg, part_db, part_dc);                                                     \
     break;
     LN_CASE(1) LN_CASE(2) LN_CASE(3) LN_CASE(4) LN_CASE(5) LN_CASE(6) LN_CASE(7) LN_CASE(8)
 #undef LN_CASE
@@ -164,43 +175,68 @@ void launch_ln_bwd(const float* dy, const float* x, const float* mu, const float
   }
 }
 template void launch_ln_bwd<float>(const float*, const float*, const float*, const float*, const float*, int, int,
-                                   const float*, float*, float*, float*, float*, hipStream_t);
+                                   const float*, float*, float*, float*, float*, float*, hipStream_t);
 template void launch_ln_bwd<bf16>(const float*, const float*, const float*, const float*, const float*, int, int,
-                                  const float*, float*, bf16*, float*, float*, hipStream_t);
+                                  const float*, float*, bf16*, float*, float*, float*, hipStream_t);
 
 // out[c] = sum over p < P of part[p][c] in a fixed order: a block covers 16
 // columns with 16 row groups; thread (c, r) sums p = r, r + 16, ... for its
-// column, then the 16 group sums are added in r order. Two vectors at once
-// (the dg and db partials of one LayerNorm).
+// column, then the 16 group sums are added in r order. Up to three vectors at
+// once (the dg, db and output-column partials of one LayerNorm); pb/pc and
+// ob/oc may be null.
 __global__ void __launch_bounds__(256) colsum_partials_kernel(const float* __restrict__ pa, const float* __restrict__ pb,
-                                                              int P, int C, float* __restrict__ oa,
-                                                              float* __restrict__ ob) {
-  __shared__ float sa[16][17], sb[16][17];
+                                                              const float* __restrict__ pc, int P, int C,
+                                                              float* __restrict__ oa, float* __restrict__ ob,
+                                                              float* __restrict__ oc) {
+  __shared__ float sa[16][17], sb[16][17], sc[16][17];
   const int cc = threadIdx.x & 15, r = threadIdx.x >> 4;
   const int c = blockIdx.x * 16 + cc;
-  float a = 0.f, b = 0.f;
-  if (c < C)
-    for (int p = r; p < P; p += 16) {
+  float a = 0.f, b = 0.f, d = 0.f;
+  if (c < C) {
+    int p = r;
+    // batches of 8 partial rows: loads in flight together, added in order
+    for (; p + 7 * 16 < P; p += 8 * 16) {
+      float va[8], vb[8], vc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const long o = (long)(p + 16 * u) * C + c;
+        va[u] = pa[o];
+        vb[u] = pb ? pb[o] : 0.f;
+        vc[u] = pc ? pc[o] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a += va[u];
+        b += vb[u];
+        d += vc[u];
+      }
+    }
+    for (; p < P; p += 16) {
       a += pa[(long)p * C + c];
       if (pb) b += pb[(long)p * C + c];
+      if (pc) d += pc[(long)p * C + c];
     }
+  }
   sa[r][cc] = a;
   sb[r][cc] = b;
+  sc[r][cc] = d;
   __syncthreads();
   if (r == 0 && c < C) {
-    float ta = 0.f, tb = 0.f;
+    float ta = 0.f, tb = 0.f, td = 0.f;
     for (int k = 0; k < 16; ++k) {
       ta += sa[k][cc];
       tb += sb[k][cc];
+      td += sc[k][cc];
     }
     oa[c] = ta;
     if (ob) ob[c] = tb;
+    if (oc) oc[c] = td;
   }
 }
 
 void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob,
-                            hipStream_t s) {
-  hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + 15) / 16), dim3(256), 0, s, pa, pb, P, C, oa, ob);
+                            hipStream_t s, const float* pc, float* oc) {
+  hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + 15) / 16), dim3(256), 0, s, pa, pb, pc, P, C, oa, ob, oc);
 }
 
 // Column sums of an [M, N] matrix (bias gradients), N a multiple of 4. Stage
@@ -228,11 +264,23 @@ __global__ void __launch_bounds__(256) colsum_stage1_kernel(const T* __restrict_
   const long r0 = (long)blockIdx.y * kColRows;
   const long r1 = min((long)M, r0 + kColRows);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (c < N)
-    for (long r = r0 + g; r < r1; r += 4) {
+  if (c < N) {
+    long r = r0 + g;
+    // batches of 8 rows: all loads in flight first, then added in row order
+    for (; r + 28 < r1; r += 32) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = Quad<T>::ld(a + (r + 4 * u) * lda + c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+      }
+    }
+    for (; r < r1; r += 4) {
       float4 v = Quad<T>::ld(a + r * lda + c);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
+  }
   s[g][lane] = acc;
   __syncthreads();
   if (g == 0 && c < N) {

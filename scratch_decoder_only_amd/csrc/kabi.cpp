@@ -39,20 +39,22 @@ int lmk_layernorm_fwd(int precision, const float* x, const float* g, const float
 }
 
 int64_t lmk_layernorm_bwd_ws_floats(int M, int C) {
-  return 2L * ((M + kLnRowsPerBlock - 1) / kLnRowsPerBlock) * C;
+  return 3L * ((M + kLnRowsPerBlock - 1) / kLnRowsPerBlock) * C;
 }
 
 int lmk_layernorm_bwd(int precision, const float* dy, const float* x, const float* mu, const float* rstd,
                       const float* g, int M, int C, const float* g_in, float* g_out, void* g_act, float* dgamma,
-                      float* dbeta, float* ws, void* stream) {
+                      float* dbeta, float* dsum, float* ws, void* stream) {
   if (!ln_shape_ok(M, C) || M == 0) return -1;
   long nb = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
+  float* pc = dsum ? ws + 2 * nb * C : nullptr;
   if (precision)
-    launch_ln_bwd<bf16>(dy, x, mu, rstd, g, M, C, g_in, g_out, reinterpret_cast<bf16*>(g_act), ws, ws + nb * C, S(stream));
+    launch_ln_bwd<bf16>(dy, x, mu, rstd, g, M, C, g_in, g_out, reinterpret_cast<bf16*>(g_act), ws, ws + nb * C, pc,
+                        S(stream));
   else
     launch_ln_bwd<float>(dy, x, mu, rstd, g, M, C, g_in, g_out, reinterpret_cast<float*>(g_act), ws, ws + nb * C,
-                         S(stream));
-  launch_colsum_partials(ws, ws + nb * C, (int)nb, C, dgamma, dbeta, S(stream));
+                         pc, S(stream));
+  launch_colsum_partials(ws, ws + nb * C, (int)nb, C, dgamma, dbeta, S(stream), pc, dsum);
   return 0;
 }
 
@@ -108,9 +110,9 @@ int lmk_xent(int precision, void* z, int64_t ldz, int M, int V, const int32_t* t
 }
 
 int lmk_csr(const int32_t* keys, int M, int nkeys, int32_t* counts, int32_t* offsets, int32_t* chunk_base,
-            int32_t* perm, void* stream) {
-  if (M < 0 || nkeys <= 0) return -1;
-  EmbedBwdWs w{counts, offsets, chunk_base, perm, nullptr};
+            int32_t* perm, int32_t* rank, void* stream) {
+  if (M < 0 || nkeys <= 0 || (M > 0 && !rank)) return -1;
+  EmbedBwdWs w{counts, offsets, chunk_base, perm, nullptr, rank};
   launch_csr(keys, M, nkeys, w, S(stream));
   return 0;
 }
@@ -120,7 +122,7 @@ int64_t lmk_segment_sum_ws_floats(int M, int nkeys, int C) { return embed_bwd_ma
 int lmk_segment_sum(const float* dx, int M, int C, int nkeys, int32_t* counts, int32_t* offsets, int32_t* chunk_base,
                     int32_t* perm, float* partial, float* dst, int accumulate, void* stream) {
   if (M < 0 || nkeys <= 0 || C <= 0) return -1;
-  EmbedBwdWs w{counts, offsets, chunk_base, perm, partial};
+  EmbedBwdWs w{counts, offsets, chunk_base, perm, partial, nullptr};
   launch_segment_sum(dx, nullptr, M, C, nkeys, w, dst, accumulate != 0, S(stream));
   return 0;
 }

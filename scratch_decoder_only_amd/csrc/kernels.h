@@ -72,8 +72,9 @@ void launch_ln_fwd(const float* x, const float* g, const float* b, int M, int C,
 template <typename T>
 void launch_ln_bwd(const float* dy, const float* x, const float* mu, const float* rstd, const float* g, int M,
                    int C, const float* g_in, float* g_out, T* g_act, float* part_dg, float* part_db,
-                   hipStream_t s);
-void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob, hipStream_t s);
+                   float* part_dc, hipStream_t s);
+void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob, hipStream_t s,
+                            const float* pc = nullptr, float* oc = nullptr);
 template <typename T>
 void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s);
 
@@ -117,6 +118,7 @@ struct EmbedBwdWs {
   int32_t* chunk_base; // [nkeys + 1]
   int32_t* perm;       // [M]
   float* partial;      // [max_chunks, C]
+  int32_t* rank;       // [M] scratch of the sort
 };
 void launch_csr(const int32_t* keys, int M, int nkeys, EmbedBwdWs ws, hipStream_t s);
 // dst[key] (+)= sum of dx rows of that key. accumulate: add onto dst (rows of

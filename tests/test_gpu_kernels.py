@@ -153,12 +153,15 @@ def test_layernorm_fwd_bwd(sd, prec, C):
     dg = t.zeros(C, device="cuda")
     db = t.zeros(C, device="cuda")
     ws = t.zeros(sd.layernorm_bwd_ws_floats(M, C), device="cuda")
-    sd.layernorm_bwd(prec, dev(dy), dev(x), mu, rs, dev(g), gout, gout, gact, dg, db, ws)
+    dsum = t.zeros(C, device="cuda")
+    sd.layernorm_bwd(prec, dev(dy), dev(x), mu, rs, dev(g), gout, gout, gact, dg, db, ws, dsum=dsum)
     edx, edg, edb = oracle.layernorm_bwd(dy, x, host(mu), host(rs), g)
     t.cuda.synchronize()
     assert rel(host(gout), gin + edx) <= 2e-5
     assert rel(host(gact), gin + edx) <= tol(prec, False)
     assert rel(host(dg), edg) <= 2e-5 and rel(host(db), edb) <= 2e-5
+    # column sums of the output gradient (the bias gradient fused into this pass)
+    assert rel(host(dsum), (gin.astype(np.float64) + edx).sum(axis=0)) <= 2e-5
 
 
 # ------------------------------------------------- index layout, embedding
@@ -318,7 +321,8 @@ def test_csr_bit_exact_and_segment_sums(sd, nkeys, M):
     C = 128
     counts, offsets, chunk = (t.zeros(nkeys + 1, dtype=t.int32, device="cuda") for _ in range(3))
     perm = t.zeros(M, dtype=t.int32, device="cuda")
-    sd.csr(dev(keys), M, nkeys, counts, offsets, chunk, perm)
+    rank = t.full((M,), 7, dtype=t.int32, device="cuda")  # stale scratch must not matter
+    sd.csr(dev(keys), M, nkeys, counts, offsets, chunk, perm, rank)
     eoff, eperm = oracle.csr_by_key(keys, nkeys)
     t.cuda.synchronize()
     assert np.array_equal(offsets.cpu().numpy(), eoff)
