@@ -484,7 +484,8 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
       at.qkv = qkv; at.start = m->start; at.end = m->end; at.B = B; at.T = T; at.H = (int)H; at.D = m->D;
       at.o = o; at.lse = m->lse + l * M * H; at.dout = dO; at.delta = m->delta; at.dqkv = dbig;
       static const char* names[3] = {"attn_bwd_delta", "attn_bwd_dq", "attn_bwd_dkv"};
-      for (int part = 0; part < 3; ++part)
+      // bf16: the dQ pass computes delta itself (part 0 launches nothing)
+      for (int part = m->bf ? 1 : 0; part < 3; ++part)
         Lr.run(names[part], 0, part == 0 ? Mf * C * 2 * A : 0, [&] {
           rc |= m->bf ? attn_bwd_part_bf16(at, part, s) : attn_bwd_part_f32(at, part, s);
         });

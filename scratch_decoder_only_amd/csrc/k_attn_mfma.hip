@@ -168,6 +168,19 @@ __device__ __forceinline__ void zero(f32x16_t& a) {
   for (int e = 0; e < 16; ++e) a[e] = 0.f;
 }
 
+// Work item of a block: (batch x head, first of its 128 rows). Under the
+// causal mask a block's work grows with its query rows (forward, dQ) or
+// shrinks with its key rows (dK/dV), so items are numbered longest first over
+// the whole grid: item i takes size class i / (B H) and head row i % (B H).
+// Consecutive blocks land on different XCDs, so every XCD gets the same mix
+// of long and short items, and the long ones start first.
+__device__ __forceinline__ void item_rows(const AttnArgs& a, bool queries, int& bh, int& r0) {
+  const int BH = a.B * a.H, nt = (a.T + 127) / 128;
+  const int k = blockIdx.x / BH;
+  bh = blockIdx.x - k * BH;
+  r0 = (queries ? nt - 1 - k : k) * 128;
+}
+
 // ----------------------------------------------------------------- forward
 template <int D>
 __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
@@ -176,8 +189,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sV[2][RowTile<D>::ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = a.T, H = a.H, C = H * D;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int q0 = (gridDim.x - 1 - blockIdx.x) * 128;  // longest rows first
+  int bh, q0;
+  item_rows(a, true, bh, q0);
+  const int b = bh / H, h = bh % H;
   const long ld = 3L * C;
   const bf16* base = reinterpret_cast<const bf16*>(a.qkv) + (long)b * T * ld;
   const int32_t* start = a.start + (long)b * T;
@@ -300,35 +314,6 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- delta
-// delta_i = dO_i . O_i, D/8 lanes per (row, head), 8 values each.
-template <int D>
-__global__ void __launch_bounds__(256) attn_delta_kernel_v(AttnArgs a) {
-  constexpr int LPR = D / 8;
-  const long idx = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;  // (b, t, h) flat
-  const int sub = threadIdx.x % LPR;
-  const int H = a.H, T = a.T, C = H * D;
-  const long total = (long)a.B * T * H;
-  float v = 0.f;
-  if (idx < total) {
-    const long off = (idx / H) * C + (idx % H) * D + sub * 8;
-    const uint4 x = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16*>(a.dout) + off);
-    const uint4 y = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16*>(a.o) + off);
-    const uint32_t xa[4] = {x.x, x.y, x.z, x.w}, ya[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v += __uint_as_float(xa[k] << 16) * __uint_as_float(ya[k] << 16);
-      v += __uint_as_float(xa[k] & 0xffff0000u) * __uint_as_float(ya[k] & 0xffff0000u);
-    }
-  }
-#pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  if (idx < total && sub == 0) {
-    const long row = idx / H, bb = row / T, t = row % T;
-    a.delta[(bb * H + idx % H) * T + t] = v;
-  }
-}
-
 // ------------------------------------------------------------ dQ pass
 template <int D>
 __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
@@ -337,8 +322,9 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sV[2][RowTile<D>::ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = a.T, H = a.H, C = H * D;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int q0 = (gridDim.x - 1 - blockIdx.x) * 128;  // longest rows first
+  int bh, q0;
+  item_rows(a, true, bh, q0);
+  const int b = bh / H, h = bh % H;
   const long ld = 3L * C;
   const bf16* base = reinterpret_cast<const bf16*>(a.qkv) + (long)b * T * ld;
   const bf16* dob = reinterpret_cast<const bf16*>(a.dout) + (long)b * T * C;
@@ -351,10 +337,23 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
   const bool wave_last_ok = qw0 + 31 < T;
   const int qs_last = __shfl(qs, 31, 64);
   const float lse2 = qv ? a.lse[((long)b * H + h) * T + q] * kLog2e : 0.f;
-  const float dlt = qv ? a.delta[((long)b * H + h) * T + q] : 0.f;
   bf16x8_t qf[KS], df[KS];
   frags_global<D>(qf, base, ld, q, T, h * D, lane);
   frags_global<D>(df, dob, C, q, T, h * D, lane);
+  // delta_q = dO_q . O_q (lanes l and l ^ 32 hold the two halves of the row);
+  // written out for the dK/dV pass, which runs after this one
+  float dlt;
+  {
+    bf16x8_t of[KS];
+    frags_global<D>(of, reinterpret_cast<const bf16*>(a.o) + (long)b * T * C, C, q, T, h * D, lane);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) part += (float)df[ks][i] * (float)of[ks][i];
+    dlt = part + __shfl_xor(part, 32, 64);
+    if (qv && lane < 32) a.delta[((long)b * H + h) * T + q] = dlt;
+  }
   TileLoad<D> lk, lv;
   lk.init(base, ld, T, C + h * D, tid);
   lv.init(base, ld, T, 2 * C + h * D, tid);
@@ -434,8 +433,9 @@ __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) int sS[2][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = a.T, H = a.H, C = H * D;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int kb0 = blockIdx.x * 128;  // keys near the row start see the most queries: dispatched first
+  int bh, kb0;
+  item_rows(a, false, bh, kb0);
+  const int b = bh / H, h = bh % H;
   const long ld = 3L * C;
   const bf16* base = reinterpret_cast<const bf16*>(a.qkv) + (long)b * T * ld;
   const bf16* dob = reinterpret_cast<const bf16*>(a.dout) + (long)b * T * C;
@@ -557,17 +557,19 @@ __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
 
 template <int D>
 int fwd(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((a.T + 127) / 128, a.B * a.H);
+  dim3 grid((a.T + 127) / 128 * a.B * a.H);
   hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, a);
   return 0;
 }
 
+// Backward in passes: part 0 (row dot products delta) has nothing left to do
+// here, the dQ pass (part 1) computes and stores delta for its rows before
+// the dK/dV pass (part 2) reads it.
 template <int D>
 int bwd_part(const AttnArgs& a, int part, hipStream_t s) {
-  dim3 grid((a.T + 127) / 128, a.B * a.H);
+  dim3 grid((a.T + 127) / 128 * a.B * a.H);
   if (part == 0) {
-    const long threads = (long)a.B * a.T * a.H * (D / 8);
-    hipLaunchKernelGGL(attn_delta_kernel_v<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+    return 0;
   } else if (part == 1) {
     hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, a);
   } else {
