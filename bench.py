@@ -62,6 +62,122 @@ def attention_flops(shape, doc_ids, B, T):
     return 12.0 * shape.head_dim * shape.n_heads * shape.n_layers * pairs
 
 
+# Kernel symbol of each timing class whose HBM traffic is taken from counters
+# (a class must map to one kernel instantiation used by nothing else).
+TRAFFIC_SYMBOLS = {
+    "gemm_fc2_bwd_dx": "gemm_bf16_kernel<128, 128, 2, 2, true, false, 3,",
+    "attn_bwd_dkv": "attn_dkv_kernel<64>",
+    "attn_fwd": "attn_fwd_kernel<64>",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_c4_step.md")
+CALIB_BYTES = 1 << 30  # plain device copy used to scale the counters
+
+
+def source_digest():
+    """Hash of the kernel sources; counters taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "scratch_decoder_only_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_summary(fetch_dir, write_dir, out=TRAFFIC_FILE, cmd=""):
+    """Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) from two rocprofv3
+    --pmc runs, scaled by what the same counters read for the calibration copy
+    of CALIB_BYTES bytes; writes the summary with its machine-readable record."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        acc = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+
+    fetch_all, write_all = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    fetch = {k: (sum(v) / len(v), len(v)) for k, v in fetch_all.items()}
+    write = {k: (sum(v) / len(v), len(v)) for k, v in write_all.items()}
+    # the calibration copy: the largest dispatch of a copy kernel (it moves
+    # more bytes than any other copy of the run)
+    cal = [(max(v), k) for k, v in fetch_all.items() if "copy" in k.lower()]
+    if not cal:
+        raise SystemExit("no calibration copy in the counter data")
+    cf, ck = max(cal)
+    cw = max(write_all.get(ck, [0.0]))
+    f_scale = CALIB_BYTES / (cf * 1024)
+    w_scale = CALIB_BYTES / (cw * 1024) if cw > 0 else 1.0
+    rec = {"source_digest": source_digest(), "calib_kernel": ck, "calib_bytes": CALIB_BYTES,
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "classes": {}}
+    lines = []
+    for cls, sym in TRAFFIC_SYMBOLS.items():
+        ks = [k for k in fetch if sym in k]
+        if not ks:
+            continue
+        k = ks[0]
+        fb = fetch[k][0] * 1024 * f_scale
+        wb = write.get(k, (0.0, 0))[0] * 1024 * w_scale
+        rec["classes"][cls] = {"kernel": k, "dispatches": fetch[k][1], "fetch_kib": round(fetch[k][0], 1),
+                               "write_kib": round(write.get(k, (0.0, 0))[0], 1), "bytes_per_launch": round(fb + wb)}
+        lines.append(f"| {cls} | `{k[:90]}` | {fetch[k][1]} | {fetch[k][0]:.1f} | {write.get(k, (0, 0))[0]:.1f} | "
+                     f"{(fb + wb) / 1e6:.2f} |")
+    with open(out, "w") as fh:
+        fh.write("# HBM traffic per launch from hardware counters (GPT-2-small-shaped step, C4)\n\n")
+        fh.write("Commands (run from the repository root on one MI355X):\n\n```\n" + cmd + "\n```\n\n")
+        fh.write(f"Calibration: `{ck[:80]}` copying {CALIB_BYTES} bytes read FETCH_SIZE {cf:.1f} KiB "
+                 f"and WRITE_SIZE {cw:.1f} KiB; scale factors {f_scale:.4f} (fetch) and "
+                 f"{w_scale:.4f} (write) turn counter KiB into bytes.\n\n")
+        fh.write("| class | kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | "
+                 "scaled MB/launch |\n|---|---|---|---|---|---|\n")
+        fh.write("\n".join(lines) + "\n\n")
+        fh.write("Record read by bench.py (null traffic once the kernel sources differ from source_digest):\n\n")
+        fh.write("```json\n" + json.dumps(rec, indent=1) + "\n```\n")
+    print(out)
+
+
+def stats_summary(stats_csv, out, cmd="", steps=7):
+    """Kernel table from a rocprofv3 --stats kernel_stats.csv (Name, Calls,
+    TotalDurationNs, AverageNs), sorted by total time."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    with open(out, "w") as fh:
+        fh.write("# C4 training step: rocprofv3 kernel statistics\n\n")
+        fh.write("Workload: " + WORKLOADS["C4"] + ", one MI355X.\n\n")
+        fh.write("Command (repository root, on the GPU host):\n\n```\n" + cmd + "\n```\n\n")
+        fh.write(f"The run covers {steps} training steps (warm-up + timed) plus the parameter upload; totals are "
+                 f"over all of them (per-step time = total / {steps}). Source: the run's kernel_stats.csv.\n\n")
+        fh.write("| kernel | calls | total ms | avg us | share |\n|---|---:|---:|---:|---:|\n")
+        for r in rows:
+            t = float(r["TotalDurationNs"])
+            if t < 0.002 * total:
+                continue
+            fh.write(f"| `{r['Name'][:110]}` | {r['Calls']} | {t / 1e6:.2f} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{100 * t / total:.1f}% |\n")
+        fh.write(f"\nAll kernels: {total / 1e6:.2f} ms, {total / 1e6 / steps:.3f} ms per step.\n")
+    print(out)
+
+
+def traffic_of(cls):
+    """Counter-based HBM bytes per launch of a timing class, or None (no record,
+    or taken on different kernel sources)."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+        rec = json.loads(txt[txt.index("```json") + 7: txt.rindex("```")])
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest() or cls not in rec.get("classes", {}):
+        return None
+    return rec["classes"][cls]["bytes_per_launch"]
+
+
 def cpu_baseline(shape, budget_s=30.0):
     """The oracle (float64 numpy, untuned) on a bounded sample of the workload:
     one full step at batch 1 (same width, depth, vocabulary and sequence)."""
@@ -92,7 +208,20 @@ def main():
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prof", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run one plain device copy of a known size (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--pmc-cmd", default="", help="command line recorded in the summary")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
+                    help="write the kernel table of a rocprofv3 --stats run and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, cmd=args.pmc_cmd)
+        return
+    if args.stats_summary:
+        stats_summary(*args.stats_summary, cmd=args.pmc_cmd, steps=args.steps + args.warmup)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -114,6 +243,12 @@ def main():
     tgt = torch.from_numpy(batch.targets).cuda()
     doc = None if batch.doc_ids is None else torch.from_numpy(batch.doc_ids).cuda()
     stream = torch.cuda.current_stream()
+    if args.calib_copy:
+        src = torch.ones(CALIB_BYTES // 4, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     step_no = [0]
 
     def step():
@@ -173,16 +308,17 @@ def main():
         dom = max(prof.items(), key=lambda kv: kv[1]["ms"])
         name, v = dom
         per_launch_ms = v["ms"] / v["launches"]
+        traffic = traffic_of(name)
         if v["flops"] > 0:
             ach = v["flops"] / v["launches"] / (per_launch_ms * 1e-3) / 1e12
             out["roofline"] = {"kernel": name, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-                               "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                               "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
                                "per_launch_ms": round(per_launch_ms, 5),
                                "algorithmic_per_launch": v["flops"] / v["launches"]}
         else:
             ach = v["bytes"] / v["launches"] / (per_launch_ms * 1e-3) / 1e9
             out["roofline"] = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                               "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                               "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                                "per_launch_ms": round(per_launch_ms, 5),
                                "algorithmic_per_launch": v["bytes"] / v["launches"]}
         out["kernels"] = {k: {"ms_per_step": round(v["ms"] / args.steps, 4),

@@ -956,12 +956,6 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_bf16_pipe_kernel(GemmArgs
           if (it + S - 2 < nk) wait_vmcnt<(S - 2) * NLD>();
           else wait_vmcnt<0>();
           lds_barrier();
-          if (it + S - 1 < nk) {
-            constexpr int NX = (I + S - 1) % S;
-            bf16* sx = stage(std::integral_constant<int, NX>{});
-            la.load(sx, kb + (it + S - 1) * BK, ke);
-            lb.load(sx + LA::ELEMS, kb + (it + S - 1) * BK, ke);
-          }
           const bf16* sa = stage(I_);
           const bf16* sb = sa + LA::ELEMS;
           bf16x8_t af[2][TM], bfr[2][TN];
@@ -972,18 +966,38 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_bf16_pipe_kernel(GemmArgs
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const int f = ks & 1;
+            if (ks < 2) {
+              // the loads of step it + S - 1 (A during k-step 0, B during
+              // k-step 1), spread between the MFMAs; issued even past the
+              // last step, where every lane's offset is out of range (zeros
+              // into a stage nobody reads), so no branch splits the schedule
+              constexpr int NX = (I + S - 1) % S;
+              bf16* sx = stage(std::integral_constant<int, NX>{});
+              const int kn = it + S - 1 < nk ? kb + (it + S - 1) * BK : ke;
+              if (ks == 0) la.load(sx, kn, ke);
+              else lb.load(sx + LA::ELEMS, kn, ke);
+            }
             if (ks + 1 < KS) {
 #pragma unroll
               for (int i = 0; i < TM; ++i) af[f ^ 1][i] = LA::frag(sa, wm * WTM + i * 32, ks + 1, lane);
 #pragma unroll
               for (int j = 0; j < TN; ++j) bfr[f ^ 1][j] = LB::frag(sb, wn * WTN + j * 32, ks + 1, lane);
             }
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
               for (int j = 0; j < TN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[f][j], af[f][i], acc[i][j], 0, 0, 0);
+            // after each MFMA: one LDS read of the next k-step, one direct
+            // load and its address arithmetic
+#pragma unroll
+            for (int q = 0; q < TM * TN; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+              __builtin_amdgcn_sched_group_barrier(0x004, 2, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
           }
         }
