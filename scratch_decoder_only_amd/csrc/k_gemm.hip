@@ -5,14 +5,16 @@
 // Operations": matmul is the bottleneck); its CPU tiling for L1 is prior art,
 // here the contraction runs on the gfx950 matrix cores.
 //
-// bf16 path: 256 threads (2 x 2 wavefronts), block tile BM x BN, K step 64,
-// two LDS stages (global loads for step k+1 are in flight while step k runs on
-// the MFMA units). LDS rows hold 64 K-values plus 8 bf16 of padding (144 B),
-// which keeps the 16-byte fragment reads of 32 consecutive rows conflict-free.
-// Operands whose contiguous axis is M or N (the backward's dY^T and X^T, and
-// W read along its rows for dX) are loaded as 8 x 8 bf16 blocks and transposed
-// in registers before the LDS store, so every fragment read is K-contiguous.
-// Each wavefront computes (BM/2) x (BN/2) with v_mfma_f32_32x32x16_bf16.
+// bf16 path, v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
+//  * gemm_bf16_kernel: block tile BM x BN (default 128 x 128, 4 wavefronts of
+//    64 x 64, two blocks per CU), K step 64, two LDS stages fed from registers
+//    loaded two K steps ahead; LDS-staged epilogue.
+//  * gemm_bf16_pipe_kernel: persistent 256 x 256 tiles (8 wavefronts), direct
+//    global-to-LDS loads in S stages, register epilogue; used where the
+//    operand-load path rather than the matrix core bounds the 128 x 128 tile.
+// Operands whose contiguous axis is M or N (the backward's dY^T and X^T, and W
+// read along its rows for dX) stay in their memory layout in LDS and are read
+// as MFMA fragments with the transposing LDS read.
 //
 // fp32 path: fp32 matrix and vector peaks are equal on this chip (157 TF), so
 // the fp32 GEMM is a plain LDS-tiled FMA kernel (64 x 64 tile, 4 x 4 per
@@ -885,9 +887,9 @@ __device__ __forceinline__ void pipe_tile(int u, int tiles_m, int tiles_n, int& 
   tn = in / gsize;
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int S, bool AK, bool BKC, int EPI, typename TC>
-__global__ void __launch_bounds__(WGM * WGN * 64) gemm_bf16_pipe_kernel(GemmArgs p, int units, int tiles_m,
-                                                                         int tiles_n) {
+template <int BM, int BN, int WGM, int WGN, int BK, int S, int OCC, bool AK, bool BKC, int EPI, typename TC>
+__global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+    gemm_bf16_pipe_kernel(GemmArgs p, int units, int tiles_m, int tiles_n) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -1055,12 +1057,15 @@ static bool check_bf16(const GemmOp& op) {
 // (4 waves of 64 x 64, two blocks per CU), 2 = 256 x 96 (4 waves of 64 x 96),
 // 3 = 256 x 256 (8 waves of 64 x 128, two waves per SIMD).
 static int tiles_of(const GemmOp& op, int cfg) {
-  const int BM = (cfg == 1 || cfg == 4 || cfg == 5) ? 128 : 256;
-  const int BN = cfg == 2 ? 96 : (cfg == 3 || cfg >= 7) ? 256 : 128;
+  const int BM = (cfg == 1 || cfg == 4 || cfg == 5 || cfg == 13) ? 128 : 256;
+  const int BN = cfg == 2 ? 96 : (cfg == 3 || (cfg >= 7 && cfg != 12)) ? 256 : 128;
   return ((op.M + BM - 1) / BM) * ((op.N + BN - 1) / BN);
 }
 
-static bool is_pipe(int cfg) { return cfg >= 9 && cfg <= 11; }
+// Blocks of a configuration resident on one CU (the persistent grid's depth).
+static int blocks_per_cu(int cfg) { return cfg == 12 || cfg == 13 ? 2 : 1; }
+
+static bool is_pipe(int cfg) { return cfg >= 9 && cfg <= 13; }
 
 // Compute units of the current device (the persistent grid's size).
 static int device_cus() {
@@ -1084,7 +1089,7 @@ static int forced_cfg() {
 
 static int pick_cfg(const GemmOp& op) {
   const int f = forced_cfg();
-  if (f >= 0 && f <= 11 && (f != 2 || op.N % 96 == 0)) return f;
+  if (f >= 0 && f <= 13 && (f != 2 || op.N % 96 == 0)) return f;
   // Measured on the GPT-2-small-shaped step: the persistent 256 x 256 kernel
   // (8 waves of 128 x 64) wins on the vocabulary projection's forward (very
   // wide N) and its input gradient (very long K), and on the MLP weight
@@ -1104,7 +1109,7 @@ int gemm_bf16_splits(const GemmOp& op) {
     // persistent grid of one block per CU: pick the K split whose work units
     // fill the last round best (smallest split within 10% of the best fill),
     // with at least 512 K-values per slice
-    const int cus = device_cus();
+    const int cus = device_cus() * blocks_per_cu(cfg);
     auto fill = [&](int s) {
       const long u = (long)tiles * s;
       return (double)u / (double)(((u + cus - 1) / cus) * cus);
@@ -1146,31 +1151,34 @@ static int dispatch_bf16_direct(const GemmOp& op, const GemmArgs& a, int splits,
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int S, bool AK, bool BKC, int EPI, typename TC>
+// OCC: waves per SIMD the kernel is compiled for; blocks per CU = 4 OCC /
+// (WGM WGN), and the persistent grid holds that many blocks per CU.
+template <int BM, int BN, int WGM, int WGN, int BK, int S, int OCC, bool AK, bool BKC, int EPI, typename TC>
 static void launch_bf16_pipe(const GemmArgs& a, int splits, hipStream_t s) {
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   const int units = tiles_m * tiles_n * splits;
-  int nb = device_cus();
+  constexpr int per_cu = 4 * OCC / (WGM * WGN) > 0 ? 4 * OCC / (WGM * WGN) : 1;
+  int nb = device_cus() * per_cu;
   if (units < nb) nb = units;
   nb = (nb + 7) / 8 * 8;  // whole XCD rounds
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI, TC>), dim3(nb),
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI, TC>), dim3(nb),
                      dim3(WGM * WGN * 64), 0, s, a, units, tiles_m, tiles_n);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int S, bool AK, bool BKC>
+template <int BM, int BN, int WGM, int WGN, int BK, int S, int OCC, bool AK, bool BKC>
 static int dispatch_bf16_pipe(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
   if (splits > 1) {
-    launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_PARTIAL, float>(a, splits, s);
+    launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_PARTIAL, float>(a, splits, s);
     return 0;
   }
   switch (op.epi) {
     case EPI_STORE:
-      if (op.c_f32) launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_STORE, float>(a, 1, s);
-      else launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_STORE, bf16>(a, 1, s);
+      if (op.c_f32) launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_STORE, float>(a, 1, s);
+      else launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_STORE, bf16>(a, 1, s);
       return 0;
-    case EPI_RESID: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
-    case EPI_GELU: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
-    case EPI_DGELU: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
+    case EPI_RESID: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
+    case EPI_GELU: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
+    case EPI_DGELU: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
     default: return -1;
   }
 }
@@ -1211,9 +1219,11 @@ static int dispatch_bf16_epi(const GemmOp& op, const GemmArgs& a, int splits, hi
     case 6: return dispatch_bf16_direct<256, 128, 2, 2, 2, AK, BKC>(op, a, splits, s);
     case 7: return dispatch_bf16_direct<256, 256, 4, 2, 2, AK, BKC>(op, a, splits, s);
     case 8: return dispatch_bf16_direct<256, 256, 2, 2, 2, AK, BKC>(op, a, splits, s);
-    case 9: return dispatch_bf16_pipe<256, 256, 4, 2, 64, 2, AK, BKC>(op, a, splits, s);
-    case 10: return dispatch_bf16_pipe<256, 256, 4, 2, 32, 4, AK, BKC>(op, a, splits, s);
-    case 11: return dispatch_bf16_pipe<256, 256, 2, 4, 64, 2, AK, BKC>(op, a, splits, s);
+    case 9: return dispatch_bf16_pipe<256, 256, 4, 2, 64, 2, 2, AK, BKC>(op, a, splits, s);
+    case 10: return dispatch_bf16_pipe<256, 256, 4, 2, 32, 4, 2, AK, BKC>(op, a, splits, s);
+    case 11: return dispatch_bf16_pipe<256, 256, 2, 4, 64, 2, 2, AK, BKC>(op, a, splits, s);
+    case 12: return dispatch_bf16_pipe<256, 128, 4, 2, 32, 2, 4, AK, BKC>(op, a, splits, s);
+    case 13: return dispatch_bf16_pipe<128, 256, 2, 4, 32, 2, 4, AK, BKC>(op, a, splits, s);
     default: return dispatch_bf16_cfg<128, 128, 2, 2, AK, BKC>(op, a, splits, s);
   }
 }
