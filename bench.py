@@ -208,6 +208,7 @@ def main():
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prof", action="store_true")
+    ap.add_argument("--ckpt", metavar="DIR", help="also time a checkpoint save and load of the model in DIR")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain device copy of a known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -328,6 +329,24 @@ def main():
                           for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}
         log(f"bench: profiled pass {total_ms / args.steps:.3f} ms/step; dominant {name} "
             f"{per_launch_ms:.4f} ms/launch; GEMM+attention MFMA util {out['mfma_util']}")
+
+    if args.ckpt:
+        # checkpoint file of the multi-step driver: parameters + both Adam moments
+        os.makedirs(args.ckpt, exist_ok=True)
+        path = os.path.join(args.ckpt, f"bench_{args.config}.safetensors")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        model.save(path, step_no[0])
+        t_save = time.perf_counter() - t0
+        size = os.path.getsize(path)
+        t0 = time.perf_counter()
+        got = model.load(path)
+        t_load = time.perf_counter() - t0
+        os.remove(path)
+        out["checkpoint"] = {"bytes": size, "save_s": round(t_save, 3), "load_s": round(t_load, 3),
+                             "save_gbs": round(size / t_save / 1e9, 2), "load_gbs": round(size / t_load / 1e9, 2),
+                             "step": got}
+        log(f"bench: checkpoint {size / 1e9:.2f} GB saved in {t_save:.2f} s, loaded in {t_load:.2f} s")
 
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a bounded sample")

@@ -149,6 +149,36 @@ lm_status forward_logits(lm_model* model, const int32_t* d_tokens, const int32_t
 /* Thread-local message for the last non-OK status of this thread. */
 const char* lm_last_error(void);
 
+/* The configuration the model was created with. */
+lm_status model_config(const lm_model* model, lm_config* out);
+
+/* ---- multi-step training (LucilleAI page, usage of its trainers: a cosine
+ * learning-rate scheduler with warm-up steps and a minimum rate, checkpoints
+ * every N steps and runs resumed from one; Smallem page, "Les regles du jeu":
+ * weight files carry a JSON header) ---- */
+
+/* Learning rate of 1-based step `step` (values below 1 count as 1): linear
+ * warm-up lr_max * step / warmup_steps while step <= warmup_steps; then a half
+ * cosine from lr_max down to lr_min, lr_min + (lr_max - lr_min) (1 + cos(pi p))
+ * / 2 with p = (step - warmup_steps) / (total_steps - warmup_steps); lr_min
+ * from total_steps on. total_steps <= warmup_steps: lr_max after the warm-up
+ * (no decay). Pure host function, evaluated in double. */
+float lm_lr_schedule(int32_t step, int32_t warmup_steps, int32_t total_steps, float lr_max, float lr_min);
+
+/* Checkpoint file in the safetensors layout: 8-byte little-endian header
+ * length, JSON header, raw little-endian fp32 data. Tensors "param.<name>",
+ * "adam_m.<name>", "adam_v.<name>" for every entry of the parameter table
+ * (shape [rows, cols], or [rows] for vectors), back to back in that order;
+ * "__metadata__" holds format "lmstep-checkpoint", version, step and the model
+ * dimensions as strings. model_save synchronises `stream`, writes path.tmp and
+ * renames it to path. model_load checks the format, every dimension, dtype,
+ * shape and offset (LM_ERR_SHAPE on a model mismatch, LM_ERR_ARG on a bad
+ * file), restores parameters (and their bf16 copy) and both moments, and
+ * returns the saved step in *step (nullable). Gradients are not saved: the
+ * next train_step recomputes them. */
+lm_status model_save(const lm_model* model, const char* path, int32_t step, void* stream);
+lm_status model_load(lm_model* model, const char* path, int32_t* step, void* stream);
+
 /* ---- measurement hooks (used by the benchmark) ----
  * With profiling on, every kernel launch of train_step is bracketed by a pair
  * of HIP events recorded on the step's stream, and model_profile_read sums

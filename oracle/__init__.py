@@ -31,3 +31,4 @@ from .model import (  # noqa: F401
     train_step,
     csr_by_key,
 )
+from .schedule import lr_schedule  # noqa: F401

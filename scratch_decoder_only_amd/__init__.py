@@ -72,6 +72,10 @@ _sig("train_step", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.c_int3
                            ctypes.POINTER(LmOptim), c_void_p, c_void_p])
 _sig("forward_logits", c_int, [c_void_p, c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_void_p])
 _sig("lm_last_error", c_char_p, [])
+_sig("model_config", c_int, [c_void_p, ctypes.POINTER(LmConfig)])
+_sig("lm_lr_schedule", ctypes.c_float, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float])
+_sig("model_save", c_int, [c_void_p, c_char_p, ctypes.c_int32, c_void_p])
+_sig("model_load", c_int, [c_void_p, c_char_p, ctypes.POINTER(ctypes.c_int32), c_void_p])
 _sig("model_profile_enable", c_int, [c_void_p, c_int])
 _sig("model_profile_read", c_int, [c_void_p, ctypes.POINTER(LmProfileEntry), ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_int32), c_int])
@@ -218,6 +222,17 @@ class Model:
                "forward_logits")
         return out
 
+    # ---- checkpoints
+    def save(self, path: str, step: int):
+        """Parameters and Adam moments to a checkpoint file (safetensors layout)."""
+        _check(_lib.model_save(self._h, os.fsencode(path), int(step), _stream()), "model_save")
+
+    def load(self, path: str) -> int:
+        """Restores parameters and moments from a checkpoint; returns its step."""
+        st = ctypes.c_int32(0)
+        _check(_lib.model_load(self._h, os.fsencode(path), ctypes.byref(st), _stream()), "model_load")
+        return st.value
+
     # ---- measurement hooks
     def profile(self, enable: bool):
         _check(_lib.model_profile_enable(self._h, 1 if enable else 0), "model_profile_enable")
@@ -230,6 +245,39 @@ class Model:
                "model_profile_read")
         return {e.name.decode(): {"launches": e.launches, "ms": e.ms, "flops": e.flops, "bytes": e.bytes}
                 for e in arr[:n.value]}
+
+
+# ------------------------------------------------------------ training driver
+
+def lr_schedule(step: int, warmup_steps: int, total_steps: int, lr_max: float, lr_min: float) -> float:
+    """Learning rate of 1-based step: linear warm-up, then a half cosine down
+    to lr_min at total_steps (the library's lm_lr_schedule)."""
+    return float(_lib.lm_lr_schedule(int(step), int(warmup_steps), int(total_steps), float(lr_max), float(lr_min)))
+
+
+def train(model: "Model", batch, steps: int, *, lr_max: float, lr_min: float = 0.0, warmup_steps: int = 0,
+          total_steps: Optional[int] = None, start_step: int = 1, save_every: int = 0, ckpt_path=None, **opt):
+    """Runs `steps` training steps from `start_step` on the model's stream.
+
+    batch: (tokens, targets, doc_ids) device tensors, or a callable step ->
+    such a tuple. The learning rate follows lr_schedule(step, warmup_steps,
+    total_steps or the last step, lr_max, lr_min); every `save_every` steps the
+    model is saved to ckpt_path. opt: beta1, beta2, eps, weight_decay, clip.
+    Returns the per-step losses as a device tensor (no host synchronisation).
+    """
+    torch = _torch()
+    last = start_step + steps - 1
+    total = last if total_steps is None else total_steps
+    losses = torch.zeros(steps, dtype=torch.float32, device=model.stats.device)
+    for i in range(steps):
+        step = start_step + i
+        tok, tgt, doc = batch(step) if callable(batch) else batch
+        lr = lr_schedule(step, warmup_steps, total, lr_max, lr_min)
+        model.train_step(tok, tgt, doc, lr=lr, step=step, **opt)
+        losses[i:i + 1].copy_(model.stats[0:1])
+        if save_every and ckpt_path and step % save_every == 0:
+            model.save(ckpt_path, step)
+    return losses
 
 
 # --------------------------------------------------------------- kernel level

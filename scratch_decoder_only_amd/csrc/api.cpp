@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/lmstep.h"
+#include "host.h"
 #include "kernels.h"
 
 using namespace lm;
@@ -24,6 +25,13 @@ lm_status fail(lm_status st, const std::string& msg) {
   g_err = msg;
   return st;
 }
+
+}  // namespace
+
+// Error message for the other host files of the library (checkpoint I/O).
+lm_status lm::set_error(lm_status st, const std::string& msg) { return fail(st, msg); }
+
+namespace {
 
 constexpr size_t kAlign = 256;
 
@@ -565,6 +573,12 @@ lm_status model_create(const lm_config* cfg, void* d_arena, size_t arena_bytes, 
 }
 
 void model_destroy(lm_model* m) { delete m; }
+
+lm_status model_config(const lm_model* m, lm_config* out) {
+  if (!m || !out) return fail(LM_ERR_ARG, "model or out is NULL");
+  *out = m->cfg;
+  return LM_OK;
+}
 
 lm_status model_param_table(const lm_model* m, lm_tensor_info* out, int32_t* count, int64_t* total) {
   if (!m || !count) return fail(LM_ERR_ARG, "model or count is NULL");

@@ -182,6 +182,21 @@ def make_batch(shape: ModelShape, seed: Optional[int] = None) -> Batch:
     return Batch(tokens, targets, doc_ids, n_docs)
 
 
+def structured_batch(shape: ModelShape, seed: int = 7, period: int = 16, batch: Optional[int] = None) -> Batch:
+    """Learnable synthetic text for loss-descent runs (no corpus exists here):
+    a seeded cycle of `period` distinct ids; every row starts at a random point
+    of the cycle and walks it, so the next id is a function of the current
+    one. T + 1 ids per row: inputs the first T, targets the last T."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B = shape.batch if batch is None else batch
+    T, V = shape.seq, shape.vocab
+    cycle = rng.choice(V, size=min(period, V), replace=False).astype(np.int32)
+    starts = rng.integers(0, len(cycle), size=B)
+    idx = (starts[:, None] + np.arange(T + 1)[None, :]) % len(cycle)
+    ids = cycle[idx]
+    return Batch(np.ascontiguousarray(ids[:, :T]), np.ascontiguousarray(ids[:, 1:]), None, B)
+
+
 # --------------------------------------------------------------------- parameters
 
 def param_specs(shape: ModelShape) -> List[Tuple[str, Tuple[int, ...]]]:
