@@ -209,6 +209,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prof", action="store_true")
     ap.add_argument("--ckpt", metavar="DIR", help="also time a checkpoint save and load of the model in DIR")
+    ap.add_argument("--gen", type=int, default=0, metavar="N",
+                    help="also time greedy generation of N tokens per row after a 128-token prompt")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain device copy of a known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -329,6 +331,31 @@ def main():
                           for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}
         log(f"bench: profiled pass {total_ms / args.steps:.3f} ms/step; dominant {name} "
             f"{per_launch_ms:.4f} ms/launch; GEMM+attention MFMA util {out['mfma_util']}")
+
+    if args.gen:
+        # generation through forward_logits (no key/value cache) and the
+        # next-token kernel; the sampler alone on the last position's logits
+        T0 = min(128, T - args.gen)
+        prompt = tok[:, :T0].contiguous()
+        sd.generate(model, prompt, 1)  # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        sd.generate(model, prompt, args.gen)
+        torch.cuda.synchronize()
+        t_gen = time.perf_counter() - t0
+        logits = model.forward_logits(prompt)[:, T0 - 1, :]
+        u = torch.rand(B, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            sd.sample_tokens(logits, 1.0, 50, u)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["generation"] = {"batch": B, "prompt": T0, "new_tokens": args.gen, "kv_cache": False,
+                             "tokens_per_s": round(B * args.gen / t_gen, 1),
+                             "ms_per_token_step": round(t_gen / args.gen * 1e3, 3),
+                             "sample_us_per_call": round(e0.elapsed_time(e1) / 10 * 1e3, 1)}
+        log(f"bench: generation {B}x{args.gen} tokens in {t_gen:.2f} s")
 
     if args.ckpt:
         # checkpoint file of the multi-step driver: parameters + both Adam moments

@@ -179,6 +179,20 @@ float lm_lr_schedule(int32_t step, int32_t warmup_steps, int32_t total_steps, fl
 lm_status model_save(const lm_model* model, const char* path, int32_t step, void* stream);
 lm_status model_load(lm_model* model, const char* path, int32_t* step, void* stream);
 
+/* ---- generation (RustGPT page, technical list: greedy decoding; LucilleAI
+ * page: a sampler with temperature and top-k) ----
+ * Next token of each of `rows` rows of fp32 logits (row r starts at
+ * d_logits + r * ld, `vocab` columns; ld >= vocab), into d_out [rows] int32.
+ * temperature <= 0: greedy, the largest logit, ties to the smallest id
+ * (d_uniforms may be NULL). Otherwise the top_k largest logits (top_k <= 0 or
+ * >= vocab: all; ties at the k-th value go to the smaller ids) with weights
+ * exp((z - z_max) / temperature); the caller's uniform u in [0, 1) for the row
+ * (d_uniforms [rows], device) picks the smallest kept id whose running weight
+ * sum, in ascending id order, reaches u times the total. Deterministic: the
+ * same inputs give the same ids. Enqueued on `stream`. */
+lm_status sample_tokens(const float* d_logits, int32_t rows, int32_t vocab, int64_t ld, float temperature,
+                        int32_t top_k, const float* d_uniforms, int32_t* d_out, void* stream);
+
 /* ---- measurement hooks (used by the benchmark) ----
  * With profiling on, every kernel launch of train_step is bracketed by a pair
  * of HIP events recorded on the step's stream, and model_profile_read sums

@@ -32,3 +32,4 @@ from .model import (  # noqa: F401
     csr_by_key,
 )
 from .schedule import lr_schedule  # noqa: F401
+from .generate import next_token, kept_ids, cdf_bounds  # noqa: F401

@@ -76,6 +76,8 @@ _sig("model_config", c_int, [c_void_p, ctypes.POINTER(LmConfig)])
 _sig("lm_lr_schedule", ctypes.c_float, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float])
 _sig("model_save", c_int, [c_void_p, c_char_p, ctypes.c_int32, c_void_p])
 _sig("model_load", c_int, [c_void_p, c_char_p, ctypes.POINTER(ctypes.c_int32), c_void_p])
+_sig("sample_tokens", c_int, [c_void_p, ctypes.c_int32, ctypes.c_int32, c_int64, ctypes.c_float, ctypes.c_int32,
+                              c_void_p, c_void_p, c_void_p])
 _sig("model_profile_enable", c_int, [c_void_p, c_int])
 _sig("model_profile_read", c_int, [c_void_p, ctypes.POINTER(LmProfileEntry), ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_int32), c_int])
@@ -278,6 +280,48 @@ def train(model: "Model", batch, steps: int, *, lr_max: float, lr_min: float = 0
         if save_every and ckpt_path and step % save_every == 0:
             model.save(ckpt_path, step)
     return losses
+
+
+# ------------------------------------------------------------------ generation
+
+def sample_tokens(logits, temperature: float = 0.0, top_k: int = 0, uniforms=None, out=None):
+    """Next token of each row of `logits` (a 2-D fp32 CUDA tensor whose rows
+    may be strided): greedy for temperature <= 0, else top-k sampling that
+    picks with the given per-row uniforms in [0, 1) (a CUDA fp32 tensor)."""
+    torch = _torch()
+    rows, vocab = logits.shape
+    assert logits.dtype == torch.float32 and logits.stride(1) == 1
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    _check(_lib.sample_tokens(_ptr(logits), rows, vocab, logits.stride(0), float(temperature), int(top_k),
+                              _ptr(uniforms), _ptr(out), _stream()), "sample_tokens")
+    return out
+
+
+def generate(model: "Model", prompt, n_new: int, *, temperature: float = 0.0, top_k: int = 0, seed: int = 0):
+    """Extends each row of `prompt` ([B, T0] int32 CUDA tensor) by n_new tokens:
+    every new token comes from forward_logits over the whole sequence so far
+    (no key/value cache) and sample_tokens on its last position. Uniforms for
+    sampling are drawn on the host from numpy's PCG64(seed), one per row and
+    step, and passed in. Returns the [B, T0 + n_new] token tensor."""
+    torch = _torch()
+    B, T0 = prompt.shape
+    if T0 + n_new > model.cfg.max_seq:
+        raise LmError("prompt plus new tokens exceed max_seq")
+    toks = torch.zeros((B, T0 + n_new), dtype=torch.int32, device=prompt.device)
+    toks[:, :T0] = prompt
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for i in range(n_new):
+        T = T0 + i
+        cur = toks[:, :T].contiguous()
+        logits = model.forward_logits(cur)
+        last = logits[:, T - 1, :]
+        u = None
+        if temperature > 0:
+            u = torch.from_numpy(rng.random(B).astype(np.float32)).to(prompt.device)
+        nxt = sample_tokens(last, temperature, top_k, u)
+        toks[:, T] = nxt
+    return toks
 
 
 # --------------------------------------------------------------- kernel level

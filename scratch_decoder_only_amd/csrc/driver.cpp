@@ -1,5 +1,5 @@
-// Multi-step training around train_step: the learning-rate schedule and
-// checkpoint files.
+// Multi-step training around train_step (the learning-rate schedule and
+// checkpoint files) and the host side of generation (next-token choice).
 //
 // Schedule (LucilleAI page, usage of the SFT trainer: a cosine scheduler with
 // warm-up steps and a minimum learning rate): linear warm-up to lr_max, then a
@@ -26,6 +26,7 @@
 
 #include "../../include/lmstep.h"
 #include "host.h"
+#include "kernels.h"
 
 using lm::set_error;
 
@@ -334,6 +335,19 @@ lm_status model_load(lm_model* m, const char* path, int32_t* step, void* stream)
     if ((st = model_set(m, sec.buf, host.get(), 0, stream)) != LM_OK) return st;
   }
   if (step) *step = (int32_t)saved_step;
+  return LM_OK;
+}
+
+lm_status sample_tokens(const float* d_logits, int32_t rows, int32_t vocab, int64_t ld, float temperature,
+                        int32_t top_k, const float* d_uniforms, int32_t* d_out, void* stream) {
+  if (!d_logits || !d_out) return set_error(LM_ERR_ARG, "logits or out is NULL");
+  if (rows < 0 || vocab < 1 || ld < vocab) return set_error(LM_ERR_SHAPE, "need rows >= 0, vocab >= 1, ld >= vocab");
+  if (temperature > 0.f && !d_uniforms) return set_error(LM_ERR_ARG, "sampling needs one uniform per row");
+  if (rows == 0) return LM_OK;
+  lm::launch_sample(d_logits, rows, vocab, (long)ld, temperature, top_k, d_uniforms, d_out,
+                    reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(LM_ERR_HIP, std::string("sample_tokens: ") + hipGetErrorString(e));
   return LM_OK;
 }
 

@@ -152,4 +152,11 @@ struct AdamArgs {
 void launch_adamw(const AdamArgs& a, hipStream_t s);
 void launch_make_shadow(const float* p, long n, bf16* shadow, long split, long shift, hipStream_t s);
 
+// ------------------------------------------------------------- generation
+// Next token of each of `rows` logit rows (row r at logits + r * ld, V
+// columns): greedy when temperature <= 0, else top-k sampling with the given
+// uniforms; out [rows].
+void launch_sample(const float* logits, int rows, int V, long ld, float temperature, int top_k, const float* u,
+                   int32_t* out, hipStream_t s);
+
 }  // namespace lm

@@ -1,6 +1,8 @@
-"""The multi-step driver's learning-rate schedule: the oracle against closed
-forms of its reading (warm-up line, half cosine, floor), and the library's
-host function (lm_lr_schedule, no GPU involved) against the oracle."""
+"""Pins of the multi-step driver's and the generator's oracle functions:
+the learning-rate schedule against closed forms of its reading (warm-up line,
+half cosine, floor), the library's host schedule (lm_lr_schedule, no GPU
+involved) against the oracle, and the next-token choice against closed forms
+(ties, equal logits, the two-token logistic, top-1)."""
 import ctypes
 import math
 import os
@@ -64,3 +66,43 @@ def test_library_schedule_matches_oracle(lib, W, S, lr, lo):
         ref = oracle.lr_schedule(k, W, S, ctypes.c_float(lr).value, ctypes.c_float(lo).value)
         # the library rounds its float64 value to fp32 once
         assert abs(got - ref) <= 2 ** -23 * abs(ref) + 1e-30, (k, got, ref)
+
+
+# ------------------------------------------------------------- generation
+# Pins of the oracle's next-token choice (closed forms of the sampler reading).
+
+def test_greedy_takes_the_first_of_tied_maxima():
+    z = [0.5, 2.0, -1.0, 2.0, 1.9]
+    assert oracle.next_token(z, 0.0, 0, 0.3) == 1
+    assert oracle.next_token(z, -1.0, 3, 0.9) == 1
+
+
+def test_equal_logits_sample_uniformly_over_the_kept_ids():
+    V, k = 40, 8
+    z = [0.25] * V
+    for j in range(k):
+        u = (j + 0.5) / k
+        # ties at the k-th value keep the smaller ids: ids 0..k-1, picked by floor(u k)
+        assert oracle.next_token(z, 1.3, k, u) == j
+    assert oracle.next_token(z, 1.3, 0, 0.999) == V - 1
+
+
+def test_two_tokens_follow_the_logistic():
+    a, b, T = 0.3, 1.1, 0.7
+    p0 = 1.0 / (1.0 + math.exp((b - a) / T))
+    assert oracle.next_token([a, b], T, 0, p0 * 0.999) == 0
+    assert oracle.next_token([a, b], T, 0, p0 * 1.001) == 1
+
+
+def test_top_1_is_greedy_and_top_k_drops_the_rest():
+    z = [0.1, 3.0, 2.5, -4.0, 2.9]
+    for u in (0.0, 0.3, 0.999):
+        assert oracle.next_token(z, 2.0, 1, u) == 1
+    # top 3 = {1, 2, 4}: ids 0 and 3 never come out
+    picks = {oracle.next_token(z, 5.0, 3, u) for u in [i / 97 for i in range(97)]}
+    assert picks == {1, 2, 4}
+
+
+def test_low_temperature_approaches_greedy():
+    z = [0.0, 1.0, 0.99, -2.0]
+    assert oracle.next_token(z, 1e-3, 0, 0.5) == 1
