@@ -50,18 +50,23 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 
 // tanh(y) = 1 - 2 / (exp(2y) + 1): saturates to +-1 without overflow trouble.
-__device__ __forceinline__ float tanh_exp(float y) { return 1.0f - 2.0f / (__expf(2.0f * y) + 1.0f); }
 
-// GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
-__device__ __forceinline__ float gelu_f(float u) {
-  const float c = 0.7978845608028654f, a = 0.044715f;
-  return 0.5f * u * (1.0f + tanh_exp(c * (u + a * u * u * u)));
+// GELU, tanh form: 0.5 u (1 + tanh(y)), y = sqrt(2/pi) (u + 0.044715 u^3),
+// evaluated as u s with s = 0.5 (1 + tanh(y)) = 1 / (1 + exp(-2y)) (the same
+// function); the reciprocal is the hardware one (about 1 ulp), so no IEEE
+// division sequence runs per element.
+__device__ __forceinline__ float gelu_sigmoid(float u) {
+  const float c2 = 2.0f * 0.7978845608028654f, a = 0.044715f;
+  const float y2 = c2 * u * __builtin_fmaf(a, u * u, 1.0f);
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-y2));
 }
-// Its derivative: 0.5 (1 + t) + 0.5 u (1 - t^2) c (1 + 3 a u^2).
+__device__ __forceinline__ float gelu_f(float u) { return u * gelu_sigmoid(u); }
+// Its derivative: 0.5 (1 + t) + 0.5 u (1 - t^2) c (1 + 3 a u^2) with t =
+// tanh(y); in terms of s: s + 2 u s (1 - s) c (1 + 3 a u^2).
 __device__ __forceinline__ float gelu_grad_f(float u) {
   const float c = 0.7978845608028654f, a = 0.044715f;
-  float t = tanh_exp(c * (u + a * u * u * u));
-  return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * c * (1.0f + 3.0f * a * u * u);
+  const float s = gelu_sigmoid(u);
+  return __builtin_fmaf(2.0f * c * u * s * (1.0f - s), __builtin_fmaf(3.0f * a, u * u, 1.0f), s);
 }
 
 }  // namespace lm

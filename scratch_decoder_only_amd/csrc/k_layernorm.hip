@@ -102,16 +102,38 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const float* __restrict__ d
   }
   const long r0 = (long)blockIdx.x * kLnRowsPerBlock;
   const long r1 = min((long)M, r0 + kLnRowsPerBlock);
-  for (long m = r0 + w; m < r1; m += 4) {
+  // the next row's inputs are loaded while the current row is computed
+  float2 dn[NV], xn[NV], gn[NV];
+  float mun = 0.f, rn = 0.f;
+  auto load_row = [&](long m) {
     const float2* dyr = reinterpret_cast<const float2*>(dy + m * C);
     const float2* xr = reinterpret_cast<const float2*>(x + m * C);
-    const float mu = mu_in[m], r = rstd_in[m];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      dn[j] = dyr[lane + 64 * j];
+      xn[j] = xr[lane + 64 * j];
+      gn[j] = g_in ? reinterpret_cast<const float2*>(g_in + m * C)[lane + 64 * j] : make_float2(0.f, 0.f);
+    }
+    mun = mu_in[m];
+    rn = rstd_in[m];
+  };
+  if (r0 + w < r1) load_row(r0 + w);
+  for (long m = r0 + w; m < r1; m += 4) {
+    float2 dv[NV], xv[NV], gi[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      dv[j] = dn[j];
+      xv[j] = xn[j];
+      gi[j] = gn[j];
+    }
+    const float mu = mun, r = rn;
+    if (m + 4 < r1) load_row(m + 4);
     float2 xh[NV], dxh[NV];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      float2 d = dyr[lane + 64 * j], xv = xr[lane + 64 * j];
-      xh[j] = make_float2((xv.x - mu) * r, (xv.y - mu) * r);
+      const float2 d = dv[j];
+      xh[j] = make_float2((xv[j].x - mu) * r, (xv[j].y - mu) * r);
       dxh[j] = make_float2(d.x * gg[j].x, d.y * gg[j].y);
       s1 += dxh[j].x + dxh[j].y;
       s2 += dxh[j].x * xh[j].x + dxh[j].y * xh[j].y;
@@ -123,20 +145,17 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const float* __restrict__ d
     const float m1 = wave_sum(s1) * (1.0f / C), m2 = wave_sum(s2) * (1.0f / C);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      int c = 2 * (lane + 64 * j);
-      float dx0 = r * (dxh[j].x - m1 - xh[j].x * m2);
-      float dx1 = r * (dxh[j].y - m1 - xh[j].y * m2);
-      if (g_in) {
-        float2 gi = reinterpret_cast<const float2*>(g_in + m * C)[lane + 64 * j];
-        dx0 += gi.x;
-        dx1 += gi.y;
-      }
+      const int c = 2 * (lane + 64 * j);
+      const float dx0 = r * (dxh[j].x - m1 - xh[j].x * m2) + gi[j].x;
+      const float dx1 = r * (dxh[j].y - m1 - xh[j].y * m2) + gi[j].y;
       reinterpret_cast<float2*>(g_out + m * C)[lane + 64 * j] = make_float2(dx0, dx1);
       adc[j].x += dx0;
       adc[j].y += dx1;
       if (g_act) {
-        Act<T>::st(g_act, m * C + c, dx0);
-        Act<T>::st(g_act, m * C + c + 1, dx1);
+        if (sizeof(T) == 2)  // two adjacent bf16 in one 4-byte store
+          reinterpret_cast<uint32_t*>(g_act)[(m * C + c) >> 1] = (uint32_t)f2bf(dx0) | ((uint32_t)f2bf(dx1) << 16);
+        else
+          reinterpret_cast<float2*>(g_act)[(m * C + c) >> 1] = make_float2(dx0, dx1);
       }
     }
   }

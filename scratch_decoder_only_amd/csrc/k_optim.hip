@@ -65,27 +65,31 @@ void launch_norm_finalize(const double* part, float clip, float* norm_scale, uin
   hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(256), 0, s, part, clip, norm_scale, flags, stats);
 }
 
-__device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, const AdamArgs& a, float sc) {
+// rb1, rb2: 1 / (1 - beta^t), computed once per thread; the per-element
+// division by sqrt(v_hat) + eps uses the hardware reciprocal (about 1 ulp).
+__device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, const AdamArgs& a, float sc,
+                                         float rb1, float rb2) {
   const float gh = sc * g;
   m = a.beta1 * m + (1.0f - a.beta1) * gh;
   v = a.beta2 * v + (1.0f - a.beta2) * gh * gh;
-  const float mh = m / a.bc1, vh = v / a.bc2;
-  p = p - a.lr * (mh / (sqrtf(vh) + a.eps) + a.wd * p);
+  const float mh = m * rb1, vh = v * rb2;
+  p = p - a.lr * (mh * __builtin_amdgcn_rcpf(sqrtf(vh) + a.eps) + a.wd * p);
 }
 
 __global__ void __launch_bounds__(256) adamw_kernel(AdamArgs a) {
   if (*a.flags & 1u) return;  // non-finite gradient norm: leave everything as it was
   const float sc = a.norm_scale[1];
+  const float rb1 = 1.0f / a.bc1, rb2 = 1.0f / a.bc2;
   const long n4 = a.n / 4;
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
     float4 p = reinterpret_cast<float4*>(a.p)[i];
     float4 g = reinterpret_cast<const float4*>(a.g)[i];
     float4 m = reinterpret_cast<float4*>(a.m)[i];
     float4 v = reinterpret_cast<float4*>(a.v)[i];
-    adam_one(p.x, g.x, m.x, v.x, a, sc);
-    adam_one(p.y, g.y, m.y, v.y, a, sc);
-    adam_one(p.z, g.z, m.z, v.z, a, sc);
-    adam_one(p.w, g.w, m.w, v.w, a, sc);
+    adam_one(p.x, g.x, m.x, v.x, a, sc, rb1, rb2);
+    adam_one(p.y, g.y, m.y, v.y, a, sc, rb1, rb2);
+    adam_one(p.z, g.z, m.z, v.z, a, sc, rb1, rb2);
+    adam_one(p.w, g.w, m.w, v.w, a, sc, rb1, rb2);
     reinterpret_cast<float4*>(a.p)[i] = p;
     reinterpret_cast<float4*>(a.m)[i] = m;
     reinterpret_cast<float4*>(a.v)[i] = v;
