@@ -27,52 +27,62 @@ __global__ void csr_count_kernel(const int32_t* __restrict__ keys, int M, int nk
 }
 
 // Exclusive scans of counts (-> offsets) and of ceil(count / kSegRows)
-// (-> chunk_base), each with nkeys + 1 entries. One block of 1024 threads;
-// every thread scans a contiguous slice serially (its loads issued in
-// batches of 8), then the slice totals are scanned in LDS.
+// (-> chunk_base), each with nkeys + 1 entries. One block of 1024 threads
+// walks the keys in rounds of 4096 (4 consecutive keys per thread, loads
+// coalesced across the block): per round a wavefront scan, the 16 wavefront
+// totals in LDS, and a running carry.
 __global__ void __launch_bounds__(1024) csr_scan_kernel(const int32_t* __restrict__ counts, int nkeys,
                                                         int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ chunk_base) {
-  __shared__ int s_a[1024], s_b[1024];
+  __shared__ int s_a[16], s_b[16];
   const int n = nkeys + 1;
-  const int per = (n + 1023) / 1024;
-  const int t = threadIdx.x, lo = t * per, hi = min(n, lo + per);
-  auto cnt = [&](int v) { return v < hi && v < nkeys ? counts[v] : 0; };
-  int sa = 0, sb = 0;
-  for (int v = lo; v < hi; v += 8) {
-    int c[8];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int carry_a = 0, carry_b = 0;
+  for (int base = 0; base < n; base += 4096) {
+    const int i0 = base + 4 * t;
+    int c[4], a = 0, b = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) c[u] = cnt(v + u);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      sa += c[u];
-      sb += (c[u] + kSegRows - 1) / kSegRows;
+    for (int u = 0; u < 4; ++u) {
+      c[u] = i0 + u < nkeys ? counts[i0 + u] : 0;
+      a += c[u];
+      b += (c[u] + kSegRows - 1) / kSegRows;
     }
-  }
-  s_a[t] = sa;
-  s_b[t] = sb;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the 1024 slice totals
-  for (int o = 1; o < 1024; o <<= 1) {
-    int a = t >= o ? s_a[t - o] : 0, b = t >= o ? s_b[t - o] : 0;
-    __syncthreads();
-    s_a[t] += a;
-    s_b[t] += b;
-    __syncthreads();
-  }
-  int ra = s_a[t] - sa, rb = s_b[t] - sb;
-  for (int v = lo; v < hi; v += 8) {
-    int c[8];
+    int xa = a, xb = b;  // inclusive wavefront scans
 #pragma unroll
-    for (int u = 0; u < 8; ++u) c[u] = cnt(v + u);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (v + u < hi) {
-        offsets[v + u] = ra;
-        chunk_base[v + u] = rb;
-        ra += c[u];
-        rb += (c[u] + kSegRows - 1) / kSegRows;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int ya = __shfl_up(xa, o, 64), yb = __shfl_up(xb, o, 64);
+      if (lane >= o) {
+        xa += ya;
+        xb += yb;
       }
+    }
+    __syncthreads();
+    if (lane == 63) {
+      s_a[w] = xa;
+      s_b[w] = xb;
+    }
+    __syncthreads();
+    int pa = 0, pb = 0, ta = 0, tb = 0;
+    for (int q = 0; q < 16; ++q) {
+      if (q < w) {
+        pa += s_a[q];
+        pb += s_b[q];
+      }
+      ta += s_a[q];
+      tb += s_b[q];
+    }
+    int ra = carry_a + pa + xa - a, rb = carry_b + pb + xb - b;  // exclusive prefix of key i0
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u < n) {
+        offsets[i0 + u] = ra;
+        chunk_base[i0 + u] = rb;
+      }
+      ra += c[u];
+      rb += (c[u] + kSegRows - 1) / kSegRows;
+    }
+    carry_a += ta;
+    carry_b += tb;
   }
 }
 
@@ -119,24 +129,49 @@ __device__ __forceinline__ int find_key(const int32_t* __restrict__ chunk_base, 
 
 // One block per chunk (grid-stride): sum its rows in sorted order. A key with
 // a single chunk is added to dst directly; otherwise the chunk sum goes to
-// partial[w].
+// partial[w]. The chunk's row ids are staged in LDS; with C a multiple of 4
+// each thread sums 4 columns and keeps 8 rows' loads in flight (the additions
+// stay in row order).
 __global__ void __launch_bounds__(256) segsum_chunks_kernel(const float* __restrict__ dx, int C, int nkeys,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ chunk_base,
                                                             const int32_t* __restrict__ perm,
                                                             float* __restrict__ partial, float* __restrict__ dst) {
+  __shared__ int s_rows[kSegRows];
   const int total = chunk_base[nkeys];
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const int v = find_key(chunk_base, nkeys, w);
     const int j = w - chunk_base[v];
     const int s0 = offsets[v] + j * kSegRows;
     const int s1 = min(offsets[v + 1], s0 + kSegRows);
+    const int nr = s1 - s0;
     const bool single = (chunk_base[v + 1] - chunk_base[v]) == 1;
-    for (int c = threadIdx.x; c < C; c += 256) {
-      float acc = 0.f;
-      for (int s = s0; s < s1; ++s) acc += dx[(long)perm[s] * C + c];
-      if (single) dst[(long)v * C + c] += acc;
-      else partial[(long)w * C + c] = acc;
+    __syncthreads();  // the previous chunk's rows are no longer read
+    if ((int)threadIdx.x < nr) s_rows[threadIdx.x] = perm[s0 + threadIdx.x];
+    __syncthreads();
+    if ((C & 3) == 0) {
+      for (int c4 = threadIdx.x; c4 < (C >> 2); c4 += 256) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        int r = 0;
+        for (; r + 8 <= nr; r += 8) {
+          f32x4_t x[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const f32x4_t*>(dx + (long)s_rows[r + u] * C + 4 * c4);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc += x[u];
+        }
+        for (; r < nr; ++r) acc += *reinterpret_cast<const f32x4_t*>(dx + (long)s_rows[r] * C + 4 * c4);
+        float* o = single ? dst + (long)v * C + 4 * c4 : partial + (long)w * C + 4 * c4;
+        if (single) *reinterpret_cast<f32x4_t*>(o) += acc;
+        else *reinterpret_cast<f32x4_t*>(o) = acc;
+      }
+    } else {
+      for (int c = threadIdx.x; c < C; c += 256) {
+        float acc = 0.f;
+        for (int r = 0; r < nr; ++r) acc += dx[(long)s_rows[r] * C + c];
+        if (single) dst[(long)v * C + c] += acc;
+        else partial[(long)w * C + c] = acc;
+      }
     }
   }
 }

@@ -55,7 +55,9 @@ __global__ void __launch_bounds__(256) xent_kernel(T* __restrict__ z, long ldz, 
                                                    const int32_t* __restrict__ n_valid,
                                                    float* __restrict__ row_loss) {
   constexpr int NV = Vec16<T>::N;
-  __shared__ float s_m[256], s_s[256];
+  constexpr int U = 4;  // vectors in flight per thread
+  __shared__ float s_m[4], s_s[4];
+  __shared__ float s_lse;
   const long row = blockIdx.x;
   T* zr = z + row * ldz;
   const int t = tgt[row];
@@ -63,47 +65,153 @@ __global__ void __launch_bounds__(256) xent_kernel(T* __restrict__ z, long ldz, 
   const int nvec = (int)(ldz / NV);
   float m = -INFINITY, s = 0.f;
   if (valid) {
-    for (int v = threadIdx.x; v < nvec; v += 256) {
-      float x[NV];
-      Vec16<T>::load(zr + (long)v * NV, x);
+    for (int v0 = threadIdx.x; v0 < nvec; v0 += 256 * U) {
+      float x[U][NV];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * 256;
+        if (v < nvec) Vec16<T>::load(zr + (long)v * NV, x[u]);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (v >= nvec || v * NV + i >= V) x[u][i] = -INFINITY;
+      }
       float cm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        if (v * NV + i >= V) x[i] = -INFINITY;
-        cm = fmaxf(cm, x[i]);
-      }
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) cm = fmaxf(cm, x[u][i]);
       if (cm == -INFINITY) continue;
       if (cm > m) {
         s = s * __expf(m - cm);
         m = cm;
       }
 #pragma unroll
-      for (int i = 0; i < NV; ++i) s += __expf(x[i] - m);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) s += __expf(x[u][i] - m);
     }
   }
-  s_m[threadIdx.x] = m;
-  s_s[threadIdx.x] = s;
+  // combine (max, sum) pairs: within the wavefront, then the 4 wavefronts in order
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) merge_ms(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_m[w] = m;
+    s_s[w] = s;
+  }
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) {
-      float mm = s_m[threadIdx.x], ss = s_s[threadIdx.x];
-      merge_ms(mm, ss, s_m[threadIdx.x + o], s_s[threadIdx.x + o]);
-      s_m[threadIdx.x] = mm;
-      s_s[threadIdx.x] = ss;
-    }
-    __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = s_m[0], ss = s_s[0];
+    for (int q = 1; q < 4; ++q) merge_ms(mm, ss, s_m[q], s_s[q]);
+    const float lse = mm + __logf(ss);
+    s_lse = lse;
+    row_loss[row] = valid ? lse - Act<T>::ld(zr, t) : 0.f;
   }
-  const float lse = s_m[0] + __logf(s_s[0]);
+  __syncthreads();  // z[t] has been read before it is overwritten
+  const float lse = s_lse;
   const int n = *n_valid;
   const float inv_n = n > 0 ? 1.0f / (float)n : 0.f;
-  if (threadIdx.x == 0) row_loss[row] = valid ? lse - Act<T>::ld(zr, t) : 0.f;
-  __syncthreads();  // every thread has read z[t] (via lse) before it is overwritten
-  for (int v = threadIdx.x; v < nvec; v += 256) {
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += 256 * U) {
+    float x[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * 256;
+      if (v < nvec && valid) Vec16<T>::load(zr + (long)v * NV, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * 256;
+      if (v >= nvec) continue;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int j = v * NV + i;
+        float d = 0.f;
+        if (valid && j < V) d = (__expf(x[u][i] - lse) - (j == t ? 1.f : 0.f)) * inv_n;
+        x[u][i] = d;
+      }
+      Vec16<T>::store(zr + (long)v * NV, x[u]);
+    }
+  }
+}
+
+// The same computation with the row held in registers between the passes:
+// 1024 threads, thread t owns the 16-byte vectors t, t + 1024, ... (NCH of
+// them), so the logits are read from memory once. Used when the row fits
+// (ldz <= 1024 * NCH * vector width).
+template <typename T, int NCH>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) xent_reg_kernel(T* __restrict__ z, long ldz, int V,
+                                                        const int32_t* __restrict__ tgt,
+                                                        const int32_t* __restrict__ n_valid,
+                                                        float* __restrict__ row_loss) {
+  constexpr int NV = Vec16<T>::N;
+  __shared__ float s_m[16], s_s[16];
+  __shared__ float s_lse;
+  const long row = blockIdx.x;
+  T* zr = z + row * ldz;
+  const int t = tgt[row];
+  const bool valid = t >= 0 && t < V;
+  const int nvec = (int)(ldz / NV);
+  // the row stays in registers as loaded (16 bytes per vector), unpacked on use
+  uint4 raw[NCH];
+  auto unpack = [&](int q, float* x) {
+    const int v = threadIdx.x + q * 1024;
+    Vec16<T>::load(reinterpret_cast<const T*>(&raw[q]), x);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (v >= nvec || v * NV + i >= V) x[i] = -INFINITY;
+  };
+  float m = -INFINITY, s = 0.f;
+  if (valid) {
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int v = threadIdx.x + q * 1024;
+      raw[q] = v < nvec ? *reinterpret_cast<const uint4*>(zr + (long)v * NV) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      float x[NV];
+      unpack(q, x);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) m = fmaxf(m, x[i]);
+    }
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < NCH; ++q) {
+        float x[NV];
+        unpack(q, x);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) s += __expf(x[i] - m);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) merge_ms(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_m[w] = m;
+    s_s[w] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = s_m[0], ss = s_s[0];
+    for (int q = 1; q < 16; ++q) merge_ms(mm, ss, s_m[q], s_s[q]);
+    const float lse = mm + __logf(ss);
+    s_lse = lse;
+    row_loss[row] = valid ? lse - Act<T>::ld(zr, t) : 0.f;
+  }
+  __syncthreads();  // z[t] has been read before it is overwritten
+  const float lse = s_lse;
+  const int n = *n_valid;
+  const float inv_n = n > 0 ? 1.0f / (float)n : 0.f;
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    const int v = threadIdx.x + q * 1024;
+    if (v >= nvec) continue;
     float x[NV];
-    Vec16<T>::load(zr + (long)v * NV, x);
+    if (valid) unpack(q, x);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      int j = v * NV + i;
+      const int j = v * NV + i;
       float d = 0.f;
       if (valid && j < V) d = (__expf(x[i] - lse) - (j == t ? 1.f : 0.f)) * inv_n;
       x[i] = d;
@@ -115,6 +223,15 @@ __global__ void __launch_bounds__(256) xent_kernel(T* __restrict__ z, long ldz, 
 template <typename T>
 void launch_xent(T* z, long ldz, int M, int V, const int32_t* tgt, const int32_t* n_valid, float* row_loss,
                  hipStream_t s) {
+  const long nvec = ldz / Vec16<T>::N;
+  const long nch = (nvec + 1023) / 1024;
+#define XENT_REG(N)                                                                                        \
+  if (nch <= N) {                                                                                          \
+    hipLaunchKernelGGL((xent_reg_kernel<T, N>), dim3(M), dim3(1024), 0, s, z, ldz, V, tgt, n_valid, row_loss); \
+    return;                                                                                                \
+  }
+  XENT_REG(1) XENT_REG(2) XENT_REG(4) XENT_REG(8)
+#undef XENT_REG
   hipLaunchKernelGGL(xent_kernel<T>, dim3(M), dim3(256), 0, s, z, ldz, V, tgt, n_valid, row_loss);
 }
 template void launch_xent<float>(float*, long, int, int, const int32_t*, const int32_t*, float*, hipStream_t);

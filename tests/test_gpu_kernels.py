@@ -280,11 +280,13 @@ def test_attention_fwd_bwd(sd, prec, D, packed):
 
 # ----------------------------------------------------------- cross-entropy
 
+# V = 50257 and 70000 also cover the row-in-memory kernel (rows too long to
+# stay in registers) next to the register-resident one
 @pytest.mark.parametrize("prec", [0, 1])
-@pytest.mark.parametrize("V", [257, 8000])
+@pytest.mark.parametrize("V", [257, 8000, 50257, 70000])
 def test_cross_entropy(sd, prec, V):
     t = torch()
-    M = 300
+    M = 300 if V < 50000 else 64
     ldz = (V + 127) // 128 * 128
     rng = np.random.default_rng(V + prec)
     z = (rng.standard_normal((M, V)) * 3).astype(np.float32)
