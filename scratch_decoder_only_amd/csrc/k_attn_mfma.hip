@@ -286,10 +286,14 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
     const float corr = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
     l = l * corr + ls;
     m = mn;
+    // once the running maxima settle, no lane's changes: skip the rescale
+    // (a wavefront-uniform test, so no divergence)
+    if (__builtin_amdgcn_ballot_w64(corr != 1.f) != 0) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc_o[dt][e] *= corr;
+        for (int e = 0; e < 16; ++e) acc_o[dt][e] *= corr;
+    }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const bf16x8_t pf = as_frag(pack_frag(&p[st >> 1][(st & 1) * 8]));

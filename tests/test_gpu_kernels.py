@@ -278,6 +278,24 @@ def test_attention_fwd_bwd(sd, prec, D, packed):
             assert rel(g, e) <= 2e-2 and cos(g, e) >= 0.9995, i
 
 
+# ------------------------------------------------------------ column sums
+
+@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("M,N", [(300, 768), (1000, 2304), (129, 3076)])
+def test_column_sums(sd, prec, M, N):
+    """Bias gradients: out[c] = sum over rows of a[:, c] (fixed order, 8 or 4
+    columns per thread depending on the alignment of N)."""
+    t = torch()
+    rng = np.random.default_rng(M + N + prec)
+    a = rng.standard_normal((M, N)).astype(np.float32)
+    a = bf16_exact(a) if prec else a
+    out = t.zeros(N, device="cuda")
+    ws = t.zeros(sd.colsum_ws_floats(M, N), device="cuda")
+    sd.colsum(prec, act(a, prec), N, M, N, out, ws)
+    t.cuda.synchronize()
+    assert rel(host(out), a.astype(np.float64).sum(axis=0)) <= 2e-6
+
+
 # ----------------------------------------------------------- cross-entropy
 
 # V = 50257 and 70000 also cover the row-in-memory kernel (rows too long to
