@@ -337,12 +337,15 @@ def main():
         # next-token kernel; the sampler alone on the last position's logits
         T0 = min(128, T - args.gen)
         prompt = tok[:, :T0].contiguous()
-        sd.generate(model, prompt, 1)  # warm-up
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        sd.generate(model, prompt, args.gen)
-        torch.cuda.synchronize()
-        t_gen = time.perf_counter() - t0
+        rates = {}
+        for cached in (False, True):
+            sd.generate(model, prompt, 2, kv_cache=cached)  # warm-up
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            sd.generate(model, prompt, args.gen, kv_cache=cached)
+            torch.cuda.synchronize()
+            rates[cached] = time.perf_counter() - t0
+        t_gen = rates[False]
         logits = model.forward_logits(prompt)[:, T0 - 1, :]
         u = torch.rand(B, device="cuda")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -351,11 +354,13 @@ def main():
             sd.sample_tokens(logits, 1.0, 50, u)
         e1.record(stream)
         torch.cuda.synchronize()
-        out["generation"] = {"batch": B, "prompt": T0, "new_tokens": args.gen, "kv_cache": False,
-                             "tokens_per_s": round(B * args.gen / t_gen, 1),
-                             "ms_per_token_step": round(t_gen / args.gen * 1e3, 3),
+        out["generation"] = {"batch": B, "prompt": T0, "new_tokens": args.gen,
+                             "tokens_per_s_recompute": round(B * args.gen / rates[False], 1),
+                             "tokens_per_s_kv_cache": round(B * args.gen / rates[True], 1),
+                             "ms_per_token_step_kv_cache": round(rates[True] / args.gen * 1e3, 3),
                              "sample_us_per_call": round(e0.elapsed_time(e1) / 10 * 1e3, 1)}
-        log(f"bench: generation {B}x{args.gen} tokens in {t_gen:.2f} s")
+        log(f"bench: generation {B}x{args.gen} tokens: {rates[False]:.2f} s recomputing, "
+            f"{rates[True]:.2f} s with the cache")
 
     if args.ckpt:
         # checkpoint file of the multi-step driver: parameters + both Adam moments

@@ -193,6 +193,23 @@ lm_status model_load(lm_model* model, const char* path, int32_t* step, void* str
 lm_status sample_tokens(const float* d_logits, int32_t rows, int32_t vocab, int64_t ld, float temperature,
                         int32_t top_k, const float* d_uniforms, int32_t* d_out, void* stream);
 
+/* Key/value cache for `batch` rows: per layer, K [batch][max_seq][d_model]
+ * then V of the same shape, in the activation type (bf16 for precision 1,
+ * else fp32). The caller allocates lm_kv_cache_bytes(cfg, batch) bytes of
+ * device memory and passes the same batch to every call on that cache.
+ * model_prefill runs the forward pass over d_tokens [B, T] (one document per
+ * row), fills cache positions 0 .. T-1 and writes the logits of each row's
+ * last position to d_logits [B, vocab] fp32. model_decode takes one new token
+ * per row (d_tokens [B]) at position pos (1 <= pos < max_seq; positions
+ * 0 .. pos-1 already cached), appends its keys and values at pos, attends
+ * over positions 0 .. pos and writes its logits to d_logits [B, vocab].
+ * Both overwrite the model's forward activations (not its parameters). */
+size_t lm_kv_cache_bytes(const lm_config* cfg, int32_t batch);
+lm_status model_prefill(lm_model* model, const int32_t* d_tokens, int32_t B, int32_t T, void* d_cache,
+                        float* d_logits, void* stream);
+lm_status model_decode(lm_model* model, const int32_t* d_tokens, int32_t B, int32_t pos, void* d_cache,
+                       float* d_logits, void* stream);
+
 /* ---- measurement hooks (used by the benchmark) ----
  * With profiling on, every kernel launch of train_step is bracketed by a pair
  * of HIP events recorded on the step's stream, and model_profile_read sums

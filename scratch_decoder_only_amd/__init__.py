@@ -76,6 +76,9 @@ _sig("model_config", c_int, [c_void_p, ctypes.POINTER(LmConfig)])
 _sig("lm_lr_schedule", ctypes.c_float, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float])
 _sig("model_save", c_int, [c_void_p, c_char_p, ctypes.c_int32, c_void_p])
 _sig("model_load", c_int, [c_void_p, c_char_p, ctypes.POINTER(ctypes.c_int32), c_void_p])
+_sig("lm_kv_cache_bytes", c_size_t, [ctypes.POINTER(LmConfig), ctypes.c_int32])
+_sig("model_prefill", c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_void_p, c_void_p])
+_sig("model_decode", c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_void_p, c_void_p])
 _sig("sample_tokens", c_int, [c_void_p, ctypes.c_int32, ctypes.c_int32, c_int64, ctypes.c_float, ctypes.c_int32,
                               c_void_p, c_void_p, c_void_p])
 _sig("model_profile_enable", c_int, [c_void_p, c_int])
@@ -224,6 +227,35 @@ class Model:
                "forward_logits")
         return out
 
+    # ---- generation with a key/value cache
+    def kv_cache(self, batch: int):
+        """Device buffer for the key/value cache of `batch` rows."""
+        torch = _torch()
+        n = _lib.lm_kv_cache_bytes(ctypes.byref(self.cfg), int(batch))
+        if n == 0:
+            _check(LM_ERR_SHAPE, "lm_kv_cache_bytes")
+        return torch.empty(int(n), dtype=torch.uint8, device=self.stats.device)
+
+    def prefill(self, tokens, cache, out=None):
+        """Forward over tokens [B, T] (filling cache positions < T); returns the
+        logits [B, vocab] of each row's last position."""
+        torch = _torch()
+        B, T = tokens.shape
+        if out is None:
+            out = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _check(_lib.model_prefill(self._h, _ptr(tokens), B, T, _ptr(cache), _ptr(out), _stream()), "model_prefill")
+        return out
+
+    def decode(self, tokens, pos: int, cache, out=None):
+        """One new token per row (tokens [B]) at position pos; returns its logits [B, vocab]."""
+        torch = _torch()
+        B = tokens.shape[0]
+        if out is None:
+            out = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _check(_lib.model_decode(self._h, _ptr(tokens), B, int(pos), _ptr(cache), _ptr(out), _stream()),
+               "model_decode")
+        return out
+
     # ---- checkpoints
     def save(self, path: str, step: int):
         """Parameters and Adam moments to a checkpoint file (safetensors layout)."""
@@ -298,12 +330,16 @@ def sample_tokens(logits, temperature: float = 0.0, top_k: int = 0, uniforms=Non
     return out
 
 
-def generate(model: "Model", prompt, n_new: int, *, temperature: float = 0.0, top_k: int = 0, seed: int = 0):
-    """Extends each row of `prompt` ([B, T0] int32 CUDA tensor) by n_new tokens:
-    every new token comes from forward_logits over the whole sequence so far
-    (no key/value cache) and sample_tokens on its last position. Uniforms for
-    sampling are drawn on the host from numpy's PCG64(seed), one per row and
-    step, and passed in. Returns the [B, T0 + n_new] token tensor."""
+def generate(model: "Model", prompt, n_new: int, *, temperature: float = 0.0, top_k: int = 0, seed: int = 0,
+             kv_cache: bool = True):
+    """Extends each row of `prompt` ([B, T0] int32 CUDA tensor) by n_new tokens.
+
+    kv_cache=True: one prefill over the prompt, then one decode step per new
+    token against the key/value cache. kv_cache=False: forward_logits over the
+    whole sequence so far for every new token. Either way sample_tokens picks
+    the token from the last position's logits; uniforms for sampling are drawn
+    on the host from numpy's PCG64(seed), one per row and step, and passed in.
+    Returns the [B, T0 + n_new] token tensor."""
     torch = _torch()
     B, T0 = prompt.shape
     if T0 + n_new > model.cfg.max_seq:
@@ -311,16 +347,19 @@ def generate(model: "Model", prompt, n_new: int, *, temperature: float = 0.0, to
     toks = torch.zeros((B, T0 + n_new), dtype=torch.int32, device=prompt.device)
     toks[:, :T0] = prompt
     rng = np.random.Generator(np.random.PCG64(seed))
+    cache = model.kv_cache(B) if kv_cache and n_new > 0 else None
     for i in range(n_new):
         T = T0 + i
-        cur = toks[:, :T].contiguous()
-        logits = model.forward_logits(cur)
-        last = logits[:, T - 1, :]
+        if cache is None:
+            last = model.forward_logits(toks[:, :T].contiguous())[:, T - 1, :]
+        elif i == 0:
+            last = model.prefill(toks[:, :T].contiguous(), cache)
+        else:
+            last = model.decode(toks[:, T - 1].contiguous(), T - 1, cache)
         u = None
         if temperature > 0:
             u = torch.from_numpy(rng.random(B).astype(np.float32)).to(prompt.device)
-        nxt = sample_tokens(last, temperature, top_k, u)
-        toks[:, T] = nxt
+        toks[:, T] = sample_tokens(last, temperature, top_k, u)
     return toks
 
 

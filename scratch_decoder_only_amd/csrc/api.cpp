@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/lmstep.h"
@@ -411,6 +412,78 @@ int forward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* d
   return rc;
 }
 
+// One generation step with a key/value cache: B new tokens, all at position
+// pos, run through every block with M = B rows; each block appends its keys
+// and values at pos and attends over cache positions 0 .. pos; the head
+// writes B rows of logits. Same kernels and epilogues as the forward pass.
+template <typename E>
+int decode_pass(lm_model* m, Launcher& Lr, const int32_t* tok, int B, int pos, E* cache) {
+  hipStream_t s = Lr.s;
+  const long M = B, C = m->C, F = m->F, H = m->H, S = m->S;
+  const double Mf = (double)M, A = (double)sizeof(E);
+  int rc = 0;
+  launch_fill_u32(reinterpret_cast<uint32_t*>(m->pos), (uint32_t)pos, M, s);
+  Lr.run("embed_fwd", 0, Mf * C * 12.0, [&] {
+    launch_embed_fwd(tok, m->pos, m->params + m->o_wte, m->params + m->o_wpe, (int)M, (int)C, m->V, m->x, m->flags, s);
+  });
+  for (int l = 0; l < m->L; ++l) {
+    const auto& b = m->blk[l];
+    float* xl = m->x + l * M * C;
+    float* xml = m->xm + l * M * C;
+    E* y1 = m->act<E>(m->y1, l * M * C);
+    E* qkv = m->act<E>(m->qkv, l * M * 3 * C);
+    E* o = m->act<E>(m->o, l * M * C);
+    E* y2 = m->act<E>(m->y2, l * M * C);
+    E* u = m->act<E>(m->u, l * M * F);
+    E* a = m->act<E>(m->a, l * M * F);
+    E* kc = cache + 2L * l * B * S * C;
+    E* vc = kc + (long)B * S * C;
+    Lr.run("layernorm_fwd", 0, Mf * C * (4 + A), [&] {
+      launch_ln_fwd<E>(xl, m->P_(b.ln1_g), m->P_(b.ln1_b), (int)M, (int)C, m->cfg.ln_eps, y1, m->mu1 + l * M,
+                       m->r1 + l * M, s);
+    });
+    {
+      GemmOp op = fwd_op(m, y1, M, C, b.w_qkv, 3 * C, qkv, EPI_STORE);
+      op.bias = m->P_(b.b_qkv);
+      Lr.run("gemm_qkv_fwd", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, op, s); });
+    }
+    Lr.run("attn_decode", 0, 0, [&] {
+      launch_kv_store<E>(qkv, B, 1, (int)C, (int)S, pos, kc, vc, s);
+      rc |= launch_attn_decode<E>(qkv, kc, vc, B, (int)H, m->D, (int)S, pos + 1, o, m->gemm_ws, s);
+    });
+    {
+      GemmOp op = fwd_op(m, o, M, C, b.w_o, C, xml, EPI_RESID);
+      op.bias = m->P_(b.b_o); op.R = xl; op.ldr = C;
+      Lr.run("gemm_attnout_fwd", 2.0 * M * C * C, 0, [&] { rc |= gemm(m, op, s); });
+    }
+    Lr.run("layernorm_fwd", 0, Mf * C * (4 + A), [&] {
+      launch_ln_fwd<E>(xml, m->P_(b.ln2_g), m->P_(b.ln2_b), (int)M, (int)C, m->cfg.ln_eps, y2, m->mu2 + l * M,
+                       m->r2 + l * M, s);
+    });
+    {
+      GemmOp op = fwd_op(m, y2, M, C, b.w_fc, F, u, EPI_GELU);
+      op.bias = m->P_(b.b_fc); op.aux = a; op.ld_aux = F;
+      Lr.run("gemm_fc1_fwd", 2.0 * M * F * C, 0, [&] { rc |= gemm(m, op, s); });
+    }
+    {
+      GemmOp op = fwd_op(m, a, M, F, b.w_proj, C, m->x + (l + 1) * M * C, EPI_RESID);
+      op.bias = m->P_(b.b_proj); op.R = xml; op.ldr = C;
+      Lr.run("gemm_fc2_fwd", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, op, s); });
+    }
+  }
+  E* hf = m->act<E>(m->hf, 0);
+  Lr.run("layernorm_fwd", 0, Mf * C * (4 + A), [&] {
+    launch_ln_fwd<E>(m->x + m->L * M * C, m->P_(m->o_lnf_g), m->P_(m->o_lnf_b), (int)M, (int)C, m->cfg.ln_eps, hf,
+                     m->muf, m->rf, s);
+  });
+  {
+    GemmOp op = fwd_op(m, hf, M, C, m->o_wte, m->bf ? m->Vp : m->V, m->act<E>(m->logits, 0), EPI_STORE);
+    op.ldc = m->ldz;
+    Lr.run("gemm_head_fwd", 2.0 * M * m->V * C, 0, [&] { rc |= gemm(m, op, s); });
+  }
+  return rc;
+}
+
 template <typename E>
 int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* tgt, int B, int T, float* stats) {
   hipStream_t s = Lr.s;
@@ -689,6 +762,63 @@ lm_status forward_logits(lm_model* m, const int32_t* tok, const int32_t* doc, in
   }
   if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
   return hip_status("forward_logits");
+}
+
+size_t lm_kv_cache_bytes(const lm_config* cfg, int32_t batch) {
+  if (!cfg || batch < 1 || lm_workspace_bytes(cfg) == 0) return 0;
+  const size_t elem = cfg->precision ? 2 : 4;
+  return 2ull * cfg->n_layers * (size_t)batch * cfg->max_seq * cfg->d_model * elem;
+}
+
+lm_status model_prefill(lm_model* m, const int32_t* tok, int32_t B, int32_t T, void* d_cache, float* d_logits,
+                        void* stream) {
+  if (!m || !tok || !d_cache || !d_logits) return fail(LM_ERR_ARG, "model, tokens, cache or logits is NULL");
+  lm_status st = check_batch(m, B, T);
+  if (st != LM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Launcher Lr(m, s);
+  const long C = m->C, S = m->S, M = (long)B * T;
+  int rc;
+  launch_fill_u32(m->flags, 0u, 4, s);
+  auto fill = [&](auto* cache) {
+    using E = std::remove_pointer_t<decltype(cache)>;
+    for (int l = 0; l < m->L; ++l) {
+      E* kc = cache + 2L * l * B * S * C;
+      launch_kv_store<E>(m->act<E>(m->qkv, l * M * 3 * C), B, T, (int)C, (int)S, 0, kc, kc + (long)B * S * C, s);
+    }
+    // logits of each row's last position
+    launch_logits_out<E>(m->act<E>(m->logits, 0) + (long)(T - 1) * m->ldz, (long)T * m->ldz, B, m->V, d_logits, s);
+  };
+  if (m->bf) {
+    rc = forward_pass<bf16>(m, Lr, tok, nullptr, B, T);
+    fill(reinterpret_cast<bf16*>(d_cache));
+  } else {
+    rc = forward_pass<float>(m, Lr, tok, nullptr, B, T);
+    fill(reinterpret_cast<float*>(d_cache));
+  }
+  if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
+  return hip_status("model_prefill");
+}
+
+lm_status model_decode(lm_model* m, const int32_t* tok, int32_t B, int32_t pos, void* d_cache, float* d_logits,
+                       void* stream) {
+  if (!m || !tok || !d_cache || !d_logits) return fail(LM_ERR_ARG, "model, tokens, cache or logits is NULL");
+  lm_status st = check_batch(m, B, 1);
+  if (st != LM_OK) return st;
+  if (pos < 1 || pos >= m->S) return fail(LM_ERR_SHAPE, "pos must be in [1, max_seq): the cache holds positions < pos");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Launcher Lr(m, s);
+  int rc;
+  launch_fill_u32(m->flags, 0u, 4, s);
+  if (m->bf) {
+    rc = decode_pass<bf16>(m, Lr, tok, B, pos, reinterpret_cast<bf16*>(d_cache));
+    launch_logits_out<bf16>(m->act<bf16>(m->logits, 0), m->ldz, B, m->V, d_logits, s);
+  } else {
+    rc = decode_pass<float>(m, Lr, tok, B, pos, reinterpret_cast<float*>(d_cache));
+    launch_logits_out<float>(m->act<float>(m->logits, 0), m->ldz, B, m->V, d_logits, s);
+  }
+  if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
+  return hip_status("model_decode");
 }
 
 const char* lm_last_error(void) { return g_err.c_str(); }

@@ -1,0 +1,118 @@
+// Generation with a key/value cache: each new token's keys and values are
+// appended to a per-layer cache, and its query attends to the cached keys of
+// its row (causal: every cached position is at or before it). The attention
+// of one query per (row, head) is the same operation as the training path's
+// (Feste page, "Model Architecture": scores scaled by 1/sqrt(D), softmax,
+// weighted sum of values), written here for one query at a time.
+//
+// Cache layout, per layer: K [B][S][C] then V [B][S][C] in the activation
+// type (S = max_seq, C = d_model, head h at columns h*D .. h*D+D-1).
+#include "kernels.h"
+
+namespace lm {
+
+namespace {
+
+// cache rows (b, t0 .. t0+T-1) of layer l's K and V from qkv rows [B*T, 3C]
+template <typename E>
+__global__ void kv_store_kernel(const E* __restrict__ qkv, int B, int T, int C, int S, int t0,
+                                E* __restrict__ kc, E* __restrict__ vc) {
+  const long r = blockIdx.x;  // b * T + t
+  const int b = (int)(r / T), t = (int)(r % T);
+  const E* src = qkv + r * 3L * C;
+  E* dk = kc + ((long)b * S + t0 + t) * C;
+  E* dv = vc + ((long)b * S + t0 + t) * C;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    dk[c] = src[C + c];
+    dv[c] = src[2 * C + c];
+  }
+}
+
+// One block per (row b, head h): query = qkv[b][h*D ..], keys/values 0 .. n-1
+// of the cache. The block's scores, then their exponentials, sit in its own
+// row of the global scratch sbuf (n <= S floats); fixed-order reductions;
+// o[b][h*D + d] in the activation type.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_decode_kernel(const T* __restrict__ qkv, const T* __restrict__ kc,
+                                                          const T* __restrict__ vc, int H, int S, int n,
+                                                          T* __restrict__ o, float* __restrict__ sbuf) {
+  constexpr int NT = 256;
+  __shared__ float s_q[D];
+  __shared__ float s_red[NT / 64];
+  __shared__ float s_part[NT / D][D];
+  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  const int C = H * D, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float* sc = sbuf + (long)blockIdx.x * S;  // this block's scores
+  if (tid < D) s_q[tid] = Act<T>::ld(qkv, (long)b * 3 * C + h * D + tid);
+  __syncthreads();
+  const float scale = 1.0f / sqrtf((float)D);
+  const T* kb = kc + (long)b * S * C + h * D;
+  const T* vb = vc + (long)b * S * C + h * D;
+  // scores and their maximum
+  float mx = -INFINITY;
+  for (int j = tid; j < n; j += NT) {
+    float acc = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) acc += s_q[d] * Act<T>::ld(kb, (long)j * C + d);
+    acc *= scale;
+    sc[j] = acc;
+    mx = fmaxf(mx, acc);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) s_red[w] = mx;
+  __syncthreads();
+  mx = s_red[0];
+  for (int q = 1; q < NT / 64; ++q) mx = fmaxf(mx, s_red[q]);
+  __syncthreads();
+  // exponentials and their sum (per thread in key order, then the block in order)
+  float sum = 0.f;
+  for (int j = tid; j < n; j += NT) {
+    const float p = __expf(sc[j] - mx);
+    sc[j] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) s_red[w] = sum;
+  __syncthreads();
+  sum = 0.f;
+  for (int q = 0; q < NT / 64; ++q) sum += s_red[q];
+  // o[d] = sum_j p_j v_j[d] / sum: thread (g, d) takes keys g, g + NT/D, ...
+  const int d = tid % D, g = tid / D;
+  float acc = 0.f;
+  for (int j = g; j < n; j += NT / D) acc += sc[j] * Act<T>::ld(vb, (long)j * C + d);
+  s_part[g][d] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f;
+    for (int q = 0; q < NT / D; ++q) t += s_part[q][tid];
+    Act<T>::st(o, (long)b * C + h * D + tid, t / sum);
+  }
+}
+
+}  // namespace
+
+template <typename E>
+void launch_kv_store(const E* qkv, int B, int T_, int C, int S, int t0, E* kc, E* vc, hipStream_t s) {
+  hipLaunchKernelGGL(kv_store_kernel<E>, dim3(B * T_), dim3(256), 0, s, qkv, B, T_, C, S, t0, kc, vc);
+}
+template void launch_kv_store<float>(const float*, int, int, int, int, int, float*, float*, hipStream_t);
+template void launch_kv_store<bf16>(const bf16*, int, int, int, int, int, bf16*, bf16*, hipStream_t);
+
+template <typename T>
+int launch_attn_decode(const T* qkv, const T* kc, const T* vc, int B, int H, int D, int S, int n, T* o, float* sbuf,
+                       hipStream_t s) {
+  if (D == 64)
+    hipLaunchKernelGGL((attn_decode_kernel<T, 64>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf);
+  else if (D == 32)
+    hipLaunchKernelGGL((attn_decode_kernel<T, 32>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf);
+  else
+    return -1;
+  return 0;
+}
+template int launch_attn_decode<float>(const float*, const float*, const float*, int, int, int, int, int, float*,
+                                       float*, hipStream_t);
+template int launch_attn_decode<bf16>(const bf16*, const bf16*, const bf16*, int, int, int, int, int, bf16*, float*,
+                                      hipStream_t);
+
+}  // namespace lm

@@ -153,6 +153,14 @@ void launch_adamw(const AdamArgs& a, hipStream_t s);
 void launch_make_shadow(const float* p, long n, bf16* shadow, long split, long shift, hipStream_t s);
 
 // ------------------------------------------------------------- generation
+// Key/value cache (per layer K [B][S][C] then V [B][S][C]): rows t0 .. t0+T-1
+// of each row b from qkv [B*T, 3C]; one query per (row, head) against cache
+// positions 0 .. n-1 (sbuf: B*H*S floats of scratch).
+template <typename E>
+void launch_kv_store(const E* qkv, int B, int T_, int C, int S, int t0, E* kc, E* vc, hipStream_t s);
+template <typename T>
+int launch_attn_decode(const T* qkv, const T* kc, const T* vc, int B, int H, int D, int S, int n, T* o, float* sbuf,
+                       hipStream_t s);
 // Next token of each of `rows` logit rows (row r at logits + r * ld, V
 // columns): greedy when temperature <= 0, else top-k sampling with the given
 // uniforms; out [rows].

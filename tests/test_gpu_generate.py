@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import dev, torch
+from helpers import cos, dev, rel, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +110,56 @@ def test_sampled_generation_is_reproducible(sd):
     assert t.equal(a, b)
     assert not t.equal(a, c)
     assert int(a.max()) < shape.vocab and int(a.min()) >= 0
+
+
+# ------------------------------------------------------- key/value cache
+
+@pytest.mark.parametrize("name", ["C1", "C2"])
+def test_cached_decode_matches_oracle(sd, name):
+    """prefill over a prompt, then decode steps fed known tokens: the logits of
+    every step against the oracle's forward pass over the sequence so far
+    (fp32: rel <= 1e-4; bf16: cos >= 0.999)."""
+    t = torch()
+    shape = synth.SHAPES[name]
+    params = synth.init_params(shape)
+    model = sd.Model(shape, max_batch=2)
+    model.set(sd.LM_PARAMS, params)
+    toks = synth.make_batch(shape).tokens[:2]
+    T0, steps = 10, 6
+    cache = model.kv_cache(2)
+    got = [model.prefill(dev(toks[:, :T0]), cache).cpu().numpy()]
+    for i in range(steps):
+        pos = T0 + i
+        got.append(model.decode(dev(np.ascontiguousarray(toks[:, pos])), pos, cache).cpu().numpy())
+    t.cuda.synchronize()
+    p64 = {k: v.astype(np.float64) for k, v in params.items()}
+    for i, g in enumerate(got):
+        T = T0 + i
+        z, _ = oracle.forward(p64, shape, toks[:, :T], None, keep=False)
+        ref = z[:, T - 1, :]
+        if shape.precision == "fp32":
+            assert rel(g, ref) <= 1e-4, (i, rel(g, ref))
+        else:
+            assert cos(g, ref) >= 0.999, (i, cos(g, ref))
+
+
+def test_cached_greedy_generation_equals_recomputed(sd):
+    t = torch()
+    shape = synth.SHAPES["C1"]
+    model = sd.Model(shape, max_batch=4)
+    model.set(sd.LM_PARAMS, synth.init_params(shape))
+    prompt = dev(synth.make_batch(shape).tokens[:4, :16])
+    a = sd.generate(model, prompt, 12, kv_cache=True)
+    b = sd.generate(model, prompt, 12, kv_cache=False)
+    assert t.equal(a, b)
+
+
+def test_decode_rejects_bad_positions(sd):
+    shape = synth.SHAPES["C1"]
+    model = sd.Model(shape, max_batch=2)
+    cache = model.kv_cache(2)
+    tok = dev(np.zeros(2, np.int32))
+    with pytest.raises(RuntimeError):
+        model.decode(tok, 0, cache)
+    with pytest.raises(RuntimeError):
+        model.decode(tok, shape.max_seq, cache)
