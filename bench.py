@@ -209,6 +209,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prof", action="store_true")
     ap.add_argument("--ckpt", metavar="DIR", help="also time a checkpoint save and load of the model in DIR")
+    ap.add_argument("--untied-head", action="store_true",
+                    help="also time the step of the same model with a separate vocabulary projection and bias")
     ap.add_argument("--gen", type=int, default=0, metavar="N",
                     help="also time greedy generation of N tokens per row after a 128-token prompt")
     ap.add_argument("--calib-copy", action="store_true",
@@ -361,6 +363,30 @@ def main():
                              "sample_us_per_call": round(e0.elapsed_time(e1) / 10 * 1e3, 1)}
         log(f"bench: generation {B}x{args.gen} tokens: {rates[False]:.2f} s recomputing, "
             f"{rates[True]:.2f} s with the cache")
+
+    if args.untied_head:
+        # the same workload with head.w [V, C] and head.b [V] instead of the
+        # projection tied to wte: one more weight-gradient-sized AdamW range
+        # and the head bias gradient
+        ushape = shape.replace(untied_head=True)
+        um = sd.Model(ushape, max_batch=B)
+        um.set(sd.LM_PARAMS, synth.init_params(ushape))
+        for i in range(args.warmup):
+            um.train_step(tok, tgt, doc, lr=shape.lr, step=i + 1, beta1=shape.beta1, beta2=shape.beta2,
+                          eps=shape.eps, weight_decay=shape.weight_decay, clip=shape.clip)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            um.train_step(tok, tgt, doc, lr=shape.lr, step=args.warmup + i + 1, beta1=shape.beta1,
+                          beta2=shape.beta2, eps=shape.eps, weight_decay=shape.weight_decay, clip=shape.clip)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ums = ev0.elapsed_time(ev1) / args.steps
+        out["untied_head"] = {"ms_per_step": round(ums, 4), "tokens_per_s": round(B * T / (ums / 1e3), 1),
+                              "params": int(sum(r * c for _, _, r, c in um.table)),
+                              "loss": round(float(um.stats[0]), 4)}
+        log(f"bench: untied head {ums:.3f} ms/step, {B * T / (ums / 1e3):,.0f} tokens/s")
+        del um
 
     if args.ckpt:
         # checkpoint file of the multi-step driver: parameters + both Adam moments

@@ -22,7 +22,9 @@
  * Readings fixed by this library where the pages are silent: GELU is the tanh
  * form 0.5u(1 + tanh(sqrt(2/pi)(u + 0.044715u^3))); LayerNorm uses the biased
  * variance; the attention scale is 1/sqrt(D); positions restart at 0 in every
- * packed document; the vocabulary projection is tied to wte and has no bias;
+ * packed document; the vocabulary projection is tied to wte and has no bias
+ * unless untied_head asks for a separate one with a bias (RustGPT page, file
+ * list: its output projection is a layer of its own);
  * the loss is the mean over positions whose target is >= 0; the clip factor is
  * clip/n only when the global norm n exceeds clip; weight decay applies to
  * every parameter as lr*wd*p on the pre-update p.
@@ -65,11 +67,14 @@ typedef enum {
  * dimension d_model / n_heads must be 32 or 64; d_mlp a multiple of 64.
  * precision: 0 = fp32 everywhere; 1 = bf16 GEMM/attention operands with fp32
  * accumulation, fp32 residual stream, statistics, loss, gradients, Adam
- * moments and master weights. */
+ * moments and master weights.
+ * untied_head: 0 = logits z = h_f wte^T (tied, no bias); 1 = z = h_f
+ * head.w^T + head.b with a separate head.w [V,C] and head.b [V]. */
 typedef struct {
   int32_t vocab, d_model, n_heads, d_mlp, n_layers, max_seq, max_batch;
   int32_t precision;
   float ln_eps; /* LayerNorm epsilon, e.g. 1e-5 */
+  int32_t untied_head;
 } lm_config;
 
 /* Optimiser settings for one step. step is 1-based and drives the Adam bias
@@ -86,9 +91,12 @@ typedef enum { LM_PARAMS = 0, LM_GRADS = 1, LM_ADAM_M = 2, LM_ADAM_V = 3 } lm_bu
  * Order: wte[V,C], wpe[max_seq,C]; per block l: ln1.g, ln1.b [C],
  * attn.w_qkv [3C,C], attn.b_qkv [3C], attn.w_o [C,C], attn.b_o [C], ln2.g,
  * ln2.b [C], mlp.w_fc [F,C], mlp.b_fc [F], mlp.w_proj [C,F], mlp.b_proj [C];
- * then lnf.g, lnf.b [C]. Names are "wte", "blocks.<l>.attn.w_qkv", "lnf.g"...
- * Offsets are 64-float (256-byte) aligned; gaps hold zeros. Weight matrices
- * are [out, in] row-major (Y = X W^T + b). */
+ * then lnf.g, lnf.b [C]; with untied_head, head.w [V,C] and head.b [V] last.
+ * Names are "wte", "blocks.<l>.attn.w_qkv", "lnf.g", "head.w"...
+ * Offsets are 64-float (256-byte) aligned; gaps hold zeros. With bf16
+ * precision wte and head.w reserve round_up(V, 128) rows, and head.b as many
+ * entries; model_set keeps those padding rows zero in every buffer. Weight
+ * matrices are [out, in] row-major (Y = X W^T + b). */
 typedef struct {
   char name[48];
   int64_t offset, rows, cols;

@@ -29,7 +29,8 @@ design notes): GELU is the tanh form; LayerNorm uses the biased variance and
 eps = 1e-5; the attention scale is 1/sqrt(D); the mask admits key j for query
 i iff start(i) <= j <= i (same document, not in the future); positions restart
 at 0 in each packed document; the vocabulary projection is tied to wte with no
-bias; the loss is the mean over positions whose target is >= 0; the clip is on
+bias, unless the parameters hold a separate head ("head.w" [V, C] and "head.b"
+[V], the RustGPT page's output projection, a linear layer of its own); the loss is the mean over positions whose target is >= 0; the clip is on
 the global L2 norm of all gradients, applied only when the norm exceeds it;
 AdamW decays every parameter by lr * wd * p (pre-update p).
 
@@ -322,7 +323,9 @@ def forward(params: Dict[str, np.ndarray], cfg, tok, doc_ids=None, keep=True):
     x0 = wte[tok] + wpe[pos]; per block l:
       y1 = LN1(x); qkv = y1 W_qkv^T + b_qkv; o = MHSA(q, k, v); x += o W_o^T + b_o
       y2 = LN2(x); u = y2 W_fc^T + b_fc; a = GELU(u); x += a W_proj^T + b_proj
-    h_f = LN_f(x); z = h_f wte^T (tied head, no bias).
+    h_f = LN_f(x); z = h_f wte^T (tied head, no bias), or, with a separate
+    head in params (RustGPT page, file list: output_projection),
+    z = h_f head.w^T + head.b.
     Returns (z [B, T, V], cache) where cache holds what the backward reads.
     """
     tok = np.asarray(tok)
@@ -351,7 +354,10 @@ def forward(params: Dict[str, np.ndarray], cfg, tok, doc_ids=None, keep=True):
                      y2=y2, mu2=mu2, r2=r2, u=u, a=a)
             cache["layers"].append(c)
     hf, muf, rf = layernorm_fwd(x, params["lnf.g"], params["lnf.b"], eps)
-    z = hf @ _p(params, "wte").T
+    if "head.w" in params:
+        z = linear_fwd(hf, params["head.w"], params["head.b"])
+    else:
+        z = hf @ _p(params, "wte").T
     cache.update(x_f=x, hf=hf, muf=muf, rf=rf)
     return z, cache
 
@@ -368,11 +374,16 @@ def loss_and_grads(params: Dict[str, np.ndarray], cfg, tok, tgt, doc_ids=None):
     V, C = np.shape(params["wte"])
     S = np.shape(params["wpe"])[0]
     g: Dict[str, np.ndarray] = {}
-    # tied head z = h_f wte^T
-    dz2 = dz.reshape(-1, V)
-    hf2 = cache["hf"].reshape(-1, C)
-    dwte_head = dz2.T @ hf2
-    dhf = (dz2 @ _p(params, "wte")).reshape(cache["hf"].shape)
+    if "head.w" in params:
+        # separate head z = h_f head.w^T + head.b
+        dhf, g["head.w"], g["head.b"] = linear_bwd(dz, cache["hf"], params["head.w"])
+        dwte_head = 0.0
+    else:
+        # tied head z = h_f wte^T
+        dz2 = dz.reshape(-1, V)
+        hf2 = cache["hf"].reshape(-1, C)
+        dwte_head = dz2.T @ hf2
+        dhf = (dz2 @ _p(params, "wte")).reshape(cache["hf"].shape)
     dx, g["lnf.g"], g["lnf.b"] = layernorm_bwd(dhf, cache["x_f"], cache["muf"], cache["rf"], params["lnf.g"])
     for l in reversed(range(cfg.n_layers)):
         p = f"blocks.{l}."

@@ -37,7 +37,8 @@ EPI_STORE, EPI_RESID, EPI_GELU, EPI_DGELU = 0, 1, 2, 3
 class LmConfig(ctypes.Structure):
     _fields_ = [("vocab", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("d_mlp", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("max_seq", ctypes.c_int32),
-                ("max_batch", ctypes.c_int32), ("precision", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+                ("max_batch", ctypes.c_int32), ("precision", ctypes.c_int32), ("ln_eps", ctypes.c_float),
+                ("untied_head", ctypes.c_int32)]
 
 
 class LmOptim(ctypes.Structure):
@@ -141,14 +142,16 @@ class Model:
     """One model instance on the current CUDA (HIP) device.
 
     dims: object with vocab, d_model, n_heads, d_mlp, n_layers, max_seq,
-    ln_eps (e.g. a synth.ModelShape); precision "fp32" or "bf16".
+    ln_eps and optionally untied_head (e.g. a synth.ModelShape); precision
+    "fp32" or "bf16".
     """
 
     def __init__(self, dims, max_batch: int, precision: Optional[str] = None, device="cuda"):
         torch = _torch()
         prec = precision or getattr(dims, "precision", "bf16")
         self.cfg = LmConfig(dims.vocab, dims.d_model, dims.n_heads, dims.d_mlp, dims.n_layers, dims.max_seq,
-                            max_batch, 1 if prec == "bf16" else 0, float(getattr(dims, "ln_eps", 1e-5)))
+                            max_batch, 1 if prec == "bf16" else 0, float(getattr(dims, "ln_eps", 1e-5)),
+                            1 if getattr(dims, "untied_head", False) else 0)
         self.precision = prec
         nbytes = _lib.lm_workspace_bytes(ctypes.byref(self.cfg))
         if nbytes == 0:

@@ -108,12 +108,13 @@ struct lm_model {
   lm_config cfg;
   int V, C, H, D, F, L, S, Bmax;
   bool bf;   // bf16 compute
-  long Vp;   // padded vocabulary (columns of the logits, rows of the bf16 wte copy)
+  bool untied;  // separate vocabulary projection head.w [V, C] with bias head.b [V]
+  long Vp;   // padded vocabulary (columns of the logits; rows reserved for wte and head.w)
   long ldz;  // leading dimension of the logits
   std::vector<TensorInfo> table;
   long P = 0;  // floats in the flat parameter buffer
   // tensor offsets
-  long o_wte, o_wpe, o_lnf_g, o_lnf_b;
+  long o_wte, o_wpe, o_lnf_g, o_lnf_b, o_head_w, o_head_b;
   struct Blk {
     long ln1_g, ln1_b, w_qkv, b_qkv, w_o, b_o, ln2_g, ln2_b, w_fc, b_fc, w_proj, b_proj;
   };
@@ -121,7 +122,7 @@ struct lm_model {
   size_t act_size;  // bytes of one activation element
   // arena slices
   float *params, *grads, *adam_m, *adam_v;
-  bf16* shadow;  // bf16 copy of the parameters (bf16 path), wte padded to Vp rows
+  bf16* shadow;  // bf16 copy of the flat parameter buffer (bf16 path)
   float* x;      // [L+1][M][C]
   float* xm;     // [L][M][C]
   char *y1, *qkv, *o, *y2, *u, *a, *hf, *logits;
@@ -146,11 +147,9 @@ struct lm_model {
     return reinterpret_cast<T*>(base + elem_off * act_size);
   }
   // operand copy of a weight: bf16 shadow (bf16 path) or the fp32 master
-  const void* W(long off) const {
-    if (!bf) return params + off;
-    long o = off >= o_wte + (long)V * C ? off + (Vp - V) * C : off;
-    return shadow + o;
-  }
+  const void* W(long off) const { return bf ? static_cast<const void*>(shadow + off) : params + off; }
+  // the vocabulary projection's weight (wte when tied)
+  long head_w() const { return untied ? o_head_w : o_wte; }
 };
 
 namespace {
@@ -167,20 +166,24 @@ lm_status validate(const lm_config* c) {
   if (D != 32 && D != 64) return fail(LM_ERR_UNSUPPORTED, "head dimension must be 32 or 64");
   if (c->d_mlp % 64) return fail(LM_ERR_UNSUPPORTED, "d_mlp must be a multiple of 64");
   if (c->precision != 0 && c->precision != 1) return fail(LM_ERR_ARG, "precision must be 0 (fp32) or 1 (bf16)");
+  if (c->untied_head != 0 && c->untied_head != 1) return fail(LM_ERR_ARG, "untied_head must be 0 or 1");
   if (!(c->ln_eps >= 0.f)) return fail(LM_ERR_ARG, "ln_eps must be >= 0");
   if ((long)c->max_batch * c->max_seq > (1L << 24)) return fail(LM_ERR_SHAPE, "max_batch * max_seq too large");
   return LM_OK;
 }
 
+// The vocabulary-sized tensors reserve Vp rows (and the head bias ldz
+// entries): the padding stays zero, so the GEMMs and the bf16 copy can treat
+// them as Vp x C without a separate padded buffer.
 void build_table(lm_model* m) {
-  auto add = [&](const std::string& n, long rows, long cols) {
+  auto add = [&](const std::string& n, long rows, long cols, long reserve = 0) {
     long off = m->P;
     m->table.push_back({n, off, rows, cols});
-    m->P = round_up(off + rows * cols, 64);
+    m->P = round_up(off + std::max(rows * cols, reserve), 64);
     return off;
   };
   const int V = m->V, C = m->C, F = m->F, S = m->S;
-  m->o_wte = add("wte", V, C);
+  m->o_wte = add("wte", V, C, m->Vp * C);
   m->o_wpe = add("wpe", S, C);
   m->blk.resize(m->L);
   for (int l = 0; l < m->L; ++l) {
@@ -201,6 +204,11 @@ void build_table(lm_model* m) {
   }
   m->o_lnf_g = add("lnf.g", C, 1);
   m->o_lnf_b = add("lnf.b", C, 1);
+  m->o_head_w = m->o_head_b = -1;
+  if (m->untied) {
+    m->o_head_w = add("head.w", V, C, m->Vp * C);
+    m->o_head_b = add("head.b", V, 1, std::max(m->Vp, m->ldz));
+  }
 }
 
 // Lays out every slice of the arena (base == nullptr: size only).
@@ -212,7 +220,7 @@ void carve(lm_model* m, char* base) {
   m->grads = c.take<float>(m->P);
   m->adam_m = c.take<float>(m->P);
   m->adam_v = c.take<float>(m->P);
-  m->shadow = m->bf ? c.take<bf16>(m->P + (m->Vp - m->V) * C) : nullptr;
+  m->shadow = m->bf ? c.take<bf16>(m->P) : nullptr;
   m->x = c.take<float>((L + 1) * M * C);
   m->xm = c.take<float>(L * M * C);
   m->y1 = c.take<char>(L * M * C * A);
@@ -239,7 +247,7 @@ void carve(lm_model* m, char* base) {
   long ln_blocks = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
   m->ln_part = c.take<float>(3 * ln_blocks * C);
   long col_blocks = (M + kColRows - 1) / kColRows;
-  m->col_part = c.take<float>(col_blocks * std::max(F, 3 * C));
+  m->col_part = c.take<float>(col_blocks * std::max(std::max(F, 3 * C), m->untied ? m->ldz : 0L));
   m->gemm_ws_floats = 8L * std::max(F, 3 * C) * std::max(F, C);
   m->gemm_ws = c.take<float>(m->gemm_ws_floats);
   for (int k = 0; k < 2; ++k) {
@@ -276,6 +284,7 @@ lm_model* new_model(const lm_config* cfg) {
   m->S = cfg->max_seq;
   m->Bmax = cfg->max_batch;
   m->bf = cfg->precision == 1;
+  m->untied = cfg->untied_head == 1;
   m->act_size = m->bf ? 2 : 4;
   m->Vp = m->bf ? round_up(m->V, 128) : m->V;
   m->ldz = m->bf ? m->Vp : round_up(m->V, 4);
@@ -345,6 +354,16 @@ GemmOp dw_op(const void* dY, long M, long N, const void* X, long K, float* dW) {
   return op;
 }
 
+// Vocabulary projection z = h_f W^T (+ b): W = wte (tied) or head.w with the
+// bias head.b (untied). bf16: N = Vp; the padding rows of W are zero, so the
+// padding columns of z are too (plus the zero padding of the bias).
+GemmOp head_op(lm_model* m, const void* hf, long M, void* z) {
+  GemmOp op = fwd_op(m, hf, M, m->C, m->head_w(), m->bf ? m->Vp : m->V, z, EPI_STORE);
+  op.ldc = m->ldz;
+  if (m->untied) op.bias = m->P_(m->o_head_b);
+  return op;
+}
+
 template <typename E>
 int forward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* doc, int B, int T) {
   hipStream_t s = Lr.s;
@@ -404,9 +423,7 @@ int forward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* d
                      m->muf, m->rf, s);
   });
   {
-    // tied vocabulary projection z = h_f wte^T (bf16: N = Vp, padded rows of the copy are 0)
-    GemmOp op = fwd_op(m, hf, M, C, m->o_wte, m->bf ? m->Vp : m->V, m->act<E>(m->logits, 0), EPI_STORE);
-    op.ldc = m->ldz;
+    GemmOp op = head_op(m, hf, M, m->act<E>(m->logits, 0));
     Lr.run("gemm_head_fwd", 2.0 * M * m->V * C, 0, [&] { rc |= gemm(m, op, s); });
   }
   return rc;
@@ -477,8 +494,7 @@ int decode_pass(lm_model* m, Launcher& Lr, const int32_t* tok, int B, int pos, E
                      m->muf, m->rf, s);
   });
   {
-    GemmOp op = fwd_op(m, hf, M, C, m->o_wte, m->bf ? m->Vp : m->V, m->act<E>(m->logits, 0), EPI_STORE);
-    op.ldc = m->ldz;
+    GemmOp op = head_op(m, hf, M, m->act<E>(m->logits, 0));
     Lr.run("gemm_head_fwd", 2.0 * M * m->V * C, 0, [&] { rc |= gemm(m, op, s); });
   }
   return rc;
@@ -496,15 +512,21 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   Lr.run("loss_reduce", 0, 4.0 * M, [&] { launch_loss_reduce(m->row_loss, (int)M, m->n_valid, stats, s); });
   E* hf = m->act<E>(m->hf, 0);
   E* g_act = m->act<E>(m->g_act, 0);
-  // head: dwte = dz^T h_f (first writer of the wte gradient); dh_f = dz wte
+  // head: dW = dz^T h_f (tied: the first writer of the wte gradient); dh_f =
+  // dz W; untied: the bias gradient is the column sums of dz (its zero
+  // padding columns give the zero padding of the bias gradient)
   {
-    GemmOp op = dw_op(z, M, m->bf ? m->Vp : V, hf, C, m->grads + m->o_wte);
+    GemmOp op = dw_op(z, M, m->bf ? m->Vp : V, hf, C, m->grads + m->head_w());
     op.lda = m->ldz;
     op.M_out = (int)V;
     Lr.run("gemm_head_bwd_dw", 2.0 * M * V * C, 0, [&] { rc |= gemm(m, op, s); });
   }
+  if (m->untied)
+    Lr.run("bias_grad", 0, Mf * m->ldz * A, [&] {
+      launch_colsum<E>(z, m->ldz, (int)M, (int)m->ldz, m->col_part, m->grads + m->o_head_b, s);
+    });
   {
-    GemmOp op = dx_op(m, z, M, m->bf ? m->Vp : V, m->o_wte, C, m->dy, EPI_STORE);
+    GemmOp op = dx_op(m, z, M, m->bf ? m->Vp : V, m->head_w(), C, m->dy, EPI_STORE);
     op.lda = m->ldz;
     op.c_f32 = true;
     Lr.run("gemm_head_bwd_dx", 2.0 * M * V * C, 0, [&] { rc |= gemm(m, op, s); });
@@ -580,10 +602,11 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
     }
     ln_bwd(xl, m->mu1 + l * M, m->r1 + l * M, b.ln1_g, b.ln1_b, m->g, l > 0 ? m->grads + m->blk[l - 1].b_proj : nullptr);
   }
-  // embedding: dwte[tok] += dx0 (on top of the head part), dwpe[pos] = sum dx0
+  // embedding: dwte[tok] += dx0 (on top of the tied head's part, else from
+  // zero), dwpe[pos] = sum dx0
   Lr.run("embed_bwd", 0, Mf * C * 8, [&] {
     launch_csr(tok, (int)M, m->V, m->emb_tok, s);
-    launch_segment_sum(m->g, tok, (int)M, (int)C, m->V, m->emb_tok, m->grads + m->o_wte, true, s);
+    launch_segment_sum(m->g, tok, (int)M, (int)C, m->V, m->emb_tok, m->grads + m->o_wte, !m->untied, s);
     launch_csr(m->pos, (int)M, m->S, m->emb_pos, s);
     launch_segment_sum(m->g, m->pos, (int)M, (int)C, m->S, m->emb_pos, m->grads + m->o_wpe, false, s);
   });
@@ -632,8 +655,7 @@ lm_status model_create(const lm_config* cfg, void* d_arena, size_t arena_bytes, 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // zero parameters, gradients, moments and the bf16 copy (one contiguous run)
   char* z0 = reinterpret_cast<char*>(m->params);
-  char* z1 = m->shadow ? reinterpret_cast<char*>(m->shadow + m->P + (m->Vp - m->V) * m->C)
-                       : reinterpret_cast<char*>(m->adam_v + m->P);
+  char* z1 = m->shadow ? reinterpret_cast<char*>(m->shadow + m->P) : reinterpret_cast<char*>(m->adam_v + m->P);
   launch_fill_u32(reinterpret_cast<uint32_t*>(z0), 0u, (long)((z1 - z0) / 4), s);
   launch_fill_u32(m->flags, 0u, 4, s);
   st = hip_status("model_create");
@@ -688,7 +710,19 @@ lm_status model_set(lm_model* m, lm_buf which, const float* src, int src_on_devi
   size_t bytes = (size_t)m->P * 4;
   hipError_t e = hipMemcpyAsync(dst, src, bytes, src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return fail(LM_ERR_HIP, std::string("model_set: ") + hipGetErrorString(e));
-  if (which == LM_PARAMS && m->bf) launch_make_shadow(m->params, m->P, m->shadow, (long)m->V * m->C, (m->Vp - m->V) * m->C, s);
+  {
+    // the padding rows of the vocabulary-sized tensors stay zero whatever
+    // the caller's gaps hold
+    auto zero = [&](long off, long n) {
+      if (n > 0) launch_fill_u32(reinterpret_cast<uint32_t*>(dst + off), 0u, n, s);
+    };
+    zero(m->o_wte + (long)m->V * m->C, (m->Vp - m->V) * m->C);
+    if (m->untied) {
+      zero(m->o_head_w + (long)m->V * m->C, (m->Vp - m->V) * m->C);
+      zero(m->o_head_b + m->V, std::max(m->Vp, m->ldz) - m->V);
+    }
+  }
+  if (which == LM_PARAMS && m->bf) launch_make_shadow(m->params, m->P, m->shadow, m->P, 0, s);
   if (!src_on_device) {
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail(LM_ERR_HIP, std::string("model_set: ") + hipGetErrorString(e));
@@ -738,7 +772,7 @@ lm_status train_step(lm_model* m, const int32_t* tok, const int32_t* tgt, const 
   a.bc1 = (float)(1.0 - std::pow((double)opt->beta1, (double)opt->step));
   a.bc2 = (float)(1.0 - std::pow((double)opt->beta2, (double)opt->step));
   a.norm_scale = m->norm_scale; a.flags = m->flags;
-  a.shadow = m->shadow; a.shadow_split = (long)m->V * m->C; a.shadow_shift = (m->Vp - m->V) * m->C;
+  a.shadow = m->shadow; a.shadow_split = m->P; a.shadow_shift = 0;
   Lr.run("adamw", 0, (m->bf ? 34.0 : 32.0) * m->P, [&] { launch_adamw(a, s); });
   Lr.run("misc", 0, 0, [&] { launch_write_flags(m->flags, stats, s); });
   return hip_status("train_step");

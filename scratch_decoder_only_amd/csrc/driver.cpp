@@ -77,7 +77,8 @@ std::map<std::string, std::string> config_meta(const lm_config& c, int32_t step)
           {"n_layers", std::to_string(c.n_layers)},
           {"max_seq", std::to_string(c.max_seq)},
           {"precision", std::to_string(c.precision)},
-          {"ln_eps", eps}};
+          {"ln_eps", eps},
+          {"untied_head", std::to_string(c.untied_head)}};
 }
 
 std::string shape_json(const lm_tensor_info& t) {
@@ -295,6 +296,8 @@ lm_status model_load(lm_model* m, const char* path, int32_t* step, void* stream)
   if (meta_str("format") != kFormat) return set_error(LM_ERR_ARG, "not an lmstep checkpoint");
   for (const auto& kv : config_meta(cfg, 0)) {
     if (kv.first == "step" || kv.first == "format" || kv.first == "version") continue;
+    // files written before the separate head existed hold the tied model
+    if (kv.first == "untied_head" && meta_str("untied_head") == "<missing>" && kv.second == "0") continue;
     if (meta_str(kv.first.c_str()) != kv.second)
       return set_error(LM_ERR_SHAPE, "checkpoint " + kv.first + " = " + meta_str(kv.first.c_str()) +
                                          " does not match the model's " + kv.second);

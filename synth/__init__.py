@@ -54,6 +54,9 @@ class ModelShape:
     # scale the std of the residual output projections (w_o, w_proj) by
     # 1/sqrt(2 * n_layers) (GPT-2 style); only the GPT-2-small shape does
     scaled_resid_init: bool = False
+    # a separate vocabulary projection with bias (head.w [V, C], head.b [V])
+    # instead of the one tied to wte
+    untied_head: bool = False
 
     @property
     def head_dim(self) -> int:
@@ -203,7 +206,8 @@ def param_specs(shape: ModelShape) -> List[Tuple[str, Tuple[int, ...]]]:
     """Names and shapes of the model's parameters, in storage order.
 
     Weight matrices are [out, in] row-major. The vocabulary projection is tied
-    to wte, so there is no separate head matrix.
+    to wte, so there is no separate head matrix, unless the shape asks for an
+    untied head: then head.w [V, C] and head.b [V] come last.
     """
     V, C, F, S = shape.vocab, shape.d_model, shape.d_mlp, shape.max_seq
     out = [("wte", (V, C)), ("wpe", (S, C))]
@@ -218,6 +222,8 @@ def param_specs(shape: ModelShape) -> List[Tuple[str, Tuple[int, ...]]]:
             (p + "mlp.w_proj", (C, F)), (p + "mlp.b_proj", (C,)),
         ]
     out += [("lnf.g", (C,)), ("lnf.b", (C,))]
+    if shape.untied_head:
+        out += [("head.w", (V, C)), ("head.b", (V,))]
     return out
 
 

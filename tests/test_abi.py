@@ -58,7 +58,8 @@ def _cfg(**kw):
 
 
 @pytest.mark.parametrize("bad", [dict(d_model=96), dict(n_heads=3), dict(n_heads=1), dict(d_mlp=100),
-                                 dict(vocab=0), dict(max_seq=0), dict(precision=2), dict(d_model=2048, n_heads=32)])
+                                 dict(vocab=0), dict(max_seq=0), dict(precision=2), dict(d_model=2048, n_heads=32),
+                                 dict(untied_head=2)])
 def test_invalid_configs_are_rejected(lib, bad):
     import scratch_decoder_only_amd as sd
     cfg = _cfg(**bad)
@@ -81,6 +82,10 @@ def test_workspace_size_and_arena_checks(lib):
     assert sd.lib.model_create(ctypes.byref(cfg), ctypes.c_void_p(258), need, None, ctypes.byref(h)) == sd.LM_ERR_WORKSPACE
     bf = _cfg(precision=1)
     assert sd.lib.lm_workspace_bytes(ctypes.byref(bf)) > 0
+    # a separate head adds head.w [V, C] and head.b [V] to each of the four
+    # fp32 buffers
+    un = _cfg(untied_head=1)
+    assert sd.lib.lm_workspace_bytes(ctypes.byref(un)) >= need + 4 * 4 * (257 * 128 + 257)
 
 
 def test_kernel_entry_points_reject_bad_shapes(lib):

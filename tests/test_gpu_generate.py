@@ -114,14 +114,17 @@ def test_sampled_generation_is_reproducible(sd):
 
 # ------------------------------------------------------- key/value cache
 
-@pytest.mark.parametrize("name", ["C1", "C2"])
-def test_cached_decode_matches_oracle(sd, name):
+@pytest.mark.parametrize("name,untied", [("C1", False), ("C2", False), ("C1", True), ("C2", True)])
+def test_cached_decode_matches_oracle(sd, name, untied):
     """prefill over a prompt, then decode steps fed known tokens: the logits of
     every step against the oracle's forward pass over the sequence so far
-    (fp32: rel <= 1e-4; bf16: cos >= 0.999)."""
+    (fp32: rel <= 1e-4; bf16: cos >= 0.999), with the tied head and with a
+    separate head and bias."""
     t = torch()
-    shape = synth.SHAPES[name]
+    shape = synth.SHAPES[name].replace(untied_head=untied)
     params = synth.init_params(shape)
+    if untied:
+        params["head.b"] = synth.random_tensor(np.random.default_rng(5), params["head.b"].shape, 0.5)
     model = sd.Model(shape, max_batch=2)
     model.set(sd.LM_PARAMS, params)
     toks = synth.make_batch(shape).tokens[:2]

@@ -135,6 +135,56 @@ def test_train_step_matches_oracle(sd, name, batch):
     compare(shape, got, ref, params)
 
 
+@pytest.mark.parametrize("name,batch", [("C1", 4), ("C2", 16), ("C3", 8)])
+def test_untied_head_step_matches_oracle(sd, name, batch):
+    """A separate vocabulary projection with bias (head.w, head.b) instead of
+    the tied one, checked like the tied step; the bias starts off zero so its
+    forward term is exercised too."""
+    shape = synth.SHAPES[name].with_batch(batch).replace(untied_head=True)
+    print(f"untied-head train_step parity {name} B={batch} T={shape.seq}", flush=True)
+    tok, tgt, doc = _inputs(shape, batch)
+    params = synth.init_params(shape)
+    params["head.b"] = synth.random_tensor(np.random.default_rng(3), params["head.b"].shape, 0.5)
+    got = run_gpu(sd, shape, tok, tgt, doc, params)
+    ref = run_oracle(shape, tok, tgt, doc, params)
+    assert set(got["grads"]) == set(ref["grads"]) and "head.w" in got["grads"]
+    compare(shape, got, ref, params)
+
+
+@pytest.mark.parametrize("untied", [False, True])
+def test_vocab_padding_rows_stay_zero(sd, untied):
+    """bf16 reserves round_up(V, 128) rows for wte (and head.w, head.b): after
+    parameters with garbage in those gaps are set and a step runs, every
+    buffer's padding is zero and the logits equal those of a clean upload."""
+    t = torch()
+    shape = synth.C2.with_batch(2).replace(untied_head=untied)
+    tok, tgt, doc = _inputs(shape, 2)
+    params = synth.init_params(shape)
+    clean = sd.Model(shape, max_batch=2)
+    clean.set(sd.LM_PARAMS, params)
+    model = sd.Model(shape, max_batch=2)
+    table = model.table
+    flat = np.zeros(model.total, np.float32)
+    for name, off, rows, cols in table:
+        flat[off:off + rows * cols] = params[name].reshape(-1)
+    ends = sorted((off, off + rows * cols) for _, off, rows, cols in table)
+    gaps = [(e, nxt[0]) for (o, e), nxt in zip(ends, ends[1:] + [(model.total, 0)]) if nxt[0] > e]
+    for a, b in gaps:
+        flat[a:b] = 7.0
+    model.set_flat_device(sd.LM_PARAMS, dev(flat))
+    za = clean.forward_logits(dev(tok)).cpu().numpy()
+    zb = model.forward_logits(dev(tok)).cpu().numpy()
+    assert np.array_equal(za, zb)
+    model.train_step(dev(tok), dev(tgt), None, lr=shape.lr, step=1, clip=shape.clip)
+    t.cuda.synchronize()
+    for which in (sd.LM_PARAMS, sd.LM_GRADS, sd.LM_ADAM_M, sd.LM_ADAM_V):
+        f = model.get_flat(which)
+        for name, off, rows, cols in table:
+            if name in ("wte", "head.w", "head.b"):
+                nxt = min([o for o, _ in ends if o > off] + [model.total])
+                assert not np.any(f[off + rows * cols:nxt]), (which, name)
+
+
 def test_fp32_path_on_a_packed_workload(sd):
     """The fp32 path with a block-diagonal mask (C3's packing at C1-like size)."""
     shape = synth.C3.replace(precision="fp32", batch=4, seq=256, max_seq=256, vocab=300, n_layers=2)

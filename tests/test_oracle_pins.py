@@ -47,6 +47,9 @@ def random_params(cfg, seed, std=0.3):
         p[q + "mlp.b_proj"] = rng.standard_normal(C) * 0.1
     p["lnf.g"] = 1 + 0.2 * rng.standard_normal(C)
     p["lnf.b"] = 0.2 * rng.standard_normal(C)
+    if getattr(cfg, "untied_head", False):
+        p["head.w"] = rng.standard_normal((V, C)) * std
+        p["head.b"] = rng.standard_normal(V) * 0.1
     return p
 
 
@@ -66,10 +69,12 @@ def tiny_batch(cfg, seed=3):
 
 # ------------------------------------------------------------- P8: finite diffs
 
-def test_finite_difference_gradients_every_parameter():
+@pytest.mark.parametrize("untied", [False, True])
+def test_finite_difference_gradients_every_parameter(untied):
     """P8: the whole hand-derived backward against central differences in
-    float64 (Smallem page: gradient checks need double precision)."""
-    cfg = tiny_cfg()
+    float64 (Smallem page: gradient checks need double precision), with the
+    tied head and with a separate head and bias."""
+    cfg = tiny_cfg(untied_head=untied)
     params = random_params(cfg, 7)
     tok, tgt, doc = tiny_batch(cfg)
     loss, grads, _, n = oracle.loss_and_grads(params, cfg, tok, tgt, doc)
@@ -144,18 +149,21 @@ def _torch_loss(tp, cfg, tok, tgt, doc):
         a = torch.nn.functional.gelu(u, approximate="tanh")
         x = x + torch.nn.functional.linear(a, tp[p + "mlp.w_proj"], tp[p + "mlp.b_proj"])
     hf = ln(x, tp["lnf.g"], tp["lnf.b"])
-    z = hf @ tp["wte"].T
+    if "head.w" in tp:
+        z = torch.nn.functional.linear(hf, tp["head.w"], tp["head.b"])
+    else:
+        z = hf @ tp["wte"].T
     tgt_t = torch.as_tensor(tgt.astype(np.int64)).reshape(-1)
     return torch.nn.functional.cross_entropy(z.reshape(-1, cfg.vocab), tgt_t, ignore_index=-1), z
 
 
-@pytest.mark.parametrize("which", ["tiny", "c1_like"])
+@pytest.mark.parametrize("which", ["tiny", "tiny_untied", "c1_like"])
 def test_torch_autograd_cross_check(which):
     """P15: gradients of the hand-derived backward equal torch's autograd of
     the same network to 1e-10 relative per tensor; logits and loss too."""
     torch = pytest.importorskip("torch")
-    if which == "tiny":
-        cfg = tiny_cfg()
+    if which.startswith("tiny"):
+        cfg = tiny_cfg(untied_head=which == "tiny_untied")
         params = random_params(cfg, 5)
         tok, tgt, doc = tiny_batch(cfg, 9)
     else:
@@ -448,6 +456,36 @@ def test_head_and_tied_embedding_sum_rules():
     tok, tgt, doc = tiny_batch(cfg)
     _, grads, _, _ = oracle.loss_and_grads(params, cfg, tok, tgt, doc)
     np.testing.assert_allclose(grads["wte"].sum(axis=0), grads["wpe"].sum(axis=0), atol=1e-12)
+
+
+def test_untied_head_reduces_to_tied_and_bias_rule():
+    """A separate head equal to wte with a zero bias computes the tied model:
+    the same logits and loss, and the tied wte gradient splits into the
+    embedding part (untied wte) plus the head part (head.w). The head bias
+    gradient is the column sum of dz, and dz rows sum to 0, so it sums to 0
+    over the vocabulary."""
+    cfg = tiny_cfg()
+    ucfg = tiny_cfg(untied_head=True)
+    params = random_params(cfg, 12)
+    tok, tgt, doc = tiny_batch(cfg)
+    loss_t, g_t, z_t, _ = oracle.loss_and_grads(params, cfg, tok, tgt, doc)
+    up = dict(params, **{"head.w": params["wte"].copy(), "head.b": np.zeros(cfg.vocab)})
+    loss_u, g_u, z_u, _ = oracle.loss_and_grads(up, ucfg, tok, tgt, doc)
+    assert loss_u == pytest.approx(loss_t, rel=1e-14)
+    np.testing.assert_allclose(z_u, z_t, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(g_u["wte"] + g_u["head.w"], g_t["wte"], rtol=1e-12, atol=1e-14)
+    for k in params:
+        if k != "wte":
+            np.testing.assert_allclose(g_u[k], g_t[k], rtol=1e-12, atol=1e-14)
+    assert abs(g_u["head.b"].sum()) < 1e-14
+    # a bias that is constant over the vocabulary shifts every logit of a row
+    # equally: softmax, loss and every other gradient are unchanged
+    up2 = dict(up, **{"head.b": np.full(cfg.vocab, 0.75)})
+    loss_c, g_c, z_c, _ = oracle.loss_and_grads(up2, ucfg, tok, tgt, doc)
+    assert loss_c == pytest.approx(loss_u, rel=1e-13)
+    np.testing.assert_allclose(z_c - 0.75, z_u, rtol=1e-13, atol=1e-13)
+    for k in g_u:
+        np.testing.assert_allclose(g_c[k], g_u[k], rtol=1e-11, atol=1e-14)
 
 
 # ----------------------------------------------------------- P12, P13: AdamW
