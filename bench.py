@@ -65,7 +65,7 @@ def attention_flops(shape, doc_ids, B, T):
 # Kernel symbol of each timing class whose HBM traffic is taken from counters
 # (a class must map to one kernel instantiation used by nothing else).
 TRAFFIC_SYMBOLS = {
-    "gemm_fc2_bwd_dx": "gemm_bf16_kernel<128, 128, 2, 2, true, false, 3,",
+    "gemm_fc2_bwd_dx": "gemm16_kernel<128, 128, 2, 2, true, false, 3,",
     "attn_bwd_dkv": "attn_dkv_kernel<64>",
     "attn_fwd": "attn_fwd_kernel<64>",
 }
@@ -209,6 +209,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prof", action="store_true")
     ap.add_argument("--ckpt", metavar="DIR", help="also time a checkpoint save and load of the model in DIR")
+    ap.add_argument("--fp16", action="store_true",
+                    help="also time the step with fp16 operands and dynamic loss scaling")
     ap.add_argument("--untied-head", action="store_true",
                     help="also time the step of the same model with a separate vocabulary projection and bias")
     ap.add_argument("--gen", type=int, default=0, metavar="N",
@@ -364,29 +366,43 @@ def main():
         log(f"bench: generation {B}x{args.gen} tokens: {rates[False]:.2f} s recomputing, "
             f"{rates[True]:.2f} s with the cache")
 
+    def time_variant(vshape):
+        """ms per step of the same workload on a model of another variant."""
+        vm = sd.Model(vshape, max_batch=B)
+        vm.set(sd.LM_PARAMS, synth.init_params(vshape))
+        kw = dict(lr=shape.lr, beta1=shape.beta1, beta2=shape.beta2, eps=shape.eps,
+                  weight_decay=shape.weight_decay, clip=shape.clip)
+        for i in range(args.warmup):
+            vm.train_step(tok, tgt, doc, step=i + 1, **kw)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            vm.train_step(tok, tgt, doc, step=args.warmup + i + 1, **kw)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        vms = ev0.elapsed_time(ev1) / args.steps
+        return vm, vms
+
     if args.untied_head:
         # the same workload with head.w [V, C] and head.b [V] instead of the
         # projection tied to wte: one more weight-gradient-sized AdamW range
         # and the head bias gradient
-        ushape = shape.replace(untied_head=True)
-        um = sd.Model(ushape, max_batch=B)
-        um.set(sd.LM_PARAMS, synth.init_params(ushape))
-        for i in range(args.warmup):
-            um.train_step(tok, tgt, doc, lr=shape.lr, step=i + 1, beta1=shape.beta1, beta2=shape.beta2,
-                          eps=shape.eps, weight_decay=shape.weight_decay, clip=shape.clip)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(args.steps):
-            um.train_step(tok, tgt, doc, lr=shape.lr, step=args.warmup + i + 1, beta1=shape.beta1,
-                          beta2=shape.beta2, eps=shape.eps, weight_decay=shape.weight_decay, clip=shape.clip)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ums = ev0.elapsed_time(ev1) / args.steps
+        um, ums = time_variant(shape.replace(untied_head=True))
         out["untied_head"] = {"ms_per_step": round(ums, 4), "tokens_per_s": round(B * T / (ums / 1e3), 1),
                               "params": int(sum(r * c for _, _, r, c in um.table)),
                               "loss": round(float(um.stats[0]), 4)}
         log(f"bench: untied head {ums:.3f} ms/step, {B * T / (ums / 1e3):,.0f} tokens/s")
         del um
+
+    if args.fp16:
+        # fp16 operands with dynamic loss scaling instead of bf16
+        fm, fms = time_variant(shape.replace(precision="fp16"))
+        sc = fm.loss_scaler()
+        out["fp16"] = {"ms_per_step": round(fms, 4), "tokens_per_s": round(B * T / (fms / 1e3), 1),
+                       "loss": round(float(fm.stats[0]), 4), "loss_scale": sc["scale"],
+                       "finite_steps_in_a_row": sc["good_steps"]}
+        log(f"bench: fp16 {fms:.3f} ms/step, {B * T / (fms / 1e3):,.0f} tokens/s, loss scale {sc['scale']:g}")
+        del fm
 
     if args.ckpt:
         # checkpoint file of the multi-step driver: parameters + both Adam moments

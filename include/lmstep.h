@@ -67,7 +67,11 @@ typedef enum {
  * dimension d_model / n_heads must be 32 or 64; d_mlp a multiple of 64.
  * precision: 0 = fp32 everywhere; 1 = bf16 GEMM/attention operands with fp32
  * accumulation, fp32 residual stream, statistics, loss, gradients, Adam
- * moments and master weights.
+ * moments and master weights; 2 = the same with fp16 operands and dynamic
+ * loss scaling (LucilleAI page: FP16 autocast with a GradScaler): the loss
+ * gradient is multiplied by a scale S, the gradients are divided by S before
+ * the clip and the update, and a step whose gradients overflow (non-finite
+ * norm) is skipped and S multiplied by the backoff factor (lm_loss_scaler).
  * untied_head: 0 = logits z = h_f wte^T (tied, no bias); 1 = z = h_f
  * head.w^T + head.b with a separate head.w [V,C] and head.b [V]. */
 typedef struct {
@@ -137,12 +141,14 @@ lm_status model_get(const lm_model* model, lm_buf which, float* dst, int dst_on_
  *             row; a maximal run of equal ids is one document, attention stays
  *             inside it and positions restart at its first token
  * Computes the mean loss over valid targets, every gradient (kept raw,
- * before clipping, in the LM_GRADS buffer), the global norm n, the clip factor
- * and the AdamW update of parameters and moments.
+ * before clipping, in the LM_GRADS buffer; with precision 2 multiplied by the
+ * loss scale of the step), the global norm n, the clip factor and the AdamW
+ * update of parameters and moments.
  *   d_stats (may be NULL): 4 floats written on the device:
  *     [0] loss, [1] pre-clip gradient norm, [2] flags, [3] number of valid
  *     targets. flags bit 0: the norm was not finite, so the update was skipped
- *     and parameters and moments are unchanged; bit 1 (only with LMSTEP_CHECK=1
+ *     and parameters and moments are unchanged (precision 2: the loss scale
+ *     is multiplied by its backoff factor); bit 1 (only with LMSTEP_CHECK=1
  *     in the environment): a token, target or doc id was out of range or doc ids
  *     decreased. */
 lm_status train_step(lm_model* model, const int32_t* d_tokens, const int32_t* d_targets,
@@ -153,6 +159,24 @@ lm_status train_step(lm_model* model, const int32_t* d_tokens, const int32_t* d_
  * z = LN_f(x_L) wte^T. No loss, no backward, no update. */
 lm_status forward_logits(lm_model* model, const int32_t* d_tokens, const int32_t* d_doc_ids,
                          int32_t B, int32_t T, float* d_logits, void* stream);
+
+/* Dynamic loss scale of precision 2. scale: S, the factor on the loss
+ * gradient (default 65536); after `interval` steps in a row with a finite
+ * gradient norm S is multiplied by growth (default 2000 and 2), after a
+ * non-finite one (the step is skipped) by backoff (default 0.5); good_steps:
+ * the current run of finite steps. S and good_steps live on the device and
+ * change inside train_step without a host round trip. Models of precision 0
+ * and 1 have no scaler (LM_ERR_UNSUPPORTED). */
+typedef struct {
+  float scale, growth, backoff;
+  int32_t interval, good_steps;
+} lm_loss_scaler;
+
+/* Sets the scaler (synchronises stream). Requires scale > 0 finite, growth
+ * >= 1, 0 < backoff <= 1, interval >= 1, 0 <= good_steps < interval. */
+lm_status model_set_loss_scaler(lm_model* model, const lm_loss_scaler* scaler, void* stream);
+/* Reads the scaler (synchronises stream). */
+lm_status model_get_loss_scaler(const lm_model* model, lm_loss_scaler* out, void* stream);
 
 /* Thread-local message for the last non-OK status of this thread. */
 const char* lm_last_error(void);

@@ -8,7 +8,8 @@
  * void*; every call only enqueues work and returns 0, or a negative value if
  * the shape breaks the kernel's rules (nothing is enqueued then).
  * precision: 0 = fp32 activations (float), 1 = bf16 activations (uint16_t
- * storage of bfloat16). Statistics, residuals and gradients stay fp32.
+ * storage of bfloat16), 2 = fp16 activations (IEEE binary16). Statistics,
+ * residuals and gradients stay fp32.
  */
 #ifndef LMSTEP_KERNELS_H
 #define LMSTEP_KERNELS_H
@@ -84,9 +85,12 @@ int lmk_attn_bwd(int precision, const void* qkv, const void* o, const float* lse
 /* Softmax cross-entropy over z [M, ldz] (V valid columns, ldz a multiple of
  * 8) and targets [M] (-1 = ignored): loss[0] = mean over valid rows of
  * lse - z[tgt]; z is overwritten with dz = (softmax - onehot)/N (0 on ignored
- * rows and padding columns); loss[3] = N. ws: int32 [4] + fp32 [M] scratch. */
+ * rows and padding columns); loss[3] = N. ws: int32 [4] + fp32 [M] scratch.
+ * loss_scale (nullable, one device float S): dz is multiplied by S (the
+ * gradient of S times the loss, for fp16 training with loss scaling, the
+ * LucilleAI page's GradScaler); the loss is not. */
 int lmk_xent(int precision, void* z, int64_t ldz, int M, int V, const int32_t* tgt, float* loss, int32_t* ws_n,
-             float* ws_rows, uint32_t* flags, void* stream);
+             float* ws_rows, uint32_t* flags, const float* loss_scale, void* stream);
 
 /* Stable counting sort of keys [M] in [0, nkeys): counts/offsets/chunk_base
  * [nkeys+1], perm [M] (rows of key v at perm[offsets[v] .. offsets[v+1]),
@@ -102,16 +106,24 @@ int64_t lmk_segment_sum_ws_floats(int M, int nkeys, int C);
 
 /* Global L2 norm of g [n] and the clip factor: norm_scale = [n, s], s =
  * clip/n if n > clip > 0 else 1 (RustGPT page: clip to L2 norm 5.0); flags
- * bit 0 if n is not finite. part: double scratch [1024]. */
+ * bit 0 if n is not finite. part: double scratch [1024].
+ * scale_state (nullable, device float[2] = [S, finite steps in a row]): g
+ * holds S times the gradient; then n is the norm of g divided by S,
+ * norm_scale[1] = s / S, and the state follows the dynamic loss-scale rule
+ * (LucilleAI page: GradScaler): a non-finite n sets S = S * backoff and the
+ * count to 0; otherwise the count grows by one, and on reaching `interval`
+ * S = S * growth and the count is 0. Without a state, growth, backoff and
+ * interval are ignored. */
 int lmk_grad_norm(const float* g, int64_t n, float clip, double* part, float* norm_scale, uint32_t* flags,
-                  void* stream);
+                  float* scale_state, float growth, float backoff, int interval, void* stream);
 
 /* AdamW with decoupled weight decay (Feste page, "Manual Backpropagation")
  * on n elements (n a multiple of 4), gradient scaled by norm_scale[1];
- * skipped entirely when flags bit 0 is set; shadow (nullable) gets bf16(p). */
+ * skipped entirely when flags bit 0 is set; shadow (nullable) gets p rounded to
+ * fp16 (shadow_f16 = 1) or bf16 (0). */
 int lmk_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float beta1, float beta2, float eps,
               float weight_decay, int step, const float* norm_scale, const uint32_t* flags, uint16_t* shadow,
-              void* stream);
+              int shadow_f16, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,3 +33,4 @@ from .model import (  # noqa: F401
 )
 from .schedule import lr_schedule  # noqa: F401
 from .generate import next_token, kept_ids, cdf_bounds  # noqa: F401
+from .scaler import loss_scale_update, loss_scale_trace  # noqa: F401

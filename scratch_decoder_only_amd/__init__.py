@@ -32,6 +32,7 @@ c_char_p, c_double = ctypes.c_char_p, ctypes.c_double
 LM_OK, LM_ERR_ARG, LM_ERR_WORKSPACE, LM_ERR_SHAPE, LM_ERR_HIP, LM_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 LM_PARAMS, LM_GRADS, LM_ADAM_M, LM_ADAM_V = 0, 1, 2, 3
 EPI_STORE, EPI_RESID, EPI_GELU, EPI_DGELU = 0, 1, 2, 3
+PRECISIONS = {"fp32": 0, "bf16": 1, "fp16": 2}
 
 
 class LmConfig(ctypes.Structure):
@@ -39,6 +40,11 @@ class LmConfig(ctypes.Structure):
                 ("d_mlp", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("max_batch", ctypes.c_int32), ("precision", ctypes.c_int32), ("ln_eps", ctypes.c_float),
                 ("untied_head", ctypes.c_int32)]
+
+
+class LmLossScaler(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("growth", ctypes.c_float), ("backoff", ctypes.c_float),
+                ("interval", ctypes.c_int32), ("good_steps", ctypes.c_int32)]
 
 
 class LmOptim(ctypes.Structure):
@@ -82,6 +88,8 @@ _sig("model_prefill", c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32
 _sig("model_decode", c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_void_p, c_void_p])
 _sig("sample_tokens", c_int, [c_void_p, ctypes.c_int32, ctypes.c_int32, c_int64, ctypes.c_float, ctypes.c_int32,
                               c_void_p, c_void_p, c_void_p])
+_sig("model_set_loss_scaler", c_int, [c_void_p, ctypes.POINTER(LmLossScaler), c_void_p])
+_sig("model_get_loss_scaler", c_int, [c_void_p, ctypes.POINTER(LmLossScaler), c_void_p])
 _sig("model_profile_enable", c_int, [c_void_p, c_int])
 _sig("model_profile_read", c_int, [c_void_p, ctypes.POINTER(LmProfileEntry), ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_int32), c_int])
@@ -98,12 +106,13 @@ _sig("lmk_index_layout", c_int, [_P, c_int, c_int, _P, _P, _P, _P, _P])
 _sig("lmk_embed_fwd", c_int, [_P, _P, _P, _P, c_int, c_int, c_int, _P, _P, _P])
 _sig("lmk_attn_fwd", c_int, [c_int, _P, _P, _P, c_int, c_int, c_int, c_int, _P, _P, _P])
 _sig("lmk_attn_bwd", c_int, [c_int, _P, _P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, _P, _P, _P])
-_sig("lmk_xent", c_int, [c_int, _P, c_int64, c_int, c_int, _P, _P, _P, _P, _P, _P])
+_sig("lmk_xent", c_int, [c_int, _P, c_int64, c_int, c_int, _P, _P, _P, _P, _P, _P, _P])
 _sig("lmk_csr", c_int, [_P, c_int, c_int, _P, _P, _P, _P, _P, _P])
 _sig("lmk_segment_sum", c_int, [_P, c_int, c_int, c_int, _P, _P, _P, _P, _P, _P, c_int, _P])
 _sig("lmk_segment_sum_ws_floats", c_int64, [c_int, c_int, c_int])
-_sig("lmk_grad_norm", c_int, [_P, c_int64, c_float, _P, _P, _P, _P])
-_sig("lmk_adamw", c_int, [_P, _P, _P, _P, c_int64, c_float, c_float, c_float, c_float, c_float, c_int, _P, _P, _P, _P])
+_sig("lmk_grad_norm", c_int, [_P, c_int64, c_float, _P, _P, _P, _P, c_float, c_float, c_int, _P])
+_sig("lmk_adamw", c_int, [_P, _P, _P, _P, c_int64, c_float, c_float, c_float, c_float, c_float, c_int, _P, _P, _P, c_int,
+                          _P])
 
 lib = _lib
 
@@ -143,14 +152,14 @@ class Model:
 
     dims: object with vocab, d_model, n_heads, d_mlp, n_layers, max_seq,
     ln_eps and optionally untied_head (e.g. a synth.ModelShape); precision
-    "fp32" or "bf16".
+    "fp32", "bf16" or "fp16" (fp16 operands with dynamic loss scaling).
     """
 
     def __init__(self, dims, max_batch: int, precision: Optional[str] = None, device="cuda"):
         torch = _torch()
         prec = precision or getattr(dims, "precision", "bf16")
         self.cfg = LmConfig(dims.vocab, dims.d_model, dims.n_heads, dims.d_mlp, dims.n_layers, dims.max_seq,
-                            max_batch, 1 if prec == "bf16" else 0, float(getattr(dims, "ln_eps", 1e-5)),
+                            max_batch, PRECISIONS[prec], float(getattr(dims, "ln_eps", 1e-5)),
                             1 if getattr(dims, "untied_head", False) else 0)
         self.precision = prec
         nbytes = _lib.lm_workspace_bytes(ctypes.byref(self.cfg))
@@ -260,6 +269,17 @@ class Model:
         return out
 
     # ---- checkpoints
+    # ---- dynamic loss scale (precision "fp16")
+    def loss_scaler(self) -> Dict[str, float]:
+        ls = LmLossScaler()
+        _check(_lib.model_get_loss_scaler(self._h, ctypes.byref(ls), _stream()), "model_get_loss_scaler")
+        return {"scale": ls.scale, "growth": ls.growth, "backoff": ls.backoff, "interval": ls.interval,
+                "good_steps": ls.good_steps}
+
+    def set_loss_scaler(self, scale=65536.0, growth=2.0, backoff=0.5, interval=2000, good_steps=0):
+        ls = LmLossScaler(scale, growth, backoff, interval, good_steps)
+        _check(_lib.model_set_loss_scaler(self._h, ctypes.byref(ls), _stream()), "model_set_loss_scaler")
+
     def save(self, path: str, step: int):
         """Parameters and Adam moments to a checkpoint file (safetensors layout)."""
         _check(_lib.model_save(self._h, os.fsencode(path), int(step), _stream()), "model_save")
@@ -426,9 +446,9 @@ def attn_bwd(precision, qkv, o, lse, dout, start, end, B, T, H, D, delta, dqkv):
                               D, _ptr(delta), _ptr(dqkv), _stream()), "lmk_attn_bwd")
 
 
-def xent(precision, z, ldz, M, V, tgt, loss, ws_n, ws_rows, flags):
+def xent(precision, z, ldz, M, V, tgt, loss, ws_n, ws_rows, flags, loss_scale=None):
     _kcheck(_lib.lmk_xent(precision, _ptr(z), ldz, M, V, _ptr(tgt), _ptr(loss), _ptr(ws_n), _ptr(ws_rows),
-                          _ptr(flags), _stream()), "lmk_xent")
+                          _ptr(flags), _ptr(loss_scale), _stream()), "lmk_xent")
 
 
 def csr(keys, M, nkeys, counts, offsets, chunk_base, perm, rank):
@@ -445,11 +465,11 @@ def segment_sum(dx, M, C, nkeys, counts, offsets, chunk_base, perm, partial, dst
                                  _ptr(partial), _ptr(dst), int(accumulate), _stream()), "lmk_segment_sum")
 
 
-def grad_norm(g, clip, part, norm_scale, flags):
-    _kcheck(_lib.lmk_grad_norm(_ptr(g), g.numel(), clip, _ptr(part), _ptr(norm_scale), _ptr(flags), _stream()),
-            "lmk_grad_norm")
+def grad_norm(g, clip, part, norm_scale, flags, scale_state=None, growth=2.0, backoff=0.5, interval=2000):
+    _kcheck(_lib.lmk_grad_norm(_ptr(g), g.numel(), clip, _ptr(part), _ptr(norm_scale), _ptr(flags), _ptr(scale_state),
+                               growth, backoff, interval, _stream()), "lmk_grad_norm")
 
 
-def adamw(p, g, m, v, lr, beta1, beta2, eps, wd, step, norm_scale, flags, shadow=None):
+def adamw(p, g, m, v, lr, beta1, beta2, eps, wd, step, norm_scale, flags, shadow=None, shadow_f16=False):
     _kcheck(_lib.lmk_adamw(_ptr(p), _ptr(g), _ptr(m), _ptr(v), p.numel(), lr, beta1, beta2, eps, wd, step,
-                           _ptr(norm_scale), _ptr(flags), _ptr(shadow), _stream()), "lmk_adamw")
+                           _ptr(norm_scale), _ptr(flags), _ptr(shadow), int(shadow_f16), _stream()), "lmk_adamw")

@@ -107,7 +107,8 @@ struct Profiler {
 struct lm_model {
   lm_config cfg;
   int V, C, H, D, F, L, S, Bmax;
-  bool bf;   // bf16 compute
+  int prec;  // 0 fp32, 1 bf16, 2 fp16 (with dynamic loss scaling)
+  bool h16;  // 16-bit operands (bf16 or fp16)
   bool untied;  // separate vocabulary projection head.w [V, C] with bias head.b [V]
   long Vp;   // padded vocabulary (columns of the logits; rows reserved for wte and head.w)
   long ldz;  // leading dimension of the logits
@@ -122,7 +123,7 @@ struct lm_model {
   size_t act_size;  // bytes of one activation element
   // arena slices
   float *params, *grads, *adam_m, *adam_v;
-  bf16* shadow;  // bf16 copy of the flat parameter buffer (bf16 path)
+  uint16_t* shadow;  // 16-bit copy of the flat parameter buffer (bf16 or fp16 path)
   float* x;      // [L+1][M][C]
   float* xm;     // [L][M][C]
   char *y1, *qkv, *o, *y2, *u, *a, *hf, *logits;
@@ -135,6 +136,9 @@ struct lm_model {
   int32_t *start, *end, *pos, *n_valid;
   uint32_t* flags;
   float *row_loss, *norm_scale, *stats_own;
+  float* scale_state;                 // fp16: [loss scale S, finite steps in a row]
+  float ls_growth = 2.f, ls_backoff = 0.5f;
+  int ls_interval = 2000;
   double* norm_part;
   size_t bytes = 0;
   Profiler prof;
@@ -146,10 +150,21 @@ struct lm_model {
   T* act(char* base, long elem_off) const {
     return reinterpret_cast<T*>(base + elem_off * act_size);
   }
-  // operand copy of a weight: bf16 shadow (bf16 path) or the fp32 master
-  const void* W(long off) const { return bf ? static_cast<const void*>(shadow + off) : params + off; }
+  // operand copy of a weight: the 16-bit copy (bf16 or fp16 path) or the fp32 master
+  const void* W(long off) const { return h16 ? static_cast<const void*>(shadow + off) : params + off; }
   // the vocabulary projection's weight (wte when tied)
   long head_w() const { return untied ? o_head_w : o_wte; }
+  // the dynamic loss scale (fp16 only)
+  LossScaler scaler() const {
+    LossScaler ls;
+    if (prec == 2) {
+      ls.state = scale_state;
+      ls.growth = ls_growth;
+      ls.backoff = ls_backoff;
+      ls.interval = ls_interval;
+    }
+    return ls;
+  }
 };
 
 namespace {
@@ -165,7 +180,8 @@ lm_status validate(const lm_config* c) {
   int D = c->d_model / c->n_heads;
   if (D != 32 && D != 64) return fail(LM_ERR_UNSUPPORTED, "head dimension must be 32 or 64");
   if (c->d_mlp % 64) return fail(LM_ERR_UNSUPPORTED, "d_mlp must be a multiple of 64");
-  if (c->precision != 0 && c->precision != 1) return fail(LM_ERR_ARG, "precision must be 0 (fp32) or 1 (bf16)");
+  if (c->precision < 0 || c->precision > 2)
+    return fail(LM_ERR_ARG, "precision must be 0 (fp32), 1 (bf16) or 2 (fp16 with loss scaling)");
   if (c->untied_head != 0 && c->untied_head != 1) return fail(LM_ERR_ARG, "untied_head must be 0 or 1");
   if (!(c->ln_eps >= 0.f)) return fail(LM_ERR_ARG, "ln_eps must be >= 0");
   if ((long)c->max_batch * c->max_seq > (1L << 24)) return fail(LM_ERR_SHAPE, "max_batch * max_seq too large");
@@ -220,7 +236,7 @@ void carve(lm_model* m, char* base) {
   m->grads = c.take<float>(m->P);
   m->adam_m = c.take<float>(m->P);
   m->adam_v = c.take<float>(m->P);
-  m->shadow = m->bf ? c.take<bf16>(m->P) : nullptr;
+  m->shadow = m->h16 ? c.take<uint16_t>(m->P) : nullptr;
   m->x = c.take<float>((L + 1) * M * C);
   m->xm = c.take<float>(L * M * C);
   m->y1 = c.take<char>(L * M * C * A);
@@ -268,6 +284,7 @@ void carve(lm_model* m, char* base) {
   m->row_loss = c.take<float>(M);
   m->norm_scale = c.take<float>(4);
   m->stats_own = c.take<float>(4);
+  m->scale_state = c.take<float>(2);
   m->norm_part = c.take<double>(kNormBlocks);
   m->bytes = align_up(c.off, kAlign);
 }
@@ -283,11 +300,12 @@ lm_model* new_model(const lm_config* cfg) {
   m->L = cfg->n_layers;
   m->S = cfg->max_seq;
   m->Bmax = cfg->max_batch;
-  m->bf = cfg->precision == 1;
+  m->prec = cfg->precision;
+  m->h16 = m->prec != 0;
   m->untied = cfg->untied_head == 1;
-  m->act_size = m->bf ? 2 : 4;
-  m->Vp = m->bf ? round_up(m->V, 128) : m->V;
-  m->ldz = m->bf ? m->Vp : round_up(m->V, 4);
+  m->act_size = m->h16 ? 2 : 4;
+  m->Vp = m->h16 ? round_up(m->V, 128) : m->V;
+  m->ldz = m->h16 ? m->Vp : round_up(m->V, 4);
   build_table(m);
   carve(m, nullptr);
   const char* chk = getenv("LMSTEP_CHECK");
@@ -323,7 +341,9 @@ struct Launcher {
 };
 
 int gemm(lm_model* m, const GemmOp& op, hipStream_t s) {
-  return m->bf ? gemm_bf16(op, m->gemm_ws, m->gemm_ws_floats, s) : gemm_f32(op, m->gemm_ws, m->gemm_ws_floats, s);
+  if (m->prec == 2) return gemm_f16(op, m->gemm_ws, m->gemm_ws_floats, s);
+  if (m->prec == 1) return gemm_bf16(op, m->gemm_ws, m->gemm_ws_floats, s);
+  return gemm_f32(op, m->gemm_ws, m->gemm_ws_floats, s);
 }
 
 // Y = X W^T (+ epilogue), X [M, K] activation, W [N, K] weight.
@@ -358,10 +378,19 @@ GemmOp dw_op(const void* dY, long M, long N, const void* X, long K, float* dW) {
 // bias head.b (untied). bf16: N = Vp; the padding rows of W are zero, so the
 // padding columns of z are too (plus the zero padding of the bias).
 GemmOp head_op(lm_model* m, const void* hf, long M, void* z) {
-  GemmOp op = fwd_op(m, hf, M, m->C, m->head_w(), m->bf ? m->Vp : m->V, z, EPI_STORE);
+  GemmOp op = fwd_op(m, hf, M, m->C, m->head_w(), m->h16 ? m->Vp : m->V, z, EPI_STORE);
   op.ldc = m->ldz;
   if (m->untied) op.bias = m->P_(m->o_head_b);
   return op;
+}
+
+// Runs f(tag) with a null pointer of the model's activation type (float,
+// bf16 or f16) as the tag.
+template <typename F>
+int with_act(const lm_model* m, F&& f) {
+  if (m->prec == 2) return f(static_cast<f16*>(nullptr));
+  if (m->prec == 1) return f(static_cast<bf16*>(nullptr));
+  return f(static_cast<float*>(nullptr));
 }
 
 template <typename E>
@@ -396,7 +425,10 @@ int forward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* d
       Lr.run("gemm_qkv_fwd", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, op, s); });
     }
     at.qkv = qkv; at.o = o; at.lse = m->lse + l * M * H;
-    Lr.run("attn_fwd", 0, 0, [&] { rc |= m->bf ? attn_fwd_bf16(at, s) : attn_fwd_f32(at, s); });
+    Lr.run("attn_fwd", 0, 0, [&] {
+      if constexpr (std::is_same_v<E, float>) rc |= attn_fwd_f32(at, s);
+      else rc |= attn_fwd16<E>(at, s);
+    });
     {
       GemmOp op = fwd_op(m, o, M, C, b.w_o, C, xml, EPI_RESID);
       op.bias = m->P_(b.b_o); op.R = xl; op.ldr = C;
@@ -508,7 +540,9 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   int rc = 0;
   E* z = m->act<E>(m->logits, 0);
   Lr.run("count_valid", 0, 4.0 * M, [&] { launch_count_valid(tgt, (int)M, m->V, m->n_valid, stats, m->flags, s); });
-  Lr.run("xent", 0, Mf * V * 2 * A, [&] { launch_xent<E>(z, m->ldz, (int)M, m->V, tgt, m->n_valid, m->row_loss, s); });
+  Lr.run("xent", 0, Mf * V * 2 * A, [&] {
+    launch_xent<E>(z, m->ldz, (int)M, m->V, tgt, m->n_valid, m->row_loss, m->scaler().state, s);
+  });
   Lr.run("loss_reduce", 0, 4.0 * M, [&] { launch_loss_reduce(m->row_loss, (int)M, m->n_valid, stats, s); });
   E* hf = m->act<E>(m->hf, 0);
   E* g_act = m->act<E>(m->g_act, 0);
@@ -516,7 +550,7 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   // dz W; untied: the bias gradient is the column sums of dz (its zero
   // padding columns give the zero padding of the bias gradient)
   {
-    GemmOp op = dw_op(z, M, m->bf ? m->Vp : V, hf, C, m->grads + m->head_w());
+    GemmOp op = dw_op(z, M, m->h16 ? m->Vp : V, hf, C, m->grads + m->head_w());
     op.lda = m->ldz;
     op.M_out = (int)V;
     Lr.run("gemm_head_bwd_dw", 2.0 * M * V * C, 0, [&] { rc |= gemm(m, op, s); });
@@ -526,7 +560,7 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
       launch_colsum<E>(z, m->ldz, (int)M, (int)m->ldz, m->col_part, m->grads + m->o_head_b, s);
     });
   {
-    GemmOp op = dx_op(m, z, M, m->bf ? m->Vp : V, m->head_w(), C, m->dy, EPI_STORE);
+    GemmOp op = dx_op(m, z, M, m->h16 ? m->Vp : V, m->head_w(), C, m->dy, EPI_STORE);
     op.lda = m->ldz;
     op.c_f32 = true;
     Lr.run("gemm_head_bwd_dx", 2.0 * M * V * C, 0, [&] { rc |= gemm(m, op, s); });
@@ -588,9 +622,10 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
       at.o = o; at.lse = m->lse + l * M * H; at.dout = dO; at.delta = m->delta; at.dqkv = dbig;
       static const char* names[3] = {"attn_bwd_delta", "attn_bwd_dq", "attn_bwd_dkv"};
       // bf16: the dQ pass computes delta itself (part 0 launches nothing)
-      for (int part = m->bf ? 1 : 0; part < 3; ++part)
+      for (int part = m->h16 ? 1 : 0; part < 3; ++part)
         Lr.run(names[part], 0, part == 0 ? Mf * C * 2 * A : 0, [&] {
-          rc |= m->bf ? attn_bwd_part_bf16(at, part, s) : attn_bwd_part_f32(at, part, s);
+          if constexpr (std::is_same_v<E, float>) rc |= attn_bwd_part_f32(at, part, s);
+          else rc |= attn_bwd_part16<E>(at, part, s);
         });
     }
     Lr.run("gemm_qkv_bwd_dw", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, dw_op(dbig, M, 3 * C, y1, C, m->grads + b.w_qkv), s); });
@@ -658,6 +693,14 @@ lm_status model_create(const lm_config* cfg, void* d_arena, size_t arena_bytes, 
   char* z1 = m->shadow ? reinterpret_cast<char*>(m->shadow + m->P) : reinterpret_cast<char*>(m->adam_v + m->P);
   launch_fill_u32(reinterpret_cast<uint32_t*>(z0), 0u, (long)((z1 - z0) / 4), s);
   launch_fill_u32(m->flags, 0u, 4, s);
+  if (m->prec == 2) {
+    // the default dynamic loss scale: S = 2^16, no finite steps yet
+    const float init[2] = {65536.f, 0.f};
+    uint32_t bits[2];
+    std::memcpy(bits, init, sizeof(bits));
+    launch_fill_u32(reinterpret_cast<uint32_t*>(m->scale_state), bits[0], 1, s);
+    launch_fill_u32(reinterpret_cast<uint32_t*>(m->scale_state) + 1, bits[1], 1, s);
+  }
   st = hip_status("model_create");
   if (st != LM_OK) {
     delete m;
@@ -722,7 +765,7 @@ lm_status model_set(lm_model* m, lm_buf which, const float* src, int src_on_devi
       zero(m->o_head_b + m->V, std::max(m->Vp, m->ldz) - m->V);
     }
   }
-  if (which == LM_PARAMS && m->bf) launch_make_shadow(m->params, m->P, m->shadow, m->P, 0, s);
+  if (which == LM_PARAMS && m->h16) launch_make_shadow(m->params, m->P, m->shadow, m->prec == 2, s);
   if (!src_on_device) {
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail(LM_ERR_HIP, std::string("model_set: ") + hipGetErrorString(e));
@@ -754,17 +797,14 @@ lm_status train_step(lm_model* m, const int32_t* tok, const int32_t* tgt, const 
   Launcher Lr(m, s);
   int rc = 0;
   Lr.run("misc", 0, 0, [&] { launch_fill_u32(m->flags, 0u, 4, s); });
-  if (m->bf) {
-    rc |= forward_pass<bf16>(m, Lr, tok, doc, B, T);
-    rc |= backward_pass<bf16>(m, Lr, tok, tgt, B, T, stats);
-  } else {
-    rc |= forward_pass<float>(m, Lr, tok, doc, B, T);
-    rc |= backward_pass<float>(m, Lr, tok, tgt, B, T, stats);
-  }
+  rc |= with_act(m, [&](auto tag) {
+    using E = std::remove_pointer_t<decltype(tag)>;
+    return forward_pass<E>(m, Lr, tok, doc, B, T) | backward_pass<E>(m, Lr, tok, tgt, B, T, stats);
+  });
   if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
   Lr.run("grad_norm", 0, 4.0 * m->P, [&] {
     launch_sumsq_partials(m->grads, m->P, m->norm_part, s);
-    launch_norm_finalize(m->norm_part, opt->clip_norm, m->norm_scale, m->flags, stats, s);
+    launch_norm_finalize(m->norm_part, opt->clip_norm, m->norm_scale, m->flags, stats, m->scaler(), s);
   });
   AdamArgs a{};
   a.p = m->params; a.g = m->grads; a.m = m->adam_m; a.v = m->adam_v; a.n = m->P;
@@ -772,8 +812,8 @@ lm_status train_step(lm_model* m, const int32_t* tok, const int32_t* tgt, const 
   a.bc1 = (float)(1.0 - std::pow((double)opt->beta1, (double)opt->step));
   a.bc2 = (float)(1.0 - std::pow((double)opt->beta2, (double)opt->step));
   a.norm_scale = m->norm_scale; a.flags = m->flags;
-  a.shadow = m->shadow; a.shadow_split = m->P; a.shadow_shift = 0;
-  Lr.run("adamw", 0, (m->bf ? 34.0 : 32.0) * m->P, [&] { launch_adamw(a, s); });
+  a.shadow = m->shadow; a.shadow_f16 = m->prec == 2;
+  Lr.run("adamw", 0, (m->h16 ? 34.0 : 32.0) * m->P, [&] { launch_adamw(a, s); });
   Lr.run("misc", 0, 0, [&] { launch_write_flags(m->flags, stats, s); });
   return hip_status("train_step");
 }
@@ -787,13 +827,12 @@ lm_status forward_logits(lm_model* m, const int32_t* tok, const int32_t* doc, in
   Launcher Lr(m, s);
   int rc;
   launch_fill_u32(m->flags, 0u, 4, s);
-  if (m->bf) {
-    rc = forward_pass<bf16>(m, Lr, tok, doc, B, T);
-    launch_logits_out<bf16>(m->act<bf16>(m->logits, 0), m->ldz, B * T, m->V, d_logits, s);
-  } else {
-    rc = forward_pass<float>(m, Lr, tok, doc, B, T);
-    launch_logits_out<float>(m->act<float>(m->logits, 0), m->ldz, B * T, m->V, d_logits, s);
-  }
+  rc = with_act(m, [&](auto tag) {
+    using E = std::remove_pointer_t<decltype(tag)>;
+    const int r = forward_pass<E>(m, Lr, tok, doc, B, T);
+    launch_logits_out<E>(m->act<E>(m->logits, 0), m->ldz, B * T, m->V, d_logits, s);
+    return r;
+  });
   if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
   return hip_status("forward_logits");
 }
@@ -823,13 +862,12 @@ lm_status model_prefill(lm_model* m, const int32_t* tok, int32_t B, int32_t T, v
     // logits of each row's last position
     launch_logits_out<E>(m->act<E>(m->logits, 0) + (long)(T - 1) * m->ldz, (long)T * m->ldz, B, m->V, d_logits, s);
   };
-  if (m->bf) {
-    rc = forward_pass<bf16>(m, Lr, tok, nullptr, B, T);
-    fill(reinterpret_cast<bf16*>(d_cache));
-  } else {
-    rc = forward_pass<float>(m, Lr, tok, nullptr, B, T);
-    fill(reinterpret_cast<float*>(d_cache));
-  }
+  rc = with_act(m, [&](auto tag) {
+    using E = std::remove_pointer_t<decltype(tag)>;
+    const int r = forward_pass<E>(m, Lr, tok, nullptr, B, T);
+    fill(reinterpret_cast<E*>(d_cache));
+    return r;
+  });
   if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
   return hip_status("model_prefill");
 }
@@ -844,15 +882,48 @@ lm_status model_decode(lm_model* m, const int32_t* tok, int32_t B, int32_t pos, 
   Launcher Lr(m, s);
   int rc;
   launch_fill_u32(m->flags, 0u, 4, s);
-  if (m->bf) {
-    rc = decode_pass<bf16>(m, Lr, tok, B, pos, reinterpret_cast<bf16*>(d_cache));
-    launch_logits_out<bf16>(m->act<bf16>(m->logits, 0), m->ldz, B, m->V, d_logits, s);
-  } else {
-    rc = decode_pass<float>(m, Lr, tok, B, pos, reinterpret_cast<float*>(d_cache));
-    launch_logits_out<float>(m->act<float>(m->logits, 0), m->ldz, B, m->V, d_logits, s);
-  }
+  rc = with_act(m, [&](auto tag) {
+    using E = std::remove_pointer_t<decltype(tag)>;
+    const int r = decode_pass<E>(m, Lr, tok, B, pos, reinterpret_cast<E*>(d_cache));
+    launch_logits_out<E>(m->act<E>(m->logits, 0), m->ldz, B, m->V, d_logits, s);
+    return r;
+  });
   if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
   return hip_status("model_decode");
+}
+
+lm_status model_set_loss_scaler(lm_model* m, const lm_loss_scaler* ls, void* stream) {
+  if (!m || !ls) return fail(LM_ERR_ARG, "model or scaler is NULL");
+  if (m->prec != 2) return fail(LM_ERR_UNSUPPORTED, "loss scaling belongs to the fp16 precision (2)");
+  if (!(ls->scale > 0.f) || !std::isfinite(ls->scale) || !(ls->growth >= 1.f) || !(ls->backoff > 0.f) ||
+      !(ls->backoff <= 1.f) || ls->interval < 1 || ls->good_steps < 0 || ls->good_steps >= ls->interval)
+    return fail(LM_ERR_ARG, "loss scaler: need scale > 0 finite, growth >= 1, 0 < backoff <= 1, interval >= 1, "
+                            "0 <= good_steps < interval");
+  m->ls_growth = ls->growth;
+  m->ls_backoff = ls->backoff;
+  m->ls_interval = ls->interval;
+  const float st[2] = {ls->scale, (float)ls->good_steps};
+  hipError_t e = hipMemcpyAsync(m->scale_state, st, sizeof(st), hipMemcpyHostToDevice,
+                                reinterpret_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_ERR_HIP, std::string("model_set_loss_scaler: ") + hipGetErrorString(e));
+  return LM_OK;
+}
+
+lm_status model_get_loss_scaler(const lm_model* m, lm_loss_scaler* out, void* stream) {
+  if (!m || !out) return fail(LM_ERR_ARG, "model or out is NULL");
+  if (m->prec != 2) return fail(LM_ERR_UNSUPPORTED, "loss scaling belongs to the fp16 precision (2)");
+  float st[2];
+  hipError_t e = hipMemcpyAsync(st, m->scale_state, sizeof(st), hipMemcpyDeviceToHost,
+                                reinterpret_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LM_ERR_HIP, std::string("model_get_loss_scaler: ") + hipGetErrorString(e));
+  out->scale = st[0];
+  out->good_steps = (int32_t)st[1];
+  out->growth = m->ls_growth;
+  out->backoff = m->ls_backoff;
+  out->interval = m->ls_interval;
+  return LM_OK;
 }
 
 const char* lm_last_error(void) { return g_err.c_str(); }

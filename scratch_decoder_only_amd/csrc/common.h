@@ -7,8 +7,10 @@
 namespace lm {
 
 typedef uint16_t bf16;  // storage of a bfloat16 value (upper half of an fp32)
+typedef _Float16 f16;   // IEEE binary16
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -32,6 +34,51 @@ template <> struct Act<bf16> {
   static __device__ __forceinline__ float ld(const bf16* p, long i) { return bf2f(p[i]); }
   static __device__ __forceinline__ void st(bf16* p, long i, float v) { p[i] = f2bf(v); }
 };
+template <> struct Act<f16> {
+  static __device__ __forceinline__ float ld(const f16* p, long i) { return (float)p[i]; }
+  static __device__ __forceinline__ void st(f16* p, long i, float v) { p[i] = (f16)v; }
+};
+
+// The two 16-bit operand types (bf16, f16) as raw bits: conversions of one
+// value and of a packed pair (low half first), round to nearest even; fp16
+// overflows to +-inf.
+template <typename E> struct H16;
+template <> struct H16<bf16> {
+  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  static __device__ __forceinline__ uint32_t bits(float f) { return f2bf(f); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, v2));
+  }
+};
+template <> struct H16<f16> {
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+  static __device__ __forceinline__ uint32_t bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, v2));
+  }
+};
+
+// 32x32x16 matrix-core product with fp32 accumulation, operands as 8 raw
+// 16-bit values per lane of the type E.
+template <typename E>
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c);
+template <>
+__device__ __forceinline__ f32x16_t mfma32<bf16>(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16_t mfma32<f16>(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

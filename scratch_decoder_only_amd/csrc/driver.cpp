@@ -211,9 +211,24 @@ lm_status model_save(const lm_model* m, const char* path, int32_t step, void* st
   if ((st = read_table(m, tb)) != LM_OK) return st;
 
   // header: every tensor of every section, data offsets back to back
+  std::map<std::string, std::string> meta = config_meta(cfg, step);
+  if (cfg.precision == 2) {
+    // the dynamic loss scale is part of an fp16 run's state
+    lm_loss_scaler ls;
+    if ((st = model_get_loss_scaler(m, &ls, stream)) != LM_OK) return st;
+    char v[32];
+    std::snprintf(v, sizeof(v), "%.9g", (double)ls.scale);
+    meta["loss_scale"] = v;
+    std::snprintf(v, sizeof(v), "%.9g", (double)ls.growth);
+    meta["loss_scale_growth"] = v;
+    std::snprintf(v, sizeof(v), "%.9g", (double)ls.backoff);
+    meta["loss_scale_backoff"] = v;
+    meta["loss_scale_interval"] = std::to_string(ls.interval);
+    meta["loss_scale_good_steps"] = std::to_string(ls.good_steps);
+  }
   std::string h = "{\"__metadata__\":{";
   bool first = true;
-  for (const auto& kv : config_meta(cfg, step)) {
+  for (const auto& kv : meta) {
     h += (first ? "\"" : ",\"") + kv.first + "\":\"" + kv.second + "\"";
     first = false;
   }
@@ -336,6 +351,15 @@ lm_status model_load(lm_model* m, const char* path, int32_t* step, void* stream)
         return set_error(LM_ERR_ARG, "reading " + name + " failed");
     }
     if ((st = model_set(m, sec.buf, host.get(), 0, stream)) != LM_OK) return st;
+  }
+  if (cfg.precision == 2 && meta_str("loss_scale") != "<missing>") {
+    lm_loss_scaler ls;
+    ls.scale = std::strtof(meta_str("loss_scale").c_str(), nullptr);
+    ls.growth = std::strtof(meta_str("loss_scale_growth").c_str(), nullptr);
+    ls.backoff = std::strtof(meta_str("loss_scale_backoff").c_str(), nullptr);
+    ls.interval = (int32_t)std::strtol(meta_str("loss_scale_interval").c_str(), nullptr, 10);
+    ls.good_steps = (int32_t)std::strtol(meta_str("loss_scale_good_steps").c_str(), nullptr, 10);
+    if ((st = model_set_loss_scaler(m, &ls, stream)) != LM_OK) return st;
   }
   if (step) *step = (int32_t)saved_step;
   return LM_OK;

@@ -1,5 +1,5 @@
 // Causal (optionally block-diagonal) multi-head self-attention on the gfx950
-// matrix cores, bf16 operands with fp32 accumulation.
+// matrix cores, 16-bit operands (bf16 or fp16, E) with fp32 accumulation.
 //
 // What is computed (Feste page, "Model Architecture": scores of future
 // positions are -inf before the softmax; 768 = 12 heads x 64): for query i and
@@ -13,7 +13,7 @@
 // 32 rows (queries in the forward and dQ passes, keys in the dK/dV pass) and
 // walks 64-row tiles of the other side, staged in LDS with a two-stage
 // pipeline (the next tile's buffer loads are in flight during the MFMAs of the
-// current one). The MFMA is v_mfma_f32_32x32x16_bf16 (lane l holds row l%32 of
+// current one). The MFMA is v_mfma_f32_32x32x16_bf16 or _f16 (lane l holds row l%32 of
 // a 32x16 operand, k-slots 8(l/32)..8(l/32)+7; the 32x32 result gives lane l
 // column l%32 and rows 8(e/4) + 4(l/32) + e%4, e = 0..15).
 // Forward and dQ compute S^T = K Q^T, so lane l keeps one query (l%32): the
@@ -63,17 +63,13 @@ struct RowTile {
   static __device__ __forceinline__ int off(int r, int c) { return r * D + ((c ^ sw(r)) << 3); }
 };
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 values to a packed bf16 pair (round to nearest even), one
-// conversion instruction.
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
-}
+// Fragments hold 8 raw 16-bit values; pairs of fp32 values become packed
+// 16-bit pairs with one conversion instruction (round to nearest even).
 __device__ __forceinline__ bf16x8_t as_frag(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+template <typename E>
 __device__ __forceinline__ uint4 pack_frag(const float* v) {
-  return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+  return make_uint4(H16<E>::pack(v[0], v[1]), H16<E>::pack(v[2], v[3]), H16<E>::pack(v[4], v[5]),
+                    H16<E>::pack(v[6], v[7]));
 }
 
 // Loader of one 64-row tile (rows r0..r0+63 of a [T, ld] bf16 matrix, columns
@@ -153,12 +149,13 @@ __device__ __forceinline__ void frags_global(bf16x8_t* f, const bf16* __restrict
 __device__ __forceinline__ int acc_row(int e, int lane) { return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3); }
 
 // Store the 16 accumulators of one 32-wide d tile of row `dst`: d = acc_row(e).
+template <typename E>
 __device__ __forceinline__ void store_acc_row(bf16* __restrict__ dst, const f32x16_t& acc, float scale, int lane) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     int d = g * 8 + (lane >> 5) * 4;
-    uint2 w = make_uint2(pack2(acc[4 * g] * scale, acc[4 * g + 1] * scale),
-                         pack2(acc[4 * g + 2] * scale, acc[4 * g + 3] * scale));
+    uint2 w = make_uint2(H16<E>::pack(acc[4 * g] * scale, acc[4 * g + 1] * scale),
+                         H16<E>::pack(acc[4 * g + 2] * scale, acc[4 * g + 3] * scale));
     *reinterpret_cast<uint2*>(dst + d) = w;
   }
 }
@@ -182,7 +179,7 @@ __device__ __forceinline__ void item_rows(const AttnArgs& a, bool queries, int& 
 }
 
 // ----------------------------------------------------------------- forward
-template <int D>
+template <int D, typename E>
 __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][RowTile<D>::ELEMS];
@@ -234,8 +231,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
       zero(s[sub]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sK[cur], sub * 32, ks, lane), qf[ks], s[sub], 0,
-                                                         0, 0);
+        s[sub] = mfma32<E>(frag_r<D>(sK[cur], sub * 32, ks, lane), qf[ks], s[sub]);
     }
     // A tile every score of which is kept (all 64 keys at or before the
     // wave's first query and at or after its last query's start) needs no
@@ -296,11 +292,10 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const bf16x8_t pf = as_frag(pack_frag(&p[st >> 1][(st & 1) * 8]));
+      const bf16x8_t pf = as_frag(pack_frag<E>(&p[st >> 1][(st & 1) * 8]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sV[cur], dt, st * 16, lane), pf, acc_o[dt], 0,
-                                                            0, 0);
+        acc_o[dt] = mfma32<E>(frag_t<D>(sV[cur], dt, st * 16, lane), pf, acc_o[dt]);
     }
     if (kt < kt1) {
       lk.store(sK[cur ^ 1]);
@@ -313,13 +308,13 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     bf16* orow = reinterpret_cast<bf16*>(a.o) + ((long)b * T + q) * C + h * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) store_acc_row(orow + dt * 32, acc_o[dt], inv, lane);
+    for (int dt = 0; dt < DT; ++dt) store_acc_row<E>(orow + dt * 32, acc_o[dt], inv, lane);
     if (lane < 32) a.lse[((long)b * H + h) * T + q] = (m + __log2f(l)) * 0.6931471805599453f;
   }
 }
 
 // ------------------------------------------------------------ dQ pass
-template <int D>
+template <int D, typename E>
 __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][RowTile<D>::ELEMS];
@@ -352,9 +347,15 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
     frags_global<D>(of, reinterpret_cast<const bf16*>(a.o) + (long)b * T * C, C, q, T, h * D, lane);
     float part = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 x = __builtin_bit_cast(uint4, df[ks]), y = __builtin_bit_cast(uint4, of[ks]);
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) part += (float)df[ks][i] * (float)of[ks][i];
+      for (int i = 0; i < 4; ++i) {
+        part += H16<E>::lo(xw[i]) * H16<E>::lo(yw[i]);
+        part += H16<E>::hi(xw[i]) * H16<E>::hi(yw[i]);
+      }
+    }
     dlt = part + __shfl_xor(part, 32, 64);
     if (qv && lane < 32) a.delta[((long)b * H + h) * T + q] = dlt;
   }
@@ -386,8 +387,8 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
       zero(dp);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sK[cur], sub * 32, ks, lane), qf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sV[cur], sub * 32, ks, lane), df[ks], dp, 0, 0, 0);
+        s = mfma32<E>(frag_r<D>(sK[cur], sub * 32, ks, lane), qf[ks], s);
+        dp = mfma32<E>(frag_r<D>(sV[cur], sub * 32, ks, lane), df[ks], dp);
       }
       float ds[16];
       const int kb = k0 + sub * 32;
@@ -405,11 +406,11 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8_t f = as_frag(pack_frag(&ds[st * 8]));
+        const bf16x8_t f = as_frag(pack_frag<E>(&ds[st * 8]));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sK[cur], dt, sub * 32 + st * 16, lane), f,
-                                                            acc[dt], 0, 0, 0);
+          acc[dt] = mfma32<E>(frag_t<D>(sK[cur], dt, sub * 32 + st * 16, lane), f,
+                                                            acc[dt]);
       }
     }
     if (kt < kt1) {
@@ -422,12 +423,12 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
     const float scale = 1.0f / sqrtf((float)D);
     bf16* row = reinterpret_cast<bf16*>(a.dqkv) + ((long)b * T + q) * ld + h * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) store_acc_row(row + dt * 32, acc[dt], scale, lane);
+    for (int dt = 0; dt < DT; ++dt) store_acc_row<E>(row + dt * 32, acc[dt], scale, lane);
   }
 }
 
 // ---------------------------------------------------------- dK / dV pass
-template <int D>
+template <int D, typename E>
 __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sQ[2][RowTile<D>::ELEMS];
@@ -496,8 +497,8 @@ __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
       zero(dp);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sQ[cur], sub * 32, ks, lane), kf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_r<D>(sdO[cur], sub * 32, ks, lane), vf[ks], dp, 0, 0, 0);
+        s = mfma32<E>(frag_r<D>(sQ[cur], sub * 32, ks, lane), kf[ks], s);
+        dp = mfma32<E>(frag_r<D>(sdO[cur], sub * 32, ks, lane), vf[ks], dp);
       }
       float p[16], ds[16];
       // rows of element e: sub*32 + acc_row(e), four consecutive rows per
@@ -530,14 +531,14 @@ __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8_t pf = as_frag(pack_frag(&p[st * 8]));
-        const bf16x8_t sf = as_frag(pack_frag(&ds[st * 8]));
+        const bf16x8_t pf = as_frag(pack_frag<E>(&p[st * 8]));
+        const bf16x8_t sf = as_frag(pack_frag<E>(&ds[st * 8]));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sdO[cur], dt, sub * 32 + st * 16, lane), pf,
-                                                           dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sQ[cur], dt, sub * 32 + st * 16, lane), sf,
-                                                           dk[dt], 0, 0, 0);
+          dv[dt] = mfma32<E>(frag_t<D>(sdO[cur], dt, sub * 32 + st * 16, lane), pf,
+                                                           dv[dt]);
+          dk[dt] = mfma32<E>(frag_t<D>(sQ[cur], dt, sub * 32 + st * 16, lane), sf,
+                                                           dk[dt]);
         }
       }
     }
@@ -553,53 +554,63 @@ __global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
     bf16* row = reinterpret_cast<bf16*>(a.dqkv) + ((long)b * T + key) * ld;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      store_acc_row(row + C + h * D + dt * 32, dk[dt], scale, lane);
-      store_acc_row(row + 2 * C + h * D + dt * 32, dv[dt], 1.0f, lane);
+      store_acc_row<E>(row + C + h * D + dt * 32, dk[dt], scale, lane);
+      store_acc_row<E>(row + 2 * C + h * D + dt * 32, dv[dt], 1.0f, lane);
     }
   }
 }
 
-template <int D>
+template <int D, typename E>
 int fwd(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.T + 127) / 128 * a.B * a.H);
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, E>), grid, dim3(256), 0, s, a);
   return 0;
 }
 
 // Backward in passes: part 0 (row dot products delta) has nothing left to do
 // here, the dQ pass (part 1) computes and stores delta for its rows before
 // the dK/dV pass (part 2) reads it.
-template <int D>
+template <int D, typename E>
 int bwd_part(const AttnArgs& a, int part, hipStream_t s) {
   dim3 grid((a.T + 127) / 128 * a.B * a.H);
   if (part == 0) {
     return 0;
   } else if (part == 1) {
-    hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_dq_kernel<D, E>), grid, dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(attn_dkv_kernel<D>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_dkv_kernel<D, E>), grid, dim3(256), 0, s, a);
   }
   return 0;
 }
 
 }  // namespace
 
-int attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
-  if (a.D == 64) return fwd<64>(a, s);
-  if (a.D == 32) return fwd<32>(a, s);
+template <typename E>
+int attn_fwd16(const AttnArgs& a, hipStream_t s) {
+  if (a.D == 64) return fwd<64, E>(a, s);
+  if (a.D == 32) return fwd<32, E>(a, s);
   return -1;
 }
 
-int attn_bwd_part_bf16(const AttnArgs& a, int part, hipStream_t s) {
-  if (a.D == 64) return bwd_part<64>(a, part, s);
-  if (a.D == 32) return bwd_part<32>(a, part, s);
+template <typename E>
+int attn_bwd_part16(const AttnArgs& a, int part, hipStream_t s) {
+  if (a.D == 64) return bwd_part<64, E>(a, part, s);
+  if (a.D == 32) return bwd_part<32, E>(a, part, s);
   return -1;
 }
 
-int attn_bwd_bf16(const AttnArgs& a, hipStream_t s) {
+template <typename E>
+int attn_bwd16(const AttnArgs& a, hipStream_t s) {
   int rc = 0;
-  for (int part = 0; part < 3; ++part) rc |= attn_bwd_part_bf16(a, part, s);
+  for (int part = 0; part < 3; ++part) rc |= attn_bwd_part16<E>(a, part, s);
   return rc;
 }
+
+template int attn_fwd16<bf16>(const AttnArgs&, hipStream_t);
+template int attn_fwd16<f16>(const AttnArgs&, hipStream_t);
+template int attn_bwd_part16<bf16>(const AttnArgs&, int, hipStream_t);
+template int attn_bwd_part16<f16>(const AttnArgs&, int, hipStream_t);
+template int attn_bwd16<bf16>(const AttnArgs&, hipStream_t);
+template int attn_bwd16<f16>(const AttnArgs&, hipStream_t);
 
 }  // namespace lm

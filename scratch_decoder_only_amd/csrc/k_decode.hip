@@ -98,6 +98,7 @@ void launch_kv_store(const E* qkv, int B, int T_, int C, int S, int t0, E* kc, E
 }
 template void launch_kv_store<float>(const float*, int, int, int, int, int, float*, float*, hipStream_t);
 template void launch_kv_store<bf16>(const bf16*, int, int, int, int, int, bf16*, bf16*, hipStream_t);
+template void launch_kv_store<f16>(const f16*, int, int, int, int, int, f16*, f16*, hipStream_t);
 
 template <typename T>
 int launch_attn_decode(const T* qkv, const T* kc, const T* vc, int B, int H, int D, int S, int n, T* o, float* sbuf,
@@ -114,5 +115,7 @@ template int launch_attn_decode<float>(const float*, const float*, const float*,
                                        float*, hipStream_t);
 template int launch_attn_decode<bf16>(const bf16*, const bf16*, const bf16*, int, int, int, int, int, bf16*, float*,
                                       hipStream_t);
+template int launch_attn_decode<f16>(const f16*, const f16*, const f16*, int, int, int, int, int, f16*, float*,
+                                     hipStream_t);
 
 }  // namespace lm

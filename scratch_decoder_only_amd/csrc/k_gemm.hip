@@ -5,11 +5,12 @@
 // Operations": matmul is the bottleneck); its CPU tiling for L1 is prior art,
 // here the contraction runs on the gfx950 matrix cores.
 //
-// bf16 path, v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
-//  * gemm_bf16_kernel: block tile BM x BN (default 128 x 128, 4 wavefronts of
-//    64 x 64, two blocks per CU), K step 64, two LDS stages fed from registers
-//    loaded two K steps ahead; LDS-staged epilogue.
-//  * gemm_bf16_pipe_kernel: persistent 256 x 256 tiles (8 wavefronts), direct
+// 16-bit path: bf16 or fp16 operands (E), v_mfma_f32_32x32x16_bf16 / _f16
+// with fp32 accumulation:
+//  * gemm16_kernel: block tile BM x BN (128 x 128, 4 wavefronts of 64 x 64,
+//    two blocks per CU), K step 64, two LDS stages fed from registers loaded
+//    two K steps ahead; LDS-staged epilogue.
+//  * gemm16_pipe_kernel: persistent 256 x 256 tiles (8 wavefronts), direct
 //    global-to-LDS loads in S stages, register epilogue; used where the
 //    operand-load path rather than the matrix core bounds the 128 x 128 tile.
 // Operands whose contiguous axis is M or N (the backward's dY^T and X^T, and W
@@ -66,21 +67,23 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, long row, long col, 
   }
 }
 
-// Epilogue of 8 consecutive output columns (bf16 path; columns col..col+7
+// Epilogue of 8 consecutive output columns (16-bit path; columns col..col+7
 // exist, leading dimensions are multiples of 8).
-__device__ __forceinline__ void ld8_bf16(const bf16* p, float* v) {
+template <typename E>
+__device__ __forceinline__ void ld8_h(const void* p, float* v) {
   const uint4 u = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    v[2 * i] = H16<E>::lo(w[i]);
+    v[2 * i + 1] = H16<E>::hi(w[i]);
   }
 }
-__device__ __forceinline__ void st8_bf16(bf16* p, const float* v) {
+template <typename E>
+__device__ __forceinline__ void st8_h(void* p, const float* v) {
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) w[i] = H16<E>::pack(v[2 * i], v[2 * i + 1]);
   *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 __device__ __forceinline__ void ld8_f32(const float* p, float* v) {
@@ -92,7 +95,7 @@ __device__ __forceinline__ void st8_f32(float* p, const float* v) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-template <int EPI, typename TC>
+template <int EPI, typename TC, typename E>
 __device__ __forceinline__ void epilogue8(const GemmArgs& p, long row, long col, float* v, int z) {
   if (EPI == EPI_PARTIAL) {
     st8_f32(reinterpret_cast<float*>(p.C) + z * p.split_stride + row * p.ldc + col, v);
@@ -106,7 +109,7 @@ __device__ __forceinline__ void epilogue8(const GemmArgs& p, long row, long col,
   }
   if (EPI == EPI_STORE) {
     if (sizeof(TC) == 4) st8_f32(reinterpret_cast<float*>(p.C) + row * p.ldc + col, v);
-    else st8_bf16(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+    else st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
   } else if (EPI == EPI_RESID) {
     float r[8];
     ld8_f32(p.R + row * p.ldr + col, r);
@@ -114,21 +117,21 @@ __device__ __forceinline__ void epilogue8(const GemmArgs& p, long row, long col,
     for (int i = 0; i < 8; ++i) v[i] += r[i];
     st8_f32(reinterpret_cast<float*>(p.C) + row * p.ldc + col, v);
   } else if (EPI == EPI_GELU) {
-    st8_bf16(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+    st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
     float a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = gelu_f(v[i]);
-    st8_bf16(reinterpret_cast<bf16*>(p.aux) + row * p.ld_aux + col, a);
+    st8_h<E>(reinterpret_cast<E*>(p.aux) + row * p.ld_aux + col, a);
   } else if (EPI == EPI_DGELU) {
     float u[8];
-    ld8_bf16(reinterpret_cast<const bf16*>(p.aux) + row * p.ld_aux + col, u);
+    ld8_h<E>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col, u);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] *= gelu_grad_f(u[i]);
-    st8_bf16(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+    st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
   }
 }
 
-// ------------------------------------------------------------ bf16 MFMA GEMM
+// ---------------------------------------------------------- 16-bit MFMA GEMM
 // Block tile BM x BN, K step 64, WGM x WGN wavefronts (wave tile WTM x WTN,
 // multiples of 32), two LDS stages; global loads of step k+1 are issued before
 // the MFMAs of step k.
@@ -250,71 +253,6 @@ struct Tile {
   }
 };
 
-// Direct global -> LDS tile loads (buffer_load_dwordx4 ... lds): lane j of a
-// wavefront writes its 16 bytes at the wave's LDS base + 16 j (checked on the
-// device), so each lane fetches the global chunk that belongs at its LDS slot
-// under the swizzles above. No VGPR staging and no ds_write; the MFMA
-// fragment reads are the same as for Tile. ROWS must be 128 or 256.
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-template <int ROWS, bool KC, int NT>
-struct DTile {
-  static_assert(ROWS == 128 || ROWS == 256, "direct tiles hold 128 or 256 rows");
-  using Base = Tile<ROWS, KC, NT>;
-  static constexpr int ELEMS = Base::ELEMS;
-  static constexpr int CHUNKS = ROWS * 8;     // 16-byte chunks per K step
-  static constexpr int NW = NT / 64;          // wavefronts
-  static constexpr int NI = CHUNKS / 64 / NW; // load instructions per wavefront per K step
-  static_assert(NI * 64 * NW == CHUNKS, "whole wavefront loads");
-  __amdgpu_buffer_rsrc_t rsrc;
-  unsigned voff[NI];
-  int kin[NI];
-  bool cok[NI];
-  unsigned kstride;
-  int wbase;  // this wavefront's first 16-byte slot
-
-  __device__ __forceinline__ void init(const bf16* g, long ld, int row0, int rows_total, int K, int tid) {
-    long origin, extent;
-    if (KC) {
-      origin = (long)row0 * ld;
-      extent = (long)(rows_total - 1 - row0) * ld + K;
-    } else {
-      origin = row0;
-      extent = (long)(K - 1) * ld + (rows_total - row0);
-    }
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(g + origin), (short)0,
-                                             (int)min(extent * 2, (long)0x7fffffff), 0x00020000);
-    kstride = KC ? 2u : (unsigned)(ld * 2);
-    const int w = tid >> 6, lane = tid & 63;
-    wbase = w * NI * 64;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int pos = wbase + i * 64 + lane;  // LDS slot this lane fills
-      if (KC) {
-        const int row = pos >> 3, kc = (pos & 7) ^ ((row >> 1) & 7);
-        voff[i] = (unsigned)(((long)row * ld + kc * 8) * 2);
-        kin[i] = kc * 8;
-        cok[i] = true;
-      } else {
-        const int k = pos / (ROWS / 8), q = (pos % (ROWS / 8)) ^ ((k & 3) << 2);
-        voff[i] = (unsigned)(((long)k * ld + q * 8) * 2);
-        kin[i] = k;
-        cok[i] = row0 + q * 8 < rows_total;
-      }
-    }
-  }
-
-  // Issue the loads of the K step at k0 into LDS stage s (asynchronous).
-  __device__ __forceinline__ void load(bf16* s, int k0, int k_end) const {
-    const unsigned ko = (unsigned)k0 * kstride;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const unsigned vo = (cok[i] && k0 + kin[i] < k_end) ? voff[i] + ko : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(s + (wbase + i * 64) * 8), 16, (int)vo, 0, 0, 0);
-    }
-  }
-};
-
 // s_waitcnt with only the vector-memory counter limited to n (n < 64).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -346,10 +284,10 @@ struct GemmOcc {
   static constexpr int value = blocks * WGM * WGN / 4 > 0 ? blocks * WGM * WGN / 4 : 1;
 };
 
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC>
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC, typename E>
 __global__ void __launch_bounds__(WGM * WGN * 64)
     __attribute__((amdgpu_waves_per_eu(GemmOcc<BM, BN, WGM, WGN>::value, GemmOcc<BM, BN, WGM, WGN>::value)))
-    gemm_bf16_kernel(GemmArgs p) {
+    gemm16_kernel(GemmArgs p) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -424,7 +362,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32<E>(af[f][i], bfr[f][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
     la.store(ra[P ^ 1], sA[P ^ 1], tid);
@@ -469,7 +407,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
         const float4 x0 = *reinterpret_cast<const float4*>(sC + r * CP + c8);
         const float4 x1 = *reinterpret_cast<const float4*>(sC + r * CP + c8 + 4);
         v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-        epilogue8<EPI, TC>(p, row, col, v, z);
+        epilogue8<EPI, TC, E>(p, row, col, v, z);
       }
     }
     __syncthreads();
@@ -543,139 +481,6 @@ __global__ void splitk_reduce_kernel(GemmArgs p, const float* __restrict__ part,
   }
 }
 
-// GEMM with direct-to-LDS tile loads and S LDS stages: the loads of K step
-// it + S - 1 are issued at the top of step it, and before the barrier that
-// ends step it only those of step it + 1 are waited for.
-template <int BM, int BN, int WGM, int WGN, int S, bool AK, bool BKC, int EPI, typename TC>
-__global__ void __launch_bounds__(WGM * WGN * 64)
-    __attribute__((amdgpu_waves_per_eu((160 * 1024) / (S * 2 * 64 * (BM + BN)) * WGM * WGN / 4 > 0
-                                           ? (160 * 1024) / (S * 2 * 64 * (BM + BN)) * WGM * WGN / 4 : 1,
-                                       (160 * 1024) / (S * 2 * 64 * (BM + BN)) * WGM * WGN / 4 > 0
-                                           ? (160 * 1024) / (S * 2 * 64 * (BM + BN)) * WGM * WGN / 4 : 1)))
-    gemm_bf16_direct_kernel(GemmArgs p) {
-  constexpr int NT = WGM * WGN * 64;
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  using TA = DTile<BM, AK, NT>;
-  using TB = DTile<BN, BKC, NT>;
-  using FA = Tile<BM, AK, NT>;
-  using FB = Tile<BN, BKC, NT>;
-  __shared__ __attribute__((aligned(16))) bf16 sA[S][TA::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sB[S][TB::ELEMS];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  int tmi, tni;
-  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tmi, tni);
-  const int m0 = tmi * BM, n0 = tni * BN;
-  const int z = blockIdx.y;
-  const int k_begin = z * p.k_split;
-  const int k_end = min(p.K, k_begin + p.k_split);
-  const int nk = (k_end - k_begin + kBK - 1) / kBK;
-  const bf16* A = reinterpret_cast<const bf16*>(p.A);
-  const bf16* B = reinterpret_cast<const bf16*>(p.B);
-
-  TA la;
-  TB lb;
-  FA fa;
-  FB fb;
-  la.init(A, p.lda, m0, p.M, p.K, tid);
-  lb.init(B, p.ldb, n0, p.N, p.K, tid);
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  // prologue: steps 0 .. S-2 in flight (clamped steps re-load the last one)
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st) {
-    const int kk = k_begin + min(st, max(nk - 1, 0)) * kBK;
-    la.load(sA[st], kk, k_end);
-    lb.load(sB[st], kk, k_end);
-  }
-  wait_vmcnt<(S - 2) * (TA::NI + TB::NI)>();
-  __syncthreads();
-
-  // Every fragment of the current stage is read before the next loads are
-  // issued: the compiler waits for all outstanding LDS-DMA loads before any
-  // later LDS read, so no LDS read may follow the loads inside an iteration.
-  bf16x8_t af[kBK / 16][TM], bfr[kBK / 16][TN];
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it % S;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[ks][i] = fa.frag(sA[cur], wm * WTM + i * 32, ks, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[ks][j] = fb.frag(sB[cur], wn * WTN + j * 32, ks, lane);
-    }
-    // phases pinned in order: fragment reads | next loads | MFMAs | wait + barrier
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      const int nxt = (it + S - 1) % S;
-      const int kk = k_begin + min(it + S - 1, nk - 1) * kBK;
-      la.load(sA[nxt], kk, k_end);
-      lb.load(sB[nxt], kk, k_end);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // the loads of step it + 1 are the oldest outstanding ones
-    wait_vmcnt<(S - 2) * (TA::NI + TB::NI)>();
-    __syncthreads();
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
-
-  // Epilogue through LDS in passes of ER = min(WTM, 64) rows per wave row.
-  constexpr int CP = BN + 4;
-  constexpr int ER = WTM < 64 ? WTM : 64;
-  constexpr int TE = ER / 32;  // MFMA row tiles per pass
-  static_assert(sizeof(sA) + sizeof(sB) >= ER * CP * 4, "epilogue tile fits in the stage buffers");
-  float* sC = reinterpret_cast<float*>(&sA[0][0]);
-#pragma unroll 1
-  for (int w = 0; w < WGM; ++w) {
-#pragma unroll
-    for (int h = 0; h < TM / TE; ++h) {
-      if (wm == w) {
-#pragma unroll
-        for (int i = 0; i < TE; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int r = i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-              const int c = wn * WTN + j * 32 + (lane & 31);
-              sC[r * CP + c] = acc[h * TE + i][j][e];
-            }
-      }
-      __syncthreads();
-      for (int c = tid; c < ER * BN / 8; c += NT) {
-        const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
-        const long row = m0 + w * WTM + h * ER + r, col = n0 + c8;
-        if (row < p.M_out && col < p.N) {
-          float v[8];
-          const float4 x0 = *reinterpret_cast<const float4*>(sC + r * CP + c8);
-          const float4 x1 = *reinterpret_cast<const float4*>(sC + r * CP + c8 + 4);
-          v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-          epilogue8<EPI, TC>(p, row, col, v, z);
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 // --------------------------------------------- persistent pipelined GEMM
 // Large tiles (256 x 256 with 8 wavefronts) cut the global-load bytes per
 // flop to what one CU's load path sustains (about 50 B/clock measured, while
@@ -691,6 +496,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
 // 16-byte stores (no LDS staging, no barrier). Blocks are persistent: each
 // walks work units (tile, K slice) with a stride of the grid, and the first
 // loads of its next unit are issued before the epilogue of the current one.
+//
+// A direct load (buffer_load_dwordx4 ... lds) from lane j of a wavefront
+// writes its 16 bytes at the wave's LDS base + 16 j (checked on the device),
+// so each lane fetches the global chunk that belongs at its LDS slot under the
+// swizzles below; no VGPR staging and no ds_write.
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int ROWS, bool KC, int NT, int BK>
 struct PTile {
@@ -802,44 +613,42 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Epilogue of 4 consecutive output columns col..col+3 of one row.
-template <int EPI, typename TC>
+template <int EPI, typename TC, typename E>
 __device__ __forceinline__ void epilogue4(const GemmArgs& p, long row, long col, f32x4_t v, int z) {
   if (EPI == EPI_PARTIAL) {
     *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + z * p.split_stride + row * p.ldc + col) = v;
     return;
   }
   if (EPI != EPI_DGELU && p.bias) v += *reinterpret_cast<const f32x4_t*>(p.bias + col);
-  auto st4 = [](bf16* d, f32x4_t x) {
-    const uint32_t w0 = (uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16);
-    const uint32_t w1 = (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16);
-    *reinterpret_cast<uint2*>(d) = make_uint2(w0, w1);
+  auto st4 = [](E* d, f32x4_t x) {
+    *reinterpret_cast<uint2*>(d) = make_uint2(H16<E>::pack(x[0], x[1]), H16<E>::pack(x[2], x[3]));
   };
   if (EPI == EPI_STORE) {
     if (sizeof(TC) == 4) *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + row * p.ldc + col) = v;
-    else st4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+    else st4(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
   } else if (EPI == EPI_RESID) {
     v += *reinterpret_cast<const f32x4_t*>(p.R + row * p.ldr + col);
     *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + row * p.ldc + col) = v;
   } else if (EPI == EPI_GELU) {
-    st4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+    st4(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
     f32x4_t a;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = gelu_f(v[i]);
-    st4(reinterpret_cast<bf16*>(p.aux) + row * p.ld_aux + col, a);
+    st4(reinterpret_cast<E*>(p.aux) + row * p.ld_aux + col, a);
   } else if (EPI == EPI_DGELU) {
-    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16*>(p.aux) + row * p.ld_aux + col);
-    v[0] *= gelu_grad_f(__uint_as_float(u.x << 16));
-    v[1] *= gelu_grad_f(__uint_as_float(u.x & 0xffff0000u));
-    v[2] *= gelu_grad_f(__uint_as_float(u.y << 16));
-    v[3] *= gelu_grad_f(__uint_as_float(u.y & 0xffff0000u));
-    st4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + col, v);
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col);
+    v[0] *= gelu_grad_f(H16<E>::lo(u.x));
+    v[1] *= gelu_grad_f(H16<E>::hi(u.x));
+    v[2] *= gelu_grad_f(H16<E>::lo(u.y));
+    v[3] *= gelu_grad_f(H16<E>::hi(u.y));
+    st4(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
   }
 }
 
 // Split-K reduction, 4 columns per thread (N a multiple of 4, leading
 // dimensions multiples of 8): sums the S partial slices in slice order, then
 // applies the real epilogue.
-template <int EPI, typename TC>
+template <int EPI, typename TC, typename E>
 __global__ void __launch_bounds__(256) splitk_reduce4_kernel(GemmArgs p, const float* __restrict__ part, int S,
                                                             long part_ld) {
   const int nq = p.N >> 2;
@@ -861,7 +670,7 @@ __global__ void __launch_bounds__(256) splitk_reduce4_kernel(GemmArgs p, const f
       acc += d;
     }
     for (; z < S; ++z) acc += *reinterpret_cast<const f32x4_t*>(src + z * slice);
-    epilogue4<EPI, TC>(p, row, col, acc, 0);
+    epilogue4<EPI, TC, E>(p, row, col, acc, 0);
   }
 }
 
@@ -887,9 +696,10 @@ __device__ __forceinline__ void pipe_tile(int u, int tiles_m, int tiles_n, int& 
   tn = in / gsize;
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int S, int OCC, bool AK, bool BKC, int EPI, typename TC>
+template <int BM, int BN, int WGM, int WGN, int BK, int S, int OCC, bool AK, bool BKC, int EPI, typename TC,
+          typename E>
 __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-    gemm_bf16_pipe_kernel(GemmArgs p, int units, int tiles_m, int tiles_n) {
+    gemm16_pipe_kernel(GemmArgs p, int units, int tiles_m, int tiles_n) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -989,7 +799,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
             for (int i = 0; i < TM; ++i)
 #pragma unroll
               for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[f][j], af[f][i], acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma32<E>(bfr[f][j], af[f][i], acc[i][j]);
             // after each MFMA: one LDS read of the next k-step, one direct
             // load and its address arithmetic
 #pragma unroll
@@ -1024,7 +834,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
           const long col = (long)tn * BN + wn * WTN + j * 32 + g * 8 + (lane >> 5) * 4;
           if (col < p.N) {
             f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            epilogue4<EPI, TC>(p, row, col, v, z);
+            epilogue4<EPI, TC, E>(p, row, col, v, z);
           }
         }
     }
@@ -1043,7 +853,7 @@ static GemmArgs make_args(const GemmOp& op) {
   return a;
 }
 
-static bool check_bf16(const GemmOp& op) {
+static bool check_16(const GemmOp& op) {
   if (op.lda % 8 || op.ldb % 8) return false;
   // 8-column epilogue chunks: N and every leading dimension of the outputs
   if (op.N % 8 || op.ldc % 8 || (op.R && op.ldr % 8) || (op.aux && op.ld_aux % 8)) return false;
@@ -1053,19 +863,15 @@ static bool check_bf16(const GemmOp& op) {
   return true;
 }
 
-// Tile configurations: 0 = 256 x 128 (4 waves of 128 x 64), 1 = 128 x 128
-// (4 waves of 64 x 64, two blocks per CU), 2 = 256 x 96 (4 waves of 64 x 96),
-// 3 = 256 x 256 (8 waves of 64 x 128, two waves per SIMD).
+// Tile configurations: 1 = gemm16_kernel 128 x 128 (4 wavefronts of 64 x 64,
+// two blocks per CU); 11 = gemm16_pipe_kernel, persistent 256 x 256 (8
+// wavefronts of 128 x 64, two per SIMD, one block per CU).
+constexpr int kCfgSmall = 1, kCfgPipe = 11;
+
 static int tiles_of(const GemmOp& op, int cfg) {
-  const int BM = (cfg == 1 || cfg == 4 || cfg == 5 || cfg == 13) ? 128 : 256;
-  const int BN = cfg == 2 ? 96 : (cfg == 3 || (cfg >= 7 && cfg != 12)) ? 256 : 128;
-  return ((op.M + BM - 1) / BM) * ((op.N + BN - 1) / BN);
+  const int T = cfg == kCfgPipe ? 256 : 128;
+  return ((op.M + T - 1) / T) * ((op.N + T - 1) / T);
 }
-
-// Blocks of a configuration resident on one CU (the persistent grid's depth).
-static int blocks_per_cu(int cfg) { return cfg == 12 || cfg == 13 ? 2 : 1; }
-
-static bool is_pipe(int cfg) { return cfg >= 9 && cfg <= 13; }
 
 // Compute units of the current device (the persistent grid's size).
 static int device_cus() {
@@ -1079,37 +885,39 @@ static int device_cus() {
   return n[d];
 }
 
+// LMSTEP_GEMM_CFG=1 or 11 forces a configuration (measurements).
 static int forced_cfg() {
   static int v = [] {
     const char* e = getenv("LMSTEP_GEMM_CFG");
-    return e ? atoi(e) : -1;
+    const int c = e ? atoi(e) : -1;
+    return c == kCfgSmall || c == kCfgPipe ? c : -1;
   }();
   return v;
 }
 
 static int pick_cfg(const GemmOp& op) {
   const int f = forced_cfg();
-  if (f >= 0 && f <= 13 && (f != 2 || op.N % 96 == 0)) return f;
+  if (f >= 0) return f;
   // Measured on the GPT-2-small-shaped step: the persistent 256 x 256 kernel
-  // (8 waves of 128 x 64) wins on the vocabulary projection's forward (very
-  // wide N) and its input gradient (very long K), and on the MLP weight
-  // gradients (3072 x 768 outputs over K = 8192); 128 x 128 at two blocks per
-  // CU wins everywhere else.
+  // wins on the vocabulary projection's forward (very wide N) and its input
+  // gradient (very long K), and on the MLP weight gradients (3072 x 768
+  // outputs over K = 8192); 128 x 128 at two blocks per CU wins everywhere
+  // else.
   const int mn_max = op.M > op.N ? op.M : op.N, mn_min = op.M < op.N ? op.M : op.N;
-  if (op.N >= 16384 || op.K >= 16384) return 11;
-  if (op.K >= 8192 && mn_max >= 3072 && mn_max <= 4096 && mn_min <= 1024) return 11;
-  return 1;
+  if (op.N >= 16384 || op.K >= 16384) return kCfgPipe;
+  if (op.K >= 8192 && mn_max >= 3072 && mn_max <= 4096 && mn_min <= 1024) return kCfgPipe;
+  return kCfgSmall;
 }
 
-int gemm_bf16_splits(const GemmOp& op) {
+int gemm16_splits(const GemmOp& op) {
   if (op.force_split > 0) return op.force_split;
   const int cfg = pick_cfg(op);
   const int tiles = tiles_of(op, cfg);
-  if (is_pipe(cfg)) {
+  if (cfg == kCfgPipe) {
     // persistent grid of one block per CU: pick the K split whose work units
     // fill the last round best (smallest split within 10% of the best fill),
     // with at least 512 K-values per slice
-    const int cus = device_cus() * blocks_per_cu(cfg);
+    const int cus = device_cus();
     auto fill = [&](int s) {
       const long u = (long)tiles * s;
       return (double)u / (double)(((u + cus - 1) / cus) * cus);
@@ -1126,175 +934,124 @@ int gemm_bf16_splits(const GemmOp& op) {
   return s;
 }
 
-template <int BM, int BN, int WGM, int WGN, int S, bool AK, bool BKC, int EPI, typename TC>
-static void launch_bf16_direct(const GemmArgs& a, int splits, hipStream_t s) {
-  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_direct_kernel<BM, BN, WGM, WGN, S, AK, BKC, EPI, TC>), dim3(tiles, splits),
-                     dim3(WGM * WGN * 64), 0, s, a);
-}
-
-template <int BM, int BN, int WGM, int WGN, int S, bool AK, bool BKC>
-static int dispatch_bf16_direct(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
-  if (splits > 1) {
-    launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_PARTIAL, float>(a, splits, s);
-    return 0;
-  }
-  switch (op.epi) {
-    case EPI_STORE:
-      if (op.c_f32) launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_STORE, float>(a, 1, s);
-      else launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_STORE, bf16>(a, 1, s);
-      return 0;
-    case EPI_RESID: launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
-    case EPI_GELU: launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
-    case EPI_DGELU: launch_bf16_direct<BM, BN, WGM, WGN, S, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
-    default: return -1;
-  }
-}
-
 // OCC: waves per SIMD the kernel is compiled for; blocks per CU = 4 OCC /
 // (WGM WGN), and the persistent grid holds that many blocks per CU.
-template <int BM, int BN, int WGM, int WGN, int BK, int S, int OCC, bool AK, bool BKC, int EPI, typename TC>
-static void launch_bf16_pipe(const GemmArgs& a, int splits, hipStream_t s) {
+template <int BM, int BN, int WGM, int WGN, int BK, int S, int OCC, bool AK, bool BKC, int EPI, typename TC,
+          typename E>
+static void launch_pipe(const GemmArgs& a, int splits, hipStream_t s) {
   const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   const int units = tiles_m * tiles_n * splits;
   constexpr int per_cu = 4 * OCC / (WGM * WGN) > 0 ? 4 * OCC / (WGM * WGN) : 1;
   int nb = device_cus() * per_cu;
   if (units < nb) nb = units;
   nb = (nb + 7) / 8 * 8;  // whole XCD rounds
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI, TC>), dim3(nb),
+  hipLaunchKernelGGL((gemm16_pipe_kernel<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI, TC, E>), dim3(nb),
                      dim3(WGM * WGN * 64), 0, s, a, units, tiles_m, tiles_n);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int S, int OCC, bool AK, bool BKC>
-static int dispatch_bf16_pipe(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
-  if (splits > 1) {
-    launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_PARTIAL, float>(a, splits, s);
-    return 0;
-  }
-  switch (op.epi) {
-    case EPI_STORE:
-      if (op.c_f32) launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_STORE, float>(a, 1, s);
-      else launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_STORE, bf16>(a, 1, s);
-      return 0;
-    case EPI_RESID: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
-    case EPI_GELU: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
-    case EPI_DGELU: launch_bf16_pipe<BM, BN, WGM, WGN, BK, S, OCC, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
-    default: return -1;
-  }
-}
-
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC>
-static void launch_bf16(const GemmArgs& a, int splits, hipStream_t s) {
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC, typename E>
+static void launch_small(const GemmArgs& a, int splits, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BKC, EPI, TC>), dim3(tiles, splits),
+  hipLaunchKernelGGL((gemm16_kernel<BM, BN, WGM, WGN, AK, BKC, EPI, TC, E>), dim3(tiles, splits),
                      dim3(WGM * WGN * 64), 0, s, a);
 }
 
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC>
-static int dispatch_bf16_cfg(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
+// One launch of configuration cfg with the epilogue EPI and output type TC.
+template <bool AK, bool BKC, int EPI, typename TC, typename E>
+static void launch_cfg(int cfg, const GemmArgs& a, int splits, hipStream_t s) {
+  if (cfg == kCfgPipe) launch_pipe<256, 256, 2, 4, 64, 2, 2, AK, BKC, EPI, TC, E>(a, splits, s);
+  else launch_small<128, 128, 2, 2, AK, BKC, EPI, TC, E>(a, splits, s);
+}
+
+template <bool AK, bool BKC, typename E>
+static int dispatch_16(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
+  const int cfg = pick_cfg(op);
   if (splits > 1) {
-    launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_PARTIAL, float>(a, splits, s);
+    launch_cfg<AK, BKC, EPI_PARTIAL, float, E>(cfg, a, splits, s);
     return 0;
   }
   switch (op.epi) {
     case EPI_STORE:
-      if (op.c_f32) launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_STORE, float>(a, 1, s);
-      else launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_STORE, bf16>(a, 1, s);
+      if (op.c_f32) launch_cfg<AK, BKC, EPI_STORE, float, E>(cfg, a, 1, s);
+      else launch_cfg<AK, BKC, EPI_STORE, E, E>(cfg, a, 1, s);
       return 0;
-    case EPI_RESID: launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_RESID, float>(a, 1, s); return 0;
-    case EPI_GELU: launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_GELU, bf16>(a, 1, s); return 0;
-    case EPI_DGELU: launch_bf16<BM, BN, WGM, WGN, AK, BKC, EPI_DGELU, bf16>(a, 1, s); return 0;
+    case EPI_RESID: launch_cfg<AK, BKC, EPI_RESID, float, E>(cfg, a, 1, s); return 0;
+    case EPI_GELU: launch_cfg<AK, BKC, EPI_GELU, E, E>(cfg, a, 1, s); return 0;
+    case EPI_DGELU: launch_cfg<AK, BKC, EPI_DGELU, E, E>(cfg, a, 1, s); return 0;
     default: return -1;
   }
 }
 
-template <bool AK, bool BKC>
-static int dispatch_bf16_epi(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
-  switch (pick_cfg(op)) {
-    case 0: return dispatch_bf16_cfg<256, 128, 2, 2, AK, BKC>(op, a, splits, s);
-    case 2: return dispatch_bf16_cfg<256, 96, 4, 1, AK, BKC>(op, a, splits, s);
-    case 3: return dispatch_bf16_cfg<256, 256, 4, 2, AK, BKC>(op, a, splits, s);
-    case 4: return dispatch_bf16_direct<128, 128, 2, 2, 2, AK, BKC>(op, a, splits, s);
-    case 5: return dispatch_bf16_direct<128, 128, 2, 2, 3, AK, BKC>(op, a, splits, s);
-    case 6: return dispatch_bf16_direct<256, 128, 2, 2, 2, AK, BKC>(op, a, splits, s);
-    case 7: return dispatch_bf16_direct<256, 256, 4, 2, 2, AK, BKC>(op, a, splits, s);
-    case 8: return dispatch_bf16_direct<256, 256, 2, 2, 2, AK, BKC>(op, a, splits, s);
-    case 9: return dispatch_bf16_pipe<256, 256, 4, 2, 64, 2, 2, AK, BKC>(op, a, splits, s);
-    case 10: return dispatch_bf16_pipe<256, 256, 4, 2, 32, 4, 2, AK, BKC>(op, a, splits, s);
-    case 11: return dispatch_bf16_pipe<256, 256, 2, 4, 64, 2, 2, AK, BKC>(op, a, splits, s);
-    case 12: return dispatch_bf16_pipe<256, 128, 4, 2, 32, 2, 4, AK, BKC>(op, a, splits, s);
-    case 13: return dispatch_bf16_pipe<128, 256, 2, 4, 32, 2, 4, AK, BKC>(op, a, splits, s);
-    default: return dispatch_bf16_cfg<128, 128, 2, 2, AK, BKC>(op, a, splits, s);
-  }
-}
-
-template <typename TA>
-static void launch_reduce(const GemmOp& op, const GemmArgs& a, const float* part, int S, hipStream_t s) {
-  long ld = op.N;
-  if (sizeof(TA) == 2) {
-    // bf16 path: N and all leading dimensions are multiples of 8
-    long total = (long)a.M_out * (op.N / 4);
-    long blocks = (total + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    dim3 g((unsigned)blocks), b(256);
-    switch (op.epi) {
-      case EPI_STORE:
-        if (op.c_f32) hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_STORE, float>), g, b, 0, s, a, part, S, ld);
-        else hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_STORE, bf16>), g, b, 0, s, a, part, S, ld);
-        break;
-      case EPI_RESID: hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_RESID, float>), g, b, 0, s, a, part, S, ld); break;
-      case EPI_GELU: hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_GELU, bf16>), g, b, 0, s, a, part, S, ld); break;
-      case EPI_DGELU: hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_DGELU, bf16>), g, b, 0, s, a, part, S, ld); break;
-      default: break;
-    }
-    return;
-  }
-  long total = (long)op.M * op.N;
+// Split-K reduction of the 16-bit path (N and all leading dimensions are
+// multiples of 8).
+template <typename E>
+static void launch_reduce16(const GemmOp& op, const GemmArgs& a, const float* part, int S, hipStream_t s) {
+  const long ld = op.N;
+  long total = (long)a.M_out * (op.N / 4);
   long blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   dim3 g((unsigned)blocks), b(256);
   switch (op.epi) {
     case EPI_STORE:
-      if (op.c_f32) hipLaunchKernelGGL((splitk_reduce_kernel<EPI_STORE, float, TA>), g, b, 0, s, a, part, S, ld);
-      else hipLaunchKernelGGL((splitk_reduce_kernel<EPI_STORE, TA, TA>), g, b, 0, s, a, part, S, ld);
+      if (op.c_f32) hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_STORE, float, E>), g, b, 0, s, a, part, S, ld);
+      else hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_STORE, E, E>), g, b, 0, s, a, part, S, ld);
       break;
-    case EPI_RESID: hipLaunchKernelGGL((splitk_reduce_kernel<EPI_RESID, float, TA>), g, b, 0, s, a, part, S, ld); break;
-    case EPI_GELU: hipLaunchKernelGGL((splitk_reduce_kernel<EPI_GELU, TA, TA>), g, b, 0, s, a, part, S, ld); break;
-    case EPI_DGELU: hipLaunchKernelGGL((splitk_reduce_kernel<EPI_DGELU, TA, TA>), g, b, 0, s, a, part, S, ld); break;
+    case EPI_RESID: hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_RESID, float, E>), g, b, 0, s, a, part, S, ld); break;
+    case EPI_GELU: hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_GELU, E, E>), g, b, 0, s, a, part, S, ld); break;
+    case EPI_DGELU: hipLaunchKernelGGL((splitk_reduce4_kernel<EPI_DGELU, E, E>), g, b, 0, s, a, part, S, ld); break;
     default: break;
   }
 }
 
-int gemm_bf16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
+// Split-K reduction of the fp32 path.
+static void launch_reduce32(const GemmOp& op, const GemmArgs& a, const float* part, int S, hipStream_t s) {
+  const long ld = op.N;
+  long total = (long)op.M * op.N;
+  long blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  dim3 g((unsigned)blocks), b(256);
+  switch (op.epi) {
+    case EPI_STORE: hipLaunchKernelGGL((splitk_reduce_kernel<EPI_STORE, float, float>), g, b, 0, s, a, part, S, ld); break;
+    case EPI_RESID: hipLaunchKernelGGL((splitk_reduce_kernel<EPI_RESID, float, float>), g, b, 0, s, a, part, S, ld); break;
+    case EPI_GELU: hipLaunchKernelGGL((splitk_reduce_kernel<EPI_GELU, float, float>), g, b, 0, s, a, part, S, ld); break;
+    case EPI_DGELU: hipLaunchKernelGGL((splitk_reduce_kernel<EPI_DGELU, float, float>), g, b, 0, s, a, part, S, ld); break;
+    default: break;
+  }
+}
+
+template <typename E>
+static int gemm16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
   if (op.M <= 0 || op.N <= 0) return 0;
-  if (!check_bf16(op)) return -1;
+  if (!check_16(op)) return -1;
   GemmArgs a = make_args(op);
-  int splits = gemm_bf16_splits(op);
+  int splits = gemm16_splits(op);
   if (splits > 1 && (long)splits * op.M * op.N > ws_floats) splits = 1;
+  // K slices are multiples of the K step (which can leave a single slice)
+  int per = op.K;
   if (splits > 1) {
-    // K slices are multiples of the K step
-    int per = (op.K + splits - 1) / splits;
+    per = (op.K + splits - 1) / splits;
     per = (per + kBK - 1) / kBK * kBK;
     splits = (op.K + per - 1) / per;
-    GemmArgs pa = a;
+  }
+  GemmArgs pa = a;
+  if (splits > 1) {
     pa.C = ws;
     pa.ldc = op.N;
     pa.k_split = per;
     pa.split_stride = (long)op.M * op.N;
-    int rc;
-    if (op.a_kc && op.b_kc) rc = dispatch_bf16_epi<true, true>(op, pa, splits, s);
-    else if (op.a_kc) rc = dispatch_bf16_epi<true, false>(op, pa, splits, s);
-    else if (!op.b_kc) rc = dispatch_bf16_epi<false, false>(op, pa, splits, s);
-    else rc = dispatch_bf16_epi<false, true>(op, pa, splits, s);
-    if (rc) return rc;
-    launch_reduce<bf16>(op, a, ws, splits, s);
-    return 0;
   }
-  if (op.a_kc && op.b_kc) return dispatch_bf16_epi<true, true>(op, a, 1, s);
-  if (op.a_kc) return dispatch_bf16_epi<true, false>(op, a, 1, s);
-  if (!op.b_kc) return dispatch_bf16_epi<false, false>(op, a, 1, s);
-  return dispatch_bf16_epi<false, true>(op, a, 1, s);
+  int rc;
+  if (op.a_kc && op.b_kc) rc = dispatch_16<true, true, E>(op, pa, splits, s);
+  else if (op.a_kc) rc = dispatch_16<true, false, E>(op, pa, splits, s);
+  else if (!op.b_kc) rc = dispatch_16<false, false, E>(op, pa, splits, s);
+  else rc = dispatch_16<false, true, E>(op, pa, splits, s);
+  if (rc) return rc;
+  if (splits > 1) launch_reduce16<E>(op, a, ws, splits, s);
+  return 0;
 }
+
+int gemm_bf16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) { return gemm16<bf16>(op, ws, ws_floats, s); }
+int gemm_f16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) { return gemm16<f16>(op, ws, ws_floats, s); }
 
 template <bool AK, bool BKC>
 static int dispatch_f32(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {
@@ -1318,10 +1075,14 @@ int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
   if (op.force_split <= 0)
     while (tiles * splits < 256 && op.K / (splits * 2) >= 256) splits *= 2;
   if (splits > 1 && (long)splits * op.M * op.N > ws_floats) splits = 1;
+  // K slices are multiples of 16 (which can leave a single slice)
+  int per = op.K;
   if (splits > 1) {
-    int per = (op.K + splits - 1) / splits;
+    per = (op.K + splits - 1) / splits;
     per = (per + 15) / 16 * 16;
     splits = (op.K + per - 1) / per;
+  }
+  if (splits > 1) {
     GemmArgs pa = a;
     pa.C = ws;
     pa.ldc = op.N;
@@ -1333,7 +1094,7 @@ int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
     else if (!op.b_kc) rc = dispatch_f32<false, false>(op, pa, splits, s);
     else rc = dispatch_f32<false, true>(op, pa, splits, s);
     if (rc) return rc;
-    launch_reduce<float>(op, a, ws, splits, s);
+    launch_reduce32(op, a, ws, splits, s);
     return 0;
   }
   if (op.a_kc && op.b_kc) return dispatch_f32<true, true>(op, a, 1, s);

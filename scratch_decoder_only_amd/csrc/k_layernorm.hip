@@ -71,6 +71,8 @@ template void launch_ln_fwd<float>(const float*, const float*, const float*, int
                                    float*, hipStream_t);
 template void launch_ln_fwd<bf16>(const float*, const float*, const float*, int, int, float, bf16*, float*,
                                   float*, hipStream_t);
+template void launch_ln_fwd<f16>(const float*, const float*, const float*, int, int, float, f16*, float*,
+                                 float*, hipStream_t);
 
 // Backward. Each block owns kLnRowsPerBlock consecutive rows; wave w takes
 // rows w, w+4, ... of them. g_out = g_in + dx (g_in may alias g_out or be
@@ -152,8 +154,8 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const float* __restrict__ d
       adc[j].x += dx0;
       adc[j].y += dx1;
       if (g_act) {
-        if (sizeof(T) == 2)  // two adjacent bf16 in one 4-byte store
-          reinterpret_cast<uint32_t*>(g_act)[(m * C + c) >> 1] = (uint32_t)f2bf(dx0) | ((uint32_t)f2bf(dx1) << 16);
+        if constexpr (sizeof(T) == 2)  // two adjacent 16-bit values in one 4-byte store
+          reinterpret_cast<uint32_t*>(g_act)[(m * C + c) >> 1] = H16<T>::pack(dx0, dx1);
         else
           reinterpret_cast<float2*>(g_act)[(m * C + c) >> 1] = make_float2(dx0, dx1);
       }
@@ -197,6 +199,8 @@ template void launch_ln_bwd<float>(const float*, const float*, const float*, con
                                    const float*, float*, float*, float*, float*, float*, hipStream_t);
 template void launch_ln_bwd<bf16>(const float*, const float*, const float*, const float*, const float*, int, int,
                                   const float*, float*, bf16*, float*, float*, float*, hipStream_t);
+template void launch_ln_bwd<f16>(const float*, const float*, const float*, const float*, const float*, int, int,
+                                 const float*, float*, f16*, float*, float*, float*, hipStream_t);
 
 // out[c] = sum over p < P of part[p][c] in a fixed order: a block covers 16
 // columns with 16 row groups; thread (c, r) sums p = r, r + 16, ... for its
@@ -266,11 +270,10 @@ template <typename T> struct Quad;
 template <> struct Quad<float> {
   static __device__ __forceinline__ float4 ld(const float* p) { return *reinterpret_cast<const float4*>(p); }
 };
-template <> struct Quad<bf16> {
-  static __device__ __forceinline__ float4 ld(const bf16* p) {
+template <typename T> struct Quad {  // 16-bit types
+  static __device__ __forceinline__ float4 ld(const T* p) {
     uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                       __uint_as_float(u.y & 0xffff0000u));
+    return make_float4(H16<T>::lo(u.x), H16<T>::hi(u.x), H16<T>::lo(u.y), H16<T>::hi(u.y));
   }
 };
 
@@ -310,10 +313,11 @@ __global__ void __launch_bounds__(256) colsum_stage1_kernel(const T* __restrict_
   }
 }
 
-// bf16 input with N and lda multiples of 8: 8 columns (one 16-byte load) per
-// thread, 512 per block; the same row order per column as above.
-__global__ void __launch_bounds__(256) colsum8_bf16_kernel(const bf16* __restrict__ a, long lda, int M, int N,
-                                                           float* __restrict__ part) {
+// 16-bit input with N and lda multiples of 8: 8 columns (one 16-byte load)
+// per thread, 512 per block; the same row order per column as above.
+template <typename T>
+__global__ void __launch_bounds__(256) colsum8_h16_kernel(const T* __restrict__ a, long lda, int M, int N,
+                                                          float* __restrict__ part) {
   __shared__ float s[4][8][64];
   const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int c = (blockIdx.x * 64 + lane) * 8;
@@ -324,8 +328,8 @@ __global__ void __launch_bounds__(256) colsum8_bf16_kernel(const bf16* __restric
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += __uint_as_float(w[i] << 16);
-      acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+      acc[2 * i] += H16<T>::lo(w[i]);
+      acc[2 * i + 1] += H16<T>::hi(w[i]);
     }
   };
   if (c < N) {
@@ -355,14 +359,18 @@ __global__ void __launch_bounds__(256) colsum8_bf16_kernel(const bf16* __restric
 template <typename T>
 void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s) {
   int P = (M + kColRows - 1) / kColRows;
-  if (sizeof(T) == 2 && N % 8 == 0 && lda % 8 == 0)
-    hipLaunchKernelGGL(colsum8_bf16_kernel, dim3((N / 8 + 63) / 64, P), dim3(256), 0, s,
-                       reinterpret_cast<const bf16*>(a), lda, M, N, part);
-  else
+  if constexpr (sizeof(T) == 2) {
+    if (N % 8 == 0 && lda % 8 == 0) {
+      hipLaunchKernelGGL(colsum8_h16_kernel<T>, dim3((N / 8 + 63) / 64, P), dim3(256), 0, s, a, lda, M, N, part);
+      launch_colsum_partials(part, nullptr, P, N, out, nullptr, s);
+      return;
+    }
+  }
     hipLaunchKernelGGL(colsum_stage1_kernel<T>, dim3((N / 4 + 63) / 64, P), dim3(256), 0, s, a, lda, M, N, part);
   launch_colsum_partials(part, nullptr, P, N, out, nullptr, s);
 }
 template void launch_colsum<float>(const float*, long, int, int, float*, float*, hipStream_t);
 template void launch_colsum<bf16>(const bf16*, long, int, int, float*, float*, hipStream_t);
+template void launch_colsum<f16>(const f16*, long, int, int, float*, float*, hipStream_t);
 
 }  // namespace lm

@@ -7,8 +7,16 @@
 // with gh = s g and a 1-based step t:
 //   m = b1 m + (1 - b1) gh;  v = b2 v + (1 - b2) gh^2
 //   p = p - lr (m / (1 - b1^t) / (sqrt(v / (1 - b2^t)) + eps) + wd p)
-// and the bf16 operand copy of p is refreshed in the same pass. A non-finite
+// and the 16-bit operand copy of p is refreshed in the same pass. A non-finite
 // norm skips the update entirely (flags bit 0).
+//
+// fp16 training scales the loss by S (a power of two) before the backward
+// (LucilleAI page: FP16 autocast with a GradScaler), so the buffer holds S g:
+// the norm is taken of S g and divided by S, the clip factor comes from the
+// true norm, and AdamW multiplies by (clip factor) / S. The scale then
+// follows the usual dynamic rule: a non-finite norm (an overflow somewhere)
+// skips the step and multiplies S by the backoff factor; after `interval`
+// finite steps in a row S is multiplied by the growth factor.
 #include "kernels.h"
 
 namespace lm {
@@ -39,7 +47,8 @@ void launch_sumsq_partials(const float* g, long n, double* part, hipStream_t s) 
 
 __global__ void __launch_bounds__(256) norm_finalize_kernel(const double* __restrict__ part, float clip,
                                                             float* __restrict__ norm_scale,
-                                                            uint32_t* __restrict__ flags, float* __restrict__ stats) {
+                                                            uint32_t* __restrict__ flags, float* __restrict__ stats,
+                                                            LossScaler ls) {
   __shared__ double s[256];
   double acc = 0.0;
   for (int i = threadIdx.x; i < kNormBlocks; i += 256) acc += part[i];
@@ -50,19 +59,31 @@ __global__ void __launch_bounds__(256) norm_finalize_kernel(const double* __rest
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    double n = sqrt(s[0]);
+    const double S = ls.state ? (double)ls.state[0] : 1.0;
+    double n = sqrt(s[0]) / S;
     bool finite = isfinite(n);
     double sc = (finite && clip > 0.f && n > (double)clip) ? (double)clip / n : 1.0;
     norm_scale[0] = (float)n;
-    norm_scale[1] = (float)sc;
+    norm_scale[1] = (float)(sc / S);
     if (!finite) atomicOr(flags, 1u);
     if (stats) stats[1] = (float)n;
+    if (ls.state) {
+      if (!finite) {
+        ls.state[0] = (float)(S * (double)ls.backoff);
+        ls.state[1] = 0.f;
+      } else if (ls.state[1] + 1.f >= (float)ls.interval) {
+        ls.state[0] = (float)(S * (double)ls.growth);
+        ls.state[1] = 0.f;
+      } else {
+        ls.state[1] += 1.f;
+      }
+    }
   }
 }
 
 void launch_norm_finalize(const double* part, float clip, float* norm_scale, uint32_t* flags, float* stats,
-                          hipStream_t s) {
-  hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(256), 0, s, part, clip, norm_scale, flags, stats);
+                          LossScaler ls, hipStream_t s) {
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(256), 0, s, part, clip, norm_scale, flags, stats, ls);
 }
 
 // rb1, rb2: 1 / (1 - beta^t), computed once per thread; the per-element
@@ -94,12 +115,9 @@ __global__ void __launch_bounds__(256) adamw_kernel(AdamArgs a) {
     reinterpret_cast<float4*>(a.m)[i] = m;
     reinterpret_cast<float4*>(a.v)[i] = v;
     if (a.shadow) {
-      long e = i * 4;
-      long o = e < a.shadow_split ? e : e + a.shadow_shift;
-      uint2 w;
-      w.x = (uint32_t)f2bf(p.x) | ((uint32_t)f2bf(p.y) << 16);
-      w.y = (uint32_t)f2bf(p.z) | ((uint32_t)f2bf(p.w) << 16);
-      *reinterpret_cast<uint2*>(a.shadow + o) = w;
+      const uint2 w = a.shadow_f16 ? make_uint2(H16<f16>::pack(p.x, p.y), H16<f16>::pack(p.z, p.w))
+                                   : make_uint2(H16<bf16>::pack(p.x, p.y), H16<bf16>::pack(p.z, p.w));
+      *reinterpret_cast<uint2*>(a.shadow + i * 4) = w;
     }
   }
 }
@@ -112,18 +130,15 @@ void launch_adamw(const AdamArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
 }
 
-__global__ void make_shadow_kernel(const float* __restrict__ p, long n, bf16* __restrict__ shadow, long split,
-                                   long shift) {
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
-    long o = i < split ? i : i + shift;
-    shadow[o] = f2bf(p[i]);
-  }
+__global__ void make_shadow_kernel(const float* __restrict__ p, long n, uint16_t* __restrict__ shadow, int to_f16) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
+    shadow[i] = (uint16_t)(to_f16 ? H16<f16>::bits(p[i]) : H16<bf16>::bits(p[i]));
 }
 
-void launch_make_shadow(const float* p, long n, bf16* shadow, long split, long shift, hipStream_t s) {
+void launch_make_shadow(const float* p, long n, uint16_t* shadow, bool to_f16, hipStream_t s) {
   long blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(make_shadow_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, shadow, split, shift);
+  hipLaunchKernelGGL(make_shadow_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, shadow, to_f16 ? 1 : 0);
 }
 
 }  // namespace lm

@@ -179,12 +179,15 @@ __global__ void convert_kernel(const float* __restrict__ src, T* __restrict__ ds
   for (; i < n; i += stride) Act<T>::st(dst, i, src[i]);
 }
 
-void launch_f32_to_bf16(const float* src, bf16* dst, long n, hipStream_t s) {
+template <typename T>
+void launch_f32_to(const float* src, T* dst, long n, hipStream_t s) {
   if (n <= 0) return;
   long blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(convert_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  hipLaunchKernelGGL(convert_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
 }
+template void launch_f32_to<bf16>(const float*, bf16*, long, hipStream_t);
+template void launch_f32_to<f16>(const float*, f16*, long, hipStream_t);
 
 // Logits of the forward-only call: act [M, ldz] -> fp32 [M, V].
 template <typename T>
@@ -202,5 +205,6 @@ void launch_logits_out(const T* z, long ldz, int M, int V, float* out, hipStream
 }
 template void launch_logits_out<float>(const float*, long, int, int, float*, hipStream_t);
 template void launch_logits_out<bf16>(const bf16*, long, int, int, float*, hipStream_t);
+template void launch_logits_out<f16>(const f16*, long, int, int, float*, hipStream_t);
 
 }  // namespace lm

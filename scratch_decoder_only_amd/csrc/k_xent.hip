@@ -2,7 +2,10 @@
 //
 // Over the valid rows (target >= 0, N of them): row loss = logsumexp(z) -
 // z[target]; dz = (softmax(z) - onehot(target)) / N, written over z in place;
-// rows with target -1 get dz = 0; padding columns V..ldz-1 are zeroed.
+// rows with target -1 get dz = 0; padding columns V..ldz-1 are zeroed. With
+// a loss scale S (fp16 training), dz is multiplied by S: the gradient of S
+// times the loss, so that small gradients stay above fp16's underflow; the
+// reported loss is not scaled.
 // (Cross-entropy loss: RustGPT page, technical-implementation list; the V
 // outputs form a distribution summing to 1: Smallem page, "Ce qu'est un modele
 // de langage".)
@@ -12,22 +15,21 @@
 
 namespace lm {
 
-template <typename T> struct Vec16;
-template <> struct Vec16<bf16> {
+template <typename T> struct Vec16 {  // 16-bit types (bf16, f16)
   static constexpr int N = 8;
-  static __device__ __forceinline__ void load(const bf16* p, float* out) {
+  static __device__ __forceinline__ void load(const T* p, float* out) {
     uint4 u = *reinterpret_cast<const uint4*>(p);
     uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(w[i] << 16);
-      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      out[2 * i] = H16<T>::lo(w[i]);
+      out[2 * i + 1] = H16<T>::hi(w[i]);
     }
   }
-  static __device__ __forceinline__ void store(bf16* p, const float* v) {
+  static __device__ __forceinline__ void store(T* p, const float* v) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = H16<T>::pack(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
@@ -53,6 +55,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) xent_kernel(T* __restrict__ z, long ldz, int V,
                                                    const int32_t* __restrict__ tgt,
                                                    const int32_t* __restrict__ n_valid,
+                                                   const float* __restrict__ loss_scale,
                                                    float* __restrict__ row_loss) {
   constexpr int NV = Vec16<T>::N;
   constexpr int U = 4;  // vectors in flight per thread
@@ -110,7 +113,7 @@ __global__ void __launch_bounds__(256) xent_kernel(T* __restrict__ z, long ldz, 
   __syncthreads();  // z[t] has been read before it is overwritten
   const float lse = s_lse;
   const int n = *n_valid;
-  const float inv_n = n > 0 ? 1.0f / (float)n : 0.f;
+  const float inv_n = (n > 0 ? 1.0f / (float)n : 0.f) * (loss_scale ? *loss_scale : 1.0f);
   for (int v0 = threadIdx.x; v0 < nvec; v0 += 256 * U) {
     float x[U][NV];
 #pragma unroll
@@ -142,6 +145,7 @@ template <typename T, int NCH>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) xent_reg_kernel(T* __restrict__ z, long ldz, int V,
                                                         const int32_t* __restrict__ tgt,
                                                         const int32_t* __restrict__ n_valid,
+                                                        const float* __restrict__ loss_scale,
                                                         float* __restrict__ row_loss) {
   constexpr int NV = Vec16<T>::N;
   __shared__ float s_m[16], s_s[16];
@@ -202,7 +206,7 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
   __syncthreads();  // z[t] has been read before it is overwritten
   const float lse = s_lse;
   const int n = *n_valid;
-  const float inv_n = n > 0 ? 1.0f / (float)n : 0.f;
+  const float inv_n = (n > 0 ? 1.0f / (float)n : 0.f) * (loss_scale ? *loss_scale : 1.0f);
 #pragma unroll
   for (int q = 0; q < NCH; ++q) {
     const int v = threadIdx.x + q * 1024;
@@ -222,19 +226,24 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
 
 template <typename T>
 void launch_xent(T* z, long ldz, int M, int V, const int32_t* tgt, const int32_t* n_valid, float* row_loss,
-                 hipStream_t s) {
+                 const float* loss_scale, hipStream_t s) {
   const long nvec = ldz / Vec16<T>::N;
   const long nch = (nvec + 1023) / 1024;
 #define XENT_REG(N)                                                                                        \
   if (nch <= N) {                                                                                          \
-    hipLaunchKernelGGL((xent_reg_kernel<T, N>), dim3(M), dim3(1024), 0, s, z, ldz, V, tgt, n_valid, row_loss); \
+    hipLaunchKernelGGL((xent_reg_kernel<T, N>), dim3(M), dim3(1024), 0, s, z, ldz, V, tgt, n_valid, loss_scale, \
+                       row_loss);                                                                                \
     return;                                                                                                \
   }
   XENT_REG(1) XENT_REG(2) XENT_REG(4) XENT_REG(8)
 #undef XENT_REG
-  hipLaunchKernelGGL(xent_kernel<T>, dim3(M), dim3(256), 0, s, z, ldz, V, tgt, n_valid, row_loss);
+  hipLaunchKernelGGL(xent_kernel<T>, dim3(M), dim3(256), 0, s, z, ldz, V, tgt, n_valid, loss_scale, row_loss);
 }
-template void launch_xent<float>(float*, long, int, int, const int32_t*, const int32_t*, float*, hipStream_t);
-template void launch_xent<bf16>(bf16*, long, int, int, const int32_t*, const int32_t*, float*, hipStream_t);
+template void launch_xent<float>(float*, long, int, int, const int32_t*, const int32_t*, float*, const float*,
+                                 hipStream_t);
+template void launch_xent<bf16>(bf16*, long, int, int, const int32_t*, const int32_t*, float*, const float*,
+                                hipStream_t);
+template void launch_xent<f16>(f16*, long, int, int, const int32_t*, const int32_t*, float*, const float*,
+                               hipStream_t);
 
 }  // namespace lm

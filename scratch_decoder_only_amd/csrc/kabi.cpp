@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "../../include/lmstep_kernels.h"
 #include "kernels.h"
@@ -9,6 +10,19 @@
 using namespace lm;
 
 static hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// precision: 0 fp32, 1 bf16, 2 fp16 (the activation / operand storage type);
+// f gets a null pointer of that type as a tag. Other values: -1.
+template <typename F>
+static int with_prec(int precision, F&& f) {
+  switch (precision) {
+    case 0: return f(static_cast<float*>(nullptr));
+    case 1: return f(static_cast<bf16*>(nullptr));
+    case 2: return f(static_cast<f16*>(nullptr));
+    default: return -1;
+  }
+}
+#define ACT_T std::remove_pointer_t<decltype(tag)>
 
 extern "C" {
 
@@ -25,7 +39,10 @@ int lmk_gemm(int precision, int M, int N, int K, const void* A, int64_t lda, int
   op.force_split = force_split; op.M_out = M_out;
   if (epi == EPI_RESID && !R) return -1;
   if ((epi == EPI_GELU || epi == EPI_DGELU) && !aux) return -1;
-  return precision ? gemm_bf16(op, ws, ws_floats, S(stream)) : gemm_f32(op, ws, ws_floats, S(stream));
+  if (precision == 2) return gemm_f16(op, ws, ws_floats, S(stream));
+  if (precision == 1) return gemm_bf16(op, ws, ws_floats, S(stream));
+  if (precision == 0) return gemm_f32(op, ws, ws_floats, S(stream));
+  return -1;
 }
 
 static bool ln_shape_ok(int M, int C) { return M >= 0 && C >= 128 && C <= 1024 && C % 128 == 0; }
@@ -33,9 +50,10 @@ static bool ln_shape_ok(int M, int C) { return M >= 0 && C >= 128 && C <= 1024 &
 int lmk_layernorm_fwd(int precision, const float* x, const float* g, const float* b, int M, int C, float eps, void* y,
                       float* mu, float* rstd, void* stream) {
   if (!ln_shape_ok(M, C)) return -1;
-  if (precision) launch_ln_fwd<bf16>(x, g, b, M, C, eps, reinterpret_cast<bf16*>(y), mu, rstd, S(stream));
-  else launch_ln_fwd<float>(x, g, b, M, C, eps, reinterpret_cast<float*>(y), mu, rstd, S(stream));
-  return 0;
+  return with_prec(precision, [&](auto tag) {
+    launch_ln_fwd<ACT_T>(x, g, b, M, C, eps, reinterpret_cast<ACT_T*>(y), mu, rstd, S(stream));
+    return 0;
+  });
 }
 
 int64_t lmk_layernorm_bwd_ws_floats(int M, int C) {
@@ -48,12 +66,12 @@ int lmk_layernorm_bwd(int precision, const float* dy, const float* x, const floa
   if (!ln_shape_ok(M, C) || M == 0) return -1;
   long nb = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
   float* pc = dsum ? ws + 2 * nb * C : nullptr;
-  if (precision)
-    launch_ln_bwd<bf16>(dy, x, mu, rstd, g, M, C, g_in, g_out, reinterpret_cast<bf16*>(g_act), ws, ws + nb * C, pc,
-                        S(stream));
-  else
-    launch_ln_bwd<float>(dy, x, mu, rstd, g, M, C, g_in, g_out, reinterpret_cast<float*>(g_act), ws, ws + nb * C,
+  const int rc = with_prec(precision, [&](auto tag) {
+    launch_ln_bwd<ACT_T>(dy, x, mu, rstd, g, M, C, g_in, g_out, reinterpret_cast<ACT_T*>(g_act), ws, ws + nb * C,
                          pc, S(stream));
+    return 0;
+  });
+  if (rc) return rc;
   launch_colsum_partials(ws, ws + nb * C, (int)nb, C, dgamma, dbeta, S(stream), pc, dsum);
   return 0;
 }
@@ -62,9 +80,10 @@ int64_t lmk_colsum_ws_floats(int M, int N) { return (int64_t)((M + kColRows - 1)
 
 int lmk_colsum(int precision_of_a, const void* a, int64_t lda, int M, int N, float* out, float* ws, void* stream) {
   if (M <= 0 || N <= 0 || N % 4 || lda % 4) return -1;
-  if (precision_of_a) launch_colsum<bf16>(reinterpret_cast<const bf16*>(a), lda, M, N, ws, out, S(stream));
-  else launch_colsum<float>(reinterpret_cast<const float*>(a), lda, M, N, ws, out, S(stream));
-  return 0;
+  return with_prec(precision_of_a, [&](auto tag) {
+    launch_colsum<ACT_T>(reinterpret_cast<const ACT_T*>(a), lda, M, N, ws, out, S(stream));
+    return 0;
+  });
 }
 
 int lmk_index_layout(const int32_t* doc, int B, int T, int32_t* start, int32_t* end, int32_t* pos, uint32_t* flags,
@@ -86,7 +105,10 @@ int lmk_attn_fwd(int precision, const void* qkv, const int32_t* start, const int
   if (B <= 0 || T <= 0 || H <= 0 || (D != 32 && D != 64)) return -1;
   AttnArgs a{};
   a.qkv = qkv; a.start = start; a.end = end; a.B = B; a.T = T; a.H = H; a.D = D; a.o = o; a.lse = lse;
-  return precision ? attn_fwd_bf16(a, S(stream)) : attn_fwd_f32(a, S(stream));
+  return with_prec(precision, [&](auto tag) {
+    if constexpr (std::is_same_v<ACT_T, float>) return attn_fwd_f32(a, S(stream));
+    else return attn_fwd16<ACT_T>(a, S(stream));
+  });
 }
 
 int lmk_attn_bwd(int precision, const void* qkv, const void* o, const float* lse, const void* dout,
@@ -96,15 +118,20 @@ int lmk_attn_bwd(int precision, const void* qkv, const void* o, const float* lse
   AttnArgs a{};
   a.qkv = qkv; a.start = start; a.end = end; a.B = B; a.T = T; a.H = H; a.D = D;
   a.o = const_cast<void*>(o); a.lse = const_cast<float*>(lse); a.dout = dout; a.delta = delta; a.dqkv = dqkv;
-  return precision ? attn_bwd_bf16(a, S(stream)) : attn_bwd_f32(a, S(stream));
+  return with_prec(precision, [&](auto tag) {
+    if constexpr (std::is_same_v<ACT_T, float>) return attn_bwd_f32(a, S(stream));
+    else return attn_bwd16<ACT_T>(a, S(stream));
+  });
 }
 
 int lmk_xent(int precision, void* z, int64_t ldz, int M, int V, const int32_t* tgt, float* loss, int32_t* ws_n,
-             float* ws_rows, uint32_t* flags, void* stream) {
-  if (M <= 0 || V <= 0 || ldz < V || ldz % 8) return -1;
+             float* ws_rows, uint32_t* flags, const float* loss_scale, void* stream) {
+  if (M <= 0 || V <= 0 || ldz < V || ldz % 8 || precision < 0 || precision > 2) return -1;
   launch_count_valid(tgt, M, V, ws_n, loss, flags, S(stream));
-  if (precision) launch_xent<bf16>(reinterpret_cast<bf16*>(z), ldz, M, V, tgt, ws_n, ws_rows, S(stream));
-  else launch_xent<float>(reinterpret_cast<float*>(z), ldz, M, V, tgt, ws_n, ws_rows, S(stream));
+  with_prec(precision, [&](auto tag) {
+    launch_xent<ACT_T>(reinterpret_cast<ACT_T*>(z), ldz, M, V, tgt, ws_n, ws_rows, loss_scale, S(stream));
+    return 0;
+  });
   launch_loss_reduce(ws_rows, M, ws_n, loss, S(stream));
   return 0;
 }
@@ -128,25 +155,32 @@ int lmk_segment_sum(const float* dx, int M, int C, int nkeys, int32_t* counts, i
 }
 
 int lmk_grad_norm(const float* g, int64_t n, float clip, double* part, float* norm_scale, uint32_t* flags,
-                  void* stream) {
-  if (n < 0) return -1;
+                  float* scale_state, float growth, float backoff, int interval, void* stream) {
+  if (n < 0 || (scale_state && (interval < 1 || !(growth >= 1.f) || !(backoff > 0.f)))) return -1;
+  LossScaler ls;
+  ls.state = scale_state;
+  ls.growth = growth;
+  ls.backoff = backoff;
+  ls.interval = interval;
   launch_sumsq_partials(g, n, part, S(stream));
-  launch_norm_finalize(part, clip, norm_scale, flags, nullptr, S(stream));
+  launch_norm_finalize(part, clip, norm_scale, flags, nullptr, ls, S(stream));
   return 0;
 }
 
 int lmk_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float beta1, float beta2, float eps,
               float weight_decay, int step, const float* norm_scale, const uint32_t* flags, uint16_t* shadow,
-              void* stream) {
+              int shadow_f16, void* stream) {
   if (n < 0 || n % 4 || step < 1) return -1;
   AdamArgs a{};
   a.p = p; a.g = g; a.m = m; a.v = v; a.n = n;
   a.lr = lr; a.beta1 = beta1; a.beta2 = beta2; a.eps = eps; a.wd = weight_decay;
   a.bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
   a.bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
-  a.norm_scale = norm_scale; a.flags = flags; a.shadow = shadow; a.shadow_split = n; a.shadow_shift = 0;
+  a.norm_scale = norm_scale; a.flags = flags; a.shadow = shadow; a.shadow_f16 = shadow_f16 != 0;
   launch_adamw(a, S(stream));
   return 0;
 }
 
 }  // extern "C"
+
+#undef ACT_T

@@ -48,9 +48,10 @@ struct GemmOp {
 // rules (leading dims and K-contiguous K multiples of 8, M/N multiples of 8
 // for the non-K-contiguous operands).
 int gemm_bf16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
+int gemm_f16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
 int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
-// Split count the bf16 dispatcher would pick (for workspace sizing).
-int gemm_bf16_splits(const GemmOp& op);
+// Split count the 16-bit dispatcher would pick (for workspace sizing).
+int gemm16_splits(const GemmOp& op);
 
 // -------------------------------------------------------------- rows etc.
 void launch_fill_u32(uint32_t* p, uint32_t v, long n, hipStream_t s);
@@ -62,7 +63,8 @@ void launch_count_valid(const int32_t* tgt, int M, int V, int32_t* n_out, float*
                         hipStream_t s);
 void launch_loss_reduce(const float* row_loss, int M, const int32_t* n_valid, float* out, hipStream_t s);
 void launch_write_flags(const uint32_t* flags, float* stats, hipStream_t s);
-void launch_f32_to_bf16(const float* src, bf16* dst, long n, hipStream_t s);
+template <typename T>
+void launch_f32_to(const float* src, T* dst, long n, hipStream_t s);
 template <typename T>
 void launch_logits_out(const T* z, long ldz, int M, int V, float* out, hipStream_t s);
 
@@ -78,9 +80,10 @@ void launch_colsum_partials(const float* pa, const float* pb, int P, int C, floa
 template <typename T>
 void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s);
 
+// loss_scale (nullable, device): dz is multiplied by *loss_scale.
 template <typename T>
 void launch_xent(T* z, long ldz, int M, int V, const int32_t* tgt, const int32_t* n_valid, float* row_loss,
-                 hipStream_t s);
+                 const float* loss_scale, hipStream_t s);
 
 // -------------------------------------------------------------- attention
 // qkv [B*T, 3C] (q | k | v, head h in columns h*D..h*D+D-1 of each third),
@@ -97,13 +100,18 @@ struct AttnArgs {
   float* delta;      // [B, H, T] rowsum(dO * O)
   void* dqkv;        // [B*T, 3C]
 };
-int attn_fwd_bf16(const AttnArgs& a, hipStream_t s);
+// E: bf16 or f16 operands (matrix cores); the fp32 path has its own kernels.
+template <typename E>
+int attn_fwd16(const AttnArgs& a, hipStream_t s);
 int attn_fwd_f32(const AttnArgs& a, hipStream_t s);
 // Backward in three launches: delta = rowsum(dO * O), the dQ pass, the dK/dV
-// pass (part 0, 1, 2); attn_bwd_* runs all three.
-int attn_bwd_part_bf16(const AttnArgs& a, int part, hipStream_t s);
+// pass (part 0, 1, 2); attn_bwd* runs all three. The 16-bit dQ pass computes
+// delta itself (part 0 launches nothing there).
+template <typename E>
+int attn_bwd_part16(const AttnArgs& a, int part, hipStream_t s);
 int attn_bwd_part_f32(const AttnArgs& a, int part, hipStream_t s);
-int attn_bwd_bf16(const AttnArgs& a, hipStream_t s);
+template <typename E>
+int attn_bwd16(const AttnArgs& a, hipStream_t s);
 int attn_bwd_f32(const AttnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------ embedding backward
@@ -131,10 +139,19 @@ long embed_bwd_max_chunks(int M, int nkeys);
 // --------------------------------------------------------------- optimiser
 constexpr int kNormBlocks = 1024;
 void launch_sumsq_partials(const float* g, long n, double* part, hipStream_t s);
-// Final norm: stats[1] = n; scale = clip/n if n > clip > 0 else 1; sets flags
-// bit 0 if n is not finite.
+// Dynamic loss scale of fp16 training: state[0] = S, state[1] = finite steps
+// in a row (device memory, updated by launch_norm_finalize); state = nullptr
+// means no scaling.
+struct LossScaler {
+  float* state = nullptr;
+  float growth = 2.f, backoff = 0.5f;
+  int interval = 2000;
+};
+// Final norm: the partial sums are of (S g)^2; n = sqrt(sum) / S, stats[1] =
+// n; clip factor c = clip/n if n > clip > 0 else 1; norm_scale = [n, c / S];
+// sets flags bit 0 if n is not finite; then updates the loss scale.
 void launch_norm_finalize(const double* part, float clip, float* norm_scale, uint32_t* flags, float* stats,
-                          hipStream_t s);
+                          LossScaler ls, hipStream_t s);
 struct AdamArgs {
   float* p;
   const float* g;
@@ -145,12 +162,11 @@ struct AdamArgs {
   float bc1, bc2;  // 1 - beta1^t, 1 - beta2^t
   const float* norm_scale;  // [norm, scale]
   const uint32_t* flags;
-  bf16* shadow;      // bf16 copy (nullable)
-  long shadow_split; // elements < split map to shadow[i]; others to shadow[i + shadow_shift]
-  long shadow_shift;
+  uint16_t* shadow;  // 16-bit copy of p at the same offsets (nullable)
+  int shadow_f16;    // the copy is fp16 (else bf16)
 };
 void launch_adamw(const AdamArgs& a, hipStream_t s);
-void launch_make_shadow(const float* p, long n, bf16* shadow, long split, long shift, hipStream_t s);
+void launch_make_shadow(const float* p, long n, uint16_t* shadow, bool to_f16, hipStream_t s);
 
 // ------------------------------------------------------------- generation
 // Key/value cache (per layer K [B][S][C] then V [B][S][C]): rows t0 .. t0+T-1

@@ -37,7 +37,7 @@ class ModelShape:
     max_seq: int
     batch: int
     seq: int
-    precision: str  # "fp32" or "bf16" (bf16 compute, fp32 master weights)
+    precision: str  # "fp32", "bf16" or "fp16" (16-bit compute, fp32 master weights; fp16 with loss scaling)
     # token-id distribution: ("uniform", 0.0) or ("zipf", s)
     ids: Tuple[str, float]
     # packing: None, ("uniform", lo, hi) or ("loguniform", lo, hi) document lengths

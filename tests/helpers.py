@@ -25,10 +25,23 @@ def bf16_exact(a):
     return t.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(t.bfloat16).to(t.float32).numpy()
 
 
-def act(a, precision):
-    """Activation tensor on the device: bf16 (precision 1) or fp32 (0)."""
+def act_dtype(precision):
+    """Storage type of activations: fp32 (precision 0), bf16 (1), fp16 (2)."""
     t = torch()
-    return dev(np.asarray(a, np.float32), t.bfloat16 if precision else t.float32)
+    return {0: t.float32, 1: t.bfloat16, 2: t.float16}[precision]
+
+
+def exact(a, precision):
+    """a rounded (RNE) to the activation type of `precision`, as float32, so
+    the oracle sees exactly the operand values the kernels read."""
+    t = torch()
+    x = t.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return x.to(act_dtype(precision)).to(t.float32).numpy()
+
+
+def act(a, precision):
+    """Activation tensor on the device in the type of `precision`."""
+    return dev(np.asarray(a, np.float32), act_dtype(precision))
 
 
 def host(x):

@@ -58,7 +58,7 @@ def _cfg(**kw):
 
 
 @pytest.mark.parametrize("bad", [dict(d_model=96), dict(n_heads=3), dict(n_heads=1), dict(d_mlp=100),
-                                 dict(vocab=0), dict(max_seq=0), dict(precision=2), dict(d_model=2048, n_heads=32),
+                                 dict(vocab=0), dict(max_seq=0), dict(precision=3), dict(d_model=2048, n_heads=32),
                                  dict(untied_head=2)])
 def test_invalid_configs_are_rejected(lib, bad):
     import scratch_decoder_only_amd as sd
@@ -82,6 +82,7 @@ def test_workspace_size_and_arena_checks(lib):
     assert sd.lib.model_create(ctypes.byref(cfg), ctypes.c_void_p(258), need, None, ctypes.byref(h)) == sd.LM_ERR_WORKSPACE
     bf = _cfg(precision=1)
     assert sd.lib.lm_workspace_bytes(ctypes.byref(bf)) > 0
+    assert sd.lib.lm_workspace_bytes(ctypes.byref(_cfg(precision=2))) == sd.lib.lm_workspace_bytes(ctypes.byref(bf))
     # a separate head adds head.w [V, C] and head.b [V] to each of the four
     # fp32 buffers
     un = _cfg(untied_head=1)
@@ -98,5 +99,5 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
     # attention head dim 48 is not supported
     assert sd.lib.lmk_attn_fwd(1, P, P, P, 1, 8, 2, 48, P, P, None) != 0
     # AdamW needs a multiple of 4 elements and step >= 1
-    assert sd.lib.lmk_adamw(P, P, P, P, 6, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, P, P, None, None) != 0
-    assert sd.lib.lmk_adamw(P, P, P, P, 8, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0, P, P, None, None) != 0
+    assert sd.lib.lmk_adamw(P, P, P, P, 6, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, P, P, None, 0, None) != 0
+    assert sd.lib.lmk_adamw(P, P, P, P, 8, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0, P, P, None, 0, None) != 0

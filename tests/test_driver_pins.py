@@ -7,6 +7,7 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -106,3 +107,33 @@ def test_top_1_is_greedy_and_top_k_drops_the_rest():
 def test_low_temperature_approaches_greedy():
     z = [0.0, 1.0, 0.99, -2.0]
     assert oracle.next_token(z, 1e-3, 0, 0.5) == 1
+
+
+# ------------------------------------------------------ dynamic loss scale
+
+def test_loss_scale_rule_matches_torch_update_op():
+    """The scaler's rule against torch's own loss-scale update operator (a
+    library routine written independently), on a random finite / overflow
+    sequence with a short interval and with the default one."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    for interval, growth, backoff in [(3, 2.0, 0.5), (2000, 2.0, 0.5), (5, 4.0, 0.25)]:
+        flags = rng.random(400) < 0.93
+        got = oracle.loss_scale_trace(65536.0, flags, growth, backoff, interval)
+        s = torch.tensor([65536.0])
+        g = torch.tensor([0], dtype=torch.int32)
+        f = torch.tensor([0.0])
+        for i, fin in enumerate(flags):
+            f.fill_(0.0 if fin else 1.0)
+            torch._amp_update_scale_(s, g, f, growth, backoff, interval)
+            assert got[i] == (s.item(), g.item()), (interval, i)
+
+
+def test_loss_scale_closed_forms():
+    """k finite steps from a fresh run multiply S by growth^(k // interval);
+    each overflow divides it by 1/backoff and restarts the run."""
+    tr = oracle.loss_scale_trace(1024.0, [True] * 10, interval=3)
+    assert [s for s, _ in tr] == [1024, 1024, 2048, 2048, 2048, 4096, 4096, 4096, 8192, 8192]
+    assert [g for _, g in tr] == [1, 2, 0, 1, 2, 0, 1, 2, 0, 1]
+    tr = oracle.loss_scale_trace(1024.0, [True, True, False, False, True], interval=3)
+    assert tr == [(1024, 1), (1024, 2), (512, 0), (256, 0), (256, 1)]

@@ -74,24 +74,38 @@ def test_scheduled_steps_match_oracle(sd):
         v0 = {k: a.astype(np.float64) for k, a in got["v"].items()}
 
 
-@pytest.mark.parametrize("name", ["C1", "C2"])
+@pytest.mark.parametrize("name", ["C1", "C2", "C2-fp16"])
 def test_checkpoint_resume_is_bit_exact(sd, name, tmp_path):
+    """fp16: the checkpoint also carries the loss scale and its run of finite
+    steps (interval 2 here, so both change during the run)."""
     t = torch()
-    shape = synth.SHAPES[name]
+    fp16 = name.endswith("fp16")
+    shape = synth.SHAPES[name.split("-")[0]]
+    if fp16:
+        shape = shape.replace(precision="fp16")
     b = synth.make_batch(shape)
     batch = (dev(b.tokens), dev(b.targets), None)
     kw = dict(lr_max=shape.lr, lr_min=shape.lr / 10, warmup_steps=2, total_steps=6, **_opt(shape))
     path = str(tmp_path / "ck.safetensors")
 
-    a = _model(sd, shape, shape.batch)
+    def fresh():
+        mdl = _model(sd, shape, shape.batch)
+        if fp16:
+            mdl.set_loss_scaler(scale=1024.0, interval=2)
+        return mdl
+
+    a = fresh()
     la = sd.train(a, batch, 6, save_every=3, ckpt_path=path, **kw)   # saves after step 3 and step 6
     os.replace(path, path + ".6")
-    a3 = _model(sd, shape, shape.batch)
+    a3 = fresh()
     sd.train(a3, batch, 3, save_every=3, ckpt_path=path, **kw)       # the step-3 checkpoint
     bmodel = sd.Model(shape, max_batch=shape.batch)
     assert bmodel.load(path) == 3
     for which in (sd.LM_PARAMS, sd.LM_ADAM_M, sd.LM_ADAM_V):
         assert np.array_equal(bmodel.get_flat(which), a3.get_flat(which))
+    if fp16:
+        assert bmodel.loss_scaler() == a3.loss_scaler()
+        assert a3.loss_scaler()["scale"] == 2048.0 and a3.loss_scaler()["good_steps"] == 1
     lb = sd.train(bmodel, batch, 3, start_step=4, **kw)
     t.cuda.synchronize()
     for which in (sd.LM_PARAMS, sd.LM_ADAM_M, sd.LM_ADAM_V):

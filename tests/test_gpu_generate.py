@@ -114,14 +114,17 @@ def test_sampled_generation_is_reproducible(sd):
 
 # ------------------------------------------------------- key/value cache
 
-@pytest.mark.parametrize("name,untied", [("C1", False), ("C2", False), ("C1", True), ("C2", True)])
-def test_cached_decode_matches_oracle(sd, name, untied):
+@pytest.mark.parametrize("name,untied,prec", [("C1", False, None), ("C2", False, None), ("C1", True, None),
+                                              ("C2", True, None), ("C2", False, "fp16")])
+def test_cached_decode_matches_oracle(sd, name, untied, prec):
     """prefill over a prompt, then decode steps fed known tokens: the logits of
     every step against the oracle's forward pass over the sequence so far
-    (fp32: rel <= 1e-4; bf16: cos >= 0.999), with the tied head and with a
-    separate head and bias."""
+    (fp32: rel <= 1e-4; bf16 and fp16: cos >= 0.999), with the tied head and
+    with a separate head and bias."""
     t = torch()
     shape = synth.SHAPES[name].replace(untied_head=untied)
+    if prec:
+        shape = shape.replace(precision=prec)
     params = synth.init_params(shape)
     if untied:
         params["head.b"] = synth.random_tensor(np.random.default_rng(5), params["head.b"].shape, 0.5)

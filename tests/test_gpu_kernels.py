@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import act, bf16_exact, cos, dev, host, rel, torch
+from helpers import act, act_dtype, cos, dev, exact, host, rel, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -35,13 +35,13 @@ def _operands(rng, prec, *shapes, scale=1.0):
     out = []
     for s in shapes:
         a = (rng.standard_normal(s) * scale).astype(np.float32)
-        out.append(bf16_exact(a) if prec else a)
+        out.append(exact(a, prec))
     return out
 
 
 # ------------------------------------------------------------------- GEMM
 
-@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("prec", [0, 1, 2])
 @pytest.mark.parametrize("layout", ["fwd", "dx", "dw"])
 @pytest.mark.parametrize("MNK", [(200, 136, 72), (1000, 648, 576), (8, 8, 8), (136, 264, 1536)])
 @pytest.mark.parametrize("split", [0, 3])
@@ -69,7 +69,7 @@ def test_gemm_layouts(sd, prec, layout, MNK, split):
     assert rel(host(C), expect) <= tol(prec, True)
 
 
-@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("prec", [0, 1, 2])
 @pytest.mark.parametrize("epi", ["store", "resid", "gelu", "dgelu"])
 @pytest.mark.parametrize("split", [0, 2])
 def test_gemm_epilogues(sd, prec, epi, split):
@@ -80,7 +80,7 @@ def test_gemm_epilogues(sd, prec, epi, split):
     X, W = _operands(rng, prec, (M, K), (N, K), scale=0.3)
     bias = rng.standard_normal(N).astype(np.float32)
     ws = t.zeros(4 * M * N, dtype=t.float32, device="cuda")
-    adt = t.bfloat16 if prec else t.float32
+    adt = act_dtype(prec)
     lin = oracle.linear_fwd(X, W, bias)
     args = dict(bias=dev(bias), force_split=split, ws=ws)
     if epi == "store":
@@ -103,7 +103,7 @@ def test_gemm_epilogues(sd, prec, epi, split):
         assert rel(host(Aout), oracle.gelu(lin)) <= tol(prec, False)
     else:
         u = rng.standard_normal((M, N)).astype(np.float32) * 2
-        u = bf16_exact(u) if prec else u
+        u = exact(u, prec)
         C = t.zeros((M, N), dtype=adt, device="cuda")
         args.pop("bias")
         sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, C, N, sd.EPI_DGELU, aux=act(u, prec),
@@ -128,7 +128,7 @@ def test_gemm_output_row_limit(sd):
 
 # -------------------------------------------------------------- LayerNorm
 
-@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("prec", [0, 1, 2])
 @pytest.mark.parametrize("C", [128, 768])
 def test_layernorm_fwd_bwd(sd, prec, C):
     t = torch()
@@ -137,7 +137,7 @@ def test_layernorm_fwd_bwd(sd, prec, C):
     x = (rng.standard_normal((M, C)) * 2 + 0.3).astype(np.float32)
     g = (1 + 0.2 * rng.standard_normal(C)).astype(np.float32)
     b = (0.1 * rng.standard_normal(C)).astype(np.float32)
-    adt = t.bfloat16 if prec else t.float32
+    adt = act_dtype(prec)
     y = t.zeros((M, C), dtype=adt, device="cuda")
     mu = t.zeros(M, device="cuda")
     rs = t.zeros(M, device="cuda")
@@ -230,7 +230,7 @@ def test_embedding_forward(sd):
 
 # -------------------------------------------------------------- attention
 
-@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("prec", [0, 1, 2])
 @pytest.mark.parametrize("D", [32, 64])
 @pytest.mark.parametrize("packed", [False, True])
 def test_attention_fwd_bwd(sd, prec, D, packed):
@@ -240,13 +240,13 @@ def test_attention_fwd_bwd(sd, prec, D, packed):
     rng = np.random.default_rng(D + 2 * prec + 4 * packed)
     print(f"attention prec={prec} D={D} packed={packed}", flush=True)
     qkv = (rng.standard_normal((B, T, 3 * C)) * 1.5).astype(np.float32)
-    qkv = bf16_exact(qkv) if prec else qkv
+    qkv = exact(qkv, prec)
     doc = _doc_ids(rng, B, T, (1, 90)) if packed else None
     start_np, _ = oracle.index_layout(doc, B, T)
     start, end, pos = (t.zeros((B, T), dtype=t.int32, device="cuda") for _ in range(3))
     flags = t.zeros(4, dtype=t.int32, device="cuda")
     sd.index_layout(None if doc is None else dev(doc), B, T, start, end, pos, flags)
-    adt = t.bfloat16 if prec else t.float32
+    adt = act_dtype(prec)
     o = t.zeros((B, T, C), dtype=adt, device="cuda")
     lse = t.zeros((B, H, T), device="cuda")
     qkv_d = act(qkv, prec)
@@ -262,7 +262,7 @@ def test_attention_fwd_bwd(sd, prec, D, packed):
     assert rel(host(o), eo) <= (2e-5 if prec == 0 else 8e-3)
     assert np.abs(host(lse) - else_).max() <= (2e-5 if prec == 0 else 2e-3)
     do = rng.standard_normal((B, T, C)).astype(np.float32)
-    do = bf16_exact(do) if prec else do
+    do = exact(do, prec)
     dqkv = t.zeros((B, T, 3 * C), dtype=adt, device="cuda")
     delta = t.zeros((B, H, T), device="cuda")
     sd.attn_bwd(prec, qkv_d, o, lse, act(do, prec), start, end, B, T, H, D, delta, dqkv)
@@ -280,7 +280,7 @@ def test_attention_fwd_bwd(sd, prec, D, packed):
 
 # ------------------------------------------------------------ column sums
 
-@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("prec", [0, 1, 2])
 @pytest.mark.parametrize("M,N", [(300, 768), (1000, 2304), (129, 3076)])
 def test_column_sums(sd, prec, M, N):
     """Bias gradients: out[c] = sum over rows of a[:, c] (fixed order, 8 or 4
@@ -288,7 +288,7 @@ def test_column_sums(sd, prec, M, N):
     t = torch()
     rng = np.random.default_rng(M + N + prec)
     a = rng.standard_normal((M, N)).astype(np.float32)
-    a = bf16_exact(a) if prec else a
+    a = exact(a, prec)
     out = t.zeros(N, device="cuda")
     ws = t.zeros(sd.colsum_ws_floats(M, N), device="cuda")
     sd.colsum(prec, act(a, prec), N, M, N, out, ws)
@@ -300,7 +300,7 @@ def test_column_sums(sd, prec, M, N):
 
 # V = 50257 and 70000 also cover the row-in-memory kernel (rows too long to
 # stay in registers) next to the register-resident one
-@pytest.mark.parametrize("prec", [0, 1])
+@pytest.mark.parametrize("prec", [0, 1, 2])
 @pytest.mark.parametrize("V", [257, 8000, 50257, 70000])
 def test_cross_entropy(sd, prec, V):
     t = torch()
@@ -308,7 +308,7 @@ def test_cross_entropy(sd, prec, V):
     ldz = (V + 127) // 128 * 128
     rng = np.random.default_rng(V + prec)
     z = (rng.standard_normal((M, V)) * 3).astype(np.float32)
-    z = bf16_exact(z) if prec else z
+    z = exact(z, prec)
     tgt = rng.integers(0, V, M).astype(np.int32)
     tgt[::7] = -1
     zp = np.zeros((M, ldz), np.float32)
@@ -328,6 +328,15 @@ def test_cross_entropy(sd, prec, V):
     assert rel(got[:, :V], edz) <= (2e-5 if prec == 0 else 6e-3)
     assert np.all(got[:, V:] == 0)
     assert np.all(got[tgt < 0] == 0)
+    # with a loss scale S = 1024 dz is S times as large and the loss unchanged
+    zd2 = act(zp, prec)
+    S = dev(np.array([1024.0], np.float32))
+    sd.xent(prec, zd2, ldz, M, V, dev(tgt), loss, ws_n, ws_rows, flags, loss_scale=S)
+    t.cuda.synchronize()
+    assert abs(float(loss[0]) - el) <= 2e-5 * abs(el)
+    assert rel(host(zd2)[:, :V] / 1024.0, edz) <= (2e-5 if prec == 0 else 6e-3)
+    if prec == 0:
+        assert np.array_equal(host(zd2), got * 1024.0)  # a power of two scales exactly
 
 
 # ------------------------------------------------ embedding backward (CSR)
@@ -392,6 +401,45 @@ def test_grad_norm_and_adamw(sd, clip):
     assert np.all(np.abs(host(pd) - ep) <= 4 * ulp + 1e-5 * np.abs(ep - p))
     assert rel(host(md), em) <= 1e-6 and rel(host(vd), ev) <= 1e-6
     assert t.equal(shadow, pd.to(t.bfloat16))
+    # the fp16 operand copy
+    pd2, md2, vd2 = dev(p), dev(m), dev(v)
+    sh16 = t.zeros(n, dtype=t.float16, device="cuda")
+    sd.adamw(pd2, gd, md2, vd2, 3e-4, 0.9, 0.999, 1e-8, 0.1, 3, ns, flags, sh16, shadow_f16=True)
+    t.cuda.synchronize()
+    assert t.equal(pd2, pd) and t.equal(sh16, pd2.to(t.float16))
+
+
+def test_grad_norm_with_loss_scale(sd):
+    """The buffer holds S g: the norm and clip factor are those of g, the
+    update factor is (clip factor) / S, and the scale state follows the
+    oracle's rule (finite steps, growth at the interval, backoff on inf)."""
+    t = torch()
+    rng = np.random.default_rng(4)
+    n = 100_000
+    g = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    S0 = 4096.0
+    gs = dev(g * np.float32(S0))
+    part = t.zeros(1024, dtype=t.float64, device="cuda")
+    ns = t.zeros(2, device="cuda")
+    flags = t.zeros(4, dtype=t.int32, device="cuda")
+    state = dev(np.array([S0, 0.0], np.float32))
+    en, es = oracle.grad_norm_and_scale({"g": g}, 1.0)
+    trace = []
+    for i in range(4):
+        sd.grad_norm(gs, 1.0, part, ns, flags, scale_state=state, growth=2.0, backoff=0.5, interval=3)
+        t.cuda.synchronize()
+        if i == 0:
+            assert abs(float(ns[0]) - en) <= 1e-6 * en
+            assert abs(float(ns[1]) * S0 - es) <= 1e-6 * es
+        trace.append((float(state[0]), int(state[1])))
+    assert int(flags[0]) & 1 == 0
+    g_inf = g.copy()
+    g_inf[7] = np.inf
+    sd.grad_norm(dev(g_inf), 1.0, part, ns, flags, scale_state=state, growth=2.0, backoff=0.5, interval=3)
+    t.cuda.synchronize()
+    trace.append((float(state[0]), int(state[1])))
+    assert int(flags[0]) & 1
+    assert trace == oracle.loss_scale_trace(S0, [True] * 4 + [False], 2.0, 0.5, 3)
 
 
 def test_adamw_skips_on_nonfinite_norm(sd):

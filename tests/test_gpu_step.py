@@ -49,11 +49,13 @@ def run_gpu(sd, shape, tok, tgt, doc, params, step=1, m=None, v=None):
     tok_d, tgt_d = dev(tok), dev(tgt)
     doc_d = None if doc is None else dev(doc)
     logits = model.forward_logits(tok_d, doc_d)
+    # fp16: the gradient buffer holds S g for the loss scale S of the step
+    S = model.loss_scaler()["scale"] if shape.precision == "fp16" else 1.0
     stats = model.train_step(tok_d, tgt_d, doc_d, lr=shape.lr, step=step, beta1=shape.beta1, beta2=shape.beta2,
                              eps=shape.eps, weight_decay=shape.weight_decay, clip=shape.clip)
     t.cuda.synchronize()
     return {"model": model, "logits": host(logits), "stats": stats.cpu().numpy().astype(np.float64),
-            "grads": model.get(sd.LM_GRADS), "params": model.get(sd.LM_PARAMS),
+            "grads": {k: g / S for k, g in model.get(sd.LM_GRADS).items()}, "params": model.get(sd.LM_PARAMS),
             "m": model.get(sd.LM_ADAM_M), "v": model.get(sd.LM_ADAM_V)}
 
 
@@ -183,6 +185,61 @@ def test_vocab_padding_rows_stay_zero(sd, untied):
             if name in ("wte", "head.w", "head.b"):
                 nxt = min([o for o, _ in ends if o > off] + [model.total])
                 assert not np.any(f[off + rows * cols:nxt]), (which, name)
+
+
+@pytest.mark.parametrize("name,batch", [("C2", 16), ("C3", 8), ("C4", 1)])
+def test_fp16_step_matches_oracle(sd, name, batch):
+    """fp16 operands with the default loss scale (2^16): the same bounds as
+    the bf16 path, on gradients divided by the step's scale."""
+    shape = synth.SHAPES[name].with_batch(batch).replace(precision="fp16")
+    print(f"fp16 train_step parity {name} B={batch} T={shape.seq}", flush=True)
+    tok, tgt, doc = _inputs(shape, batch)
+    params = synth.init_params(shape)
+    got = run_gpu(sd, shape, tok, tgt, doc, params)
+    assert got["model"].loss_scaler()["scale"] == 65536.0  # one finite step: no change yet
+    ref = run_oracle(shape, tok, tgt, doc, params)
+    compare(shape, got, ref, params)
+
+
+def test_fp16_loss_scale_backoff_and_growth(sd):
+    """An overflowing scale (2^60: the scaled loss gradient exceeds fp16)
+    skips the step bit-exactly and halves S until the gradients are finite;
+    then S doubles after every `interval` finite steps. The scale sequence
+    follows the oracle's rule fed with the steps' finite flags."""
+    t = torch()
+    shape = synth.C2.with_batch(4).replace(precision="fp16")
+    tok, tgt, doc = _inputs(shape, 4)
+    model = sd.Model(shape, max_batch=4)
+    model.set(sd.LM_PARAMS, synth.init_params(shape))
+    model.set_loss_scaler(scale=2.0 ** 60, growth=2.0, backoff=0.25, interval=3)
+    p0 = model.get_flat(sd.LM_PARAMS)
+    flags, scales = [], []
+    for step in range(1, 31):
+        before = [model.get_flat(b) for b in (sd.LM_PARAMS, sd.LM_ADAM_M, sd.LM_ADAM_V)]
+        st = model.train_step(dev(tok), dev(tgt), None, lr=shape.lr, step=step, clip=shape.clip)
+        finite = (int(st.cpu().numpy()[2]) & 1) == 0
+        flags.append(finite)
+        sc = model.loss_scaler()
+        scales.append((sc["scale"], sc["good_steps"]))
+        if not finite:  # skipped: parameters and moments untouched
+            after = [model.get_flat(b) for b in (sd.LM_PARAMS, sd.LM_ADAM_M, sd.LM_ADAM_V)]
+            assert all(np.array_equal(x, y) for x, y in zip(before, after)), step
+    t.cuda.synchronize()
+    assert not flags[0] and any(flags), flags
+    assert scales == oracle.loss_scale_trace(2.0 ** 60, flags, 2.0, 0.25, 3)
+    assert not np.array_equal(model.get_flat(sd.LM_PARAMS), p0)
+
+
+def test_fp16_scaler_is_fp16_only(sd):
+    shape = synth.C1
+    model = sd.Model(shape, max_batch=1)
+    with pytest.raises(RuntimeError):
+        model.loss_scaler()
+    m16 = sd.Model(shape.replace(precision="fp16"), max_batch=1)
+    with pytest.raises(RuntimeError):
+        m16.set_loss_scaler(scale=0.0)
+    with pytest.raises(RuntimeError):
+        m16.set_loss_scaler(interval=0)
 
 
 def test_fp32_path_on_a_packed_workload(sd):
