@@ -156,9 +156,11 @@ struct MNPitch {  // elements per k-row of an M/N-contiguous tile (>= 128 for th
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 
+// The LDS pointer is made by an address-space cast of the shared-array
+// pointer (not through an integer), so the compiler keeps track of which LDS
+// array a read comes from.
 __device__ __forceinline__ bf16x4_t ds_read_tr(const bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) bf16*)((uintptr_t)p)));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const __attribute__((address_space(3))) bf16*)p);
 }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -369,10 +371,16 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
     lb.store(rb[P ^ 1], sB[P ^ 1], tid);
     __syncthreads();
   };
-  for (int it = 0; it < nk; it += 2) {
+  // Whole pairs in the loop and an odd last step after it: with no path from
+  // the middle of a pair back to the loop head, the wait-count analysis sees
+  // only the set being refilled as in flight at the head, instead of waiting
+  // for every outstanding load there.
+  int it = 0;
+  for (; it + 1 < nk; it += 2) {
     step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < nk) step(std::integral_constant<int, 1>{}, it + 1);
+    step(std::integral_constant<int, 1>{}, it + 1);
   }
+  if (it < nk) step(std::integral_constant<int, 0>{}, it);
 
   // Epilogue through LDS: the wave row w (WGN wavefronts, WTM rows) writes its
   // fp32 accumulators to LDS (row pitch BN + 4 floats), then all threads walk
@@ -899,12 +907,12 @@ static int pick_cfg(const GemmOp& op) {
   const int f = forced_cfg();
   if (f >= 0) return f;
   // Measured on the GPT-2-small-shaped step: the persistent 256 x 256 kernel
-  // wins on the vocabulary projection's forward (very wide N) and its input
-  // gradient (very long K), and on the MLP weight gradients (3072 x 768
-  // outputs over K = 8192); 128 x 128 at two blocks per CU wins everywhere
-  // else.
+  // wins on the vocabulary projection's forward (very wide N), its input
+  // gradient (very long K) and its weight gradient (very tall M), and on the
+  // MLP weight gradients (3072 x 768 outputs over K = 8192); 128 x 128 at two
+  // blocks per CU wins everywhere else.
   const int mn_max = op.M > op.N ? op.M : op.N, mn_min = op.M < op.N ? op.M : op.N;
-  if (op.N >= 16384 || op.K >= 16384) return kCfgPipe;
+  if (op.M >= 16384 || op.N >= 16384 || op.K >= 16384) return kCfgPipe;
   if (op.K >= 8192 && mn_max >= 3072 && mn_max <= 4096 && mn_min <= 1024) return kCfgPipe;
   return kCfgSmall;
 }

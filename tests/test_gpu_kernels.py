@@ -64,9 +64,15 @@ def test_gemm_layouts(sd, prec, layout, MNK, split):
         expect = oracle.linear_bwd(dY, X, np.zeros((M, N)))[1]
     C = t.zeros((M, N), dtype=t.float32, device="cuda")
     ws = t.zeros(4 * M * N + 16, dtype=t.float32, device="cuda")
-    sd.gemm(prec, M, N, K, act(A, prec), lda, akc, act(B, prec), ldb, bkc, C, N, c_f32=True, force_split=split, ws=ws)
+    Ad, Bd = act(A, prec), act(B, prec)
+    sd.gemm(prec, M, N, K, Ad, lda, akc, Bd, ldb, bkc, C, N, c_f32=True, force_split=split, ws=ws)
     t.cuda.synchronize()
     assert rel(host(C), expect) <= tol(prec, True)
+    # slices are summed in a fixed order: a second run is bit-identical
+    C2 = t.zeros_like(C)
+    sd.gemm(prec, M, N, K, Ad, lda, akc, Bd, ldb, bkc, C2, N, c_f32=True, force_split=split, ws=ws)
+    t.cuda.synchronize()
+    assert t.equal(C, C2)
 
 
 @pytest.mark.parametrize("prec", [0, 1, 2])
