@@ -46,8 +46,11 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x
   for (int j = 0; j < NV; ++j) {
     int c = 2 * (lane + 64 * j);
     float2 gg = g2[lane + 64 * j], bb = b2[lane + 64 * j];
-    Act<T>::st(y, m * C + c, (v[j].x - mu) * r * gg.x + bb.x);
-    Act<T>::st(y, m * C + c + 1, (v[j].y - mu) * r * gg.y + bb.y);
+    const float y0 = (v[j].x - mu) * r * gg.x + bb.x, y1 = (v[j].y - mu) * r * gg.y + bb.y;
+    if constexpr (sizeof(T) == 2)  // two adjacent 16-bit values in one 4-byte store
+      reinterpret_cast<uint32_t*>(y)[(m * C + c) >> 1] = H16<T>::pack(y0, y1);
+    else
+      reinterpret_cast<float2*>(y)[(m * C + c) >> 1] = make_float2(y0, y1);
   }
   if (lane == 0) {
     mu_out[m] = mu;
@@ -217,18 +220,19 @@ __global__ void __launch_bounds__(256) colsum_partials_kernel(const float* __res
   float a = 0.f, b = 0.f, d = 0.f;
   if (c < C) {
     int p = r;
-    // batches of 8 partial rows: loads in flight together, added in order
-    for (; p + 7 * 16 < P; p += 8 * 16) {
-      float va[8], vb[8], vc[8];
+    // batches of 16 partial rows: loads in flight together (the sums are
+    // latency-bound), added in order
+    for (; p + 15 * 16 < P; p += 16 * 16) {
+      float va[16], vb[16], vc[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const long o = (long)(p + 16 * u) * C + c;
         va[u] = pa[o];
         vb[u] = pb ? pb[o] : 0.f;
         vc[u] = pc ? pc[o] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         a += va[u];
         b += vb[u];
         d += vc[u];
