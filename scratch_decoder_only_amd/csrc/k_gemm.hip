@@ -316,6 +316,43 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
   TB lb;
   la.init(A, p.lda, m0, p.M, p.K, tid);
   lb.init(B, p.ldb, n0, p.N, p.K, tid);
+  // GELU' epilogue: this thread's chunks of u (16 bytes per 8-column chunk of
+  // the epilogue walk below) are loaded now, so their latency hides behind
+  // the K loop instead of stalling the epilogue
+  constexpr int CPT = WTM * BN / 8 / NT;  // epilogue chunks per thread and wave row
+  constexpr bool PRE_U = EPI == EPI_DGELU && CPT * NT * 8 == WTM * BN;
+  // residual epilogue: the fp32 residual chunks of the first wave row are
+  // loaded now as well (32 bytes per chunk; the other rows' when the
+  // epilogue starts, as the K loop's registers are free by then)
+  constexpr bool PRE_R = EPI == EPI_RESID && CPT * NT * 8 == WTM * BN;
+  float4 rpre[PRE_R ? 2 * CPT : 1];
+  auto load_r = [&](int w, int q, float4& lo, float4& hi) {
+    const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+    const long row = m0 + w * WTM + r, col = n0 + c8;
+    if (row < p.M_out && col < p.N) {
+      lo = *reinterpret_cast<const float4*>(p.R + row * p.ldr + col);
+      hi = *reinterpret_cast<const float4*>(p.R + row * p.ldr + col + 4);
+    } else {
+      lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if constexpr (PRE_R) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) load_r(0, q, rpre[2 * q], rpre[2 * q + 1]);
+  }
+  uint4 upre[PRE_U ? WGM * CPT : 1];
+  if constexpr (PRE_U) {
+#pragma unroll
+    for (int w = 0; w < WGM; ++w)
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+        const long row = m0 + w * WTM + r, col = n0 + c8;
+        upre[w * CPT + q] = (row < p.M_out && col < p.N)
+                                ? *reinterpret_cast<const uint4*>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col)
+                                : make_uint4(0, 0, 0, 0);
+      }
+  }
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -392,8 +429,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
   static_assert(WTM * CP * 4 <= 2 * (TA::ELEMS + TB::ELEMS) * 2, "epilogue tile fits in the stage buffers");
   float* sC = reinterpret_cast<float*>(&sA[0][0]);
   static_assert(sizeof(sA) + sizeof(sB) >= WTM * CP * 4, "");
-#pragma unroll 1
-  for (int w = 0; w < WGM; ++w) {
+  auto stage_acc = [&](int w) {
     if (wm == w) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -407,6 +443,70 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
           }
     }
     __syncthreads();
+  };
+  if constexpr (PRE_U) {
+#pragma unroll
+    for (int w = 0; w < WGM; ++w) {
+      stage_acc(w);
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+        const long row = m0 + w * WTM + r, col = n0 + c8;
+        if (row < p.M_out && col < p.N) {
+          float v[8];
+          ld8_f32(sC + r * CP + c8, v);
+          const uint4 uu = upre[w * CPT + q];
+          const uint32_t uw[4] = {uu.x, uu.y, uu.z, uu.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] *= gelu_grad_f(H16<E>::lo(uw[i]));
+            v[2 * i + 1] *= gelu_grad_f(H16<E>::hi(uw[i]));
+          }
+          st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  if constexpr (PRE_R) {
+#pragma unroll
+    for (int w = 0; w < WGM; ++w) {
+      float4 rnext[2 * CPT];
+      if (w + 1 < WGM) {
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) load_r(w + 1, q, rnext[2 * q], rnext[2 * q + 1]);
+      }
+      stage_acc(w);
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+        const long row = m0 + w * WTM + r, col = n0 + c8;
+        if (row < p.M_out && col < p.N) {
+          float v[8], b[8];
+          ld8_f32(sC + r * CP + c8, v);
+          if (p.bias) {
+            ld8_f32(p.bias + col, b);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] += b[i];
+          }
+          const float4 lo = rpre[2 * q], hi = rpre[2 * q + 1];
+          v[0] += lo.x; v[1] += lo.y; v[2] += lo.z; v[3] += lo.w;
+          v[4] += hi.x; v[5] += hi.y; v[6] += hi.z; v[7] += hi.w;
+          st8_f32(reinterpret_cast<float*>(p.C) + row * p.ldc + col, v);
+        }
+      }
+      if (w + 1 < WGM) {
+#pragma unroll
+        for (int q = 0; q < 2 * CPT; ++q) rpre[q] = rnext[q];
+      }
+      __syncthreads();
+    }
+    return;
+  }
+#pragma unroll 1
+  for (int w = 0; w < WGM; ++w) {
+    stage_acc(w);
     for (int c = tid; c < WTM * BN / 8; c += NT) {
       const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
       const long row = m0 + w * WTM + r, col = n0 + c8;
