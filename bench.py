@@ -65,6 +65,9 @@ def attention_flops(shape, doc_ids, B, T):
 # Kernel symbol of each timing class whose HBM traffic is taken from counters
 # (a class must map to one kernel instantiation used by nothing else).
 TRAFFIC_SYMBOLS = {
+    "gemm_head_bwd_dw": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, false, false, 0, float,",
+    "gemm_head_fwd": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, true, true, 0,",
+    "gemm_fc1_fwd": "gemm16_kernel<128, 128, 2, 2, true, true, 2,",
     "gemm_fc2_bwd_dx": "gemm16_kernel<128, 128, 2, 2, true, false, 3,",
     "attn_bwd_dkv": "attn_dkv_kernel<64>",
     "attn_fwd": "attn_fwd_kernel<64>",

@@ -261,18 +261,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Maps the linear block id to a tile so that consecutive tiles of the grouped
-// order share an XCD (blocks are dealt to the 8 XCDs round-robin): each XCD
-// gets a contiguous range of tiles, walked GROUP_M m-tiles at a time, so an
-// XCD's L2 keeps the A row-panels and B column-panels its tiles share.
-__device__ __forceinline__ void tile_of(int b, int nb, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int xcd = b & 7, local = b >> 3, q = nb >> 3, r = nb & 7;
-  const int t = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+// Work unit u -> (tile m, tile n, K slice z). Units are numbered slice-major
+// and, inside a slice, in groups of GM m-tiles walked n-tile by n-tile. Block
+// b runs on XCD b % 8; the 32 blocks of one XCD take 32 consecutive units per
+// round, so the panels they share stay in that XCD's L2.
+__device__ __forceinline__ int pipe_unit(int round, int b, int nblocks) {
+  const int xcd = b & 7, local = b >> 3;
+  const int per_xcd = nblocks >> 3;  // nblocks is a multiple of 8
+  return round * nblocks + xcd * per_xcd + local;
+}
+__device__ __forceinline__ void pipe_tile(int u, int tiles_m, int tiles_n, int& tm, int& tn, int& z) {
+  const int tiles = tiles_m * tiles_n;
+  z = u / tiles;
+  const int t = u - z * tiles;
   constexpr int GM = 8;
   const int per_group = GM * tiles_n;
   const int group = t / per_group, first_m = group * GM;
   const int gsize = min(tiles_m - first_m, GM);
-  const int in = t % per_group;
+  const int in = t - group * per_group;
   tm = first_m + in % gsize;
   tn = in / gsize;
 }
@@ -286,10 +292,15 @@ struct GemmOcc {
   static constexpr int value = blocks * WGM * WGN / 4 > 0 ? blocks * WGM * WGN / 4 : 1;
 };
 
+// Persistent over work units (tile, K slice): the grid holds two blocks per
+// CU and each block walks units with a stride of the grid (XCD-aware order,
+// as for the 256 x 256 kernel). The first two K steps of a block's next unit
+// are loaded into registers right after the current unit's K loop, so their
+// latency hides behind the current unit's epilogue.
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC, typename E>
 __global__ void __launch_bounds__(WGM * WGN * 64)
     __attribute__((amdgpu_waves_per_eu(GemmOcc<BM, BN, WGM, WGN>::value, GemmOcc<BM, BN, WGM, WGN>::value)))
-    gemm16_kernel(GemmArgs p) {
+    gemm16_kernel(GemmArgs p, int units) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -302,65 +313,18 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  int tmi, tni;
-  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tmi, tni);
-  const int m0 = tmi * BM, n0 = tni * BN;
-  const int z = blockIdx.y;
-  const int k_begin = z * p.k_split;
-  const int k_end = min(p.K, k_begin + p.k_split);
-  const int nk = (k_end - k_begin + kBK - 1) / kBK;
+  const int nb = gridDim.x;
   const bf16* A = reinterpret_cast<const bf16*>(p.A);
   const bf16* B = reinterpret_cast<const bf16*>(p.B);
+  // the K range of slice z
+  auto k_range = [&](int z, int& kb, int& ke, int& nk) {
+    kb = z * p.k_split;
+    ke = min(p.K, kb + p.k_split);
+    nk = (ke - kb + kBK - 1) / kBK;
+  };
 
   TA la;
   TB lb;
-  la.init(A, p.lda, m0, p.M, p.K, tid);
-  lb.init(B, p.ldb, n0, p.N, p.K, tid);
-  // GELU' epilogue: this thread's chunks of u (16 bytes per 8-column chunk of
-  // the epilogue walk below) are loaded now, so their latency hides behind
-  // the K loop instead of stalling the epilogue
-  constexpr int CPT = WTM * BN / 8 / NT;  // epilogue chunks per thread and wave row
-  constexpr bool PRE_U = EPI == EPI_DGELU && CPT * NT * 8 == WTM * BN;
-  // residual epilogue: the fp32 residual chunks of the first wave row are
-  // loaded now as well (32 bytes per chunk; the other rows' when the
-  // epilogue starts, as the K loop's registers are free by then)
-  constexpr bool PRE_R = EPI == EPI_RESID && CPT * NT * 8 == WTM * BN;
-  float4 rpre[PRE_R ? 2 * CPT : 1];
-  auto load_r = [&](int w, int q, float4& lo, float4& hi) {
-    const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
-    const long row = m0 + w * WTM + r, col = n0 + c8;
-    if (row < p.M_out && col < p.N) {
-      lo = *reinterpret_cast<const float4*>(p.R + row * p.ldr + col);
-      hi = *reinterpret_cast<const float4*>(p.R + row * p.ldr + col + 4);
-    } else {
-      lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  if constexpr (PRE_R) {
-#pragma unroll
-    for (int q = 0; q < CPT; ++q) load_r(0, q, rpre[2 * q], rpre[2 * q + 1]);
-  }
-  uint4 upre[PRE_U ? WGM * CPT : 1];
-  if constexpr (PRE_U) {
-#pragma unroll
-    for (int w = 0; w < WGM; ++w)
-#pragma unroll
-      for (int q = 0; q < CPT; ++q) {
-        const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
-        const long row = m0 + w * WTM + r, col = n0 + c8;
-        upre[w * CPT + q] = (row < p.M_out && col < p.N)
-                                ? *reinterpret_cast<const uint4*>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col)
-                                : make_uint4(0, 0, 0, 0);
-      }
-  }
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
   // Software pipeline, two K steps of global loads in flight: at step it the
   // LDS stage it%2 holds K step it, register set (it+1)%2 holds (or is
   // receiving) step it+1, and step it+2 is loaded into set it%2. Loads past
@@ -369,156 +333,222 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
   // unrolled by two so the register sets stay static.
   uint4 ra[2][TA::NL], rb[2][TB::NL];
   bf16x8_t af[2][TM], bfr[2][TN];
-  auto kstep = [&](int it) { return k_begin + min(it, max(nk - 1, 0)) * kBK; };
-  la.load(ra[0], kstep(0), k_end);
-  lb.load(rb[0], kstep(0), k_end);
-  la.load(ra[1], kstep(1), k_end);
-  lb.load(rb[1], kstep(1), k_end);
-  la.store(ra[0], sA[0], tid);
-  lb.store(rb[0], sB[0], tid);
-  __syncthreads();
-
-  auto step = [&](auto P_, int it) {
-    constexpr int P = decltype(P_)::value;
-    la.load(ra[P], kstep(it + 2), k_end);
-    lb.load(rb[P], kstep(it + 2), k_end);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) af[0][i] = la.frag(sA[P], wm * WTM + i * 32, 0, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[0][j] = lb.frag(sB[P], wn * WTN + j * 32, 0, lane);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int f = ks & 1;
-      if (ks + 1 < kBK / 16) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[f ^ 1][i] = la.frag(sA[P], wm * WTM + i * 32, ks + 1, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[f ^ 1][j] = lb.frag(sB[P], wn * WTN + j * 32, ks + 1, lane);
-      }
-      // keep the reads of k-step ks+1 ahead of the MFMAs of k-step ks
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = mfma32<E>(af[f][i], bfr[f][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    la.store(ra[P ^ 1], sA[P ^ 1], tid);
-    lb.store(rb[P ^ 1], sB[P ^ 1], tid);
-    __syncthreads();
+  // set up the loaders for unit u and load its first two K steps
+  auto prologue = [&](int u) {
+    int tm, tn, z, kb, ke, nk;
+    pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
+    k_range(z, kb, ke, nk);
+    la.init(A, p.lda, tm * BM, p.M, p.K, tid);
+    lb.init(B, p.ldb, tn * BN, p.N, p.K, tid);
+    la.load(ra[0], kb, ke);
+    lb.load(rb[0], kb, ke);
+    la.load(ra[1], kb + min(1, max(nk - 1, 0)) * kBK, ke);
+    lb.load(rb[1], kb + min(1, max(nk - 1, 0)) * kBK, ke);
   };
-  // Whole pairs in the loop and an odd last step after it: with no path from
-  // the middle of a pair back to the loop head, the wait-count analysis sees
-  // only the set being refilled as in flight at the head, instead of waiting
-  // for every outstanding load there.
-  int it = 0;
-  for (; it + 1 < nk; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
-  }
-  if (it < nk) step(std::integral_constant<int, 0>{}, it);
 
-  // Epilogue through LDS: the wave row w (WGN wavefronts, WTM rows) writes its
-  // fp32 accumulators to LDS (row pitch BN + 4 floats), then all threads walk
-  // that WTM x BN region in 8-column chunks, so bias, residual and GELU
-  // operands are read and results written with 16- and 32-byte accesses.
-  // Accumulator element e of tile (i, j): row (e/4)*8 + (lane/32)*4 + e%4,
-  // column lane%32.
+  // epilogue operands loaded ahead (one 8-column chunk per thread and pass):
+  // GELU': this thread's chunks of u, at the unit's start, so their latency
+  // hides behind the K loop; residual: the first wave row's fp32 chunks at
+  // the unit's start, the next row's before each staging pass
+  constexpr int CPT = WTM * BN / 8 / NT;  // epilogue chunks per thread and wave row
+  constexpr bool PRE_U = EPI == EPI_DGELU && CPT * NT * 8 == WTM * BN;
+  constexpr bool PRE_R = EPI == EPI_RESID && CPT * NT * 8 == WTM * BN;
+  float4 rpre[PRE_R ? 2 * CPT : 1];
+  uint4 upre[PRE_U ? WGM * CPT : 1];
+  f32x16_t acc[TM][TN];
   constexpr int CP = BN + 4;
   static_assert(WTM * CP * 4 <= 2 * (TA::ELEMS + TB::ELEMS) * 2, "epilogue tile fits in the stage buffers");
   float* sC = reinterpret_cast<float*>(&sA[0][0]);
-  static_assert(sizeof(sA) + sizeof(sB) >= WTM * CP * 4, "");
-  auto stage_acc = [&](int w) {
-    if (wm == w) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-            const int c = wn * WTN + j * 32 + (lane & 31);
-            sC[r * CP + c] = acc[i][j][e];
-          }
-    }
-    __syncthreads();
-  };
-  if constexpr (PRE_U) {
-#pragma unroll
-    for (int w = 0; w < WGM; ++w) {
-      stage_acc(w);
-#pragma unroll
-      for (int q = 0; q < CPT; ++q) {
-        const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
-        const long row = m0 + w * WTM + r, col = n0 + c8;
-        if (row < p.M_out && col < p.N) {
-          float v[8];
-          ld8_f32(sC + r * CP + c8, v);
-          const uint4 uu = upre[w * CPT + q];
-          const uint32_t uw[4] = {uu.x, uu.y, uu.z, uu.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[2 * i] *= gelu_grad_f(H16<E>::lo(uw[i]));
-            v[2 * i + 1] *= gelu_grad_f(H16<E>::hi(uw[i]));
-          }
-          st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
-        }
-      }
-      __syncthreads();
-    }
-    return;
-  }
-  if constexpr (PRE_R) {
-#pragma unroll
-    for (int w = 0; w < WGM; ++w) {
-      float4 rnext[2 * CPT];
-      if (w + 1 < WGM) {
-#pragma unroll
-        for (int q = 0; q < CPT; ++q) load_r(w + 1, q, rnext[2 * q], rnext[2 * q + 1]);
-      }
-      stage_acc(w);
-#pragma unroll
-      for (int q = 0; q < CPT; ++q) {
-        const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
-        const long row = m0 + w * WTM + r, col = n0 + c8;
-        if (row < p.M_out && col < p.N) {
-          float v[8], b[8];
-          ld8_f32(sC + r * CP + c8, v);
-          if (p.bias) {
-            ld8_f32(p.bias + col, b);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] += b[i];
-          }
-          const float4 lo = rpre[2 * q], hi = rpre[2 * q + 1];
-          v[0] += lo.x; v[1] += lo.y; v[2] += lo.z; v[3] += lo.w;
-          v[4] += hi.x; v[5] += hi.y; v[6] += hi.z; v[7] += hi.w;
-          st8_f32(reinterpret_cast<float*>(p.C) + row * p.ldc + col, v);
-        }
-      }
-      if (w + 1 < WGM) {
-#pragma unroll
-        for (int q = 0; q < 2 * CPT; ++q) rpre[q] = rnext[q];
-      }
-      __syncthreads();
-    }
-    return;
-  }
-#pragma unroll 1
-  for (int w = 0; w < WGM; ++w) {
-    stage_acc(w);
-    for (int c = tid; c < WTM * BN / 8; c += NT) {
-      const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+
+  // The next unit's first loads land while this unit's outputs are written;
+  // epilogues that hold operands loaded ahead load a unit's first steps at
+  // its start instead (the registers would not hold both).
+  constexpr bool OVERLAP = !PRE_U && !PRE_R;
+  int round = 0;
+  int u = pipe_unit(0, blockIdx.x, nb);
+  if (OVERLAP && u < units) prologue(u);
+  for (; u < units; u = pipe_unit(++round, blockIdx.x, nb)) {
+    if (!OVERLAP) prologue(u);
+    int tm, tn, z, k_begin, k_end, nk;
+    pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
+    k_range(z, k_begin, k_end, nk);
+    const int m0 = tm * BM, n0 = tn * BN;
+    auto load_r = [&](int w, int q, float4& lo, float4& hi) {
+      const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
       const long row = m0 + w * WTM + r, col = n0 + c8;
       if (row < p.M_out && col < p.N) {
-        float v[8];
-        const float4 x0 = *reinterpret_cast<const float4*>(sC + r * CP + c8);
-        const float4 x1 = *reinterpret_cast<const float4*>(sC + r * CP + c8 + 4);
-        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-        epilogue8<EPI, TC, E>(p, row, col, v, z);
+        lo = *reinterpret_cast<const float4*>(p.R + row * p.ldr + col);
+        hi = *reinterpret_cast<const float4*>(p.R + row * p.ldr + col + 4);
+      } else {
+        lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    if constexpr (PRE_R) {
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) load_r(0, q, rpre[2 * q], rpre[2 * q + 1]);
+    }
+    if constexpr (PRE_U) {
+#pragma unroll
+      for (int w = 0; w < WGM; ++w)
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+          const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+          const long row = m0 + w * WTM + r, col = n0 + c8;
+          upre[w * CPT + q] =
+              (row < p.M_out && col < p.N)
+                  ? *reinterpret_cast<const uint4*>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col)
+                  : make_uint4(0, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    auto kstep = [&](int it) { return k_begin + min(it, max(nk - 1, 0)) * kBK; };
+    la.store(ra[0], sA[0], tid);
+    lb.store(rb[0], sB[0], tid);
+    __syncthreads();
+
+    auto step = [&](auto P_, int it) {
+      constexpr int P = decltype(P_)::value;
+      la.load(ra[P], kstep(it + 2), k_end);
+      lb.load(rb[P], kstep(it + 2), k_end);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[0][i] = la.frag(sA[P], wm * WTM + i * 32, 0, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[0][j] = lb.frag(sB[P], wn * WTN + j * 32, 0, lane);
+#pragma unroll
+      for (int ks = 0; ks < kBK / 16; ++ks) {
+        const int f = ks & 1;
+        if (ks + 1 < kBK / 16) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) af[f ^ 1][i] = la.frag(sA[P], wm * WTM + i * 32, ks + 1, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bfr[f ^ 1][j] = lb.frag(sB[P], wn * WTN + j * 32, ks + 1, lane);
+        }
+        // keep the reads of k-step ks+1 ahead of the MFMAs of k-step ks
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = mfma32<E>(af[f][i], bfr[f][j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      la.store(ra[P ^ 1], sA[P ^ 1], tid);
+      lb.store(rb[P ^ 1], sB[P ^ 1], tid);
+      __syncthreads();
+    };
+    // Whole pairs in the loop and an odd last step after it: with no path
+    // from the middle of a pair back to the loop head, the wait-count
+    // analysis sees only the set being refilled as in flight at the head,
+    // instead of waiting for every outstanding load there.
+    int it = 0;
+    for (; it + 1 < nk; it += 2) {
+      step(std::integral_constant<int, 0>{}, it);
+      step(std::integral_constant<int, 1>{}, it + 1);
+    }
+    if (it < nk) step(std::integral_constant<int, 0>{}, it);
+
+    const int un = pipe_unit(round + 1, blockIdx.x, nb);
+    if (OVERLAP && un < units) prologue(un);
+
+    // Epilogue through LDS: the wave row w (WGN wavefronts, WTM rows) writes
+    // its fp32 accumulators to LDS (row pitch BN + 4 floats), then all
+    // threads walk that WTM x BN region in 8-column chunks, so bias, residual
+    // and GELU operands are read and results written with 16- and 32-byte
+    // accesses. Accumulator element e of tile (i, j): row (e/4)*8 +
+    // (lane/32)*4 + e%4, column lane%32.
+    auto stage_acc = [&](int w) {
+      if (wm == w) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int r = i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+              const int c = wn * WTN + j * 32 + (lane & 31);
+              sC[r * CP + c] = acc[i][j][e];
+            }
+      }
+      __syncthreads();
+    };
+    if constexpr (PRE_U) {
+#pragma unroll
+      for (int w = 0; w < WGM; ++w) {
+        stage_acc(w);
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+          const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+          const long row = m0 + w * WTM + r, col = n0 + c8;
+          if (row < p.M_out && col < p.N) {
+            float v[8];
+            ld8_f32(sC + r * CP + c8, v);
+            const uint4 uu = upre[w * CPT + q];
+            const uint32_t uw[4] = {uu.x, uu.y, uu.z, uu.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[2 * i] *= gelu_grad_f(H16<E>::lo(uw[i]));
+              v[2 * i + 1] *= gelu_grad_f(H16<E>::hi(uw[i]));
+            }
+            st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
+          }
+        }
+        __syncthreads();
+      }
+    } else if constexpr (PRE_R) {
+#pragma unroll
+      for (int w = 0; w < WGM; ++w) {
+        float4 rnext[2 * CPT];
+        if (w + 1 < WGM) {
+#pragma unroll
+          for (int q = 0; q < CPT; ++q) load_r(w + 1, q, rnext[2 * q], rnext[2 * q + 1]);
+        }
+        stage_acc(w);
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+          const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+          const long row = m0 + w * WTM + r, col = n0 + c8;
+          if (row < p.M_out && col < p.N) {
+            float v[8], b[8];
+            ld8_f32(sC + r * CP + c8, v);
+            if (p.bias) {
+              ld8_f32(p.bias + col, b);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) v[i] += b[i];
+            }
+            const float4 lo = rpre[2 * q], hi = rpre[2 * q + 1];
+            v[0] += lo.x; v[1] += lo.y; v[2] += lo.z; v[3] += lo.w;
+            v[4] += hi.x; v[5] += hi.y; v[6] += hi.z; v[7] += hi.w;
+            st8_f32(reinterpret_cast<float*>(p.C) + row * p.ldc + col, v);
+          }
+        }
+        if (w + 1 < WGM) {
+#pragma unroll
+          for (int q = 0; q < 2 * CPT; ++q) rpre[q] = rnext[q];
+        }
+        __syncthreads();
+      }
+    } else {
+#pragma unroll 1
+      for (int w = 0; w < WGM; ++w) {
+        stage_acc(w);
+        for (int c = tid; c < WTM * BN / 8; c += NT) {
+          const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+          const long row = m0 + w * WTM + r, col = n0 + c8;
+          if (row < p.M_out && col < p.N) {
+            float v[8];
+            ld8_f32(sC + r * CP + c8, v);
+            epilogue8<EPI, TC, E>(p, row, col, v, z);
+          }
+        }
+        __syncthreads();
       }
     }
-    __syncthreads();
   }
 }
 
@@ -782,28 +812,6 @@ __global__ void __launch_bounds__(256) splitk_reduce4_kernel(GemmArgs p, const f
   }
 }
 
-// Work unit u -> (tile m, tile n, K slice z). Units are numbered slice-major
-// and, inside a slice, in groups of GM m-tiles walked n-tile by n-tile. Block
-// b runs on XCD b % 8; the 32 blocks of one XCD take 32 consecutive units per
-// round, so the panels they share stay in that XCD's L2.
-__device__ __forceinline__ int pipe_unit(int round, int b, int nblocks) {
-  const int xcd = b & 7, local = b >> 3;
-  const int per_xcd = nblocks >> 3;  // nblocks is a multiple of 8
-  return round * nblocks + xcd * per_xcd + local;
-}
-__device__ __forceinline__ void pipe_tile(int u, int tiles_m, int tiles_n, int& tm, int& tn, int& z) {
-  const int tiles = tiles_m * tiles_n;
-  z = u / tiles;
-  const int t = u - z * tiles;
-  constexpr int GM = 8;
-  const int per_group = GM * tiles_n;
-  const int group = t / per_group, first_m = group * GM;
-  const int gsize = min(tiles_m - first_m, GM);
-  const int in = t - group * per_group;
-  tm = first_m + in % gsize;
-  tn = in / gsize;
-}
-
 template <int BM, int BN, int WGM, int WGN, int BK, int S, int OCC, bool AK, bool BKC, int EPI, typename TC,
           typename E>
 __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
@@ -1059,9 +1067,18 @@ static void launch_pipe(const GemmArgs& a, int splits, hipStream_t s) {
 
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BKC, int EPI, typename TC, typename E>
 static void launch_small(const GemmArgs& a, int splits, hipStream_t s) {
-  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm16_kernel<BM, BN, WGM, WGN, AK, BKC, EPI, TC, E>), dim3(tiles, splits),
-                     dim3(WGM * WGN * 64), 0, s, a);
+  const int units = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * splits;
+  // Measured on the step's shapes: the GELU epilogue (two outputs, no loaded
+  // operand) and the split-K partials gain from a persistent grid (as many
+  // blocks as fit on the CUs at once), whose next-unit loads overlap the
+  // epilogue; the other epilogues run one block per unit.
+  constexpr bool persist = EPI == EPI_GELU || EPI == EPI_PARTIAL;
+  constexpr int per_cu = (160 * 1024) / (2 * 2 * 64 * (BM + BN)) > 0 ? (160 * 1024) / (2 * 2 * 64 * (BM + BN)) : 1;
+  int nb = persist ? device_cus() * per_cu : units;
+  if (units < nb) nb = units;
+  nb = (nb + 7) / 8 * 8;  // whole XCD rounds
+  hipLaunchKernelGGL((gemm16_kernel<BM, BN, WGM, WGN, AK, BKC, EPI, TC, E>), dim3(nb), dim3(WGM * WGN * 64), 0, s,
+                     a, units);
 }
 
 // One launch of configuration cfg with the epilogue EPI and output type TC.
