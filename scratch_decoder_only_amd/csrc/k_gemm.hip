@@ -726,7 +726,7 @@ struct PTile {
   }
 };
 
-// One LDS array per pipeline stage (a distinct object per I).
+// One LDS array per pipeline stage and operand (a distinct object per I).
 template <int I, int ELEMS>
 __device__ __forceinline__ bf16* lds_stage() {
   __shared__ __attribute__((aligned(1024))) bf16 buf[ELEMS];
@@ -823,7 +823,6 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
   static_assert(S >= 2, "at least two stages");
   using LA = PTile<BM, AK, NT, BK>;
   using LB = PTile<BN, BKC, NT, BK>;
-  constexpr int SE = LA::ELEMS + LB::ELEMS;  // bf16 elements per stage: A tile, then B tile
   constexpr int NLD = LA::NI + LB::NI;       // load instructions per wavefront per K step
   constexpr int KS = BK / 16;
 
@@ -835,7 +834,10 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
 
   LA la;
   LB lb;
-  auto stage = [](auto I_) -> bf16* { return lds_stage<decltype(I_)::value, SE>(); };
+  // A and B tiles of a stage are separate arrays: the compiler then keeps
+  // the direct loads into one apart from the reads of the others.
+  auto stage = [](auto I_) -> bf16* { return lds_stage<2 * decltype(I_)::value, LA::ELEMS>(); };
+  auto stage_b = [](auto I_) -> bf16* { return lds_stage<2 * decltype(I_)::value + 1, LB::ELEMS>(); };
   auto k_range = [&](int z, int& kb, int& ke) {
     kb = z * p.k_split;
     ke = min(p.K, kb + p.k_split);
@@ -852,7 +854,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
       constexpr int I = decltype(I_)::value;
       if (I < nk) {
         la.load(stage(I_), kb + I * BK, ke);
-        lb.load(stage(I_) + LA::ELEMS, kb + I * BK, ke);
+        lb.load(stage_b(I_), kb + I * BK, ke);
       }
     });
   };
@@ -885,7 +887,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
           else wait_vmcnt<0>();
           lds_barrier();
           const bf16* sa = stage(I_);
-          const bf16* sb = sa + LA::ELEMS;
+          const bf16* sb = stage_b(I_);
           bf16x8_t af[2][TM], bfr[2][TN];
 #pragma unroll
           for (int i = 0; i < TM; ++i) af[0][i] = LA::frag(sa, wm * WTM + i * 32, 0, lane);
@@ -901,9 +903,10 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
               // into a stage nobody reads), so no branch splits the schedule
               constexpr int NX = (I + S - 1) % S;
               bf16* sx = stage(std::integral_constant<int, NX>{});
+              bf16* sxb = stage_b(std::integral_constant<int, NX>{});
               const int kn = it + S - 1 < nk ? kb + (it + S - 1) * BK : ke;
               if (ks == 0) la.load(sx, kn, ke);
-              else lb.load(sx + LA::ELEMS, kn, ke);
+              else lb.load(sxb, kn, ke);
             }
             if (ks + 1 < KS) {
 #pragma unroll

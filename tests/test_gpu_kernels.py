@@ -118,6 +118,57 @@ def test_gemm_epilogues(sd, prec, epi, split):
         assert rel(host(C), oracle.linear_fwd(X, W) * oracle.gelu_grad(u)) <= tol(prec, False)
 
 
+# Shapes with one dimension of 16384 or more run on the persistent 256 x 256
+# kernel (the others on the 128 x 128 one): every layout, ragged tails in all
+# three dimensions, with and without a K split.
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("layout", ["fwd", "dx", "dw"])
+@pytest.mark.parametrize("MNK", [(16392, 264, 200), (136, 16520, 96), (264, 136, 16400)])
+@pytest.mark.parametrize("split", [0, 3])
+def test_gemm_layouts_wide(sd, prec, layout, MNK, split):
+    test_gemm_layouts(sd, prec, layout, MNK, split)
+
+
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("epi", ["store", "resid", "gelu", "dgelu"])
+def test_gemm_epilogues_wide(sd, prec, epi):
+    t = torch()
+    M, N, K = 16392, 200, 136
+    rng = np.random.default_rng(23 + prec)
+    print(f"gemm wide epilogue prec={prec} epi={epi}", flush=True)
+    X, W = _operands(rng, prec, (M, K), (N, K), scale=0.3)
+    bias = rng.standard_normal(N).astype(np.float32)
+    adt = act_dtype(prec)
+    lin = oracle.linear_fwd(X, W, bias)
+    args = dict(bias=dev(bias))
+    if epi == "store":
+        C = t.zeros((M, N), dtype=adt, device="cuda")
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, C, N, sd.EPI_STORE, **args)
+        t.cuda.synchronize()
+        assert rel(host(C), lin) <= tol(prec, False)
+    elif epi == "resid":
+        R = rng.standard_normal((M, N)).astype(np.float32)
+        C = t.zeros((M, N), dtype=t.float32, device="cuda")
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, C, N, sd.EPI_RESID, R=dev(R), ldr=N, **args)
+        t.cuda.synchronize()
+        assert rel(host(C), R + lin) <= tol(prec, True)
+    elif epi == "gelu":
+        U = t.zeros((M, N), dtype=adt, device="cuda")
+        Aout = t.zeros((M, N), dtype=adt, device="cuda")
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, U, N, sd.EPI_GELU, aux=Aout, ld_aux=N, **args)
+        t.cuda.synchronize()
+        assert rel(host(U), lin) <= tol(prec, False)
+        assert rel(host(Aout), oracle.gelu(lin)) <= tol(prec, False)
+    else:
+        u = exact(rng.standard_normal((M, N)).astype(np.float32) * 2, prec)
+        C = t.zeros((M, N), dtype=adt, device="cuda")
+        args.pop("bias")
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, C, N, sd.EPI_DGELU, aux=act(u, prec),
+                ld_aux=N, **args)
+        t.cuda.synchronize()
+        assert rel(host(C), oracle.linear_fwd(X, W) * oracle.gelu_grad(u)) <= tol(prec, False)
+
+
 def test_gemm_output_row_limit(sd):
     """Rows >= M_out are computed but never stored (the padded vocabulary)."""
     t = torch()
