@@ -942,29 +942,76 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
         }
       });
     }
-    // every wavefront is done reading the stages: start the next unit's loads,
-    // then write this unit's outputs while they land
+    // Outputs through LDS. Every wavefront is done reading the stages; each
+    // owns a 32 x 64 fp32 region of the stage-1 arrays. Pass i writes
+    // accumulator rows i*32 .. +31 (element e of tile (i, j): row lane % 32,
+    // column j*32 + (e/4)*8 + (lane/32)*4 + e%4), 16-byte chunk c of row r at
+    // c ^ (r % 16), reads them back with consecutive lanes on consecutive
+    // columns of a row and stores them, so each store instruction writes
+    // whole row segments (4 rows x 256 B of fp32, or 8 rows x 128 B of 16-bit
+    // values) instead of 16 bytes in each of 32 rows. The next unit's first
+    // loads (into stage 0) are issued after the last pass's region reads and
+    // overlap its stores: no direct load may be in flight while the regions
+    // are used, or the compiler's wait counting holds the reads until the
+    // loads land.
     lds_barrier();
+    static_assert(WTN == 64, "epilogue regions hold 64 columns");
+    constexpr int NW = WGM * WGN, REG = 32 * WTN;
+    static_assert((NW / 2) * REG * 4 <= LA::ELEMS * 2 && (NW / 2) * REG * 4 <= LB::ELEMS * 2,
+                  "epilogue regions fit in stage 1");
+    constexpr bool H = sizeof(TC) == 2;  // 16-bit outputs: 8 columns per lane, else 4
+    constexpr int NQ = H ? 4 : 8;        // store chunks per lane and pass
     const int un = pipe_unit(round + 1, blockIdx.x, nb);
-    if (un < units) prologue(un);
-
-    // accumulator element e of tile (i, j): row lane % 32, column
-    // (e / 4) * 8 + (lane / 32) * 4 + e % 4
+    const long col0 = (long)tn * BN + wn * WTN;
+    // (the two halves of the wavefronts take the two arrays in separate code
+    // paths, so each access has one known LDS object)
+    auto epilogue_via = [&](float* reg) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const long row = (long)tm * BM + wm * WTM + i * 32 + (lane & 31);
-      if (row >= p.M_out) continue;
+      for (int i = 0; i < TM; ++i) {
+        const int rw = lane & 31;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const long col = (long)tn * BN + wn * WTN + j * 32 + g * 8 + (lane >> 5) * 4;
-          if (col < p.N) {
-            f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            epilogue4<EPI, TC, E>(p, row, col, v, z);
+          for (int g = 0; g < 4; ++g) {
+            const int c = j * 8 + g * 2 + (lane >> 5);
+            *reinterpret_cast<f32x4_t*>(reg + rw * 64 + ((c ^ (rw & 15)) << 2)) =
+                f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          }
+        f32x4_t out[H ? 2 * NQ : NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          if constexpr (H) {
+            const int r = q * 8 + (lane >> 3), c = (lane & 7) * 2;
+            out[2 * q] = *reinterpret_cast<const f32x4_t*>(reg + r * 64 + ((c ^ (r & 15)) << 2));
+            out[2 * q + 1] = *reinterpret_cast<const f32x4_t*>(reg + r * 64 + (((c + 1) ^ (r & 15)) << 2));
+          } else {
+            const int r = q * 4 + (lane >> 4), c = lane & 15;
+            out[q] = *reinterpret_cast<const f32x4_t*>(reg + r * 64 + ((c ^ (r & 15)) << 2));
           }
         }
-    }
+        const long row0 = (long)tm * BM + wm * WTM + i * 32;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          if constexpr (H) {
+            const int r = q * 8 + (lane >> 3), c = (lane & 7) * 2;
+            const long row = row0 + r, col = col0 + c * 4;
+            if (row < p.M_out && col < p.N) {
+              const f32x4_t lo = out[2 * q], hi = out[2 * q + 1];
+              float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              epilogue8<EPI, TC, E>(p, row, col, v, z);
+            }
+          } else {
+            const int r = q * 4 + (lane >> 4), c = lane & 15;
+            const long row = row0 + r, col = col0 + c * 4;
+            if (row < p.M_out && col < p.N) epilogue4<EPI, TC, E>(p, row, col, out[q], z);
+          }
+        }
+      }
+    };
+    constexpr std::integral_constant<int, 1> I1{};
+    if (wave < NW / 2) epilogue_via(reinterpret_cast<float*>(stage(I1)) + wave * REG);
+    else epilogue_via(reinterpret_cast<float*>(stage_b(I1)) + (wave - NW / 2) * REG);
+    if (un < units) prologue(un);
   }
   // no direct load may still be writing LDS when the workgroup ends
   wait_vmcnt<0>();

@@ -13,44 +13,63 @@
 
 namespace lm {
 
-// NV float2 per lane: C = 128 * NV.
+// C = 128 * NV; a lane holds NV values in float4 chunks when NV is even
+// (16-byte accesses), else in float2 chunks. Chunk j of a lane covers
+// columns W (lane + 64 j) .. + W - 1, W the chunk width.
 template <int NV, typename T>
 __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                      const float* __restrict__ b, int M, float eps,
                                                      T* __restrict__ y, float* __restrict__ mu_out,
                                                      float* __restrict__ rstd_out) {
   constexpr int C = 128 * NV;
+  constexpr int W = NV % 2 == 0 ? 4 : 2;  // floats per chunk
+  constexpr int NC = C / (64 * W);        // chunks per lane
   const int lane = threadIdx.x & 63;
   const long m = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
-  const float2* xr = reinterpret_cast<const float2*>(x + m * C);
-  float2 v[NV];
+  float v[NC][W];
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    v[j] = xr[lane + 64 * j];
-    s += v[j].x + v[j].y;
+  for (int j = 0; j < NC; ++j) {
+    const long o = m * C + (long)W * (lane + 64 * j);
+    if constexpr (W == 4) {
+      const float4 t = *reinterpret_cast<const float4*>(x + o);
+      v[j][0] = t.x; v[j][1] = t.y; v[j][2] = t.z; v[j][3] = t.w;
+    } else {
+      const float2 t = *reinterpret_cast<const float2*>(x + o);
+      v[j][0] = t.x; v[j][1] = t.y;
+    }
+#pragma unroll
+    for (int e = 0; e < W; ++e) s += v[j][e];
   }
   const float mu = wave_sum(s) * (1.0f / C);
   float q = 0.f;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    float a = v[j].x - mu, c = v[j].y - mu;
-    q += a * a + c * c;
-  }
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      const float a = v[j][e] - mu;
+      q += a * a;
+    }
   const float var = wave_sum(q) * (1.0f / C);
   const float r = 1.0f / sqrtf(var + eps);
-  const float2* g2 = reinterpret_cast<const float2*>(g);
-  const float2* b2 = reinterpret_cast<const float2*>(b);
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    int c = 2 * (lane + 64 * j);
-    float2 gg = g2[lane + 64 * j], bb = b2[lane + 64 * j];
-    const float y0 = (v[j].x - mu) * r * gg.x + bb.x, y1 = (v[j].y - mu) * r * gg.y + bb.y;
-    if constexpr (sizeof(T) == 2)  // two adjacent 16-bit values in one 4-byte store
-      reinterpret_cast<uint32_t*>(y)[(m * C + c) >> 1] = H16<T>::pack(y0, y1);
-    else
-      reinterpret_cast<float2*>(y)[(m * C + c) >> 1] = make_float2(y0, y1);
+  for (int j = 0; j < NC; ++j) {
+    const int c = W * (lane + 64 * j);
+    float o[W];
+#pragma unroll
+    for (int e = 0; e < W; ++e) o[e] = (v[j][e] - mu) * r * g[c + e] + b[c + e];
+    if constexpr (sizeof(T) == 2) {  // adjacent 16-bit values packed in pairs
+      if constexpr (W == 4)
+        *reinterpret_cast<uint2*>(y + m * C + c) = make_uint2(H16<T>::pack(o[0], o[1]), H16<T>::pack(o[2], o[3]));
+      else
+        *reinterpret_cast<uint32_t*>(y + m * C + c) = H16<T>::pack(o[0], o[1]);
+    } else {
+      if constexpr (W == 4)
+        *reinterpret_cast<float4*>(y + m * C + c) = make_float4(o[0], o[1], o[2], o[3]);
+      else
+        *reinterpret_cast<float2*>(y + m * C + c) = make_float2(o[0], o[1]);
+    }
   }
   if (lane == 0) {
     mu_out[m] = mu;
@@ -206,54 +225,70 @@ template void launch_ln_bwd<f16>(const float*, const float*, const float*, const
                                  const float*, float*, f16*, float*, float*, float*, hipStream_t);
 
 // out[c] = sum over p < P of part[p][c] in a fixed order: a block covers 16
-// columns with 16 row groups; thread (c, r) sums p = r, r + 16, ... for its
-// column, then the 16 group sums are added in r order. Up to three vectors at
-// once (the dg, db and output-column partials of one LayerNorm); pb/pc and
-// ob/oc may be null.
-__global__ void __launch_bounds__(256) colsum_partials_kernel(const float* __restrict__ pa, const float* __restrict__ pb,
+// columns with 64 row groups (a wavefront reads 4 rows x 64 bytes); thread
+// (c, r) sums p = r, r + 64, ... for its column, then the group sums are
+// added in r order (eight runs of eight, then the eight run sums). Up to
+// three vectors at once (the dg, db and output-column partials of one
+// LayerNorm); pb/pc and ob/oc may be null. The sums are latency-bound (a few
+// MB, just written): many wavefronts, each with its loads in flight together.
+constexpr int kPartCols = 16, kPartGroups = 64;
+__global__ void __launch_bounds__(1024) colsum_partials_kernel(const float* __restrict__ pa, const float* __restrict__ pb,
                                                               const float* __restrict__ pc, int P, int C,
                                                               float* __restrict__ oa, float* __restrict__ ob,
                                                               float* __restrict__ oc) {
-  __shared__ float sa[16][17], sb[16][17], sc[16][17];
-  const int cc = threadIdx.x & 15, r = threadIdx.x >> 4;
-  const int c = blockIdx.x * 16 + cc;
+  __shared__ float sm[3][kPartGroups][kPartCols];
+  __shared__ float sr[3][8][kPartCols];
+  const int cc = threadIdx.x % kPartCols, r = threadIdx.x / kPartCols;
+  const int c = blockIdx.x * kPartCols + cc;
   float a = 0.f, b = 0.f, d = 0.f;
   if (c < C) {
     int p = r;
-    // batches of 16 partial rows: loads in flight together (the sums are
-    // latency-bound), added in order
-    for (; p + 15 * 16 < P; p += 16 * 16) {
-      float va[16], vb[16], vc[16];
+    for (; p + 7 * kPartGroups < P; p += 8 * kPartGroups) {
+      float va[8], vb[8], vc[8];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const long o = (long)(p + 16 * u) * C + c;
+      for (int u = 0; u < 8; ++u) {
+        const long o = (long)(p + kPartGroups * u) * C + c;
         va[u] = pa[o];
         vb[u] = pb ? pb[o] : 0.f;
         vc[u] = pc ? pc[o] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < 8; ++u) {
         a += va[u];
         b += vb[u];
         d += vc[u];
       }
     }
-    for (; p < P; p += 16) {
+    for (; p < P; p += kPartGroups) {
       a += pa[(long)p * C + c];
       if (pb) b += pb[(long)p * C + c];
       if (pc) d += pc[(long)p * C + c];
     }
   }
-  sa[r][cc] = a;
-  sb[r][cc] = b;
-  sc[r][cc] = d;
+  sm[0][r][cc] = a;
+  sm[1][r][cc] = b;
+  sm[2][r][cc] = d;
+  __syncthreads();
+  if (r < 8) {
+    float ta = 0.f, tb = 0.f, td = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ta += sm[0][r * 8 + k][cc];
+      tb += sm[1][r * 8 + k][cc];
+      td += sm[2][r * 8 + k][cc];
+    }
+    sr[0][r][cc] = ta;
+    sr[1][r][cc] = tb;
+    sr[2][r][cc] = td;
+  }
   __syncthreads();
   if (r == 0 && c < C) {
     float ta = 0.f, tb = 0.f, td = 0.f;
-    for (int k = 0; k < 16; ++k) {
-      ta += sa[k][cc];
-      tb += sb[k][cc];
-      td += sc[k][cc];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ta += sr[0][k][cc];
+      tb += sr[1][k][cc];
+      td += sr[2][k][cc];
     }
     oa[c] = ta;
     if (ob) ob[c] = tb;
@@ -263,7 +298,9 @@ __global__ void __launch_bounds__(256) colsum_partials_kernel(const float* __res
 
 void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob,
                             hipStream_t s, const float* pc, float* oc) {
-  hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + 15) / 16), dim3(256), 0, s, pa, pb, pc, P, C, oa, ob, oc);
+  static_assert(kPartCols * kPartGroups == 1024 && kPartGroups == 64, "block shape");
+  hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + kPartCols - 1) / kPartCols), dim3(1024), 0, s, pa, pb, pc, P,
+                     C, oa, ob, oc);
 }
 
 // Column sums of an [M, N] matrix (bias gradients), N a multiple of 4. Stage
