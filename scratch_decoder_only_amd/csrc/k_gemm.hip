@@ -949,11 +949,14 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
     // c ^ (r % 16), reads them back with consecutive lanes on consecutive
     // columns of a row and stores them, so each store instruction writes
     // whole row segments (4 rows x 256 B of fp32, or 8 rows x 128 B of 16-bit
-    // values) instead of 16 bytes in each of 32 rows. The next unit's first
-    // loads (into stage 0) are issued after the last pass's region reads and
-    // overlap its stores: no direct load may be in flight while the regions
-    // are used, or the compiler's wait counting holds the reads until the
-    // loads land.
+    // values) instead of 16 bytes in each of 32 rows. The last K steps issue
+    // loads past the end of K (zeros into a stage nobody reads, possibly
+    // stage 1): every wavefront waits for its own before the barrier, so no
+    // direct load is still writing the regions. The next unit's first loads
+    // (into stage 0) are issued after the outputs: issued before, they would
+    // be in flight during the region reads, which the compiler's wait
+    // counting would then hold until the loads land.
+    wait_vmcnt<0>();
     lds_barrier();
     static_assert(WTN == 64, "epilogue regions hold 64 columns");
     constexpr int NW = WGM * WGN, REG = 32 * WTN;
