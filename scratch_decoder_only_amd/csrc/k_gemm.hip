@@ -850,6 +850,32 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
     kb = z * p.k_split;
     ke = min(p.K, kb + p.k_split);
   };
+  // Output chunks of a lane in epilogue pass i (accumulator rows i*32 ..
+  // +31 of the wave tile): chunk q is row q*RPQ + lane / (64 / RPQ), columns
+  // from (lane % (64 / RPQ)) * CW, CW = 8 for 16-bit outputs, 4 for fp32.
+  constexpr bool H = sizeof(TC) == 2;
+  constexpr int CW = H ? 8 : 4, LPR = 64 / CW, RPQ = 64 / LPR, NQ = 32 / RPQ;
+  // The residual or GELU input is loaded ahead into registers (when the wave
+  // tile is small enough to keep them): the passes i < PRE_I with the unit's
+  // first K steps, so their latency hides behind the K loop, the others at
+  // the start of the epilogue. (Two passes of the GELU input take 32 VGPRs,
+  // one pass of the fp32 residual as many.)
+  constexpr bool PRE = (EPI == EPI_RESID || EPI == EPI_DGELU) && TM <= 2;
+  constexpr int PRE_I = EPI == EPI_DGELU ? TM : 1;
+  uint4 pre[PRE ? TM : 1][PRE ? NQ : 1];
+  auto load_pre = [&](int tm, int tn, int i) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const long row = (long)tm * BM + wm * WTM + i * 32 + q * RPQ + lane / LPR;
+      const long col = (long)tn * BN + wn * WTN + (lane % LPR) * CW;
+      const bool ok = row < p.M_out && col < p.N;
+      if constexpr (EPI == EPI_DGELU)  // 8 16-bit values
+        pre[i][q] = ok ? *reinterpret_cast<const uint4*>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col)
+                       : make_uint4(0, 0, 0, 0);
+      else  // 4 fp32 values
+        pre[i][q] = ok ? *reinterpret_cast<const uint4*>(p.R + row * p.ldr + col) : make_uint4(0, 0, 0, 0);
+    }
+  };
   // set up the loaders of unit u and issue its first S - 1 K steps
   auto prologue = [&](int u) {
     int tm, tn, z, kb, ke;
@@ -865,6 +891,10 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
         lb.load(stage_b(I_), kb + I * BK, ke);
       }
     });
+    if constexpr (PRE) {
+#pragma unroll
+      for (int i = 0; i < PRE_I; ++i) load_pre(tm, tn, i);
+    }
   };
 
   f32x16_t acc[TM][TN];
@@ -958,12 +988,14 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
     // counting would then hold until the loads land.
     wait_vmcnt<0>();
     lds_barrier();
+    if constexpr (PRE) {
+#pragma unroll
+      for (int i = PRE_I; i < TM; ++i) load_pre(tm, tn, i);
+    }
     static_assert(WTN == 64, "epilogue regions hold 64 columns");
     constexpr int NW = WGM * WGN, REG = 32 * WTN;
     static_assert((NW / 2) * REG * 4 <= LA::ELEMS * 2 && (NW / 2) * REG * 4 <= LB::ELEMS * 2,
                   "epilogue regions fit in stage 1");
-    constexpr bool H = sizeof(TC) == 2;  // 16-bit outputs: 8 columns per lane, else 4
-    constexpr int NQ = H ? 4 : 8;        // store chunks per lane and pass
     const int un = pipe_unit(round + 1, blockIdx.x, nb);
     const long col0 = (long)tn * BN + wn * WTN;
     // (the two halves of the wavefronts take the two arrays in separate code
@@ -983,30 +1015,35 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
         f32x4_t out[H ? 2 * NQ : NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          if constexpr (H) {
-            const int r = q * 8 + (lane >> 3), c = (lane & 7) * 2;
-            out[2 * q] = *reinterpret_cast<const f32x4_t*>(reg + r * 64 + ((c ^ (r & 15)) << 2));
+          const int r = q * RPQ + lane / LPR, c = (lane % LPR) * (CW / 4);
+          out[H ? 2 * q : q] = *reinterpret_cast<const f32x4_t*>(reg + r * 64 + ((c ^ (r & 15)) << 2));
+          if constexpr (H)
             out[2 * q + 1] = *reinterpret_cast<const f32x4_t*>(reg + r * 64 + (((c + 1) ^ (r & 15)) << 2));
-          } else {
-            const int r = q * 4 + (lane >> 4), c = lane & 15;
-            out[q] = *reinterpret_cast<const f32x4_t*>(reg + r * 64 + ((c ^ (r & 15)) << 2));
-          }
         }
         const long row0 = (long)tm * BM + wm * WTM + i * 32;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          if constexpr (H) {
-            const int r = q * 8 + (lane >> 3), c = (lane & 7) * 2;
-            const long row = row0 + r, col = col0 + c * 4;
-            if (row < p.M_out && col < p.N) {
-              const f32x4_t lo = out[2 * q], hi = out[2 * q + 1];
-              float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              epilogue8<EPI, TC, E>(p, row, col, v, z);
-            }
+          const long row = row0 + q * RPQ + lane / LPR, col = col0 + (lane % LPR) * CW;
+          if (row >= p.M_out || col >= p.N) continue;
+          if constexpr (PRE && EPI == EPI_DGELU) {
+            const f32x4_t lo = out[2 * q], hi = out[2 * q + 1];
+            const uint4 u = pre[i][q];
+            float v[8] = {lo[0] * gelu_grad_f(H16<E>::lo(u.x)), lo[1] * gelu_grad_f(H16<E>::hi(u.x)),
+                          lo[2] * gelu_grad_f(H16<E>::lo(u.y)), lo[3] * gelu_grad_f(H16<E>::hi(u.y)),
+                          hi[0] * gelu_grad_f(H16<E>::lo(u.z)), hi[1] * gelu_grad_f(H16<E>::hi(u.z)),
+                          hi[2] * gelu_grad_f(H16<E>::lo(u.w)), hi[3] * gelu_grad_f(H16<E>::hi(u.w))};
+            st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
+          } else if constexpr (PRE && EPI == EPI_RESID) {
+            f32x4_t v = out[q];
+            if (p.bias) v += *reinterpret_cast<const f32x4_t*>(p.bias + col);
+            v += __builtin_bit_cast(f32x4_t, pre[i][q]);
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + row * p.ldc + col) = v;
+          } else if constexpr (H) {
+            const f32x4_t lo = out[2 * q], hi = out[2 * q + 1];
+            float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            epilogue8<EPI, TC, E>(p, row, col, v, z);
           } else {
-            const int r = q * 4 + (lane >> 4), c = lane & 15;
-            const long row = row0 + r, col = col0 + c * 4;
-            if (row < p.M_out && col < p.N) epilogue4<EPI, TC, E>(p, row, col, out[q], z);
+            epilogue4<EPI, TC, E>(p, row, col, out[q], z);
           }
         }
       }
@@ -1081,13 +1118,14 @@ static int pick_cfg(const GemmOp& op) {
   // wins on the vocabulary projection's forward (very wide N), its input
   // gradient (very long K) and its weight gradient (very tall M), and on the
   // MLP weight gradients (3072 x 768 outputs over K = 8192); 128 x 128 at two
-  // blocks per CU everywhere else: the direct-load persistent kernel (7-11%
-  // faster) unless the epilogue loads an operand (residual, GELU input), which
-  // the register-staged kernel loads ahead of the K loop's end.
+  // blocks per CU everywhere else: the direct-load persistent kernel (6-12%
+  // faster), except for the residual epilogue, whose fp32 operand the
+  // register-staged kernel loads ahead more fully (the persistent one holds
+  // only the first of its two passes through the K loop; 7% slower).
   const int mn_max = op.M > op.N ? op.M : op.N, mn_min = op.M < op.N ? op.M : op.N;
   if (op.M >= 16384 || op.N >= 16384 || op.K >= 16384) return kCfgPipe;
   if (op.K >= 8192 && mn_max >= 3072 && mn_max <= 4096 && mn_min <= 1024) return kCfgPipe;
-  if (op.epi == EPI_RESID || op.epi == EPI_DGELU) return kCfgSmall;
+  if (op.epi == EPI_RESID) return kCfgSmall;
   return kCfgPipe128;
 }
 
