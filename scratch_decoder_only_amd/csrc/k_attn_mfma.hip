@@ -178,9 +178,14 @@ __device__ __forceinline__ void item_rows(const AttnArgs& a, bool queries, int& 
   r0 = (queries ? nt - 1 - k : k) * 128;
 }
 
+// Occupancy: each kernel is compiled for as many wavefronts per SIMD as its
+// registers allow without spilling (forward and dQ 3, dK/dV 2); left to
+// itself the compiler took more registers (1-2 wavefronts per SIMD) and
+// parked values in the accumulation registers, which measured 4-5% slower.
+
 // ----------------------------------------------------------------- forward
 template <int D, typename E>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) attn_fwd_kernel(AttnArgs a) {
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][RowTile<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][RowTile<D>::ELEMS];
@@ -315,7 +320,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------ dQ pass
 template <int D, typename E>
-__global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) attn_dq_kernel(AttnArgs a) {
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][RowTile<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][RowTile<D>::ELEMS];
@@ -429,7 +434,7 @@ __global__ void __launch_bounds__(256) attn_dq_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------- dK / dV pass
 template <int D, typename E>
-__global__ void __launch_bounds__(256) attn_dkv_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_dkv_kernel(AttnArgs a) {
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sQ[2][RowTile<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 sdO[2][RowTile<D>::ELEMS];
