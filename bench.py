@@ -69,6 +69,7 @@ TRAFFIC_SYMBOLS = {
     "gemm_head_fwd": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, true, true, 0,",
     "gemm_fc1_fwd": "gemm16_pipe_kernel<128, 128, 2, 2, 64, 2, 2, true, true, 2,",
     "gemm_fc2_bwd_dx": "gemm16_pipe_kernel<128, 128, 2, 2, 64, 2, 2, true, false, 3,",
+    "adamw": "adamw_kernel(",
     "attn_bwd_dkv": "attn_dkv_kernel<64>",
     "attn_fwd": "attn_fwd_kernel<64>",
 }

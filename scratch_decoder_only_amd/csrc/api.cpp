@@ -813,7 +813,8 @@ lm_status train_step(lm_model* m, const int32_t* tok, const int32_t* tgt, const 
   a.bc2 = (float)(1.0 - std::pow((double)opt->beta2, (double)opt->step));
   a.norm_scale = m->norm_scale; a.flags = m->flags;
   a.shadow = m->shadow; a.shadow_f16 = m->prec == 2;
-  Lr.run("adamw", 0, (m->h16 ? 34.0 : 32.0) * m->P, [&] { launch_adamw(a, s); });
+  // p, g, m, v read (16 B), p, m, v written (12 B), plus the 16-bit copy (2 B)
+  Lr.run("adamw", 0, (m->h16 ? 30.0 : 28.0) * m->P, [&] { launch_adamw(a, s); });
   Lr.run("misc", 0, 0, [&] { launch_write_flags(m->flags, stats, s); });
   return hip_status("train_step");
 }
