@@ -802,20 +802,22 @@ __global__ void __launch_bounds__(256) splitk_reduce4_kernel(GemmArgs p, const f
   const long slice = (long)p.M * part_ld;
   for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (long)gridDim.x * blockDim.x) {
     const long row = q / nq, col = (q - row * nq) * 4;
-    const float* src = part + row * part_ld + col;
-    f32x4_t acc = *reinterpret_cast<const f32x4_t*>(src);
+    // each partial is read once: nontemporal loads
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(part + row * part_ld + col);
+    const long sl4 = slice / 4;
+    f32x4_t acc = __builtin_nontemporal_load(src);
     int z = 1;
     for (; z + 3 < S; z += 4) {
-      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + z * slice);
-      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + (z + 1) * slice);
-      const f32x4_t c = *reinterpret_cast<const f32x4_t*>(src + (z + 2) * slice);
-      const f32x4_t d = *reinterpret_cast<const f32x4_t*>(src + (z + 3) * slice);
+      const f32x4_t a = __builtin_nontemporal_load(src + z * sl4);
+      const f32x4_t b = __builtin_nontemporal_load(src + (z + 1) * sl4);
+      const f32x4_t c = __builtin_nontemporal_load(src + (z + 2) * sl4);
+      const f32x4_t d = __builtin_nontemporal_load(src + (z + 3) * sl4);
       acc += a;
       acc += b;
       acc += c;
       acc += d;
     }
-    for (; z < S; ++z) acc += *reinterpret_cast<const f32x4_t*>(src + z * slice);
+    for (; z < S; ++z) acc += __builtin_nontemporal_load(src + z * sl4);
     epilogue4<EPI, TC, E>(p, row, col, acc, 0);
   }
 }

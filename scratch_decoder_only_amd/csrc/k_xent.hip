@@ -15,6 +15,18 @@
 
 namespace lm {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte nontemporal load and store: the logits are streamed through once
+// per pass (far more of them than the caches hold).
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st_nt16(void* p, uint4 u) {
+  __builtin_nontemporal_store(u32x4_t{u.x, u.y, u.z, u.w}, reinterpret_cast<u32x4_t*>(p));
+}
+
 template <typename T> struct Vec16 {  // 16-bit types (bf16, f16)
   static constexpr int N = 8;
   static __device__ __forceinline__ void load(const T* p, float* out) {
@@ -32,6 +44,12 @@ template <typename T> struct Vec16 {  // 16-bit types (bf16, f16)
     for (int i = 0; i < 4; ++i) w[i] = H16<T>::pack(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
+  static __device__ __forceinline__ void store_nt(T* p, const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = H16<T>::pack(v[2 * i], v[2 * i + 1]);
+    st_nt16(p, make_uint4(w[0], w[1], w[2], w[3]));
+  }
 };
 template <> struct Vec16<float> {
   static constexpr int N = 4;
@@ -41,6 +59,9 @@ template <> struct Vec16<float> {
   }
   static __device__ __forceinline__ void store(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  static __device__ __forceinline__ void store_nt(float* p, const float* v) {
+    st_nt16(p, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])));
   }
 };
 
@@ -169,7 +190,7 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
       const int v = threadIdx.x + q * 1024;
-      raw[q] = v < nvec ? *reinterpret_cast<const uint4*>(zr + (long)v * NV) : make_uint4(0, 0, 0, 0);
+      raw[q] = v < nvec ? ld_nt16(zr + (long)v * NV) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
@@ -220,7 +241,7 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
       if (valid && j < V) d = (__expf(x[i] - lse) - (j == t ? 1.f : 0.f)) * inv_n;
       x[i] = d;
     }
-    Vec16<T>::store(zr + (long)v * NV, x);
+    Vec16<T>::store_nt(zr + (long)v * NV, x);
   }
 }
 
