@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lm {
 
 typedef uint16_t bf16;  // storage of a bfloat16 value (upper half of an fp32)
@@ -115,5 +117,33 @@ __device__ __forceinline__ float gelu_grad_f(float u) {
   const float s = gelu_sigmoid(u);
   return __builtin_fmaf(2.0f * c * u * s * (1.0f - s), __builtin_fmaf(3.0f * a, u * u, 1.0f), s);
 }
+
+// Wait until at most n vector-memory operations of this wavefront are
+// outstanding (loads, stores and direct-to-LDS loads count alike, in order).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without a memory fence: LDS data from direct loads is
+// made visible by each wavefront's own vmcnt wait before it; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1 (compile-time indices).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+constexpr unsigned kOutOfRange = 0x80000000u;  // a byte offset past every buffer's range
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 }  // namespace lm

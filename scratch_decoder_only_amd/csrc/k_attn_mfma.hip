@@ -41,9 +41,10 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 
+// (an address-space cast, not a cast through an integer: the compiler keeps
+// track of which LDS array the read addresses)
 __device__ __forceinline__ bf16x4_t ds_read_tr(const bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) bf16*)((uintptr_t)p)));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const __attribute__((address_space(3))) bf16*)p);
 }
 
 // Row-major [64 rows][D] LDS tile, 16-byte chunks XOR-swizzled per row so that

@@ -164,7 +164,6 @@ __device__ __forceinline__ bf16x4_t ds_read_tr(const bf16* p) {
 }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-constexpr unsigned kOutOfRange = 0x80000000u;  // a byte offset past every buffer's range
 
 template <int ROWS, bool KC, int NT>
 struct Tile {
@@ -256,10 +255,6 @@ struct Tile {
 };
 
 // s_waitcnt with only the vector-memory counter limited to n (n < 64).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Work unit u -> (tile m, tile n, K slice z). Units are numbered slice-major
 // and, inside a slice, in groups of GM m-tiles walked n-tile by n-tile. Block
@@ -647,7 +642,6 @@ __global__ void splitk_reduce_kernel(GemmArgs p, const float* __restrict__ part,
 // writes its 16 bytes at the wave's LDS base + 16 j (checked on the device),
 // so each lane fetches the global chunk that belongs at its LDS slot under the
 // swizzles below; no VGPR staging and no ds_write.
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int ROWS, bool KC, int NT, int BK>
 struct PTile {
@@ -741,22 +735,7 @@ __device__ __forceinline__ bf16* lds_stage() {
   return buf;
 }
 
-// Workgroup barrier without a memory fence: LDS data from direct loads is
-// made visible by each wavefront's own vmcnt wait before it; the empty asm
-// statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (N > 0) {
-    static_for<N - 1>(f);
-    f(std::integral_constant<int, N - 1>{});
-  }
-}
 
 // Epilogue of 4 consecutive output columns col..col+3 of one row.
 template <int EPI, typename TC, typename E>
