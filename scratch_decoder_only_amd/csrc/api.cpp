@@ -4,6 +4,7 @@
 // device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -261,7 +262,9 @@ void carve(lm_model* m, char* base) {
   m->dbig = c.take<char>(M * std::max(F, 3 * C) * A);
   m->dO = c.take<char>(M * C * A);
   long ln_blocks = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
-  m->ln_part = c.take<float>(3 * ln_blocks * C);
+  // partial sums of every LayerNorm of the backward (2 per block + the
+  // final one), reduced together once the backward is done
+  m->ln_part = c.take<float>((2 * L + 1) * 3 * ln_blocks * C);
   long col_blocks = (M + kColRows - 1) / kColRows;
   m->col_part = c.take<float>(col_blocks * std::max(std::max(F, 3 * C), m->untied ? m->ldz : 0L));
   m->gemm_ws_floats = 8L * std::max(F, 3 * C) * std::max(F, C);
@@ -566,23 +569,45 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
     Lr.run("gemm_head_bwd_dx", 2.0 * M * V * C, 0, [&] { rc |= gemm(m, op, s); });
   }
   long ln_blocks = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
-  float* pdg = m->ln_part;
-  float* pdb = m->ln_part + ln_blocks * C;
-  float* pdc = m->ln_part + 2 * ln_blocks * C;
   // LayerNorm backward; the column sums of its output gradient g are the
   // gradient of the bias added to the residual stream right before the
   // LayerNorm's input (b_proj of the block below for ln_1 and ln_f, b_o of
-  // the same block for ln_2), so they come out of the same pass (dcol).
+  // the same block for ln_2), so they come out of the same pass (dcol). Each
+  // LayerNorm writes its per-block partial sums into a slot of its own; all
+  // slots are reduced in one launch after the backward (the sums are only
+  // read by the optimizer).
+  ColsumBatch lnb{};
+  int n_ln = 0;
+  double ln_red_bytes = 0;
   auto ln_bwd = [&](const float* x, const float* mu, const float* r, long g_off, long b_off, const float* g_in,
                     float* dcol) {
+    float* pdg = m->ln_part + (long)n_ln * 3 * ln_blocks * C;
+    float* pdb = pdg + ln_blocks * C;
+    float* pdc = pdg + 2 * ln_blocks * C;
     Lr.run("layernorm_bwd", 0, Mf * C * ((g_in ? 4 * 4 : 3 * 4) + A), [&] {
       launch_ln_bwd<E>(m->dy, x, mu, r, m->P_(g_off), (int)M, (int)C, g_in, m->g, g_act, pdg, pdb,
                        dcol ? pdc : nullptr, s);
     });
-    Lr.run("layernorm_bwd_reduce", 0, (dcol ? 3.0 : 2.0) * ln_blocks * C * 4, [&] {
-      launch_colsum_partials(pdg, pdb, (int)ln_blocks, (int)C, m->grads + g_off, m->grads + b_off, s,
-                             dcol ? pdc : nullptr, dcol);
-    });
+    lnb.pa[n_ln] = pdg;
+    lnb.pb[n_ln] = pdb;
+    lnb.pc[n_ln] = dcol ? pdc : nullptr;
+    lnb.oa[n_ln] = m->grads + g_off;
+    lnb.ob[n_ln] = m->grads + b_off;
+    lnb.oc[n_ln] = dcol;
+    ln_red_bytes += (dcol ? 3.0 : 2.0) * ln_blocks * C * 4;
+    ++n_ln;
+  };
+  // the collected reductions, kColsumBatch per launch
+  auto ln_reduce = [&] {
+    for (int i0 = 0; i0 < n_ln; i0 += kColsumBatch) {
+      ColsumBatch part{};
+      const int n = std::min(kColsumBatch, n_ln - i0);
+      for (int i = 0; i < n; ++i) {
+        part.pa[i] = lnb.pa[i0 + i]; part.pb[i] = lnb.pb[i0 + i]; part.pc[i] = lnb.pc[i0 + i];
+        part.oa[i] = lnb.oa[i0 + i]; part.ob[i] = lnb.ob[i0 + i]; part.oc[i] = lnb.oc[i0 + i];
+      }
+      launch_colsum_partials_batch(part, n, (int)ln_blocks, (int)C, s);
+    }
   };
   ln_bwd(m->x + m->L * M * C, m->muf, m->rf, m->o_lnf_g, m->o_lnf_b, nullptr, m->grads + m->blk[m->L - 1].b_proj);
   E* dbig = m->act<E>(m->dbig, 0);
@@ -639,6 +664,7 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   }
   // embedding: dwte[tok] += dx0 (on top of the tied head's part, else from
   // zero), dwpe[pos] = sum dx0
+  Lr.run("layernorm_bwd_reduce", 0, ln_red_bytes, ln_reduce);
   Lr.run("embed_bwd", 0, Mf * C * 8, [&] {
     launch_csr(tok, (int)M, m->V, m->emb_tok, s);
     launch_segment_sum(m->g, tok, (int)M, (int)C, m->V, m->emb_tok, m->grads + m->o_wte, !m->untied, s);

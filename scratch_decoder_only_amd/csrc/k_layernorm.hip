@@ -232,10 +232,10 @@ template void launch_ln_bwd<f16>(const float*, const float*, const float*, const
 // LayerNorm); pb/pc and ob/oc may be null. The sums are latency-bound (a few
 // MB, just written): many wavefronts, each with its loads in flight together.
 constexpr int kPartCols = 16, kPartGroups = 64;
-__global__ void __launch_bounds__(1024) colsum_partials_kernel(const float* __restrict__ pa, const float* __restrict__ pb,
-                                                              const float* __restrict__ pc, int P, int C,
-                                                              float* __restrict__ oa, float* __restrict__ ob,
-                                                              float* __restrict__ oc) {
+__device__ __forceinline__ void colsum_partials_block(const float* __restrict__ pa, const float* __restrict__ pb,
+                                                      const float* __restrict__ pc, int P, int C,
+                                                      float* __restrict__ oa, float* __restrict__ ob,
+                                                      float* __restrict__ oc) {
   __shared__ float sm[3][kPartGroups][kPartCols];
   __shared__ float sr[3][8][kPartCols];
   const int cc = threadIdx.x % kPartCols, r = threadIdx.x / kPartCols;
@@ -296,11 +296,31 @@ __global__ void __launch_bounds__(1024) colsum_partials_kernel(const float* __re
   }
 }
 
+__global__ void __launch_bounds__(1024) colsum_partials_kernel(const float* __restrict__ pa, const float* __restrict__ pb,
+                                                              const float* __restrict__ pc, int P, int C,
+                                                              float* __restrict__ oa, float* __restrict__ ob,
+                                                              float* __restrict__ oc) {
+  colsum_partials_block(pa, pb, pc, P, C, oa, ob, oc);
+}
+
+// Several independent reductions of the same shape in one launch
+// (blockIdx.y picks the set).
+__global__ void __launch_bounds__(1024) colsum_partials_batch_kernel(ColsumBatch bt, int P, int C) {
+  const int i = blockIdx.y;
+  colsum_partials_block(bt.pa[i], bt.pb[i], bt.pc[i], P, C, bt.oa[i], bt.ob[i], bt.oc[i]);
+}
+
 void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob,
                             hipStream_t s, const float* pc, float* oc) {
   static_assert(kPartCols * kPartGroups == 1024 && kPartGroups == 64, "block shape");
   hipLaunchKernelGGL(colsum_partials_kernel, dim3((C + kPartCols - 1) / kPartCols), dim3(1024), 0, s, pa, pb, pc, P,
                      C, oa, ob, oc);
+}
+
+void launch_colsum_partials_batch(const ColsumBatch& bt, int n, int P, int C, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(colsum_partials_batch_kernel, dim3((C + kPartCols - 1) / kPartCols, n), dim3(1024), 0, s, bt, P,
+                     C);
 }
 
 // Column sums of an [M, N] matrix (bias gradients), N a multiple of 4. Stage

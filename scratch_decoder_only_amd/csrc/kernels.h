@@ -77,6 +77,19 @@ void launch_ln_bwd(const float* dy, const float* x, const float* mu, const float
                    float* part_dc, hipStream_t s);
 void launch_colsum_partials(const float* pa, const float* pb, int P, int C, float* oa, float* ob, hipStream_t s,
                             const float* pc = nullptr, float* oc = nullptr);
+// Up to kColsumBatch reductions of the same shape (P partial rows, C
+// columns) in one launch; set i reads pa/pb/pc[i] and writes oa/ob/oc[i]
+// (pb, pc, ob, oc may be null).
+constexpr int kColsumBatch = 32;
+struct ColsumBatch {
+  const float* pa[kColsumBatch];
+  const float* pb[kColsumBatch];
+  const float* pc[kColsumBatch];
+  float* oa[kColsumBatch];
+  float* ob[kColsumBatch];
+  float* oc[kColsumBatch];
+};
+void launch_colsum_partials_batch(const ColsumBatch& bt, int n, int P, int C, hipStream_t s);
 template <typename T>
 void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s);
 
