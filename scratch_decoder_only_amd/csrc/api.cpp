@@ -131,7 +131,7 @@ struct lm_model {
   float *mu1, *r1, *mu2, *r2, *muf, *rf, *lse;
   float *g, *dy, *delta;
   char *g_act, *dbig, *dO;
-  float *ln_part, *col_part, *gemm_ws;
+  float *ln_part, *col_part, *bias_part, *gemm_ws;
   long gemm_ws_floats;
   EmbedBwdWs emb_tok, emb_pos;
   int32_t *start, *end, *pos, *n_valid;
@@ -267,6 +267,9 @@ void carve(lm_model* m, char* base) {
   m->ln_part = c.take<float>((2 * L + 1) * 3 * ln_blocks * C);
   long col_blocks = (M + kColRows - 1) / kColRows;
   m->col_part = c.take<float>(col_blocks * std::max(std::max(F, 3 * C), m->untied ? m->ldz : 0L));
+  // per-block partial column sums of every MLP-in and QKV bias gradient,
+  // reduced together after the backward
+  m->bias_part = c.take<float>(L * col_blocks * (F + 3 * C));
   m->gemm_ws_floats = 8L * std::max(F, 3 * C) * std::max(F, C);
   m->gemm_ws = c.take<float>(m->gemm_ws_floats);
   for (int k = 0; k < 2; ++k) {
@@ -578,6 +581,11 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   // read by the optimizer).
   ColsumBatch lnb{};
   int n_ln = 0;
+  const long col_blocks = (M + kColRows - 1) / kColRows;
+  auto fc_part = [&](int l) { return m->bias_part + (long)l * col_blocks * (F + 3 * C); };
+  auto qkv_part = [&](int l) { return fc_part(l) + col_blocks * F; };
+  std::vector<float*> fc_pa(m->L), fc_oa(m->L), qkv_pa(m->L), qkv_oa(m->L);
+  struct { std::vector<float*>& pa; std::vector<float*>& oa; } fcb{fc_pa, fc_oa}, qkvb{qkv_pa, qkv_oa};
   double ln_red_bytes = 0;
   auto ln_bwd = [&](const float* x, const float* mu, const float* r, long g_off, long b_off, const float* g_in,
                     float* dcol) {
@@ -631,7 +639,9 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
     }
     // MLP in: u = y2 W_fc^T + b_fc
     Lr.run("gemm_fc1_bwd_dw", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, dw_op(dbig, M, F, y2, C, m->grads + b.w_fc), s); });
-    Lr.run("bias_grad", 0, Mf * F * A, [&] { launch_colsum<E>(dbig, F, (int)M, (int)F, m->col_part, m->grads + b.b_fc, s); });
+    Lr.run("bias_grad", 0, Mf * F * A, [&] { launch_colsum_stage1<E>(dbig, F, (int)M, (int)F, fc_part(l), s); });
+    fcb.pa[l] = fc_part(l);
+    fcb.oa[l] = m->grads + b.b_fc;
     {
       GemmOp op = dx_op(m, dbig, M, F, b.w_fc, C, m->dy, EPI_STORE);
       op.c_f32 = true;
@@ -654,7 +664,9 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
         });
     }
     Lr.run("gemm_qkv_bwd_dw", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, dw_op(dbig, M, 3 * C, y1, C, m->grads + b.w_qkv), s); });
-    Lr.run("bias_grad", 0, Mf * 3 * C * A, [&] { launch_colsum<E>(dbig, 3 * C, (int)M, (int)(3 * C), m->col_part, m->grads + b.b_qkv, s); });
+    Lr.run("bias_grad", 0, Mf * 3 * C * A, [&] { launch_colsum_stage1<E>(dbig, 3 * C, (int)M, (int)(3 * C), qkv_part(l), s); });
+    qkvb.pa[l] = qkv_part(l);
+    qkvb.oa[l] = m->grads + b.b_qkv;
     {
       GemmOp op = dx_op(m, dbig, M, 3 * C, b.w_qkv, C, m->dy, EPI_STORE);
       op.c_f32 = true;
@@ -665,6 +677,19 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   // embedding: dwte[tok] += dx0 (on top of the tied head's part, else from
   // zero), dwpe[pos] = sum dx0
   Lr.run("layernorm_bwd_reduce", 0, ln_red_bytes, ln_reduce);
+  // the MLP-in and QKV bias gradients from their partial sums, in batches
+  Lr.run("bias_grad_reduce", 0, 4.0 * col_blocks * (F + 3 * C) * m->L, [&] {
+    for (int l0 = 0; l0 < m->L; l0 += kColsumBatch) {
+      const int n = std::min(kColsumBatch, m->L - l0);
+      ColsumBatch f{}, q{};
+      for (int i = 0; i < n; ++i) {
+        f.pa[i] = fcb.pa[l0 + i]; f.oa[i] = fcb.oa[l0 + i];
+        q.pa[i] = qkvb.pa[l0 + i]; q.oa[i] = qkvb.oa[l0 + i];
+      }
+      launch_colsum_partials_batch(f, n, (int)col_blocks, (int)F, s);
+      launch_colsum_partials_batch(q, n, (int)col_blocks, (int)(3 * C), s);
+    }
+  });
   Lr.run("embed_bwd", 0, Mf * C * 8, [&] {
     launch_csr(tok, (int)M, m->V, m->emb_tok, s);
     launch_segment_sum(m->g, tok, (int)M, (int)C, m->V, m->emb_tok, m->grads + m->o_wte, !m->untied, s);

@@ -418,18 +418,25 @@ __global__ void __launch_bounds__(256) colsum8_h16_kernel(const T* __restrict__ 
 }
 
 template <typename T>
-void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s) {
-  int P = (M + kColRows - 1) / kColRows;
+void launch_colsum_stage1(const T* a, long lda, int M, int N, float* part, hipStream_t s) {
+  const int P = (M + kColRows - 1) / kColRows;
   if constexpr (sizeof(T) == 2) {
     if (N % 8 == 0 && lda % 8 == 0) {
       hipLaunchKernelGGL(colsum8_h16_kernel<T>, dim3((N / 8 + 63) / 64, P), dim3(256), 0, s, a, lda, M, N, part);
-      launch_colsum_partials(part, nullptr, P, N, out, nullptr, s);
       return;
     }
   }
-    hipLaunchKernelGGL(colsum_stage1_kernel<T>, dim3((N / 4 + 63) / 64, P), dim3(256), 0, s, a, lda, M, N, part);
-  launch_colsum_partials(part, nullptr, P, N, out, nullptr, s);
+  hipLaunchKernelGGL(colsum_stage1_kernel<T>, dim3((N / 4 + 63) / 64, P), dim3(256), 0, s, a, lda, M, N, part);
 }
+
+template <typename T>
+void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s) {
+  launch_colsum_stage1<T>(a, lda, M, N, part, s);
+  launch_colsum_partials(part, nullptr, (M + kColRows - 1) / kColRows, N, out, nullptr, s);
+}
+template void launch_colsum_stage1<float>(const float*, long, int, int, float*, hipStream_t);
+template void launch_colsum_stage1<bf16>(const bf16*, long, int, int, float*, hipStream_t);
+template void launch_colsum_stage1<f16>(const f16*, long, int, int, float*, hipStream_t);
 template void launch_colsum<float>(const float*, long, int, int, float*, float*, hipStream_t);
 template void launch_colsum<bf16>(const bf16*, long, int, int, float*, float*, hipStream_t);
 template void launch_colsum<f16>(const f16*, long, int, int, float*, float*, hipStream_t);

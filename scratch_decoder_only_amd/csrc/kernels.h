@@ -92,6 +92,10 @@ struct ColsumBatch {
 void launch_colsum_partials_batch(const ColsumBatch& bt, int n, int P, int C, hipStream_t s);
 template <typename T>
 void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s);
+// Its first stage alone: the (M / kColRows rounded up) x N partial rows,
+// reduced later (launch_colsum_partials[_batch]).
+template <typename T>
+void launch_colsum_stage1(const T* a, long lda, int M, int N, float* part, hipStream_t s);
 
 // loss_scale (nullable, device): dz is multiplied by *loss_scale.
 template <typename T>
