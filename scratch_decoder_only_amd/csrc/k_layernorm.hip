@@ -111,87 +111,114 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const float* __restrict__ d
                                                      float* __restrict__ part_dg, float* __restrict__ part_db,
                                                      float* __restrict__ part_dc) {
   constexpr int C = 128 * NV;
+  // a lane holds its values in float4 chunks when NV is even (16-byte
+  // accesses), else in float2 chunks; chunk j covers columns
+  // W (lane + 64 j) .. + W - 1
+  constexpr int W = NV % 2 == 0 ? 4 : 2, NC = C / (64 * W);
   __shared__ float s_dg[4][C];
   __shared__ float s_db[4][C];
   __shared__ float s_dc[4][C];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float2 gg[NV], adg[NV], adb[NV], adc[NV];
-  const float2* g2 = reinterpret_cast<const float2*>(g);
+  auto ld = [](const float* p, float* v) {
+    if constexpr (W == 4) {
+      const f32x4_t t = *reinterpret_cast<const f32x4_t*>(p);
+      v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+    } else {
+      const float2 t = *reinterpret_cast<const float2*>(p);
+      v[0] = t.x; v[1] = t.y;
+    }
+  };
+  float gg[NC][W], adg[NC][W], adb[NC][W], adc[NC][W];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    gg[j] = g2[lane + 64 * j];
-    adg[j] = make_float2(0.f, 0.f);
-    adb[j] = make_float2(0.f, 0.f);
-    adc[j] = make_float2(0.f, 0.f);
+  for (int j = 0; j < NC; ++j) {
+    ld(g + W * (lane + 64 * j), gg[j]);
+#pragma unroll
+    for (int e = 0; e < W; ++e) adg[j][e] = adb[j][e] = adc[j][e] = 0.f;
   }
   const long r0 = (long)blockIdx.x * kLnRowsPerBlock;
   const long r1 = min((long)M, r0 + kLnRowsPerBlock);
   // the next row's inputs are loaded while the current row is computed
-  float2 dn[NV], xn[NV], gn[NV];
+  float dn[NC][W], xn[NC][W], gn[NC][W];
   float mun = 0.f, rn = 0.f;
   auto load_row = [&](long m) {
-    const float2* dyr = reinterpret_cast<const float2*>(dy + m * C);
-    const float2* xr = reinterpret_cast<const float2*>(x + m * C);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      dn[j] = dyr[lane + 64 * j];
-      xn[j] = xr[lane + 64 * j];
-      gn[j] = g_in ? reinterpret_cast<const float2*>(g_in + m * C)[lane + 64 * j] : make_float2(0.f, 0.f);
+    for (int j = 0; j < NC; ++j) {
+      const long o = m * C + W * (lane + 64 * j);
+      ld(dy + o, dn[j]);
+      ld(x + o, xn[j]);
+      if (g_in) ld(g_in + o, gn[j]);
+      else
+#pragma unroll
+        for (int e = 0; e < W; ++e) gn[j][e] = 0.f;
     }
     mun = mu_in[m];
     rn = rstd_in[m];
   };
   if (r0 + w < r1) load_row(r0 + w);
   for (long m = r0 + w; m < r1; m += 4) {
-    float2 dv[NV], xv[NV], gi[NV];
+    float dv[NC][W], xv[NC][W], gi[NC][W];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      dv[j] = dn[j];
-      xv[j] = xn[j];
-      gi[j] = gn[j];
-    }
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        dv[j][e] = dn[j][e];
+        xv[j][e] = xn[j][e];
+        gi[j][e] = gn[j][e];
+      }
     const float mu = mun, r = rn;
     if (m + 4 < r1) load_row(m + 4);
-    float2 xh[NV], dxh[NV];
+    float xh[NC][W], dxh[NC][W];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const float2 d = dv[j];
-      xh[j] = make_float2((xv[j].x - mu) * r, (xv[j].y - mu) * r);
-      dxh[j] = make_float2(d.x * gg[j].x, d.y * gg[j].y);
-      s1 += dxh[j].x + dxh[j].y;
-      s2 += dxh[j].x * xh[j].x + dxh[j].y * xh[j].y;
-      adg[j].x += d.x * xh[j].x;
-      adg[j].y += d.y * xh[j].y;
-      adb[j].x += d.x;
-      adb[j].y += d.y;
-    }
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        const float d = dv[j][e];
+        xh[j][e] = (xv[j][e] - mu) * r;
+        dxh[j][e] = d * gg[j][e];
+        s1 += dxh[j][e];
+        s2 += dxh[j][e] * xh[j][e];
+        adg[j][e] += d * xh[j][e];
+        adb[j][e] += d;
+      }
     const float m1 = wave_sum(s1) * (1.0f / C), m2 = wave_sum(s2) * (1.0f / C);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int c = 2 * (lane + 64 * j);
-      const float dx0 = r * (dxh[j].x - m1 - xh[j].x * m2) + gi[j].x;
-      const float dx1 = r * (dxh[j].y - m1 - xh[j].y * m2) + gi[j].y;
-      reinterpret_cast<float2*>(g_out + m * C)[lane + 64 * j] = make_float2(dx0, dx1);
-      adc[j].x += dx0;
-      adc[j].y += dx1;
-      if (g_act) {
-        if constexpr (sizeof(T) == 2)  // two adjacent 16-bit values in one 4-byte store
-          reinterpret_cast<uint32_t*>(g_act)[(m * C + c) >> 1] = H16<T>::pack(dx0, dx1);
-        else
-          reinterpret_cast<float2*>(g_act)[(m * C + c) >> 1] = make_float2(dx0, dx1);
+    for (int j = 0; j < NC; ++j) {
+      const int c = W * (lane + 64 * j);
+      float o[W];
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        o[e] = r * (dxh[j][e] - m1 - xh[j][e] * m2) + gi[j][e];
+        adc[j][e] += o[e];
+      }
+      if constexpr (W == 4) {
+        *reinterpret_cast<f32x4_t*>(g_out + m * C + c) = f32x4_t{o[0], o[1], o[2], o[3]};
+        if (g_act) {
+          if constexpr (sizeof(T) == 2)  // adjacent 16-bit values packed in pairs
+            *reinterpret_cast<uint2*>(g_act + m * C + c) = make_uint2(H16<T>::pack(o[0], o[1]), H16<T>::pack(o[2], o[3]));
+          else
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(g_act) + m * C + c) = f32x4_t{o[0], o[1], o[2], o[3]};
+        }
+      } else {
+        *reinterpret_cast<float2*>(g_out + m * C + c) = make_float2(o[0], o[1]);
+        if (g_act) {
+          if constexpr (sizeof(T) == 2)
+            *reinterpret_cast<uint32_t*>(g_act + m * C + c) = H16<T>::pack(o[0], o[1]);
+          else
+            *reinterpret_cast<float2*>(reinterpret_cast<float*>(g_act) + m * C + c) = make_float2(o[0], o[1]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    int c = 2 * (lane + 64 * j);
-    s_dg[w][c] = adg[j].x;
-    s_dg[w][c + 1] = adg[j].y;
-    s_db[w][c] = adb[j].x;
-    s_db[w][c + 1] = adb[j].y;
-    s_dc[w][c] = adc[j].x;
-    s_dc[w][c + 1] = adc[j].y;
+  for (int j = 0; j < NC; ++j) {
+    const int c = W * (lane + 64 * j);
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      s_dg[w][c + e] = adg[j][e];
+      s_db[w][c + e] = adb[j][e];
+      s_dc[w][c + e] = adc[j][e];
+    }
   }
   __syncthreads();
   for (int c = threadIdx.x; c < C; c += 256) {
