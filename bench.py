@@ -62,14 +62,21 @@ def attention_flops(shape, doc_ids, B, T):
     return 12.0 * shape.head_dim * shape.n_heads * shape.n_layers * pairs
 
 
-# Kernel symbol of each timing class whose HBM traffic is taken from counters
-# (a class must map to one kernel instantiation used by nothing else).
+# Kernel symbol of each timing class whose HBM traffic is taken from counters:
+# a class maps to one kernel instantiation used by nothing else, or to
+# (symbol, period, phase) when two classes share an instantiation in a fixed
+# alternation: the class takes that kernel's dispatches whose index, in
+# dispatch order, is phase modulo period (the attention-output and MLP-out
+# forward GEMMs share the residual-epilogue kernel and alternate, attention
+# output first, in every block).
 TRAFFIC_SYMBOLS = {
     "gemm_head_bwd_dw": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, false, false, 0, float,",
     "gemm_head_fwd": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, true, true, 0,",
     "gemm_fc1_fwd": "gemm16_pipe_kernel<128, 128, 2, 2, 64, 2, 2, true, true, 2,",
     "gemm_fc2_bwd_dx": "gemm16_pipe_kernel<128, 128, 2, 2, 64, 2, 2, true, false, 3,",
     "adamw": "adamw_kernel(",
+    "gemm_attnout_fwd": ("gemm16_kernel<128, 128, 2, 2, true, true, 1, float,", 2, 0),
+    "gemm_fc2_fwd": ("gemm16_kernel<128, 128, 2, 2, true, true, 1, float,", 2, 1),
     "attn_bwd_dkv": "attn_dkv_kernel<64>",
     "attn_fwd": "attn_fwd_kernel<64>",
 }
@@ -97,17 +104,20 @@ def pmc_summary(fetch_dir, write_dir, out=TRAFFIC_FILE, cmd=""):
     import glob
 
     def read(d, counter):
+        """kernel name -> [(dispatch id, value)] in dispatch order"""
         acc = {}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] != counter:
                     continue
-                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return acc
+                acc.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        return {k: [v for _, v in sorted(x)] for k, x in acc.items()}
 
     fetch_all, write_all = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
-    fetch = {k: (sum(v) / len(v), len(v)) for k, v in fetch_all.items()}
-    write = {k: (sum(v) / len(v), len(v)) for k, v in write_all.items()}
+
+    def mean_of(vals, period, phase):
+        sel = vals[phase::period]
+        return (sum(sel) / len(sel), len(sel)) if sel else (0.0, 0)
     # the calibration copy: the largest dispatch of a copy kernel (it moves
     # more bytes than any other copy of the run)
     cal = [(max(v), k) for k, v in fetch_all.items() if "copy" in k.lower()]
@@ -120,17 +130,19 @@ def pmc_summary(fetch_dir, write_dir, out=TRAFFIC_FILE, cmd=""):
     rec = {"source_digest": source_digest(), "calib_kernel": ck, "calib_bytes": CALIB_BYTES,
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "classes": {}}
     lines = []
-    for cls, sym in TRAFFIC_SYMBOLS.items():
-        ks = [k for k in fetch if sym in k]
+    for cls, spec in TRAFFIC_SYMBOLS.items():
+        sym, period, phase = (spec, 1, 0) if isinstance(spec, str) else spec
+        ks = [k for k in fetch_all if sym in k]
         if not ks:
             continue
         k = ks[0]
-        fb = fetch[k][0] * 1024 * f_scale
-        wb = write.get(k, (0.0, 0))[0] * 1024 * w_scale
-        rec["classes"][cls] = {"kernel": k, "dispatches": fetch[k][1], "fetch_kib": round(fetch[k][0], 1),
-                               "write_kib": round(write.get(k, (0.0, 0))[0], 1), "bytes_per_launch": round(fb + wb)}
-        lines.append(f"| {cls} | `{k[:90]}` | {fetch[k][1]} | {fetch[k][0]:.1f} | {write.get(k, (0, 0))[0]:.1f} | "
-                     f"{(fb + wb) / 1e6:.2f} |")
+        fm, fn = mean_of(fetch_all[k], period, phase)
+        wm, _ = mean_of(write_all.get(k, []), period, phase)
+        fb = fm * 1024 * f_scale
+        wb = wm * 1024 * w_scale
+        rec["classes"][cls] = {"kernel": k, "dispatches": fn, "fetch_kib": round(fm, 1), "write_kib": round(wm, 1),
+                               "bytes_per_launch": round(fb + wb)}
+        lines.append(f"| {cls} | `{k[:90]}` | {fn} | {fm:.1f} | {wm:.1f} | {(fb + wb) / 1e6:.2f} |")
     with open(out, "w") as fh:
         fh.write("# HBM traffic per launch from hardware counters (GPT-2-small-shaped step, C4)\n\n")
         fh.write("Commands (run from the repository root on one MI355X):\n\n```\n" + cmd + "\n```\n\n")
