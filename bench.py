@@ -178,6 +178,27 @@ def stats_summary(stats_csv, out, cmd="", steps=7):
             fh.write(f"| `{r['Name'][:110]}` | {r['Calls']} | {t / 1e6:.2f} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{100 * t / total:.1f}% |\n")
         fh.write(f"\nAll kernels: {total / 1e6:.2f} ms, {total / 1e6 / steps:.3f} ms per step.\n")
+        # per timing class, for the classes with hardware-counter records:
+        # average dispatch duration from the run's kernel trace (a kernel
+        # shared by two alternating classes is split the same way as the
+        # counters)
+        trace = os.path.join(os.path.dirname(stats_csv), os.path.basename(stats_csv).replace("kernel_stats",
+                                                                                               "kernel_trace"))
+        if os.path.exists(trace):
+            durs = {}
+            for r in csv.DictReader(open(trace)):
+                durs.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            fh.write("\nPer timing class (dispatches of its kernel, from the kernel trace):\n\n"
+                     "| class | dispatches | avg us |\n|---|---:|---:|\n")
+            for cls, spec in TRAFFIC_SYMBOLS.items():
+                sym, period, phase = (spec, 1, 0) if isinstance(spec, str) else spec
+                ks = [k for k in durs if sym in k]
+                if not ks:
+                    continue
+                sel = [d for _, d in sorted(durs[ks[0]])][phase::period]
+                if sel:
+                    fh.write(f"| {cls} | {len(sel)} | {sum(sel) / len(sel) / 1e3:.1f} |\n")
     print(out)
 
 
