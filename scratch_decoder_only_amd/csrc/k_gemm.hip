@@ -1129,9 +1129,12 @@ int gemm16_splits(const GemmOp& op) {
       if ((s == 1 || op.K / s >= 512) && fill(s) >= 0.9 * best) return s;
     return 1;
   }
-  // split K when the tile grid cannot fill the 256 compute units and K is long
+  // split K when the tile grid cannot fill the 256 compute units and K is
+  // long; for a few rows (one token per sequence when generating) each tile
+  // is a short latency-bound pass, so slices go down to 128 K-values
+  const int kmin = op.M <= 64 ? 128 : 512;
   int s = 1;
-  while (tiles * s < 256 && op.K / (s * 2) >= 512) s *= 2;
+  while (tiles * s < 256 && op.K / (s * 2) >= kmin) s *= 2;
   return s;
 }
 
