@@ -379,14 +379,14 @@ def main():
         T0 = min(128, T - args.gen)
         prompt = tok[:, :T0].contiguous()
         rates = {}
-        for cached in (False, True):
-            sd.generate(model, prompt, 2, kv_cache=cached)  # warm-up
+        for mode in ("recompute", "cache", "graph"):
+            kw = dict(kv_cache=mode != "recompute", graph=mode == "graph")
+            sd.generate(model, prompt, 3, **kw)  # warm-up
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            sd.generate(model, prompt, args.gen, kv_cache=cached)
+            sd.generate(model, prompt, args.gen, **kw)
             torch.cuda.synchronize()
-            rates[cached] = time.perf_counter() - t0
-        t_gen = rates[False]
+            rates[mode] = time.perf_counter() - t0
         logits = model.forward_logits(prompt)[:, T0 - 1, :]
         u = torch.rand(B, device="cuda")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -396,12 +396,14 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         out["generation"] = {"batch": B, "prompt": T0, "new_tokens": args.gen,
-                             "tokens_per_s_recompute": round(B * args.gen / rates[False], 1),
-                             "tokens_per_s_kv_cache": round(B * args.gen / rates[True], 1),
-                             "ms_per_token_step_kv_cache": round(rates[True] / args.gen * 1e3, 3),
+                             "tokens_per_s_recompute": round(B * args.gen / rates["recompute"], 1),
+                             "tokens_per_s_kv_cache": round(B * args.gen / rates["cache"], 1),
+                             "ms_per_token_step_kv_cache": round(rates["cache"] / args.gen * 1e3, 3),
+                             "tokens_per_s_kv_cache_graph": round(B * args.gen / rates["graph"], 1),
+                             "ms_per_token_step_kv_cache_graph": round(rates["graph"] / args.gen * 1e3, 3),
                              "sample_us_per_call": round(e0.elapsed_time(e1) / 10 * 1e3, 1)}
-        log(f"bench: generation {B}x{args.gen} tokens: {rates[False]:.2f} s recomputing, "
-            f"{rates[True]:.2f} s with the cache")
+        log(f"bench: generation {B}x{args.gen} tokens: {rates['recompute']:.3f} s recomputing, "
+            f"{rates['cache']:.3f} s with the cache, {rates['graph']:.3f} s with the cache and a decode graph")
 
     def time_variant(vshape):
         """ms per step of the same workload on a model of another variant."""

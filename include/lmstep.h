@@ -242,6 +242,18 @@ lm_status model_prefill(lm_model* model, const int32_t* d_tokens, int32_t B, int
 lm_status model_decode(lm_model* model, const int32_t* d_tokens, int32_t B, int32_t pos, void* d_cache,
                        float* d_logits, void* stream);
 
+/* model_decode_at is model_decode with the position in device memory
+ * (d_pos, one int32), read by the kernels when they run rather than when the
+ * call is made: a graph captured from one call (hipStreamBeginCapture on
+ * `stream`) can then be replayed at successive positions by rewriting
+ * *d_pos (and the tokens at d_tokens) between replays. The call itself
+ * allocates nothing and does not synchronize. A position outside
+ * [1, max_seq) is clamped into it (the kernels never touch memory outside
+ * the cache); keeping it in range is the caller's part. Errors: NULL
+ * pointers, a batch outside [1, max_batch], max_seq < 2. */
+lm_status model_decode_at(lm_model* model, const int32_t* d_tokens, int32_t B, const int32_t* d_pos,
+                          void* d_cache, float* d_logits, void* stream);
+
 /* ---- measurement hooks (used by the benchmark) ----
  * With profiling on, every kernel launch of train_step is bracketed by a pair
  * of HIP events recorded on the step's stream, and model_profile_read sums

@@ -86,6 +86,7 @@ _sig("model_load", c_int, [c_void_p, c_char_p, ctypes.POINTER(ctypes.c_int32), c
 _sig("lm_kv_cache_bytes", c_size_t, [ctypes.POINTER(LmConfig), ctypes.c_int32])
 _sig("model_prefill", c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_void_p, c_void_p])
 _sig("model_decode", c_int, [c_void_p, c_void_p, ctypes.c_int32, ctypes.c_int32, c_void_p, c_void_p, c_void_p])
+_sig("model_decode_at", c_int, [c_void_p, c_void_p, ctypes.c_int32, c_void_p, c_void_p, c_void_p, c_void_p])
 _sig("sample_tokens", c_int, [c_void_p, ctypes.c_int32, ctypes.c_int32, c_int64, ctypes.c_float, ctypes.c_int32,
                               c_void_p, c_void_p, c_void_p])
 _sig("model_set_loss_scaler", c_int, [c_void_p, ctypes.POINTER(LmLossScaler), c_void_p])
@@ -268,6 +269,17 @@ class Model:
                "model_decode")
         return out
 
+    def decode_at(self, tokens, pos, cache, out=None):
+        """decode with the position in device memory (pos: int32 CUDA tensor of
+        one element, read when the kernels run; clamped to [1, max_seq))."""
+        torch = _torch()
+        B = tokens.shape[0]
+        if out is None:
+            out = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _check(_lib.model_decode_at(self._h, _ptr(tokens), B, _ptr(pos), _ptr(cache), _ptr(out), _stream()),
+               "model_decode_at")
+        return out
+
     # ---- checkpoints
     # ---- dynamic loss scale (precision "fp16")
     def loss_scaler(self) -> Dict[str, float]:
@@ -353,13 +365,47 @@ def sample_tokens(logits, temperature: float = 0.0, top_k: int = 0, uniforms=Non
     return out
 
 
+class DecodeGraph:
+    """One decode step of `model` on `cache` (batch rows), captured once as a
+    HIP graph and replayed per token: step(tokens, pos) copies the tokens into
+    the graph's input, writes pos to its device position and replays; the
+    logits land in the graph's output [batch, vocab] (returned, overwritten
+    by the next step). The first step runs eagerly and also warms the path
+    up; the graph is captured right after it."""
+
+    def __init__(self, model: "Model", cache, batch: int):
+        torch = _torch()
+        dev = cache.device
+        self.model, self.cache = model, cache
+        self.tok = torch.zeros(batch, dtype=torch.int32, device=dev)
+        self.pos = torch.ones(1, dtype=torch.int32, device=dev)
+        self.out = torch.empty((batch, model.cfg.vocab), dtype=torch.float32, device=dev)
+        self.graph = None
+
+    def step(self, tokens, pos: int):
+        torch = _torch()
+        self.tok.copy_(tokens)
+        self.pos.fill_(int(pos))
+        if self.graph is None:
+            self.model.decode_at(self.tok, self.pos, self.cache, out=self.out)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.model.decode_at(self.tok, self.pos, self.cache, out=self.out)
+            self.graph = g
+        else:
+            self.graph.replay()
+        return self.out
+
+
 def generate(model: "Model", prompt, n_new: int, *, temperature: float = 0.0, top_k: int = 0, seed: int = 0,
-             kv_cache: bool = True):
+             kv_cache: bool = True, graph: bool = False):
     """Extends each row of `prompt` ([B, T0] int32 CUDA tensor) by n_new tokens.
 
     kv_cache=True: one prefill over the prompt, then one decode step per new
-    token against the key/value cache. kv_cache=False: forward_logits over the
-    whole sequence so far for every new token. Either way sample_tokens picks
+    token against the key/value cache (graph=True: the decode step replayed
+    from a captured HIP graph, DecodeGraph). kv_cache=False: forward_logits
+    over the whole sequence so far for every new token. Either way sample_tokens picks
     the token from the last position's logits; uniforms for sampling are drawn
     on the host from numpy's PCG64(seed), one per row and step, and passed in.
     Returns the [B, T0 + n_new] token tensor."""
@@ -371,12 +417,15 @@ def generate(model: "Model", prompt, n_new: int, *, temperature: float = 0.0, to
     toks[:, :T0] = prompt
     rng = np.random.Generator(np.random.PCG64(seed))
     cache = model.kv_cache(B) if kv_cache and n_new > 0 else None
+    dg = DecodeGraph(model, cache, B) if cache is not None and graph else None
     for i in range(n_new):
         T = T0 + i
         if cache is None:
             last = model.forward_logits(toks[:, :T].contiguous())[:, T - 1, :]
         elif i == 0:
             last = model.prefill(toks[:, :T].contiguous(), cache)
+        elif dg is not None:
+            last = dg.step(toks[:, T - 1], T - 1)
         else:
             last = model.decode(toks[:, T - 1].contiguous(), T - 1, cache)
         u = None

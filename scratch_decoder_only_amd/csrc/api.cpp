@@ -471,13 +471,17 @@ int forward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* d
 // pos, run through every block with M = B rows; each block appends its keys
 // and values at pos and attends over cache positions 0 .. pos; the head
 // writes B rows of logits. Same kernels and epilogues as the forward pass.
+// d_pos (nullable): the position in device memory instead of pos, read by
+// the kernels when they run (clamped to [1, max_seq - 1]).
 template <typename E>
-int decode_pass(lm_model* m, Launcher& Lr, const int32_t* tok, int B, int pos, E* cache) {
+int decode_pass(lm_model* m, Launcher& Lr, const int32_t* tok, int B, int pos, E* cache,
+                const int32_t* d_pos = nullptr) {
   hipStream_t s = Lr.s;
   const long M = B, C = m->C, F = m->F, H = m->H, S = m->S;
   const double Mf = (double)M, A = (double)sizeof(E);
   int rc = 0;
-  launch_fill_u32(reinterpret_cast<uint32_t*>(m->pos), (uint32_t)pos, M, s);
+  if (d_pos) launch_fill_pos(m->pos, d_pos, (int)S, M, s);
+  else launch_fill_u32(reinterpret_cast<uint32_t*>(m->pos), (uint32_t)pos, M, s);
   Lr.run("embed_fwd", 0, Mf * C * 12.0, [&] {
     launch_embed_fwd(tok, m->pos, m->params + m->o_wte, m->params + m->o_wpe, (int)M, (int)C, m->V, m->x, m->flags, s);
   });
@@ -503,8 +507,8 @@ int decode_pass(lm_model* m, Launcher& Lr, const int32_t* tok, int B, int pos, E
       Lr.run("gemm_qkv_fwd", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, op, s); });
     }
     Lr.run("attn_decode", 0, 0, [&] {
-      launch_kv_store<E>(qkv, B, 1, (int)C, (int)S, pos, kc, vc, s);
-      rc |= launch_attn_decode<E>(qkv, kc, vc, B, (int)H, m->D, (int)S, pos + 1, o, m->gemm_ws, s);
+      launch_kv_store<E>(qkv, B, 1, (int)C, (int)S, pos, kc, vc, s, d_pos);
+      rc |= launch_attn_decode<E>(qkv, kc, vc, B, (int)H, m->D, (int)S, pos + 1, o, m->gemm_ws, s, d_pos);
     });
     {
       GemmOp op = fwd_op(m, o, M, C, b.w_o, C, xml, EPI_RESID);
@@ -924,24 +928,39 @@ lm_status model_prefill(lm_model* m, const int32_t* tok, int32_t B, int32_t T, v
   return hip_status("model_prefill");
 }
 
-lm_status model_decode(lm_model* m, const int32_t* tok, int32_t B, int32_t pos, void* d_cache, float* d_logits,
-                       void* stream) {
-  if (!m || !tok || !d_cache || !d_logits) return fail(LM_ERR_ARG, "model, tokens, cache or logits is NULL");
-  lm_status st = check_batch(m, B, 1);
-  if (st != LM_OK) return st;
-  if (pos < 1 || pos >= m->S) return fail(LM_ERR_SHAPE, "pos must be in [1, max_seq): the cache holds positions < pos");
+static lm_status decode_common(lm_model* m, const int32_t* tok, int32_t B, int32_t pos, const int32_t* d_pos,
+                               void* d_cache, float* d_logits, void* stream, const char* what) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   Launcher Lr(m, s);
   int rc;
   launch_fill_u32(m->flags, 0u, 4, s);
   rc = with_act(m, [&](auto tag) {
     using E = std::remove_pointer_t<decltype(tag)>;
-    const int r = decode_pass<E>(m, Lr, tok, B, pos, reinterpret_cast<E*>(d_cache));
+    const int r = decode_pass<E>(m, Lr, tok, B, pos, reinterpret_cast<E*>(d_cache), d_pos);
     launch_logits_out<E>(m->act<E>(m->logits, 0), m->ldz, B, m->V, d_logits, s);
     return r;
   });
   if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
-  return hip_status("model_decode");
+  return hip_status(what);
+}
+
+lm_status model_decode(lm_model* m, const int32_t* tok, int32_t B, int32_t pos, void* d_cache, float* d_logits,
+                       void* stream) {
+  if (!m || !tok || !d_cache || !d_logits) return fail(LM_ERR_ARG, "model, tokens, cache or logits is NULL");
+  lm_status st = check_batch(m, B, 1);
+  if (st != LM_OK) return st;
+  if (pos < 1 || pos >= m->S) return fail(LM_ERR_SHAPE, "pos must be in [1, max_seq): the cache holds positions < pos");
+  return decode_common(m, tok, B, pos, nullptr, d_cache, d_logits, stream, "model_decode");
+}
+
+lm_status model_decode_at(lm_model* m, const int32_t* tok, int32_t B, const int32_t* d_pos, void* d_cache,
+                          float* d_logits, void* stream) {
+  if (!m || !tok || !d_pos || !d_cache || !d_logits)
+    return fail(LM_ERR_ARG, "model, tokens, position, cache or logits is NULL");
+  lm_status st = check_batch(m, B, 1);
+  if (st != LM_OK) return st;
+  if (m->S < 2) return fail(LM_ERR_SHAPE, "max_seq must be at least 2 to decode");
+  return decode_common(m, tok, B, 0, d_pos, d_cache, d_logits, stream, "model_decode_at");
 }
 
 lm_status model_set_loss_scaler(lm_model* m, const lm_loss_scaler* ls, void* stream) {

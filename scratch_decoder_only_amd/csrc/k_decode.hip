@@ -16,9 +16,11 @@ namespace {
 // cache rows (b, t0 .. t0+T-1) of layer l's K and V from qkv rows [B*T, 3C]
 template <typename E>
 __global__ void kv_store_kernel(const E* __restrict__ qkv, int B, int T, int C, int S, int t0,
-                                E* __restrict__ kc, E* __restrict__ vc) {
+                                E* __restrict__ kc, E* __restrict__ vc, const int32_t* __restrict__ d_pos) {
+  if (d_pos) t0 = decode_pos(d_pos, S);
   const long r = blockIdx.x;  // b * T + t
   const int b = (int)(r / T), t = (int)(r % T);
+  if (t0 + t >= S) return;
   const E* src = qkv + r * 3L * C;
   E* dk = kc + ((long)b * S + t0 + t) * C;
   E* dv = vc + ((long)b * S + t0 + t) * C;
@@ -35,7 +37,9 @@ __global__ void kv_store_kernel(const E* __restrict__ qkv, int B, int T, int C, 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) attn_decode_kernel(const T* __restrict__ qkv, const T* __restrict__ kc,
                                                           const T* __restrict__ vc, int H, int S, int n,
-                                                          T* __restrict__ o, float* __restrict__ sbuf) {
+                                                          T* __restrict__ o, float* __restrict__ sbuf,
+                                                          const int32_t* __restrict__ d_pos) {
+  if (d_pos) n = decode_pos(d_pos, S) + 1;
   constexpr int NT = 256;
   __shared__ float s_q[D];
   __shared__ float s_red[NT / 64];
@@ -101,7 +105,9 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(const T* __restrict__ 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) attn_decode16_kernel(const T* __restrict__ qkv, const T* __restrict__ kc,
                                                             const T* __restrict__ vc, int H, int S, int n,
-                                                            T* __restrict__ o, float* __restrict__ sbuf) {
+                                                            T* __restrict__ o, float* __restrict__ sbuf,
+                                                            const int32_t* __restrict__ d_pos) {
+  if (d_pos) n = decode_pos(d_pos, S) + 1;
   constexpr int NT = 256, LK = D / 8, KPI = 64 / LK, KPB = KPI * (NT / 64);
   __shared__ float s_red[NT / 64];
   __shared__ float s_part[NT / 64][D];
@@ -196,35 +202,49 @@ __global__ void __launch_bounds__(256) attn_decode16_kernel(const T* __restrict_
 }
 
 template <typename E>
-void launch_kv_store(const E* qkv, int B, int T_, int C, int S, int t0, E* kc, E* vc, hipStream_t s) {
-  hipLaunchKernelGGL(kv_store_kernel<E>, dim3(B * T_), dim3(256), 0, s, qkv, B, T_, C, S, t0, kc, vc);
+void launch_kv_store(const E* qkv, int B, int T_, int C, int S, int t0, E* kc, E* vc, hipStream_t s,
+                     const int32_t* d_pos) {
+  hipLaunchKernelGGL(kv_store_kernel<E>, dim3(B * T_), dim3(256), 0, s, qkv, B, T_, C, S, t0, kc, vc, d_pos);
 }
-template void launch_kv_store<float>(const float*, int, int, int, int, int, float*, float*, hipStream_t);
-template void launch_kv_store<bf16>(const bf16*, int, int, int, int, int, bf16*, bf16*, hipStream_t);
-template void launch_kv_store<f16>(const f16*, int, int, int, int, int, f16*, f16*, hipStream_t);
+template void launch_kv_store<float>(const float*, int, int, int, int, int, float*, float*, hipStream_t,
+                                     const int32_t*);
+template void launch_kv_store<bf16>(const bf16*, int, int, int, int, int, bf16*, bf16*, hipStream_t, const int32_t*);
+template void launch_kv_store<f16>(const f16*, int, int, int, int, int, f16*, f16*, hipStream_t, const int32_t*);
+
+__global__ void fill_pos_kernel(int32_t* __restrict__ dst, const int32_t* __restrict__ d_pos, int S, long n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = decode_pos(d_pos, S);
+}
+void launch_fill_pos(int32_t* dst, const int32_t* d_pos, int S, long n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(fill_pos_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, d_pos, S, n);
+}
 
 template <typename T>
 int launch_attn_decode(const T* qkv, const T* kc, const T* vc, int B, int H, int D, int S, int n, T* o, float* sbuf,
-                       hipStream_t s) {
+                       hipStream_t s, const int32_t* d_pos) {
   if (D != 64 && D != 32) return -1;
   if constexpr (sizeof(T) == 2) {
     if (D == 64)
-      hipLaunchKernelGGL((attn_decode16_kernel<T, 64>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf);
+      hipLaunchKernelGGL((attn_decode16_kernel<T, 64>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf,
+                         d_pos);
     else
-      hipLaunchKernelGGL((attn_decode16_kernel<T, 32>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf);
+      hipLaunchKernelGGL((attn_decode16_kernel<T, 32>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf,
+                         d_pos);
   } else {
     if (D == 64)
-      hipLaunchKernelGGL((attn_decode_kernel<T, 64>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf);
+      hipLaunchKernelGGL((attn_decode_kernel<T, 64>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf,
+                         d_pos);
     else
-      hipLaunchKernelGGL((attn_decode_kernel<T, 32>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf);
+      hipLaunchKernelGGL((attn_decode_kernel<T, 32>), dim3(B * H), dim3(256), 0, s, qkv, kc, vc, H, S, n, o, sbuf,
+                         d_pos);
   }
   return 0;
 }
 template int launch_attn_decode<float>(const float*, const float*, const float*, int, int, int, int, int, float*,
-                                       float*, hipStream_t);
+                                       float*, hipStream_t, const int32_t*);
 template int launch_attn_decode<bf16>(const bf16*, const bf16*, const bf16*, int, int, int, int, int, bf16*, float*,
-                                      hipStream_t);
+                                      hipStream_t, const int32_t*);
 template int launch_attn_decode<f16>(const f16*, const f16*, const f16*, int, int, int, int, int, f16*, float*,
-                                     hipStream_t);
+                                     hipStream_t, const int32_t*);
 
 }  // namespace lm

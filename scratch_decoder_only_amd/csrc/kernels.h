@@ -189,11 +189,21 @@ void launch_make_shadow(const float* p, long n, uint16_t* shadow, bool to_f16, h
 // Key/value cache (per layer K [B][S][C] then V [B][S][C]): rows t0 .. t0+T-1
 // of each row b from qkv [B*T, 3C]; one query per (row, head) against cache
 // positions 0 .. n-1 (sbuf: B*H*S floats of scratch).
+// d_pos (nullable): the generation position in device memory, read when the
+// kernels run (so a captured graph can be replayed at later positions),
+// clamped to [1, S-1]; it then replaces t0 (kv_store) and n = pos + 1.
 template <typename E>
-void launch_kv_store(const E* qkv, int B, int T_, int C, int S, int t0, E* kc, E* vc, hipStream_t s);
+void launch_kv_store(const E* qkv, int B, int T_, int C, int S, int t0, E* kc, E* vc, hipStream_t s,
+                     const int32_t* d_pos = nullptr);
 template <typename T>
 int launch_attn_decode(const T* qkv, const T* kc, const T* vc, int B, int H, int D, int S, int n, T* o, float* sbuf,
-                       hipStream_t s);
+                       hipStream_t s, const int32_t* d_pos = nullptr);
+// dst[0 .. n-1] = *d_pos clamped to [1, S-1]
+void launch_fill_pos(int32_t* dst, const int32_t* d_pos, int S, long n, hipStream_t s);
+__device__ __forceinline__ int decode_pos(const int32_t* d_pos, int S) {
+  const int p = *d_pos;
+  return p < 1 ? 1 : (p > S - 1 ? S - 1 : p);
+}
 // Next token of each of `rows` logit rows (row r at logits + r * ld, V
 // columns): greedy when temperature <= 0, else top-k sampling with the given
 // uniforms; out [rows].

@@ -169,3 +169,82 @@ def test_decode_rejects_bad_positions(sd):
         model.decode(tok, 0, cache)
     with pytest.raises(RuntimeError):
         model.decode(tok, shape.max_seq, cache)
+
+
+# ------------------------------------------------- device position and graphs
+
+def _prefilled(sd, name, B, T0):
+    shape = synth.SHAPES[name]
+    model = sd.Model(shape, max_batch=B)
+    model.set(sd.LM_PARAMS, synth.init_params(shape))
+    toks = dev(np.ascontiguousarray(synth.make_batch(shape).tokens[:B]))
+    cache = model.kv_cache(B)
+    cache.zero_()
+    model.prefill(toks[:, :T0].contiguous(), cache)
+    return shape, model, toks, cache
+
+
+@pytest.mark.parametrize("name", ["C1", "C2"])
+def test_decode_at_equals_decode(sd, name):
+    """The device-position variant runs the same kernels: bit-identical logits
+    and cache contents."""
+    t = torch()
+    B, T0 = 2, 9
+    shape, model, toks, cache = _prefilled(sd, name, B, T0)
+    cache2 = cache.clone()
+    pos_d = t.zeros(1, dtype=t.int32, device="cuda")
+    for p in range(T0, T0 + 4):
+        a = model.decode(toks[:, p].contiguous(), p, cache)
+        pos_d.fill_(p)
+        b = model.decode_at(toks[:, p].contiguous(), pos_d, cache2)
+        t.cuda.synchronize()
+        assert t.equal(a, b), p
+    assert t.equal(cache, cache2)
+
+
+def test_decode_graph_replays_match_eager(sd):
+    """A captured decode step replayed at successive positions, with eager
+    work on the stream between replays, gives the eager logits bit for bit at
+    every replay."""
+    t = torch()
+    B, T0 = 4, 12
+    shape, model, toks, cache = _prefilled(sd, "C2", B, T0)
+    cache_g = cache.clone()
+    dg = sd.DecodeGraph(model, cache_g, B)
+    for p in range(T0, T0 + 6):
+        ref = model.decode(toks[:, p].contiguous(), p, cache).clone()
+        _ = (t.arange(1000, device="cuda", dtype=t.float32) * 2).sum()  # unrelated eager work
+        got = dg.step(toks[:, p], p).clone()
+        t.cuda.synchronize()
+        assert t.equal(ref, got), p
+    assert dg.graph is not None
+
+
+@pytest.mark.parametrize("temperature,top_k", [(0.0, 0), (1.0, 20)])
+def test_generate_with_graph_equals_eager(sd, temperature, top_k):
+    t = torch()
+    shape = synth.SHAPES["C1"]
+    model = sd.Model(shape, max_batch=4)
+    model.set(sd.LM_PARAMS, synth.init_params(shape))
+    prompt = dev(synth.make_batch(shape).tokens[:4, :16])
+    a = sd.generate(model, prompt, 10, temperature=temperature, top_k=top_k, seed=7)
+    b = sd.generate(model, prompt, 10, temperature=temperature, top_k=top_k, seed=7, graph=True)
+    assert t.equal(a, b)
+
+
+def test_decode_at_clamps_the_position(sd):
+    """A device position past the cache is clamped to max_seq - 1: the same
+    result as decoding there, and nothing outside the cache is touched."""
+    t = torch()
+    B, T0 = 2, 8
+    shape, model, toks, cache = _prefilled(sd, "C1", B, T0)
+    cache2 = cache.clone()
+    S = shape.max_seq
+    tok = toks[:, T0].contiguous()
+    a = model.decode(tok, S - 1, cache)
+    b = model.decode_at(tok, t.tensor([S + 7], dtype=t.int32, device="cuda"), cache2)
+    t.cuda.synchronize()
+    assert t.equal(a, b)
+    assert t.equal(cache, cache2)
+    with pytest.raises(RuntimeError):
+        model.decode_at(tok, None, cache2)
