@@ -169,6 +169,23 @@ def test_gemm_epilogues_wide(sd, prec, epi):
         assert rel(host(C), oracle.linear_fwd(X, W) * oracle.gelu_grad(u)) <= tol(prec, False)
 
 
+@pytest.mark.parametrize("prec", [1, 2])
+def test_gemm_store_16bit_tall(sd, prec):
+    """The QKV-projection shape class (K-contiguous operands, 16-bit store with
+    bias, M >= 4096) runs on the 192 x 128 tiles: ragged in M (8200 = 42 x 192 +
+    136), N and K."""
+    t = torch()
+    M, N, K = 8200, 264, 200
+    rng = np.random.default_rng(41 + prec)
+    print(f"gemm tall store prec={prec}", flush=True)
+    X, W = _operands(rng, prec, (M, K), (N, K), scale=0.3)
+    bias = rng.standard_normal(N).astype(np.float32)
+    C = t.zeros((M, N), dtype=act_dtype(prec), device="cuda")
+    sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, C, N, sd.EPI_STORE, bias=dev(bias))
+    t.cuda.synchronize()
+    assert rel(host(C), oracle.linear_fwd(X, W, bias)) <= tol(prec, False)
+
+
 def test_gemm_output_row_limit(sd):
     """Rows >= M_out are computed but never stored (the padded vocabulary)."""
     t = torch()
