@@ -20,6 +20,7 @@
 // fp32 path: fp32 matrix and vector peaks are equal on this chip (157 TF), so
 // the fp32 GEMM is a plain LDS-tiled FMA kernel (64 x 64 tile, 4 x 4 per
 // thread).
+#include <algorithm>
 #include <cstdlib>
 #include <type_traits>
 
@@ -85,6 +86,16 @@ __device__ __forceinline__ void st8_h(void* p, const float* v) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = H16<E>::pack(v[2 * i], v[2 * i + 1]);
   *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+// 8 values as 16-bit through a buffer resource (an offset past the range is
+// dropped; the store still counts as an outstanding memory operation)
+typedef unsigned int w4_t __attribute__((ext_vector_type(4)));
+template <typename E>
+__device__ __forceinline__ void bst8_h(__amdgpu_buffer_rsrc_t r, unsigned off, const float* v) {
+  w4_t w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = H16<E>::pack(v[2 * i], v[2 * i + 1]);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, 0);
 }
 __device__ __forceinline__ void ld8_f32(const float* p, float* v) {
   const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
@@ -843,19 +854,34 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
   // the start of the epilogue. (Two passes of the GELU input take 32 VGPRs,
   // one pass of the fp32 residual as many.)
   constexpr bool PRE = (EPI == EPI_RESID || EPI == EPI_DGELU) && TM <= 2;
+  // 16-bit plain and GELU outputs: the next unit's first loads are issued
+  // before the outputs, which go out through buffer stores (an out-of-range
+  // offset is dropped but still counted), so the next unit's first wait can
+  // leave exactly NST stores of each wavefront in flight
+  constexpr bool EARLY = ((EPI == EPI_STORE && TM <= 3) || (EPI == EPI_GELU && TM <= 2)) && H && S == 2 && !PRE;
   constexpr int PRE_I = EPI == EPI_DGELU ? TM : 1;
   uint4 pre[PRE ? TM : 1][PRE ? NQ : 1];
+  // Through a buffer resource from the tile's origin: every lane issues its
+  // load (an offset past the range reads zeros), so the number of loads in
+  // flight after a unit's first K steps is known exactly.
   auto load_pre = [&](int tm, int tn, int i) {
+    constexpr int ES = EPI == EPI_DGELU ? 2 : 4;  // 8 16-bit or 4 fp32 values
+    const long r0 = (long)tm * BM, c0 = (long)tn * BN;
+    const long ld = EPI == EPI_DGELU ? p.ld_aux : p.ldr;
+    const char* base = EPI == EPI_DGELU ? reinterpret_cast<const char*>(p.aux) : reinterpret_cast<const char*>(p.R);
+    const long n = r0 < p.M_out ? ((p.M_out - 1 - r0) * ld + p.N - c0) * ES : 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (r0 * ld + c0) * ES), (short)0, (int)min(n, (long)0x7fffffff), 0x00020000);
+    // offsets within the tile fit in 32 bits (the dispatcher checks the
+    // leading dimensions)
+    const int ldi = (int)ld, rows = (int)min((long)BM, p.M_out - r0), cols = (int)min((long)BN, p.N - c0);
+    const int lr0 = wm * WTM + i * 32 + lane / LPR, lc = wn * WTN + (lane % LPR) * CW;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const long row = (long)tm * BM + wm * WTM + i * 32 + q * RPQ + lane / LPR;
-      const long col = (long)tn * BN + wn * WTN + (lane % LPR) * CW;
-      const bool ok = row < p.M_out && col < p.N;
-      if constexpr (EPI == EPI_DGELU)  // 8 16-bit values
-        pre[i][q] = ok ? *reinterpret_cast<const uint4*>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col)
-                       : make_uint4(0, 0, 0, 0);
-      else  // 4 fp32 values
-        pre[i][q] = ok ? *reinterpret_cast<const uint4*>(p.R + row * p.ldr + col) : make_uint4(0, 0, 0, 0);
+      const int lr = lr0 + q * RPQ;
+      const bool ok = lr < rows && lc < cols;
+      const w4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, ok ? (lr * ldi + lc) * ES : (int)kOutOfRange, 0, 0);
+      pre[i][q] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   };
   // set up the loaders of unit u and issue its first S - 1 K steps
@@ -879,6 +905,11 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
     }
   };
 
+  constexpr int NST = EARLY ? TM * NQ * (EPI == EPI_GELU ? 2 : 1) : 0;
+  // the residual / GELU-input loads a unit's prologue issues after its first
+  // K steps' loads: the first step need not wait for them
+  constexpr int NPRE = PRE ? PRE_I * NQ : 0;
+  static_assert(NST + NPRE + (S - 2) * NLD < 64, "vmcnt range");
   f32x16_t acc[TM][TN];
   int round = 0;
   int u = pipe_unit(0, blockIdx.x, nb);
@@ -903,7 +934,13 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
           // own loads of step it complete (later steps may still be landing),
           // then every wavefront's: the stage is readable, and the stage read
           // at step it - 1 is free
-          if (it + S - 2 < nk) wait_vmcnt<(S - 2) * NLD>();
+          if (I == 0 && it0 == 0 && EARLY && round > 0) {
+            if (it + S - 2 < nk) wait_vmcnt<(S - 2) * NLD + NPRE + NST>();
+            else wait_vmcnt<NPRE + NST>();
+          } else if (I == 0 && it0 == 0) {
+            if (it + S - 2 < nk) wait_vmcnt<(S - 2) * NLD + NPRE>();
+            else wait_vmcnt<NPRE>();
+          } else if (it + S - 2 < nk) wait_vmcnt<(S - 2) * NLD>();
           else wait_vmcnt<0>();
           lds_barrier();
           const bf16* sa = stage(I_);
@@ -965,9 +1002,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
     // loads past the end of K (zeros into a stage nobody reads, possibly
     // stage 1): every wavefront waits for its own before the barrier, so no
     // direct load is still writing the regions. The next unit's first loads
-    // (into stage 0) are issued after the outputs: issued before, they would
-    // be in flight during the region reads, which the compiler's wait
-    // counting would then hold until the loads land.
+    // (into stage 0) never overlap the region accesses: the compiler's wait
+    // counting would hold those until the loads land. Where they follow the
+    // stores, the next unit's first wait also waits for those stores (the
+    // counter retires in issue order); for 16-bit plain and GELU outputs
+    // (EARLY) every pass is read back into registers first, then the loads
+    // are issued, then the stores, which the first wait leaves in flight.
     wait_vmcnt<0>();
     lds_barrier();
     if constexpr (PRE) {
@@ -980,9 +1020,35 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
                   "epilogue regions fit in stage 1");
     const int un = pipe_unit(round + 1, blockIdx.x, nb);
     const long col0 = (long)tn * BN + wn * WTN;
+    __amdgpu_buffer_rsrc_t rc, rx;
+    // EARLY: the bias of the lane's 8 columns (the same in every pass),
+    // loaded before anything else is in flight and added as the outputs of
+    // every pass are read back from the regions, all before the next unit's
+    // loads start
+    // (plain stores keep them packed, the GELU epilogue in fp32)
+    constexpr bool EG = EARLY && EPI == EPI_GELU, ES = EARLY && EPI == EPI_STORE;
+    float bv[EARLY ? 8 : 1];
+    f32x4_t outs[EG ? TM : 1][EG ? 2 * NQ : 1];
+    w4_t outp[ES ? TM : 1][ES ? NQ : 1];
+    if constexpr (EARLY) {
+      const long cl = col0 + (lane % LPR) * CW;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+      if (p.bias && cl < p.N) ld8_f32(p.bias + cl, bv);
+      // resources from the tile's origin to the last output element
+      const long r0 = (long)tm * BM, c0 = (long)tn * BN;
+      const long nc = r0 < p.M_out ? ((p.M_out - 1 - r0) * p.ldc + p.N - c0) * 2 : 0;
+      rc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<E*>(p.C) + r0 * p.ldc + c0, (short)0,
+                                             (int)min(nc, (long)0x7fffffff), 0x00020000);
+      if constexpr (EPI == EPI_GELU) {
+        const long na = r0 < p.M_out ? ((p.M_out - 1 - r0) * p.ld_aux + p.N - c0) * 2 : 0;
+        rx = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<E*>(p.aux) + r0 * p.ld_aux + c0, (short)0,
+                                               (int)min(na, (long)0x7fffffff), 0x00020000);
+      }
+    }
     // (the two halves of the wavefronts take the two arrays in separate code
     // paths, so each access has one known LDS object)
-    auto epilogue_via = [&](float* reg) {
+    auto epilogue_via = [&](float* __restrict__ reg) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int rw = lane & 31;
@@ -1006,6 +1072,16 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           const long row = row0 + q * RPQ + lane / LPR, col = col0 + (lane % LPR) * CW;
+          if constexpr (EG) {
+            outs[i][2 * q] = out[2 * q] + f32x4_t{bv[0], bv[1], bv[2], bv[3]};
+            outs[i][2 * q + 1] = out[2 * q + 1] + f32x4_t{bv[4], bv[5], bv[6], bv[7]};
+            continue;
+          } else if constexpr (ES) {
+            const f32x4_t lo = out[2 * q], hi = out[2 * q + 1];
+            outp[i][q] = w4_t{H16<E>::pack(lo[0] + bv[0], lo[1] + bv[1]), H16<E>::pack(lo[2] + bv[2], lo[3] + bv[3]),
+                              H16<E>::pack(hi[0] + bv[4], hi[1] + bv[5]), H16<E>::pack(hi[2] + bv[6], hi[3] + bv[7])};
+            continue;
+          }
           if (row >= p.M_out || col >= p.N) continue;
           if constexpr (PRE && EPI == EPI_DGELU) {
             const f32x4_t lo = out[2 * q], hi = out[2 * q + 1];
@@ -1033,7 +1109,34 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
     constexpr std::integral_constant<int, 1> I1{};
     if (wave < NW / 2) epilogue_via(reinterpret_cast<float*>(stage(I1)) + wave * REG);
     else epilogue_via(reinterpret_cast<float*>(stage_b(I1)) + (wave - NW / 2) * REG);
-    if (un < units) prologue(un);
+    if constexpr (!EARLY) {
+      if (un < units) prologue(un);
+    } else {
+      // (the bias loads are done by now; an explicit wait tells the compiler
+      // so, else the register uses it moves past the next loads wait for them)
+      wait_vmcnt<0>();
+      if (un < units) prologue(un);
+      const int rows = (int)min((long)BM, p.M_out - (long)tm * BM), cols = (int)min((long)BN, p.N - (long)tn * BN);
+      const int ldc = (int)p.ldc, ldx = (int)p.ld_aux;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int lr = wm * WTM + i * 32 + q * RPQ + lane / LPR, lc = wn * WTN + (lane % LPR) * CW;
+          const bool ok = lr < rows && lc < cols;
+          const unsigned oc = ok ? (unsigned)((lr * ldc + lc) * 2) : kOutOfRange;
+          if constexpr (ES) {
+            __builtin_amdgcn_raw_buffer_store_b128(outp[i][q], rc, (int)oc, 0, 0);
+          } else {
+            const f32x4_t lo = outs[i][2 * q], hi = outs[i][2 * q + 1];
+            float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            bst8_h<E>(rc, oc, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gelu_f(v[e]);
+            bst8_h<E>(rx, ok ? (unsigned)((lr * ldx + lc) * 2) : kOutOfRange, v);
+          }
+        }
+    }
   }
   // no direct load may still be writing LDS when the workgroup ends
   wait_vmcnt<0>();
@@ -1051,6 +1154,10 @@ static GemmArgs make_args(const GemmOp& op) {
 
 static bool check_16(const GemmOp& op) {
   if (op.lda % 8 || op.ldb % 8) return false;
+  // epilogue operands and outputs are addressed by 32-bit byte offsets within
+  // a tile of up to 256 rows
+  const long ld_max = std::max(op.ldc, std::max(op.R ? op.ldr : 0L, op.aux ? op.ld_aux : 0L));
+  if (256L * ld_max * 4 >= (1L << 31)) return false;
   // 8-column epilogue chunks: N and every leading dimension of the outputs
   if (op.N % 8 || op.ldc % 8 || (op.R && op.ldr % 8) || (op.aux && op.ld_aux % 8)) return false;
   if ((op.a_kc || op.b_kc) && op.K % 8) return false;

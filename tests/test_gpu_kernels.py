@@ -186,6 +186,37 @@ def test_gemm_store_16bit_tall(sd, prec):
     assert rel(host(C), oracle.linear_fwd(X, W, bias)) <= tol(prec, False)
 
 
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("epi,b_kc", [("store", True), ("store", False), ("gelu", True), ("gelu", False)])
+def test_gemm_persistent_rounds(sd, prec, epi, b_kc):
+    """More tiles than the persistent grid holds (731 units of 192 x 128 for
+    the K-contiguous store, 1105 of 128 x 128 otherwise, for 512 blocks), so
+    blocks run several units and a unit's first loads overlap the previous
+    unit's stores; ragged in M (8200), N (2056) and K (200), with bias."""
+    t = torch()
+    M, N, K = 8200, 2056, 200
+    rng = np.random.default_rng(57 + prec + 2 * b_kc)
+    print(f"gemm persistent rounds prec={prec} epi={epi} b_kc={b_kc}", flush=True)
+    X, W = _operands(rng, prec, (M, K), (N, K), scale=0.3)
+    bias = rng.standard_normal(N).astype(np.float32)
+    adt = act_dtype(prec)
+    Wd = act(W, prec) if b_kc else act(np.ascontiguousarray(W.T), prec)
+    ldb = K if b_kc else N
+    lin = oracle.linear_fwd(X, W, bias)
+    C = t.zeros((M, N), dtype=adt, device="cuda")
+    if epi == "store":
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, Wd, ldb, b_kc, C, N, sd.EPI_STORE, bias=dev(bias))
+        t.cuda.synchronize()
+        assert rel(host(C), lin) <= tol(prec, False)
+    else:
+        Aout = t.zeros((M, N), dtype=adt, device="cuda")
+        sd.gemm(prec, M, N, K, act(X, prec), K, True, Wd, ldb, b_kc, C, N, sd.EPI_GELU, aux=Aout, ld_aux=N,
+                bias=dev(bias))
+        t.cuda.synchronize()
+        assert rel(host(C), lin) <= tol(prec, False)
+        assert rel(host(Aout), oracle.gelu(lin)) <= tol(prec, False)
+
+
 def test_gemm_output_row_limit(sd):
     """Rows >= M_out are computed but never stored (the padded vocabulary)."""
     t = torch()
