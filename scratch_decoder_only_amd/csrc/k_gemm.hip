@@ -383,15 +383,18 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
     pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
     k_range(z, k_begin, k_end, nk);
     const int m0 = tm * BM, n0 = tn * BN;
+    // every thread issues its residual loads (outside the output: from the
+    // residual's first element, the values then dropped), so the compiler
+    // counts the loads in flight exactly and the stores need not wait for
+    // one another
     auto load_r = [&](int w, int q, float4& lo, float4& hi) {
       const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
       const long row = m0 + w * WTM + r, col = n0 + c8;
-      if (row < p.M_out && col < p.N) {
-        lo = *reinterpret_cast<const float4*>(p.R + row * p.ldr + col);
-        hi = *reinterpret_cast<const float4*>(p.R + row * p.ldr + col + 4);
-      } else {
-        lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      const bool ok = row < p.M_out && col < p.N;
+      const float* src = p.R + (ok ? row * p.ldr + col : 0);
+      lo = *reinterpret_cast<const float4*>(src);
+      hi = *reinterpret_cast<const float4*>(src + 4);
+      if (!ok) lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
     };
     if constexpr (PRE_R) {
 #pragma unroll
@@ -515,6 +518,17 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
         __syncthreads();
       }
     } else if constexpr (PRE_R) {
+      // the bias of the thread's 8 columns, the same in every chunk, loaded
+      // once: a load per chunk would wait for the stores before it (the
+      // vector-memory counter retires in issue order)
+      static_assert(NT % (BN / 8) == 0, "a thread's chunks share their columns");
+      float bcol[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bcol[i] = 0.f;
+      {
+        const long col = n0 + (tid % (BN / 8)) * 8;
+        if (p.bias && col < p.N) ld8_f32(p.bias + col, bcol);
+      }
 #pragma unroll
       for (int w = 0; w < WGM; ++w) {
         float4 rnext[2 * CPT];
@@ -528,13 +542,10 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
           const int c = tid + q * NT, r = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
           const long row = m0 + w * WTM + r, col = n0 + c8;
           if (row < p.M_out && col < p.N) {
-            float v[8], b[8];
+            float v[8];
             ld8_f32(sC + r * CP + c8, v);
-            if (p.bias) {
-              ld8_f32(p.bias + col, b);
 #pragma unroll
-              for (int i = 0; i < 8; ++i) v[i] += b[i];
-            }
+            for (int i = 0; i < 8; ++i) v[i] += bcol[i];
             const float4 lo = rpre[2 * q], hi = rpre[2 * q + 1];
             v[0] += lo.x; v[1] += lo.y; v[2] += lo.z; v[3] += lo.w;
             v[4] += hi.x; v[5] += hi.y; v[6] += hi.z; v[7] += hi.w;
@@ -1010,10 +1021,6 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
     // are issued, then the stores, which the first wait leaves in flight.
     wait_vmcnt<0>();
     lds_barrier();
-    if constexpr (PRE) {
-#pragma unroll
-      for (int i = PRE_I; i < TM; ++i) load_pre(tm, tn, i);
-    }
     static_assert(WTN == 64, "epilogue regions hold 64 columns");
     constexpr int NW = WGM * WGN, REG = 32 * WTN;
     static_assert((NW / 2) * REG * 4 <= LA::ELEMS * 2 && (NW / 2) * REG * 4 <= LB::ELEMS * 2,
@@ -1022,10 +1029,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
     const long col0 = (long)tn * BN + wn * WTN;
     __amdgpu_buffer_rsrc_t rc, rx;
     // EARLY: the bias of the lane's 8 columns (the same in every pass),
-    // loaded before anything else is in flight and added as the outputs of
-    // every pass are read back from the regions, all before the next unit's
-    // loads start
-    // (plain stores keep them packed, the GELU epilogue in fp32)
+    // loaded once before anything else is in flight (a load per store would
+    // wait for the stores before it, the counter retiring in issue order) and
+    // added as the outputs of every pass are read back from the regions
+    // (plain stores keep them packed, the GELU epilogue in fp32), all before
+    // the next unit's loads start. (The other paths load it per chunk: held
+    // in registers it measured slower on the wide bias-free GEMMs.)
     constexpr bool EG = EARLY && EPI == EPI_GELU, ES = EARLY && EPI == EPI_STORE;
     float bv[EARLY ? 8 : 1];
     f32x4_t outs[EG ? TM : 1][EG ? 2 * NQ : 1];
@@ -1035,6 +1044,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
 #pragma unroll
       for (int e = 0; e < 8; ++e) bv[e] = 0.f;
       if (p.bias && cl < p.N) ld8_f32(p.bias + cl, bv);
+    }
+    if constexpr (PRE) {
+#pragma unroll
+      for (int i = PRE_I; i < TM; ++i) load_pre(tm, tn, i);
+    }
+    if constexpr (EARLY) {
       // resources from the tile's origin to the last output element
       const long r0 = (long)tm * BM, c0 = (long)tn * BN;
       const long nc = r0 < p.M_out ? ((p.M_out - 1 - r0) * p.ldc + p.N - c0) * 2 : 0;
