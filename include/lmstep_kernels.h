@@ -93,9 +93,9 @@ int lmk_xent(int precision, void* z, int64_t ldz, int M, int V, const int32_t* t
              float* ws_rows, uint32_t* flags, const float* loss_scale, void* stream);
 
 /* Stable counting sort of keys [M] in [0, nkeys): counts/offsets/chunk_base
- * [nkeys+1], perm [M] (rows of key v at perm[offsets[v] .. offsets[v+1]),
- * ascending); rank [M] int32 scratch (each row's count of equal keys before
- * it). */
+ * [nkeys+1], 16-byte aligned, perm [M] (rows of key v at
+ * perm[offsets[v] .. offsets[v+1]), ascending); rank [M] int32 scratch (each
+ * row's count of equal keys before it). -1 on a bad size or alignment. */
 int lmk_csr(const int32_t* keys, int M, int nkeys, int32_t* counts, int32_t* offsets, int32_t* chunk_base,
             int32_t* perm, int32_t* rank, void* stream);
 /* dst[v,:] (+)= sum of dx rows with key v, in perm order (after lmk_csr).

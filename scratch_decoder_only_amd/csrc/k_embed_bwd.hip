@@ -27,62 +27,113 @@ __global__ void csr_count_kernel(const int32_t* __restrict__ keys, int M, int nk
 }
 
 // Exclusive scans of counts (-> offsets) and of ceil(count / kSegRows)
-// (-> chunk_base), each with nkeys + 1 entries. One block of 1024 threads
-// walks the keys in rounds of 4096 (4 consecutive keys per thread, loads
-// coalesced across the block): per round a wavefront scan, the 16 wavefront
-// totals in LDS, and a running carry.
-__global__ void __launch_bounds__(1024) csr_scan_kernel(const int32_t* __restrict__ counts, int nkeys,
-                                                        int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ chunk_base) {
-  __shared__ int s_a[16], s_b[16];
+// (-> chunk_base), each with nkeys + 1 entries, by one block of 512 threads
+// in rounds of 4096 keys, the loads of RB rounds issued at once (8
+// consecutive keys per thread per round, held in registers), so the memory
+// latency is paid once per RB rounds rather than once per round: per round a
+// wavefront scan; then the first wavefront turns the wavefront totals of the
+// batch into exclusive prefixes in LDS (carrying the running totals between
+// batches), and each thread writes its keys.
+template <int RB>
+__global__ void __launch_bounds__(512) csr_scan_pre_kernel(const int32_t* __restrict__ counts, int nkeys,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ chunk_base) {
+  constexpr int NW = 8, KPT = 8, RK = 512 * KPT;
+  __shared__ int s_a[RB][NW], s_b[RB][NW];
   const int n = nkeys + 1;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  int carry_a = 0, carry_b = 0;
-  for (int base = 0; base < n; base += 4096) {
-    const int i0 = base + 4 * t;
-    int c[4], a = 0, b = 0;
+  int carry_a = 0, carry_b = 0;  // (wavefront 0)
+  for (int base = 0; base < n; base += RB * RK) {
+    int c[RB][KPT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      c[u] = i0 + u < nkeys ? counts[i0 + u] : 0;
-      a += c[u];
-      b += (c[u] + kSegRows - 1) / kSegRows;
+    for (int r = 0; r < RB; ++r) {
+      const int i0 = base + r * RK + t * KPT;
+      if (i0 + KPT <= nkeys) {  // two 16-byte loads (the arrays are 16-byte aligned)
+        const int4 lo = *reinterpret_cast<const int4*>(counts + i0), hi = *reinterpret_cast<const int4*>(counts + i0 + 4);
+        c[r][0] = lo.x; c[r][1] = lo.y; c[r][2] = lo.z; c[r][3] = lo.w;
+        c[r][4] = hi.x; c[r][5] = hi.y; c[r][6] = hi.z; c[r][7] = hi.w;
+      } else {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) c[r][u] = i0 + u < nkeys ? counts[i0 + u] : 0;
+      }
     }
-    int xa = a, xb = b;  // inclusive wavefront scans
+    int ea[RB], eb[RB];  // exclusive prefix of the thread's keys within its wavefront
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int ya = __shfl_up(xa, o, 64), yb = __shfl_up(xb, o, 64);
-      if (lane >= o) {
-        xa += ya;
-        xb += yb;
+    for (int r = 0; r < RB; ++r) {
+      int a = 0, b = 0;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        a += c[r][u];
+        b += (c[r][u] + kSegRows - 1) / kSegRows;
+      }
+      int xa = a, xb = b;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int ya = __shfl_up(xa, o, 64), yb = __shfl_up(xb, o, 64);
+        if (lane >= o) {
+          xa += ya;
+          xb += yb;
+        }
+      }
+      ea[r] = xa - a;
+      eb[r] = xb - b;
+      if (lane == 63) {
+        s_a[r][w] = xa;
+        s_b[r][w] = xb;
       }
     }
     __syncthreads();
-    if (lane == 63) {
-      s_a[w] = xa;
-      s_b[w] = xb;
+    if (w == 0) {
+      // the RB x NW wavefront totals of the batch, one per lane in key order,
+      // scanned across the wavefront
+      static_assert(RB * NW <= 64, "one wavefront holds the batch's totals");
+      const int r = lane / NW, q = lane % NW;
+      const bool in = lane < RB * NW;
+      const int va = in ? s_a[r][q] : 0, vb = in ? s_b[r][q] : 0;
+      int xa = va, xb = vb;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int ya = __shfl_up(xa, o, 64), yb = __shfl_up(xb, o, 64);
+        if (lane >= o) {
+          xa += ya;
+          xb += yb;
+        }
+      }
+      if (in) {
+        s_a[r][q] = carry_a + xa - va;
+        s_b[r][q] = carry_b + xb - vb;
+      }
+      carry_a += __shfl(xa, 63, 64);
+      carry_b += __shfl(xb, 63, 64);
     }
     __syncthreads();
-    int pa = 0, pb = 0, ta = 0, tb = 0;
-    for (int q = 0; q < 16; ++q) {
-      if (q < w) {
-        pa += s_a[q];
-        pb += s_b[q];
-      }
-      ta += s_a[q];
-      tb += s_b[q];
-    }
-    int ra = carry_a + pa + xa - a, rb = carry_b + pb + xb - b;  // exclusive prefix of key i0
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (i0 + u < n) {
-        offsets[i0 + u] = ra;
-        chunk_base[i0 + u] = rb;
+    for (int r = 0; r < RB; ++r) {
+      int ra = s_a[r][w] + ea[r], rb = s_b[r][w] + eb[r];
+      int oa[KPT], ob[KPT];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        oa[u] = ra;
+        ob[u] = rb;
+        ra += c[r][u];
+        rb += (c[r][u] + kSegRows - 1) / kSegRows;
       }
-      ra += c[u];
-      rb += (c[u] + kSegRows - 1) / kSegRows;
+      const int i0 = base + r * RK + t * KPT;
+      if (i0 + KPT <= n) {
+        *reinterpret_cast<int4*>(offsets + i0) = make_int4(oa[0], oa[1], oa[2], oa[3]);
+        *reinterpret_cast<int4*>(offsets + i0 + 4) = make_int4(oa[4], oa[5], oa[6], oa[7]);
+        *reinterpret_cast<int4*>(chunk_base + i0) = make_int4(ob[0], ob[1], ob[2], ob[3]);
+        *reinterpret_cast<int4*>(chunk_base + i0 + 4) = make_int4(ob[4], ob[5], ob[6], ob[7]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u)
+          if (i0 + u < n) {
+            offsets[i0 + u] = oa[u];
+            chunk_base[i0 + u] = ob[u];
+          }
+      }
     }
-    carry_a += ta;
-    carry_b += tb;
+    __syncthreads();  // the prefixes are read before the next batch overwrites them
   }
 }
 
@@ -193,7 +244,10 @@ __global__ void __launch_bounds__(256) segsum_keys_kernel(int C, int nkeys, cons
 void launch_csr(const int32_t* keys, int M, int nkeys, EmbedBwdWs ws, hipStream_t s) {
   launch_fill_u32(reinterpret_cast<uint32_t*>(ws.counts), 0u, nkeys + 1, s);
   if (M > 0) hipLaunchKernelGGL(csr_count_kernel, dim3((M + 255) / 256), dim3(256), 0, s, keys, M, nkeys, ws.counts);
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, ws.counts, nkeys, ws.offsets, ws.chunk_base);
+  if (nkeys + 1 <= 4096)
+    hipLaunchKernelGGL(csr_scan_pre_kernel<1>, dim3(1), dim3(512), 0, s, ws.counts, nkeys, ws.offsets, ws.chunk_base);
+  else
+    hipLaunchKernelGGL(csr_scan_pre_kernel<8>, dim3(1), dim3(512), 0, s, ws.counts, nkeys, ws.offsets, ws.chunk_base);
   if (M > 0) {
     const int nb = (M + 255) / 256;
     launch_fill_u32(reinterpret_cast<uint32_t*>(ws.rank), 0u, M, s);

@@ -139,6 +139,8 @@ int lmk_xent(int precision, void* z, int64_t ldz, int M, int V, const int32_t* t
 int lmk_csr(const int32_t* keys, int M, int nkeys, int32_t* counts, int32_t* offsets, int32_t* chunk_base,
             int32_t* perm, int32_t* rank, void* stream) {
   if (M < 0 || nkeys <= 0 || (M > 0 && !rank)) return -1;
+  auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  if (!a16(counts) || !a16(offsets) || !a16(chunk_base)) return -1;
   EmbedBwdWs w{counts, offsets, chunk_base, perm, nullptr, rank};
   launch_csr(keys, M, nkeys, w, S(stream));
   return 0;

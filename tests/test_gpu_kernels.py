@@ -446,8 +446,11 @@ def test_cross_entropy(sd, prec, V):
 
 # ------------------------------------------------ embedding backward (CSR)
 
-@pytest.mark.parametrize("nkeys,M", [(1000, 5000), (64, 3000), (50257, 8192)])
+@pytest.mark.parametrize("nkeys,M", [(1000, 5000), (64, 3000), (50257, 8192), (4095, 3000), (4096, 3000),
+                                     (70000, 20000)])
 def test_csr_bit_exact_and_segment_sums(sd, nkeys, M):
+    """Key counts scanned in one round of 4096 (up to 4095 keys: nkeys + 1
+    entries), in one batch of rounds, and over several batches (70000)."""
     t = torch()
     import synth
     rng = np.random.Generator(np.random.PCG64(nkeys))
