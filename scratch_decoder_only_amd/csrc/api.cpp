@@ -269,7 +269,9 @@ void carve(lm_model* m, char* base) {
   m->col_part = c.take<float>(col_blocks * std::max(std::max(F, 3 * C), m->untied ? m->ldz : 0L));
   // per-block partial column sums of every MLP-in and QKV bias gradient,
   // reduced together after the backward
-  m->bias_part = c.take<float>(L * col_blocks * (F + 3 * C));
+  // (the MLP-in slot holds up to two partial rows per row block: those the
+  // GELU' GEMM epilogue writes)
+  m->bias_part = c.take<float>(L * col_blocks * (2 * F + 3 * C));
   m->gemm_ws_floats = 8L * std::max(F, 3 * C) * std::max(F, C);
   m->gemm_ws = c.take<float>(m->gemm_ws_floats);
   for (int k = 0; k < 2; ++k) {
@@ -586,8 +588,22 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   ColsumBatch lnb{};
   int n_ln = 0;
   const long col_blocks = (M + kColRows - 1) / kColRows;
-  auto fc_part = [&](int l) { return m->bias_part + (long)l * col_blocks * (F + 3 * C); };
-  auto qkv_part = [&](int l) { return fc_part(l) + col_blocks * F; };
+  auto fc_part = [&](int l) { return m->bias_part + (long)l * col_blocks * (2 * F + 3 * C); };
+  auto qkv_part = [&](int l) { return fc_part(l) + 2 * col_blocks * F; };
+  // the MLP-in bias gradient's partial sums come from the GELU' GEMM's
+  // epilogue where its kernel writes them (fc_rows rows), else from a column
+  // sum over its output (col_blocks rows)
+  long fc_rows = col_blocks;
+  bool fc_fused = false;
+  if (m->prec != 0) {
+    GemmOp probe = dx_op(m, m->g_act, M, C, 0, F, m->dbig, EPI_DGELU);
+    probe.aux = m->dbig; probe.ld_aux = F;
+    const int rows = gemm16_colsum_rows(probe);
+    if (rows > 0 && rows <= 2 * col_blocks) {
+      fc_fused = true;
+      fc_rows = rows;
+    }
+  }
   std::vector<float*> fc_pa(m->L), fc_oa(m->L), qkv_pa(m->L), qkv_oa(m->L);
   struct { std::vector<float*>& pa; std::vector<float*>& oa; } fcb{fc_pa, fc_oa}, qkvb{qkv_pa, qkv_oa};
   double ln_red_bytes = 0;
@@ -639,11 +655,13 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
     {
       GemmOp op = dx_op(m, g_act, M, C, b.w_proj, F, dbig, EPI_DGELU);
       op.aux = u; op.ld_aux = F;
+      if (fc_fused) op.colsum = fc_part(l);
       Lr.run("gemm_fc2_bwd_dx", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, op, s); });
     }
     // MLP in: u = y2 W_fc^T + b_fc
     Lr.run("gemm_fc1_bwd_dw", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, dw_op(dbig, M, F, y2, C, m->grads + b.w_fc), s); });
-    Lr.run("bias_grad", 0, Mf * F * A, [&] { launch_colsum_stage1<E>(dbig, F, (int)M, (int)F, fc_part(l), s); });
+    if (!fc_fused)
+      Lr.run("bias_grad", 0, Mf * F * A, [&] { launch_colsum_stage1<E>(dbig, F, (int)M, (int)F, fc_part(l), s); });
     fcb.pa[l] = fc_part(l);
     fcb.oa[l] = m->grads + b.b_fc;
     {
@@ -682,7 +700,7 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   // zero), dwpe[pos] = sum dx0
   Lr.run("layernorm_bwd_reduce", 0, ln_red_bytes, ln_reduce);
   // the MLP-in and QKV bias gradients from their partial sums, in batches
-  Lr.run("bias_grad_reduce", 0, 4.0 * col_blocks * (F + 3 * C) * m->L, [&] {
+  Lr.run("bias_grad_reduce", 0, 4.0 * (fc_rows * F + col_blocks * 3 * C) * m->L, [&] {
     for (int l0 = 0; l0 < m->L; l0 += kColsumBatch) {
       const int n = std::min(kColsumBatch, m->L - l0);
       ColsumBatch f{}, q{};
@@ -690,7 +708,7 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
         f.pa[i] = fcb.pa[l0 + i]; f.oa[i] = fcb.oa[l0 + i];
         q.pa[i] = qkvb.pa[l0 + i]; q.oa[i] = qkvb.oa[l0 + i];
       }
-      launch_colsum_partials_batch(f, n, (int)col_blocks, (int)F, s);
+      launch_colsum_partials_batch(f, n, (int)fc_rows, (int)F, s);
       launch_colsum_partials_batch(q, n, (int)col_blocks, (int)(3 * C), s);
     }
   });

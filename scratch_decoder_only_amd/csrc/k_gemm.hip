@@ -44,6 +44,7 @@ struct GemmArgs {
   int M_out;          // rows < M_out are stored
   int k_split;        // K elements per blockIdx.z slice
   long split_stride;  // floats between the partial outputs of two slices
+  float* colsum;      // GemmOp::colsum
 };
 
 // Epilogue of one output element (shared by both GEMM kernels and the
@@ -921,6 +922,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
   // K steps' loads: the first step need not wait for them
   constexpr int NPRE = PRE ? PRE_I * NQ : 0;
   static_assert(NST + NPRE + (S - 2) * NLD < 64, "vmcnt range");
+  // GELU' epilogue of 128-row tiles in wave rows of 64: the column sums of
+  // the outputs (GemmOp::colsum), per lane over its rows of the unit
+  constexpr bool CSUM = EPI == EPI_DGELU && PRE && H && BM == 128 && WGM == 2;
+  float csum[CSUM ? 8 : 1];
+#pragma unroll
+  for (int e = 0; e < (CSUM ? 8 : 1); ++e) csum[e] = 0.f;
   f32x16_t acc[TM][TN];
   int round = 0;
   int u = pipe_unit(0, blockIdx.x, nb);
@@ -1106,6 +1113,10 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
                           hi[0] * gelu_grad_f(H16<E>::lo(u.z)), hi[1] * gelu_grad_f(H16<E>::hi(u.z)),
                           hi[2] * gelu_grad_f(H16<E>::lo(u.w)), hi[3] * gelu_grad_f(H16<E>::hi(u.w))};
             st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
+            if constexpr (CSUM) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) csum[e] += v[e];
+            }
           } else if constexpr (PRE && EPI == EPI_RESID) {
             f32x4_t v = out[q];
             if (p.bias) v += *reinterpret_cast<const f32x4_t*>(p.bias + col);
@@ -1124,6 +1135,24 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
     constexpr std::integral_constant<int, 1> I1{};
     if (wave < NW / 2) epilogue_via(reinterpret_cast<float*>(stage(I1)) + wave * REG);
     else epilogue_via(reinterpret_cast<float*>(stage_b(I1)) + (wave - NW / 2) * REG);
+    if constexpr (CSUM) {
+      // lanes l, l + LPR, ... hold the same 8 columns: a fixed xor tree over
+      // them, then the wave row's 64-row sums of its 64 columns
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) csum[e] += __shfl_xor(csum[e], o, 64);
+      if (p.colsum && lane < LPR) {
+        const long col = col0 + lane * CW;
+        if (col < p.N) {
+          float* d = p.colsum + ((long)tm * WGM + wm) * p.N + col;
+          *reinterpret_cast<f32x4_t*>(d) = f32x4_t{csum[0], csum[1], csum[2], csum[3]};
+          *reinterpret_cast<f32x4_t*>(d + 4) = f32x4_t{csum[4], csum[5], csum[6], csum[7]};
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) csum[e] = 0.f;
+    }
     if constexpr (!EARLY) {
       if (un < units) prologue(un);
     } else {
@@ -1164,6 +1193,7 @@ static GemmArgs make_args(const GemmOp& op) {
   a.bias = op.bias; a.R = op.R; a.ldr = op.ldr; a.aux = op.aux; a.ld_aux = op.ld_aux;
   a.M = op.M; a.N = op.N; a.K = op.K; a.k_split = op.K; a.split_stride = 0;
   a.M_out = op.M_out > 0 && op.M_out < op.M ? op.M_out : op.M;
+  a.colsum = op.colsum;
   return a;
 }
 
@@ -1236,6 +1266,13 @@ static int pick_cfg(const GemmOp& op) {
   // epilogues)
   if (op.a_kc && op.b_kc && op.epi == EPI_STORE && op.M >= 4096 && !op.c_f32) return kCfgPipe192;
   return kCfgPipe128;
+}
+
+int gemm16_colsum_rows(const GemmOp& op) {
+  // the persistent 128 x 128 kernel's GELU' epilogue, in one K slice
+  if (op.epi != EPI_DGELU || (op.M_out > 0 && op.M_out < op.M)) return 0;
+  if (pick_cfg(op) != kCfgPipe128 || gemm16_splits(op) != 1) return 0;
+  return 2 * ((op.M + 127) / 128);
 }
 
 int gemm16_splits(const GemmOp& op) {
@@ -1371,6 +1408,7 @@ template <typename E>
 static int gemm16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
   if (op.M <= 0 || op.N <= 0) return 0;
   if (!check_16(op)) return -1;
+  if (op.colsum && gemm16_colsum_rows(op) == 0) return -1;
   GemmArgs a = make_args(op);
   int splits = gemm16_splits(op);
   if (splits > 1 && (long)splits * op.M * op.N > ws_floats) splits = 1;
@@ -1416,6 +1454,7 @@ static int dispatch_f32(const GemmOp& op, const GemmArgs& a, int splits, hipStre
 }
 
 int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
+  if (op.colsum) return -1;  // (16-bit GELU' epilogue only)
   if (op.M <= 0 || op.N <= 0) return 0;
   GemmArgs a = make_args(op);
   long tiles = (long)((op.M + 63) / 64) * ((op.N + 63) / 64);

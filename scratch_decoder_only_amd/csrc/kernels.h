@@ -42,6 +42,11 @@ struct GemmOp {
   long ld_aux = 0;
   int force_split = 0;  // > 0: use exactly this many K splits (tests)
   int M_out = 0;        // > 0: store only rows < M_out (rows M_out..M-1 are padding)
+  // EPI_DGELU, 16-bit, where gemm16_colsum_rows says the kernel writes them:
+  // the column sums of the output (fp32, before rounding) over each 64-row
+  // half of each 128-row block; row 2b + h of colsum [2 ceil(M / 128)][N]
+  // holds rows 128 b + 64 h .. + 63.
+  float* colsum = nullptr;
 };
 
 // Returns 0 or a negative code if the shape breaks the kernel's alignment
@@ -52,6 +57,9 @@ int gemm_f16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
 int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
 // Split count the 16-bit dispatcher would pick (for workspace sizing).
 int gemm16_splits(const GemmOp& op);
+// Rows of GemmOp::colsum the 16-bit dispatcher's kernel writes for op, or 0
+// where it cannot (then colsum must stay null).
+int gemm16_colsum_rows(const GemmOp& op);
 
 // -------------------------------------------------------------- rows etc.
 void launch_fill_u32(uint32_t* p, uint32_t v, long n, hipStream_t s);
