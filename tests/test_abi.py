@@ -101,3 +101,10 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
     # AdamW needs a multiple of 4 elements and step >= 1
     assert sd.lib.lmk_adamw(P, P, P, P, 6, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, P, P, None, 0, None) != 0
     assert sd.lib.lmk_adamw(P, P, P, P, 8, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0, P, P, None, 0, None) != 0
+    # the key-count arrays of the counting sort must be 16-byte aligned
+    Q = ctypes.c_void_p(260)
+    assert sd.lib.lmk_csr(P, 16, 64, Q, P, P, P, P, None) != 0
+    assert sd.lib.lmk_csr(P, 16, 64, P, P, Q, P, P, None) != 0
+    # 16-bit GEMM outputs are addressed with 32-bit offsets within a tile
+    assert sd.lib.lmk_gemm(1, 16, 16, 16, P, 16, 1, P, 16, 1, P, 1 << 22, 0, 0, None, None, 0, None, 0, 0, 0,
+                           None, 0, None) != 0
