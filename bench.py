@@ -77,9 +77,15 @@ TRAFFIC_SYMBOLS = {
     "adamw": "adamw_kernel(",
     "gemm_attnout_fwd": ("gemm16_kernel<128, 128, 2, 2, true, true, 1, float,", 2, 0),
     "gemm_fc2_fwd": ("gemm16_kernel<128, 128, 2, 2, true, true, 1, float,", 2, 1),
-    "attn_bwd_dkv": "attn_dkv_kernel<64>",
-    "attn_fwd": "attn_fwd_kernel<64>",
+    "attn_bwd_dkv": "attn_dkv_kernel<64, unsigned short>",
+    "attn_bwd_dq": "attn_dq_kernel<64, unsigned short>",
+    "attn_fwd": "attn_fwd_kernel<64, unsigned short>",
+    "layernorm_fwd": "ln_fwd_kernel<6, unsigned short>",
+    "layernorm_bwd": "ln_bwd_kernel<6, unsigned short>",
+    "xent": "xent_reg_kernel<unsigned short,",
 }
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters_c4_step.md")
+SIMDS = 1024  # 256 compute units x 4 SIMDs
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_c4_step.md")
 CALIB_BYTES = 1 << 30  # plain device copy used to scale the counters
 
@@ -157,6 +163,77 @@ def pmc_summary(fetch_dir, write_dir, out=TRAFFIC_FILE, cmd=""):
     print(out)
 
 
+def mfma_summary(pmc_dir, out=MFMA_FILE, cmd=""):
+    """MFMA utilisation of the GEMM and attention kernels from one rocprofv3
+    --pmc run with SQ_INSTS_VALU_MFMA_MOPS_BF16 (MFMA operations / 512),
+    SQ_VALU_MFMA_BUSY_CYCLES (matrix-core busy cycles summed over the SIMDs)
+    and GRBM_GUI_ACTIVE (GPU busy cycles per XCD): per kernel, the busy
+    fraction = MFMA busy cycles / (GPU cycles x SIMDs), which does not depend
+    on the clock, and the matrix flops the hardware executed (attention score
+    recomputation included)."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            d = per.setdefault(k, {})
+            c = r["Counter_Name"]
+            v = float(r["Counter_Value"])
+            if c == "GRBM_GUI_ACTIVE":
+                d[c] = max(d.get(c, 0.0), v)  # per XCD: the longest
+            else:
+                d[c] = d.get(c, 0.0) + v
+    by = {}
+    for (_, name), d in per.items():
+        if not ("gemm16" in name or "attn_" in name) or "GRBM_GUI_ACTIVE" not in d:
+            continue
+        e = by.setdefault(name, {"n": 0, "busy": 0.0, "gpu": 0.0, "mops": 0.0})
+        e["n"] += 1
+        e["busy"] += d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        e["gpu"] += d["GRBM_GUI_ACTIVE"]
+        e["mops"] += d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+    if not by:
+        raise SystemExit("no GEMM or attention dispatches with MFMA counters in " + pmc_dir)
+    tot_busy = sum(e["busy"] for e in by.values())
+    tot_gpu = sum(e["gpu"] for e in by.values())
+    rec = {"source_digest": source_digest(), "busy_frac": round(tot_busy / (tot_gpu * SIMDS), 4),
+           "mfma_flops": sum(e["mops"] for e in by.values()) * 512, "kernels": {}}
+    lines = []
+    for name, e in sorted(by.items(), key=lambda kv: -kv[1]["gpu"]):
+        frac = e["busy"] / (e["gpu"] * SIMDS)
+        rec["kernels"][name] = {"dispatches": e["n"], "busy_frac": round(frac, 4),
+                                "mfma_flops_per_dispatch": e["mops"] * 512 / e["n"]}
+        lines.append(f"| `{name[:100]}` | {e['n']} | {e['gpu'] / e['n']:.0f} | {frac:.3f} | "
+                     f"{e['mops'] * 512 / e['n'] / 1e9:.2f} |")
+    with open(out, "w") as fh:
+        fh.write("# MFMA utilisation from hardware counters (GPT-2-small-shaped step, C4)\n\n")
+        fh.write("Command (repository root, on one MI355X):\n\n```\n" + cmd + "\n```\n\n")
+        fh.write("Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE of the busiest XCD x "
+                 f"{SIMDS} SIMDs): the share of the kernel's GPU cycles in which the matrix cores were "
+                 "busy, whatever the clock ran at. MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the "
+                 "attention kernels' score recomputation included).\n\n")
+        fh.write(f"All GEMM and attention dispatches: busy fraction **{rec['busy_frac']:.3f}** "
+                 "(cycle-weighted).\n\n")
+        fh.write("| kernel | dispatches | GPU cycles / dispatch | MFMA busy | MFMA GFLOP / dispatch |\n"
+                 "|---|---:|---:|---:|---:|\n")
+        fh.write("\n".join(lines) + "\n\n")
+        fh.write("Record read by bench.py (ignored once the kernel sources differ from source_digest):\n\n")
+        fh.write("```json\n" + json.dumps(rec, indent=1) + "\n```\n")
+    print(out)
+
+
+def mfma_record():
+    try:
+        txt = open(MFMA_FILE).read()
+        rec = json.loads(txt[txt.index("```json") + 7: txt.rindex("```")])
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec
+
+
 def stats_summary(stats_csv, out, cmd="", steps=7):
     """Kernel table from a rocprofv3 --stats kernel_stats.csv (Name, Calls,
     TotalDurationNs, AverageNs), sorted by total time."""
@@ -215,12 +292,37 @@ def traffic_of(cls):
     return rec["classes"][cls]["bytes_per_launch"]
 
 
-def cpu_baseline(shape, budget_s=30.0):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads():
+    """Threads numpy's BLAS runs its products on (what the oracle's matmuls use)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return int(os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+
+
+def cpu_baseline(shape, batch=1):
     """The oracle (float64 numpy, untuned) on a bounded sample of the workload:
-    one full step at batch 1 (same width, depth, vocabulary and sequence)."""
+    one full step at `batch` rows (default 1; same width, depth, vocabulary and
+    sequence). A full GPT-2-small-shaped batch of 8 rows takes about a minute
+    on 16 host threads, beyond what the default run should spend on the
+    baseline; --cpu-batch 8 times it."""
     import oracle
     import synth
-    sample = shape.with_batch(1)
+    sample = shape.with_batch(batch)
     b = synth.make_batch(sample)
     params = synth.init_params(sample)
     zeros = {k: np.zeros_like(v, dtype=np.float64) for k, v in params.items()}
@@ -228,13 +330,10 @@ def cpu_baseline(shape, budget_s=30.0):
     oracle.train_step(params, zeros, zeros, sample, b.tokens, b.targets, b.doc_ids, step=1, lr=sample.lr,
                       weight_decay=sample.weight_decay, clip=sample.clip)
     dt = time.perf_counter() - t0
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    threads = int(os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or cores)
-    return {"value": sample.seq / dt, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
-            "sample": f"one full fp64 step at batch 1 x seq {sample.seq} of the same model ({dt:.1f} s)"}
+    threads = blas_threads()
+    return {"value": batch * sample.seq / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full fp64 step at batch {batch} x seq {sample.seq} of the same model ({dt:.1f} s)",
+            "cpu_model": cpu_model(), "blas_threads": threads}
 
 
 def main():
@@ -259,9 +358,15 @@ def main():
     ap.add_argument("--pmc-cmd", default="", help="command line recorded in the summary")
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
                     help="write the kernel table of a rocprofv3 --stats run and exit")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="summarise a rocprofv3 --pmc run of the MFMA counters and exit")
+    ap.add_argument("--cpu-batch", type=int, default=1, help="rows of the CPU oracle's timed step")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, cmd=args.pmc_cmd)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary, cmd=args.pmc_cmd)
         return
     if args.stats_summary:
         stats_summary(*args.stats_summary, cmd=args.pmc_cmd, steps=args.steps + args.warmup)
@@ -325,6 +430,11 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if shape.precision == "bf16" else "f32",
            "data": "synthetic (seeded Zipf token ids, random-init weights)",
            "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}", "global_batch": B, "seq_len": T}}
+    n_valid = int((batch.targets >= 0).sum())
+    if n_valid < B * T:
+        # packed rows: positions that carry a loss target (padding excluded)
+        out["valid_target_tokens_per_s"] = round(n_valid / (ms / 1e3), 1)
+        out["valid_targets"] = n_valid
 
     if not args.no_prof:
         model.profile(True)
@@ -370,6 +480,10 @@ def main():
                               "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["flops"] and v["ms"] else None,
                               "gbs": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["bytes"] and v["ms"] else None}
                           for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}
+        rec = mfma_record() if args.config == "C4" else None
+        if rec:
+            out["mfma_counters"] = {"busy_frac": rec["busy_frac"],
+                                    "source": os.path.relpath(MFMA_FILE, ROOT)}
         log(f"bench: profiled pass {total_ms / args.steps:.3f} ms/step; dominant {name} "
             f"{per_launch_ms:.4f} ms/launch; GEMM+attention MFMA util {out['mfma_util']}")
 
@@ -463,7 +577,7 @@ def main():
 
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(shape)
+        out["cpu_baseline"] = cpu_baseline(shape, args.cpu_batch)
     print(json.dumps(out), flush=True)
 
 

@@ -63,8 +63,13 @@ typedef enum {
   LM_ERR_UNSUPPORTED = -5  /* valid but not implemented (e.g. head dim 48) */
 } lm_status;
 
-/* Model dimensions. d_model must be a multiple of 64 and of n_heads; the head
- * dimension d_model / n_heads must be 32 or 64; d_mlp a multiple of 64.
+/* Model dimensions. d_model must be a multiple of 128 (at most 1024) and of
+ * n_heads; the head dimension d_model / n_heads must be 32 or 64; d_mlp a
+ * multiple of 64; max_batch * max_seq at most 2^24, and small enough that
+ * every 16-bit GEMM operand of a step (the largest is the vocabulary-wide
+ * logits, max_batch * max_seq * round_up(vocab, 128) values) spans less than
+ * 2 GiB: lm_workspace_bytes returns 0 and model_create LM_ERR_UNSUPPORTED
+ * otherwise.
  * precision: 0 = fp32 everywhere; 1 = bf16 GEMM/attention operands with fp32
  * accumulation, fp32 residual stream, statistics, loss, gradients, Adam
  * moments and master weights; 2 = the same with fp16 operands and dynamic
@@ -134,7 +139,13 @@ lm_status model_set(lm_model* model, lm_buf which, const float* src, int src_on_
 lm_status model_get(const lm_model* model, lm_buf which, float* dst, int dst_on_device, void* stream);
 
 /* One training step on a batch of B rows of T tokens (B <= max_batch,
- * T <= max_seq):
+ * T <= max_seq): the forward pass of the pre-LayerNorm stack (Feste page,
+ * "Model Architecture"), the mean softmax cross-entropy over the valid
+ * targets (RustGPT page, technical-implementation list), the hand-derived
+ * backward pass through every layer (Feste page, "Manual Backpropagation"),
+ * the global L2 gradient norm with clipping (RustGPT page: clip to an L2 norm
+ * of 5.0) and one AdamW update with decoupled weight decay (Feste page,
+ * "Manual Backpropagation"). Arguments:
  *   d_tokens  [B,T] int32 in [0, vocab)
  *   d_targets [B,T] int32 in [-1, vocab); -1 = no loss at this position
  *   d_doc_ids [B,T] int32 non-decreasing per row, or NULL for one document per
@@ -148,15 +159,23 @@ lm_status model_get(const lm_model* model, lm_buf which, float* dst, int dst_on_
  *     [0] loss, [1] pre-clip gradient norm, [2] flags, [3] number of valid
  *     targets. flags bit 0: the norm was not finite, so the update was skipped
  *     and parameters and moments are unchanged (precision 2: the loss scale
- *     is multiplied by its backoff factor); bit 1 (only with LMSTEP_CHECK=1
- *     in the environment): a token, target or doc id was out of range or doc ids
- *     decreased. */
+ *     is multiplied by its backoff factor); bit 1: a token, target or doc id
+ *     was out of range or doc ids decreased along a row (checked on the device
+ *     in every step; an out-of-range token is clamped into [0, vocab) and an
+ *     out-of-range target counts as ignored, so the step stays in bounds).
+ * Every shape rule of the kernels is checked when the model is created, so
+ * train_step either returns an error before enqueuing anything (NULL
+ * pointers, B or T out of range, bad optimiser settings) or enqueues the
+ * whole step. */
 lm_status train_step(lm_model* model, const int32_t* d_tokens, const int32_t* d_targets,
                      const int32_t* d_doc_ids, int32_t B, int32_t T, const lm_optim* opt,
                      float* d_stats, void* stream);
 
-/* Forward pass only: d_logits [B,T,vocab] fp32 (row-major) receives
- * z = LN_f(x_L) wte^T. No loss, no backward, no update. */
+/* Forward pass only (Feste page, "Model Architecture"; Smallem page, "Ce
+ * qu'est un modele de langage": one score per vocabulary entry at every
+ * position): d_logits [B,T,vocab] fp32 (row-major) receives z = LN_f(x_L)
+ * wte^T (tied head), or z = LN_f(x_L) head.w^T + head.b with untied_head.
+ * No loss, no backward, no update. Errors as for train_step. */
 lm_status forward_logits(lm_model* model, const int32_t* d_tokens, const int32_t* d_doc_ids,
                          int32_t B, int32_t T, float* d_logits, void* stream);
 

@@ -36,10 +36,25 @@ enum { LMK_EPI_STORE = 0, LMK_EPI_RESID = 1, LMK_EPI_GELU = 2, LMK_EPI_DGELU = 3
  * are computed but not stored. force_split > 0 forces that many K slices
  * (summed in slice order); ws is an fp32 scratch of ws_floats for them.
  * bf16 rules: lda, ldb multiples of 8; K a multiple of 8 when an operand is
- * K-contiguous; M (N) a multiple of 8 when A (B) is not. */
+ * K-contiguous; M (N) a multiple of 8 when A (B) is not; N and the output
+ * leading dimensions multiples of 8; each operand spans less than 2 GiB
+ * (its loads use 32-bit byte offsets); an output tile of 256 rows spans less
+ * than 2 GiB. */
 int lmk_gemm(int precision, int M, int N, int K, const void* A, int64_t lda, int a_kc, const void* B, int64_t ldb,
              int b_kc, void* C, int64_t ldc, int epi, int c_f32, const float* bias, const float* R, int64_t ldr,
              void* aux, int64_t ld_aux, int force_split, int M_out, float* ws, int64_t ws_floats, void* stream);
+
+/* lmk_gemm with an explicit tile configuration of the 16-bit path instead of
+ * the dispatcher's choice (cfg 0 = the dispatcher's choice), for tests that
+ * must run a given kernel and for measurements: 1 = 128 x 128 register-staged
+ * kernel, 11 = persistent 256 x 256, 12 = persistent 128 x 128, 14 =
+ * persistent 192 x 128 (K-contiguous operands and a 16-bit plain store only).
+ * Rejected (-1, nothing enqueued): an unknown cfg, one that does not run the
+ * layout and epilogue asked for, any cfg > 0 with precision 0. */
+int lmk_gemm_cfg(int cfg, int precision, int M, int N, int K, const void* A, int64_t lda, int a_kc, const void* B,
+                 int64_t ldb, int b_kc, void* C, int64_t ldc, int epi, int c_f32, const float* bias, const float* R,
+                 int64_t ldr, void* aux, int64_t ld_aux, int force_split, int M_out, float* ws, int64_t ws_floats,
+                 void* stream);
 
 /* LayerNorm over rows of x [M,C] fp32 (biased variance): y = g (x-mu) rstd + b
  * (y in the activation type), mu and rstd [M] fp32 (RustGPT page, file list:

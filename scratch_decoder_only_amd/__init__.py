@@ -98,6 +98,8 @@ _sig("model_profile_read", c_int, [c_void_p, ctypes.POINTER(LmProfileEntry), cty
 _P = c_void_p
 _sig("lmk_gemm", c_int, [c_int, c_int, c_int, c_int, _P, c_int64, c_int, _P, c_int64, c_int, _P, c_int64, c_int, c_int,
                          _P, _P, c_int64, _P, c_int64, c_int, c_int, _P, c_int64, _P])
+_sig("lmk_gemm_cfg", c_int, [c_int, c_int, c_int, c_int, c_int, _P, c_int64, c_int, _P, c_int64, c_int, _P, c_int64,
+                             c_int, c_int, _P, _P, c_int64, _P, c_int64, c_int, c_int, _P, c_int64, _P])
 _sig("lmk_layernorm_fwd", c_int, [c_int, _P, _P, _P, c_int, c_int, c_float, _P, _P, _P, _P])
 _sig("lmk_layernorm_bwd", c_int, [c_int, _P, _P, _P, _P, _P, c_int, c_int, _P, _P, _P, _P, _P, _P, _P, _P])
 _sig("lmk_layernorm_bwd_ws_floats", c_int64, [c_int, c_int])
@@ -146,6 +148,32 @@ def _stream(stream=None) -> int:
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
+
+
+def _need(t, name: str, dtype, device=None, shape=None, min_numel: int = 0, min_bytes: int = 0):
+    """Checks a tensor argument before its pointer crosses the C ABI: a
+    contiguous CUDA tensor of `dtype` on `device`, of `shape` and at least
+    `min_numel` elements / `min_bytes` bytes (the kernels read and write by
+    raw pointer, so a wrong dtype, device or size would be read as garbage or
+    written out of bounds)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise LmError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise LmError(f"{name} must be a CUDA (HIP) device tensor, got one on {t.device}")
+    if device is not None and t.device != device:
+        raise LmError(f"{name} is on {t.device} but the model is on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise LmError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise LmError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise LmError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.numel() < min_numel:
+        raise LmError(f"{name} needs at least {min_numel} elements, got {t.numel()}")
+    if t.numel() * t.element_size() < min_bytes:
+        raise LmError(f"{name} needs at least {min_bytes} bytes, got {t.numel() * t.element_size()}")
+    return t
 
 
 class Model:
@@ -205,7 +233,14 @@ class Model:
         flat = np.ascontiguousarray(self.flatten(named))
         _check(_lib.model_set(self._h, which, flat.ctypes.data, 0, _stream()), "model_set")
 
+    def _tokens(self, t, name="tokens", ndim=2):
+        torch = _torch()
+        if not isinstance(t, torch.Tensor) or t.dim() != ndim:
+            raise LmError(f"{name} must be a {ndim}-D int32 CUDA tensor")
+        return _need(t, name, torch.int32, self.stats.device)
+
     def set_flat_device(self, which: int, t):
+        _need(t, "src", _torch().float32, self.stats.device, min_numel=self.total)
         _check(_lib.model_set(self._h, which, _ptr(t), 1, _stream()), "model_set")
 
     def get(self, which: int) -> Dict[str, np.ndarray]:
@@ -219,23 +254,31 @@ class Model:
         return flat
 
     def get_flat_device(self, which: int, out):
+        _need(out, "out", _torch().float32, self.stats.device, min_numel=self.total)
         _check(_lib.model_get(self._h, which, _ptr(out), 1, _stream()), "model_get")
 
     # ---- the step
     def train_step(self, tokens, targets, doc_ids=None, *, lr, step, beta1=0.9, beta2=0.999, eps=1e-8,
                    weight_decay=0.0, clip=1.0, stats=None):
-        B, T = tokens.shape
+        torch = _torch()
+        B, T = self._tokens(tokens).shape
+        _need(targets, "targets", torch.int32, self.stats.device, shape=(B, T))
+        if doc_ids is not None:
+            _need(doc_ids, "doc_ids", torch.int32, self.stats.device, shape=(B, T))
         opt = LmOptim(lr, beta1, beta2, eps, weight_decay, clip, step)
-        st = self.stats if stats is None else stats
+        st = self.stats if stats is None else _need(stats, "stats", torch.float32, self.stats.device, min_numel=4)
         _check(_lib.train_step(self._h, _ptr(tokens), _ptr(targets), _ptr(doc_ids), B, T, ctypes.byref(opt),
                                _ptr(st), _stream()), "train_step")
         return st
 
     def forward_logits(self, tokens, doc_ids=None, out=None):
         torch = _torch()
-        B, T = tokens.shape
+        B, T = self._tokens(tokens).shape
+        if doc_ids is not None:
+            _need(doc_ids, "doc_ids", torch.int32, self.stats.device, shape=(B, T))
         if out is None:
             out = torch.empty((B, T, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _need(out, "out", torch.float32, self.stats.device, min_numel=B * T * self.cfg.vocab)
         _check(_lib.forward_logits(self._h, _ptr(tokens), _ptr(doc_ids), B, T, _ptr(out), _stream()),
                "forward_logits")
         return out
@@ -249,22 +292,32 @@ class Model:
             _check(LM_ERR_SHAPE, "lm_kv_cache_bytes")
         return torch.empty(int(n), dtype=torch.uint8, device=self.stats.device)
 
+    def _cache(self, cache, batch: int):
+        n = _lib.lm_kv_cache_bytes(ctypes.byref(self.cfg), int(batch))
+        if n == 0:
+            _check(LM_ERR_SHAPE, "lm_kv_cache_bytes")
+        return _need(cache, "cache", None, self.stats.device, min_bytes=int(n))
+
     def prefill(self, tokens, cache, out=None):
         """Forward over tokens [B, T] (filling cache positions < T); returns the
         logits [B, vocab] of each row's last position."""
         torch = _torch()
-        B, T = tokens.shape
+        B, T = self._tokens(tokens).shape
+        self._cache(cache, B)
         if out is None:
             out = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _need(out, "out", torch.float32, self.stats.device, min_numel=B * self.cfg.vocab)
         _check(_lib.model_prefill(self._h, _ptr(tokens), B, T, _ptr(cache), _ptr(out), _stream()), "model_prefill")
         return out
 
     def decode(self, tokens, pos: int, cache, out=None):
         """One new token per row (tokens [B]) at position pos; returns its logits [B, vocab]."""
         torch = _torch()
-        B = tokens.shape[0]
+        B = self._tokens(tokens, ndim=1).shape[0]
+        self._cache(cache, B)
         if out is None:
             out = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _need(out, "out", torch.float32, self.stats.device, min_numel=B * self.cfg.vocab)
         _check(_lib.model_decode(self._h, _ptr(tokens), B, int(pos), _ptr(cache), _ptr(out), _stream()),
                "model_decode")
         return out
@@ -273,9 +326,12 @@ class Model:
         """decode with the position in device memory (pos: int32 CUDA tensor of
         one element, read when the kernels run; clamped to [1, max_seq))."""
         torch = _torch()
-        B = tokens.shape[0]
+        B = self._tokens(tokens, ndim=1).shape[0]
+        self._cache(cache, B)
+        _need(pos, "pos", torch.int32, self.stats.device, min_numel=1)
         if out is None:
             out = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _need(out, "out", torch.float32, self.stats.device, min_numel=B * self.cfg.vocab)
         _check(_lib.model_decode_at(self._h, _ptr(tokens), B, _ptr(pos), _ptr(cache), _ptr(out), _stream()),
                "model_decode_at")
         return out
@@ -356,10 +412,16 @@ def sample_tokens(logits, temperature: float = 0.0, top_k: int = 0, uniforms=Non
     may be strided): greedy for temperature <= 0, else top-k sampling that
     picks with the given per-row uniforms in [0, 1) (a CUDA fp32 tensor)."""
     torch = _torch()
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2 or not logits.is_cuda:
+        raise LmError("logits must be a 2-D CUDA tensor")
     rows, vocab = logits.shape
-    assert logits.dtype == torch.float32 and logits.stride(1) == 1
+    if logits.dtype != torch.float32 or logits.stride(1) != 1 or logits.stride(0) < vocab:
+        raise LmError("logits must be float32 with contiguous rows")
+    if temperature > 0:
+        _need(uniforms, "uniforms", torch.float32, logits.device, min_numel=rows)
     if out is None:
         out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    _need(out, "out", torch.int32, logits.device, min_numel=rows)
     _check(_lib.sample_tokens(_ptr(logits), rows, vocab, logits.stride(0), float(temperature), int(top_k),
                               _ptr(uniforms), _ptr(out), _stream()), "sample_tokens")
     return out
@@ -440,8 +502,8 @@ def generate(model: "Model", prompt, n_new: int, *, temperature: float = 0.0, to
 # tensors are torch CUDA tensors.
 
 def gemm(precision, M, N, K, A, lda, a_kc, B, ldb, b_kc, C, ldc, epi=EPI_STORE, c_f32=False, bias=None, R=None,
-         ldr=0, aux=None, ld_aux=0, force_split=0, M_out=0, ws=None):
-    rc = _lib.lmk_gemm(precision, M, N, K, _ptr(A), lda, int(a_kc), _ptr(B), ldb, int(b_kc), _ptr(C), ldc, epi,
+         ldr=0, aux=None, ld_aux=0, force_split=0, M_out=0, ws=None, cfg=0):
+    rc = _lib.lmk_gemm_cfg(int(cfg), precision, M, N, K, _ptr(A), lda, int(a_kc), _ptr(B), ldb, int(b_kc), _ptr(C), ldc, epi,
                        int(c_f32), _ptr(bias), _ptr(R), ldr, _ptr(aux), ld_aux, force_split, M_out, _ptr(ws),
                        0 if ws is None else ws.numel(), _stream())
     _kcheck(rc, "lmk_gemm")

@@ -143,7 +143,6 @@ struct lm_model {
   double* norm_part;
   size_t bytes = 0;
   Profiler prof;
-  int check = 0;
 
   long M() const { return (long)Bmax * S; }
   const float* P_(long off) const { return params + off; }
@@ -272,7 +271,9 @@ void carve(lm_model* m, char* base) {
   // (the MLP-in slot holds up to two partial rows per row block: those the
   // GELU' GEMM epilogue writes)
   m->bias_part = c.take<float>(L * col_blocks * (2 * F + 3 * C));
-  m->gemm_ws_floats = 8L * std::max(F, 3 * C) * std::max(F, C);
+  // split-K partials of the GEMMs; also the decode attention's score
+  // scratch (max_batch * H * max_seq floats), which runs between GEMMs
+  m->gemm_ws_floats = std::max(8L * std::max(F, 3 * C) * std::max(F, C), (long)m->Bmax * m->H * m->S);
   m->gemm_ws = c.take<float>(m->gemm_ws_floats);
   for (int k = 0; k < 2; ++k) {
     EmbedBwdWs& e = k == 0 ? m->emb_tok : m->emb_pos;
@@ -316,8 +317,6 @@ lm_model* new_model(const lm_config* cfg) {
   m->ldz = m->h16 ? m->Vp : round_up(m->V, 4);
   build_table(m);
   carve(m, nullptr);
-  const char* chk = getenv("LMSTEP_CHECK");
-  m->check = chk && atoi(chk) != 0;
   return m;
 }
 
@@ -390,6 +389,63 @@ GemmOp head_op(lm_model* m, const void* hf, long M, void* z) {
   op.ldc = m->ldz;
   if (m->untied) op.bias = m->P_(m->o_head_b);
   return op;
+}
+
+// Every GEMM a step launches, built as the passes build them for the largest
+// batch the model accepts (M = max_batch * max_seq), checked against the
+// dispatcher's rules without launching anything. The rules depend on the row
+// count only through the bytes an operand spans, which grow with it, so
+// every smaller batch passes too: a step can then never stop part-way
+// through its launches on a rejected shape.
+lm_status check_model_shapes(lm_model* m) {
+  static const char dummy[256] = {0};
+  void* X = const_cast<char*>(dummy);
+  const float* R = reinterpret_cast<const float*>(dummy);
+  const long M = m->M(), C = m->C, F = m->F;
+  const long Vh = m->h16 ? m->Vp : m->V;
+  const lm_model::Blk b{};
+  std::vector<std::pair<const char*, GemmOp>> ops;
+  {
+    GemmOp op = fwd_op(m, X, M, C, b.w_qkv, 3 * C, X, EPI_STORE);
+    op.bias = R;
+    ops.push_back({"QKV projection", op});
+    op = fwd_op(m, X, M, C, b.w_o, C, X, EPI_RESID);
+    op.bias = R; op.R = R; op.ldr = C;
+    ops.push_back({"attention output", op});
+    op = fwd_op(m, X, M, C, b.w_fc, F, X, EPI_GELU);
+    op.bias = R; op.aux = X; op.ld_aux = F;
+    ops.push_back({"MLP in", op});
+    op = fwd_op(m, X, M, F, b.w_proj, C, X, EPI_RESID);
+    op.bias = R; op.R = R; op.ldr = C;
+    ops.push_back({"MLP out", op});
+    ops.push_back({"vocabulary projection", head_op(m, X, M, X)});
+    op = dw_op(X, M, Vh, X, C, const_cast<float*>(R));
+    op.lda = m->ldz; op.M_out = m->V;
+    ops.push_back({"vocabulary weight gradient", op});
+    op = dx_op(m, X, M, Vh, 0, C, X, EPI_STORE);
+    op.lda = m->ldz; op.c_f32 = true;
+    ops.push_back({"vocabulary input gradient", op});
+    ops.push_back({"MLP-out weight gradient", dw_op(X, M, C, X, F, const_cast<float*>(R))});
+    op = dx_op(m, X, M, C, 0, F, X, EPI_DGELU);
+    op.aux = X; op.ld_aux = F;
+    ops.push_back({"MLP-out input gradient", op});
+    ops.push_back({"MLP-in weight gradient", dw_op(X, M, F, X, C, const_cast<float*>(R))});
+    op = dx_op(m, X, M, F, 0, C, X, EPI_STORE);
+    op.c_f32 = true;
+    ops.push_back({"MLP-in input gradient", op});
+    ops.push_back({"attention-output weight gradient", dw_op(X, M, C, X, C, const_cast<float*>(R))});
+    ops.push_back({"attention-output input gradient", dx_op(m, X, M, C, 0, C, X, EPI_STORE)});
+    ops.push_back({"QKV weight gradient", dw_op(X, M, 3 * C, X, C, const_cast<float*>(R))});
+    op = dx_op(m, X, M, 3 * C, 0, C, X, EPI_STORE);
+    op.c_f32 = true;
+    ops.push_back({"QKV input gradient", op});
+  }
+  for (auto& [what, op] : ops)
+    if (gemm_check(op, m->h16))
+      return fail(LM_ERR_UNSUPPORTED, std::string("the ") + what + " GEMM breaks the kernels' limits at " +
+                                          "max_batch * max_seq = " + std::to_string(M) +
+                                          " rows (each 16-bit operand must span less than 2 GiB)");
+  return LM_OK;
 }
 
 // Runs f(tag) with a null pointer of the model's activation type (float,
@@ -585,8 +641,13 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   // LayerNorm writes its per-block partial sums into a slot of its own; all
   // slots are reduced in one launch after the backward (the sums are only
   // read by the optimizer).
-  ColsumBatch lnb{};
-  int n_ln = 0;
+  // (one descriptor per LayerNorm, 2L + 1 of them; launched kColsumBatch at
+  // a time)
+  struct LnPart {
+    const float *pa, *pb, *pc;
+    float *oa, *ob, *oc;
+  };
+  std::vector<LnPart> lnb;
   const long col_blocks = (M + kColRows - 1) / kColRows;
   auto fc_part = [&](int l) { return m->bias_part + (long)l * col_blocks * (2 * F + 3 * C); };
   auto qkv_part = [&](int l) { return fc_part(l) + 2 * col_blocks * F; };
@@ -609,35 +670,33 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   double ln_red_bytes = 0;
   auto ln_bwd = [&](const float* x, const float* mu, const float* r, long g_off, long b_off, const float* g_in,
                     float* dcol) {
-    float* pdg = m->ln_part + (long)n_ln * 3 * ln_blocks * C;
+    float* pdg = m->ln_part + (long)lnb.size() * 3 * ln_blocks * C;
     float* pdb = pdg + ln_blocks * C;
     float* pdc = pdg + 2 * ln_blocks * C;
     Lr.run("layernorm_bwd", 0, Mf * C * ((g_in ? 4 * 4 : 3 * 4) + A), [&] {
       launch_ln_bwd<E>(m->dy, x, mu, r, m->P_(g_off), (int)M, (int)C, g_in, m->g, g_act, pdg, pdb,
                        dcol ? pdc : nullptr, s);
     });
-    lnb.pa[n_ln] = pdg;
-    lnb.pb[n_ln] = pdb;
-    lnb.pc[n_ln] = dcol ? pdc : nullptr;
-    lnb.oa[n_ln] = m->grads + g_off;
-    lnb.ob[n_ln] = m->grads + b_off;
-    lnb.oc[n_ln] = dcol;
+    lnb.push_back({pdg, pdb, dcol ? pdc : nullptr, m->grads + g_off, m->grads + b_off, dcol});
     ln_red_bytes += (dcol ? 3.0 : 2.0) * ln_blocks * C * 4;
-    ++n_ln;
   };
   // the collected reductions, kColsumBatch per launch
   auto ln_reduce = [&] {
+    const int n_ln = (int)lnb.size();
     for (int i0 = 0; i0 < n_ln; i0 += kColsumBatch) {
       ColsumBatch part{};
       const int n = std::min(kColsumBatch, n_ln - i0);
       for (int i = 0; i < n; ++i) {
-        part.pa[i] = lnb.pa[i0 + i]; part.pb[i] = lnb.pb[i0 + i]; part.pc[i] = lnb.pc[i0 + i];
-        part.oa[i] = lnb.oa[i0 + i]; part.ob[i] = lnb.ob[i0 + i]; part.oc[i] = lnb.oc[i0 + i];
+        const LnPart& d = lnb[i0 + i];
+        part.pa[i] = d.pa; part.pb[i] = d.pb; part.pc[i] = d.pc;
+        part.oa[i] = d.oa; part.ob[i] = d.ob; part.oc[i] = d.oc;
       }
       launch_colsum_partials_batch(part, n, (int)ln_blocks, (int)C, s);
     }
   };
-  ln_bwd(m->x + m->L * M * C, m->muf, m->rf, m->o_lnf_g, m->o_lnf_b, nullptr, m->grads + m->blk[m->L - 1].b_proj);
+  // (with no blocks the final LayerNorm reads the embeddings: no bias below it)
+  ln_bwd(m->x + m->L * M * C, m->muf, m->rf, m->o_lnf_g, m->o_lnf_b, nullptr,
+         m->L > 0 ? m->grads + m->blk[m->L - 1].b_proj : nullptr);
   E* dbig = m->act<E>(m->dbig, 0);
   E* dO = m->act<E>(m->dO, 0);
   for (int l = m->L - 1; l >= 0; --l) {
@@ -741,7 +800,7 @@ extern "C" {
 size_t lm_workspace_bytes(const lm_config* cfg) {
   if (validate(cfg) != LM_OK) return 0;
   lm_model* m = new_model(cfg);
-  size_t b = m->bytes;
+  size_t b = check_model_shapes(m) == LM_OK ? m->bytes : 0;
   delete m;
   return b;
 }
@@ -754,6 +813,10 @@ lm_status model_create(const lm_config* cfg, void* d_arena, size_t arena_bytes, 
   if (!d_arena) return fail(LM_ERR_ARG, "arena is NULL");
   if (reinterpret_cast<uintptr_t>(d_arena) % kAlign) return fail(LM_ERR_WORKSPACE, "arena must be 256-byte aligned");
   lm_model* m = new_model(cfg);
+  if ((st = check_model_shapes(m)) != LM_OK) {
+    delete m;
+    return st;
+  }
   if (arena_bytes < m->bytes) {
     size_t need = m->bytes;
     delete m;
@@ -874,7 +937,7 @@ lm_status train_step(lm_model* m, const int32_t* tok, const int32_t* tgt, const 
     using E = std::remove_pointer_t<decltype(tag)>;
     return forward_pass<E>(m, Lr, tok, doc, B, T) | backward_pass<E>(m, Lr, tok, tgt, B, T, stats);
   });
-  if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
+  if (rc) return fail(LM_ERR_HIP, "internal error: a kernel rejected a shape accepted when the model was created");
   Lr.run("grad_norm", 0, 4.0 * m->P, [&] {
     launch_sumsq_partials(m->grads, m->P, m->norm_part, s);
     launch_norm_finalize(m->norm_part, opt->clip_norm, m->norm_scale, m->flags, stats, m->scaler(), s);
@@ -907,7 +970,7 @@ lm_status forward_logits(lm_model* m, const int32_t* tok, const int32_t* doc, in
     launch_logits_out<E>(m->act<E>(m->logits, 0), m->ldz, B * T, m->V, d_logits, s);
     return r;
   });
-  if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
+  if (rc) return fail(LM_ERR_HIP, "internal error: a kernel rejected a shape accepted when the model was created");
   return hip_status("forward_logits");
 }
 
@@ -942,7 +1005,7 @@ lm_status model_prefill(lm_model* m, const int32_t* tok, int32_t B, int32_t T, v
     fill(reinterpret_cast<E*>(d_cache));
     return r;
   });
-  if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
+  if (rc) return fail(LM_ERR_HIP, "internal error: a kernel rejected a shape accepted when the model was created");
   return hip_status("model_prefill");
 }
 
@@ -958,7 +1021,7 @@ static lm_status decode_common(lm_model* m, const int32_t* tok, int32_t B, int32
     launch_logits_out<E>(m->act<E>(m->logits, 0), m->ldz, B, m->V, d_logits, s);
     return r;
   });
-  if (rc) return fail(LM_ERR_UNSUPPORTED, "a kernel rejected its shape");
+  if (rc) return fail(LM_ERR_HIP, "internal error: a kernel rejected a shape accepted when the model was created");
   return hip_status(what);
 }
 

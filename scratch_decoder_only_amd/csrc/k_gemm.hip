@@ -17,9 +17,10 @@
 // read along its rows for dX) stay in their memory layout in LDS and are read
 // as MFMA fragments with the transposing LDS read.
 //
-// fp32 path: fp32 matrix and vector peaks are equal on this chip (157 TF), so
-// the fp32 GEMM is a plain LDS-tiled FMA kernel (64 x 64 tile, 4 x 4 per
-// thread).
+// fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tile, 4 x 4 per thread).
+// Its vector-FMA peak is half the fp32 matrix-core peak (packed fp32
+// instructions stay off in this build), but the fp32 workloads are a few
+// hundred million flops per step and bound by launch latency, not by either.
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
@@ -1197,8 +1198,20 @@ static GemmArgs make_args(const GemmOp& op) {
   return a;
 }
 
+// Bytes an operand spans from its first element: rows of ld elements,
+// the last one `width` long (K-contiguous: M or N rows of K; otherwise K
+// rows of M or N).
+static long span_bytes(long rows, long ld, long width, long elem) {
+  return rows <= 0 ? 0 : ((rows - 1) * ld + width) * elem;
+}
+
 static bool check_16(const GemmOp& op) {
   if (op.lda % 8 || op.ldb % 8) return false;
+  // the operand loaders address each operand through a buffer resource with
+  // a 32-bit range and 32-bit per-lane byte offsets
+  const long a_span = op.a_kc ? span_bytes(op.M, op.lda, op.K, 2) : span_bytes(op.K, op.lda, op.M, 2);
+  const long b_span = op.b_kc ? span_bytes(op.N, op.ldb, op.K, 2) : span_bytes(op.K, op.ldb, op.N, 2);
+  if (a_span > 0x7fffffffL || b_span > 0x7fffffffL) return false;
   // epilogue operands and outputs are addressed by 32-bit byte offsets within
   // a tile of up to 256 rows
   const long ld_max = std::max(op.ldc, std::max(op.R ? op.ldr : 0L, op.aux ? op.ld_aux : 0L));
@@ -1236,19 +1249,17 @@ static int device_cus() {
   return n[d];
 }
 
-// LMSTEP_GEMM_CFG=1 or 11 forces a configuration (measurements).
-static int forced_cfg() {
-  static int v = [] {
-    const char* e = getenv("LMSTEP_GEMM_CFG");
-    const int c = e ? atoi(e) : -1;
-    return c == kCfgSmall || c == kCfgPipe || c == kCfgPipe128 || c == kCfgPipe192 ? c : -1;
-  }();
-  return v;
+// Configurations a caller may ask for (GemmOp::cfg) for an op: every
+// configuration runs every layout and epilogue except the 192 x 128 one,
+// which takes K-contiguous operands and a plain 16-bit store only.
+static bool cfg_allowed(const GemmOp& op, int cfg) {
+  if (cfg == kCfgSmall || cfg == kCfgPipe || cfg == kCfgPipe128) return true;
+  if (cfg == kCfgPipe192) return op.a_kc && op.b_kc && op.epi == EPI_STORE && !op.c_f32;
+  return false;
 }
 
 static int pick_cfg(const GemmOp& op) {
-  const int f = forced_cfg();
-  if (f >= 0) return f;
+  if (op.cfg > 0) return op.cfg;
   // Measured on the GPT-2-small-shaped step: the persistent 256 x 256 kernel
   // wins on the vocabulary projection's forward (very wide N), its input
   // gradient (very long K) and its weight gradient (very tall M), and on the
@@ -1404,11 +1415,19 @@ static void launch_reduce32(const GemmOp& op, const GemmArgs& a, const float* pa
   }
 }
 
-template <typename E>
-static int gemm16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
+int gemm_check(const GemmOp& op, bool h16) {
+  if (op.cfg > 0 && (!h16 || !cfg_allowed(op, op.cfg))) return -1;
+  if (!h16) return op.colsum ? -1 : 0;
   if (op.M <= 0 || op.N <= 0) return 0;
   if (!check_16(op)) return -1;
   if (op.colsum && gemm16_colsum_rows(op) == 0) return -1;
+  return 0;
+}
+
+template <typename E>
+static int gemm16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
+  if (gemm_check(op, true)) return -1;
+  if (op.M <= 0 || op.N <= 0) return 0;
   GemmArgs a = make_args(op);
   int splits = gemm16_splits(op);
   if (splits > 1 && (long)splits * op.M * op.N > ws_floats) splits = 1;
@@ -1454,7 +1473,7 @@ static int dispatch_f32(const GemmOp& op, const GemmArgs& a, int splits, hipStre
 }
 
 int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
-  if (op.colsum) return -1;  // (16-bit GELU' epilogue only)
+  if (gemm_check(op, false)) return -1;  // (colsum: 16-bit GELU' epilogue only)
   if (op.M <= 0 || op.N <= 0) return 0;
   GemmArgs a = make_args(op);
   long tiles = (long)((op.M + 63) / 64) * ((op.N + 63) / 64);

@@ -26,11 +26,13 @@ static int with_prec(int precision, F&& f) {
 
 extern "C" {
 
-int lmk_gemm(int precision, int M, int N, int K, const void* A, int64_t lda, int a_kc, const void* B, int64_t ldb,
-             int b_kc, void* C, int64_t ldc, int epi, int c_f32, const float* bias, const float* R, int64_t ldr,
-             void* aux, int64_t ld_aux, int force_split, int M_out, float* ws, int64_t ws_floats, void* stream) {
-  if (!A || !B || !C || M < 0 || N < 0 || K < 0 || epi < 0 || epi > 3) return -1;
+int lmk_gemm_cfg(int cfg, int precision, int M, int N, int K, const void* A, int64_t lda, int a_kc, const void* B,
+                 int64_t ldb, int b_kc, void* C, int64_t ldc, int epi, int c_f32, const float* bias, const float* R,
+                 int64_t ldr, void* aux, int64_t ld_aux, int force_split, int M_out, float* ws, int64_t ws_floats,
+                 void* stream) {
+  if (!A || !B || !C || M < 0 || N < 0 || K < 0 || epi < 0 || epi > 3 || cfg < 0) return -1;
   GemmOp op;
+  op.cfg = cfg;
   op.M = M; op.N = N; op.K = K;
   op.A = A; op.lda = lda; op.a_kc = a_kc != 0;
   op.B = B; op.ldb = ldb; op.b_kc = b_kc != 0;
@@ -43,6 +45,13 @@ int lmk_gemm(int precision, int M, int N, int K, const void* A, int64_t lda, int
   if (precision == 1) return gemm_bf16(op, ws, ws_floats, S(stream));
   if (precision == 0) return gemm_f32(op, ws, ws_floats, S(stream));
   return -1;
+}
+
+int lmk_gemm(int precision, int M, int N, int K, const void* A, int64_t lda, int a_kc, const void* B, int64_t ldb,
+             int b_kc, void* C, int64_t ldc, int epi, int c_f32, const float* bias, const float* R, int64_t ldr,
+             void* aux, int64_t ld_aux, int force_split, int M_out, float* ws, int64_t ws_floats, void* stream) {
+  return lmk_gemm_cfg(0, precision, M, N, K, A, lda, a_kc, B, ldb, b_kc, C, ldc, epi, c_f32, bias, R, ldr, aux,
+                      ld_aux, force_split, M_out, ws, ws_floats, stream);
 }
 
 static bool ln_shape_ok(int M, int C) { return M >= 0 && C >= 128 && C <= 1024 && C % 128 == 0; }

@@ -47,6 +47,10 @@ struct GemmOp {
   // half of each 128-row block; row 2b + h of colsum [2 ceil(M / 128)][N]
   // holds rows 128 b + 64 h .. + 63.
   float* colsum = nullptr;
+  // > 0: this tile configuration instead of the dispatcher's choice (16-bit
+  // path; tests and measurements); an unknown one, or one that does not run
+  // the op's layout and epilogue, is rejected
+  int cfg = 0;
 };
 
 // Returns 0 or a negative code if the shape breaks the kernel's alignment
@@ -55,6 +59,9 @@ struct GemmOp {
 int gemm_bf16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
 int gemm_f16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
 int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
+// 0 if the dispatcher of the 16-bit (h16) or fp32 path accepts op, else -1:
+// the checks the launch itself makes, without launching (no pointer is read).
+int gemm_check(const GemmOp& op, bool h16);
 // Split count the 16-bit dispatcher would pick (for workspace sizing).
 int gemm16_splits(const GemmOp& op);
 // Rows of GemmOp::colsum the 16-bit dispatcher's kernel writes for op, or 0

@@ -108,3 +108,70 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
     # 16-bit GEMM outputs are addressed with 32-bit offsets within a tile
     assert sd.lib.lmk_gemm(1, 16, 16, 16, P, 16, 1, P, 16, 1, P, 1 << 22, 0, 0, None, None, 0, None, 0, 0, 0,
                            None, 0, None) != 0
+
+
+def test_gemm_operands_spanning_2gib_are_rejected(lib):
+    """16-bit operand loads use 32-bit byte offsets: an operand whose rows span
+    2 GiB or more is refused (nothing enqueued), e.g. the vocabulary weight
+    gradient's logits operand at V = 50257 with 24576 token rows."""
+    import scratch_decoder_only_amd as sd
+    P = ctypes.c_void_p(256)
+    Vp, M, C = 50304, 24576, 768
+    # dW = dz^T h: A = dz [M, Vp] read along its rows (M/N-contiguous), K = M
+    assert sd.lib.lmk_gemm(1, Vp, C, M, P, Vp, 0, P, C, 0, P, C, 0, 1, None, None, 0, None, 0, 0, 0,
+                           None, 0, None) != 0
+    # the same product at 16384 token rows spans 1.65 GB: accepted by the checks
+    # (the call would launch, so only the checking helper is asked here)
+    cfg = _cfg(vocab=50257, d_model=768, n_heads=12, d_mlp=3072, n_layers=1, max_seq=1024, max_batch=16,
+               precision=1)
+    assert sd.lib.lm_workspace_bytes(ctypes.byref(cfg)) > 0
+
+
+@pytest.mark.parametrize("prec", [1, 2])
+def test_models_whose_operands_exceed_the_kernel_limits_fail_at_creation(lib, prec):
+    """Every shape rule of the step's kernels is checked when the model is
+    created, at max_batch * max_seq rows, so that train_step can never stop
+    half-way through its launches on a rejected shape."""
+    import scratch_decoder_only_amd as sd
+    cfg = _cfg(vocab=50257, d_model=768, n_heads=12, d_mlp=3072, n_layers=1, max_seq=1024, max_batch=24,
+               precision=prec)
+    assert sd.lib.lm_workspace_bytes(ctypes.byref(cfg)) == 0
+    h = ctypes.c_void_p()
+    rc = sd.lib.model_create(ctypes.byref(cfg), ctypes.c_void_p(256), 1 << 40, None, ctypes.byref(h))
+    assert rc == sd.LM_ERR_UNSUPPORTED and not h.value
+    msg = sd.lib.lm_last_error()
+    assert b"2 GiB" in msg and b"vocabulary" in msg
+
+
+def test_gemm_configuration_requests_are_checked(lib):
+    import scratch_decoder_only_amd as sd
+    P = ctypes.c_void_p(256)
+    args = (64, 64, 64, P, 64, 1, P, 64, 1, P, 64)
+    tail = (None, 0, None, 0, 0, 0, None, 0, None)
+    # unknown configuration
+    assert sd.lib.lmk_gemm_cfg(99, 1, *args, 0, 0, None, *tail) != 0
+    # the 192 x 128 configuration runs a plain 16-bit store only, not the residual epilogue
+    assert sd.lib.lmk_gemm_cfg(14, 1, *args, 1, 1, None, P, 64, None, 0, 0, 0, None, 0, None) != 0
+    # nor K-contiguous / M-contiguous mixed layouts
+    assert sd.lib.lmk_gemm_cfg(14, 1, 64, 64, 64, P, 64, 1, P, 64, 0, P, 64, 0, 0, None, *tail) != 0
+    # no configuration exists for the fp32 path
+    assert sd.lib.lmk_gemm_cfg(12, 0, *args, 0, 1, None, *tail) != 0
+
+
+def test_binding_rejects_tensors_of_the_wrong_kind():
+    """The binding checks dtype, device, contiguity and size before a pointer
+    crosses the ABI (checked here with CPU tensors: nothing reaches a kernel)."""
+    torch = pytest.importorskip("torch")
+    import scratch_decoder_only_amd as sd
+    with pytest.raises(sd.LmError, match="CUDA"):
+        sd._need(torch.zeros(4, dtype=torch.int32), "tokens", torch.int32)
+    with pytest.raises(sd.LmError, match="torch tensor"):
+        sd._need([1, 2, 3], "tokens", torch.int32)
+    if torch.cuda.is_available():
+        x = torch.zeros((4, 6), dtype=torch.int64, device="cuda")
+        with pytest.raises(sd.LmError, match="int32"):
+            sd._need(x, "tokens", torch.int32)
+        with pytest.raises(sd.LmError, match="contiguous"):
+            sd._need(x.to(torch.int32).t(), "tokens", torch.int32)
+        with pytest.raises(sd.LmError, match="at least 30"):
+            sd._need(x.to(torch.int32), "out", torch.int32, min_numel=30)

@@ -109,6 +109,74 @@ def test_low_temperature_approaches_greedy():
     assert oracle.next_token(z, 1e-3, 0, 0.5) == 1
 
 
+def _brute_top_k(z, k):
+    """Top k ids by (-value, id), by an insertion sort written out in plain
+    Python (independent of the oracle's sort routines), in ascending id order."""
+    chosen = []
+    for i, v in enumerate(z):
+        pos = len(chosen)
+        while pos > 0 and (-z[chosen[pos - 1]], chosen[pos - 1]) > (-v, i):
+            pos -= 1
+        chosen.insert(pos, i)
+        del chosen[k:]
+    return sorted(chosen)
+
+
+@pytest.mark.parametrize("V,k", [(300, 37), (300, 1), (1000, 250), (65, 64)])
+def test_kept_ids_of_wide_vocabularies_match_a_brute_force_sort(V, k):
+    """kept_ids for V > 64 (its library-sort branch) against the brute-force
+    (-z, id) order, with values planted so that many tie at the k-th largest
+    value: the kept ids must then be the smallest ids of that tie."""
+    rng = np.random.default_rng(V + k)
+    z = rng.integers(0, 6, V).astype(np.float64) * 0.5  # few distinct values: large ties
+    kth = sorted(z, reverse=True)[k - 1]
+    assert np.sum(z == kth) > 1  # the k-th value is tied
+    got = oracle.kept_ids(z, k)
+    assert list(got) == _brute_top_k(list(z), k)
+    # the tie at the k-th value is cut at the smallest ids
+    above = np.flatnonzero(z > kth)
+    tied = np.flatnonzero(z == kth)
+    assert set(got) == set(above) | set(tied[: k - above.size])
+
+
+def test_cdf_bounds_of_equal_logits_are_j_over_k():
+    V, k = 300, 12
+    ids, lo, hi = oracle.cdf_bounds(np.full(V, -0.75), 0.8, k)
+    assert list(ids) == list(range(k))
+    j = np.arange(k)
+    assert np.allclose(lo, j / k, rtol=0, atol=1e-15) and np.allclose(hi, (j + 1) / k, rtol=0, atol=1e-15)
+
+
+def test_cdf_bounds_of_two_tokens_are_logistic():
+    a, b, T = -0.4, 0.9, 1.7
+    p0 = 1.0 / (1.0 + math.exp((b - a) / T))
+    ids, lo, hi = oracle.cdf_bounds([a, b], T, 0)
+    assert list(ids) == [0, 1]
+    assert lo[0] == 0.0 and abs(hi[0] - p0) <= 1e-15 and abs(lo[1] - p0) <= 1e-15 and hi[1] == 1.0
+
+
+def test_cdf_bounds_partition_the_unit_interval_by_softmax_weights():
+    """V = 300 with ties planted at the k-th value: the intervals follow the
+    kept ids in ascending order, tile [0, 1] without gaps, and each has the
+    width of its id's tempered softmax weight over the kept set (computed by
+    plain summation in Python)."""
+    V, k, T = 300, 40, 0.6
+    rng = np.random.default_rng(7)
+    z = np.round(rng.normal(size=V), 1)
+    ids, lo, hi = oracle.cdf_bounds(z, T, k)
+    assert list(ids) == _brute_top_k(list(z), k)
+    zmax = max(z)
+    w = [math.exp((z[i] - zmax) / T) for i in ids]
+    tot = math.fsum(w)
+    assert lo[0] == 0.0 and abs(hi[-1] - 1.0) <= 1e-12
+    assert np.array_equal(lo[1:], hi[:-1])
+    assert np.allclose(hi - lo, np.array(w) / tot, rtol=1e-12, atol=0)
+    # next_token picks the id whose interval holds u
+    for j in range(0, k, 7):
+        u = 0.5 * (lo[j] + hi[j])
+        assert oracle.next_token(z, T, k, u) == ids[j]
+
+
 # ------------------------------------------------------ dynamic loss scale
 
 def test_loss_scale_rule_matches_torch_update_op():
