@@ -48,7 +48,9 @@ int lmk_gemm(int precision, int M, int N, int K, const void* A, int64_t lda, int
  * the dispatcher's choice (cfg 0 = the dispatcher's choice), for tests that
  * must run a given kernel and for measurements: 1 = 128 x 128 register-staged
  * kernel, 11 = persistent 256 x 256, 12 = persistent 128 x 128, 14 =
- * persistent 192 x 128 (K-contiguous operands and a 16-bit plain store only).
+ * persistent 192 x 128 (K-contiguous operands and a 16-bit plain store only),
+ * 15 / 16 = persistent K-split kernel at 128 x 192 / 128 x 128 (eight
+ * wavefronts, one block per CU).
  * Rejected (-1, nothing enqueued): an unknown cfg, one that does not run the
  * layout and epilogue asked for, any cfg > 0 with precision 0. */
 int lmk_gemm_cfg(int cfg, int precision, int M, int N, int K, const void* A, int64_t lda, int a_kc, const void* B,

@@ -669,8 +669,7 @@ __global__ void splitk_reduce_kernel(GemmArgs p, const float* __restrict__ part,
 
 template <int ROWS, bool KC, int NT, int BK>
 struct PTile {
-  static_assert(ROWS == 128 || ROWS == 256 || (KC && ROWS == 192),
-                "pipelined tiles hold 128 or 256 rows (K-contiguous: also 192)");
+  static_assert(ROWS == 128 || ROWS == 256 || ROWS == 192, "pipelined tiles hold 128, 192 or 256 rows");
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
   static constexpr int CPR = BK / 8;                  // 16-byte chunks per K-contiguous row
   static constexpr int RPW = 128 / BK;                // K-contiguous rows per 256-byte bank window
@@ -688,9 +687,16 @@ struct PTile {
   int wbase;
 
   // KC: chunk c of row r at position c ^ ((r / RPW) % CPR), so 16 lanes
-  // reading 16 consecutive rows at one chunk cover distinct banks. MN: chunk q
-  // of k-row k at q ^ ((k & 3) << 2) (the transposing reads take 4 k-rows).
+  // reading 16 consecutive rows at one chunk cover distinct banks. MN: the
+  // transposing reads of half a wavefront take 4 consecutive k-rows (k0 a
+  // multiple of 4) x 4 chunks; chunk q of k-row k sits at q ^ mn_sw(k). With
+  // a 256-byte-multiple row pitch (128 or 256 rows) every k-row starts on
+  // bank 0 and mn_sw = (k & 3) << 2 puts the 4 rows on 4 distinct 16-bank
+  // windows; with the 384-byte pitch of 192 rows, k-rows alternate between
+  // banks 0 and 32, and mn_sw = ((k >> 1) & 1) << 2 separates the two rows
+  // of each parity (the 4-chunk xor stays inside the row's 24 chunks).
   static __device__ __forceinline__ int kc_pos(int row, int c) { return c ^ ((row / RPW) % CPR); }
+  static __device__ __forceinline__ int mn_sw(int k) { return ROWS == 192 ? ((k >> 1) & 1) << 2 : (k & 3) << 2; }
 
   __device__ __forceinline__ void setup(const bf16* g, long ld, int row0, int rows_total, int K, int tid) {
     long origin, extent;
@@ -715,7 +721,7 @@ struct PTile {
         kin[i] = kc * 8;
         cok[i] = true;
       } else {
-        const int k = pos / (ROWS / 8), q = (pos % (ROWS / 8)) ^ ((k & 3) << 2);
+        const int k = pos / (ROWS / 8), q = (pos % (ROWS / 8)) ^ mn_sw(k);
         voff[i] = (unsigned)(((long)k * ld + q * 8) * 2);
         kin[i] = k;
         cok[i] = row0 + q * 8 < rows_total;
@@ -745,8 +751,8 @@ struct PTile {
       const int m = row0 + (g & 1) * 16 + 4 * (i & 3);
       const int k = ks * 16 + (g >> 1) * 8 + (i >> 2);
       const int q = m >> 3, h = m & 7;
-      const bf16* p0 = s + k * PITCH + ((q ^ ((k & 3) << 2)) << 3) + h;
-      const bf16* p1 = s + (k + 4) * PITCH + ((q ^ (((k + 4) & 3) << 2)) << 3) + h;
+      const bf16* p0 = s + k * PITCH + ((q ^ mn_sw(k)) << 3) + h;
+      const bf16* p1 = s + (k + 4) * PITCH + ((q ^ mn_sw(k + 4)) << 3) + h;
       bf16x4_t lo = ds_read_tr(p0), hi = ds_read_tr(p1);
       return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
@@ -1187,6 +1193,307 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
   wait_vmcnt<0>();
 }
 
+// --------------------------------------------- persistent K-split GEMM
+// One block of eight wavefronts per CU on a 128 x (64 TN) tile. The
+// wavefronts form two groups of four, each group a 2 x 2 grid of 64 x 32 TN
+// wave tiles over the whole block tile; every K step of 64 is split between
+// the groups (group g takes k-slices 2g and 2g + 1), so each SIMD runs one
+// wavefront of each group: while one waits on the step's barrier or its
+// fragment reads, the other issues matrix instructions. A second wavefront
+// per SIMD would otherwise need a tile twice as large, and the tile count of
+// the 768-wide outputs at 8192 rows (exactly one 128 x 192 tile per CU; 3 and
+// 4 per CU for the 2304- and 3072-wide ones) would no longer fill the chip.
+// Operands arrive by direct-to-LDS loads in three stages (two K steps ahead),
+// one LDS array per stage and operand as in the persistent kernel above.
+// At the end of a tile the groups add their partial sums through LDS: group g
+// keeps its wave tile's rows 32 g .. 32 g + 31 and receives the other group's
+// partial sums of them (a + b, the same in either order: the result does not
+// depend on which group arrives first), then stores those 32 rows straight
+// from registers; the residual or GELU input of those rows is loaded ahead,
+// with the tile's first K steps.
+template <int TN, int S, bool AK, bool BKC, int EPI, typename TC, typename E>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+    gemm16_ksplit_kernel(GemmArgs p, int units, int tiles_m, int tiles_n) {
+  constexpr int BM = 128, TM = 2, WTM = 64, WTN = 32 * TN, BN = 2 * WTN, BK = 64, NT = 512;
+  static_assert(S == 3 || S == 4, "three or four stages");
+  using LA = PTile<BM, AK, NT, BK>;
+  using LB = PTile<BN, BKC, NT, BK>;
+  constexpr int NLD = LA::NI + LB::NI;  // load instructions per wavefront per K step
+  constexpr bool H = sizeof(TC) == 2;
+  // epilogue operands, 4 columns of a row per chunk, TN * 4 chunks per lane:
+  // the 16-bit GELU input (8 bytes a chunk) is loaded with the tile's first
+  // K steps; the fp32 residual (16 bytes a chunk: 48 more registers through
+  // the K loop would spill) right after the K loop, its latency partly
+  // hidden by the exchange of the partial sums
+  constexpr bool PRE = EPI == EPI_DGELU;
+  constexpr bool POST = EPI == EPI_RESID;
+  constexpr int NPRE = PRE ? TN * 4 : 0;
+  static_assert(NPRE + NLD < 64, "vmcnt range");
+  // exchange regions: 32 x WTN fp32 per wavefront, in the stage arrays (two
+  // per B stage array; with three stages the last two in A stages 0 and 1),
+  // and the tile's bias in A stage S - 1 (S = 4) or 2
+  constexpr int REG = 32 * WTN;  // floats
+  static_assert(2 * REG * 4 <= LB::ELEMS * 2 && REG * 4 <= LA::ELEMS * 2, "exchange regions fit");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+  const bf16* A = reinterpret_cast<const bf16*>(p.A);
+  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+  const int nb = gridDim.x;
+  auto sa = [](auto I_) -> bf16* { return lds_stage<2 * decltype(I_)::value, LA::ELEMS>(); };
+  auto sb = [](auto I_) -> bf16* { return lds_stage<2 * decltype(I_)::value + 1, LB::ELEMS>(); };
+  // region r of the exchange as an fp32 pointer into one known LDS array
+  // (waves 0..5: the B stage arrays, two per array; 6, 7: A stages 0, 1)
+  auto with_region = [&](int r, auto&& f) {
+    constexpr std::integral_constant<int, 0> I0{};
+    constexpr std::integral_constant<int, 1> I1{};
+    constexpr std::integral_constant<int, 2> I2{};
+    constexpr std::integral_constant<int, S == 4 ? 3 : 0> I3{};
+    switch (r) {
+      case 0: f(reinterpret_cast<float*>(sb(I0))); break;
+      case 1: f(reinterpret_cast<float*>(sb(I0)) + REG); break;
+      case 2: f(reinterpret_cast<float*>(sb(I1))); break;
+      case 3: f(reinterpret_cast<float*>(sb(I1)) + REG); break;
+      case 4: f(reinterpret_cast<float*>(sb(I2))); break;
+      case 5: f(reinterpret_cast<float*>(sb(I2)) + REG); break;
+      case 6:
+        if constexpr (S == 4) f(reinterpret_cast<float*>(sb(I3)));
+        else f(reinterpret_cast<float*>(sa(I0)));
+        break;
+      default:
+        if constexpr (S == 4) f(reinterpret_cast<float*>(sb(I3)) + REG);
+        else f(reinterpret_cast<float*>(sa(I1)));
+        break;
+    }
+  };
+  // the tile's bias in a stage array no exchange region uses
+  auto bias_lds = [&]() -> float* {
+    return reinterpret_cast<float*>(sa(std::integral_constant<int, S == 4 ? S - 1 : 2>{}));
+  };
+
+  LA la;
+  LB lb;
+  // lane's output chunk (j, c4): row lane % 32 of the group's 32 rows,
+  // columns j * 32 + c4 * 8 + (lane / 32) * 4 .. + 3 of the wave tile
+  const int lrow = wm * WTM + grp * 32 + (lane & 31);
+  auto lcol = [&](int j, int c4) { return wn * WTN + j * 32 + c4 * 8 + (lane >> 5) * 4; };
+  typedef unsigned int w2_t __attribute__((ext_vector_type(2)));
+  typedef std::conditional_t<EPI == EPI_DGELU, w2_t, uint4> pre_t;
+  pre_t pre[PRE || POST ? TN * 4 : 1];
+  // the tile's bias: loaded by wavefront 0 with the tile's first loads, kept
+  // in LDS for the epilogue
+  constexpr bool BIAS = EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_GELU;
+  static_assert(BN * 4 <= LA::ELEMS * 2, "the bias fits in an A stage");
+  f32x4_t bias_r = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto load_pre = [&](int tm, int tn) {
+    constexpr int ES = EPI == EPI_DGELU ? 2 : 4;
+    const long r0 = (long)tm * BM, c0 = (long)tn * BN;
+    const long ld = EPI == EPI_DGELU ? p.ld_aux : p.ldr;
+    const char* base = EPI == EPI_DGELU ? reinterpret_cast<const char*>(p.aux) : reinterpret_cast<const char*>(p.R);
+    const long n = r0 < p.M_out ? ((p.M_out - 1 - r0) * ld + p.N - c0) * ES : 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (r0 * ld + c0) * ES), (short)0, (int)min(n, (long)0x7fffffff), 0x00020000);
+    const int ldi = (int)ld, rows = (int)min((long)BM, p.M_out - r0), cols = (int)min((long)BN, p.N - c0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int lc = lcol(j, c4);
+        const int off = lrow < rows && lc < cols ? (lrow * ldi + lc) * ES : (int)kOutOfRange;
+        if constexpr (ES == 4) {
+          const w4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+          pre[j * 4 + c4] = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          pre[j * 4 + c4] = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        }
+      }
+  };
+  auto prologue = [&](int u) {
+    int tm, tn, z;
+    pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
+    const int kb = z * p.k_split, ke = min(p.K, kb + p.k_split);
+    if constexpr (BIAS) {
+      // the tile's bias, by wavefront 0 ahead of the stage loads (the first
+      // K step waits for it with them); zero where absent, so the epilogue
+      // adds it unconditionally. (A load inside the K loop would make the
+      // compiler wait for every outstanding load before the register's
+      // later uses.)
+      if (wave == 0 && lane < BN / 4) {
+        const long col = (long)tn * BN + lane * 4;
+        bias_r = p.bias && col < p.N ? *reinterpret_cast<const f32x4_t*>(p.bias + col)
+                                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    la.setup(A, p.lda, tm * BM, p.M, p.K, tid);
+    lb.setup(B, p.ldb, tn * BN, p.N, p.K, tid);
+    // the first S - 1 K steps, issued even past the end of K (zeros into a
+    // stage nobody reads), so every wavefront has the same loads in flight
+    static_for<S - 1>([&](auto I_) {
+      constexpr int I = decltype(I_)::value;
+      const int k0 = kb + I * BK < ke ? kb + I * BK : ke;
+      la.load(sa(I_), k0, ke);
+      lb.load(sb(I_), k0, ke);
+    });
+    if constexpr (PRE) load_pre(tm, tn);
+  };
+
+  f32x16_t acc[TM][TN];
+  int round = 0;
+  int u = pipe_unit(0, blockIdx.x, nb);
+  for (; u < units; u = pipe_unit(++round, blockIdx.x, nb)) {
+    int tm, tn, z;
+    pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
+    const int kb = z * p.k_split, ke = min(p.K, kb + p.k_split);
+    const int nk = (ke - kb + BK - 1) / BK;
+    prologue(u);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // One K step at stage I (it = the step's index).
+    auto kstep = [&](auto I_, int it) {
+      constexpr int I = decltype(I_)::value;
+      // this wavefront's loads of step it have landed (the S - 2 later
+      // steps' may still be landing; the epilogue operands, issued after
+      // the first S - 1 steps, before step 2), then every wavefront's:
+      // stage I is readable, and the stage read at step it - 1 is free
+      if (it < 2) wait_vmcnt<(S - 2) * NLD + NPRE>();
+      else wait_vmcnt<(S - 2) * NLD>();
+      lds_barrier();
+      const bf16* a_s = sa(I_);
+      const bf16* b_s = sb(I_);
+      bf16x8_t af[2][TM], bfr[2][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[0][i] = LA::frag(a_s, wm * WTM + i * 32, 2 * grp, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[0][j] = LB::frag(b_s, wn * WTN + j * 32, 2 * grp, lane);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        // the loads of step it + S - 1 into the stage read at step it - 1
+        // (A during the first k-slice, B during the second)
+        constexpr int NX = (I + S - 1) % S;
+        const int kn = it + S - 1 < nk ? kb + (it + S - 1) * BK : ke;
+        if (kk == 0) la.load(sa(std::integral_constant<int, NX>{}), kn, ke);
+        else lb.load(sb(std::integral_constant<int, NX>{}), kn, ke);
+        if (kk == 0) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) af[1][i] = LA::frag(a_s, wm * WTM + i * 32, 2 * grp + 1, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bfr[1][j] = LB::frag(b_s, wn * WTN + j * 32, 2 * grp + 1, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32<E>(bfr[kk][j], af[kk][i], acc[i][j]);
+#pragma unroll
+        for (int q = 0; q < TM * TN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // Whole groups of S steps in the loop and the remaining steps after it:
+    // with a conditional step inside the loop, the wait-count analysis would
+    // see a path on which the stage about to be read was loaded last, and wait
+    // for every outstanding load before its reads.
+    int it0 = 0;
+    for (; it0 + S <= nk; it0 += S) static_for<S>([&](auto I_) { kstep(I_, it0 + decltype(I_)::value); });
+    static_for<S - 1>([&](auto I_) {
+      if (it0 + decltype(I_)::value < nk) kstep(I_, it0 + decltype(I_)::value);
+    });
+    // no direct load is still writing a stage and every wavefront is done
+    // reading them: the stages become the exchange regions; the tile's bias
+    // (loaded by wavefront 0 with the tile's first loads) goes to LDS, so
+    // that the epilogue's bias reads do not wait for its stores
+    wait_vmcnt<0>();
+    lds_barrier();
+    if constexpr (BIAS) {
+      if (wave == 0 && lane < BN / 4) *reinterpret_cast<f32x4_t*>(bias_lds() + lane * 4) = bias_r;
+    }
+    if constexpr (POST) load_pre(tm, tn);
+    const long r0 = (long)tm * BM, c0 = (long)tn * BN;
+    const int rows = (int)min((long)BM, p.M_out - r0), cols = (int)min((long)BN, p.N - c0);
+    const int ldc = (int)p.ldc, ldx = (int)p.ld_aux;
+    // stores through resources from the tile's origin (an offset past the
+    // range is dropped)
+    auto rsrc_of = [&](void* base, long ld, int es) {
+      const long n = r0 < p.M_out ? ((p.M_out - 1 - r0) * ld + p.N - c0) * es : 0;
+      return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(base) + (r0 * ld + c0) * es, (short)0,
+                                               (int)min(n, (long)0x7fffffff), 0x00020000);
+    };
+    void* cbase = EPI == EPI_PARTIAL ? static_cast<void*>(reinterpret_cast<float*>(p.C) + (long)z * p.split_stride)
+                                     : p.C;
+    const __amdgpu_buffer_rsrc_t rc = rsrc_of(cbase, p.ldc, H ? 2 : 4);
+    const __amdgpu_buffer_rsrc_t rx = EPI == EPI_GELU ? rsrc_of(p.aux, p.ld_aux, 2) : rc;
+    typedef unsigned int w2_t __attribute__((ext_vector_type(2)));
+    // the epilogue of chunk q (j = q / 4, c4 = q % 4) with its summed value v
+    auto store = [&](int q, f32x4_t v) {
+      const int lc = lcol(q >> 2, q & 3);
+      const bool ok = lrow < rows && lc < cols;
+      if constexpr (BIAS) v += *reinterpret_cast<const f32x4_t*>(bias_lds() + lc);
+      if constexpr (EPI == EPI_RESID) v += __builtin_bit_cast(f32x4_t, pre[q]);
+      if constexpr (EPI == EPI_DGELU) {
+        const w2_t uu = pre[q];
+        v[0] *= gelu_grad_f(H16<E>::lo(uu[0]));
+        v[1] *= gelu_grad_f(H16<E>::hi(uu[0]));
+        v[2] *= gelu_grad_f(H16<E>::lo(uu[1]));
+        v[3] *= gelu_grad_f(H16<E>::hi(uu[1]));
+      }
+      if constexpr (H) {
+        const w2_t w = w2_t{H16<E>::pack(v[0], v[1]), H16<E>::pack(v[2], v[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(w, rc, ok ? (lrow * ldc + lc) * 2 : (int)kOutOfRange, 0, 0);
+        if constexpr (EPI == EPI_GELU) {
+          const w2_t g = w2_t{H16<E>::pack(gelu_f(v[0]), gelu_f(v[1])), H16<E>::pack(gelu_f(v[2]), gelu_f(v[3]))};
+          __builtin_amdgcn_raw_buffer_store_b64(g, rx, ok ? (lrow * ldx + lc) * 2 : (int)kOutOfRange, 0, 0);
+        }
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(w4_t, v), rc,
+                                               ok ? (lrow * ldc + lc) * 4 : (int)kOutOfRange, 0, 0);
+      }
+    };
+    // (the group is uniform over a wavefront: one code path per group keeps
+    // the accumulator indices compile-time constants; both paths meet the
+    // same two barriers)
+    auto exchange = [&](auto G_) {
+      constexpr int G = decltype(G_)::value;
+      with_region(wave, [&](float* __restrict__ reg) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const f32x16_t& a = acc[G ^ 1][j];
+            *reinterpret_cast<f32x4_t*>(reg + ((j * 4 + c4) * 64 + lane) * 4) =
+                f32x4_t{a[4 * c4], a[4 * c4 + 1], a[4 * c4 + 2], a[4 * c4 + 3]};
+          }
+      });
+      lds_barrier();
+      with_region(wave ^ 4, [&](const float* __restrict__ reg) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const f32x16_t& a = acc[G][j];
+            store(j * 4 + c4, f32x4_t{a[4 * c4], a[4 * c4 + 1], a[4 * c4 + 2], a[4 * c4 + 3]} +
+                                  *reinterpret_cast<const f32x4_t*>(reg + ((j * 4 + c4) * 64 + lane) * 4));
+          }
+      });
+      // the regions and the bias are read: the next tile's loads may
+      // overwrite the stages
+      lds_barrier();
+    };
+    if (grp == 0) exchange(std::integral_constant<int, 0>{});
+    else exchange(std::integral_constant<int, 1>{});
+  }
+  // no direct load may still be writing LDS when the workgroup ends
+  wait_vmcnt<0>();
+}
+
 // ------------------------------------------------------------- dispatch
 static GemmArgs make_args(const GemmOp& op) {
   GemmArgs a;
@@ -1230,11 +1537,20 @@ static bool check_16(const GemmOp& op) {
 // CU); 12 = gemm16_pipe_kernel, persistent 128 x 128 (4 wavefronts of 64 x 64,
 // two blocks per CU); 14 = the same at 192 x 128 (wavefronts of 96 x 64, two
 // blocks per CU in 160 KB of LDS), K-contiguous operands and a plain store.
+// 15, 16 = gemm16_ksplit_kernel, persistent 128 x 192 and 128 x 128 (one
+// block of eight wavefronts per CU, the K step split between two groups of
+// four).
 constexpr int kCfgSmall = 1, kCfgPipe = 11, kCfgPipe128 = 12, kCfgPipe192 = 14;
+constexpr int kCfgKs192 = 15, kCfgKs128 = 16;
+
+static bool is_ksplit(int cfg) { return cfg == kCfgKs192 || cfg == kCfgKs128; }
 
 static int tiles_of(const GemmOp& op, int cfg) {
-  const int T = cfg == kCfgPipe ? 256 : 128;
-  return ((op.M + T - 1) / T) * ((op.N + T - 1) / T);
+  int TMr = 128, TNc = 128;
+  if (cfg == kCfgPipe) TMr = TNc = 256;
+  else if (cfg == kCfgPipe192) TMr = 192;
+  else if (cfg == kCfgKs192) TNc = 192;
+  return ((op.M + TMr - 1) / TMr) * ((op.N + TNc - 1) / TNc);
 }
 
 // Compute units of the current device (the persistent grid's size).
@@ -1253,7 +1569,7 @@ static int device_cus() {
 // configuration runs every layout and epilogue except the 192 x 128 one,
 // which takes K-contiguous operands and a plain 16-bit store only.
 static bool cfg_allowed(const GemmOp& op, int cfg) {
-  if (cfg == kCfgSmall || cfg == kCfgPipe || cfg == kCfgPipe128) return true;
+  if (cfg == kCfgSmall || cfg == kCfgPipe || cfg == kCfgPipe128 || is_ksplit(cfg)) return true;
   if (cfg == kCfgPipe192) return op.a_kc && op.b_kc && op.epi == EPI_STORE && !op.c_f32;
   return false;
 }
@@ -1269,6 +1585,15 @@ static int pick_cfg(const GemmOp& op) {
   // register-staged kernel loads ahead more fully (the persistent one holds
   // only the first of its two passes through the K loop; 7% slower).
   const int mn_max = op.M > op.N ? op.M : op.N, mn_min = op.M < op.N ? op.M : op.N;
+  // Outputs whose 128 x 192 tiles fill the CUs in exactly one round (the
+  // 768-wide outputs at 8192 rows, including the vocabulary projection's
+  // input gradient, whose K of 50304 then needs no split): the K-split
+  // kernel, one tile per CU (measured 10-30% faster than the 128 x 128 or
+  // split 256 x 256 tiles there; with several tiles per CU it is slower).
+  {
+    const int cus = device_cus(), t = tiles_of(op, kCfgKs192);
+    if (t <= cus && 10 * t >= 9 * cus && op.K >= 512 && op.colsum == nullptr) return kCfgKs192;
+  }
   if (op.M >= 16384 || op.N >= 16384 || op.K >= 16384) return kCfgPipe;
   if (op.K >= 8192 && mn_max >= 3072 && mn_max <= 4096 && mn_min <= 1024) return kCfgPipe;
   if (op.epi == EPI_RESID) return kCfgSmall;
@@ -1290,7 +1615,7 @@ int gemm16_splits(const GemmOp& op) {
   if (op.force_split > 0) return op.force_split;
   const int cfg = pick_cfg(op);
   const int tiles = tiles_of(op, cfg);
-  if (cfg == kCfgPipe) {
+  if (cfg == kCfgPipe || is_ksplit(cfg)) {
     // persistent grid of one block per CU: pick the K split whose work units
     // fill the last round best (smallest split within 10% of the best fill),
     // with at least 512 K-values per slice
@@ -1345,10 +1670,23 @@ static void launch_small(const GemmArgs& a, int splits, hipStream_t s) {
                      a, units);
 }
 
+template <int TN, int S, bool AK, bool BKC, int EPI, typename TC, typename E>
+static void launch_ksplit(const GemmArgs& a, int splits, hipStream_t s) {
+  const int tiles_m = (a.M + 127) / 128, tiles_n = (a.N + 64 * TN - 1) / (64 * TN);
+  const int units = tiles_m * tiles_n * splits;
+  int nb = device_cus();
+  if (units < nb) nb = units;
+  nb = (nb + 7) / 8 * 8;  // whole XCD rounds
+  hipLaunchKernelGGL((gemm16_ksplit_kernel<TN, S, AK, BKC, EPI, TC, E>), dim3(nb), dim3(512), 0, s, a, units,
+                     tiles_m, tiles_n);
+}
+
 // One launch of configuration cfg with the epilogue EPI and output type TC.
 template <bool AK, bool BKC, int EPI, typename TC, typename E>
 static void launch_cfg(int cfg, const GemmArgs& a, int splits, hipStream_t s) {
-  if (cfg == kCfgPipe) launch_pipe<256, 256, 2, 4, 64, 2, 2, AK, BKC, EPI, TC, E>(a, splits, s);
+  if (cfg == kCfgKs192) launch_ksplit<3, 4, AK, BKC, EPI, TC, E>(a, splits, s);
+  else if (cfg == kCfgKs128) launch_ksplit<2, 4, AK, BKC, EPI, TC, E>(a, splits, s);
+  else if (cfg == kCfgPipe) launch_pipe<256, 256, 2, 4, 64, 2, 2, AK, BKC, EPI, TC, E>(a, splits, s);
   else if (cfg == kCfgPipe128) launch_pipe<128, 128, 2, 2, 64, 2, 2, AK, BKC, EPI, TC, E>(a, splits, s);
   else if (cfg == kCfgPipe192) {
     if constexpr (AK && BKC && EPI == EPI_STORE)

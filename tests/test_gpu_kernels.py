@@ -45,11 +45,11 @@ def _operands(rng, prec, *shapes, scale=1.0):
 @pytest.mark.parametrize("layout", ["fwd", "dx", "dw"])
 @pytest.mark.parametrize("MNK", [(200, 136, 72), (1000, 648, 576), (8, 8, 8), (136, 264, 1536)])
 @pytest.mark.parametrize("split", [0, 3])
-def test_gemm_layouts(sd, prec, layout, MNK, split):
+def test_gemm_layouts(sd, prec, layout, MNK, split, cfg=0):
     t = torch()
     M, N, K = MNK
     rng = np.random.default_rng(hash((prec, layout, MNK, split)) % 2**32)
-    print(f"gemm prec={prec} layout={layout} M,N,K={MNK} split={split}", flush=True)
+    print(f"gemm prec={prec} layout={layout} M,N,K={MNK} split={split} cfg={cfg}", flush=True)
     if layout == "fwd":      # Y = X W^T
         X, W = _operands(rng, prec, (M, K), (N, K))
         A, lda, akc, B, ldb, bkc = X, K, True, W, K, True
@@ -65,12 +65,12 @@ def test_gemm_layouts(sd, prec, layout, MNK, split):
     C = t.zeros((M, N), dtype=t.float32, device="cuda")
     ws = t.zeros(4 * M * N + 16, dtype=t.float32, device="cuda")
     Ad, Bd = act(A, prec), act(B, prec)
-    sd.gemm(prec, M, N, K, Ad, lda, akc, Bd, ldb, bkc, C, N, c_f32=True, force_split=split, ws=ws)
+    sd.gemm(prec, M, N, K, Ad, lda, akc, Bd, ldb, bkc, C, N, c_f32=True, force_split=split, ws=ws, cfg=cfg)
     t.cuda.synchronize()
     assert rel(host(C), expect) <= tol(prec, True)
     # slices are summed in a fixed order: a second run is bit-identical
     C2 = t.zeros_like(C)
-    sd.gemm(prec, M, N, K, Ad, lda, akc, Bd, ldb, bkc, C2, N, c_f32=True, force_split=split, ws=ws)
+    sd.gemm(prec, M, N, K, Ad, lda, akc, Bd, ldb, bkc, C2, N, c_f32=True, force_split=split, ws=ws, cfg=cfg)
     t.cuda.synchronize()
     assert t.equal(C, C2)
 
@@ -78,17 +78,17 @@ def test_gemm_layouts(sd, prec, layout, MNK, split):
 @pytest.mark.parametrize("prec", [0, 1, 2])
 @pytest.mark.parametrize("epi", ["store", "resid", "gelu", "dgelu"])
 @pytest.mark.parametrize("split", [0, 2])
-def test_gemm_epilogues(sd, prec, epi, split):
+def test_gemm_epilogues(sd, prec, epi, split, cfg=0, MNK=(264, 200, 320)):
     t = torch()
-    M, N, K = 264, 200, 320
+    M, N, K = MNK
     rng = np.random.default_rng(17 + prec)
-    print(f"gemm epilogue prec={prec} epi={epi} split={split}", flush=True)
+    print(f"gemm epilogue prec={prec} epi={epi} split={split} cfg={cfg} M,N,K={MNK}", flush=True)
     X, W = _operands(rng, prec, (M, K), (N, K), scale=0.3)
     bias = rng.standard_normal(N).astype(np.float32)
     ws = t.zeros(4 * M * N, dtype=t.float32, device="cuda")
     adt = act_dtype(prec)
     lin = oracle.linear_fwd(X, W, bias)
-    args = dict(bias=dev(bias), force_split=split, ws=ws)
+    args = dict(bias=dev(bias), force_split=split, ws=ws, cfg=cfg)
     if epi == "store":
         C = t.zeros((M, N), dtype=adt, device="cuda")
         sd.gemm(prec, M, N, K, act(X, prec), K, True, act(W, prec), K, True, C, N, sd.EPI_STORE, **args)
@@ -116,6 +116,27 @@ def test_gemm_epilogues(sd, prec, epi, split):
                 ld_aux=N, **args)
         t.cuda.synchronize()
         assert rel(host(C), oracle.linear_fwd(X, W) * oracle.gelu_grad(u)) <= tol(prec, False)
+
+
+# The persistent K-split kernel (configurations 15: 128 x 192 tiles, 16:
+# 128 x 128), forced: every layout and epilogue, ragged in every dimension,
+# with K splits, and with more tiles than its one-block-per-CU grid holds
+# (8200 x 776: 325 tiles of 128 x 192 for 256 blocks).
+@pytest.mark.parametrize("cfg", [15, 16])
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("layout", ["fwd", "dx", "dw"])
+@pytest.mark.parametrize("MNK,split", [((1000, 648, 576), 0), ((8200, 776, 200), 0), ((136, 264, 1536), 3),
+                                       ((8, 8, 8), 0)])
+def test_gemm_ksplit_layouts(sd, cfg, prec, layout, MNK, split):
+    test_gemm_layouts(sd, prec, layout, MNK, split, cfg=cfg)
+
+
+@pytest.mark.parametrize("cfg", [15, 16])
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("epi", ["store", "resid", "gelu", "dgelu"])
+@pytest.mark.parametrize("MNK", [(264, 200, 320), (8200, 776, 136)])
+def test_gemm_ksplit_epilogues(sd, cfg, prec, epi, MNK):
+    test_gemm_epilogues(sd, prec, epi, 0, cfg=cfg, MNK=MNK)
 
 
 # Shapes with one dimension of 16384 or more run on the persistent 256 x 256
