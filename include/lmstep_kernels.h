@@ -109,6 +109,20 @@ int lmk_attn_bwd(int precision, const void* qkv, const void* o, const float* lse
 int lmk_xent(int precision, void* z, int64_t ldz, int M, int V, const int32_t* tgt, float* loss, int32_t* ws_n,
              float* ws_rows, uint32_t* flags, const float* loss_scale, void* stream);
 
+/* lmk_xent for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels,
+ * with the valid-target count and the per-row losses in a static device
+ * buffer of this library instead of ws_n / ws_rows. The buffer holds
+ * 65536 rows (M > 65536: -1, nothing enqueued) and about 256 KB per GPU the
+ * library runs on, kept until the process ends; its address is looked up
+ * once per GPU on the first call there. The call allocates nothing. Calls
+ * that overlap on one GPU (on different streams) share the buffer and race;
+ * the count and every row's loss are rewritten by each call, so nothing
+ * carries over from one call to the next. -2 if the buffer's address cannot
+ * be obtained. */
+int lmk_xent_noalloc(int precision, void* z, int64_t ldz, int M, int V, const int32_t* tgt, float* loss,
+                     uint32_t* flags, const float* loss_scale, void* stream);
+
 /* Stable counting sort of keys [M] in [0, nkeys): counts/offsets/chunk_base
  * [nkeys+1], 16-byte aligned, perm [M] (rows of key v at
  * perm[offsets[v] .. offsets[v+1]), ascending); rank [M] int32 scratch (each

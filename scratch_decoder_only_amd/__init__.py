@@ -110,6 +110,7 @@ _sig("lmk_embed_fwd", c_int, [_P, _P, _P, _P, c_int, c_int, c_int, _P, _P, _P])
 _sig("lmk_attn_fwd", c_int, [c_int, _P, _P, _P, c_int, c_int, c_int, c_int, _P, _P, _P])
 _sig("lmk_attn_bwd", c_int, [c_int, _P, _P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, _P, _P, _P])
 _sig("lmk_xent", c_int, [c_int, _P, c_int64, c_int, c_int, _P, _P, _P, _P, _P, _P, _P])
+_sig("lmk_xent_noalloc", c_int, [c_int, _P, c_int64, c_int, c_int, _P, _P, _P, _P, _P])
 _sig("lmk_csr", c_int, [_P, c_int, c_int, _P, _P, _P, _P, _P, _P])
 _sig("lmk_segment_sum", c_int, [_P, c_int, c_int, c_int, _P, _P, _P, _P, _P, _P, c_int, _P])
 _sig("lmk_segment_sum_ws_floats", c_int64, [c_int, c_int, c_int])
@@ -560,6 +561,12 @@ def attn_bwd(precision, qkv, o, lse, dout, start, end, B, T, H, D, delta, dqkv):
 def xent(precision, z, ldz, M, V, tgt, loss, ws_n, ws_rows, flags, loss_scale=None):
     _kcheck(_lib.lmk_xent(precision, _ptr(z), ldz, M, V, _ptr(tgt), _ptr(loss), _ptr(ws_n), _ptr(ws_rows),
                           _ptr(flags), _ptr(loss_scale), _stream()), "lmk_xent")
+
+
+def xent_noalloc(precision, z, ldz, M, V, tgt, loss, flags, loss_scale=None):
+    """lmk_xent with the library's static scratch (no workspace arguments)."""
+    _kcheck(_lib.lmk_xent_noalloc(precision, _ptr(z), ldz, M, V, _ptr(tgt), _ptr(loss), _ptr(flags),
+                                  _ptr(loss_scale), _stream()), "lmk_xent_noalloc")
 
 
 def csr(keys, M, nkeys, counts, offsets, chunk_base, perm, rank):

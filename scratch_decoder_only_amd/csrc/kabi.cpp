@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/lmstep_kernels.h"
@@ -143,6 +144,42 @@ int lmk_xent(int precision, void* z, int64_t ldz, int M, int V, const int32_t* t
   });
   launch_loss_reduce(ws_rows, M, ws_n, loss, S(stream));
   return 0;
+}
+
+// Scratch of lmk_xent_noalloc: the valid-target count (int32, first 256
+// bytes) and one loss per row, in device memory the library reserves once per
+// GPU. The name is a host-side stand-in for the device array: host code uses
+// only the address hipGetSymbolAddress returns for the current device.
+constexpr int kXentNoallocRows = 1 << 16;
+constexpr int kXentNoallocHead = 64;  // floats before the per-row losses
+static __device__ __align__(256) float scratch[kXentNoallocHead + kXentNoallocRows];
+
+// The address of this GPU's scratch, looked up once per device (with that
+// device current) and kept; null if the lookup fails.
+static float* xent_scratch() {
+  static std::mutex mu;
+  static float* ptr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = static_cast<float*>(p);
+  }
+  return ptr[dev];
+}
+
+int lmk_xent_noalloc(int precision, void* z, int64_t ldz, int M, int V, const int32_t* tgt, float* loss,
+                     uint32_t* flags, const float* loss_scale, void* stream) {
+  if (M <= 0 || M > kXentNoallocRows || V <= 0 || ldz < V || ldz % 8 || precision < 0 || precision > 2) return -1;
+  if (!z || !tgt || !loss || !flags) return -1;
+  float* sp = xent_scratch();
+  if (!sp) return -2;
+  // the count and every row's loss are written before they are read: nothing
+  // to clear
+  return lmk_xent(precision, z, ldz, M, V, tgt, loss, reinterpret_cast<int32_t*>(sp), sp + kXentNoallocHead, flags,
+                  loss_scale, stream);
 }
 
 int lmk_csr(const int32_t* keys, int M, int nkeys, int32_t* counts, int32_t* offsets, int32_t* chunk_base,
