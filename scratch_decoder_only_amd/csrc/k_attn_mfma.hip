@@ -476,7 +476,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int qq = qb + tid;
       const bool ok = qq < T;
       sL[stage][tid] = ok ? lse[qq] * kLog2e : 0.f;
-      sD[stage][tid] = ok ? dl[qq] : 0.f;
+      sD[stage][tid] = ok ? -dl[qq] : 0.f;  // negated: the dP accumulators start from it
       sS[stage][tid] = ok ? start[qq] : T;  // rows past T admit no key
     }
   };
@@ -489,8 +489,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   ldo.store(sdO[0]);
   load_vec(qt0 * 64, 0);
   __syncthreads();
-  for (int qt = qt0; qt <= qt1; ++qt) {
-    const int cur = (qt - qt0) & 1;
+  // one 64-query tile in stage CUR (compile-time: every LDS read is a per-lane
+  // address plus an immediate offset)
+  auto tile = [&](auto CUR_, int qt) {
+    constexpr int cur = decltype(CUR_)::value;
     const int qb = qt * 64;
     if (qt < qt1) {
       lq.load(qb + 64);
@@ -498,40 +500,47 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      // rows of element e: sub*32 + acc_row(e), four consecutive rows per
+      // group of four elements, read as one vector. dP starts from -delta of
+      // its row (read straight into the accumulators), so the MFMAs leave
+      // dP - delta.
       f32x16_t s, dp;
       zero(s);
-      zero(dp);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(&sD[cur][sub * 32 + g * 8 + (lane >> 5) * 4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dp[4 * g + i] = D4[i];
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma32<E>(frag_r<D>(sQ[cur], sub * 32, ks, lane), kf[ks], s);
         dp = mfma32<E>(frag_r<D>(sdO[cur], sub * 32, ks, lane), vf[ks], dp);
       }
       float p[16], ds[16];
-      // rows of element e: sub*32 + acc_row(e), four consecutive rows per
-      // group of four elements, read as one vector
       const int rq = qb + sub * 32;  // first query of this 32-query block
       const bool full = wave_keys_ok && kw0 + 31 <= rq && rq + 31 < T && sS[cur][sub * 32 + 31] <= kw0;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r0 = sub * 32 + g * 8 + (lane >> 5) * 4;
         const f32x4_t L4 = *reinterpret_cast<const f32x4_t*>(&sL[cur][r0]);
-        const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(&sD[cur][r0]);
         if (full) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + i], sc, -L4[i]));
             p[4 * g + i] = pv;
-            ds[4 * g + i] = pv * (dp[4 * g + i] - D4[i]);
+            ds[4 * g + i] = pv * dp[4 * g + i];
           }
         } else {
           const int4 S4 = *reinterpret_cast<const int4*>(&sS[cur][r0]);
           const int st4[4] = {S4.x, S4.y, S4.z, S4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool ok = kv && key >= st4[i] && key <= qb + r0 + i;
+            // (non-short-circuit: the start read is not made conditional)
+            const bool ok = kv & (key >= st4[i]) & (key <= qb + r0 + i);
             const float pv = __builtin_amdgcn_exp2f(ok ? __builtin_fmaf(s[4 * g + i], sc, -L4[i]) : -INFINITY);
             p[4 * g + i] = pv;
-            ds[4 * g + i] = pv * (dp[4 * g + i] - D4[i]);
+            ds[4 * g + i] = pv * dp[4 * g + i];
           }
         }
       }
@@ -541,10 +550,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         const bf16x8_t sf = as_frag(pack_frag<E>(&ds[st * 8]));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          dv[dt] = mfma32<E>(frag_t<D>(sdO[cur], dt, sub * 32 + st * 16, lane), pf,
-                                                           dv[dt]);
-          dk[dt] = mfma32<E>(frag_t<D>(sQ[cur], dt, sub * 32 + st * 16, lane), sf,
-                                                           dk[dt]);
+          dv[dt] = mfma32<E>(frag_t<D>(sdO[cur], dt, sub * 32 + st * 16, lane), pf, dv[dt]);
+          dk[dt] = mfma32<E>(frag_t<D>(sQ[cur], dt, sub * 32 + st * 16, lane), sf, dk[dt]);
         }
       }
     }
@@ -554,7 +561,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       load_vec(qb + 64, cur ^ 1);
     }
     __syncthreads();
+  };
+  int qt = qt0;
+  for (; qt + 1 <= qt1; qt += 2) {
+    tile(std::integral_constant<int, 0>{}, qt);
+    tile(std::integral_constant<int, 1>{}, qt + 1);
   }
+  if (qt <= qt1) tile(std::integral_constant<int, 0>{}, qt);
   if (kv) {
     const float scale = 1.0f / sqrtf((float)D);
     bf16* row = reinterpret_cast<bf16*>(a.dqkv) + ((long)b * T + key) * ld;

@@ -1574,6 +1574,22 @@ static bool cfg_allowed(const GemmOp& op, int cfg) {
   return false;
 }
 
+// K slices of a K-split op: the most units that still run in one round of
+// the persistent grid (one block per CU), with at least 512 K-values per
+// slice; the fewest slices among equal fills.
+static int ksplit_slices(const GemmOp& op, int cfg) {
+  const int cus = device_cus(), tiles = tiles_of(op, cfg);
+  int best = 1;
+  for (int s = 2; s <= 16 && op.K / s >= 512; ++s)
+    if ((long)tiles * s <= cus) best = s;
+  return best;
+}
+static double ksplit_round_fill(const GemmOp& op, int cfg) {
+  const int cus = device_cus();
+  const long u = (long)tiles_of(op, cfg) * ksplit_slices(op, cfg);
+  return (double)u / (double)(((u + cus - 1) / cus) * cus);
+}
+
 static int pick_cfg(const GemmOp& op) {
   if (op.cfg > 0) return op.cfg;
   // Measured on the GPT-2-small-shaped step: the persistent 256 x 256 kernel
@@ -1585,6 +1601,18 @@ static int pick_cfg(const GemmOp& op) {
   // register-staged kernel loads ahead more fully (the persistent one holds
   // only the first of its two passes through the K loop; 7% slower).
   const int mn_max = op.M > op.N ? op.M : op.N, mn_min = op.M < op.N ? op.M : op.N;
+  // Weight gradients of the 768-wide model's blocks (both operands M/N-
+  // contiguous, K = the token count, outputs of 768 x 768 to 768 x 3072): the
+  // K-split kernel with as many K slices as fill the CUs in one round
+  // (gemm16_splits). Measured at 8192 tokens: the MLP weight gradients 50 us
+  // (128 x 192 tiles, 2 slices) against 56-58 us for 256 x 256 tiles in 7
+  // slices, the QKV one 40 us (128 x 192, 3 slices) against 45 us for 128 x
+  // 128 tiles in 4 slices of two blocks per CU, the attention-output one
+  // 22 us (128 x 128, 6-7 slices) against 26 us; several rounds of slices
+  // measured slower (no overlap of one unit's partial store with the next
+  // unit's loads). 128 x 192 tiles where they fill at least 70% of the CUs.
+  if (!op.a_kc && !op.b_kc && op.K >= 4096 && mn_min >= 768 && mn_max <= 4096 && op.colsum == nullptr)
+    return ksplit_round_fill(op, kCfgKs192) >= 0.7 ? kCfgKs192 : kCfgKs128;
   // Outputs whose 128 x 192 tiles fill the CUs in exactly one round (the
   // 768-wide outputs at 8192 rows, including the vocabulary projection's
   // input gradient, whose K of 50304 then needs no split): the K-split
@@ -1615,7 +1643,8 @@ int gemm16_splits(const GemmOp& op) {
   if (op.force_split > 0) return op.force_split;
   const int cfg = pick_cfg(op);
   const int tiles = tiles_of(op, cfg);
-  if (cfg == kCfgPipe || is_ksplit(cfg)) {
+  if (is_ksplit(cfg)) return ksplit_slices(op, cfg);
+  if (cfg == kCfgPipe) {
     // persistent grid of one block per CU: pick the K split whose work units
     // fill the last round best (smallest split within 10% of the best fill),
     // with at least 512 K-values per slice
