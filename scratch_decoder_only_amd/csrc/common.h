@@ -82,16 +82,40 @@ __device__ __forceinline__ f32x16_t mfma32<f16>(bf16x8_t a, bf16x8_t b, f32x16_t
                                                 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// Wavefront reductions in registers (no LDS round trip): DPP moves within
+// each row of 16 lanes (partners l ^ 1, l ^ 2, then the mirrored lane in the
+// other quad and in the other half-row) leave every lane with its row's
+// result; two row broadcasts combine rows 0 + 1 into row 1 and (0 + 1) +
+// (2 + 3) into row 3, whose lane 63 is read back as a scalar, so all 64
+// lanes get the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+// src from the DPP pattern in the rows of ROW_MASK, `old` in the others
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROW_MASK, 0xf, false));
 }
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op, float identity) {
+  v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]: lane l ^ 1
+  v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]: lane l ^ 2
+  v = op(v, dpp_mov<0x141>(v));  // row_half_mirror: the other quad of 8 lanes
+  v = op(v, dpp_mov<0x140>(v));  // row_mirror: the other half of 16 lanes
+  v = op(v, dpp_rows<0x142, 0xa>(identity, v));  // row_bcast:15 into rows 1, 3
+  v = op(v, dpp_rows<0x143, 0xc>(identity, v));  // row_bcast:31 into rows 2, 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+struct AddOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, AddOp(), 0.f); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, MaxOp(), -INFINITY); }
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -161,7 +161,11 @@ __global__ void __launch_bounds__(256) xent_kernel(T* __restrict__ z, long ldz, 
 // The same computation with the row held in registers between the passes:
 // 1024 threads, thread t owns the 16-byte vectors t, t + 1024, ... (NCH of
 // them), so the logits are read from memory once. Used when the row fits
-// (ldz <= 1024 * NCH * vector width).
+// (ldz <= 1024 * NCH * vector width). The vector work per logit is kept
+// small: only the chunks that reach past column V - 1 are masked (a test
+// uniform over the block), exponentials are exp2 of one fused multiply-add
+// (the 1/N scale folded into the exponent of the gradient pass), and the
+// one-hot term is subtracted by the one thread that holds the target.
 template <typename T, int NCH>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) xent_reg_kernel(T* __restrict__ z, long ldz, int V,
                                                         const int32_t* __restrict__ tgt,
@@ -169,6 +173,7 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
                                                         const float* __restrict__ loss_scale,
                                                         float* __restrict__ row_loss) {
   constexpr int NV = Vec16<T>::N;
+  constexpr float kL2e = 1.4426950408889634f;
   __shared__ float s_m[16], s_s[16];
   __shared__ float s_lse;
   const long row = blockIdx.x;
@@ -176,21 +181,30 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
   const int t = tgt[row];
   const bool valid = t >= 0 && t < V;
   const int nvec = (int)(ldz / NV);
-  // the row stays in registers as loaded (16 bytes per vector), unpacked on use
+  // the row stays in registers as loaded (16 bytes per vector), unpacked on
+  // use; columns >= V (padding, and vectors past the row) are set to -inf
+  // once, as loaded, so no pass tests them again
   uint4 raw[NCH];
-  auto unpack = [&](int q, float* x) {
-    const int v = threadIdx.x + q * 1024;
-    Vec16<T>::load(reinterpret_cast<const T*>(&raw[q]), x);
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (v >= nvec || v * NV + i >= V) x[i] = -INFINITY;
-  };
+  auto unpack = [&](int q, float* x) { Vec16<T>::load(reinterpret_cast<const T*>(&raw[q]), x); };
   float m = -INFINITY, s = 0.f;
   if (valid) {
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
       const int v = threadIdx.x + q * 1024;
-      raw[q] = v < nvec ? ld_nt16(zr + (long)v * NV) : make_uint4(0, 0, 0, 0);
+      uint4 u = v < nvec ? ld_nt16(zr + (long)v * NV) : make_uint4(0, 0, 0, 0);
+      const int lim = V - v * NV;  // elements of this vector below column V
+      uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (NV == 8) {  // two 16-bit values per word, low first
+          constexpr uint32_t ninf = sizeof(T) == 2 && std::is_same<T, bf16>::value ? 0xff80u : 0xfc00u;
+          if (2 * k + 1 >= lim) wd[k] = (wd[k] & 0xffffu) | (ninf << 16);
+          if (2 * k >= lim) wd[k] = (ninf << 16) | ninf;
+        } else {
+          if (k >= lim) wd[k] = 0xff800000u;
+        }
+      }
+      raw[q] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
@@ -199,21 +213,28 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
 #pragma unroll
       for (int i = 0; i < NV; ++i) m = fmaxf(m, x[i]);
     }
-    if (m != -INFINITY) {
+  }
+  // the row maximum, then the sum of exp(z - max), each over the wavefront
+  // (register reductions) and then over the 16 wavefronts in order
+  const int w = threadIdx.x >> 6;
+  const float mw = wave_max(m);
+  // (the unpacked values are not kept from the first pass: that would hold
+  // the whole row twice in registers)
 #pragma unroll
-      for (int q = 0; q < NCH; ++q) {
-        float x[NV];
-        unpack(q, x);
+  for (int q = 0; q < NCH; ++q) asm volatile("" : "+v"(raw[q].x), "+v"(raw[q].y), "+v"(raw[q].z), "+v"(raw[q].w));
+  if (valid && mw != -INFINITY) {
+    const float c = -mw * kL2e;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) s += __expf(x[i] - m);
-      }
+    for (int q = 0; q < NCH; ++q) {
+      float x[NV];
+      unpack(q, x);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], kL2e, c));
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) merge_ms(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
-  const int w = threadIdx.x >> 6;
+  s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) {
-    s_m[w] = m;
+    s_m[w] = mw;
     s_s[w] = s;
   }
   __syncthreads();
@@ -227,19 +248,36 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
   __syncthreads();  // z[t] has been read before it is overwritten
   const float lse = s_lse;
   const int n = *n_valid;
-  const float inv_n = (n > 0 ? 1.0f / (float)n : 0.f) * (loss_scale ? *loss_scale : 1.0f);
+  const float inv_n = n > 0 ? 1.0f / (float)n : 0.f;
+  const float scale = loss_scale ? *loss_scale : 1.0f;
+  // dz = exp(z - lse) / N = exp2(z log2(e) - (lse log2(e) - log2(1/N))) (no
+  // valid row: exp2(-inf) = 0), then times the loss scale as a separate
+  // product, so a power-of-two scale changes the bits by exactly that power
+  const float c = -(lse * kL2e - __log2f(inv_n));
+  // the thread, chunk and element that hold the target column
+  const int vt = valid ? t / NV : -1;
+  const int t_thread = vt & 1023, t_chunk = vt >> 10, t_elem = valid ? t - vt * NV : 0;
 #pragma unroll
   for (int q = 0; q < NCH; ++q) {
     const int v = threadIdx.x + q * 1024;
     if (v >= nvec) continue;
     float x[NV];
-    if (valid) unpack(q, x);
+    if (valid) {
+      unpack(q, x);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int j = v * NV + i;
-      float d = 0.f;
-      if (valid && j < V) d = (__expf(x[i] - lse) - (j == t ? 1.f : 0.f)) * inv_n;
-      x[i] = d;
+      for (int i = 0; i < NV; ++i) x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], kL2e, c));
+      if (q == t_chunk && (int)threadIdx.x == t_thread) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (i == t_elem) x[i] -= inv_n;
+      }
+      if (scale != 1.0f) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) x[i] *= scale;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) x[i] = 0.f;
     }
     Vec16<T>::store_nt(zr + (long)v * NV, x);
   }
