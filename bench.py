@@ -86,6 +86,7 @@ TRAFFIC_SYMBOLS = {
 }
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters_c4_step.md")
 SIMDS = 1024  # 256 compute units x 4 SIMDs
+XCDS = 8  # accelerator complex dies (32 compute units each)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_c4_step.md")
 CALIB_BYTES = 1 << 30  # plain device copy used to scale the counters
 
@@ -181,9 +182,14 @@ def mfma_summary(pmc_dir, out=MFMA_FILE, cmd=""):
             c = r["Counter_Name"]
             v = float(r["Counter_Value"])
             if c == "GRBM_GUI_ACTIVE":
-                d[c] = max(d.get(c, 0.0), v)  # per XCD: the longest
+                d.setdefault("grbm_rows", []).append(v)
             else:
                 d[c] = d.get(c, 0.0) + v
+    for d in per.values():
+        rows = d.pop("grbm_rows", None)
+        if rows:
+            # one row per XCD: the longest; one row: rocprofv3's sum over the XCDs
+            d["GRBM_GUI_ACTIVE"] = max(rows) if len(rows) > 1 else rows[0] / XCDS
     by = {}
     for (_, name), d in per.items():
         if not ("gemm16" in name or "attn_" in name) or "GRBM_GUI_ACTIVE" not in d:
@@ -209,8 +215,9 @@ def mfma_summary(pmc_dir, out=MFMA_FILE, cmd=""):
     with open(out, "w") as fh:
         fh.write("# MFMA utilisation from hardware counters (GPT-2-small-shaped step, C4)\n\n")
         fh.write("Command (repository root, on one MI355X):\n\n```\n" + cmd + "\n```\n\n")
-        fh.write("Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE of the busiest XCD x "
-                 f"{SIMDS} SIMDs): the share of the kernel's GPU cycles in which the matrix cores were "
+        fh.write("Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GPU cycles per XCD x "
+                 f"{SIMDS} SIMDs), GPU cycles per XCD = GRBM_GUI_ACTIVE / {XCDS} (rocprofv3 reports it summed "
+                 "over the XCDs): the share of the kernel's GPU cycles in which the matrix cores were "
                  "busy, whatever the clock ran at. MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the "
                  "attention kernels' score recomputation included).\n\n")
         fh.write(f"All GEMM and attention dispatches: busy fraction **{rec['busy_frac']:.3f}** "
