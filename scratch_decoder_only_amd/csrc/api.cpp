@@ -227,6 +227,8 @@ void build_table(lm_model* m) {
   }
 }
 
+std::vector<std::pair<const char*, GemmOp>> step_gemm_ops(lm_model* m);
+
 // Lays out every slice of the arena (base == nullptr: size only).
 void carve(lm_model* m, char* base) {
   Carver c{base};
@@ -271,9 +273,13 @@ void carve(lm_model* m, char* base) {
   // (the MLP-in slot holds up to two partial rows per row block: those the
   // GELU' GEMM epilogue writes)
   m->bias_part = c.take<float>(L * col_blocks * (2 * F + 3 * C));
-  // split-K partials of the GEMMs; also the decode attention's score
-  // scratch (max_batch * H * max_seq floats), which runs between GEMMs
+  // split-K partials of the GEMMs (at least what every GEMM of a step at
+  // max_batch rows uses: with less, a GEMM runs unsplit); also the decode
+  // attention's score scratch (max_batch * H * max_seq floats), which runs
+  // between GEMMs
   m->gemm_ws_floats = std::max(8L * std::max(F, 3 * C) * std::max(F, C), (long)m->Bmax * m->H * m->S);
+  for (auto& named : step_gemm_ops(m))
+    m->gemm_ws_floats = std::max(m->gemm_ws_floats, gemm_ws_floats_needed(named.second, m->h16));
   m->gemm_ws = c.take<float>(m->gemm_ws_floats);
   for (int k = 0; k < 2; ++k) {
     EmbedBwdWs& e = k == 0 ? m->emb_tok : m->emb_pos;
@@ -392,12 +398,10 @@ GemmOp head_op(lm_model* m, const void* hf, long M, void* z) {
 }
 
 // Every GEMM a step launches, built as the passes build them for the largest
-// batch the model accepts (M = max_batch * max_seq), checked against the
-// dispatcher's rules without launching anything. The rules depend on the row
-// count only through the bytes an operand spans, which grow with it, so
-// every smaller batch passes too: a step can then never stop part-way
-// through its launches on a rejected shape.
-lm_status check_model_shapes(lm_model* m) {
+// batch the model accepts (M = max_batch * max_seq); the operand pointers
+// are placeholders (only shapes, layouts and epilogues matter to the
+// dispatcher's rules and to the split-K workspace).
+std::vector<std::pair<const char*, GemmOp>> step_gemm_ops(lm_model* m) {
   static const char dummy[256] = {0};
   void* X = const_cast<char*>(dummy);
   const float* R = reinterpret_cast<const float*>(dummy);
@@ -440,6 +444,16 @@ lm_status check_model_shapes(lm_model* m) {
     op.c_f32 = true;
     ops.push_back({"QKV input gradient", op});
   }
+  return ops;
+}
+
+// The step's GEMMs checked against the dispatcher's rules without launching
+// anything. The rules depend on the row count only through the bytes an
+// operand spans, which grow with it, so every smaller batch passes too: a
+// step can then never stop part-way through its launches on a rejected shape.
+lm_status check_model_shapes(lm_model* m) {
+  const long M = m->M();
+  const auto ops = step_gemm_ops(m);
   for (auto& [what, op] : ops)
     if (gemm_check(op, m->h16))
       return fail(LM_ERR_UNSUPPORTED, std::string("the ") + what + " GEMM breaks the kernels' limits at " +

@@ -1592,14 +1592,14 @@ static double ksplit_round_fill(const GemmOp& op, int cfg) {
 
 static int pick_cfg(const GemmOp& op) {
   if (op.cfg > 0) return op.cfg;
-  // Measured on the GPT-2-small-shaped step: the persistent 256 x 256 kernel
-  // wins on the vocabulary projection's forward (very wide N), its input
-  // gradient (very long K) and its weight gradient (very tall M), and on the
-  // MLP weight gradients (3072 x 768 outputs over K = 8192); 128 x 128 at two
-  // blocks per CU everywhere else: the direct-load persistent kernel (6-12%
-  // faster), except for the residual epilogue, whose fp32 operand the
-  // register-staged kernel loads ahead more fully (the persistent one holds
-  // only the first of its two passes through the K loop; 7% slower).
+  // Measured on the step's shapes: the persistent 256 x 256 kernel wins on
+  // the vocabulary projection's forward (very wide N) and weight gradient
+  // (very tall M), and on the projections of the 32768-token workload (M =
+  // 32768, 512-2048 wide); 128 x 128 at two blocks per CU on most others:
+  // the direct-load persistent kernel (6-12% faster), except for the
+  // residual epilogue, whose fp32 operand the register-staged kernel loads
+  // ahead more fully (the persistent one holds only the first of its two
+  // passes through the K loop; 7% slower).
   const int mn_max = op.M > op.N ? op.M : op.N, mn_min = op.M < op.N ? op.M : op.N;
   // Weight gradients of the 768-wide model's blocks (both operands M/N-
   // contiguous, K = the token count, outputs of 768 x 768 to 768 x 3072): the
@@ -1611,8 +1611,19 @@ static int pick_cfg(const GemmOp& op) {
   // 22 us (128 x 128, 6-7 slices) against 26 us; several rounds of slices
   // measured slower (no overlap of one unit's partial store with the next
   // unit's loads). 128 x 192 tiles where they fill at least 70% of the CUs.
-  if (!op.a_kc && !op.b_kc && op.K >= 4096 && mn_min >= 768 && mn_max <= 4096 && op.colsum == nullptr)
-    return ksplit_round_fill(op, kCfgKs192) >= 0.7 ? kCfgKs192 : kCfgKs128;
+  // (The same at the smaller widths of the other workloads, 128-512: there
+  // 128 x 128 tiles, unless the width is a multiple of 192: 2x faster than
+  // the split 256 x 256 or 128 x 128 kernels at 128-wide outputs, 5-45% at
+  // 512-wide ones.)
+  if (!op.a_kc && !op.b_kc && op.K >= 4096 && mn_min >= 128 && mn_max <= 4096 && op.colsum == nullptr)
+    return op.N % 192 == 0 && ksplit_round_fill(op, kCfgKs192) >= 0.7 ? kCfgKs192 : kCfgKs128;
+  // Outputs 128 or fewer columns wide over many rows (the 128-wide model's
+  // projections to d_model): 128 x 128 tiles (a 256-wide tile would be half
+  // empty), K-split and in one round of slices when K is long (its
+  // vocabulary input and weight gradients: 52 and 50 us against 67 and 70
+  // us on 256 x 256 tiles), else two blocks per CU (10 against 22 us on the
+  // MLP-out forward).
+  if (op.N <= 128 && op.M >= 4096) return op.K >= 4096 ? kCfgKs128 : kCfgPipe128;
   // Outputs whose 128 x 192 tiles fill the CUs in exactly one round (the
   // 768-wide outputs at 8192 rows, including the vocabulary projection's
   // input gradient, whose K of 50304 then needs no split): the K-split
@@ -1622,6 +1633,10 @@ static int pick_cfg(const GemmOp& op) {
     const int cus = device_cus(), t = tiles_of(op, kCfgKs192);
     if (t <= cus && 10 * t >= 9 * cus && op.K >= 512 && op.colsum == nullptr) return kCfgKs192;
   }
+  // the GELU' input gradient: the 128 x 128 kernel, whose epilogue also
+  // writes the bias gradient's partial column sums (6% faster than 256 x 256
+  // at 32768 x 2048 before counting the separate column-sum pass it saves)
+  if (op.epi == EPI_DGELU && op.M >= 4096) return kCfgPipe128;
   if (op.M >= 16384 || op.N >= 16384 || op.K >= 16384) return kCfgPipe;
   if (op.K >= 8192 && mn_max >= 3072 && mn_max <= 4096 && mn_min <= 1024) return kCfgPipe;
   if (op.epi == EPI_RESID) return kCfgSmall;
@@ -1782,6 +1797,21 @@ static void launch_reduce32(const GemmOp& op, const GemmArgs& a, const float* pa
   }
 }
 
+// fp32 path: 64 x 64 tiles; split K while the tiles leave CUs idle
+static int gemm32_splits(const GemmOp& op) {
+  if (op.force_split > 0) return op.force_split;
+  const long tiles = (long)((op.M + 63) / 64) * ((op.N + 63) / 64);
+  int splits = 1;
+  while (tiles * splits < 256 && op.K / (splits * 2) >= 256) splits *= 2;
+  return splits;
+}
+
+long gemm_ws_floats_needed(const GemmOp& op, bool h16) {
+  if (op.M <= 0 || op.N <= 0 || op.K <= 0) return 0;
+  const int splits = h16 ? gemm16_splits(op) : gemm32_splits(op);
+  return splits > 1 ? (long)splits * op.M * op.N : 0;
+}
+
 int gemm_check(const GemmOp& op, bool h16) {
   if (op.cfg > 0 && (!h16 || !cfg_allowed(op, op.cfg))) return -1;
   if (!h16) return op.colsum ? -1 : 0;
@@ -1843,10 +1873,7 @@ int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
   if (gemm_check(op, false)) return -1;  // (colsum: 16-bit GELU' epilogue only)
   if (op.M <= 0 || op.N <= 0) return 0;
   GemmArgs a = make_args(op);
-  long tiles = (long)((op.M + 63) / 64) * ((op.N + 63) / 64);
-  int splits = op.force_split > 0 ? op.force_split : 1;
-  if (op.force_split <= 0)
-    while (tiles * splits < 256 && op.K / (splits * 2) >= 256) splits *= 2;
+  int splits = gemm32_splits(op);
   if (splits > 1 && (long)splits * op.M * op.N > ws_floats) splits = 1;
   // K slices are multiples of 16 (which can leave a single slice)
   int per = op.K;

@@ -62,6 +62,9 @@ int gemm_f32(const GemmOp& op, float* ws, long ws_floats, hipStream_t s);
 // 0 if the dispatcher of the 16-bit (h16) or fp32 path accepts op, else -1:
 // the checks the launch itself makes, without launching (no pointer is read).
 int gemm_check(const GemmOp& op, bool h16);
+// Split-K partial floats the op's launch configuration would use (0: no split);
+// with a smaller workspace the GEMM runs unsplit.
+long gemm_ws_floats_needed(const GemmOp& op, bool h16);
 // Split count the 16-bit dispatcher would pick (for workspace sizing).
 int gemm16_splits(const GemmOp& op);
 // Rows of GemmOp::colsum the 16-bit dispatcher's kernel writes for op, or 0
