@@ -28,9 +28,10 @@ enum { LMK_EPI_STORE = 0, LMK_EPI_RESID = 1, LMK_EPI_GELU = 2, LMK_EPI_DGELU = 3
  * the step: Y = X W^T, dX = dY W, dW = dY^T X), then the epilogue:
  *   STORE: C = acc + bias[j]              (C fp32 if c_f32, else activation type)
  *   RESID: C (fp32) = R[i,j] + acc + bias[j]  (residual add of a block)
- *   GELU : C = u = acc + bias[j]; aux = GELU(u), tanh form (Feste page,
- *          "Model Architecture": GELU activation)
- *   DGELU: C = acc * GELU'(aux[i,j])
+ *   GELU : u = acc + bias[j]; C = GELU'(u), aux = GELU(u), tanh form (Feste
+ *          page, "Model Architecture": GELU activation); the derivative is
+ *          stored for the backward's DGELU
+ *   DGELU: C = acc * aux[i,j]  (aux: the GELU'(u) a GELU epilogue stored)
  * A(i,k) = A[i*lda + k] if a_kc else A[k*lda + i]; B(j,k) = B[j*ldb + k] if
  * b_kc else B[k*ldb + j]. bias may be NULL. Rows >= M_out (if 0 < M_out < M)
  * are computed but not stored. force_split > 0 forces that many K slices

@@ -127,7 +127,9 @@ struct lm_model {
   uint16_t* shadow;  // 16-bit copy of the flat parameter buffer (bf16 or fp16 path)
   float* x;      // [L+1][M][C]
   float* xm;     // [L][M][C]
-  char *y1, *qkv, *o, *y2, *u, *a, *hf, *logits;
+  // gelu_d: GELU'(u) of each block's MLP-in pre-activation u, which the
+  // forward's GELU epilogue stores beside GELU(u) for the backward
+  char *y1, *qkv, *o, *y2, *gelu_d, *a, *hf, *logits;
   float *mu1, *r1, *mu2, *r2, *muf, *rf, *lse;
   float *g, *dy, *delta;
   char *g_act, *dbig, *dO;
@@ -245,7 +247,7 @@ void carve(lm_model* m, char* base) {
   m->qkv = c.take<char>(L * M * 3 * C * A);
   m->o = c.take<char>(L * M * C * A);
   m->y2 = c.take<char>(L * M * C * A);
-  m->u = c.take<char>(L * M * F * A);
+  m->gelu_d = c.take<char>(L * M * F * A);
   m->a = c.take<char>(L * M * F * A);
   m->hf = c.take<char>(M * C * A);
   m->logits = c.take<char>(M * m->ldz * A);
@@ -491,7 +493,7 @@ int forward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* d
     E* qkv = m->act<E>(m->qkv, l * M * 3 * C);
     E* o = m->act<E>(m->o, l * M * C);
     E* y2 = m->act<E>(m->y2, l * M * C);
-    E* u = m->act<E>(m->u, l * M * F);
+    E* gd = m->act<E>(m->gelu_d, l * M * F);
     E* a = m->act<E>(m->a, l * M * F);
     Lr.run("layernorm_fwd", 0, Mf * C * (4 + A), [&] {
       launch_ln_fwd<E>(xl, m->P_(b.ln1_g), m->P_(b.ln1_b), (int)M, (int)C, m->cfg.ln_eps, y1, m->mu1 + l * M,
@@ -517,7 +519,7 @@ int forward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* d
                        m->r2 + l * M, s);
     });
     {
-      GemmOp op = fwd_op(m, y2, M, C, b.w_fc, F, u, EPI_GELU);
+      GemmOp op = fwd_op(m, y2, M, C, b.w_fc, F, gd, EPI_GELU);
       op.bias = m->P_(b.b_fc); op.aux = a; op.ld_aux = F;
       Lr.run("gemm_fc1_fwd", 2.0 * M * F * C, 0, [&] { rc |= gemm(m, op, s); });
     }
@@ -565,7 +567,7 @@ int decode_pass(lm_model* m, Launcher& Lr, const int32_t* tok, int B, int pos, E
     E* qkv = m->act<E>(m->qkv, l * M * 3 * C);
     E* o = m->act<E>(m->o, l * M * C);
     E* y2 = m->act<E>(m->y2, l * M * C);
-    E* u = m->act<E>(m->u, l * M * F);
+    E* gd = m->act<E>(m->gelu_d, l * M * F);
     E* a = m->act<E>(m->a, l * M * F);
     E* kc = cache + 2L * l * B * S * C;
     E* vc = kc + (long)B * S * C;
@@ -592,7 +594,7 @@ int decode_pass(lm_model* m, Launcher& Lr, const int32_t* tok, int B, int pos, E
                        m->r2 + l * M, s);
     });
     {
-      GemmOp op = fwd_op(m, y2, M, C, b.w_fc, F, u, EPI_GELU);
+      GemmOp op = fwd_op(m, y2, M, C, b.w_fc, F, gd, EPI_GELU);
       op.bias = m->P_(b.b_fc); op.aux = a; op.ld_aux = F;
       Lr.run("gemm_fc1_fwd", 2.0 * M * F * C, 0, [&] { rc |= gemm(m, op, s); });
     }
@@ -721,13 +723,13 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
     E* qkv = m->act<E>(m->qkv, l * M * 3 * C);
     E* o = m->act<E>(m->o, l * M * C);
     E* y2 = m->act<E>(m->y2, l * M * C);
-    E* u = m->act<E>(m->u, l * M * F);
+    E* gd = m->act<E>(m->gelu_d, l * M * F);
     E* a = m->act<E>(m->a, l * M * F);
     // MLP out: x_{l+1} = xm + a W_proj^T + b_proj
     Lr.run("gemm_fc2_bwd_dw", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, dw_op(g_act, M, C, a, F, m->grads + b.w_proj), s); });
     {
       GemmOp op = dx_op(m, g_act, M, C, b.w_proj, F, dbig, EPI_DGELU);
-      op.aux = u; op.ld_aux = F;
+      op.aux = gd; op.ld_aux = F;
       if (fc_fused) op.colsum = fc_part(l);
       Lr.run("gemm_fc2_bwd_dx", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, op, s); });
     }

@@ -136,10 +136,17 @@ __device__ __forceinline__ float gelu_sigmoid(float u) {
 __device__ __forceinline__ float gelu_f(float u) { return u * gelu_sigmoid(u); }
 // Its derivative: 0.5 (1 + t) + 0.5 u (1 - t^2) c (1 + 3 a u^2) with t =
 // tanh(y); in terms of s: s + 2 u s (1 - s) c (1 + 3 a u^2).
-__device__ __forceinline__ float gelu_grad_f(float u) {
+__device__ __forceinline__ float gelu_grad_s(float u, float s) {
   const float c = 0.7978845608028654f, a = 0.044715f;
-  const float s = gelu_sigmoid(u);
   return __builtin_fmaf(2.0f * c * u * s * (1.0f - s), __builtin_fmaf(3.0f * a, u * u, 1.0f), s);
+}
+// GELU(u) and GELU'(u) from one sigmoid: the MLP-in forward stores both (the
+// activation for the MLP-out GEMM, the derivative for the backward), so the
+// backward's GELU' epilogue is a product.
+__device__ __forceinline__ void gelu_and_grad(float u, float& g, float& d) {
+  const float s = gelu_sigmoid(u);
+  g = u * s;
+  d = gelu_grad_s(u, s);
 }
 
 // Wait until at most n vector-memory operations of this wavefront are

@@ -1,6 +1,7 @@
 // Dense contractions of the step: the QKV, attention-output, MLP and tied
 // vocabulary projections, forward and backward (Y = X W^T, dX = dY W,
-// dW = dY^T X), with fused epilogues (bias, GELU, its derivative, residual
+// dW = dY^T X), with fused epilogues (bias, GELU with its derivative stored
+// beside it for the backward, the product with that derivative, residual
 // add). Matrix multiplication is where the time goes (Feste page, "Tensor
 // Operations": matmul is the bottleneck); its CPU tiling for L1 is prior art,
 // here the contraction runs on the gfx950 matrix cores.
@@ -61,12 +62,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, long row, long col, 
     float v = p.R[row * p.ldr + col] + acc + (p.bias ? p.bias[col] : 0.f);
     reinterpret_cast<float*>(p.C)[row * p.ldc + col] = v;
   } else if (EPI == EPI_GELU) {
-    float u = acc + (p.bias ? p.bias[col] : 0.f);
-    Act<TA>::st(reinterpret_cast<TA*>(p.C), row * p.ldc + col, u);
-    Act<TA>::st(reinterpret_cast<TA*>(p.aux), row * p.ld_aux + col, gelu_f(u));
+    float g, d;
+    gelu_and_grad(acc + (p.bias ? p.bias[col] : 0.f), g, d);
+    Act<TA>::st(reinterpret_cast<TA*>(p.C), row * p.ldc + col, d);
+    Act<TA>::st(reinterpret_cast<TA*>(p.aux), row * p.ld_aux + col, g);
   } else if (EPI == EPI_DGELU) {
-    float u = Act<TA>::ld(reinterpret_cast<const TA*>(p.aux), row * p.ld_aux + col);
-    Act<TA>::st(reinterpret_cast<TA*>(p.C), row * p.ldc + col, acc * gelu_grad_f(u));
+    const float d = Act<TA>::ld(reinterpret_cast<const TA*>(p.aux), row * p.ld_aux + col);
+    Act<TA>::st(reinterpret_cast<TA*>(p.C), row * p.ldc + col, acc * d);
   }
 }
 
@@ -130,16 +132,16 @@ __device__ __forceinline__ void epilogue8(const GemmArgs& p, long row, long col,
     for (int i = 0; i < 8; ++i) v[i] += r[i];
     st8_f32(reinterpret_cast<float*>(p.C) + row * p.ldc + col, v);
   } else if (EPI == EPI_GELU) {
-    st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
     float a[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = gelu_f(v[i]);
+    for (int i = 0; i < 8; ++i) gelu_and_grad(v[i], a[i], v[i]);
+    st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
     st8_h<E>(reinterpret_cast<E*>(p.aux) + row * p.ld_aux + col, a);
   } else if (EPI == EPI_DGELU) {
-    float u[8];
-    ld8_h<E>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col, u);
+    float d[8];
+    ld8_h<E>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col, d);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] *= gelu_grad_f(u[i]);
+    for (int i = 0; i < 8; ++i) v[i] *= d[i];
     st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
   }
 }
@@ -359,7 +361,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
   };
 
   // epilogue operands loaded ahead (one 8-column chunk per thread and pass):
-  // GELU': this thread's chunks of u, at the unit's start, so their latency
+  // GELU': this thread's chunks of the stored GELU'(u), at the unit's start, so their latency
   // hides behind the K loop; residual: the first wave row's fp32 chunks at
   // the unit's start, the next row's before each staging pass
   constexpr int CPT = WTM * BN / 8 / NT;  // epilogue chunks per thread and wave row
@@ -511,8 +513,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
             const uint32_t uw[4] = {uu.x, uu.y, uu.z, uu.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              v[2 * i] *= gelu_grad_f(H16<E>::lo(uw[i]));
-              v[2 * i + 1] *= gelu_grad_f(H16<E>::hi(uw[i]));
+              v[2 * i] *= H16<E>::lo(uw[i]);
+              v[2 * i + 1] *= H16<E>::hi(uw[i]);
             }
             st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
           }
@@ -786,17 +788,22 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& p, long row, long col,
     v += *reinterpret_cast<const f32x4_t*>(p.R + row * p.ldr + col);
     *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + row * p.ldc + col) = v;
   } else if (EPI == EPI_GELU) {
-    st4(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
-    f32x4_t a;
+    f32x4_t a, d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = gelu_f(v[i]);
+    for (int i = 0; i < 4; ++i) {
+      float gi, di;
+      gelu_and_grad(v[i], gi, di);
+      a[i] = gi;
+      d[i] = di;
+    }
+    st4(reinterpret_cast<E*>(p.C) + row * p.ldc + col, d);
     st4(reinterpret_cast<E*>(p.aux) + row * p.ld_aux + col, a);
   } else if (EPI == EPI_DGELU) {
     const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const E*>(p.aux) + row * p.ld_aux + col);
-    v[0] *= gelu_grad_f(H16<E>::lo(u.x));
-    v[1] *= gelu_grad_f(H16<E>::hi(u.x));
-    v[2] *= gelu_grad_f(H16<E>::lo(u.y));
-    v[3] *= gelu_grad_f(H16<E>::hi(u.y));
+    v[0] *= H16<E>::lo(u.x);
+    v[1] *= H16<E>::hi(u.x);
+    v[2] *= H16<E>::lo(u.y);
+    v[3] *= H16<E>::hi(u.y);
     st4(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
   }
 }
@@ -867,11 +874,11 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
   // from (lane % (64 / RPQ)) * CW, CW = 8 for 16-bit outputs, 4 for fp32.
   constexpr bool H = sizeof(TC) == 2;
   constexpr int CW = H ? 8 : 4, LPR = 64 / CW, RPQ = 64 / LPR, NQ = 32 / RPQ;
-  // The residual or GELU input is loaded ahead into registers (when the wave
-  // tile is small enough to keep them): the passes i < PRE_I with the unit's
-  // first K steps, so their latency hides behind the K loop, the others at
-  // the start of the epilogue. (Two passes of the GELU input take 32 VGPRs,
-  // one pass of the fp32 residual as many.)
+  // The residual or the stored GELU'(u) is loaded ahead into registers (when
+  // the wave tile is small enough to keep them): the passes i < PRE_I with the
+  // unit's first K steps, so their latency hides behind the K loop, the others
+  // at the start of the epilogue. (Two passes of the 16-bit GELU'(u) take 32
+  // VGPRs, one pass of the fp32 residual as many.)
   constexpr bool PRE = (EPI == EPI_RESID || EPI == EPI_DGELU) && TM <= 2;
   // 16-bit plain and GELU outputs: the next unit's first loads are issued
   // before the outputs, which go out through buffer stores (an out-of-range
@@ -1115,10 +1122,10 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
           if constexpr (PRE && EPI == EPI_DGELU) {
             const f32x4_t lo = out[2 * q], hi = out[2 * q + 1];
             const uint4 u = pre[i][q];
-            float v[8] = {lo[0] * gelu_grad_f(H16<E>::lo(u.x)), lo[1] * gelu_grad_f(H16<E>::hi(u.x)),
-                          lo[2] * gelu_grad_f(H16<E>::lo(u.y)), lo[3] * gelu_grad_f(H16<E>::hi(u.y)),
-                          hi[0] * gelu_grad_f(H16<E>::lo(u.z)), hi[1] * gelu_grad_f(H16<E>::hi(u.z)),
-                          hi[2] * gelu_grad_f(H16<E>::lo(u.w)), hi[3] * gelu_grad_f(H16<E>::hi(u.w))};
+            float v[8] = {lo[0] * H16<E>::lo(u.x), lo[1] * H16<E>::hi(u.x),
+                          lo[2] * H16<E>::lo(u.y), lo[3] * H16<E>::hi(u.y),
+                          hi[0] * H16<E>::lo(u.z), hi[1] * H16<E>::hi(u.z),
+                          hi[2] * H16<E>::lo(u.w), hi[3] * H16<E>::hi(u.w)};
             st8_h<E>(reinterpret_cast<E*>(p.C) + row * p.ldc + col, v);
             if constexpr (CSUM) {
 #pragma unroll
@@ -1180,11 +1187,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
             __builtin_amdgcn_raw_buffer_store_b128(outp[i][q], rc, (int)oc, 0, 0);
           } else {
             const f32x4_t lo = outs[i][2 * q], hi = outs[i][2 * q + 1];
-            float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            bst8_h<E>(rc, oc, v);
+            const float u[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            float g[8], d[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = gelu_f(v[e]);
-            bst8_h<E>(rx, ok ? (unsigned)((lr * ldx + lc) * 2) : kOutOfRange, v);
+            for (int e = 0; e < 8; ++e) gelu_and_grad(u[e], g[e], d[e]);
+            bst8_h<E>(rc, oc, d);
+            bst8_h<E>(rx, ok ? (unsigned)((lr * ldx + lc) * 2) : kOutOfRange, g);
           }
         }
     }
@@ -1209,7 +1217,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
 // keeps its wave tile's rows 32 g .. 32 g + 31 and receives the other group's
 // partial sums of them (a + b, the same in either order: the result does not
 // depend on which group arrives first), then stores those 32 rows straight
-// from registers; the residual or GELU input of those rows is loaded ahead,
+// from registers; the residual or GELU'(u) of those rows is loaded ahead,
 // with the tile's first K steps.
 template <int TN, int S, bool AK, bool BKC, int EPI, typename TC, typename E>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1221,7 +1229,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int NLD = LA::NI + LB::NI;  // load instructions per wavefront per K step
   constexpr bool H = sizeof(TC) == 2;
   // epilogue operands, 4 columns of a row per chunk, TN * 4 chunks per lane:
-  // the 16-bit GELU input (8 bytes a chunk) is loaded with the tile's first
+  // the 16-bit GELU'(u) (8 bytes a chunk) is loaded with the tile's first
   // K steps; the fp32 residual (16 bytes a chunk: 48 more registers through
   // the K loop would spill) right after the K loop, its latency partly
   // hidden by the exchange of the partial sums
@@ -1440,17 +1448,27 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       if constexpr (EPI == EPI_RESID) v += __builtin_bit_cast(f32x4_t, pre[q]);
       if constexpr (EPI == EPI_DGELU) {
         const w2_t uu = pre[q];
-        v[0] *= gelu_grad_f(H16<E>::lo(uu[0]));
-        v[1] *= gelu_grad_f(H16<E>::hi(uu[0]));
-        v[2] *= gelu_grad_f(H16<E>::lo(uu[1]));
-        v[3] *= gelu_grad_f(H16<E>::hi(uu[1]));
+        v[0] *= H16<E>::lo(uu[0]);
+        v[1] *= H16<E>::hi(uu[0]);
+        v[2] *= H16<E>::lo(uu[1]);
+        v[3] *= H16<E>::hi(uu[1]);
       }
       if constexpr (H) {
+        f32x4_t g;
+        if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float ge, de;
+            gelu_and_grad(v[e], ge, de);
+            g[e] = ge;
+            v[e] = de;
+          }
+        }
         const w2_t w = w2_t{H16<E>::pack(v[0], v[1]), H16<E>::pack(v[2], v[3])};
         __builtin_amdgcn_raw_buffer_store_b64(w, rc, ok ? (lrow * ldc + lc) * 2 : (int)kOutOfRange, 0, 0);
         if constexpr (EPI == EPI_GELU) {
-          const w2_t g = w2_t{H16<E>::pack(gelu_f(v[0]), gelu_f(v[1])), H16<E>::pack(gelu_f(v[2]), gelu_f(v[3]))};
-          __builtin_amdgcn_raw_buffer_store_b64(g, rx, ok ? (lrow * ldx + lc) * 2 : (int)kOutOfRange, 0, 0);
+          const w2_t gw = w2_t{H16<E>::pack(g[0], g[1]), H16<E>::pack(g[2], g[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(gw, rx, ok ? (lrow * ldx + lc) * 2 : (int)kOutOfRange, 0, 0);
         }
       } else {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(w4_t, v), rc,

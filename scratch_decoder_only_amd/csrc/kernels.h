@@ -18,8 +18,8 @@ constexpr int kColRows = 128;        // rows per partial in the bias-gradient co
 enum GemmEpi : int {
   EPI_STORE = 0,    // C = acc (+ bias[j]); C fp32 or activation type
   EPI_RESID = 1,    // C fp32 = R[i, j] + acc (+ bias[j])
-  EPI_GELU = 2,     // u = acc + bias[j]: C (act) = u, aux (act) = GELU(u)
-  EPI_DGELU = 3,    // C (act) = acc * GELU'(aux[i, j])
+  EPI_GELU = 2,     // u = acc + bias[j]: C (act) = GELU'(u), aux (act) = GELU(u)
+  EPI_DGELU = 3,    // C (act) = acc * aux[i, j] (aux: the GELU' the forward stored)
   EPI_PARTIAL = 4,  // C fp32 [split][M][ldc] = acc (split-K partial sums)
 };
 
