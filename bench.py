@@ -64,19 +64,27 @@ def attention_flops(shape, doc_ids, B, T):
 
 # Kernel symbol of each timing class whose HBM traffic is taken from counters:
 # a class maps to one kernel instantiation used by nothing else, or to
-# (symbol, period, phase) when two classes share an instantiation in a fixed
-# alternation: the class takes that kernel's dispatches whose index, in
+# (symbol, period, phase) when several classes share an instantiation in a
+# fixed order: the class takes that kernel's dispatches whose index, in
 # dispatch order, is phase modulo period (the attention-output and MLP-out
 # forward GEMMs share the residual-epilogue kernel and alternate, attention
-# output first, in every block).
+# output first, in every block; the backward of a block runs the MLP-out,
+# MLP-in, attention-output and QKV weight gradients in that order on one
+# K-split instantiation). The vocabulary weight gradient's count is its
+# partial-sum GEMM alone (its split-K reduction is a separate kernel).
 TRAFFIC_SYMBOLS = {
-    "gemm_head_bwd_dw": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, false, false, 0, float,",
+    "gemm_head_bwd_dw": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, false, false, 4, float,",
     "gemm_head_fwd": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, true, true, 0,",
     "gemm_fc1_fwd": "gemm16_pipe_kernel<128, 128, 2, 2, 64, 2, 2, true, true, 2,",
     "gemm_fc2_bwd_dx": "gemm16_pipe_kernel<128, 128, 2, 2, 64, 2, 2, true, false, 3,",
+    "gemm_qkv_fwd": "gemm16_pipe_kernel<192, 128, 2, 2, 64, 2, 2, true, true, 0,",
     "adamw": "adamw_kernel(",
-    "gemm_attnout_fwd": ("gemm16_kernel<128, 128, 2, 2, true, true, 1, float,", 2, 0),
-    "gemm_fc2_fwd": ("gemm16_kernel<128, 128, 2, 2, true, true, 1, float,", 2, 1),
+    "gemm_attnout_fwd": ("gemm16_ksplit_kernel<3, 4, true, true, 1, float,", 2, 0),
+    "gemm_fc2_fwd": ("gemm16_ksplit_kernel<3, 4, true, true, 1, float,", 2, 1),
+    "gemm_fc2_bwd_dw": ("gemm16_ksplit_kernel<3, 4, false, false, 4, float,", 4, 0),
+    "gemm_fc1_bwd_dw": ("gemm16_ksplit_kernel<3, 4, false, false, 4, float,", 4, 1),
+    "gemm_attnout_bwd_dw": ("gemm16_ksplit_kernel<3, 4, false, false, 4, float,", 4, 2),
+    "gemm_qkv_bwd_dw": ("gemm16_ksplit_kernel<3, 4, false, false, 4, float,", 4, 3),
     "attn_bwd_dkv": "attn_dkv_kernel<64, unsigned short>",
     "attn_bwd_dq": "attn_dq_kernel<64, unsigned short>",
     "attn_fwd": "attn_fwd_kernel<64, unsigned short>",
@@ -230,6 +238,75 @@ def mfma_summary(pmc_dir, out=MFMA_FILE, cmd=""):
     print(out)
 
 
+GAP_FILE = os.path.join(ROOT, "profiles", "gemm_attn_gap_c4_step.md")
+GAP_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY",
+                "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE")
+
+
+def gap_summary(pmc_dir, out=GAP_FILE, cmd=""):
+    """Where the GEMM and attention kernels' cycles go, from one rocprofv3
+    --pmc run with GAP_COUNTERS: per kernel (summed over its dispatches), the
+    matrix cores' busy share of the SIMD cycles, the vector ALU's and the LDS
+    instructions' active shares (SQ_ACTIVE_INST_*, in 4-cycle units, summed
+    over the SIMDs), and the share of the wavefronts' lifetime spent waiting
+    for an operand (SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES, both in 4-cycle
+    units). SIMD cycles = GRBM_GUI_ACTIVE / XCDS x SIMDS."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            d = per.setdefault(k, {})
+            c, v = r["Counter_Name"], float(r["Counter_Value"])
+            if c == "GRBM_GUI_ACTIVE":
+                d.setdefault("grbm_rows", []).append(v)
+            else:
+                d[c] = d.get(c, 0.0) + v
+    by = {}
+    for (_, name), d in per.items():
+        rows = d.pop("grbm_rows", None)
+        if not rows or not ("gemm16" in name or "attn_" in name):
+            continue
+        gpu = max(rows) if len(rows) > 1 else rows[0] / XCDS
+        e = by.setdefault(name, {"n": 0, "gpu": 0.0})
+        e["n"] += 1
+        e["gpu"] += gpu
+        for c in GAP_COUNTERS[:-1]:
+            e[c] = e.get(c, 0.0) + d.get(c, 0.0)
+    if not by:
+        raise SystemExit("no GEMM or attention dispatches with the counters in " + pmc_dir)
+    lines = []
+    rec = {"source_digest": source_digest(), "kernels": {}}
+    for name, e in sorted(by.items(), key=lambda kv: -kv[1]["gpu"]):
+        simd = e["gpu"] * SIMDS
+        mfma = e["SQ_VALU_MFMA_BUSY_CYCLES"] / simd
+        valu = e["SQ_ACTIVE_INST_VALU"] * 4 / simd
+        lds = e["SQ_ACTIVE_INST_LDS"] * 4 / simd
+        wait = e["SQ_WAIT_INST_ANY"] / e["SQ_WAVE_CYCLES"] if e["SQ_WAVE_CYCLES"] else 0.0
+        vpm = (e["SQ_INSTS_VALU"] / (e["SQ_VALU_MFMA_BUSY_CYCLES"] / 32) if e["SQ_VALU_MFMA_BUSY_CYCLES"] else 0.0)
+        rec["kernels"][name] = {"dispatches": e["n"], "mfma_busy": round(mfma, 3), "valu_active": round(valu, 3),
+                                "lds_active": round(lds, 3), "wave_wait": round(wait, 3),
+                                "valu_insts_per_mfma": round(vpm, 2)}
+        lines.append(f"| `{name[:96]}` | {e['n']} | {mfma:.3f} | {valu:.3f} | {lds:.3f} | {wait:.3f} | {vpm:.1f} |")
+    with open(out, "w") as fh:
+        fh.write("# Where the GEMM and attention cycles go (hardware counters, GPT-2-small-shaped step, C4)\n\n")
+        fh.write("Command (repository root, on one MI355X):\n\n```\n" + cmd + "\n```\n\n")
+        fh.write("Per kernel, over all its dispatches of the run. SIMD cycles = GRBM_GUI_ACTIVE / "
+                 f"{XCDS} XCDs (rocprofv3 sums it over them) x {SIMDS} SIMDs. *MFMA busy* = "
+                 "SQ_VALU_MFMA_BUSY_CYCLES / SIMD cycles; *VALU active* and *LDS active* = SQ_ACTIVE_INST_VALU "
+                 "and SQ_ACTIVE_INST_LDS (4-cycle units, summed over the SIMDs) x 4 / SIMD cycles (the VALU "
+                 "share includes issuing the MFMAs); *wave wait* = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, the share "
+                 "of the wavefronts' lifetime spent waiting for an operand (memory, LDS or a dependency); "
+                 "*VALU / MFMA* = vector instructions (MFMAs included) per 32x32x16 MFMA.\n\n")
+        fh.write("| kernel | dispatches | MFMA busy | VALU active | LDS active | wave wait | VALU / MFMA |\n"
+                 "|---|---:|---:|---:|---:|---:|---:|\n")
+        fh.write("\n".join(lines) + "\n\n")
+        fh.write("Record (taken on the sources with this digest):\n\n```json\n" + json.dumps(rec, indent=1) +
+                 "\n```\n")
+    print(out)
+
+
 def mfma_record():
     try:
         txt = open(MFMA_FILE).read()
@@ -368,12 +445,17 @@ def main():
     ap.add_argument("--mfma-summary", metavar="PMC_DIR",
                     help="summarise a rocprofv3 --pmc run of the MFMA counters and exit")
     ap.add_argument("--cpu-batch", type=int, default=1, help="rows of the CPU oracle's timed step")
+    ap.add_argument("--gap-summary", metavar="PMC_DIR",
+                    help="write the cycle-attribution table of the GEMM and attention kernels from a --pmc run")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, cmd=args.pmc_cmd)
         return
     if args.mfma_summary:
         mfma_summary(args.mfma_summary, cmd=args.pmc_cmd)
+        return
+    if args.gap_summary:
+        gap_summary(args.gap_summary, cmd=args.pmc_cmd)
         return
     if args.stats_summary:
         stats_summary(*args.stats_summary, cmd=args.pmc_cmd, steps=args.steps + args.warmup)
