@@ -68,10 +68,8 @@ def attention_flops(shape, doc_ids, B, T):
 # fixed order: the class takes that kernel's dispatches whose index, in
 # dispatch order, is phase modulo period (the attention-output and MLP-out
 # forward GEMMs share the residual-epilogue kernel and alternate, attention
-# output first, in every block; the backward of a block runs the MLP-out,
-# MLP-in, attention-output and QKV weight gradients in that order on one
-# K-split instantiation). The vocabulary weight gradient's count is its
-# partial-sum GEMM alone (its split-K reduction is a separate kernel).
+# output first, in every block). The blocks' weight gradients run as one
+# grouped launch after the backward (gemm_dw_group).
 TRAFFIC_SYMBOLS = {
     "gemm_head_bwd_dw": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, false, false, 4, float,",
     "gemm_head_fwd": "gemm16_pipe_kernel<256, 256, 2, 4, 64, 2, 2, true, true, 0,",
@@ -81,10 +79,7 @@ TRAFFIC_SYMBOLS = {
     "adamw": "adamw_kernel(",
     "gemm_attnout_fwd": ("gemm16_ksplit_kernel<3, 4, true, true, 1, float,", 2, 0),
     "gemm_fc2_fwd": ("gemm16_ksplit_kernel<3, 4, true, true, 1, float,", 2, 1),
-    "gemm_fc2_bwd_dw": ("gemm16_ksplit_kernel<3, 4, false, false, 4, float,", 4, 0),
-    "gemm_fc1_bwd_dw": ("gemm16_ksplit_kernel<3, 4, false, false, 4, float,", 4, 1),
-    "gemm_attnout_bwd_dw": ("gemm16_ksplit_kernel<3, 4, false, false, 4, float,", 4, 2),
-    "gemm_qkv_bwd_dw": ("gemm16_ksplit_kernel<3, 4, false, false, 4, float,", 4, 3),
+    "gemm_dw_group": "gemm16_ksplit_kernel<3, 4, false, false, 4, float, unsigned short, true>",
     "attn_bwd_dkv": "attn_dkv_kernel<64, unsigned short>",
     "attn_bwd_dq": "attn_dq_kernel<64, unsigned short>",
     "attn_fwd": "attn_fwd_kernel<64, unsigned short>",

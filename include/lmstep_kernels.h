@@ -59,6 +59,23 @@ int lmk_gemm_cfg(int cfg, int precision, int M, int N, int K, const void* A, int
                  int64_t ldr, void* aux, int64_t ld_aux, int force_split, int M_out, float* ws, int64_t ws_floats,
                  void* stream);
 
+/* The weight gradients of several linear layers in one launch (Feste page,
+ * "Manual Backpropagation": dW = dY^T X per layer), as the training step runs
+ * those of its blocks: problem i (i < n) computes C_i[r,c] = sum_k
+ * A_i[k*lda_i + r] B_i[k*ldb_i + c], r < M_i, c < N_i, k < K_i, with
+ * (M_i, N_i, K_i) = mnk[3i], mnk[3i+1], mnk[3i+2]; A_i and B_i 16-bit
+ * (precision 1 bf16, 2 fp16), C_i fp32 (overwritten, leading dimension ldc_i).
+ * Each output element is one fixed-order sum over k (bit-identical between
+ * runs). table: a device buffer of at least lmk_gemm_group_table_bytes(n)
+ * bytes that the call fills (the stream is synchronized first); it must not
+ * be reused until the launch has run. Rules per problem as lmk_gemm's for a
+ * dW layout (both operands not K-contiguous). Returns -1 with nothing
+ * enqueued on a bad argument or a problem the grouped kernel does not take. */
+int64_t lmk_gemm_group_table_bytes(int n);
+int lmk_gemm_group(int precision, int n, const int* mnk, const void* const* A, const int64_t* lda,
+                   const void* const* B, const int64_t* ldb, float* const* C, const int64_t* ldc, void* table,
+                   int64_t table_bytes, void* stream);
+
 /* LayerNorm over rows of x [M,C] fp32 (biased variance): y = g (x-mu) rstd + b
  * (y in the activation type), mu and rstd [M] fp32 (RustGPT page, file list:
  * layer_norm). C a multiple of 128, at most 1024. */

@@ -100,6 +100,9 @@ _sig("lmk_gemm", c_int, [c_int, c_int, c_int, c_int, _P, c_int64, c_int, _P, c_i
                          _P, _P, c_int64, _P, c_int64, c_int, c_int, _P, c_int64, _P])
 _sig("lmk_gemm_cfg", c_int, [c_int, c_int, c_int, c_int, c_int, _P, c_int64, c_int, _P, c_int64, c_int, _P, c_int64,
                              c_int, c_int, _P, _P, c_int64, _P, c_int64, c_int, c_int, _P, c_int64, _P])
+_sig("lmk_gemm_group_table_bytes", c_int64, [c_int])
+_PI, _PV, _PL = ctypes.POINTER(c_int), ctypes.POINTER(c_void_p), ctypes.POINTER(c_int64)
+_sig("lmk_gemm_group", c_int, [c_int, c_int, _PI, _PV, _PL, _PV, _PL, _PV, _PL, _P, c_int64, _P])
 _sig("lmk_layernorm_fwd", c_int, [c_int, _P, _P, _P, c_int, c_int, c_float, _P, _P, _P, _P])
 _sig("lmk_layernorm_bwd", c_int, [c_int, _P, _P, _P, _P, _P, c_int, c_int, _P, _P, _P, _P, _P, _P, _P, _P])
 _sig("lmk_layernorm_bwd_ws_floats", c_int64, [c_int, c_int])
@@ -508,6 +511,26 @@ def gemm(precision, M, N, K, A, lda, a_kc, B, ldb, b_kc, C, ldc, epi=EPI_STORE, 
                        int(c_f32), _ptr(bias), _ptr(R), ldr, _ptr(aux), ld_aux, force_split, M_out, _ptr(ws),
                        0 if ws is None else ws.numel(), _stream())
     _kcheck(rc, "lmk_gemm")
+
+
+def gemm_group_table_bytes(n):
+    return _lib.lmk_gemm_group_table_bytes(n)
+
+
+def gemm_group(precision, problems, table):
+    """Weight gradients of several layers in one launch: problems is a list of
+    (M, N, K, A, lda, B, ldb, C, ldc), C[r, c] = sum_k A[k, r] B[k, c] (fp32 C)."""
+    n = len(problems)
+    mnk = (ctypes.c_int * (3 * n))(*[int(v) for p in problems for v in p[:3]])
+    As = (c_void_p * n)(*[_ptr(p[3]) for p in problems])
+    ldas = (c_int64 * n)(*[int(p[4]) for p in problems])
+    Bs = (c_void_p * n)(*[_ptr(p[5]) for p in problems])
+    ldbs = (c_int64 * n)(*[int(p[6]) for p in problems])
+    Cs = (c_void_p * n)(*[_ptr(p[7]) for p in problems])
+    ldcs = (c_int64 * n)(*[int(p[8]) for p in problems])
+    rc = _lib.lmk_gemm_group(precision, n, mnk, As, ldas, Bs, ldbs, Cs, ldcs, _ptr(table), table.numel() *
+                             table.element_size(), _stream())
+    _kcheck(rc, "lmk_gemm_group")
 
 
 def layernorm_fwd(precision, x, g, b, eps, y, mu, rstd):

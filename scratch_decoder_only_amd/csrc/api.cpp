@@ -133,6 +133,16 @@ struct lm_model {
   float *mu1, *r1, *mu2, *r2, *muf, *rf, *lse;
   float *g, *dy, *delta;
   char *g_act, *dbig, *dO;
+  // The per-layer weight gradients of the 16-bit path, when the model has
+  // enough of their tiles to fill the CUs several times over, run as one
+  // grouped launch after the backward (no K slices, no reduction passes, one
+  // launch's fixed cost): the output gradients they read are kept per layer
+  // (g_act_l: the two LayerNorm-backward outputs of each block, du_l: the
+  // MLP-in pre-activation gradient, dqkv_l: the QKV gradient), and dw_tab is
+  // the launch's table on the device, dw_tab_host its last uploaded image.
+  bool dw_group = false;
+  char *g_act_l = nullptr, *du_l = nullptr, *dqkv_l = nullptr, *dw_tab = nullptr;
+  std::vector<char> dw_tab_host;
   float *ln_part, *col_part, *bias_part, *gemm_ws;
   long gemm_ws_floats;
   EmbedBwdWs emb_tok, emb_pos;
@@ -230,6 +240,27 @@ void build_table(lm_model* m) {
 }
 
 std::vector<std::pair<const char*, GemmOp>> step_gemm_ops(lm_model* m);
+GemmOp dw_op(const void* dY, long M, long N, const void* X, long K, float* dW);
+
+// Token counts from which the blocks' weight gradients take the grouped
+// launch (below, each GEMM's K is short enough that the per-GEMM K-split
+// launches do as well)
+constexpr long kDwGroupMinRows = 2048;
+
+// Units of a grouped launch of every block's four weight gradients at M
+// rows (-1: the grouped kernel does not take them).
+long dw_group_units(lm_model* m, long M) {
+  static const char dummy[256] = {0};
+  const void* X = dummy;
+  float* W = reinterpret_cast<float*>(const_cast<char*>(dummy));
+  const long C = m->C, F = m->F;
+  const GemmOp ops[4] = {dw_op(X, M, C, X, F, W), dw_op(X, M, F, X, C, W), dw_op(X, M, C, X, C, W),
+                         dw_op(X, M, 3 * C, X, C, W)};
+  std::vector<char> tab(gemm_group_table_bytes(4));
+  int tn = 0;
+  const int units = gemm_group_plan(ops, 4, tab.data(), &tn);
+  return units < 0 ? -1 : (long)units * m->L;
+}
 
 // Lays out every slice of the arena (base == nullptr: size only).
 void carve(lm_model* m, char* base) {
@@ -264,6 +295,12 @@ void carve(lm_model* m, char* base) {
   m->g_act = c.take<char>(M * C * A);
   m->dbig = c.take<char>(M * std::max(F, 3 * C) * A);
   m->dO = c.take<char>(M * C * A);
+  if (m->dw_group) {
+    m->g_act_l = c.take<char>(L * 2 * M * C * A);
+    m->du_l = c.take<char>(L * M * F * A);
+    m->dqkv_l = c.take<char>(L * M * 3 * C * A);
+    m->dw_tab = c.take<char>(gemm_group_table_bytes(4 * (int)L));
+  }
   long ln_blocks = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
   // partial sums of every LayerNorm of the backward (2 per block + the
   // final one), reduced together once the backward is done
@@ -324,6 +361,7 @@ lm_model* new_model(const lm_config* cfg) {
   m->Vp = m->h16 ? round_up(m->V, 128) : m->V;
   m->ldz = m->h16 ? m->Vp : round_up(m->V, 4);
   build_table(m);
+  m->dw_group = m->h16 && m->L > 0 && dw_group_units(m, m->M()) >= 2L * gemm_cus();
   carve(m, nullptr);
   return m;
 }
@@ -684,13 +722,26 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   std::vector<float*> fc_pa(m->L), fc_oa(m->L), qkv_pa(m->L), qkv_oa(m->L);
   struct { std::vector<float*>& pa; std::vector<float*>& oa; } fcb{fc_pa, fc_oa}, qkvb{qkv_pa, qkv_oa};
   double ln_red_bytes = 0;
+  // the weight gradients of the blocks: one grouped launch after the loop
+  // (reading per-layer copies of the output gradients), or each right away
+  const bool grouped = m->dw_group && M >= kDwGroupMinRows;
+  std::vector<GemmOp> dw_ops;
+  auto weight_grad = [&](const char* name, GemmOp op) {
+    if (grouped) dw_ops.push_back(op);
+    else Lr.run(name, 2.0 * op.M * op.N * op.K, 0, [&] { rc |= gemm(m, op, s); });
+  };
+  // the 16-bit output gradient of block l's MLP (k = 0) or attention (k = 1)
+  // output, which a LayerNorm backward writes
+  auto g_act_of = [&](int l, int k) -> E* {
+    return grouped && l >= 0 ? m->act<E>(m->g_act_l, ((long)l * 2 + k) * M * C) : g_act;
+  };
   auto ln_bwd = [&](const float* x, const float* mu, const float* r, long g_off, long b_off, const float* g_in,
-                    float* dcol) {
+                    float* dcol, E* g_out) {
     float* pdg = m->ln_part + (long)lnb.size() * 3 * ln_blocks * C;
     float* pdb = pdg + ln_blocks * C;
     float* pdc = pdg + 2 * ln_blocks * C;
     Lr.run("layernorm_bwd", 0, Mf * C * ((g_in ? 4 * 4 : 3 * 4) + A), [&] {
-      launch_ln_bwd<E>(m->dy, x, mu, r, m->P_(g_off), (int)M, (int)C, g_in, m->g, g_act, pdg, pdb,
+      launch_ln_bwd<E>(m->dy, x, mu, r, m->P_(g_off), (int)M, (int)C, g_in, m->g, g_out, pdg, pdb,
                        dcol ? pdc : nullptr, s);
     });
     lnb.push_back({pdg, pdb, dcol ? pdc : nullptr, m->grads + g_off, m->grads + b_off, dcol});
@@ -712,11 +763,14 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   };
   // (with no blocks the final LayerNorm reads the embeddings: no bias below it)
   ln_bwd(m->x + m->L * M * C, m->muf, m->rf, m->o_lnf_g, m->o_lnf_b, nullptr,
-         m->L > 0 ? m->grads + m->blk[m->L - 1].b_proj : nullptr);
-  E* dbig = m->act<E>(m->dbig, 0);
+         m->L > 0 ? m->grads + m->blk[m->L - 1].b_proj : nullptr, g_act_of(m->L - 1, 0));
   E* dO = m->act<E>(m->dO, 0);
   for (int l = m->L - 1; l >= 0; --l) {
     const auto& b = m->blk[l];
+    E* g_mlp = g_act_of(l, 0);
+    E* g_att = g_act_of(l, 1);
+    E* du = grouped ? m->act<E>(m->du_l, l * M * F) : m->act<E>(m->dbig, 0);
+    E* dqkv = grouped ? m->act<E>(m->dqkv_l, l * M * 3 * C) : m->act<E>(m->dbig, 0);
     float* xl = m->x + l * M * C;
     float* xml = m->xm + l * M * C;
     E* y1 = m->act<E>(m->y1, l * M * C);
@@ -726,32 +780,32 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
     E* gd = m->act<E>(m->gelu_d, l * M * F);
     E* a = m->act<E>(m->a, l * M * F);
     // MLP out: x_{l+1} = xm + a W_proj^T + b_proj
-    Lr.run("gemm_fc2_bwd_dw", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, dw_op(g_act, M, C, a, F, m->grads + b.w_proj), s); });
+    weight_grad("gemm_fc2_bwd_dw", dw_op(g_mlp, M, C, a, F, m->grads + b.w_proj));
     {
-      GemmOp op = dx_op(m, g_act, M, C, b.w_proj, F, dbig, EPI_DGELU);
+      GemmOp op = dx_op(m, g_mlp, M, C, b.w_proj, F, du, EPI_DGELU);
       op.aux = gd; op.ld_aux = F;
       if (fc_fused) op.colsum = fc_part(l);
       Lr.run("gemm_fc2_bwd_dx", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, op, s); });
     }
     // MLP in: u = y2 W_fc^T + b_fc
-    Lr.run("gemm_fc1_bwd_dw", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, dw_op(dbig, M, F, y2, C, m->grads + b.w_fc), s); });
+    weight_grad("gemm_fc1_bwd_dw", dw_op(du, M, F, y2, C, m->grads + b.w_fc));
     if (!fc_fused)
-      Lr.run("bias_grad", 0, Mf * F * A, [&] { launch_colsum_stage1<E>(dbig, F, (int)M, (int)F, fc_part(l), s); });
+      Lr.run("bias_grad", 0, Mf * F * A, [&] { launch_colsum_stage1<E>(du, F, (int)M, (int)F, fc_part(l), s); });
     fcb.pa[l] = fc_part(l);
     fcb.oa[l] = m->grads + b.b_fc;
     {
-      GemmOp op = dx_op(m, dbig, M, F, b.w_fc, C, m->dy, EPI_STORE);
+      GemmOp op = dx_op(m, du, M, F, b.w_fc, C, m->dy, EPI_STORE);
       op.c_f32 = true;
       Lr.run("gemm_fc1_bwd_dx", 2.0 * M * C * F, 0, [&] { rc |= gemm(m, op, s); });
     }
-    ln_bwd(xml, m->mu2 + l * M, m->r2 + l * M, b.ln2_g, b.ln2_b, m->g, m->grads + b.b_o);
+    ln_bwd(xml, m->mu2 + l * M, m->r2 + l * M, b.ln2_g, b.ln2_b, m->g, m->grads + b.b_o, g_att);
     // attention out: xm = x + o W_o^T + b_o
-    Lr.run("gemm_attnout_bwd_dw", 2.0 * M * C * C, 0, [&] { rc |= gemm(m, dw_op(g_act, M, C, o, C, m->grads + b.w_o), s); });
-    Lr.run("gemm_attnout_bwd_dx", 2.0 * M * C * C, 0, [&] { rc |= gemm(m, dx_op(m, g_act, M, C, b.w_o, C, dO, EPI_STORE), s); });
+    weight_grad("gemm_attnout_bwd_dw", dw_op(g_att, M, C, o, C, m->grads + b.w_o));
+    Lr.run("gemm_attnout_bwd_dx", 2.0 * M * C * C, 0, [&] { rc |= gemm(m, dx_op(m, g_att, M, C, b.w_o, C, dO, EPI_STORE), s); });
     {
       AttnArgs at{};
       at.qkv = qkv; at.start = m->start; at.end = m->end; at.B = B; at.T = T; at.H = (int)H; at.D = m->D;
-      at.o = o; at.lse = m->lse + l * M * H; at.dout = dO; at.delta = m->delta; at.dqkv = dbig;
+      at.o = o; at.lse = m->lse + l * M * H; at.dout = dO; at.delta = m->delta; at.dqkv = dqkv;
       static const char* names[3] = {"attn_bwd_delta", "attn_bwd_dq", "attn_bwd_dkv"};
       // bf16: the dQ pass computes delta itself (part 0 launches nothing)
       for (int part = m->h16 ? 1 : 0; part < 3; ++part)
@@ -760,16 +814,35 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
           else rc |= attn_bwd_part16<E>(at, part, s);
         });
     }
-    Lr.run("gemm_qkv_bwd_dw", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, dw_op(dbig, M, 3 * C, y1, C, m->grads + b.w_qkv), s); });
-    Lr.run("bias_grad", 0, Mf * 3 * C * A, [&] { launch_colsum_stage1<E>(dbig, 3 * C, (int)M, (int)(3 * C), qkv_part(l), s); });
+    weight_grad("gemm_qkv_bwd_dw", dw_op(dqkv, M, 3 * C, y1, C, m->grads + b.w_qkv));
+    Lr.run("bias_grad", 0, Mf * 3 * C * A, [&] { launch_colsum_stage1<E>(dqkv, 3 * C, (int)M, (int)(3 * C), qkv_part(l), s); });
     qkvb.pa[l] = qkv_part(l);
     qkvb.oa[l] = m->grads + b.b_qkv;
     {
-      GemmOp op = dx_op(m, dbig, M, 3 * C, b.w_qkv, C, m->dy, EPI_STORE);
+      GemmOp op = dx_op(m, dqkv, M, 3 * C, b.w_qkv, C, m->dy, EPI_STORE);
       op.c_f32 = true;
       Lr.run("gemm_qkv_bwd_dx", 2.0 * M * 3 * C * C, 0, [&] { rc |= gemm(m, op, s); });
     }
-    ln_bwd(xl, m->mu1 + l * M, m->r1 + l * M, b.ln1_g, b.ln1_b, m->g, l > 0 ? m->grads + m->blk[l - 1].b_proj : nullptr);
+    ln_bwd(xl, m->mu1 + l * M, m->r1 + l * M, b.ln1_g, b.ln1_b, m->g, l > 0 ? m->grads + m->blk[l - 1].b_proj : nullptr,
+           g_act_of(l - 1, 0));
+  }
+  if (grouped) {
+    // the table depends on the token count (the K of these GEMMs): uploaded
+    // when it differs from the last upload, after the stream has drained (the
+    // previous launch may still read the device copy)
+    std::vector<char> tab(gemm_group_table_bytes((int)dw_ops.size()));
+    int tn = 0;
+    const int units = gemm_group_plan(dw_ops.data(), (int)dw_ops.size(), tab.data(), &tn);
+    double flops = 0;
+    for (const GemmOp& op : dw_ops) flops += 2.0 * op.M * op.N * op.K;
+    if (units < 0) return -1;
+    if (tab != m->dw_tab_host) {
+      if (hipStreamSynchronize(s) != hipSuccess ||
+          hipMemcpy(m->dw_tab, tab.data(), tab.size(), hipMemcpyHostToDevice) != hipSuccess)
+        return -1;
+      m->dw_tab_host = tab;
+    }
+    Lr.run("gemm_dw_group", flops, 0, [&] { rc |= gemm_group_launch(m->prec == 2, tn, m->dw_tab, units, s); });
   }
   // embedding: dwte[tok] += dx0 (on top of the tied head's part, else from
   // zero), dwpe[pos] = sum dx0

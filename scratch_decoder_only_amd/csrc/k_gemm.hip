@@ -24,6 +24,7 @@
 // hundred million flops per step and bound by launch latency, not by either.
 #include <algorithm>
 #include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "kernels.h"
@@ -47,6 +48,14 @@ struct GemmArgs {
   int k_split;        // K elements per blockIdx.z slice
   long split_stride;  // floats between the partial outputs of two slices
   float* colsum;      // GemmOp::colsum
+};
+
+// One GEMM of a grouped launch: its arguments, its first unit in the
+// launch's unit numbering and its tile grid. The table ends with a sentinel
+// entry whose first_unit is the launch's unit count.
+struct GemmGroupEntry {
+  GemmArgs a;
+  int first_unit, tiles_m, tiles_n, pad;
 };
 
 // Epilogue of one output element (shared by both GEMM kernels and the
@@ -1219,9 +1228,14 @@ __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_pe
 // depend on which group arrives first), then stores those 32 rows straight
 // from registers; the residual or GELU'(u) of those rows is loaded ahead,
 // with the tile's first K steps.
-template <int TN, int S, bool AK, bool BKC, int EPI, typename TC, typename E>
+//
+// GROUP: the units of several GEMMs of the same layout and epilogue in one
+// launch (table tab, units numbered GEMM after GEMM), each unit one whole
+// tile over all of K; the arguments of a unit's GEMM are read from the table.
+template <int TN, int S, bool AK, bool BKC, int EPI, typename TC, typename E, bool GROUP = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-    gemm16_ksplit_kernel(GemmArgs p, int units, int tiles_m, int tiles_n) {
+    gemm16_ksplit_kernel(GemmArgs p_in, int units, int tiles_m, int tiles_n,
+                         const GemmGroupEntry* __restrict__ tab) {
   constexpr int BM = 128, TM = 2, WTM = 64, WTN = 32 * TN, BN = 2 * WTN, BK = 64, NT = 512;
   static_assert(S == 3 || S == 4, "three or four stages");
   using LA = PTile<BM, AK, NT, BK>;
@@ -1245,9 +1259,21 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
-  const bf16* A = reinterpret_cast<const bf16*>(p.A);
-  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+  GemmArgs p = p_in;
   const int nb = gridDim.x;
+  // the tile (tm, tn) and K slice z of unit u; with GROUP also its GEMM's
+  // arguments into p (units are visited in increasing order, so the table
+  // index only moves forward)
+  int gi = 0;
+  auto locate = [&](int u, int& tm, int& tn, int& z) {
+    if constexpr (GROUP) {
+      while (u >= tab[gi + 1].first_unit) ++gi;
+      p = tab[gi].a;
+      pipe_tile(u - tab[gi].first_unit, tab[gi].tiles_m, tab[gi].tiles_n, tm, tn, z);
+    } else {
+      pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
+    }
+  };
   auto sa = [](auto I_) -> bf16* { return lds_stage<2 * decltype(I_)::value, LA::ELEMS>(); };
   auto sb = [](auto I_) -> bf16* { return lds_stage<2 * decltype(I_)::value + 1, LB::ELEMS>(); };
   // region r of the exchange as an fp32 pointer into one known LDS array
@@ -1316,9 +1342,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
       }
   };
-  auto prologue = [&](int u) {
-    int tm, tn, z;
-    pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
+  auto prologue = [&](int tm, int tn, int z) {
+    const bf16* A = reinterpret_cast<const bf16*>(p.A);
+    const bf16* B = reinterpret_cast<const bf16*>(p.B);
     const int kb = z * p.k_split, ke = min(p.K, kb + p.k_split);
     if constexpr (BIAS) {
       // the tile's bias, by wavefront 0 ahead of the stage loads (the first
@@ -1350,10 +1376,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   int u = pipe_unit(0, blockIdx.x, nb);
   for (; u < units; u = pipe_unit(++round, blockIdx.x, nb)) {
     int tm, tn, z;
-    pipe_tile(u, tiles_m, tiles_n, tm, tn, z);
+    locate(u, tm, tn, z);
     const int kb = z * p.k_split, ke = min(p.K, kb + p.k_split);
     const int nk = (ke - kb + BK - 1) / BK;
-    prologue(u);
+    prologue(tm, tn, z);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1740,7 +1766,7 @@ static void launch_ksplit(const GemmArgs& a, int splits, hipStream_t s) {
   if (units < nb) nb = units;
   nb = (nb + 7) / 8 * 8;  // whole XCD rounds
   hipLaunchKernelGGL((gemm16_ksplit_kernel<TN, S, AK, BKC, EPI, TC, E>), dim3(nb), dim3(512), 0, s, a, units,
-                     tiles_m, tiles_n);
+                     tiles_m, tiles_n, (const GemmGroupEntry*)nullptr);
 }
 
 // One launch of configuration cfg with the epilogue EPI and output type TC.
@@ -1872,6 +1898,76 @@ static int gemm16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) {
 
 int gemm_bf16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) { return gemm16<bf16>(op, ws, ws_floats, s); }
 int gemm_f16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) { return gemm16<f16>(op, ws, ws_floats, s); }
+
+// ------------------------------------------------------- grouped launch
+// Weight gradients (both operands M/N-contiguous, fp32 output, plain store,
+// no bias) of many GEMMs in one persistent launch of the K-split kernel, one
+// whole tile over all of K per unit: no K slices, so no partial sums and no
+// reduction pass, and one launch's fixed cost (first loads, last stores)
+// instead of one per GEMM.
+long gemm_group_table_bytes(int n) { return (long)(n + 1) * (long)sizeof(GemmGroupEntry); }
+
+int gemm_group_plan(const GemmOp* ops, int n, void* table, int* tn) {
+  if (n < 1 || !table || !tn) return -1;
+  bool w192 = true;
+  for (int i = 0; i < n; ++i) {
+    const GemmOp& op = ops[i];
+    if (op.a_kc || op.b_kc || op.epi != EPI_STORE || !op.c_f32 || op.bias || op.R || op.aux || op.colsum ||
+        op.cfg != 0 || op.force_split > 1 || op.M <= 0 || op.N <= 0 || op.K <= 0 || !check_16(op))
+      return -1;
+    w192 = w192 && op.N % 192 == 0;
+  }
+  // 128 x 192 tiles when every output width is a multiple of 192, else 128 x 128
+  *tn = w192 ? 3 : 2;
+  const int bn = 64 * *tn;
+  GemmGroupEntry* e = static_cast<GemmGroupEntry*>(table);
+  long units = 0;
+  // (field by field into zeroed entries: the table's bytes, padding
+  // included, depend only on the ops, so callers can compare tables bytewise)
+  std::memset(table, 0, (size_t)gemm_group_table_bytes(n));
+  for (int i = 0; i < n; ++i) {
+    const GemmArgs a = make_args(ops[i]);
+    GemmArgs& d = e[i].a;
+    d.A = a.A; d.lda = a.lda; d.B = a.B; d.ldb = a.ldb; d.C = a.C; d.ldc = a.ldc;
+    d.bias = a.bias; d.R = a.R; d.ldr = a.ldr; d.aux = a.aux; d.ld_aux = a.ld_aux;
+    d.M = a.M; d.N = a.N; d.K = a.K; d.M_out = a.M_out; d.k_split = a.k_split;
+    d.split_stride = a.split_stride; d.colsum = a.colsum;
+    e[i].first_unit = (int)units;
+    e[i].tiles_m = (ops[i].M + 127) / 128;
+    e[i].tiles_n = (ops[i].N + bn - 1) / bn;
+    units += (long)e[i].tiles_m * e[i].tiles_n;
+    if (units > (1L << 30)) return -1;
+  }
+  e[n].first_unit = (int)units;
+  return (int)units;
+}
+
+// (the partial-sum epilogue of a single slice is the plain fp32 store
+// without bias, and it keeps the K loop's registers those of the split-K
+// weight-gradient launches)
+template <int TN, typename E>
+static void launch_group(const void* table, int units, hipStream_t s) {
+  int nb = device_cus();
+  if (units < nb) nb = units;
+  nb = (nb + 7) / 8 * 8;  // whole XCD rounds
+  hipLaunchKernelGGL((gemm16_ksplit_kernel<TN, 4, false, false, EPI_PARTIAL, float, E, true>), dim3(nb), dim3(512),
+                     0, s, GemmArgs{}, units, 0, 0, static_cast<const GemmGroupEntry*>(table));
+}
+
+int gemm_group_launch(bool f16_ops, int tn, const void* table_dev, int units, hipStream_t s) {
+  if (!table_dev || units < 0 || (tn != 2 && tn != 3)) return -1;
+  if (units == 0) return 0;
+  if (f16_ops) {
+    if (tn == 3) launch_group<3, f16>(table_dev, units, s);
+    else launch_group<2, f16>(table_dev, units, s);
+  } else {
+    if (tn == 3) launch_group<3, bf16>(table_dev, units, s);
+    else launch_group<2, bf16>(table_dev, units, s);
+  }
+  return 0;
+}
+
+int gemm_cus() { return device_cus(); }
 
 template <bool AK, bool BKC>
 static int dispatch_f32(const GemmOp& op, const GemmArgs& a, int splits, hipStream_t s) {

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "../../include/lmstep_kernels.h"
 #include "kernels.h"
@@ -53,6 +54,34 @@ int lmk_gemm(int precision, int M, int N, int K, const void* A, int64_t lda, int
              void* aux, int64_t ld_aux, int force_split, int M_out, float* ws, int64_t ws_floats, void* stream) {
   return lmk_gemm_cfg(0, precision, M, N, K, A, lda, a_kc, B, ldb, b_kc, C, ldc, epi, c_f32, bias, R, ldr, aux,
                       ld_aux, force_split, M_out, ws, ws_floats, stream);
+}
+
+int64_t lmk_gemm_group_table_bytes(int n) { return n < 1 ? -1 : gemm_group_table_bytes(n); }
+
+int lmk_gemm_group(int precision, int n, const int* mnk, const void* const* A, const int64_t* lda,
+                   const void* const* B, const int64_t* ldb, float* const* C, const int64_t* ldc, void* table,
+                   int64_t table_bytes, void* stream) {
+  if ((precision != 1 && precision != 2) || n < 1 || !mnk || !A || !lda || !B || !ldb || !C || !ldc || !table)
+    return -1;
+  if (table_bytes < gemm_group_table_bytes(n)) return -1;
+  std::vector<GemmOp> ops(n);
+  for (int i = 0; i < n; ++i) {
+    if (!A[i] || !B[i] || !C[i]) return -1;
+    GemmOp& op = ops[i];
+    op.M = mnk[3 * i]; op.N = mnk[3 * i + 1]; op.K = mnk[3 * i + 2];
+    op.A = A[i]; op.lda = lda[i]; op.a_kc = false;
+    op.B = B[i]; op.ldb = ldb[i]; op.b_kc = false;
+    op.C = C[i]; op.ldc = ldc[i]; op.epi = EPI_STORE; op.c_f32 = true;
+  }
+  std::vector<char> host(gemm_group_table_bytes(n));
+  int tn = 0;
+  const int units = gemm_group_plan(ops.data(), n, host.data(), &tn);
+  if (units < 0) return -1;
+  hipStream_t s = S(stream);
+  if (hipStreamSynchronize(s) != hipSuccess ||
+      hipMemcpy(table, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess)
+    return -1;
+  return gemm_group_launch(precision == 2, tn, table, units, s);
 }
 
 static bool ln_shape_ok(int M, int C) { return M >= 0 && C >= 128 && C <= 1024 && C % 128 == 0; }

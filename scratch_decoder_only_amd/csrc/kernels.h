@@ -71,6 +71,18 @@ int gemm16_splits(const GemmOp& op);
 // where it cannot (then colsum must stay null).
 int gemm16_colsum_rows(const GemmOp& op);
 
+// Grouped launch of weight-gradient GEMMs (16-bit operands, both M/N-major,
+// fp32 output, plain store, no bias): gemm_group_plan fills a table of
+// gemm_group_table_bytes(n) bytes in host memory for ops[0..n) and returns
+// the launch's unit count (-1: an op the grouped kernel does not take), with
+// the tile width in *tn; gemm_group_launch runs the launch from a device copy
+// of that table. Each output element is one unit's fixed-order sum over K.
+long gemm_group_table_bytes(int n);
+int gemm_group_plan(const GemmOp* ops, int n, void* table, int* tn);
+int gemm_group_launch(bool f16_ops, int tn, const void* table_dev, int units, hipStream_t s);
+// compute units of the current device
+int gemm_cus();
+
 // -------------------------------------------------------------- rows etc.
 void launch_fill_u32(uint32_t* p, uint32_t v, long n, hipStream_t s);
 void launch_index_layout(const int32_t* doc, int B, int T, int32_t* start, int32_t* end, int32_t* pos,

@@ -143,6 +143,31 @@ def test_models_whose_operands_exceed_the_kernel_limits_fail_at_creation(lib, pr
     assert b"2 GiB" in msg and b"vocabulary" in msg
 
 
+def test_grouped_gemm_arguments_are_checked(lib):
+    """lmk_gemm_group refuses bad arguments on the host, before any copy or
+    launch."""
+    import scratch_decoder_only_amd as sd
+    assert sd.lib.lmk_gemm_group_table_bytes(0) == -1
+    need = sd.lib.lmk_gemm_group_table_bytes(2)
+    assert need > sd.lib.lmk_gemm_group_table_bytes(1) > 0
+    P = 256
+    mnk = (ctypes.c_int * 6)(64, 64, 64, 64, 64, 64)
+    ptrs = (ctypes.c_void_p * 2)(P, P)
+    ld = (ctypes.c_int64 * 2)(64, 64)
+    bad_ld = (ctypes.c_int64 * 2)(64, 12)
+    T = ctypes.c_void_p(P)
+    call = sd.lib.lmk_gemm_group
+    # the fp32 path has no grouped kernel; empty groups; a table too small
+    assert call(0, 2, mnk, ptrs, ld, ptrs, ld, ptrs, ld, T, need, None) != 0
+    assert call(1, 0, mnk, ptrs, ld, ptrs, ld, ptrs, ld, T, need, None) != 0
+    assert call(1, 2, mnk, ptrs, ld, ptrs, ld, ptrs, ld, T, need - 1, None) != 0
+    # a 16-bit operand leading dimension that is not a multiple of 8
+    assert call(1, 2, mnk, ptrs, bad_ld, ptrs, ld, ptrs, ld, T, need, None) != 0
+    # a null operand
+    nulls = (ctypes.c_void_p * 2)(P, None)
+    assert call(1, 2, mnk, ptrs, ld, nulls, ld, ptrs, ld, T, need, None) != 0
+
+
 def test_gemm_configuration_requests_are_checked(lib):
     import scratch_decoder_only_amd as sd
     P = ctypes.c_void_p(256)

@@ -239,6 +239,40 @@ def test_gemm_persistent_rounds(sd, prec, epi, b_kc):
         assert rel(host(Aout), oracle.gelu(lin)) <= tol(prec, False)
 
 
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("case", ["w192", "w128"])
+def test_gemm_group(sd, prec, case):
+    """Weight gradients of several layers in one grouped launch (each output
+    one unit's fixed-order sum over all of K): every problem against the
+    oracle's dW = dY^T X, ragged in M, N and K; more units than the persistent
+    grid holds, so blocks walk several problems; 128 x 192 tiles when every
+    width is a multiple of 192 (w192), else 128 x 128; bit-identical reruns."""
+    t = torch()
+    if case == "w192":
+        shapes = [(200, 384, 1000), (1000, 192, 520), (136, 576, 64), (1280, 3840, 136), (2056, 1920, 200)]
+    else:
+        shapes = [(264, 200, 320), (8, 8, 8), (1000, 648, 576), (2056, 1288, 72), (1024, 1024, 96)]
+    rng = np.random.default_rng(71 + prec + 10 * len(case))
+    print(f"gemm group prec={prec} case={case}", flush=True)
+    probs, expect, outs = [], [], []
+    for (M, N, K) in shapes:
+        dY, X = _operands(rng, prec, (K, M), (K, N))
+        C = t.full((M, N), 3.0, dtype=t.float32, device="cuda")
+        probs.append((M, N, K, act(dY, prec), M, act(X, prec), N, C, N))
+        expect.append(oracle.linear_bwd(dY, X, np.zeros((M, N)))[1])
+        outs.append(C)
+    table = t.zeros(sd.gemm_group_table_bytes(len(probs)), dtype=t.uint8, device="cuda")
+    sd.gemm_group(prec, probs, table)
+    t.cuda.synchronize()
+    first = [c.clone() for c in outs]
+    for c, e in zip(outs, expect):
+        assert rel(host(c), e) <= tol(prec, True)
+    sd.gemm_group(prec, probs, table)
+    t.cuda.synchronize()
+    for c, f in zip(outs, first):
+        assert t.equal(c, f)
+
+
 def test_gemm_output_row_limit(sd):
     """Rows >= M_out are computed but never stored (the padded vocabulary)."""
     t = torch()
