@@ -105,6 +105,38 @@ def test_depth_extremes_match_oracle(sd, layers, precision):
     compare(shape, got, ref, params)
 
 
+def test_grouped_weight_gradients_follow_the_token_count(sd):
+    """The grouped weight-gradient launch's table depends on the token count
+    (the K of those GEMMs): a model that steps at 8 x 512 tokens, then at
+    4 x 512 (a new table) and 2 x 512 (below the grouping threshold: the
+    GEMMs run one by one) gives bit-for-bit the gradients and statistics of
+    fresh models stepping at those sizes directly."""
+    t = torch()
+    shape = synth.C4.replace(n_layers=2, vocab=2048).with_batch(8, 512)
+    tok, tgt, doc = _inputs(shape, 8)
+    params = synth.init_params(shape)
+    zeros = {k: np.zeros_like(a) for k, a in params.items()}
+    reused = sd.Model(shape, max_batch=8)
+
+    def step(model, B):
+        model.set(sd.LM_PARAMS, params)
+        model.set(sd.LM_ADAM_M, zeros)
+        model.set(sd.LM_ADAM_V, zeros)
+        stats = model.train_step(dev(tok[:B]), dev(tgt[:B]), None, lr=shape.lr, step=1, beta1=shape.beta1,
+                                 beta2=shape.beta2, eps=shape.eps, weight_decay=shape.weight_decay,
+                                 clip=shape.clip)
+        t.cuda.synchronize()
+        return stats.cpu().numpy(), model.get(sd.LM_GRADS)
+
+    for B in (8, 4, 2):
+        print(f"grouped weight gradients at B={B}", flush=True)
+        s_reused, g_reused = step(reused, B)
+        s_fresh, g_fresh = step(sd.Model(shape, max_batch=8), B)
+        assert np.array_equal(s_reused, s_fresh)
+        for k in g_fresh:
+            assert np.array_equal(g_reused[k], g_fresh[k]), (B, k)
+
+
 def test_binding_rejects_wrong_token_tensors_before_any_launch(sd):
     t = torch()
     shape = synth.C1.with_batch(2, 16)
