@@ -122,31 +122,23 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-// tanh(y) = 1 - 2 / (exp(2y) + 1): saturates to +-1 without overflow trouble.
-
 // GELU, tanh form: 0.5 u (1 + tanh(y)), y = sqrt(2/pi) (u + 0.044715 u^3),
-// evaluated as u s with s = 0.5 (1 + tanh(y)) = 1 / (1 + exp(-2y)) (the same
-// function); the reciprocal is the hardware one (about 1 ulp), so no IEEE
-// division sequence runs per element.
-__device__ __forceinline__ float gelu_sigmoid(float u) {
-  const float c2 = 2.0f * 0.7978845608028654f, a = 0.044715f;
-  const float y2 = c2 * u * __builtin_fmaf(a, u * u, 1.0f);
-  return __builtin_amdgcn_rcpf(1.0f + __expf(-y2));
-}
-__device__ __forceinline__ float gelu_f(float u) { return u * gelu_sigmoid(u); }
-// Its derivative: 0.5 (1 + t) + 0.5 u (1 - t^2) c (1 + 3 a u^2) with t =
-// tanh(y); in terms of s: s + 2 u s (1 - s) c (1 + 3 a u^2).
-__device__ __forceinline__ float gelu_grad_s(float u, float s) {
-  const float c = 0.7978845608028654f, a = 0.044715f;
-  return __builtin_fmaf(2.0f * c * u * s * (1.0f - s), __builtin_fmaf(3.0f * a, u * u, 1.0f), s);
-}
-// GELU(u) and GELU'(u) from one sigmoid: the MLP-in forward stores both (the
-// activation for the MLP-out GEMM, the derivative for the backward), so the
-// backward's GELU' epilogue is a product.
+// evaluated as g = u s with s = 0.5 (1 + tanh(y)) = 1 / (1 + exp(-2y)) (the
+// same function; it saturates to 0 or 1 without overflow trouble), and its
+// derivative 0.5 (1 + t) + 0.5 u (1 - t^2) c (1 + 3 a u^2), t = tanh(y), which
+// in terms of s is s + u s (1 - s) 2c (1 + 3 a u^2) = s + g (1 - s) (2c + 6ac
+// u^2). One exp2 of -2y log2(e) = u (k0 + k1 u^2) and the hardware reciprocal
+// (about 1 ulp, no IEEE division sequence) give s; with the constants folded
+// both results take 11 vector instructions. The MLP-in forward stores both
+// (the activation for the MLP-out GEMM, the derivative for the backward), so
+// the backward's GELU' epilogue is a product.
 __device__ __forceinline__ void gelu_and_grad(float u, float& g, float& d) {
-  const float s = gelu_sigmoid(u);
+  constexpr float c = 0.7978845608028654f, a = 0.044715f, l2e = 1.4426950408889634f;
+  constexpr float k0 = -2.0f * c * l2e, k1 = -2.0f * c * a * l2e;
+  const float u2 = u * u;
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u * __builtin_fmaf(k1, u2, k0)));
   g = u * s;
-  d = gelu_grad_s(u, s);
+  d = __builtin_fmaf(g * (1.0f - s), __builtin_fmaf(6.0f * a * c, u2, 2.0f * c), s);
 }
 
 // Wait until at most n vector-memory operations of this wavefront are
