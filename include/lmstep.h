@@ -41,7 +41,12 @@
  *   - train_step and forward_logits only enqueue work on the stream; they
  *     return before the GPU finishes. Host-checkable argument errors are
  *     returned before anything is enqueued. Inputs must stay valid until the
- *     stream's work completes.
+ *     stream's work completes. One exception: a 16-bit model whose blocks'
+ *     weight gradients run as one grouped launch (wide enough models, steps
+ *     of at least 2048 tokens) uploads that launch's table of GEMMs when a
+ *     step's token count B*T differs from the previous such step's, and
+ *     first synchronizes the stream (so such a step cannot be captured into
+ *     a HIP graph; steps at an unchanged token count can).
  *   - A model is not thread-safe; separate models are independent.
  */
 #ifndef LMSTEP_H

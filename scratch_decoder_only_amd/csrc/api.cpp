@@ -246,6 +246,9 @@ GemmOp dw_op(const void* dY, long M, long N, const void* X, long K, float* dW);
 // launch (below, each GEMM's K is short enough that the per-GEMM K-split
 // launches do as well)
 constexpr long kDwGroupMinRows = 2048;
+// backward_pass's return when the grouped launch's table could not be
+// uploaded (a HIP error, not a shape the kernels reject)
+constexpr int kTableUploadFailed = 2;
 
 // Units of a grouped launch of every block's four weight gradients at M
 // rows (-1: the grouped kernel does not take them).
@@ -839,7 +842,7 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
     if (tab != m->dw_tab_host) {
       if (hipStreamSynchronize(s) != hipSuccess ||
           hipMemcpy(m->dw_tab, tab.data(), tab.size(), hipMemcpyHostToDevice) != hipSuccess)
-        return -1;
+        return kTableUploadFailed;
       m->dw_tab_host = tab;
     }
     Lr.run("gemm_dw_group", flops, 0, [&] { rc |= gemm_group_launch(m->prec == 2, tn, m->dw_tab, units, s); });
@@ -1026,6 +1029,7 @@ lm_status train_step(lm_model* m, const int32_t* tok, const int32_t* tgt, const 
     using E = std::remove_pointer_t<decltype(tag)>;
     return forward_pass<E>(m, Lr, tok, doc, B, T) | backward_pass<E>(m, Lr, tok, tgt, B, T, stats);
   });
+  if (rc == kTableUploadFailed) return fail(LM_ERR_HIP, "train_step: uploading the weight-gradient table failed");
   if (rc) return fail(LM_ERR_HIP, "internal error: a kernel rejected a shape accepted when the model was created");
   Lr.run("grad_norm", 0, 4.0 * m->P, [&] {
     launch_sumsq_partials(m->grads, m->P, m->norm_part, s);
