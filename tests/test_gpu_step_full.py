@@ -9,8 +9,9 @@ GELU'-epilogue partial rows per column). The ~30M-parameter long-context
 workload (vocab 16384, d_model 512, 8 heads of 64, MLP 2048, seq 2048, packed
 documents) runs at its full batch of 16 with 4 of its 8 blocks: every
 kernel's shape depends on the row count and the widths, not on the depth
-(4 blocks already give the grouped weight-gradient launch, of 128 x 128
-tiles there, more units than twice the CUs, as 8 do), so the same
+(4 blocks already give the grouped weight-gradient launch, with partly
+empty 128 x 192 tiles at these widths, more units than twice the CUs, as 8
+do), so the same
 configurations run while the fp64 oracle stays within a few minutes.
 
 Bounds: the benchmark spec's bf16 ones (loss rel <= 2e-2, every gradient tensor
