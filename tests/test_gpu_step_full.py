@@ -138,6 +138,24 @@ def test_grouped_weight_gradients_follow_the_token_count(sd):
             assert np.array_equal(g_reused[k], g_fresh[k]), (B, k)
 
 
+@pytest.mark.parametrize("untied", [False, True])
+def test_grouped_weight_gradients_at_two_blocks_match_oracle(sd, untied):
+    """The GPT-2-small widths at 2 blocks, 4 x 512 tokens and a 2048-entry
+    vocabulary: already enough weight-gradient tiles for the grouped launch
+    (576 units), checked against the oracle tensor by tensor, with the tied
+    head and with a separate head and bias."""
+    shape = synth.C4.replace(n_layers=2, vocab=2048, untied_head=untied).with_batch(4, 512)
+    print(f"grouped weight gradients parity untied={untied}", flush=True)
+    tok, tgt, doc = _inputs(shape, 4)
+    params = synth.init_params(shape)
+    if untied:
+        params["head.b"] = synth.random_tensor(np.random.default_rng(3), params["head.b"].shape, 0.5)
+    got = run_gpu(sd, shape, tok, tgt, doc, params)
+    ref = run_oracle(shape, tok, tgt, doc, params)
+    compare(shape, got, ref, params)
+    assert min(cos(got["grads"][k], ref["grads"][k]) for k in ref["grads"] if not k.endswith("b_qkv")) >= 0.999
+
+
 def test_binding_rejects_wrong_token_tensors_before_any_launch(sd):
     t = torch()
     shape = synth.C1.with_batch(2, 16)
