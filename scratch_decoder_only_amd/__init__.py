@@ -199,6 +199,9 @@ class Model:
         if nbytes == 0:
             _check(LM_ERR_SHAPE, "lm_workspace_bytes")
         self.arena = torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+        # held by the instance: at interpreter exit the module's globals may
+        # already be gone when __del__ runs
+        self._destroy = _lib.model_destroy
         self._h = c_void_p()
         _check(_lib.model_create(ctypes.byref(self.cfg), _ptr(self.arena), nbytes, _stream(), ctypes.byref(self._h)),
                "model_create")
@@ -212,10 +215,10 @@ class Model:
         self.stats = torch.zeros(4, dtype=torch.float32, device=device)
 
     def __del__(self):
-        h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            _lib.model_destroy(h)
-            self._h = c_void_p()
+        h, destroy = getattr(self, "_h", None), getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
+            self._h = None
 
     # ---- flat buffers <-> named tensors
     def flatten(self, named: Dict[str, np.ndarray]) -> np.ndarray:
