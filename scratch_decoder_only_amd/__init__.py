@@ -24,6 +24,12 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build the HIP library first "
         "(python -c 'import __graft_entry__ as g; g.build()' or python scratch_decoder_only_amd/build.py)")
 
+# torch first: its HIP runtime and the system's share the soname
+# libamdhip64.so.7, so whichever loads first serves both. Loaded first, the
+# system runtime leaves torch without devices; loaded after torch, the library
+# runs on torch's runtime, as its streams and allocations require.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 c_int, c_int64, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t

@@ -200,3 +200,18 @@ def test_binding_rejects_tensors_of_the_wrong_kind():
             sd._need(x.to(torch.int32).t(), "tokens", torch.int32)
         with pytest.raises(sd.LmError, match="at least 30"):
             sd._need(x.to(torch.int32), "out", torch.int32, min_numel=30)
+
+
+def test_binding_imported_before_torch_uses_torchs_hip_runtime():
+    """torch's HIP runtime and the system's share one soname: whichever loads
+    first serves the process. Importing the binding first must still leave
+    torch's runtime in place (the system one left torch without devices)."""
+    import subprocess
+    import sys
+    pytest.importorskip("torch")
+    code = ("import scratch_decoder_only_amd, torch, os\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "tdir = os.path.dirname(torch.__file__)\n"
+            "assert maps and all(m.startswith(tdir) for m in maps), maps\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
