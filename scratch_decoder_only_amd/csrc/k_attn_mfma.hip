@@ -205,6 +205,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   const int qs = qv ? start[q] : 0;
   const bool wave_last_ok = qw0 + 31 < T;           // every query of the wave exists
   const int qs_last = __shfl(qs, 31, 64);           // start of the wave's last query
+  // the smallest start of the wave's queries (starts never decrease along a
+  // row); a wave with no query at all keeps every key masked
+  const int qs_first = qw0 < T ? __builtin_amdgcn_readfirstlane(qs) : T;
   bf16x8_t qf[KS];
   frags_global<D>(qf, base, ld, q, T, h * D, lane);
 
@@ -231,13 +234,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
       lk.load(k0 + 64);
       lv.load(k0 + 64);
     }
+    // 32-key halves of the tile that the mask removes for every query of the
+    // wave (all keys after its last query, or before its first query's
+    // start) add exact zeros: their matrix and softmax work is skipped
+    // (wave-uniform tests)
+    const bool live0 = k0 <= qw0 + 31 && k0 + 31 >= qs_first;
+    const bool live1 = k0 + 32 <= qw0 + 31 && k0 + 63 >= qs_first;
+    if (live0 || live1) {
     f32x16_t s[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       zero(s[sub]);
+      if (sub == 0 ? live0 : live1) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s[sub] = mfma32<E>(frag_r<D>(sK[cur], sub * 32, ks, lane), qf[ks], s[sub]);
+        for (int ks = 0; ks < KS; ++ks)
+          s[sub] = mfma32<E>(frag_r<D>(sK[cur], sub * 32, ks, lane), qf[ks], s[sub]);
+      }
     }
     // A tile every score of which is kept (all 64 keys at or before the
     // wave's first query and at or after its last query's start) needs no
@@ -298,10 +310,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      if (!((st >> 1) == 0 ? live0 : live1)) continue;
       const bf16x8_t pf = as_frag(pack_frag<E>(&p[st >> 1][(st & 1) * 8]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         acc_o[dt] = mfma32<E>(frag_t<D>(sV[cur], dt, st * 16, lane), pf, acc_o[dt]);
+    }
     }
     if (kt < kt1) {
       lk.store(sK[cur ^ 1]);
@@ -341,6 +355,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   const int qs = qv ? start[q] : 0;
   const bool wave_last_ok = qw0 + 31 < T;
   const int qs_last = __shfl(qs, 31, 64);
+  const int qs_first = qw0 < T ? __builtin_amdgcn_readfirstlane(qs) : T;
   const float lse2 = qv ? a.lse[((long)b * H + h) * T + q] * kLog2e : 0.f;
   bf16x8_t qf[KS], df[KS];
   frags_global<D>(qf, base, ld, q, T, h * D, lane);
@@ -388,6 +403,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      const int kb = k0 + sub * 32;
+      // a 32-key block the mask removes for every query of the wave (after
+      // its last query, or before its first query's start) adds exact zeros
+      if (kb > qw0 + 31 || kb + 31 < qs_first) continue;
       f32x16_t s, dp;
       zero(s);
       zero(dp);
@@ -397,7 +416,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
         dp = mfma32<E>(frag_r<D>(sV[cur], sub * 32, ks, lane), df[ks], dp);
       }
       float ds[16];
-      const int kb = k0 + sub * 32;
       if (wave_last_ok && kb + 31 <= qw0 && qs_last <= kb) {
         // every score of this 32 x 32 block is kept
 #pragma unroll
@@ -500,6 +518,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      // a 32-query block the mask removes for every key of the wave (all its
+      // queries before the wave's first key, or all their starts after its
+      // last key; the block's first query has the smallest start, and rows
+      // past T have start T) adds exact zeros
+      if (qb + sub * 32 + 31 < kw0 || __builtin_amdgcn_readfirstlane(sS[cur][sub * 32]) > kw0 + 31) continue;
       // rows of element e: sub*32 + acc_row(e), four consecutive rows per
       // group of four elements, read as one vector. dP starts from -delta of
       // its row (read straight into the accumulators), so the MFMAs leave
