@@ -190,7 +190,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][RowTile<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][RowTile<D>::ELEMS];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, H = a.H, C = H * D;
   int bh, q0;
   item_rows(a, true, bh, q0);
@@ -339,7 +339,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][RowTile<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][RowTile<D>::ELEMS];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, H = a.H, C = H * D;
   int bh, q0;
   item_rows(a, true, bh, q0);
@@ -460,7 +460,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) float sL[2][64];
   __shared__ __attribute__((aligned(16))) float sD[2][64];
   __shared__ __attribute__((aligned(16))) int sS[2][64];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, H = a.H, C = H * D;
   int bh, kb0;
   item_rows(a, false, bh, kb0);
