@@ -658,7 +658,8 @@ int decode_pass(lm_model* m, Launcher& Lr, const int32_t* tok, int B, int pos, E
 }
 
 template <typename E>
-int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* tgt, int B, int T, float* stats) {
+int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* tgt, int B, int T, float* stats,
+                  bool packed) {
   hipStream_t s = Lr.s;
   const long M = (long)B * T, C = m->C, F = m->F, H = m->H, V = m->V;
   const double Mf = (double)M, A = (double)sizeof(E);
@@ -866,8 +867,14 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   Lr.run("embed_bwd", 0, Mf * C * 8, [&] {
     launch_csr(tok, (int)M, m->V, m->emb_tok, s);
     launch_segment_sum(m->g, tok, (int)M, (int)C, m->V, m->emb_tok, m->grads + m->o_wte, !m->untied, s);
-    launch_csr(m->pos, (int)M, m->S, m->emb_pos, s);
-    launch_segment_sum(m->g, m->pos, (int)M, (int)C, m->S, m->emb_pos, m->grads + m->o_wpe, false, s);
+    // without packed documents row b T + t has position t: a column sum over
+    // the batch, with no sort
+    if (packed) {
+      launch_csr(m->pos, (int)M, m->S, m->emb_pos, s);
+      launch_segment_sum(m->g, m->pos, (int)M, (int)C, m->S, m->emb_pos, m->grads + m->o_wpe, false, s);
+    } else {
+      launch_pos_colsum(m->g, B, T, (int)C, m->S, m->grads + m->o_wpe, s);
+    }
   });
   return rc;
 }
@@ -1027,7 +1034,7 @@ lm_status train_step(lm_model* m, const int32_t* tok, const int32_t* tgt, const 
   Lr.run("misc", 0, 0, [&] { launch_fill_u32(m->flags, 0u, 4, s); });
   rc |= with_act(m, [&](auto tag) {
     using E = std::remove_pointer_t<decltype(tag)>;
-    return forward_pass<E>(m, Lr, tok, doc, B, T) | backward_pass<E>(m, Lr, tok, tgt, B, T, stats);
+    return forward_pass<E>(m, Lr, tok, doc, B, T) | backward_pass<E>(m, Lr, tok, tgt, B, T, stats, doc != nullptr);
   });
   if (rc == kTableUploadFailed) return fail(LM_ERR_HIP, "train_step: uploading the weight-gradient table failed");
   if (rc) return fail(LM_ERR_HIP, "internal error: a kernel rejected a shape accepted when the model was created");

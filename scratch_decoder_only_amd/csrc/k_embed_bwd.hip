@@ -21,9 +21,28 @@ long embed_bwd_max_chunks(int M, int nkeys) {
 
 __device__ __forceinline__ int clamp_key(int k, int nkeys) { return k < 0 ? 0 : (k >= nkeys ? nkeys - 1 : k); }
 
-__global__ void csr_count_kernel(const int32_t* __restrict__ keys, int M, int nkeys, int32_t* __restrict__ counts) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < M) atomicAdd(&counts[clamp_key(keys[i], nkeys)], 1);
+// counts[v] = #rows with key v. Each block of 256 rows first counts its equal
+// keys in LDS and only the first row of each key adds the block's count: a
+// Zipf-hot key (token id 0 holds ~14% of the rows) then takes one atomic
+// addition per block instead of one per row, which serialised on its
+// counter. Integer sums: the result does not depend on their order.
+__global__ void __launch_bounds__(256) csr_count_kernel(const int32_t* __restrict__ keys, int M, int nkeys,
+                                                        int32_t* __restrict__ counts) {
+  __shared__ int s_k[256];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int my = i < M ? clamp_key(keys[i], nkeys) : -1;
+  s_k[threadIdx.x] = my;
+  __syncthreads();
+  if (my < 0) return;
+  int cnt = 0;
+  bool first = true;
+#pragma unroll 8
+  for (int q = 0; q < 256; ++q) {
+    const bool eq = s_k[q] == my;
+    cnt += eq;
+    first = first && !(eq && q < (int)threadIdx.x);
+  }
+  if (first) atomicAdd(&counts[my], cnt);
 }
 
 // Exclusive scans of counts (-> offsets) and of ceil(count / kSegRows)
@@ -239,6 +258,40 @@ __global__ void __launch_bounds__(256) segsum_keys_kernel(int C, int nkeys, cons
       dst[(long)v * C + c] += acc;
     }
   }
+}
+
+// Position gradient of rows without packed documents: the position of row
+// b T + t is t, so dst[t] = sum over b of dx[b T + t] (t < T; rows T..S-1 of
+// dst are zero). The sum is taken as the sorted path takes it, so the result
+// is bit-identical to it: the B rows of a position in ascending order in
+// chunks of kSegRows rows, each chunk summed from zero, the chunk sums added
+// from zero in order, and the total added onto the zeroed destination.
+__global__ void __launch_bounds__(256) pos_colsum_kernel(const float* __restrict__ dx, int B, int T, int C, int S,
+                                                         float* __restrict__ dst) {
+  const int nq = C >> 2;
+  const long q = (long)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (long)S * nq) return;
+  const int t = (int)(q / nq), c = (int)(q - (long)t * nq) * 4;
+  f32x4_t out = {0.f, 0.f, 0.f, 0.f};
+  if (t < T) {
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t tot = zero;
+    for (int b0 = 0; b0 < B; b0 += kSegRows) {
+      const int b1 = min(B, b0 + kSegRows);
+      f32x4_t acc = zero;
+      for (int b = b0; b < b1; ++b) acc += *reinterpret_cast<const f32x4_t*>(dx + ((long)b * T + t) * C + c);
+      if (B <= kSegRows) tot = acc;  // one chunk: added onto the zeroed row as it is
+      else tot += acc;
+    }
+    out = zero + tot;
+  }
+  *reinterpret_cast<f32x4_t*>(dst + (long)t * C + c) = out;
+}
+
+void launch_pos_colsum(const float* dx, int B, int T, int C, int S, float* dst, hipStream_t s) {
+  const long n = (long)S * (C >> 2);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(pos_colsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dx, B, T, C, S, dst);
 }
 
 void launch_csr(const int32_t* keys, int M, int nkeys, EmbedBwdWs ws, hipStream_t s) {

@@ -182,6 +182,10 @@ void launch_csr(const int32_t* keys, int M, int nkeys, EmbedBwdWs ws, hipStream_
 void launch_segment_sum(const float* dx, const int32_t* keys, int M, int C, int nkeys, EmbedBwdWs ws, float* dst,
                         bool accumulate, hipStream_t s);
 long embed_bwd_max_chunks(int M, int nkeys);
+// dst[t] = sum over b of dx rows b T + t (t < T), zero for T <= t < S: the
+// position gradient of rows without packed documents, summed in the order of
+// launch_segment_sum (bit-identical to it); C a multiple of 4.
+void launch_pos_colsum(const float* dx, int B, int T, int C, int S, float* dst, hipStream_t s);
 
 // --------------------------------------------------------------- optimiser
 constexpr int kNormBlocks = 1024;
