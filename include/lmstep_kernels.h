@@ -143,10 +143,14 @@ int lmk_xent_noalloc(int precision, void* z, int64_t ldz, int M, int V, const in
 
 /* Stable counting sort of keys [M] in [0, nkeys): counts/offsets/chunk_base
  * [nkeys+1], 16-byte aligned, perm [M] (rows of key v at
- * perm[offsets[v] .. offsets[v+1]), ascending); rank [M] int32 scratch (each
- * row's count of equal keys before it). -1 on a bad size or alignment. */
+ * perm[offsets[v] .. offsets[v+1]), ascending); rank: int32 scratch of
+ * lmk_csr_ws_ints(M, nkeys) entries (each row's count of equal keys before
+ * it: M entries when it is counted pairwise, a [blocks of 256 rows][nkeys]
+ * table of per-block counts from 128 blocks on). -1 on a bad size or
+ * alignment. */
 int lmk_csr(const int32_t* keys, int M, int nkeys, int32_t* counts, int32_t* offsets, int32_t* chunk_base,
             int32_t* perm, int32_t* rank, void* stream);
+int64_t lmk_csr_ws_ints(int M, int nkeys);
 /* dst[v,:] (+)= sum of dx rows with key v, in perm order (after lmk_csr).
  * partial: fp32 scratch of lmk_segment_sum_ws_floats(M, nkeys, C). */
 int lmk_segment_sum(const float* dx, int M, int C, int nkeys, int32_t* counts, int32_t* offsets,

@@ -123,6 +123,7 @@ _sig("lmk_xent_noalloc", c_int, [c_int, _P, c_int64, c_int, c_int, _P, _P, _P, _
 _sig("lmk_csr", c_int, [_P, c_int, c_int, _P, _P, _P, _P, _P, _P])
 _sig("lmk_segment_sum", c_int, [_P, c_int, c_int, c_int, _P, _P, _P, _P, _P, _P, c_int, _P])
 _sig("lmk_segment_sum_ws_floats", c_int64, [c_int, c_int, c_int])
+_sig("lmk_csr_ws_ints", c_int64, [c_int, c_int])
 _sig("lmk_grad_norm", c_int, [_P, c_int64, c_float, _P, _P, _P, _P, c_float, c_float, c_int, _P])
 _sig("lmk_adamw", c_int, [_P, _P, _P, _P, c_int64, c_float, c_float, c_float, c_float, c_float, c_int, _P, _P, _P, c_int,
                           _P])
@@ -604,6 +605,10 @@ def xent_noalloc(precision, z, ldz, M, V, tgt, loss, flags, loss_scale=None):
 def csr(keys, M, nkeys, counts, offsets, chunk_base, perm, rank):
     _kcheck(_lib.lmk_csr(_ptr(keys), M, nkeys, _ptr(counts), _ptr(offsets), _ptr(chunk_base), _ptr(perm),
                          _ptr(rank), _stream()), "lmk_csr")
+
+
+def csr_ws_ints(M, nkeys):
+    return _lib.lmk_csr_ws_ints(M, nkeys)
 
 
 def segment_sum_ws_floats(M, nkeys, C):

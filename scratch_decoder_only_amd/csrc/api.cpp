@@ -330,7 +330,8 @@ void carve(lm_model* m, char* base) {
     e.offsets = c.take<int32_t>(nkeys + 1);
     e.chunk_base = c.take<int32_t>(nkeys + 1);
     e.perm = c.take<int32_t>(M);
-    e.rank = c.take<int32_t>(M);
+    e.rank_cap = csr_rank_ints((int)M, (int)nkeys);
+    e.rank = c.take<int32_t>(e.rank_cap);
     e.partial = c.take<float>(embed_bwd_max_chunks((int)M, (int)nkeys) * C);
   }
   m->start = c.take<int32_t>(M);

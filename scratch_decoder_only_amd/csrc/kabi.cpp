@@ -216,10 +216,12 @@ int lmk_csr(const int32_t* keys, int M, int nkeys, int32_t* counts, int32_t* off
   if (M < 0 || nkeys <= 0 || (M > 0 && !rank)) return -1;
   auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
   if (!a16(counts) || !a16(offsets) || !a16(chunk_base)) return -1;
-  EmbedBwdWs w{counts, offsets, chunk_base, perm, nullptr, rank};
+  EmbedBwdWs w{counts, offsets, chunk_base, perm, nullptr, rank, csr_rank_ints(M, nkeys)};
   launch_csr(keys, M, nkeys, w, S(stream));
   return 0;
 }
+
+int64_t lmk_csr_ws_ints(int M, int nkeys) { return M < 0 || nkeys <= 0 ? -1 : csr_rank_ints(M, nkeys); }
 
 int64_t lmk_segment_sum_ws_floats(int M, int nkeys, int C) { return embed_bwd_max_chunks(M, nkeys) * C; }
 

@@ -173,8 +173,12 @@ struct EmbedBwdWs {
   int32_t* chunk_base; // [nkeys + 1]
   int32_t* perm;       // [M]
   float* partial;      // [max_chunks, C]
-  int32_t* rank;       // [M] scratch of the sort
+  int32_t* rank;       // scratch of the sort: at least M ints, rank_cap in all
+  long rank_cap = 0;   // ints at rank (0: M)
 };
+// Ints of sort scratch with which launch_csr takes its linear-time rank for
+// up to M rows (M when it keeps the pairwise one).
+long csr_rank_ints(int M, int nkeys);
 void launch_csr(const int32_t* keys, int M, int nkeys, EmbedBwdWs ws, hipStream_t s);
 // dst[key] (+)= sum of dx rows of that key. accumulate: add onto dst (rows of
 // keys with no occurrence are left untouched) else overwrite (zero rows for

@@ -504,10 +504,12 @@ def test_cross_entropy(sd, prec, V):
 # ------------------------------------------------ embedding backward (CSR)
 
 @pytest.mark.parametrize("nkeys,M", [(1000, 5000), (64, 3000), (50257, 8192), (4095, 3000), (4096, 3000),
-                                     (70000, 20000)])
+                                     (70000, 20000), (50257, 33000), (16384, 32768), (2048, 32768)])
 def test_csr_bit_exact_and_segment_sums(sd, nkeys, M):
     """Key counts scanned in one round of 4096 (up to 4095 keys: nkeys + 1
-    entries), in one batch of rounds, and over several batches (70000)."""
+    entries), in one batch of rounds, and over several batches (70000); ranks
+    counted pairwise (fewer than 128 blocks of 256 rows) and from per-block
+    key counts (128 blocks and more, a ragged last block at 33000 rows)."""
     t = torch()
     import synth
     rng = np.random.Generator(np.random.PCG64(nkeys))
@@ -515,7 +517,8 @@ def test_csr_bit_exact_and_segment_sums(sd, nkeys, M):
     C = 128
     counts, offsets, chunk = (t.zeros(nkeys + 1, dtype=t.int32, device="cuda") for _ in range(3))
     perm = t.zeros(M, dtype=t.int32, device="cuda")
-    rank = t.full((M,), 7, dtype=t.int32, device="cuda")  # stale scratch must not matter
+    assert sd.csr_ws_ints(M, nkeys) == (M if M <= 127 * 256 else ((M + 255) // 256) * nkeys)
+    rank = t.full((sd.csr_ws_ints(M, nkeys),), 7, dtype=t.int32, device="cuda")  # stale scratch must not matter
     sd.csr(dev(keys), M, nkeys, counts, offsets, chunk, perm, rank)
     eoff, eperm = oracle.csr_by_key(keys, nkeys)
     t.cuda.synchronize()
