@@ -265,6 +265,26 @@ long dw_group_units(lm_model* m, long M) {
   return units < 0 ? -1 : (long)units * m->L;
 }
 
+// The vocabulary projection's weight gradient joins the blocks' grouped
+// launch (as 128 x 192 units over the same K, appended after theirs) when
+// that saves a whole round of the CUs: its units then fill the round the
+// blocks' units leave partly empty, and its own launch (256 x 256 tiles, K
+// split into slices) and split-K reduction go away. Measured on the
+// GPT-2-small-shaped step (3456 + 1572 units: 20 rounds instead of 14 + 7).
+// At the 32768-row workload the two would take as many rounds as apart
+// (1536 + 384 units), so its head keeps the separate launch.
+bool head_dw_grouped(lm_model* m, long M, const GemmOp& head) {
+  const long blocks = dw_group_units(m, M);
+  if (blocks < 0) return false;
+  std::vector<char> tab(gemm_group_table_bytes(1));
+  int tn = 0;
+  const long units = gemm_group_plan(&head, 1, tab.data(), &tn);
+  if (units < 0) return false;
+  const long cus = gemm_cus();
+  auto rounds = [&](long u) { return (u + cus - 1) / cus; };
+  return rounds(blocks + units) < rounds(blocks) + rounds(units);
+}
+
 // Lays out every slice of the arena (base == nullptr: size only).
 void carve(lm_model* m, char* base) {
   Carver c{base};
@@ -302,7 +322,7 @@ void carve(lm_model* m, char* base) {
     m->g_act_l = c.take<char>(L * 2 * M * C * A);
     m->du_l = c.take<char>(L * M * F * A);
     m->dqkv_l = c.take<char>(L * M * 3 * C * A);
-    m->dw_tab = c.take<char>(gemm_group_table_bytes(4 * (int)L));
+    m->dw_tab = c.take<char>(gemm_group_table_bytes(4 * (int)L + 1));  // + the vocabulary projection's
   }
   long ln_blocks = (M + kLnRowsPerBlock - 1) / kLnRowsPerBlock;
   // partial sums of every LayerNorm of the backward (2 per block + the
@@ -676,12 +696,16 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   // head: dW = dz^T h_f (tied: the first writer of the wte gradient); dh_f =
   // dz W; untied: the bias gradient is the column sums of dz (its zero
   // padding columns give the zero padding of the bias gradient)
-  {
-    GemmOp op = dw_op(z, M, m->h16 ? m->Vp : V, hf, C, m->grads + m->head_w());
-    op.lda = m->ldz;
-    op.M_out = (int)V;
-    Lr.run("gemm_head_bwd_dw", 2.0 * M * V * C, 0, [&] { rc |= gemm(m, op, s); });
-  }
+  // the weight gradients of the blocks: one grouped launch after the loop
+  // (reading per-layer copies of the output gradients), or each right away;
+  // the head's joins that launch where it saves a round (z and h_f stay
+  // untouched until then)
+  const bool grouped = m->dw_group && M >= kDwGroupMinRows;
+  GemmOp head_dw = dw_op(z, M, m->h16 ? m->Vp : V, hf, C, m->grads + m->head_w());
+  head_dw.lda = m->ldz;
+  head_dw.M_out = (int)V;
+  const bool head_in_group = grouped && head_dw_grouped(m, M, head_dw);
+  if (!head_in_group) Lr.run("gemm_head_bwd_dw", 2.0 * M * V * C, 0, [&] { rc |= gemm(m, head_dw, s); });
   if (m->untied)
     Lr.run("bias_grad", 0, Mf * m->ldz * A, [&] {
       launch_colsum<E>(z, m->ldz, (int)M, (int)m->ldz, m->col_part, m->grads + m->o_head_b, s);
@@ -727,9 +751,6 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
   std::vector<float*> fc_pa(m->L), fc_oa(m->L), qkv_pa(m->L), qkv_oa(m->L);
   struct { std::vector<float*>& pa; std::vector<float*>& oa; } fcb{fc_pa, fc_oa}, qkvb{qkv_pa, qkv_oa};
   double ln_red_bytes = 0;
-  // the weight gradients of the blocks: one grouped launch after the loop
-  // (reading per-layer copies of the output gradients), or each right away
-  const bool grouped = m->dw_group && M >= kDwGroupMinRows;
   std::vector<GemmOp> dw_ops;
   auto weight_grad = [&](const char* name, GemmOp op) {
     if (grouped) dw_ops.push_back(op);
@@ -832,6 +853,7 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
            g_act_of(l - 1, 0));
   }
   if (grouped) {
+    if (head_in_group) dw_ops.push_back(head_dw);
     // the table depends on the token count (the K of these GEMMs): uploaded
     // when it differs from the last upload, after the stream has drained (the
     // previous launch may still read the device copy)
@@ -839,7 +861,7 @@ int backward_pass(lm_model* m, Launcher& Lr, const int32_t* tok, const int32_t* 
     int tn = 0;
     const int units = gemm_group_plan(dw_ops.data(), (int)dw_ops.size(), tab.data(), &tn);
     double flops = 0;
-    for (const GemmOp& op : dw_ops) flops += 2.0 * op.M * op.N * op.K;
+    for (const GemmOp& op : dw_ops) flops += 2.0 * (op.M_out > 0 ? op.M_out : op.M) * op.N * op.K;
     if (units < 0) return -1;
     if (tab != m->dw_tab_host) {
       if (hipStreamSynchronize(s) != hipSuccess ||
