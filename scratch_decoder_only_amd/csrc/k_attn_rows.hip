@@ -15,6 +15,8 @@
 
 namespace lm {
 
+constexpr int kRowKeys = 4;  // keys (dK/dV: queries) whose loads go out together
+
 template <typename E>
 __global__ void __launch_bounds__(256) attn_fwd_rows_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
@@ -30,17 +32,32 @@ __global__ void __launch_bounds__(256) attn_fwd_rows_kernel(AttnArgs a) {
   const float scale = 1.0f / sqrtf((float)D);
   const int j0 = a.start[(long)b * T + i];
   float m = -INFINITY, l = 0.f, o = 0.f;
-  for (int j = j0; j <= i; ++j) {
-    float kv = act ? Act<E>::ld(qkv, base + (long)j * ld + C + h * D + lane) : 0.f;
+  auto key = [&](float kv, float vv) {
     float s = wave_sum(q * kv) * scale;
     float mn = fmaxf(m, s);
     float corr = __expf(m - mn);
     float p = __expf(s - mn);
-    float vv = act ? Act<E>::ld(qkv, base + (long)j * ld + 2 * C + h * D + lane) : 0.f;
     l = l * corr + p;
     o = o * corr + p * vv;
     m = mn;
+  };
+  auto kld = [&](int j) { return act ? Act<E>::ld(qkv, base + (long)j * ld + C + h * D + lane) : 0.f; };
+  auto vld = [&](int j) { return act ? Act<E>::ld(qkv, base + (long)j * ld + 2 * C + h * D + lane) : 0.f; };
+  // keys four at a time with their loads issued together (the row is a chain
+  // of dependent updates; loading each key just before its update left a
+  // memory latency per key), then the rest one by one, in key order
+  int j = j0;
+  for (; j + 3 <= i; j += kRowKeys) {
+    float kv[kRowKeys], vv[kRowKeys];
+#pragma unroll
+    for (int u = 0; u < kRowKeys; ++u) {
+      kv[u] = kld(j + u);
+      vv[u] = vld(j + u);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowKeys; ++u) key(kv[u], vv[u]);
   }
+  for (; j <= i; ++j) key(kld(j), vld(j));
   if (act) Act<E>::st(reinterpret_cast<E*>(a.o), ((long)b * T + i) * C + h * D + lane, o / l);
   if (lane == 0) a.lse[((long)b * H + h) * T + i] = m + __logf(l);
 }
@@ -78,14 +95,26 @@ __global__ void __launch_bounds__(256) attn_dq_rows_kernel(AttnArgs a) {
   const float lse = a.lse[((long)b * H + h) * T + i];
   const float dl = a.delta[((long)b * H + h) * T + i];
   float dq = 0.f;
-  for (int j = a.start[(long)b * T + i]; j <= i; ++j) {
-    float kv = act ? Act<E>::ld(qkv, base + (long)j * ld + C + h * D + lane) : 0.f;
-    float vv = act ? Act<E>::ld(qkv, base + (long)j * ld + 2 * C + h * D + lane) : 0.f;
+  auto key = [&](float kv, float vv) {
     float s = wave_sum(q * kv) * scale;
     float dp = wave_sum(g * vv);
     float p = __expf(s - lse);
     dq += p * (dp - dl) * kv;
+  };
+  auto kld = [&](int j) { return act ? Act<E>::ld(qkv, base + (long)j * ld + C + h * D + lane) : 0.f; };
+  auto vld = [&](int j) { return act ? Act<E>::ld(qkv, base + (long)j * ld + 2 * C + h * D + lane) : 0.f; };
+  int j = a.start[(long)b * T + i];
+  for (; j + 3 <= i; j += kRowKeys) {
+    float kv[kRowKeys], vv[kRowKeys];
+#pragma unroll
+    for (int u = 0; u < kRowKeys; ++u) {
+      kv[u] = kld(j + u);
+      vv[u] = vld(j + u);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowKeys; ++u) key(kv[u], vv[u]);
   }
+  for (; j <= i; ++j) key(kld(j), vld(j));
   if (act) Act<E>::st(reinterpret_cast<E*>(a.dqkv), ((long)b * T + i) * ld + h * D + lane, dq * scale);
 }
 
@@ -105,16 +134,32 @@ __global__ void __launch_bounds__(256) attn_dkv_rows_kernel(AttnArgs a) {
   const float vv = act ? Act<E>::ld(qkv, base + (long)j * ld + 2 * C + h * D + lane) : 0.f;
   float dk = 0.f, dv = 0.f;
   const int iend = a.end[(long)b * T + j];
-  for (int i = j; i < iend; ++i) {
-    float q = act ? Act<E>::ld(qkv, base + (long)i * ld + h * D + lane) : 0.f;
-    float g = act ? Act<E>::ld(dout, ((long)b * T + i) * C + h * D + lane) : 0.f;
+  const float* lse = a.lse + ((long)b * H + h) * T;
+  const float* dlt = a.delta + ((long)b * H + h) * T;
+  auto query = [&](float q, float g, float ls, float de) {
     float s = wave_sum(q * kv) * scale;
     float dp = wave_sum(g * vv);
-    float p = __expf(s - a.lse[((long)b * H + h) * T + i]);
-    float ds = p * (dp - a.delta[((long)b * H + h) * T + i]);
+    float p = __expf(s - ls);
+    float ds = p * (dp - de);
     dv += p * g;
     dk += ds * q;
+  };
+  auto qld = [&](int i) { return act ? Act<E>::ld(qkv, base + (long)i * ld + h * D + lane) : 0.f; };
+  auto gld = [&](int i) { return act ? Act<E>::ld(dout, ((long)b * T + i) * C + h * D + lane) : 0.f; };
+  int i = j;
+  for (; i + 3 < iend; i += kRowKeys) {
+    float q[kRowKeys], g[kRowKeys], ls[kRowKeys], de[kRowKeys];
+#pragma unroll
+    for (int u = 0; u < kRowKeys; ++u) {
+      q[u] = qld(i + u);
+      g[u] = gld(i + u);
+      ls[u] = lse[i + u];
+      de[u] = dlt[i + u];
+    }
+#pragma unroll
+    for (int u = 0; u < kRowKeys; ++u) query(q[u], g[u], ls[u], de[u]);
   }
+  for (; i < iend; ++i) query(qld(i), gld(i), lse[i], dlt[i]);
   if (act) {
     E* d = reinterpret_cast<E*>(a.dqkv);
     Act<E>::st(d, ((long)b * T + j) * ld + C + h * D + lane, dk * scale);
