@@ -1866,11 +1866,16 @@ static void launch_reduce32(const GemmOp& op, const GemmArgs& a, const float* pa
 }
 
 // fp32 path: 64 x 64 tiles; split K while the tiles leave CUs idle
+// K slices of the fp32 kernel: its tiles are serial K loops on one CU each,
+// and the small fp32 shapes have few of them (10-12 tiles of 64 x 64 for the
+// 128-wide model at 320 tokens), so K is split until the slices fill the CUs
+// or a slice would hold fewer than 64 K-values; the partials are summed in
+// slice order by the reduction pass.
 static int gemm32_splits(const GemmOp& op) {
   if (op.force_split > 0) return op.force_split;
   const long tiles = (long)((op.M + 63) / 64) * ((op.N + 63) / 64);
   int splits = 1;
-  while (tiles * splits < 256 && op.K / (splits * 2) >= 256) splits *= 2;
+  while (tiles * splits < 256 && op.K / (splits * 2) >= 64) splits *= 2;
   return splits;
 }
 
