@@ -304,6 +304,24 @@ def test_causality_bit_exact(sd, name):
         assert not np.array_equal(z0[:, cut + 1:], z1[:, cut + 1:])
 
 
+@pytest.mark.parametrize("batch", [8, 70])
+def test_unpacked_position_gradient_equals_sorted_path_bit_exact(sd, batch):
+    """Without document ids the position gradient is a column sum over the
+    batch; with one document per row it goes through the counting sort. Both
+    take the same summation order (chunks of 64 rows, chunk sums in order:
+    batch 70 gives two chunks per position), so the whole step is
+    bit-identical, the rows of positions past T included."""
+    shape = synth.C2.with_batch(batch, 32).replace(n_layers=1)
+    tok, tgt, _ = _inputs(shape, batch)
+    params = synth.init_params(shape)
+    a = run_gpu(sd, shape, tok, tgt, None, params)
+    b = run_gpu(sd, shape, tok, tgt, np.zeros(tok.shape, np.int32), params)
+    assert np.array_equal(a["stats"], b["stats"])
+    for k in a["grads"]:
+        assert np.array_equal(a["grads"][k], b["grads"][k]), k
+    assert not a["grads"]["wpe"][shape.seq:].any()
+
+
 def test_single_document_equals_causal_bit_exact(sd):
     shape = synth.C2.with_batch(2, 96)
     tok, _, _ = _inputs(shape, 2)
