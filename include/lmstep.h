@@ -43,7 +43,9 @@
  *     returned before anything is enqueued. Inputs must stay valid until the
  *     stream's work completes. One exception: a 16-bit model whose blocks'
  *     weight gradients run as one grouped launch (wide enough models, steps
- *     of at least 2048 tokens) uploads that launch's table of GEMMs when a
+ *     of at least 2048 tokens; the vocabulary projection's weight gradient
+ *     joins it where that takes fewer rounds of the compute units than two
+ *     launches) uploads that launch's table of GEMMs when a
  *     step's token count B*T differs from the previous such step's, and
  *     first synchronizes the stream (so such a step cannot be captured into
  *     a HIP graph; steps at an unchanged token count can).
