@@ -404,8 +404,8 @@ __global__ void __launch_bounds__(256) colsum_stage1_kernel(const T* __restrict_
 // 16-bit input with N and lda multiples of 8: 8 columns (one 16-byte load)
 // per thread, 512 per block; the same row order per column as above.
 template <typename T>
-__global__ void __launch_bounds__(256) colsum8_h16_kernel(const T* __restrict__ a, long lda, int M, int N,
-                                                          float* __restrict__ part) {
+__device__ __forceinline__ void colsum8_h16_block(const T* __restrict__ a, long lda, int M, int N,
+                                                  float* __restrict__ part) {
   __shared__ float s[4][8][64];
   const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int c = (blockIdx.x * 64 + lane) * 8;
@@ -443,6 +443,29 @@ __global__ void __launch_bounds__(256) colsum8_h16_kernel(const T* __restrict__ 
     *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
   }
 }
+
+template <typename T>
+__global__ void __launch_bounds__(256) colsum8_h16_kernel(const T* __restrict__ a, long lda, int M, int N,
+                                                          float* __restrict__ part) {
+  colsum8_h16_block<T>(a, lda, M, N, part);
+}
+
+// The same partial sums for several matrices of one shape in one launch
+// (blockIdx.z: the matrix), each exactly as one colsum8_h16_kernel launch
+// computes them.
+template <typename T>
+__global__ void __launch_bounds__(256) colsum8_h16_batch_kernel(Colsum16Batch b, long lda, int M, int N) {
+  colsum8_h16_block<T>(reinterpret_cast<const T*>(b.a[blockIdx.z]), lda, M, N, b.part[blockIdx.z]);
+}
+
+template <typename T>
+void launch_colsum_stage1_batch(const Colsum16Batch& b, int n, long lda, int M, int N, hipStream_t s) {
+  if (n <= 0) return;
+  const int P = (M + kColRows - 1) / kColRows;
+  hipLaunchKernelGGL(colsum8_h16_batch_kernel<T>, dim3((N / 8 + 63) / 64, P, n), dim3(256), 0, s, b, lda, M, N);
+}
+template void launch_colsum_stage1_batch<bf16>(const Colsum16Batch&, int, long, int, int, hipStream_t);
+template void launch_colsum_stage1_batch<f16>(const Colsum16Batch&, int, long, int, int, hipStream_t);
 
 template <typename T>
 void launch_colsum_stage1(const T* a, long lda, int M, int N, float* part, hipStream_t s) {

@@ -120,6 +120,15 @@ struct ColsumBatch {
   float* oc[kColsumBatch];
 };
 void launch_colsum_partials_batch(const ColsumBatch& bt, int n, int P, int C, hipStream_t s);
+// Per-row-block partial column sums (as launch_colsum_stage1) of n <=
+// kColsumBatch 16-bit matrices of one shape [M, N] (leading dimension lda;
+// N and lda multiples of 8) in one launch, matrix i into part[i].
+struct Colsum16Batch {
+  const void* a[kColsumBatch];
+  float* part[kColsumBatch];
+};
+template <typename T>
+void launch_colsum_stage1_batch(const Colsum16Batch& b, int n, long lda, int M, int N, hipStream_t s);
 template <typename T>
 void launch_colsum(const T* a, long lda, int M, int N, float* part, float* out, hipStream_t s);
 // Its first stage alone: the (M / kColRows rounded up) x N partial rows,
