@@ -159,22 +159,26 @@ __global__ void __launch_bounds__(256) xent_kernel(T* __restrict__ z, long ldz, 
 }
 
 // The same computation with the row held in registers between the passes:
-// 1024 threads, thread t owns the 16-byte vectors t, t + 1024, ... (NCH of
+// BT threads, thread t owns the 16-byte vectors t, t + BT, ... (NCH of
 // them), so the logits are read from memory once. Used when the row fits
-// (ldz <= 1024 * NCH * vector width). The vector work per logit is kept
+// (ldz <= BT * NCH * vector width), with the narrowest block of 64, 256 or
+// 1024 threads that holds it in at most 8 vectors a thread: a narrow row on
+// 1024 threads (the 8000-wide vocabulary: one vector each) left a block of
+// 16 wavefronts a short latency-bound pass, two blocks per CU. The vector work per logit is kept
 // small: only the chunks that reach past column V - 1 are masked (a test
 // uniform over the block), exponentials are exp2 of one fused multiply-add
 // (the 1/N scale folded into the exponent of the gradient pass), and the
 // one-hot term is subtracted by the one thread that holds the target.
-template <typename T, int NCH>
-__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) xent_reg_kernel(T* __restrict__ z, long ldz, int V,
+template <typename T, int NCH, int BT>
+__global__ void __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(8))) xent_reg_kernel(T* __restrict__ z, long ldz, int V,
                                                         const int32_t* __restrict__ tgt,
                                                         const int32_t* __restrict__ n_valid,
                                                         const float* __restrict__ loss_scale,
                                                         float* __restrict__ row_loss) {
   constexpr int NV = Vec16<T>::N;
   constexpr float kL2e = 1.4426950408889634f;
-  __shared__ float s_m[16], s_s[16];
+  constexpr int NW = BT / 64;  // wavefronts of the block
+  __shared__ float s_m[NW], s_s[NW];
   __shared__ float s_lse;
   const long row = blockIdx.x;
   T* zr = z + row * ldz;
@@ -190,7 +194,7 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
   if (valid) {
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-      const int v = threadIdx.x + q * 1024;
+      const int v = threadIdx.x + q * BT;
       uint4 u = v < nvec ? ld_nt16(zr + (long)v * NV) : make_uint4(0, 0, 0, 0);
       const int lim = V - v * NV;  // elements of this vector below column V
       uint32_t wd[4] = {u.x, u.y, u.z, u.w};
@@ -240,7 +244,7 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
   __syncthreads();
   if (threadIdx.x == 0) {
     float mm = s_m[0], ss = s_s[0];
-    for (int q = 1; q < 16; ++q) merge_ms(mm, ss, s_m[q], s_s[q]);
+    for (int q = 1; q < NW; ++q) merge_ms(mm, ss, s_m[q], s_s[q]);
     const float lse = mm + __logf(ss);
     s_lse = lse;
     row_loss[row] = valid ? lse - Act<T>::ld(zr, t) : 0.f;
@@ -256,10 +260,10 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) 
   const float c = -(lse * kL2e - __log2f(inv_n));
   // the thread, chunk and element that hold the target column
   const int vt = valid ? t / NV : -1;
-  const int t_thread = vt & 1023, t_chunk = vt >> 10, t_elem = valid ? t - vt * NV : 0;
+  const int t_thread = vt % BT, t_chunk = vt / BT, t_elem = valid ? t - vt * NV : 0;
 #pragma unroll
   for (int q = 0; q < NCH; ++q) {
-    const int v = threadIdx.x + q * 1024;
+    const int v = threadIdx.x + q * BT;
     if (v >= nvec) continue;
     float x[NV];
     if (valid) {
@@ -287,14 +291,19 @@ template <typename T>
 void launch_xent(T* z, long ldz, int M, int V, const int32_t* tgt, const int32_t* n_valid, float* row_loss,
                  const float* loss_scale, hipStream_t s) {
   const long nvec = ldz / Vec16<T>::N;
-  const long nch = (nvec + 1023) / 1024;
-#define XENT_REG(N)                                                                                        \
-  if (nch <= N) {                                                                                          \
-    hipLaunchKernelGGL((xent_reg_kernel<T, N>), dim3(M), dim3(1024), 0, s, z, ldz, V, tgt, n_valid, loss_scale, \
-                       row_loss);                                                                                \
-    return;                                                                                                \
+#define XENT_REG(N, BT)                                                                                       \
+  if ((nvec + BT - 1) / BT <= N) {                                                                            \
+    hipLaunchKernelGGL((xent_reg_kernel<T, N, BT>), dim3(M), dim3(BT), 0, s, z, ldz, V, tgt, n_valid, loss_scale, \
+                       row_loss);                                                                                   \
+    return;                                                                                                   \
   }
-  XENT_REG(1) XENT_REG(2) XENT_REG(4) XENT_REG(8)
+  if (nvec <= 64 * 8) {
+    XENT_REG(1, 64) XENT_REG(2, 64) XENT_REG(4, 64) XENT_REG(8, 64)
+  }
+  if (nvec <= 256 * 8) {
+    XENT_REG(1, 256) XENT_REG(2, 256) XENT_REG(4, 256) XENT_REG(8, 256)
+  }
+  XENT_REG(1, 1024) XENT_REG(2, 1024) XENT_REG(4, 1024) XENT_REG(8, 1024)
 #undef XENT_REG
   hipLaunchKernelGGL(xent_kernel<T>, dim3(M), dim3(256), 0, s, z, ldz, V, tgt, n_valid, loss_scale, row_loss);
 }
