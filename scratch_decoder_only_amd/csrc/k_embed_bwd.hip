@@ -53,15 +53,22 @@ __global__ void __launch_bounds__(256) csr_count_kernel(const int32_t* __restric
 // Linear-time rank (many row blocks): hist[b][v] becomes the number of rows
 // of key v in blocks before b (an exclusive scan over the blocks, one thread
 // per key, consecutive keys on consecutive threads).
+// (the counts of 16 blocks are loaded before any is overwritten: a load
+// after each store of the same array left a memory latency per block)
 __global__ void __launch_bounds__(256) csr_block_prefix_kernel(int32_t* __restrict__ hist, int nb, int nkeys) {
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= nkeys) return;
+  constexpr int G = 16;
   int run = 0;
-  for (int b = 0; b < nb; ++b) {
-    int32_t* h = hist + (long)b * nkeys + v;
-    const int c = *h;
-    *h = run;
-    run += c;
+  for (int b0 = 0; b0 < nb; b0 += G) {
+    int c[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) c[i] = b0 + i < nb ? hist[(long)(b0 + i) * nkeys + v] : 0;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (b0 + i < nb) hist[(long)(b0 + i) * nkeys + v] = run;
+      run += c[i];
+    }
   }
 }
 
@@ -290,8 +297,18 @@ __global__ void __launch_bounds__(256) segsum_keys_kernel(int C, int nkeys, cons
     const int b0 = chunk_base[v], b1 = chunk_base[v + 1];
     if (b1 - b0 <= 1) continue;
     for (int c = threadIdx.x; c < C; c += 256) {
+      // chunk sums added in chunk order, the loads of 8 chunks issued
+      // together (a Zipf-hot key has tens of chunks, all in this block)
       float acc = 0.f;
-      for (int w = b0; w < b1; ++w) acc += partial[(long)w * C + c];
+      int w = b0;
+      for (; w + 8 <= b1; w += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = partial[(long)(w + u) * C + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += x[u];
+      }
+      for (; w < b1; ++w) acc += partial[(long)w * C + c];
       dst[(long)v * C + c] += acc;
     }
   }
