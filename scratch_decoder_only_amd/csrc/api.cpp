@@ -385,7 +385,7 @@ lm_model* new_model(const lm_config* cfg) {
   m->Vp = m->h16 ? round_up(m->V, 128) : m->V;
   m->ldz = m->h16 ? m->Vp : round_up(m->V, 4);
   build_table(m);
-  m->dw_group = m->h16 && m->L > 0 && dw_group_units(m, m->M()) >= 2L * gemm_cus();
+  m->dw_group = m->h16 && m->L > 0 && dw_group_units(m, m->M()) > 0;
   carve(m, nullptr);
   return m;
 }
