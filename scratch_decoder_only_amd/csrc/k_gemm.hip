@@ -1936,12 +1936,14 @@ int gemm_f16(const GemmOp& op, float* ws, long ws_floats, hipStream_t s) { retur
 // instead of one per GEMM.
 long gemm_group_table_bytes(int n) { return (long)(n + 1) * (long)sizeof(GemmGroupEntry); }
 
-int gemm_group_plan(const GemmOp* ops, int n, void* table, int* tn) {
+int gemm_group_plan(const GemmOp* ops, int n, void* table, int* tn, float* const* part) {
   if (n < 1 || !table || !tn) return -1;
   for (int i = 0; i < n; ++i) {
     const GemmOp& op = ops[i];
+    // K slices (force_split > 1) need their partial-sum buffer
+    const bool sliced = op.force_split > 1 && part && part[i];
     if (op.a_kc || op.b_kc || op.epi != EPI_STORE || !op.c_f32 || op.bias || op.R || op.aux || op.colsum ||
-        op.cfg != 0 || op.force_split > 1 || op.M <= 0 || op.N <= 0 || op.K <= 0 || !check_16(op))
+        op.cfg != 0 || (op.force_split > 1 && !sliced) || op.M <= 0 || op.N <= 0 || op.K <= 0 || !check_16(op))
       return -1;
   }
   // 128 x 192 tiles, also where a width is not a multiple of 192 (the last
@@ -1962,10 +1964,18 @@ int gemm_group_plan(const GemmOp* ops, int n, void* table, int* tn) {
     d.bias = a.bias; d.R = a.R; d.ldr = a.ldr; d.aux = a.aux; d.ld_aux = a.ld_aux;
     d.M = a.M; d.N = a.N; d.K = a.K; d.M_out = a.M_out; d.k_split = a.k_split;
     d.split_stride = a.split_stride; d.colsum = a.colsum;
+    int slices = 1;
+    if (ops[i].force_split > 1) {
+      // whole K steps of 64 per slice; slice z of tile (m, n) stores into
+      // part[i] + z * M * N, rows of N floats
+      const int per = ((ops[i].K + ops[i].force_split - 1) / ops[i].force_split + 63) / 64 * 64;
+      slices = (ops[i].K + per - 1) / per;
+      d.C = part[i]; d.ldc = ops[i].N; d.k_split = per; d.split_stride = (long)ops[i].M * ops[i].N;
+    }
     e[i].first_unit = (int)units;
     e[i].tiles_m = (ops[i].M + 127) / 128;
     e[i].tiles_n = (ops[i].N + bn - 1) / bn;
-    units += (long)e[i].tiles_m * e[i].tiles_n;
+    units += (long)e[i].tiles_m * e[i].tiles_n * slices;
     if (units > (1L << 30)) return -1;
   }
   e[n].first_unit = (int)units;
@@ -1982,6 +1992,37 @@ static void launch_group(const void* table, int units, hipStream_t s) {
   nb = (nb + 7) / 8 * 8;  // whole XCD rounds
   hipLaunchKernelGGL((gemm16_ksplit_kernel<TN, 4, false, false, EPI_PARTIAL, float, E, true>), dim3(nb), dim3(512),
                      0, s, GemmArgs{}, units, 0, 0, static_cast<const GemmGroupEntry*>(table));
+}
+
+int gemm_group_slices_of(const GemmOp& op) {
+  if (op.force_split <= 1) return 1;
+  const int per = ((op.K + op.force_split - 1) / op.force_split + 63) / 64 * 64;
+  return (op.K + per - 1) / per;
+}
+
+// dst[r][c] = sum over z < S of part[z][r][c] in slice order (rows r <
+// rows, 4 columns per thread), for the sliced GEMMs of a grouped launch
+__global__ void __launch_bounds__(256) group_reduce_kernel(GroupReduce gr) {
+  const int e = blockIdx.y;
+  const float* __restrict__ part = gr.part[e];
+  float* __restrict__ dst = gr.dst[e];
+  const int nq = gr.cols[e] >> 2;
+  const long total = (long)gr.rows[e] * nq, stride4 = gr.stride[e] / 4;
+  for (long q = (long)blockIdx.x * 256 + threadIdx.x; q < total; q += (long)gridDim.x * 256) {
+    const long row = q / nq, col = (q - row * nq) * 4;
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(part + row * gr.cols[e] + col);
+    f32x4_t acc = __builtin_nontemporal_load(src);
+    for (int z = 1; z < gr.S[e]; ++z) acc += __builtin_nontemporal_load(src + z * stride4);
+    *reinterpret_cast<f32x4_t*>(dst + row * gr.ldc[e] + col) = acc;
+  }
+}
+
+void launch_group_reduce(const GroupReduce& gr, hipStream_t s) {
+  if (gr.n <= 0) return;
+  long most = 0;
+  for (int i = 0; i < gr.n; ++i) most = std::max(most, (long)gr.rows[i] * (gr.cols[i] >> 2));
+  const unsigned bx = (unsigned)std::min(1024L, (most + 255) / 256);
+  hipLaunchKernelGGL(group_reduce_kernel, dim3(bx, gr.n), dim3(256), 0, s, gr);
 }
 
 int gemm_group_launch(bool f16_ops, int tn, const void* table_dev, int units, hipStream_t s) {

@@ -78,7 +78,21 @@ int gemm16_colsum_rows(const GemmOp& op);
 // the tile width in *tn; gemm_group_launch runs the launch from a device copy
 // of that table. Each output element is one unit's fixed-order sum over K.
 long gemm_group_table_bytes(int n);
-int gemm_group_plan(const GemmOp* ops, int n, void* table, int* tn);
+// part (nullable): per op, the fp32 partial-sum buffer of an op with
+// force_split = s > 1, which then runs in K slices of whole 64-value steps
+// ([slices][M][N]; gemm_group_slices_of gives the count) to be summed by
+// launch_group_reduce; other ops store their result directly.
+int gemm_group_plan(const GemmOp* ops, int n, void* table, int* tn, float* const* part = nullptr);
+int gemm_group_slices_of(const GemmOp& op);
+constexpr int kGroupReduceMax = 32;
+struct GroupReduce {
+  int n;
+  const float* part[kGroupReduceMax];
+  float* dst[kGroupReduceMax];
+  int rows[kGroupReduceMax], cols[kGroupReduceMax], S[kGroupReduceMax];
+  long ldc[kGroupReduceMax], stride[kGroupReduceMax];
+};
+void launch_group_reduce(const GroupReduce& gr, hipStream_t s);
 int gemm_group_launch(bool f16_ops, int tn, const void* table_dev, int units, hipStream_t s);
 // compute units of the current device
 int gemm_cus();
