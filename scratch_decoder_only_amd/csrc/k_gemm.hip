@@ -1705,7 +1705,10 @@ static int pick_cfg(const GemmOp& op) {
   // writes the bias gradient's partial column sums (6% faster than 256 x 256
   // at 32768 x 2048 before counting the separate column-sum pass it saves)
   if (op.epi == EPI_DGELU && op.M >= 4096) return kCfgPipe128;
-  if (op.M >= 16384 || op.N >= 16384 || op.K >= 16384) return kCfgPipe;
+  // (16384 rows alone do not make a 256-row tile pay: at 16384 x 384 and x
+  // 512 over K = 128 the 256 x 256 tiles took 12.8 and 19.8 us, the 192 x 128
+  // and 128 x 128 ones below 10.3 and 12.1)
+  if (op.M >= 32768 || op.N >= 16384 || op.K >= 16384 || (op.M >= 16384 && op.N >= 4096)) return kCfgPipe;
   if (op.K >= 8192 && mn_max >= 3072 && mn_max <= 4096 && mn_min <= 1024) return kCfgPipe;
   if (op.epi == EPI_RESID) return kCfgSmall;
   // the QKV projection (both operands K-contiguous, a plain store): 192 x 128
